@@ -1,0 +1,197 @@
+"""Python entry to the fp64 CPU oracle of the selective scan (S6).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
+the CPU-baseline leg of the benchmark. The GPU library never imports or links
+it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``selscan_ref.c`` (plain C, IEEE double, libm); this
+module only converts arrays to float64 and calls it. The definition it
+follows, with its citations of the pages, is in the header of that file.
+
+Every array argument is converted exactly to float64 (float32 and bfloat16
+values are exactly representable). Layouts:
+
+* ``x, delta, z``: ``[batch, dim, seqlen]``
+* ``B, C``: ``[batch, dstate, seqlen]``
+* ``A``: ``[dim, dstate]``; ``D, dt_bias``: ``[dim]``
+* states: ``[batch, dim, dstate]``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "selscan_ref.c")
+_LIB_PATH = os.path.join(_HERE, "libselscan_ref.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, strict IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+               "-shared", "-pthread", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor (any dtype, any device)
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+class Oracle:
+    """The oracle library loaded from ``path`` (default: the built one)."""
+
+    def __init__(self, path: Optional[str] = None):
+        path = path or _LIB_PATH
+        if path == _LIB_PATH and not os.path.exists(path):
+            build(force=False)
+        lib = ctypes.CDLL(path)
+        lib.ssm_ref_fwd.restype = ctypes.c_int
+        lib.ssm_ref_fwd.argtypes = [_dp] * 10 + [ctypes.c_int64] * 4 + [_ip, ctypes.c_int64] + \
+            [_dp] * 4 + [ctypes.c_int]
+        lib.ssm_ref_step.restype = ctypes.c_int
+        lib.ssm_ref_step.argtypes = [_dp] * 9 + [ctypes.c_int64] * 3 + [_dp] * 2
+        self.lib = lib
+        self.path = path
+
+    def fwd(self, x, delta, A, B, C, D=None, z=None, dt_bias=None, h0=None, h0_scale=None,
+            rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
+        """Selective-scan forward over whole rows.
+
+        ``rows`` (optional) lists flat row indices ``b*dim + d`` to compute; the
+        outputs then have a leading axis of ``len(rows)`` instead of
+        ``[batch, dim]``. ``h0`` (optional, ``[batch, dim, dstate]``) is the state
+        before the first token; ``h0_scale`` its error scale (default ``|h0|``).
+
+        Returns a dict with ``y`` and ``y_scale`` (``[..., seqlen]``) and
+        ``last_state`` and ``state_scale`` (``[..., dstate]``), all float64.
+        """
+        x, delta, A, B, C = map(_f64, (x, delta, A, B, C))
+        D, z, dt_bias, h0, h0_scale = map(_f64, (D, z, dt_bias, h0, h0_scale))
+        batch, dim, L = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and A.shape == (dim, N)
+        assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
+        if z is not None:
+            assert z.shape == x.shape
+        if D is not None:
+            assert D.shape == (dim,)
+        if dt_bias is not None:
+            assert dt_bias.shape == (dim,)
+        if h0 is not None:
+            assert h0.shape == (batch, dim, N)
+        if h0_scale is not None:
+            assert h0 is not None and h0_scale.shape == h0.shape
+        if rows is None:
+            rows_arr = None
+            lead = (batch, dim)
+            nrows = batch * dim
+        else:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+            lead = (rows_arr.shape[0],)
+            nrows = rows_arr.shape[0]
+        y = np.empty(lead + (L,), np.float64)
+        ys = np.empty(lead + (L,), np.float64)
+        hs = np.empty(lead + (N,), np.float64)
+        hss = np.empty(lead + (N,), np.float64)
+        nt = nthreads or default_threads()
+        rc = self.lib.ssm_ref_fwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+            _ptr(h0), _ptr(h0_scale), batch, L, dim, N,
+            None if rows_arr is None else rows_arr.ctypes.data_as(_ip), nrows,
+            _ptr(y), _ptr(hs), _ptr(ys), _ptr(hss), nt)
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_fwd failed with code {rc}")
+        return {"y": y, "y_scale": ys, "last_state": hs, "state_scale": hss}
+
+    def step(self, state, x, delta, A, B, C, D=None, z=None, state_scale=None):
+        """One decode step from ``state`` (``[batch, dim, dstate]``).
+
+        ``delta`` is the pre-activation with any bias already added; the step
+        applies softplus to it. ``x, delta, z``: ``[batch, dim]``; ``B, C``:
+        ``[batch, dstate]``. Returns a dict with the new ``state`` and
+        ``state_scale`` and the output ``y`` and ``y_scale`` (float64). The inputs
+        are not modified.
+        """
+        h = _f64(state).copy()
+        hs = _f64(state_scale).copy() if state_scale is not None else np.abs(h)
+        x, delta, A, B, C, D, z = map(_f64, (x, delta, A, B, C, D, z))
+        batch, dim, N = h.shape
+        assert x.shape == (batch, dim) and delta.shape == (batch, dim)
+        assert A.shape == (dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
+        y = np.empty((batch, dim), np.float64)
+        ys = np.empty((batch, dim), np.float64)
+        rc = self.lib.ssm_ref_step(_ptr(h), _ptr(hs), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                  _ptr(C), _ptr(D), _ptr(z), batch, dim, N, _ptr(y), _ptr(ys))
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_step failed with code {rc}")
+        return {"y": y, "y_scale": ys, "state": h, "state_scale": hs}
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def fwd(*args, **kw):
+    """Forward through the built oracle; see ``Oracle.fwd``."""
+    return default().fwd(*args, **kw)
+
+
+def step(*args, **kw):
+    """One decode step through the built oracle; see ``Oracle.step``."""
+    return default().step(*args, **kw)
+
+
+def scaled_error(got, ref, scale, floor: float = 1e-30) -> float:
+    """max_i |got_i - ref_i| / max(scale_i, floor), NaN-aware.
+
+    Positions where ``ref`` is NaN must be NaN in ``got`` too (else the error
+    is infinite); they are excluded from the maximum. Infinite references must
+    be matched exactly.
+    """
+    got = _f64(got)
+    ref = _f64(ref)
+    scale = _f64(scale)
+    nan_ref = np.isnan(ref)
+    if np.any(np.isnan(got) != nan_ref):
+        return float("inf")
+    inf_ref = np.isinf(ref)
+    if np.any(inf_ref):
+        if np.any(got[inf_ref] != ref[inf_ref]):
+            return float("inf")
+    ok = ~(nan_ref | inf_ref)
+    if not np.any(ok):
+        return 0.0
+    err = np.abs(got[ok] - ref[ok]) / np.maximum(np.abs(scale[ok]), floor)
+    return float(np.max(err)) if err.size else 0.0

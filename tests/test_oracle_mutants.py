@@ -1,0 +1,70 @@
+"""Planted mistakes in the oracle must each be caught by at least one pin.
+
+Each mutant is a copy of ``oracle/selscan_ref.c`` with one plausible mistake
+(a dropped term, a wrong sign or index, a transposed or swapped operand),
+compiled with gcc into a temporary directory and run through every pin. CPU
+only; the built oracle itself is untouched.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "selscan_ref.c")
+
+# (name, original text, replacement). Every original must occur in the source.
+MUTANTS = [
+    ("decay_sign", "exp(dl * Ad[n])", "exp(-dl * Ad[n])"),
+    ("decay_no_delta", "exp(dl * Ad[n])", "exp(Ad[n])"),
+    ("input_no_delta", "dl * Bb[n * L + t] * x[t]", "Bb[n * L + t] * x[t]"),
+    ("B_transposed", "dl * Bb[n * L + t] * x[t]", "dl * Bb[t * N + n] * x[t]"),
+    ("readout_uses_B", "acc += Cb[n * L + t] * h[n];", "acc += Bb[n * L + t] * h[n];"),
+    ("C_time_shift", "acc += Cb[n * L + t] * h[n];",
+     "acc += Cb[n * L + (t > 0 ? t - 1 : 0)] * h[n];"),
+    ("no_D_skip", "double yv = acc + Dd * x[t];", "double yv = acc;"),
+    ("D_outside_gate", "yv *= g;", "yv = acc * g + Dd * x[t];"),
+    ("gate_sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("softplus_sign", "log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
+    ("softplus_no_max", "fmax(u, 0.0) + log1p", "log1p"),
+    ("bias_dropped", "softplus(dr[t] + bias)", "softplus(dr[t])"),
+    ("bias_outside", "softplus(dr[t] + bias)", "(softplus(dr[t]) + bias)"),
+    ("A_row_index", "j->A + d * N", "j->A + b * N"),
+    ("h0_ignored", "h[n] = j->h0 ? j->h0[row * N + n] : 0.0;", "h[n] = 0.0;"),
+    ("state_no_decay", "h[n] = abar * h[n] + bx;", "h[n] = h[n] + bx;"),
+    ("scale_no_decay", "habs[n] = abar * habs[n] + fabs(bx);", "habs[n] = habs[n] + fabs(bx);"),
+    ("scale_no_D", "double sv = acc_abs + fabs(Dd * x[t]);", "double sv = acc_abs;"),
+    ("last_state_scale_swap", "if (j->last_state) j->last_state[i * N + n] = h[n];",
+     "if (j->last_state) j->last_state[i * N + n] = habs[n];"),
+    ("step_decay_index", "exp(dl * A[d * N + n])", "exp(dl * A[n])"),
+    ("step_no_delta", "dl * B[b * N + n] * xv", "B[b * N + n] * xv"),
+    ("step_readout_B", "acc += C[b * N + n] * h[n];", "acc += B[b * N + n] * h[n];"),
+    ("step_no_D", "double yv = acc + Dd * xv;", "double yv = acc;"),
+    ("step_no_gate", "yv *= g;\n                sv *= fabs(g);\n            }\n            y[row] = yv;",
+     "sv *= fabs(g);\n            }\n            y[row] = yv;"),
+    ("step_softplus_dropped", "const double dl = softplus(delta[row]);",
+     "const double dl = delta[row];"),
+]
+
+
+@pytest.mark.parametrize("name,orig,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, orig, repl):
+    src = open(SRC).read()
+    assert src.count(orig) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(orig, repl, 1)
+    c = tmp_path / f"{name}.c"
+    c.write_text(mutated)
+    so = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", str(c), "-o",
+                    str(so), "-lm"], check=True)
+    O = oracle.Oracle(str(so))
+    caught = []
+    for pname, fn in PINS.items():
+        try:
+            fn(O)
+        except (AssertionError, FloatingPointError, ValueError, RuntimeError):
+            caught.append(pname)
+    assert caught, f"mutant {name} passed every pin"
