@@ -1,0 +1,256 @@
+"""Throughput of the selective scan on one MI355X.
+
+A step is one selscan_fwd call on the Mamba-1.4B-shaped layer (batch 8,
+L 2048, d_inner 4096, N 16; bf16 x/delta/z/B/C/y, fp32 state and arithmetic)
+with inputs resident in HBM. The line also reports the decode step on the
+2.8B-shaped state (batch 256, d_inner 5120, N 16) in microseconds, the other
+forward workloads, and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extras]
+                       [--no-cpu-baseline] [--only fwd|decode|long|m130m]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X published HBM3E bandwidth
+FP32_VEC_PEAK = 157.3e12   # FLOP/s, MI355X published fp32 vector rate
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w):
+    """HBM bytes one forward call must move: every input read once, y and the
+    final state written once (B and C re-reads by other row blocks hit cache)."""
+    es = 2 if w.dtype == "bf16" else 4
+    E = w.batch * w.seqlen * w.dim
+    n_seq = 4 if w.gate else 3                      # x, delta, (z), y
+    bc = 2 * w.batch * w.dstate * w.seqlen * es      # B, C
+    params = w.dim * w.dstate * 4 + 2 * w.dim * 4    # A, D, dt_bias
+    state = w.batch * w.dim * w.dstate * 4           # last_state
+    return n_seq * E * es + bc + params + state
+
+
+def step_bytes(w):
+    """HBM bytes of one decode step: the fp32 state read and written, the
+    per-row x, delta, z read and y written, B, C, A, D read."""
+    es = 2 if w.dtype == "bf16" else 4
+    rows = w.batch * w.dim
+    return 2 * rows * w.dstate * 4 + 4 * rows * es + 2 * w.batch * w.dstate * es \
+        + w.dim * w.dstate * 4 + w.dim * 4
+
+
+def method_flops(w):
+    """fp32 operations the method needs per forward call, counting an FMA as 2
+    and each transcendental (exp, log, reciprocal) as 1:
+    per (token, state): l*A, exp, w*B, state FMA, readout FMA  -> 7;
+    per token: bias add, softplus (exp, log, add), delta*x, D*x FMA,
+    silu (exp, add, reciprocal, multiply), gate multiply      -> 12."""
+    E = w.batch * w.seqlen * w.dim
+    return E * (7 * w.dstate + 12)
+
+
+def device_inputs(w, torch, dev):
+    from selective_state_space_48_amd import workloads as W
+
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp = W.fwd_inputs(w)
+
+    def t(a, dt=torch.float32):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+
+    return dict(x=t(inp["x"], td), delta=t(inp["delta"], td), z=t(inp["z"], td), A=t(inp["A"]),
+                B=t(inp["B"], td), C=t(inp["C"], td), D=t(inp["D"]), dt_bias=t(inp["dt_bias"]))
+
+
+def time_fwd(w, steps, warmup, torch, dev):
+    from selective_state_space_48_amd import selscan
+
+    d = device_inputs(w, torch, dev)
+    y = torch.empty_like(d["x"])
+    hs = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def run():
+        selscan.fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                    dt_bias=d["dt_bias"], y=y, last_state=hs)
+
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream(dev)   # the stream selscan launches on
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    del d, y, hs
+    return ms, wall
+
+
+def time_decode(w, steps, warmup, torch, dev):
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    p = W.params(w)
+
+    def t(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+
+    state = t(W.random_state(w))
+    A, D = t(p["A"]), t(p["D"])
+    ins = []
+    for s in range(w.steps):
+        si = W.step_inputs(w, s)
+        ins.append((t(si["x"], td), t(si["delta"], td), t(si["B"], td), t(si["C"], td),
+                    t(si["z"], td)))
+    y = torch.empty((w.batch, w.dim), dtype=td, device=dev)
+    for i in range(warmup):
+        x, dl, B, C, z = ins[i % len(ins)]
+        selscan.step(state, x, dl, A, B, C, D=D, z=z, y=y)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        x, dl, B, C, z = ins[i % len(ins)]
+        selscan.step(state, x, dl, A, B, C, D=D, z=z, y=y)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(w, target_s=8.0):
+    """The oracle on a bounded sample of the workload: the first rows of batch
+    entry 0, full sequence length, all host threads."""
+    import oracle
+    from selective_state_space_48_amd import workloads as W
+
+    nt = oracle.default_threads()
+    inp = W.fwd_inputs(w, batches=[0])
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
+    kw = dict(D=inp["D"], z=inp["z"], dt_bias=inp["dt_bias"])
+    rows = nt * 2
+    t0 = time.perf_counter()
+    oracle.fwd(*args, rows=np.arange(rows), nthreads=nt, **kw)
+    dt = time.perf_counter() - t0
+    rows = int(min(w.dim, max(rows, rows * target_s / max(dt, 1e-3))))
+    rows = max(nt, rows // nt * nt)
+    t0 = time.perf_counter()
+    oracle.fwd(*args, rows=np.arange(rows), nthreads=nt, **kw)
+    dt = time.perf_counter() - t0
+    elems = rows * w.seqlen
+    return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": nt, "kind": "oracle",
+            "sample": f"{rows} rows (batch 0, channels 0..{rows - 1}) x {w.seqlen} tokens of "
+                      f"{w.name}, fp64, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="headline forward only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m"], default=None,
+                    help="run just one workload (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the selective scan here "
+              "is built and measured on a single MI355X; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_48_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    out = {}
+    w = W.get(W.HEADLINE)
+
+    if args.only in (None, "fwd"):
+        log(f"[bench] {w.name}: {args.warmup} warmup + {args.steps} timed forward calls")
+        ms, wall = time_fwd(w, args.steps, args.warmup, torch, dev)
+        E = w.elements
+        gelem = E / (ms * 1e-3) / 1e9
+        bytes_ = algorithmic_bytes(w)
+        flops = method_flops(w)
+        hbm = bytes_ / (ms * 1e-3)
+        alu = flops / (ms * 1e-3)
+        log(f"[bench] {w.name}: {ms * 1e3:.1f} us/call, {gelem:.1f} Gelem/s, "
+            f"{hbm / 1e12:.2f} TB/s algorithmic, {alu / 1e12:.1f} TFLOP/s method")
+        out.update({
+            "metric": "selective-scan fwd Gelem/s (B*L*d_inner), Mamba-1.4B-shaped layer",
+            "value": round(gelem, 3),
+            "unit": "Gelem/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16 in/out, f32 state+math",
+            "data": "synthetic (seeded; see selective_state_space_48_amd/workloads.py)",
+            "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen,
+                       "d_inner": w.dim, "d_state": w.dstate, "gate": w.gate,
+                       "parallelism": "single GPU"},
+            "hbm": {"achieved": round(hbm / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                    "frac": round(hbm / HBM_PEAK, 4), "bytes_per_call": bytes_},
+            "roofline": {"bound": "alu", "achieved": round(alu / 1e12, 3),
+                         "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": round(alu / FP32_VEC_PEAK, 4), "traffic": None,
+                         "kernel": "fwd_kernel<bf16,G=4,gate,vec,output pass>",
+                         "flops_per_call": flops},
+            "wall_s_timed": round(wall, 4),
+        })
+
+    extras = {}
+    if not args.no_extras and args.only in (None, "decode"):
+        wd = W.get(W.DECODE)
+        log(f"[bench] {wd.name}: decode steps")
+        us = time_decode(wd, 256, 16, torch, dev) * 1e3
+        gbs = step_bytes(wd) / (us * 1e-6) / 1e9
+        log(f"[bench] decode: {us:.2f} us/step, {gbs:.0f} GB/s")
+        extras["decode"] = {"workload": wd.name, "us_per_step": round(us, 3),
+                            "achieved_GBps": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
+                            "bytes_per_step": step_bytes(wd)}
+    for key, name in (("long", "long_f32_b1_l1048576_d128"), ("m130m", "m130m_f32_b8_l2048_d1536")):
+        if args.no_extras or args.only not in (None, key):
+            continue
+        wx = W.get(name)
+        log(f"[bench] {name}: forward")
+        ms, _ = time_fwd(wx, 10, 2, torch, dev)
+        extras[key] = {"workload": name, "ms_per_call": round(ms, 4),
+                       "Gelem_per_s": round(wx.elements / (ms * 1e-3) / 1e9, 2),
+                       "frac_hbm": round(algorithmic_bytes(wx) / (ms * 1e-3) / HBM_PEAK, 4)}
+    if extras:
+        out["extras"] = extras
+
+    if args.only in (None, "fwd") and not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w)
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

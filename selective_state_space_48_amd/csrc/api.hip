@@ -1,0 +1,209 @@
+// libselscan C ABI: argument checks, launch planning, workspace, launches.
+// Every check runs before the first HIP call, so argument errors are
+// reported without touching the device (and are testable without a GPU).
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/selscan.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace selscan;
+
+namespace selscan {
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+}
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+Span span(const void* p, int64_t bytes) {
+    Span s;
+    if (p && bytes > 0) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + uintptr_t(bytes);
+    }
+    return s;
+}
+bool overlaps(const Span& a, const Span& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// Sizes in elements of the tensors of a call; false on overflow.
+struct Sizes {
+    int64_t seq;    // batch * dim * L        (x, delta, z, y)
+    int64_t bc;     // batch * N * L          (B, C)
+    int64_t param;  // dim * N                (A)
+    int64_t state;  // batch * dim * N        (states)
+    int64_t rows;   // batch * dim
+};
+bool sizes(const selscan_dims_t& d, int64_t L, Sizes* s) {
+    int64_t t;
+    if (!mul_ok(d.batch, d.dim, &s->rows)) return false;
+    if (!mul_ok(s->rows, L, &s->seq) || !mul_ok(s->seq, 4, &t)) return false;
+    if (!mul_ok(d.batch, d.dstate, &t) || !mul_ok(t, L, &s->bc) || !mul_ok(s->bc, 4, &t)) return false;
+    if (!mul_ok(d.dim, d.dstate, &s->param)) return false;
+    if (!mul_ok(s->rows, d.dstate, &s->state) || !mul_ok(s->state, 4, &t)) return false;
+    // launch geometry limits: 64-row blocks per grid, 4 lanes per row for the step
+    if (s->rows > (int64_t(1) << 36)) return false;
+    return true;
+}
+
+int check_common(const selscan_dims_t* dims, bool fwd) {
+    if (!dims) return SELSCAN_ERR_NULL;
+    if (dims->batch < 0 || dims->dim < 0 || dims->dstate < 0 || (fwd && dims->seqlen < 0))
+        return SELSCAN_ERR_DIMS;
+    if (dims->dtype != SELSCAN_F32 && dims->dtype != SELSCAN_BF16) return SELSCAN_ERR_DTYPE;
+    if (dims->dstate != kN) return SELSCAN_ERR_DSTATE;
+    return SELSCAN_OK;
+}
+
+int fwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
+             const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
+             const selscan_dims_t* dims, int32_t segments, int32_t groups, void* stream) {
+    int rc = check_common(dims, true);
+    if (rc != SELSCAN_OK) return rc;
+    if (!x || !delta || !A || !B || !C || !y) return SELSCAN_ERR_NULL;
+    if (segments < 0 || segments > 65536) return SELSCAN_ERR_CONFIG;
+    if (groups != 0 && groups != 1 && groups != 2 && groups != 4) return SELSCAN_ERR_CONFIG;
+    const int64_t L = dims->seqlen;
+    // The kernels address B/C rows with 32-bit offsets of up to N*L elements.
+    if (L >= (int64_t(1) << 27)) return SELSCAN_ERR_DIMS;
+    Sizes sz;
+    if (!sizes(*dims, L, &sz)) return SELSCAN_ERR_DIMS;
+    for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, (const void*)y,
+                          (const void*)last_state})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span out_y = span(y, sz.seq * es), out_s = span(last_state, sz.state * 4);
+    const Span ins[] = {span(x, sz.seq * es),      span(delta, sz.seq * es), span(z, sz.seq * es),
+                        span(B, sz.bc * es),       span(C, sz.bc * es),      span(A, sz.param * 4),
+                        span(D, dims->dim * 4),    span(dt_bias, dims->dim * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, out_y) || overlaps(s, out_s)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_y, out_s)) return SELSCAN_ERR_ALIAS;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sz.rows == 0) return SELSCAN_OK;
+    if (L == 0) {
+        if (last_state && launch_fill_zero(last_state, sz.state, st) != hipSuccess)
+            return SELSCAN_ERR_LAUNCH;
+        return SELSCAN_OK;
+    }
+
+    // ---- plan ----
+    FwdPlan plan{};
+    plan.groups = groups ? groups : 4;
+    plan.vec = (L * es) % 16 == 0;
+    const int64_t row_blocks = (dims->dim + kWave - 1) / kWave;
+    const int64_t waves = row_blocks * dims->batch * plan.groups;
+    int64_t S = segments;
+    if (S == 0) {
+        // Fill the machine: about two waves per SIMD (4 SIMDs x 256 CUs). Only
+        // worth a second pass when the sequence is long.
+        const int64_t target = 2048;
+        S = 1;
+        if (waves < target && L >= 16 * kChunk) {
+            S = (target + waves - 1) / waves;
+            const int64_t max_by_len = L / (8 * kChunk);
+            if (S > max_by_len) S = max_by_len;
+            if (S < 1) S = 1;
+        }
+    }
+    if (S > 1) {
+        int64_t seg_len = (L + S - 1) / S;
+        seg_len = (seg_len + kChunk - 1) / kChunk * kChunk;
+        S = (L + seg_len - 1) / seg_len;
+        plan.seg_len = seg_len;
+    } else {
+        plan.seg_len = L;
+    }
+    plan.segments = int32_t(S);
+    if (int64_t(plan.segments) * row_blocks * dims->batch > INT32_MAX) return SELSCAN_ERR_DIMS;
+
+    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state};
+    FwdShape shape{dims->batch, L, dims->dim, dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
+    void* ws = nullptr;
+    const size_t ws_bytes = fwd_workspace_bytes(shape, plan);
+    if (ws_bytes) {
+        if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return SELSCAN_ERR_ALLOC;
+        }
+    }
+    const hipError_t e = launch_fwd(t, shape, plan, ws, st);
+    if (ws) (void)hipFreeAsync(ws, st);
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int selscan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
+                const selscan_dims_t* dims, void* stream) {
+    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, 0, 0, stream);
+}
+
+int selscan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* dt_bias, void* y,
+                   float* last_state, const selscan_dims_t* dims, int32_t segments,
+                   int32_t groups, void* stream) {
+    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, segments, groups,
+                    stream);
+}
+
+int selscan_step(float* state, const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, void* y,
+                 const selscan_dims_t* dims, void* stream) {
+    int rc = check_common(dims, false);
+    if (rc != SELSCAN_OK) return rc;
+    if (!state || !x || !delta || !A || !B || !C || !y) return SELSCAN_ERR_NULL;
+    Sizes sz;
+    if (!sizes(*dims, 1, &sz)) return SELSCAN_ERR_DIMS;
+    for (const void* p : {(const void*)state, x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)y})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span out_y = span(y, sz.rows * es), io_s = span(state, sz.state * 4);
+    const Span ins[] = {span(x, sz.rows * es), span(delta, sz.rows * es), span(z, sz.rows * es),
+                        span(B, dims->batch * kN * es), span(C, dims->batch * kN * es),
+                        span(A, sz.param * 4), span(D, dims->dim * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, out_y) || overlaps(s, io_s)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_y, io_s)) return SELSCAN_ERR_ALIAS;
+    if (sz.rows == 0) return SELSCAN_OK;
+    StepTensors t{state, x, delta, A, B, C, D, z, y};
+    const hipError_t e = launch_step(t, dims->batch, dims->dim,
+                                     dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+const char* selscan_strerror(int code) {
+    switch (code) {
+        case SELSCAN_OK: return "ok";
+        case SELSCAN_ERR_NULL: return "a required pointer is NULL";
+        case SELSCAN_ERR_DIMS: return "a size is negative or too large";
+        case SELSCAN_ERR_DSTATE: return "unsupported dstate (this version supports 16)";
+        case SELSCAN_ERR_DTYPE: return "unsupported dtype";
+        case SELSCAN_ERR_LAUNCH: return "kernel launch failed";
+        case SELSCAN_ERR_ALLOC: return "workspace allocation failed";
+        case SELSCAN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case SELSCAN_ERR_ALIAS: return "an output overlaps an input or another output";
+        case SELSCAN_ERR_CONFIG: return "launch options out of range";
+        default: return "unknown error code";
+    }
+}
+
+int selscan_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Device helpers shared by the selective-scan kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace selscan {
+
+using bf16_bits = uint16_t;  // bfloat16 storage: the upper half of an fp32
+
+constexpr int kWave = 64;    // CDNA wavefront width
+constexpr int kN = 16;       // supported state size
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// ---- storage conversions -------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_bits v) { return __uint_as_float(uint32_t(v) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// Round to nearest even through the hardware conversion (v_cvt_pk_bf16_f32).
+template <> __device__ __forceinline__ bf16_bits from_f32<bf16_bits>(float v) {
+    return __builtin_bit_cast(bf16_bits, (__bf16)v);
+}
+
+// The two bfloat16 halves of a 32-bit word, as fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---- the scalar functions of the method -----------------------------------
+//
+// The hardware transcendentals work in base 2: v_exp_f32 is 2^x, v_log_f32 is
+// log2(x), v_rcp_f32 is 1/x. The step size is therefore carried in log2 units,
+// l = softplus(u) / ln 2, so that the decay exp(delta * A) is 2^(l * A) with a
+// single multiply, and delta itself is l * ln 2.
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(u) / ln 2 = max(u, 0)/ln 2 + log2(1 + e^{-|u|}).
+// log2(1 + e) is taken from w = fl(1 + e) plus a first-order correction for
+// the rounding of w: with c = e - (w - 1) (exact), log(1 + e) = log(w) + c/w
+// + O(c^2), and 1/w is replaced by 2 - w, whose error only matters when c is
+// already below half an ulp of the result. This keeps the relative accuracy
+// of small step sizes (u very negative), where 1 + e rounds to 1.
+__device__ __forceinline__ float softplus_log2(float u) {
+    const float ul = u * kLog2e;
+    const float e = exp2_hw(-fabsf(ul));
+    const float w = 1.0f + e;
+    const float c = e - (w - 1.0f);
+    const float corr = c * (2.0f - w) * kLog2e;
+    return fmaxf(ul, 0.0f) + (log2_hw(w) + corr);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z}); saturates cleanly at both ends.
+__device__ __forceinline__ float silu(float z) {
+    return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+}
+
+}  // namespace selscan

@@ -1,0 +1,528 @@
+// Forward selective scan (S6) kernels for gfx950.
+//
+// The recurrence per (batch b, channel d) row, from "State Space Models and
+// Mamba" (multigrid.ai), section "Selective state: the change that made it
+// work on text":
+//     delta_t = softplus(delta_raw_t + dt_bias_d)
+//     h_n     = exp(delta_t A_dn) h_n + delta_t B_nt x_t
+//     y_t     = (sum_n C_nt h_n + D_d x_t) silu(z_t)
+// Following the hardware-aware evaluation of "Mamba: Linear-Time Sequence
+// Modeling with Selective State Spaces" (azimuth.plus), kernel fusion: every
+// input is read from HBM once, the state lives in registers, and only y (and
+// the final state) is written back; the (B, L, D, N) state tensor never exists.
+//
+// Mapping (MI355X-first, not the pages' GPU design):
+// * One lane owns one (b, d) row and walks its tokens in order, so the scan is
+//   a plain register recurrence with no cross-lane combine at all. The 64 rows
+//   of a wave share b, which makes B_t and C_t wave-uniform: they are fetched
+//   with scalar loads into SGPRs and fed to the VALU as the scalar operand,
+//   costing no VGPRs, no LDS traffic and no vector-memory instructions.
+// * The 16 states of a row are split across the G waves of a workgroup (N/G
+//   states each), so that B*d/64*G waves fill the 1024 SIMDs. Per token and
+//   state the inner loop is one multiply (l*A), one v_exp_f32, one multiply
+//   (w*B), and two FMAs (state, readout): the measured floor of the method.
+// * Per-token work that does not depend on n (softplus, w = delta*x, D*x,
+//   silu(z)) is computed once per row and token, split between the waves by
+//   token slices and shared through LDS. Partial readouts of the G waves are
+//   summed through LDS in a fixed order (deterministic).
+// * Time advances in 32-token chunks. Each wave loads its own token slice of
+//   x, delta and z straight from HBM in 16-byte vectors, one chunk ahead, so
+//   HBM latency hides behind a chunk of arithmetic; the G slices of a chunk
+//   tile whole cache lines. Two barriers per chunk, about 54 KB of LDS at G=4.
+// * Long sequences with few rows are cut into segments scanned in parallel
+//   ("parallel scan" of the same page: the pair (decay, state) composes
+//   associatively): a state pass gives each segment's end state from zero and
+//   its summed step size, a carry pass composes them in order, and the output
+//   pass rescans each segment from its carried-in state.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace selscan {
+namespace {
+
+template <typename T> struct Elem;
+template <> struct Elem<float> { static constexpr int kPer16 = 4; };
+template <> struct Elem<bf16_bits> { static constexpr int kPer16 = 8; };
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& v, float* o) {
+    if constexpr (sizeof(T) == 4) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    } else {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float* f) {
+    uint4 v;
+    if constexpr (sizeof(T) == 4) {
+        v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+        v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
+    } else {
+        auto p = [](float a, float b) {
+            return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
+        };
+        v.x = p(f[0], f[1]); v.y = p(f[2], f[3]); v.z = p(f[4], f[5]); v.w = p(f[6], f[7]);
+    }
+    return v;
+}
+
+// An 8-byte load through the constant address space: with a wave-uniform
+// address the compiler must use a scalar (SMEM) load into SGPRs. Going
+// through an integer keeps address-space inference from turning it back into
+// a global-memory (vector) load.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ uint2 sload8(const T* p) {
+    using CP = const __attribute__((address_space(4))) u32x2*;
+    const u32x2 v = *(CP)(reinterpret_cast<uintptr_t>(p));
+    return make_uint2(v.x, v.y);
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(const uint2& v, float* o) {
+    if constexpr (sizeof(T) == 4) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    } else {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    }
+}
+
+// LDS of one workgroup: the per-token pairs (l, w) of the current chunk and
+// the partial readouts of the G waves. Row strides are odd multiples of 16
+// bytes, so 16-byte accesses by consecutive lanes to consecutive rows do not
+// conflict.
+template <int G, int CH, int MODE>
+struct alignas(16) Smem {
+    static constexpr int kPairB = CH * 8 + 16;  // float2-per-token row stride (bytes)
+    static constexpr int kYB = CH * 4 + 16;     // float-per-token row stride (bytes)
+    unsigned char lw[kWave * kPairB];
+    unsigned char yp[MODE == 0 ? G : 1][MODE == 0 ? kWave * kYB : 16];
+    double lsum[MODE == 1 ? G : 1][kWave];
+};
+
+struct FwdKArgs {
+    const void* x;
+    const void* delta;
+    const void* z;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* dt_bias;
+    void* y;
+    float* last_state;
+    const float* h0;   // [segments][rows][N] carried-in states, or null
+    float* seg_state;  // [segments][rows][N] (state pass)
+    double* seg_lsum;  // [segments][rows]    (state pass)
+    int64_t batch, L, dim, seg_len;
+    int32_t segments, row_blocks;
+};
+
+// MODE 0: output pass (y, and last_state from the final segment).
+// MODE 1: state pass (each segment's end state from zero, and its summed l).
+template <typename T, int G, bool GATE, bool VEC, int MODE>
+__global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
+    constexpr int CH = kChunk;
+    constexpr int NG = kN / G;              // states per wave
+    constexpr int TS = CH / G;              // tokens per wave in the per-token phases
+    constexpr int V = Elem<T>::kPer16;      // elements per 16-byte vector
+    constexpr int SV = TS / V;              // 16-byte vectors per row slice
+    constexpr int SB = 8 / int(sizeof(T));  // tokens per B/C sub-block (8 bytes per state)
+    constexpr int NSB = CH / SB;
+    constexpr bool LOADZ = GATE && MODE == 0;
+    static_assert(TS % V == 0 && SV >= 1, "tile shape");
+    using S = Smem<G, CH, MODE>;
+    __shared__ S sm;
+
+    const T* __restrict__ X = static_cast<const T*>(a.x);
+    const T* __restrict__ DL = static_cast<const T*>(a.delta);
+    const T* __restrict__ Z = static_cast<const T*>(a.z);
+    const T* __restrict__ Bp = static_cast<const T*>(a.B);
+    const T* __restrict__ Cp = static_cast<const T*>(a.C);
+
+    const int tid = threadIdx.x;
+    // The wave index is uniform across the wave; saying so lets every address
+    // derived from it (B and C rows) live in SGPRs.
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+
+    // block -> (segment, batch entry, 64-row block)
+    int64_t blk = blockIdx.x;
+    const int rb = int(blk % a.row_blocks);
+    blk /= a.row_blocks;
+    const int64_t b = blk % a.batch;
+    const int seg = int(blk / a.batch);
+
+    const int64_t d0 = int64_t(rb) * kWave;
+    const int64_t d = d0 + lane;
+    const bool row_ok = d < a.dim;
+    const int64_t row = b * a.dim + (row_ok ? d : d0);  // clamped for safe reads
+    const int64_t t_begin = int64_t(seg) * a.seg_len;
+    const int64_t t_end = min(a.L, t_begin + a.seg_len);
+    const int nchunks = int((t_end - t_begin + CH - 1) / CH);
+    const int n0 = wv * NG;
+
+    const float bias = (a.dt_bias && row_ok) ? a.dt_bias[d] : 0.0f;
+    const float Dd = (a.D && row_ok) ? a.D[d] : 0.0f;
+    float An[NG], h[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        An[j] = row_ok ? a.A[d * kN + n0 + j] : 0.0f;
+        h[j] = (a.h0 && row_ok) ? a.h0[(int64_t(seg) * a.batch * a.dim + b * a.dim + d) * kN + n0 + j]
+                                : 0.0f;
+    }
+    double lsum_acc = 0.0;
+
+    // ---- this wave's token slice [wv*TS, wv*TS+TS) of a chunk, straight from HBM ----
+    // Each lane reads its own row; the G waves read adjacent slices of the same
+    // rows, so every fetched cache line is used whole.
+    uint4 px[SV], pd[SV], pz[LOADZ ? SV : 1];
+    auto load_slice = [&](int c) {
+        const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
+        const int64_t off = row * a.L + ts;
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            const int64_t tk = ts + k * V;
+            if constexpr (VEC) {
+                const bool ok = tk < t_end;  // whole vector in or out (L, t_end multiples of V)
+                px[k] = ok ? *reinterpret_cast<const uint4*>(X + off + k * V) : make_uint4(0, 0, 0, 0);
+                pd[k] = ok ? *reinterpret_cast<const uint4*>(DL + off + k * V) : make_uint4(0, 0, 0, 0);
+                if constexpr (LOADZ)
+                    pz[k] = ok ? *reinterpret_cast<const uint4*>(Z + off + k * V) : make_uint4(0, 0, 0, 0);
+            } else {
+                float fx[V], fd[V], fz[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const bool ok = tk + e < t_end;
+                    fx[e] = ok ? to_f32(X[off + k * V + e]) : 0.0f;
+                    fd[e] = ok ? to_f32(DL[off + k * V + e]) : 0.0f;
+                    fz[e] = (LOADZ && ok) ? to_f32(Z[off + k * V + e]) : 0.0f;
+                }
+                px[k] = pack16<T>(fx);
+                pd[k] = pack16<T>(fd);
+                if constexpr (LOADZ) pz[k] = pack16<T>(fz);
+            }
+        }
+    };
+
+    // ---- per-token phase before the scan ----
+    // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this wave's
+    // registers until its epilogue of the same slice.
+    float dx[TS], gz[TS];
+    auto prologue = [&](int c) {
+        const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
+        float xs[TS], ds[TS], zs[TS];
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            unpack16<T>(px[k], xs + k * V);
+            unpack16<T>(pd[k], ds + k * V);
+            if constexpr (LOADZ) unpack16<T>(pz[k], zs + k * V);
+        }
+        float4* lwrow = reinterpret_cast<float4*>(&sm.lw[lane * S::kPairB]) + wv * TS / 2;
+#pragma unroll
+        for (int j = 0; j < TS; j += 2) {
+            float l[2], w[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bool ok = ts + j + u < t_end;
+                l[u] = ok ? softplus_log2(ds[j + u] + bias) : 0.0f;
+                w[u] = ok ? l[u] * kLn2 * xs[j + u] : 0.0f;
+                if constexpr (MODE == 1) lsum_acc += double(l[u]);
+                if constexpr (MODE == 0) {
+                    dx[j + u] = Dd * xs[j + u];
+                    gz[j + u] = 1.0f;
+                    if constexpr (LOADZ) gz[j + u] = silu(zs[j + u]);
+                }
+            }
+            lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
+        }
+    };
+
+    // ---- the scan over one chunk: this wave's NG states, all CH tokens ----
+    auto scan_chunk = [&](int c, bool full) {
+        const int64_t t0 = t_begin + int64_t(c) * CH;
+        const float4* lwrow = reinterpret_cast<const float4*>(&sm.lw[lane * S::kPairB]);
+        float* yrow = reinterpret_cast<float*>(&sm.yp[MODE == 0 ? wv : 0][lane * S::kYB]);
+        const T* Bc = Bp + (b * kN + n0) * a.L + t0;   // B/C at (b, n0, t0)
+        const T* Cc = Cp + (b * kN + n0) * a.L + t0;
+        if (full && VEC) {
+            // Per sub-block of SB tokens: one 8-byte scalar load per state for
+            // B (and C) into SGPRs, the (l, w) pairs from LDS, then the
+            // recurrence from registers. Offsets stay 32-bit (L < 2^31).
+            const int Ls = int(a.L);
+#pragma unroll 1
+            for (int sb = 0; sb < NSB; ++sb) {
+                uint2 Bq[NG], Cq[NG];
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    Bq[j] = sload8(Bc + (j * Ls + sb * SB));
+                    if constexpr (MODE == 0) Cq[j] = sload8(Cc + (j * Ls + sb * SB));
+                }
+                float4 lq[SB / 2];
+#pragma unroll
+                for (int k = 0; k < SB / 2; ++k) lq[k] = lwrow[sb * (SB / 2) + k];
+                float yv[SB];
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    const float l = (e & 1) ? lq[e / 2].z : lq[e / 2].x;
+                    const float w = (e & 1) ? lq[e / 2].w : lq[e / 2].y;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) {
+                        float bj[SB], cj[SB];
+                        unpack8<T>(Bq[j], bj);
+                        const float dA = exp2_hw(l * An[j]);
+                        h[j] = fmaf(dA, h[j], w * bj[e]);
+                        if constexpr (MODE == 0) {
+                            unpack8<T>(Cq[j], cj);
+                            acc = fmaf(cj[e], h[j], acc);
+                        }
+                    }
+                    yv[e] = acc;
+                }
+                if constexpr (MODE == 0) {
+                    if constexpr (SB == 4) {
+                        *reinterpret_cast<float4*>(yrow + sb * SB) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+                    } else {
+                        *reinterpret_cast<float2*>(yrow + sb * SB) = make_float2(yv[0], yv[1]);
+                    }
+                }
+            }
+        } else {
+            // Partial chunk, or rows not 16-byte aligned: token by token, only
+            // up to the segment end.
+            const float2* lw2 = reinterpret_cast<const float2*>(lwrow);
+            const int nt = full ? CH : int(t_end - t0);
+#pragma unroll 1
+            for (int t = 0; t < CH; ++t) {
+                float acc = 0.0f;
+                if (t < nt) {
+                    const float2 p = lw2[t];
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) {
+                        const int64_t o = int64_t(j) * a.L + t;
+                        const float dA = exp2_hw(p.x * An[j]);
+                        h[j] = fmaf(dA, h[j], p.y * to_f32(Bc[o]));
+                        if constexpr (MODE == 0) acc = fmaf(to_f32(Cc[o]), h[j], acc);
+                    }
+                }
+                if constexpr (MODE == 0) yrow[t] = acc;
+            }
+        }
+    };
+
+    // ---- per-token phase after the scan: sum partial readouts, D skip, gate, store ----
+    auto epilogue = [&](int c) {
+        const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
+        float yv[TS];
+#pragma unroll
+        for (int j = 0; j < TS; j += 4) {
+            float4 acc = *reinterpret_cast<const float4*>(&sm.yp[0][lane * S::kYB + (wv * TS + j) * 4]);
+#pragma unroll
+            for (int g = 1; g < G; ++g) {
+                const float4 q =
+                    *reinterpret_cast<const float4*>(&sm.yp[g][lane * S::kYB + (wv * TS + j) * 4]);
+                acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+            }
+            yv[j] = acc.x; yv[j + 1] = acc.y; yv[j + 2] = acc.z; yv[j + 3] = acc.w;
+        }
+#pragma unroll
+        for (int j = 0; j < TS; ++j) yv[j] = (yv[j] + dx[j]) * gz[j];
+        if (!row_ok) return;
+        T* Y = static_cast<T*>(a.y) + row * a.L;
+        if (VEC && ts + TS <= t_end) {
+#pragma unroll
+            for (int k = 0; k < SV; ++k)
+                *reinterpret_cast<uint4*>(Y + ts + k * V) = pack16<T>(yv + k * V);
+        } else {
+#pragma unroll
+            for (int j = 0; j < TS; ++j)
+                if (ts + j < t_end) Y[ts + j] = from_f32<T>(yv[j]);
+        }
+    };
+
+    if (nchunks > 0) {
+        load_slice(0);
+        prologue(0);
+        if (nchunks > 1) load_slice(1);
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            const bool full = t_begin + int64_t(c + 1) * CH <= t_end;
+            scan_chunk(c, full);
+            __syncthreads();
+            if constexpr (MODE == 0) epilogue(c);
+            if (c + 1 < nchunks) prologue(c + 1);
+            if (c + 2 < nchunks) load_slice(c + 2);
+            __syncthreads();
+        }
+    }
+
+    if constexpr (MODE == 0) {
+        if (a.last_state && row_ok && seg == a.segments - 1) {
+            float4* dst = reinterpret_cast<float4*>(a.last_state + (b * a.dim + d) * kN + n0);
+#pragma unroll
+            for (int k = 0; k < NG / 4; ++k)
+                dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+        }
+    } else {
+        const int64_t so = (int64_t(seg) * a.batch * a.dim + b * a.dim + d);
+        if (row_ok) {
+            float4* dst = reinterpret_cast<float4*>(a.seg_state + so * kN + n0);
+#pragma unroll
+            for (int k = 0; k < NG / 4; ++k)
+                dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+        }
+        sm.lsum[wv][lane] = lsum_acc;
+        __syncthreads();
+        if (wv == 0 && row_ok) {
+            double s = 0.0;
+#pragma unroll
+            for (int g = 0; g < G; ++g) s += sm.lsum[g][lane];
+            a.seg_lsum[so] = s;
+        }
+    }
+}
+
+// Carry pass: for each (row, n), compose the segments in order,
+//   H_{s+1} = 2^(A_n * lsum_s) H_s + state_s,  H_0 = 0,
+// and write the state entering every segment. 2^(A * sum of l) is the
+// product of the per-token decays of the segment.
+__global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
+                                                    const float* __restrict__ seg_state,
+                                                    const double* __restrict__ seg_lsum,
+                                                    float* __restrict__ carry, int64_t rows,
+                                                    int64_t dim, int32_t segments) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= rows * kN) return;
+    const int64_t r = i / kN;
+    const int n = int(i % kN);
+    const double An = A[(r % dim) * kN + n];
+    float H = 0.0f;
+    carry[i] = 0.0f;
+    constexpr int U = 8;
+    int s = 0;
+    for (; s + U <= segments - 1; s += U) {
+        float st[U];
+        double ls[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            st[u] = seg_state[int64_t(s + u) * rows * kN + i];
+            ls[u] = seg_lsum[int64_t(s + u) * rows + r];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            H = fmaf(exp2_hw(float(An * ls[u])), H, st[u]);
+            carry[int64_t(s + u + 1) * rows * kN + i] = H;
+        }
+    }
+    for (; s < segments - 1; ++s) {
+        H = fmaf(exp2_hw(float(An * seg_lsum[int64_t(s) * rows + r])), H,
+                 seg_state[int64_t(s) * rows * kN + i]);
+        carry[int64_t(s + 1) * rows * kN + i] = H;
+    }
+}
+
+template <typename T, int G, bool GATE, bool VEC, int MODE>
+hipError_t launch_one(const FwdKArgs& k, int64_t blocks, hipStream_t st) {
+    hipLaunchKernelGGL((fwd_kernel<T, G, GATE, VEC, MODE>), dim3(unsigned(blocks)),
+                       dim3(kWave * G), 0, st, k);
+    return hipGetLastError();
+}
+
+template <typename T, int G, int MODE>
+hipError_t dispatch_gv(const FwdKArgs& k, bool gate, bool vec, int64_t blocks, hipStream_t st) {
+    if (MODE == 1) gate = false;  // the state pass never reads z
+    if (gate) return vec ? launch_one<T, G, true, true, MODE>(k, blocks, st)
+                         : launch_one<T, G, true, false, MODE>(k, blocks, st);
+    return vec ? launch_one<T, G, false, true, MODE>(k, blocks, st)
+               : launch_one<T, G, false, false, MODE>(k, blocks, st);
+}
+
+template <typename T, int MODE>
+hipError_t dispatch(const FwdKArgs& k, int groups, bool gate, bool vec, int64_t blocks,
+                    hipStream_t st) {
+    switch (groups) {
+        case 1: return dispatch_gv<T, 1, MODE>(k, gate, vec, blocks, st);
+        case 2: return dispatch_gv<T, 2, MODE>(k, gate, vec, blocks, st);
+        case 4: return dispatch_gv<T, 4, MODE>(k, gate, vec, blocks, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int MODE>
+hipError_t dispatch_dtype(DType dt, const FwdKArgs& k, int groups, bool gate, bool vec,
+                          int64_t blocks, hipStream_t st) {
+    return dt == DType::BF16 ? dispatch<bf16_bits, MODE>(k, groups, gate, vec, blocks, st)
+                             : dispatch<float, MODE>(k, groups, gate, vec, blocks, st);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+}  // namespace
+
+// A fill kernel rather than a memset, so that the call stays capturable.
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+size_t fwd_workspace_bytes(const FwdShape& s, const FwdPlan& p) {
+    if (p.segments <= 1) return 0;
+    const size_t rows = size_t(s.batch) * size_t(s.dim);
+    const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
+    return 2 * align256(states) + align256(size_t(p.segments) * rows * sizeof(double));
+}
+
+hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, void* workspace,
+                      hipStream_t stream) {
+    FwdKArgs k{};
+    k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.B = t.B; k.C = t.C;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.y = t.y; k.last_state = t.last_state;
+    k.batch = s.batch; k.L = s.L; k.dim = s.dim;
+    k.seg_len = p.segments > 1 ? p.seg_len : s.L;
+    k.segments = p.segments;
+    k.row_blocks = int32_t((s.dim + kWave - 1) / kWave);
+    const bool gate = t.z != nullptr;
+    const int64_t per_seg = int64_t(k.row_blocks) * s.batch;
+
+    if (p.segments <= 1) {
+        k.h0 = nullptr;
+        return dispatch_dtype<0>(s.dtype, k, p.groups, gate, p.vec, per_seg, stream);
+    }
+    const size_t rows = size_t(s.batch) * size_t(s.dim);
+    const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* seg_state = reinterpret_cast<float*>(ws);
+    float* carry = reinterpret_cast<float*>(ws + align256(states));
+    double* seg_lsum = reinterpret_cast<double*>(ws + 2 * align256(states));
+
+    // 1) state pass over every segment but the last
+    FwdKArgs k1 = k;
+    k1.seg_state = seg_state;
+    k1.seg_lsum = seg_lsum;
+    k1.h0 = nullptr;
+    hipError_t e = dispatch_dtype<1>(s.dtype, k1, p.groups, false, p.vec,
+                                     per_seg * (p.segments - 1), stream);
+    if (e != hipSuccess) return e;
+    // 2) carries
+    const int64_t nthreads = int64_t(rows) * kN;
+    hipLaunchKernelGGL(carry_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream,
+                       t.A, seg_state, seg_lsum, carry, int64_t(rows), s.dim, p.segments);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 3) output pass from the carried-in states
+    k.h0 = carry;
+    return dispatch_dtype<0>(s.dtype, k, p.groups, gate, p.vec, per_seg * p.segments, stream);
+}
+
+}  // namespace selscan

@@ -1,0 +1,67 @@
+// Host-side launchers of the HIP kernels (internal to libselscan).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace selscan {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// Device pointers of one forward call. x/delta/z/y: [batch, dim, L];
+// B/C: [batch, N, L]; A: [dim, N]; D/dt_bias: [dim]; last_state: [batch, dim, N].
+struct FwdTensors {
+    const void* x;
+    const void* delta;
+    const void* z;  // null: no gate
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;        // null: 0
+    const float* dt_bias;  // null: 0
+    void* y;
+    float* last_state;  // null: not wanted
+};
+
+struct FwdShape {
+    int64_t batch, L, dim;
+    DType dtype;
+};
+
+// How the sequence axis is cut: `segments` runs of `seg_len` tokens each
+// (seg_len a multiple of the time tile when segments > 1); `groups` waves per
+// 64-row block, each holding N / groups states.
+struct FwdPlan {
+    int32_t segments;
+    int64_t seg_len;
+    int32_t groups;
+    bool vec;  // 16-byte vector access to rows is valid (L * elem_size % 16 == 0)
+};
+
+// Time tile (tokens per chunk) of the forward kernels.
+constexpr int kChunk = 32;
+
+// Bytes of workspace a plan needs (0 when segments == 1).
+size_t fwd_workspace_bytes(const FwdShape& s, const FwdPlan& p);
+
+// Enqueue the forward pass. `workspace` must hold fwd_workspace_bytes bytes
+// (ignored when segments == 1).
+hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, void* workspace,
+                      hipStream_t stream);
+
+struct StepTensors {
+    float* state;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;  // null: 0
+    const void* z;   // null: no gate
+    void* y;
+};
+
+hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType dtype,
+                       hipStream_t stream);
+
+}  // namespace selscan
