@@ -71,7 +71,6 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
              const selscan_dims_t* dims, int32_t segments, int32_t groups, void* stream) {
     int rc = check_common(dims, true);
     if (rc != SELSCAN_OK) return rc;
-    if (!x || !delta || !A || !B || !C || !y) return SELSCAN_ERR_NULL;
     if (segments < 0 || segments > 65536) return SELSCAN_ERR_CONFIG;
     if (groups != 0 && groups != 1 && groups != 2 && groups != 4) return SELSCAN_ERR_CONFIG;
     const int64_t L = dims->seqlen;
@@ -79,6 +78,9 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     if (L >= (int64_t(1) << 27)) return SELSCAN_ERR_DIMS;
     Sizes sz;
     if (!sizes(*dims, L, &sz)) return SELSCAN_ERR_DIMS;
+    // A tensor with no elements may come with a null pointer (torch gives one).
+    if ((sz.seq > 0 && (!x || !delta || !y)) || (sz.bc > 0 && (!B || !C)) || (sz.param > 0 && !A))
+        return SELSCAN_ERR_NULL;
     for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, (const void*)y,
                           (const void*)last_state})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
@@ -167,9 +169,12 @@ int selscan_step(float* state, const void* x, const void* delta, const float* A,
                  const selscan_dims_t* dims, void* stream) {
     int rc = check_common(dims, false);
     if (rc != SELSCAN_OK) return rc;
-    if (!state || !x || !delta || !A || !B || !C || !y) return SELSCAN_ERR_NULL;
     Sizes sz;
     if (!sizes(*dims, 1, &sz)) return SELSCAN_ERR_DIMS;
+    // A tensor with no elements may come with a null pointer (torch gives one).
+    if ((sz.rows > 0 && (!state || !x || !delta || !y)) || (dims->batch > 0 && (!B || !C)) ||
+        (sz.param > 0 && !A))
+        return SELSCAN_ERR_NULL;
     for (const void* p : {(const void*)state, x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)y})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;

@@ -14,13 +14,19 @@
 // Mapping (MI355X-first, not the pages' GPU design):
 // * One lane owns one (b, d) row and walks its tokens in order, so the scan is
 //   a plain register recurrence with no cross-lane combine at all. The 64 rows
-//   of a wave share b, which makes B_t and C_t wave-uniform: they are fetched
-//   with scalar loads into SGPRs and fed to the VALU as the scalar operand,
-//   costing no VGPRs, no LDS traffic and no vector-memory instructions.
+//   of a wave share b, which makes B_t and C_t wave-uniform: they are fed to
+//   the VALU as scalar (SGPR) operands, costing no VGPRs, no LDS traffic and
+//   no vector-memory instructions.
+// * A small pre-pass packs B and C into fp32, ordered so that the operands one
+//   wave needs for one sub-block of tokens (its N/G states x G tokens, for B
+//   and for C) are 2 x 16 contiguous floats: one s_load_dwordx16 each, loaded
+//   one sub-block ahead. This removes all scalar unpacking and address math
+//   from the inner loop, and turns B/C reads into one contiguous stream per
+//   batch entry (long rows no longer touch 2N distant pages per sub-block).
 // * The 16 states of a row are split across the G waves of a workgroup (N/G
 //   states each), so that B*d/64*G waves fill the 1024 SIMDs. Per token and
 //   state the inner loop is one multiply (l*A), one v_exp_f32, one multiply
-//   (w*B), and two FMAs (state, readout): the measured floor of the method.
+//   (w*B), and two FMAs (state, readout): the floor of the method.
 // * Per-token work that does not depend on n (softplus, w = delta*x, D*x,
 //   silu(z)) is computed once per row and token, split between the waves by
 //   token slices and shared through LDS. Partial readouts of the G waves are
@@ -70,26 +76,20 @@ __device__ __forceinline__ uint4 pack16(const float* f) {
     return v;
 }
 
-// An 8-byte load through the constant address space: with a wave-uniform
-// address the compiler must use a scalar (SMEM) load into SGPRs. Going
+// 16 floats through the constant address space: with a wave-uniform address
+// the compiler must use one scalar load (s_load_dwordx16) into SGPRs. Going
 // through an integer keeps address-space inference from turning it back into
 // a global-memory (vector) load.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-template <typename T>
-__device__ __forceinline__ uint2 sload8(const T* p) {
-    using CP = const __attribute__((address_space(4))) u32x2*;
-    const u32x2 v = *(CP)(reinterpret_cast<uintptr_t>(p));
-    return make_uint2(v.x, v.y);
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 sload64(const float* p) {
+    using CP = const __attribute__((address_space(4))) f32x16*;
+    return *(CP)(reinterpret_cast<uintptr_t>(p));
 }
 
-template <typename T>
-__device__ __forceinline__ void unpack8(const uint2& v, float* o) {
-    if constexpr (sizeof(T) == 4) {
-        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
-    } else {
-        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
-    }
-}
+// Packed operand layout (fp32): P[b][s][g][k][j][e] = (k ? C : B)[b, g*NG + j, s*G + e]
+// for sub-block s of G tokens, wave group g, state j < NG = 16/G, token e < G;
+// zero for tokens >= L. One (b, s, g) record is 2 x 16 floats.
+constexpr int kRec = 32;  // floats per (b, s, g) record
 
 // LDS of one workgroup: the per-token pairs (l, w) of the current chunk and
 // the partial readouts of the G waves. Row strides are odd multiples of 16
@@ -109,8 +109,7 @@ struct FwdKArgs {
     const void* delta;
     const void* z;
     const float* A;
-    const void* B;
-    const void* C;
+    const float* P;    // packed B/C
     const float* D;
     const float* dt_bias;
     void* y;
@@ -119,6 +118,7 @@ struct FwdKArgs {
     float* seg_state;  // [segments][rows][N] (state pass)
     double* seg_lsum;  // [segments][rows]    (state pass)
     int64_t batch, L, dim, seg_len;
+    int64_t psub;      // sub-blocks per batch entry in P
     int32_t segments, row_blocks;
 };
 
@@ -128,11 +128,11 @@ template <typename T, int G, bool GATE, bool VEC, int MODE>
 __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int CH = kChunk;
     constexpr int NG = kN / G;              // states per wave
+    constexpr int SB = G;                   // tokens per sub-block (NG * SB = 16)
+    constexpr int NSB = CH / SB;            // sub-blocks per chunk
     constexpr int TS = CH / G;              // tokens per wave in the per-token phases
     constexpr int V = Elem<T>::kPer16;      // elements per 16-byte vector
     constexpr int SV = TS / V;              // 16-byte vectors per row slice
-    constexpr int SB = 8 / int(sizeof(T));  // tokens per B/C sub-block (8 bytes per state)
-    constexpr int NSB = CH / SB;
     constexpr bool LOADZ = GATE && MODE == 0;
     static_assert(TS % V == 0 && SV >= 1, "tile shape");
     using S = Smem<G, CH, MODE>;
@@ -141,12 +141,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const T* __restrict__ X = static_cast<const T*>(a.x);
     const T* __restrict__ DL = static_cast<const T*>(a.delta);
     const T* __restrict__ Z = static_cast<const T*>(a.z);
-    const T* __restrict__ Bp = static_cast<const T*>(a.B);
-    const T* __restrict__ Cp = static_cast<const T*>(a.C);
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; saying so lets every address
-    // derived from it (B and C rows) live in SGPRs.
+    // derived from it (the packed B/C records) live in SGPRs.
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
 
@@ -211,7 +209,8 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 
     // ---- per-token phase before the scan ----
     // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this wave's
-    // registers until its epilogue of the same slice.
+    // registers until its epilogue of the same slice. Tokens past the segment
+    // end get l = w = 0, which makes their scan step the identity.
     float dx[TS], gz[TS];
     auto prologue = [&](int c) {
         const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
@@ -243,75 +242,63 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     };
 
     // ---- the scan over one chunk: this wave's NG states, all CH tokens ----
-    auto scan_chunk = [&](int c, bool full) {
-        const int64_t t0 = t_begin + int64_t(c) * CH;
-        const float4* lwrow = reinterpret_cast<const float4*>(&sm.lw[lane * S::kPairB]);
+    // Software pipeline, one sub-block ahead: wait for the previous loads,
+    // issue the next sub-block's B/C record (scalar) and (l, w) (LDS) loads,
+    // then compute from registers only. lgkmcnt covers both kinds of load, so
+    // the wait must come before the next loads are issued.
+    auto scan_chunk = [&](int c) {
+        const int64_t s0 = (t_begin + int64_t(c) * CH) / SB;          // first sub-block
+        const float* rec = a.P + ((b * a.psub + s0) * G + wv) * kRec;  // this wave's record
+        const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kPairB]);
         float* yrow = reinterpret_cast<float*>(&sm.yp[MODE == 0 ? wv : 0][lane * S::kYB]);
-        const T* Bc = Bp + (b * kN + n0) * a.L + t0;   // B/C at (b, n0, t0)
-        const T* Cc = Cp + (b * kN + n0) * a.L + t0;
-        if (full && VEC) {
-            // Per sub-block of SB tokens: one 8-byte scalar load per state for
-            // B (and C) into SGPRs, the (l, w) pairs from LDS, then the
-            // recurrence from registers. Offsets stay 32-bit (L < 2^31).
-            const int Ls = int(a.L);
-#pragma unroll 1
-            for (int sb = 0; sb < NSB; ++sb) {
-                uint2 Bq[NG], Cq[NG];
+        // Ping-pong operand buffers (two sub-blocks per loop trip), so that no
+        // register has to be copied at the loop back-edge.
+        f32x16 B0 = sload64(rec), C0, B1, C1;
+        if constexpr (MODE == 0) C0 = sload64(rec + 16);
+        float2 l0[SB], l1[SB];
+#pragma unroll
+        for (int e = 0; e < SB; ++e) l0[e] = lw2[e];
+        auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float2* lc, f32x16& Bn,
+                        f32x16& Cn, float2* ln) {
+            const int sbn = sb + 1 < NSB ? sb + 1 : sb;  // stays inside the chunk
+            __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): current operands ready
+            __builtin_amdgcn_sched_barrier(0);
+            const float* nrec = rec + int64_t(sbn) * (G * kRec);
+            Bn = sload64(nrec);
+            if constexpr (MODE == 0) Cn = sload64(nrec + 16);
+#pragma unroll
+            for (int e = 0; e < SB; ++e) ln[e] = lw2[sbn * SB + e];
+            __builtin_amdgcn_sched_barrier(0);
+            float yv[SB];
+#pragma unroll
+            for (int e = 0; e < SB; ++e) {
+                float acc = 0.0f;
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
-                    Bq[j] = sload8(Bc + (j * Ls + sb * SB));
-                    if constexpr (MODE == 0) Cq[j] = sload8(Cc + (j * Ls + sb * SB));
+                    const float dA = exp2_hw(lc[e].x * An[j]);
+                    h[j] = fmaf(dA, h[j], lc[e].y * Bc[j * SB + e]);
+                    if constexpr (MODE == 0) acc = fmaf(Cc[j * SB + e], h[j], acc);
                 }
-                float4 lq[SB / 2];
+                yv[e] = acc;
+            }
+            if constexpr (MODE == 0) {
+                if constexpr (SB >= 4) {
 #pragma unroll
-                for (int k = 0; k < SB / 2; ++k) lq[k] = lwrow[sb * (SB / 2) + k];
-                float yv[SB];
-#pragma unroll
-                for (int e = 0; e < SB; ++e) {
-                    const float l = (e & 1) ? lq[e / 2].z : lq[e / 2].x;
-                    const float w = (e & 1) ? lq[e / 2].w : lq[e / 2].y;
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < NG; ++j) {
-                        float bj[SB], cj[SB];
-                        unpack8<T>(Bq[j], bj);
-                        const float dA = exp2_hw(l * An[j]);
-                        h[j] = fmaf(dA, h[j], w * bj[e]);
-                        if constexpr (MODE == 0) {
-                            unpack8<T>(Cq[j], cj);
-                            acc = fmaf(cj[e], h[j], acc);
-                        }
-                    }
-                    yv[e] = acc;
-                }
-                if constexpr (MODE == 0) {
-                    if constexpr (SB == 4) {
-                        *reinterpret_cast<float4*>(yrow + sb * SB) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-                    } else {
-                        *reinterpret_cast<float2*>(yrow + sb * SB) = make_float2(yv[0], yv[1]);
-                    }
+                    for (int k = 0; k < SB / 4; ++k)
+                        *reinterpret_cast<float4*>(yrow + sb * SB + 4 * k) =
+                            make_float4(yv[4 * k], yv[4 * k + 1], yv[4 * k + 2], yv[4 * k + 3]);
+                } else if constexpr (SB == 2) {
+                    *reinterpret_cast<float2*>(yrow + sb * SB) = make_float2(yv[0], yv[1]);
+                } else {
+                    yrow[sb] = yv[0];
                 }
             }
-        } else {
-            // Partial chunk, or rows not 16-byte aligned: token by token, only
-            // up to the segment end.
-            const float2* lw2 = reinterpret_cast<const float2*>(lwrow);
-            const int nt = full ? CH : int(t_end - t0);
+        };
+        static_assert(NSB % 2 == 0, "sub-blocks per chunk must be even");
 #pragma unroll 1
-            for (int t = 0; t < CH; ++t) {
-                float acc = 0.0f;
-                if (t < nt) {
-                    const float2 p = lw2[t];
-#pragma unroll
-                    for (int j = 0; j < NG; ++j) {
-                        const int64_t o = int64_t(j) * a.L + t;
-                        const float dA = exp2_hw(p.x * An[j]);
-                        h[j] = fmaf(dA, h[j], p.y * to_f32(Bc[o]));
-                        if constexpr (MODE == 0) acc = fmaf(to_f32(Cc[o]), h[j], acc);
-                    }
-                }
-                if constexpr (MODE == 0) yrow[t] = acc;
-            }
+        for (int sb = 0; sb < NSB; sb += 2) {
+            half(sb, B0, C0, l0, B1, C1, l1);
+            half(sb + 1, B1, C1, l1, B0, C0, l0);
         }
     };
 
@@ -351,8 +338,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         if (nchunks > 1) load_slice(1);
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
-            const bool full = t_begin + int64_t(c + 1) * CH <= t_end;
-            scan_chunk(c, full);
+            scan_chunk(c);
             __syncthreads();
             if constexpr (MODE == 0) epilogue(c);
             if (c + 1 < nchunks) prologue(c + 1);
@@ -384,6 +370,42 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             for (int g = 0; g < G; ++g) s += sm.lsum[g][lane];
             a.seg_lsum[so] = s;
         }
+    }
+}
+
+// Pack B and C ([batch, 16, L] of T) into the fp32 record layout above, for
+// Lp >= L tokens (multiple of the chunk), zero past L. One thread takes four
+// consecutive tokens of one (b, B-or-C, n) row: coalesced reads, and with
+// G = 4 one 16-byte write.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, const T* __restrict__ C,
+                                                      float* __restrict__ P, int64_t batch, int64_t L,
+                                                      int64_t Lp) {
+    constexpr int NG = kN / G;
+    const int64_t q4 = Lp / 4;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= batch * 2 * kN * q4) return;
+    const int64_t q = i % q4;
+    int64_t r = i / q4;
+    const int n = int(r % kN);
+    r /= kN;
+    const int k = int(r % 2);
+    const int64_t b = r / 2;
+    const T* src = (k ? C : B) + (b * kN + n) * L;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t t = q * 4 + e;
+        v[e] = t < L ? to_f32(src[t]) : 0.0f;
+    }
+    const int g = n / NG, j = n % NG;
+    const int64_t psub = Lp / G;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t t = q * 4 + e;
+        const int64_t s = t / G;
+        const int eo = int(t % G);
+        P[(((b * psub + s) * G + g) * 2 + k) * 16 + j * G + eo] = v[e];
     }
 }
 
@@ -460,7 +482,26 @@ hipError_t dispatch_dtype(DType dt, const FwdKArgs& k, int groups, bool gate, bo
                              : dispatch<float, MODE>(k, groups, gate, vec, blocks, st);
 }
 
+template <typename T>
+hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, int64_t L,
+                       int64_t Lp, int groups, hipStream_t st) {
+    const int64_t n = batch * 2 * kN * (Lp / 4);
+    const dim3 grid(unsigned((n + 255) / 256)), block(256);
+    const T* b = static_cast<const T*>(B);
+    const T* c = static_cast<const T*>(C);
+    switch (groups) {
+        case 1: hipLaunchKernelGGL((pack_bc_kernel<T, 1>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
+        case 2: hipLaunchKernelGGL((pack_bc_kernel<T, 2>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
+        case 4: hipLaunchKernelGGL((pack_bc_kernel<T, 4>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Padded token count of the packed B/C: whole chunks.
+int64_t padded_len(int64_t L) { return (L + kChunk - 1) / kChunk * kChunk; }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -477,19 +518,31 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 }
 
 size_t fwd_workspace_bytes(const FwdShape& s, const FwdPlan& p) {
-    if (p.segments <= 1) return 0;
+    const size_t packed = size_t(s.batch) * size_t(padded_len(s.L)) * 2 * kN * sizeof(float);
+    if (p.segments <= 1) return align256(packed);
     const size_t rows = size_t(s.batch) * size_t(s.dim);
     const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
-    return 2 * align256(states) + align256(size_t(p.segments) * rows * sizeof(double));
+    return align256(packed) + 2 * align256(states) +
+           align256(size_t(p.segments) * rows * sizeof(double));
 }
 
 hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, void* workspace,
                       hipStream_t stream) {
+    const int64_t Lp = padded_len(s.L);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* P = reinterpret_cast<float*>(ws);
+    const size_t packed = size_t(s.batch) * size_t(Lp) * 2 * kN * sizeof(float);
+    hipError_t e = s.dtype == DType::BF16
+                       ? launch_pack<bf16_bits>(t.B, t.C, P, s.batch, s.L, Lp, p.groups, stream)
+                       : launch_pack<float>(t.B, t.C, P, s.batch, s.L, Lp, p.groups, stream);
+    if (e != hipSuccess) return e;
+
     FwdKArgs k{};
-    k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.B = t.B; k.C = t.C;
+    k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = P;
     k.D = t.D; k.dt_bias = t.dt_bias; k.y = t.y; k.last_state = t.last_state;
     k.batch = s.batch; k.L = s.L; k.dim = s.dim;
     k.seg_len = p.segments > 1 ? p.seg_len : s.L;
+    k.psub = Lp / p.groups;
     k.segments = p.segments;
     k.row_blocks = int32_t((s.dim + kWave - 1) / kWave);
     const bool gate = t.z != nullptr;
@@ -501,18 +554,16 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     }
     const size_t rows = size_t(s.batch) * size_t(s.dim);
     const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* seg_state = reinterpret_cast<float*>(ws);
-    float* carry = reinterpret_cast<float*>(ws + align256(states));
-    double* seg_lsum = reinterpret_cast<double*>(ws + 2 * align256(states));
+    float* seg_state = reinterpret_cast<float*>(ws + align256(packed));
+    float* carry = reinterpret_cast<float*>(ws + align256(packed) + align256(states));
+    double* seg_lsum = reinterpret_cast<double*>(ws + align256(packed) + 2 * align256(states));
 
     // 1) state pass over every segment but the last
     FwdKArgs k1 = k;
     k1.seg_state = seg_state;
     k1.seg_lsum = seg_lsum;
     k1.h0 = nullptr;
-    hipError_t e = dispatch_dtype<1>(s.dtype, k1, p.groups, false, p.vec,
-                                     per_seg * (p.segments - 1), stream);
+    e = dispatch_dtype<1>(s.dtype, k1, p.groups, false, p.vec, per_seg * (p.segments - 1), stream);
     if (e != hipSuccess) return e;
     // 2) carries
     const int64_t nthreads = int64_t(rows) * kN;
