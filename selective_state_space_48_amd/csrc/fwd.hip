@@ -164,8 +164,15 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const int nchunks = int((t_end - t_begin + CH - 1) / CH);
     const int n0 = wv * NG;
 
-    const float bias = (a.dt_bias && row_ok) ? a.dt_bias[d] : 0.0f;
-    const float Dd = (a.D && row_ok) ? a.D[d] : 0.0f;
+    // The per-token phases use their own mapping, chosen for memory access:
+    // thread (pr, pq) takes row pr of the block and token slice pq, so the G
+    // threads of a row are adjacent lanes reading one contiguous row segment.
+    const int pr = tid / G, pq = tid % G;
+    const int64_t dp = d0 + pr;
+    const bool prow_ok = dp < a.dim;
+    const int64_t prow = b * a.dim + (prow_ok ? dp : d0);  // clamped for safe reads
+    const float bias = (a.dt_bias && prow_ok) ? a.dt_bias[dp] : 0.0f;
+    const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
     float An[NG], h[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -175,22 +182,27 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     }
     double lsum_acc = 0.0;
 
-    // ---- this wave's token slice [wv*TS, wv*TS+TS) of a chunk, straight from HBM ----
-    // Each lane reads its own row; the G waves read adjacent slices of the same
-    // rows, so every fetched cache line is used whole.
-    uint4 px[SV], pd[SV], pz[LOADZ ? SV : 1];
-    auto load_slice = [&](int c) {
-        const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
-        const int64_t off = row * a.L + ts;
+    // ---- thread (pr, pq)'s token slice [pq*TS, pq*TS+TS) of a chunk, straight from HBM ----
+    // The G threads of a row read adjacent slices, so a wave's load covers
+    // 64/G rows with CH contiguous tokens each.
+    // Two register sets, alternating by chunk parity: the loads of chunk c+2
+    // are in flight while chunks c and c+1 are processed.
+    struct Slice {
+        uint4 x[SV], d[SV], z[LOADZ ? SV : 1];
+    };
+    Slice sl0, sl1;
+    auto load_slice = [&](int c, Slice& sl) {
+        const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
+        const int64_t off = prow * a.L + ts;
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             const int64_t tk = ts + k * V;
             if constexpr (VEC) {
                 const bool ok = tk < t_end;  // whole vector in or out (L, t_end multiples of V)
-                px[k] = ok ? *reinterpret_cast<const uint4*>(X + off + k * V) : make_uint4(0, 0, 0, 0);
-                pd[k] = ok ? *reinterpret_cast<const uint4*>(DL + off + k * V) : make_uint4(0, 0, 0, 0);
+                sl.x[k] = ok ? *reinterpret_cast<const uint4*>(X + off + k * V) : make_uint4(0, 0, 0, 0);
+                sl.d[k] = ok ? *reinterpret_cast<const uint4*>(DL + off + k * V) : make_uint4(0, 0, 0, 0);
                 if constexpr (LOADZ)
-                    pz[k] = ok ? *reinterpret_cast<const uint4*>(Z + off + k * V) : make_uint4(0, 0, 0, 0);
+                    sl.z[k] = ok ? *reinterpret_cast<const uint4*>(Z + off + k * V) : make_uint4(0, 0, 0, 0);
             } else {
                 float fx[V], fd[V], fz[V];
 #pragma unroll
@@ -200,44 +212,55 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                     fd[e] = ok ? to_f32(DL[off + k * V + e]) : 0.0f;
                     fz[e] = (LOADZ && ok) ? to_f32(Z[off + k * V + e]) : 0.0f;
                 }
-                px[k] = pack16<T>(fx);
-                pd[k] = pack16<T>(fd);
-                if constexpr (LOADZ) pz[k] = pack16<T>(fz);
+                sl.x[k] = pack16<T>(fx);
+                sl.d[k] = pack16<T>(fd);
+                if constexpr (LOADZ) sl.z[k] = pack16<T>(fz);
             }
         }
     };
 
     // ---- per-token phase before the scan ----
-    // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this wave's
+    // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this thread's
     // registers until its epilogue of the same slice. Tokens past the segment
-    // end get l = w = 0, which makes their scan step the identity.
-    float dx[TS], gz[TS];
-    auto prologue = [&](int c) {
-        const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
+    // end get l = w = 0, which makes their scan step the identity. The body is
+    // straight-line (the tail is masked with a uniform 0/1 factor, not
+    // branched around), so the TS independent softplus chains interleave.
+    float dx[TS], gz[TS];      // current chunk (for its epilogue)
+    float dxn[TS], gzn[TS];    // next chunk (written by its prologue)
+    auto prologue = [&](int c, const Slice& sl) {
+        const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
+        const int nvalid = int(min(int64_t(TS), max(int64_t(0), t_end - ts)));
         float xs[TS], ds[TS], zs[TS];
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
-            unpack16<T>(px[k], xs + k * V);
-            unpack16<T>(pd[k], ds + k * V);
-            if constexpr (LOADZ) unpack16<T>(pz[k], zs + k * V);
+            unpack16<T>(sl.x[k], xs + k * V);
+            unpack16<T>(sl.d[k], ds + k * V);
+            if constexpr (LOADZ) unpack16<T>(sl.z[k], zs + k * V);
         }
-        float4* lwrow = reinterpret_cast<float4*>(&sm.lw[lane * S::kPairB]) + wv * TS / 2;
+        float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]) + pq * TS / 2;
 #pragma unroll
         for (int j = 0; j < TS; j += 2) {
             float l[2], w[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const bool ok = ts + j + u < t_end;
-                l[u] = ok ? softplus_log2(ds[j + u] + bias) : 0.0f;
-                w[u] = ok ? l[u] * kLn2 * xs[j + u] : 0.0f;
+                const float keep = (j + u < nvalid) ? 1.0f : 0.0f;  // padded inputs are 0
+                l[u] = softplus_log2(ds[j + u] + bias) * keep;
+                w[u] = l[u] * kLn2 * xs[j + u];
                 if constexpr (MODE == 1) lsum_acc += double(l[u]);
                 if constexpr (MODE == 0) {
-                    dx[j + u] = Dd * xs[j + u];
-                    gz[j + u] = 1.0f;
-                    if constexpr (LOADZ) gz[j + u] = silu(zs[j + u]);
+                    dxn[j + u] = Dd * xs[j + u];
+                    gzn[j + u] = 1.0f;
+                    if constexpr (LOADZ) gzn[j + u] = silu(zs[j + u]);
                 }
             }
             lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
+        }
+    };
+    auto take_next = [&]() {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) {
+            dx[j] = dxn[j];
+            gz[j] = gzn[j];
         }
     };
 
@@ -304,23 +327,23 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 
     // ---- per-token phase after the scan: sum partial readouts, D skip, gate, store ----
     auto epilogue = [&](int c) {
-        const int64_t ts = t_begin + int64_t(c) * CH + wv * TS;
+        const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
         float yv[TS];
 #pragma unroll
         for (int j = 0; j < TS; j += 4) {
-            float4 acc = *reinterpret_cast<const float4*>(&sm.yp[0][lane * S::kYB + (wv * TS + j) * 4]);
+            float4 acc = *reinterpret_cast<const float4*>(&sm.yp[0][pr * S::kYB + (pq * TS + j) * 4]);
 #pragma unroll
             for (int g = 1; g < G; ++g) {
                 const float4 q =
-                    *reinterpret_cast<const float4*>(&sm.yp[g][lane * S::kYB + (wv * TS + j) * 4]);
+                    *reinterpret_cast<const float4*>(&sm.yp[g][pr * S::kYB + (pq * TS + j) * 4]);
                 acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
             }
             yv[j] = acc.x; yv[j + 1] = acc.y; yv[j + 2] = acc.z; yv[j + 3] = acc.w;
         }
 #pragma unroll
         for (int j = 0; j < TS; ++j) yv[j] = (yv[j] + dx[j]) * gz[j];
-        if (!row_ok) return;
-        T* Y = static_cast<T*>(a.y) + row * a.L;
+        if (!prow_ok) return;
+        T* Y = static_cast<T*>(a.y) + prow * a.L;
         if (VEC && ts + TS <= t_end) {
 #pragma unroll
             for (int k = 0; k < SV; ++k)
@@ -332,18 +355,32 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         }
     };
 
-    if (nchunks > 0) {
-        load_slice(0);
-        prologue(0);
-        if (nchunks > 1) load_slice(1);
+    // Per chunk: scan | barrier | prologue(c+1), loads of c+3, epilogue(c) | barrier.
+    // Loads run two chunks ahead, in the register set chunk c+1 just freed.
+    // The epilogue's y stores come last, so no wait for loads (vmcnt, which on
+    // this chip also counts stores) ever waits for freshly issued stores.
+    auto step = [&](int c, Slice& next, Slice& other) {
+        // next holds chunk c+1's inputs; other holds chunk c+2's (in flight)
+        scan_chunk(c);
         __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            scan_chunk(c);
-            __syncthreads();
-            if constexpr (MODE == 0) epilogue(c);
-            if (c + 1 < nchunks) prologue(c + 1);
-            if (c + 2 < nchunks) load_slice(c + 2);
-            __syncthreads();
+        if (c + 1 < nchunks) prologue(c + 1, next);
+        if (c + 3 < nchunks) load_slice(c + 3, next);
+        if constexpr (MODE == 0) epilogue(c);
+        take_next();
+        __syncthreads();
+        (void)other;
+    };
+    if (nchunks > 0) {
+        load_slice(0, sl0);
+        if (nchunks > 1) load_slice(1, sl1);
+        prologue(0, sl0);
+        take_next();
+        if (nchunks > 2) load_slice(2, sl0);
+        __syncthreads();
+        // chunk c+1's inputs are in sl1 for even c, sl0 for odd c
+        for (int c = 0; c < nchunks; c += 2) {
+            step(c, sl1, sl0);
+            if (c + 1 < nchunks) step(c + 1, sl0, sl1);
         }
     }
 
@@ -362,7 +399,9 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             for (int k = 0; k < NG / 4; ++k)
                 dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
         }
-        sm.lsum[wv][lane] = lsum_acc;
+        // Step-size sums were accumulated per (row pr, slice pq); add the G
+        // slices of each row in a fixed order.
+        sm.lsum[pq][pr] = lsum_acc;
         __syncthreads();
         if (wv == 0 && row_ok) {
             double s = 0.0;
