@@ -25,7 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # B/s, MI355X published HBM3E bandwidth
-FP32_VEC_PEAK = 157.3e12   # FLOP/s, MI355X published fp32 vector rate
+# VALU issue-slot peak: 256 CUs x 64 lanes (4 SIMDs x 16) x 2.4 GHz, one
+# non-packed fp32 VALU instruction per lane-slot. (The published fp32 vector
+# rate, 157.3 TFLOP/s, is this times 4: a packed FMA is 4 flops per slot.)
+SLOT_PEAK = 256 * 64 * 2.4e9
+TRANS_SLOTS = 2            # v_exp/v_log/v_rcp occupy a wave twice as long as an FMA (measured)
 
 
 def log(*a):
@@ -53,21 +57,23 @@ def step_bytes(w):
         + w.dim * w.dstate * 4 + w.dim * 4
 
 
-def method_flops(w):
-    """fp32 operations the method needs per forward call, counting an FMA as 2
-    and each transcendental (exp, log, reciprocal) as 1:
-    per (token, state): l*A, exp, w*B, state FMA, readout FMA  -> 7;
-    per token: bias add, softplus (exp, log, add), delta*x, D*x FMA,
-    silu (exp, add, reciprocal, multiply), gate multiply      -> 12."""
+def method_slots(w):
+    """VALU issue slots (lane-instructions, a transcendental = TRANS_SLOTS) the
+    method needs per forward call, at its minimum:
+    per (token, state): l*A, w*B, state FMA, readout FMA + one exp;
+    per token: softplus (add bias, exp, add, log), delta*x, D*x FMA,
+    silu (exp, add, reciprocal, multiply), gate multiply."""
     E = w.batch * w.seqlen * w.dim
-    return E * (7 * w.dstate + 12)
+    per_tn = 4 + TRANS_SLOTS
+    per_tok = 6 + 4 * TRANS_SLOTS
+    return E * (per_tn * w.dstate + per_tok)
 
 
-def device_inputs(w, torch, dev):
+def device_inputs(w, torch, dev, inp=None):
     from selective_state_space_48_amd import workloads as W
 
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    inp = W.fwd_inputs(w)
+    inp = W.fwd_inputs(w) if inp is None else inp
 
     def t(a, dt=torch.float32):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
@@ -76,10 +82,10 @@ def device_inputs(w, torch, dev):
                 B=t(inp["B"], td), C=t(inp["C"], td), D=t(inp["D"]), dt_bias=t(inp["dt_bias"]))
 
 
-def time_fwd(w, steps, warmup, torch, dev):
+def time_fwd(w, steps, warmup, torch, dev, inp=None):
     from selective_state_space_48_amd import selscan
 
-    d = device_inputs(w, torch, dev)
+    d = device_inputs(w, torch, dev, inp)
     y = torch.empty_like(d["x"])
     hs = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
 
@@ -137,29 +143,32 @@ def time_decode(w, steps, warmup, torch, dev):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(w, target_s=8.0):
-    """The oracle on a bounded sample of the workload: the first rows of batch
-    entry 0, full sequence length, all host threads."""
+def cpu_baseline(w, inp):
+    """The oracle as it stands, on the whole workload (every row, every token),
+    all host threads; about 1e9 (token, state) updates in float64."""
     import oracle
-    from selective_state_space_48_amd import workloads as W
 
     nt = oracle.default_threads()
-    inp = W.fwd_inputs(w, batches=[0])
-    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"])
-    kw = dict(D=inp["D"], z=inp["z"], dt_bias=inp["dt_bias"])
-    rows = nt * 2
     t0 = time.perf_counter()
-    oracle.fwd(*args, rows=np.arange(rows), nthreads=nt, **kw)
+    oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+               dt_bias=inp["dt_bias"], nthreads=nt)
     dt = time.perf_counter() - t0
-    rows = int(min(w.dim, max(rows, rows * target_s / max(dt, 1e-3))))
-    rows = max(nt, rows // nt * nt)
-    t0 = time.perf_counter()
-    oracle.fwd(*args, rows=np.arange(rows), nthreads=nt, **kw)
-    dt = time.perf_counter() - t0
-    elems = rows * w.seqlen
-    return {"value": round(elems / dt / 1e9, 6), "unit": "Gelem/s", "cores": nt, "kind": "oracle",
-            "sample": f"{rows} rows (batch 0, channels 0..{rows - 1}) x {w.seqlen} tokens of "
-                      f"{w.name}, fp64, {dt:.1f} s wall"}
+    return {"value": round(w.elements / dt / 1e9, 6), "unit": "Gelem/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"the whole {w.name} workload ({w.rows} rows x {w.seqlen} tokens), fp64, "
+                      f"{dt:.2f} s wall on {nt} threads"}
+
+
+def copy_calibration(torch, dev, gib=1, reps=5):
+    """A plain device copy of known size (torch's copy kernel), run under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to turn those counters into bytes."""
+    n = (gib << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    return {"copy_bytes_each_way": n * 4, "reps": reps}
 
 
 def main():
@@ -169,8 +178,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m"], default=None,
-                    help="run just one workload (for profiling)")
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "copy"], default=None,
+                    help="run just one workload (for profiling); copy = counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the selective scan here "
@@ -184,18 +193,23 @@ def main():
     dev = torch.device("cuda:0")
     out = {}
     w = W.get(W.HEADLINE)
+    if args.only == "copy":
+        print(json.dumps(copy_calibration(torch, dev)), flush=True)
+        return
 
+    inp = None
     if args.only in (None, "fwd"):
+        inp = W.fwd_inputs(w)
         log(f"[bench] {w.name}: {args.warmup} warmup + {args.steps} timed forward calls")
-        ms, wall = time_fwd(w, args.steps, args.warmup, torch, dev)
+        ms, wall = time_fwd(w, args.steps, args.warmup, torch, dev, inp)
         E = w.elements
         gelem = E / (ms * 1e-3) / 1e9
         bytes_ = algorithmic_bytes(w)
-        flops = method_flops(w)
+        slots = method_slots(w)
         hbm = bytes_ / (ms * 1e-3)
-        alu = flops / (ms * 1e-3)
+        alu = slots / (ms * 1e-3)
         log(f"[bench] {w.name}: {ms * 1e3:.1f} us/call, {gelem:.1f} Gelem/s, "
-            f"{hbm / 1e12:.2f} TB/s algorithmic, {alu / 1e12:.1f} TFLOP/s method")
+            f"{hbm / 1e12:.2f} TB/s algorithmic, {alu / 1e12:.1f} T VALU-slot/s method")
         out.update({
             "metric": "selective-scan fwd Gelem/s (B*L*d_inner), Mamba-1.4B-shaped layer",
             "value": round(gelem, 3),
@@ -215,10 +229,10 @@ def main():
             "hbm": {"achieved": round(hbm / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                     "frac": round(hbm / HBM_PEAK, 4), "bytes_per_call": bytes_},
             "roofline": {"bound": "alu", "achieved": round(alu / 1e12, 3),
-                         "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": round(alu / FP32_VEC_PEAK, 4), "traffic": None,
-                         "kernel": "fwd_kernel<bf16,G=4,gate,vec,output pass>",
-                         "flops_per_call": flops},
+                         "peak": round(SLOT_PEAK / 1e12, 3), "unit": "T VALU-slot/s",
+                         "frac": round(alu / SLOT_PEAK, 4), "traffic": None,
+                         "kernel": "fwd_kernel<bf16,G=4,gate,vec,output pass> (+ B/C pack pre-pass)",
+                         "slots_per_call": slots},
             "wall_s_timed": round(wall, 4),
         })
 
@@ -246,7 +260,7 @@ def main():
 
     if args.only in (None, "fwd") and not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, inp)
         log(f"[bench] cpu baseline: {out['cpu_baseline']}")
 
     print(json.dumps(out), flush=True)

@@ -109,11 +109,12 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     const int64_t waves = row_blocks * dims->batch * plan.groups;
     int64_t S = segments;
     if (S == 0) {
-        // Fill the machine: about two waves per SIMD (4 SIMDs x 256 CUs). Only
-        // worth a second pass when the sequence is long.
-        const int64_t target = 2048;
+        // Segmenting adds a state pass (about 0.7 of an output pass) over all
+        // but the last segment, so it only pays when the one-pass grid leaves
+        // SIMDs without a wave (1024 SIMDs). Then aim at ~3 waves per SIMD.
         S = 1;
-        if (waves < target && L >= 16 * kChunk) {
+        if (waves < 1024 && L >= 16 * kChunk) {
+            const int64_t target = 3072;
             S = (target + waves - 1) / waves;
             const int64_t max_by_len = L / (8 * kChunk);
             if (S > max_by_len) S = max_by_len;

@@ -76,6 +76,18 @@ __device__ __forceinline__ uint4 pack16(const float* f) {
     return v;
 }
 
+// Streaming 16-byte global accesses: x, delta and z are read exactly once and
+// y is written exactly once, so they are marked non-temporal (no reuse).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg_stream(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stg_stream(void* p, const uint4& v) {
+    u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 // 16 floats through the constant address space: with a wave-uniform address
 // the compiler must use one scalar load (s_load_dwordx16) into SGPRs. Going
 // through an integer keeps address-space inference from turning it back into
@@ -199,10 +211,9 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             const int64_t tk = ts + k * V;
             if constexpr (VEC) {
                 const bool ok = tk < t_end;  // whole vector in or out (L, t_end multiples of V)
-                sl.x[k] = ok ? *reinterpret_cast<const uint4*>(X + off + k * V) : make_uint4(0, 0, 0, 0);
-                sl.d[k] = ok ? *reinterpret_cast<const uint4*>(DL + off + k * V) : make_uint4(0, 0, 0, 0);
-                if constexpr (LOADZ)
-                    sl.z[k] = ok ? *reinterpret_cast<const uint4*>(Z + off + k * V) : make_uint4(0, 0, 0, 0);
+                sl.x[k] = ok ? ldg_stream(X + off + k * V) : make_uint4(0, 0, 0, 0);
+                sl.d[k] = ok ? ldg_stream(DL + off + k * V) : make_uint4(0, 0, 0, 0);
+                if constexpr (LOADZ) sl.z[k] = ok ? ldg_stream(Z + off + k * V) : make_uint4(0, 0, 0, 0);
             } else {
                 float fx[V], fd[V], fz[V];
 #pragma unroll
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         if (VEC && ts + TS <= t_end) {
 #pragma unroll
             for (int k = 0; k < SV; ++k)
-                *reinterpret_cast<uint4*>(Y + ts + k * V) = pack16<T>(yv + k * V);
+                stg_stream(Y + ts + k * V, pack16<T>(yv + k * V));
         } else {
 #pragma unroll
             for (int j = 0; j < TS; ++j)
@@ -413,39 +424,34 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 }
 
 // Pack B and C ([batch, 16, L] of T) into the fp32 record layout above, for
-// Lp >= L tokens (multiple of the chunk), zero past L. One thread takes four
-// consecutive tokens of one (b, B-or-C, n) row: coalesced reads, and with
-// G = 4 one 16-byte write.
+// Lp >= L tokens (a multiple of the chunk), zero past L. One thread writes one
+// 16-float half-record (B or C of one (b, s, g)), so a wave writes 4 KiB
+// contiguously; its reads are G consecutive tokens of NG rows, and the 8
+// sub-blocks a wave covers make them 8*G contiguous tokens per row.
 template <typename T, int G>
 __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, const T* __restrict__ C,
                                                       float* __restrict__ P, int64_t batch, int64_t L,
                                                       int64_t Lp) {
     constexpr int NG = kN / G;
-    const int64_t q4 = Lp / 4;
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= batch * 2 * kN * q4) return;
-    const int64_t q = i % q4;
-    int64_t r = i / q4;
-    const int n = int(r % kN);
-    r /= kN;
-    const int k = int(r % 2);
-    const int64_t b = r / 2;
-    const T* src = (k ? C : B) + (b * kN + n) * L;
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t t = q * 4 + e;
-        v[e] = t < L ? to_f32(src[t]) : 0.0f;
-    }
-    const int g = n / NG, j = n % NG;
     const int64_t psub = Lp / G;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;  // half-record index
+    if (i >= batch * psub * G * 2) return;
+    const int k = int(i % 2);
+    const int g = int((i / 2) % G);
+    const int64_t s = (i / (2 * G)) % psub;
+    const int64_t b = i / (2 * G * psub);
+    const T* src = (k ? C : B) + (b * kN + g * NG) * L;
+    float v[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t t = q * 4 + e;
-        const int64_t s = t / G;
-        const int eo = int(t % G);
-        P[(((b * psub + s) * G + g) * 2 + k) * 16 + j * G + eo] = v[e];
-    }
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+            const int64_t t = s * G + e;
+            v[j * G + e] = t < L ? to_f32(src[j * L + t]) : 0.0f;
+        }
+    float4* dst = reinterpret_cast<float4*>(P + i * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
 // Carry pass: for each (row, n), compose the segments in order,
@@ -524,7 +530,7 @@ hipError_t dispatch_dtype(DType dt, const FwdKArgs& k, int groups, bool gate, bo
 template <typename T>
 hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, int64_t L,
                        int64_t Lp, int groups, hipStream_t st) {
-    const int64_t n = batch * 2 * kN * (Lp / 4);
+    const int64_t n = batch * Lp * 2;  // half-records: batch * (Lp / G) * G * 2
     const dim3 grid(unsigned((n + 255) / 256)), block(256);
     const T* b = static_cast<const T*>(B);
     const T* c = static_cast<const T*>(C);

@@ -12,14 +12,18 @@
 // share a row, each owning four states as one 16-byte vector, so every wave
 // streams 1 KiB of contiguous state in and out. The per-row scalars (softplus,
 // silu) are recomputed by the four lanes rather than exchanged; the readout is
-// reduced across the quad with two cross-lane adds.
+// reduced across the quad with two cross-lane adds. Each thread takes several
+// quads so that many loads are in flight per wave.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace selscan {
 namespace {
 
-template <typename T, bool GATE>
+// Each thread owns R quads (a quad = 4 states of one row), R*256 quads per
+// block; all of a thread's loads are issued before any arithmetic so that a
+// wave has R KiB of state in flight.
+template <typename T, bool GATE, int R>
 __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ state,
                                                    const T* __restrict__ x,
                                                    const T* __restrict__ delta,
@@ -29,57 +33,69 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ state,
                                                    const float* __restrict__ D,
                                                    const T* __restrict__ z, T* __restrict__ y,
                                                    int64_t rows, int64_t dim) {
-    const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t row = gid >> 2;
-    const int q = int(gid & 3);
-    const bool ok = row < rows;
-    const int64_t r = ok ? row : rows - 1;  // clamped: every lane reads valid memory
-    const int64_t b = r / dim, d = r % dim;
-
-    float4 h = *reinterpret_cast<const float4*>(state + r * kN + q * 4);
-    const float4 a4 = *reinterpret_cast<const float4*>(A + d * kN + q * 4);
-    float bv[4], cv[4];
-    if constexpr (sizeof(T) == 4) {
-        const float4 b4 = *reinterpret_cast<const float4*>(B + b * kN + q * 4);
-        const float4 c4 = *reinterpret_cast<const float4*>(C + b * kN + q * 4);
-        bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
-        cv[0] = c4.x; cv[1] = c4.y; cv[2] = c4.z; cv[3] = c4.w;
-    } else {
-        const uint2 b2 = *reinterpret_cast<const uint2*>(B + b * kN + q * 4);
-        const uint2 c2 = *reinterpret_cast<const uint2*>(C + b * kN + q * 4);
-        bv[0] = bf16_lo(b2.x); bv[1] = bf16_hi(b2.x); bv[2] = bf16_lo(b2.y); bv[3] = bf16_hi(b2.y);
-        cv[0] = bf16_lo(c2.x); cv[1] = bf16_hi(c2.x); cv[2] = bf16_lo(c2.y); cv[3] = bf16_hi(c2.y);
+    float4 h[R], a4[R];
+    float bv[R][4], cv[R][4], xv[R], dv[R], zv[R];
+    int64_t rr[R];
+    bool ok[R];
+    int q[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int64_t gid = (int64_t(blockIdx.x) * R + k) * 256 + threadIdx.x;
+        const int64_t row = gid >> 2;
+        q[k] = int(gid & 3);
+        ok[k] = row < rows;
+        const int64_t r = ok[k] ? row : rows - 1;  // clamped: every lane reads valid memory
+        rr[k] = r;
+        const int64_t b = r / dim, d = r % dim;
+        h[k] = *reinterpret_cast<const float4*>(state + r * kN + q[k] * 4);
+        a4[k] = *reinterpret_cast<const float4*>(A + d * kN + q[k] * 4);
+        if constexpr (sizeof(T) == 4) {
+            const float4 b4 = *reinterpret_cast<const float4*>(B + b * kN + q[k] * 4);
+            const float4 c4 = *reinterpret_cast<const float4*>(C + b * kN + q[k] * 4);
+            bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
+            cv[k][0] = c4.x; cv[k][1] = c4.y; cv[k][2] = c4.z; cv[k][3] = c4.w;
+        } else {
+            const uint2 b2 = *reinterpret_cast<const uint2*>(B + b * kN + q[k] * 4);
+            const uint2 c2 = *reinterpret_cast<const uint2*>(C + b * kN + q[k] * 4);
+            bv[k][0] = bf16_lo(b2.x); bv[k][1] = bf16_hi(b2.x); bv[k][2] = bf16_lo(b2.y); bv[k][3] = bf16_hi(b2.y);
+            cv[k][0] = bf16_lo(c2.x); cv[k][1] = bf16_hi(c2.x); cv[k][2] = bf16_lo(c2.y); cv[k][3] = bf16_hi(c2.y);
+        }
+        xv[k] = to_f32(x[r]);
+        dv[k] = to_f32(delta[r]);
+        zv[k] = GATE ? to_f32(z[r]) : 0.0f;
     }
-    const float xv = to_f32(x[r]);
-    const float l = softplus_log2(to_f32(delta[r]));
-    const float w = l * kLn2 * xv;
-
-    h.x = fmaf(exp2_hw(l * a4.x), h.x, w * bv[0]);
-    h.y = fmaf(exp2_hw(l * a4.y), h.y, w * bv[1]);
-    h.z = fmaf(exp2_hw(l * a4.z), h.z, w * bv[2]);
-    h.w = fmaf(exp2_hw(l * a4.w), h.w, w * bv[3]);
-    float yp = fmaf(cv[3], h.w, fmaf(cv[2], h.z, fmaf(cv[1], h.y, cv[0] * h.x)));
-    if (ok) *reinterpret_cast<float4*>(state + r * kN + q * 4) = h;
-
-    yp += __shfl_xor(yp, 1);
-    yp += __shfl_xor(yp, 2);
-    if (ok && q == 0) {
-        float yv = yp + (D ? D[d] : 0.0f) * xv;
-        if constexpr (GATE) yv *= silu(to_f32(z[r]));
-        y[r] = from_f32<T>(yv);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const float l = softplus_log2(dv[k]);
+        const float w = l * kLn2 * xv[k];
+        h[k].x = fmaf(exp2_hw(l * a4[k].x), h[k].x, w * bv[k][0]);
+        h[k].y = fmaf(exp2_hw(l * a4[k].y), h[k].y, w * bv[k][1]);
+        h[k].z = fmaf(exp2_hw(l * a4[k].z), h[k].z, w * bv[k][2]);
+        h[k].w = fmaf(exp2_hw(l * a4[k].w), h[k].w, w * bv[k][3]);
+        if (ok[k]) *reinterpret_cast<float4*>(state + rr[k] * kN + q[k] * 4) = h[k];
+        float yp = fmaf(cv[k][3], h[k].w, fmaf(cv[k][2], h[k].z, fmaf(cv[k][1], h[k].y, cv[k][0] * h[k].x)));
+        yp += __shfl_xor(yp, 1);
+        yp += __shfl_xor(yp, 2);
+        if (ok[k] && q[k] == 0) {
+            float yv = yp + (D ? D[rr[k] % dim] : 0.0f) * xv[k];
+            if constexpr (GATE) yv *= silu(zv[k]);
+            y[rr[k]] = from_f32<T>(yv);
+        }
     }
 }
 
+constexpr int kStepR = 4;
+
 template <typename T>
 hipError_t launch_t(const StepTensors& t, int64_t rows, int64_t dim, hipStream_t st) {
-    const int64_t blocks = (rows * 4 + 255) / 256;
+    const int64_t blocks = (rows * 4 + 256 * kStepR - 1) / (256 * kStepR);
     if (t.z)
-        hipLaunchKernelGGL((step_kernel<T, true>), dim3(unsigned(blocks)), dim3(256), 0, st,
+        hipLaunchKernelGGL((step_kernel<T, true, kStepR>), dim3(unsigned(blocks)), dim3(256), 0, st,
                            t.state, static_cast<const T*>(t.x), static_cast<const T*>(t.delta), t.A,
                            static_cast<const T*>(t.B), static_cast<const T*>(t.C), t.D,
                            static_cast<const T*>(t.z), static_cast<T*>(t.y), rows, dim);
     else
-        hipLaunchKernelGGL((step_kernel<T, false>), dim3(unsigned(blocks)), dim3(256), 0, st,
+        hipLaunchKernelGGL((step_kernel<T, false, kStepR>), dim3(unsigned(blocks)), dim3(256), 0, st,
                            t.state, static_cast<const T*>(t.x), static_cast<const T*>(t.delta), t.A,
                            static_cast<const T*>(t.B), static_cast<const T*>(t.C), t.D,
                            static_cast<const T*>(nullptr), static_cast<T*>(t.y), rows, dim);
