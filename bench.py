@@ -32,6 +32,33 @@ SLOT_PEAK = 256 * 64 * 2.4e9
 TRANS_SLOTS = 2            # v_exp/v_log/v_rcp occupy a wave twice as long as an FMA (measured)
 
 
+# HBM traffic of one output-pass launch on the headline workload: rocprofv3
+# --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
+# counter reads for a copy of known size with the same access pattern
+# (profiles/ holds the runs). It is valid only for the device code it was
+# taken on, identified by the sha256 of the forward kernel's sources.
+TRAFFIC = None
+
+
+def kernel_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("fwd.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "selective_state_space_48_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Counted HBM bytes per launch, or None when the counters were taken on
+    other device code (or never)."""
+    if TRAFFIC is None or TRAFFIC["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return int(TRAFFIC["fetch_kib"] * 1024 * TRAFFIC["fetch_factor"]
+               + TRAFFIC["write_kib"] * 1024 * TRAFFIC["write_factor"])
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -98,6 +125,9 @@ def time_fwd(w, steps, warmup, torch, dev, inp=None):
     stream = torch.cuda.current_stream(dev)   # the stream selscan launches on
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The library records its own HIP events on the same stream around each
+    # output-pass kernel (the kernel that writes y), for the per-kernel time.
+    selscan.timing_start(steps)
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
@@ -105,9 +135,11 @@ def time_fwd(w, steps, warmup, torch, dev, inp=None):
     e1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
+    k_ms, k_n = selscan.timing_stop()
+    assert k_n == steps, (k_n, steps)
     ms = e0.elapsed_time(e1) / steps
     del d, y, hs
-    return ms, wall
+    return ms, wall, k_ms / k_n
 
 
 def time_decode(w, steps, warmup, torch, dev):
@@ -135,40 +167,61 @@ def time_decode(w, steps, warmup, torch, dev):
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
+    selscan.timing_start(steps)
     for i in range(steps):
         x, dl, B, C, z = ins[i % len(ins)]
         selscan.step(state, x, dl, A, B, C, D=D, z=z, y=y)
     e1.record(stream)
     torch.cuda.synchronize(dev)
-    return e0.elapsed_time(e1) / steps
+    k_ms, k_n = selscan.timing_stop()
+    assert k_n == steps, (k_n, steps)
+    return e0.elapsed_time(e1) / steps, k_ms / k_n
 
 
-def cpu_baseline(w, inp):
-    """The oracle as it stands, on the whole workload (every row, every token),
-    all host threads; about 1e9 (token, state) updates in float64."""
+def cpu_baseline(w, inp, reps=3):
+    """The oracle as it stands, on the whole workload (every row, every token;
+    about 1e9 (token, state) updates in float64), all host threads, repeated
+    ``reps`` times (some 10-30 s of CPU time in all)."""
     import oracle
 
     nt = oracle.default_threads()
     t0 = time.perf_counter()
-    oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
-               dt_bias=inp["dt_bias"], nthreads=nt)
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                   dt_bias=inp["dt_bias"], nthreads=nt)
+    dt = (time.perf_counter() - t0) / reps
     return {"value": round(w.elements / dt / 1e9, 6), "unit": "Gelem/s", "cores": nt,
             "kind": "oracle",
             "sample": f"the whole {w.name} workload ({w.rows} rows x {w.seqlen} tokens), fp64, "
-                      f"{dt:.2f} s wall on {nt} threads"}
+                      f"{reps} runs, {dt:.2f} s wall each on {nt} threads"}
 
 
-def copy_calibration(torch, dev, gib=1, reps=5):
-    """A plain device copy of known size (torch's copy kernel), run under
-    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to turn those counters into bytes."""
+def copy_calibration(torch, dev, gib=1, reps=3):
+    """Device copies of known size, run under rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE to turn those counters into bytes: torch's copy kernel, and the
+    calibration library's plain, non-temporal and row-pattern copies (the
+    access patterns of the scan kernels)."""
+    import ctypes
+
+    from selective_state_space_48_amd import build as B
+
     n = (gib << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(reps):
         dst.copy_(src)
+    lib = ctypes.CDLL(B.CALIB_LIB)
+    lib.selscan_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int32, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for mode in (0, 1, 2):
+        for _ in range(reps):
+            rc = lib.selscan_calib_copy(src.data_ptr(), dst.data_ptr(), n * 4, mode, stream)
+            assert rc == 0, rc
     torch.cuda.synchronize(dev)
-    return {"copy_bytes_each_way": n * 4, "reps": reps}
+    return {"copy_bytes_each_way": n * 4, "reps": reps,
+            "kernels": ["torch copy", "calib mode 0 plain", "calib mode 1 non-temporal",
+                        "calib mode 2 non-temporal row pattern"]}
 
 
 def main():
@@ -201,15 +254,17 @@ def main():
     if args.only in (None, "fwd"):
         inp = W.fwd_inputs(w)
         log(f"[bench] {w.name}: {args.warmup} warmup + {args.steps} timed forward calls")
-        ms, wall = time_fwd(w, args.steps, args.warmup, torch, dev, inp)
+        ms, wall, k_ms = time_fwd(w, args.steps, args.warmup, torch, dev, inp)
         E = w.elements
         gelem = E / (ms * 1e-3) / 1e9
         bytes_ = algorithmic_bytes(w)
         slots = method_slots(w)
-        hbm = bytes_ / (ms * 1e-3)
-        alu = slots / (ms * 1e-3)
-        log(f"[bench] {w.name}: {ms * 1e3:.1f} us/call, {gelem:.1f} Gelem/s, "
-            f"{hbm / 1e12:.2f} TB/s algorithmic, {alu / 1e12:.1f} T VALU-slot/s method")
+        hbm = bytes_ / (k_ms * 1e-3)
+        alu = slots / (k_ms * 1e-3)
+        log(f"[bench] {w.name}: {ms * 1e3:.1f} us/call ({k_ms * 1e3:.1f} us output-pass kernel), "
+            f"{gelem:.1f} Gelem/s, kernel at {hbm / 1e12:.2f} TB/s algorithmic, "
+            f"{alu / 1e12:.1f} T VALU-slot/s method")
+        traffic = measured_traffic()
         out.update({
             "metric": "selective-scan fwd Gelem/s (B*L*d_inner), Mamba-1.4B-shaped layer",
             "value": round(gelem, 3),
@@ -226,13 +281,14 @@ def main():
             "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen,
                        "d_inner": w.dim, "d_state": w.dstate, "gate": w.gate,
                        "parallelism": "single GPU"},
-            "hbm": {"achieved": round(hbm / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                    "frac": round(hbm / HBM_PEAK, 4), "bytes_per_call": bytes_},
             "roofline": {"bound": "alu", "achieved": round(alu / 1e12, 3),
                          "peak": round(SLOT_PEAK / 1e12, 3), "unit": "T VALU-slot/s",
-                         "frac": round(alu / SLOT_PEAK, 4), "traffic": None,
-                         "kernel": "fwd_kernel<bf16,G=4,gate,vec,output pass> (+ B/C pack pre-pass)",
-                         "slots_per_call": slots},
+                         "frac": round(alu / SLOT_PEAK, 4), "traffic": traffic,
+                         "kernel": "fwd_kernel<bf16, 4 waves, gate, 16-byte rows, output pass>",
+                         "kernel_us": round(k_ms * 1e3, 2), "slots_per_launch": slots},
+            "hbm": {"achieved": round(hbm / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                    "frac": round(hbm / HBM_PEAK, 4), "bytes_per_launch": bytes_,
+                    "traffic_over_algorithmic": None if traffic is None else round(traffic / bytes_, 3)},
             "wall_s_timed": round(wall, 4),
         })
 
@@ -240,19 +296,22 @@ def main():
     if not args.no_extras and args.only in (None, "decode"):
         wd = W.get(W.DECODE)
         log(f"[bench] {wd.name}: decode steps")
-        us = time_decode(wd, 256, 16, torch, dev) * 1e3
-        gbs = step_bytes(wd) / (us * 1e-6) / 1e9
-        log(f"[bench] decode: {us:.2f} us/step, {gbs:.0f} GB/s")
+        ms_step, k_ms = time_decode(wd, 256, 16, torch, dev)
+        us, kus = ms_step * 1e3, k_ms * 1e3
+        gbs = step_bytes(wd) / (kus * 1e-6) / 1e9
+        log(f"[bench] decode: {us:.2f} us/step ({kus:.2f} us kernel), kernel at {gbs:.0f} GB/s")
         extras["decode"] = {"workload": wd.name, "us_per_step": round(us, 3),
-                            "achieved_GBps": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
+                            "kernel_us": round(kus, 3), "achieved_GBps": round(gbs, 1),
+                            "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
                             "bytes_per_step": step_bytes(wd)}
     for key, name in (("long", "long_f32_b1_l1048576_d128"), ("m130m", "m130m_f32_b8_l2048_d1536")):
         if args.no_extras or args.only not in (None, key):
             continue
         wx = W.get(name)
         log(f"[bench] {name}: forward")
-        ms, _ = time_fwd(wx, 10, 2, torch, dev)
+        ms, _, k_ms = time_fwd(wx, 10, 2, torch, dev)
         extras[key] = {"workload": name, "ms_per_call": round(ms, 4),
+                       "output_pass_ms": round(k_ms, 4),
                        "Gelem_per_s": round(wx.elements / (ms * 1e-3) / 1e9, 2),
                        "frac_hbm": round(algorithmic_bytes(wx) / (ms * 1e-3) / HBM_PEAK, 4)}
     if extras:

@@ -48,7 +48,7 @@ typedef struct {
 #define SELSCAN_ERR_ALLOC (-6)  /* workspace allocation on the stream failed */
 #define SELSCAN_ERR_ALIGN (-7)  /* a pointer is not 16-byte aligned */
 #define SELSCAN_ERR_ALIAS (-8)  /* an output overlaps an input or another output */
-#define SELSCAN_ERR_CONFIG (-9) /* selscan_fwd_ex launch options out of range */
+#define SELSCAN_ERR_CONFIG (-9) /* options out of range, or workspace too small */
 
 /*
  * selscan_fwd — the selective scan over whole sequences.
@@ -78,31 +78,70 @@ typedef struct {
  *   D, dt_bias     : [d] fp32; NULL means 0
  *   z              : NULL means no gate (y is the SSM output itself)
  *   last_state     : [B, d, N] fp32 output; NULL means not wanted
- * Owns nothing. Long sequences with few rows use a temporary workspace of
- * about 2 * segments * B * d * N * 4 bytes, taken with hipMallocAsync on the
- * stream and released with hipFreeAsync on it (SELSCAN_ERR_ALLOC if that
- * fails). y and last_state must not overlap any input or each other.
- * Deterministic: the same inputs give the same bits.
+ * Owns nothing. The call needs a device workspace (B and C repacked as fp32,
+ * B * ceil(L/32)*32 * 128 bytes, plus per-segment states when a long sequence
+ * with few rows is split: selscan_fwd_workspace_size); selscan_fwd takes it
+ * with hipMallocAsync on the stream and returns it with hipFreeAsync on it
+ * (SELSCAN_ERR_ALLOC if that fails). selscan_fwd_ex can be handed a caller's
+ * workspace instead. y and last_state must not overlap any input or each
+ * other. Deterministic: the same inputs and launch choices give the same bits.
  */
 int selscan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                 const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
                 const selscan_dims_t* dims, void* stream);
 
 /*
- * selscan_fwd_ex — selscan_fwd with explicit launch choices (for tuning and
- * for testing one evaluation order against another). Same semantics and
- * results up to rounding.
- *   segments : number of sequence segments scanned in parallel (1 = one pass
- *              per row; > 1 = chunk states, a carry pass, then the output
- *              pass); 0 = automatic. At most 65536, and the segment length is
- *              rounded up to the kernel's time tile.
- *   groups   : waves per 64-row block, each taking N/groups states: 1, 2 or
- *              4; 0 = automatic.
+ * Options of selscan_fwd_ex. Zero-initialise, then set what is wanted.
+ *
+ *   h0        : [B, d, N] fp32, the state entering token 0 (a stored prefix
+ *               state, so that a long sequence can be fed in pieces: the scan
+ *               is a linear recurrence, "State Space Models and Mamba"
+ *               (multigrid.ai), section "It is a linear recurrence", and a
+ *               state is all that is kept between tokens, section "The state,
+ *               in bytes, against a KV cache"). NULL means zeros. Read only;
+ *               it may be the same memory as last_state (read before written
+ *               by the same row's lanes) but must not overlap y.
+ *   workspace : caller-owned device memory of workspace_bytes bytes, 256-byte
+ *               aligned, at least selscan_fwd_workspace_size(); NULL means
+ *               the library takes and returns its own on the stream. The
+ *               contents on entry do not matter; the call uses it until its
+ *               work on the stream completes.
+ *   segments  : sequence segments scanned in parallel (1 = one pass per row;
+ *               > 1 = segment states, a carry pass, then the output pass);
+ *               0 = automatic. At most 65536; the segment length is rounded
+ *               up to the kernels' 32-token tile. Results agree to rounding.
+ *   groups    : waves per 64-row block, each taking N/groups states: 1, 2 or
+ *               4; 0 = automatic. Results agree to rounding.
+ */
+typedef struct {
+    const float* h0;
+    void* workspace;
+    uint64_t workspace_bytes;
+    int32_t segments;
+    int32_t groups;
+} selscan_fwd_opts_t;
+
+/*
+ * selscan_fwd_ex — selscan_fwd with an initial state, a caller workspace and
+ * explicit launch choices (opts may be NULL: all defaults, which is
+ * selscan_fwd). With h0 the recurrence starts from h0 instead of zero:
+ * splitting a sequence at any token and passing the first part's last_state
+ * as h0 of the second gives the unsplit result up to rounding.
+ * Errors as selscan_fwd, plus SELSCAN_ERR_CONFIG for options out of range or
+ * a workspace that is too small or misaligned.
  */
 int selscan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* dt_bias, void* y,
-                   float* last_state, const selscan_dims_t* dims, int32_t segments,
-                   int32_t groups, void* stream);
+                   float* last_state, const selscan_dims_t* dims,
+                   const selscan_fwd_opts_t* opts, void* stream);
+
+/*
+ * Bytes of workspace selscan_fwd_ex needs for these dims and options (h0 and
+ * the workspace fields of opts are ignored; opts may be NULL). Host only.
+ * Returns SELSCAN_OK and sets *bytes, or an argument error.
+ */
+int selscan_fwd_workspace_size(const selscan_dims_t* dims, const selscan_fwd_opts_t* opts,
+                               uint64_t* bytes);
 
 /*
  * selscan_step — one decode step, updating the state in place.
@@ -130,6 +169,22 @@ int selscan_fwd_ex(const void* x, const void* delta, const float* A, const void*
 int selscan_step(float* state, const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, void* y,
                  const selscan_dims_t* dims, void* stream);
+
+/*
+ * Kernel timing for measurement harnesses. selscan_timing_start(capacity)
+ * creates capacity pairs of HIP events (once, reused) and from then on every
+ * selscan_fwd / selscan_fwd_ex call records one pair on its stream around its
+ * output-pass kernel (the kernel that writes y; the B/C repack and, for a
+ * split sequence, the state and carry passes are outside the pair) and every
+ * selscan_step call around its kernel, until capacity pairs are used.
+ * selscan_timing_stop waits for the recorded events, writes the summed
+ * elapsed milliseconds and the number of recorded launches, and stops
+ * recording. Not thread-safe: one measuring thread at a time.
+ * Errors: SELSCAN_ERR_CONFIG (capacity outside 1..65536, or stop without
+ * start), SELSCAN_ERR_NULL, SELSCAN_ERR_LAUNCH (a HIP event call failed).
+ */
+int selscan_timing_start(int32_t capacity);
+int selscan_timing_stop(double* total_ms, int32_t* launches);
 
 /* A static, human-readable message for a return code. */
 const char* selscan_strerror(int code);

@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libselscan.so")
 SOURCES = ["api.hip", "fwd.hip", "step.hip"]
+# Counter-calibration copies (measurement only), a library of their own.
+CALIB_LIB = os.path.join(PKG, "libselscan_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -38,13 +41,10 @@ def _run(cmd):
     return res.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source (in parallel) and link one shared library; returns its path."""
-    objdir = os.path.join(PKG, "_build")
-    os.makedirs(objdir, exist_ok=True)
+def _compile_link(sources, lib, objdir, verbose):
     inc = ["-I", os.path.join(ROOT, "include")]
     jobs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         jobs.append([HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
@@ -56,12 +56,24 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
         if verbose and msgs:
             print("\n".join(msgs))
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = lib + f".tmp{os.getpid()}"
     objs = [j[-1] for j in jobs]
     rc, msgs = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     if rc != 0:
         raise RuntimeError("link failed:\n" + "\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel) and link libselscan.so and the
+    counter-calibration library; returns the path of libselscan.so."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        futs = [ex.submit(_compile_link, SOURCES, LIB, objdir, verbose),
+                ex.submit(_compile_link, CALIB_SOURCES, CALIB_LIB, objdir, verbose)]
+        for f in futs:
+            f.result()
     return LIB
 
 

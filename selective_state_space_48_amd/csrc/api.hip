@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <vector>
+
 #include "../../include/selscan.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -12,11 +14,12 @@ using namespace selscan;
 
 namespace selscan {
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st);
 }
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -66,47 +69,15 @@ int check_common(const selscan_dims_t* dims, bool fwd) {
     return SELSCAN_OK;
 }
 
-int fwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
-             const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
-             const selscan_dims_t* dims, int32_t segments, int32_t groups, void* stream) {
-    int rc = check_common(dims, true);
-    if (rc != SELSCAN_OK) return rc;
-    if (segments < 0 || segments > 65536) return SELSCAN_ERR_CONFIG;
-    if (groups != 0 && groups != 1 && groups != 2 && groups != 4) return SELSCAN_ERR_CONFIG;
+// Launch plan of a forward call (shared by the call and the workspace query).
+int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdPlan* plan) {
     const int64_t L = dims->seqlen;
-    // The kernels address B/C rows with 32-bit offsets of up to N*L elements.
-    if (L >= (int64_t(1) << 27)) return SELSCAN_ERR_DIMS;
-    Sizes sz;
-    if (!sizes(*dims, L, &sz)) return SELSCAN_ERR_DIMS;
-    // A tensor with no elements may come with a null pointer (torch gives one).
-    if ((sz.seq > 0 && (!x || !delta || !y)) || (sz.bc > 0 && (!B || !C)) || (sz.param > 0 && !A))
-        return SELSCAN_ERR_NULL;
-    for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, (const void*)y,
-                          (const void*)last_state})
-        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
-    const Span out_y = span(y, sz.seq * es), out_s = span(last_state, sz.state * 4);
-    const Span ins[] = {span(x, sz.seq * es),      span(delta, sz.seq * es), span(z, sz.seq * es),
-                        span(B, sz.bc * es),       span(C, sz.bc * es),      span(A, sz.param * 4),
-                        span(D, dims->dim * 4),    span(dt_bias, dims->dim * 4)};
-    for (const Span& s : ins)
-        if (overlaps(s, out_y) || overlaps(s, out_s)) return SELSCAN_ERR_ALIAS;
-    if (overlaps(out_y, out_s)) return SELSCAN_ERR_ALIAS;
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (sz.rows == 0) return SELSCAN_OK;
-    if (L == 0) {
-        if (last_state && launch_fill_zero(last_state, sz.state, st) != hipSuccess)
-            return SELSCAN_ERR_LAUNCH;
-        return SELSCAN_OK;
-    }
-
-    // ---- plan ----
-    FwdPlan plan{};
-    plan.groups = groups ? groups : 4;
-    plan.vec = (L * es) % 16 == 0;
+    *plan = FwdPlan{};
+    plan->groups = groups ? groups : 4;
+    plan->vec = (L * es) % 16 == 0;
     const int64_t row_blocks = (dims->dim + kWave - 1) / kWave;
-    const int64_t waves = row_blocks * dims->batch * plan.groups;
+    const int64_t waves = row_blocks * dims->batch * plan->groups;
     int64_t S = segments;
     if (S == 0) {
         // Segmenting adds a state pass (about 0.7 of an output pass) over all
@@ -121,29 +92,112 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
             if (S < 1) S = 1;
         }
     }
-    if (S > 1) {
+    if (S > 1 && L > 0) {
         int64_t seg_len = (L + S - 1) / S;
         seg_len = (seg_len + kChunk - 1) / kChunk * kChunk;
         S = (L + seg_len - 1) / seg_len;
-        plan.seg_len = seg_len;
+        plan->seg_len = seg_len;
     } else {
-        plan.seg_len = L;
+        S = 1;
+        plan->seg_len = L;
     }
-    plan.segments = int32_t(S);
-    if (int64_t(plan.segments) * row_blocks * dims->batch > INT32_MAX) return SELSCAN_ERR_DIMS;
+    plan->segments = int32_t(S);
+    if (int64_t(plan->segments) * row_blocks * dims->batch > INT32_MAX) return SELSCAN_ERR_DIMS;
+    return SELSCAN_OK;
+}
 
-    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state};
+int check_opts(const selscan_fwd_opts_t& o) {
+    if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
+    if (o.groups != 0 && o.groups != 1 && o.groups != 2 && o.groups != 4) return SELSCAN_ERR_CONFIG;
+    return SELSCAN_OK;
+}
+
+int check_fwd_dims(const selscan_dims_t* dims, Sizes* sz) {
+    int rc = check_common(dims, true);
+    if (rc != SELSCAN_OK) return rc;
+    // The kernels address B/C rows with 32-bit offsets of up to N*L elements.
+    if (dims->seqlen >= (int64_t(1) << 27)) return SELSCAN_ERR_DIMS;
+    if (!sizes(*dims, dims->seqlen, sz)) return SELSCAN_ERR_DIMS;
+    return SELSCAN_OK;
+}
+
+// Measurement hook state (selscan_timing_*). One pair of events per launch.
+struct Timing {
+    bool on = false;
+    int32_t used = 0;
+    std::vector<hipEvent_t> ev;  // 2 per launch, created once, kept for reuse
+};
+Timing g_timing;
+
+// The next unused event pair, or nulls when not timing or full.
+void next_events(hipEvent_t* b, hipEvent_t* e) {
+    *b = *e = nullptr;
+    if (!g_timing.on || 2 * size_t(g_timing.used + 1) > g_timing.ev.size()) return;
+    *b = g_timing.ev[2 * g_timing.used];
+    *e = g_timing.ev[2 * g_timing.used + 1];
+    ++g_timing.used;
+}
+
+int fwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
+             const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
+             const selscan_dims_t* dims, const selscan_fwd_opts_t* opts, void* stream) {
+    Sizes sz;
+    int rc = check_fwd_dims(dims, &sz);
+    if (rc != SELSCAN_OK) return rc;
+    const selscan_fwd_opts_t o = opts ? *opts : selscan_fwd_opts_t{};
+    rc = check_opts(o);
+    if (rc != SELSCAN_OK) return rc;
+    const int64_t L = dims->seqlen;
+    // A tensor with no elements may come with a null pointer (torch gives one).
+    if ((sz.seq > 0 && (!x || !delta || !y)) || (sz.bc > 0 && (!B || !C)) || (sz.param > 0 && !A))
+        return SELSCAN_ERR_NULL;
+    for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, (const void*)y,
+                          (const void*)last_state, (const void*)o.h0})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u)) return SELSCAN_ERR_CONFIG;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span out_y = span(y, sz.seq * es), out_s = span(last_state, sz.state * 4);
+    const Span ins[] = {span(x, sz.seq * es),      span(delta, sz.seq * es), span(z, sz.seq * es),
+                        span(B, sz.bc * es),       span(C, sz.bc * es),      span(A, sz.param * 4),
+                        span(D, dims->dim * 4),    span(dt_bias, dims->dim * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, out_y) || overlaps(s, out_s)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_y, out_s)) return SELSCAN_ERR_ALIAS;
+    // h0 may be last_state itself (each row's state is read before it is
+    // written), but no other overlap with an output.
+    const Span in_h0 = span(o.h0, sz.state * 4);
+    if (overlaps(in_h0, out_y)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(in_h0, out_s) && static_cast<const void*>(o.h0) != static_cast<const void*>(last_state))
+        return SELSCAN_ERR_ALIAS;
+
+    FwdPlan plan{};
+    rc = make_plan(dims, o.segments, o.groups, &plan);
+    if (rc != SELSCAN_OK) return rc;
     FwdShape shape{dims->batch, L, dims->dim, dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
-    void* ws = nullptr;
-    const size_t ws_bytes = fwd_workspace_bytes(shape, plan);
-    if (ws_bytes) {
+    const size_t ws_bytes = (sz.rows > 0 && L > 0) ? fwd_workspace_bytes(shape, plan) : 0;
+    if (o.workspace && o.workspace_bytes < ws_bytes) return SELSCAN_ERR_CONFIG;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sz.rows == 0) return SELSCAN_OK;
+    if (L == 0) {
+        if (!last_state) return SELSCAN_OK;
+        const hipError_t e = o.h0 ? launch_copy_f32(last_state, o.h0, sz.state, st)
+                                  : launch_fill_zero(last_state, sz.state, st);
+        return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+    }
+
+    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state, o.h0};
+    next_events(&plan.ev_begin, &plan.ev_end);
+    void* ws = o.workspace;
+    const bool own = ws == nullptr;
+    if (own) {
         if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
             (void)hipGetLastError();
             return SELSCAN_ERR_ALLOC;
         }
     }
     const hipError_t e = launch_fwd(t, shape, plan, ws, st);
-    if (ws) (void)hipFreeAsync(ws, st);
+    if (own) (void)hipFreeAsync(ws, st);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 
@@ -154,15 +208,32 @@ extern "C" {
 int selscan_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                 const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
                 const selscan_dims_t* dims, void* stream) {
-    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, 0, 0, stream);
+    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, nullptr, stream);
 }
 
 int selscan_fwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* dt_bias, void* y,
-                   float* last_state, const selscan_dims_t* dims, int32_t segments,
-                   int32_t groups, void* stream) {
-    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, segments, groups,
-                    stream);
+                   float* last_state, const selscan_dims_t* dims,
+                   const selscan_fwd_opts_t* opts, void* stream) {
+    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, opts, stream);
+}
+
+int selscan_fwd_workspace_size(const selscan_dims_t* dims, const selscan_fwd_opts_t* opts,
+                               uint64_t* bytes) {
+    if (!bytes) return SELSCAN_ERR_NULL;
+    Sizes sz;
+    int rc = check_fwd_dims(dims, &sz);
+    if (rc != SELSCAN_OK) return rc;
+    const selscan_fwd_opts_t o = opts ? *opts : selscan_fwd_opts_t{};
+    rc = check_opts(o);
+    if (rc != SELSCAN_OK) return rc;
+    FwdPlan plan{};
+    rc = make_plan(dims, o.segments, o.groups, &plan);
+    if (rc != SELSCAN_OK) return rc;
+    FwdShape shape{dims->batch, dims->seqlen, dims->dim,
+                   dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
+    *bytes = (sz.rows > 0 && dims->seqlen > 0) ? fwd_workspace_bytes(shape, plan) : 0;
+    return SELSCAN_OK;
 }
 
 int selscan_step(float* state, const void* x, const void* delta, const float* A, const void* B,
@@ -188,10 +259,46 @@ int selscan_step(float* state, const void* x, const void* delta, const float* A,
     if (overlaps(out_y, io_s)) return SELSCAN_ERR_ALIAS;
     if (sz.rows == 0) return SELSCAN_OK;
     StepTensors t{state, x, delta, A, B, C, D, z, y};
+    hipEvent_t eb, ee;
+    next_events(&eb, &ee);
     const hipError_t e = launch_step(t, dims->batch, dims->dim,
                                      dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
-                                     static_cast<hipStream_t>(stream));
+                                     static_cast<hipStream_t>(stream), eb, ee);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+int selscan_timing_start(int32_t capacity) {
+    if (capacity < 1 || capacity > 65536) return SELSCAN_ERR_CONFIG;
+    while (g_timing.ev.size() < 2 * size_t(capacity)) {
+        hipEvent_t ev;
+        if (hipEventCreate(&ev) != hipSuccess) {
+            (void)hipGetLastError();
+            return SELSCAN_ERR_LAUNCH;
+        }
+        g_timing.ev.push_back(ev);
+    }
+    g_timing.on = true;
+    g_timing.used = 0;
+    return SELSCAN_OK;
+}
+
+int selscan_timing_stop(double* total_ms, int32_t* launches) {
+    if (!total_ms || !launches) return SELSCAN_ERR_NULL;
+    if (!g_timing.on) return SELSCAN_ERR_CONFIG;
+    g_timing.on = false;
+    double sum = 0.0;
+    for (int32_t i = 0; i < g_timing.used; ++i) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) {
+            (void)hipGetLastError();
+            return SELSCAN_ERR_LAUNCH;
+        }
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = g_timing.used;
+    return SELSCAN_OK;
 }
 
 const char* selscan_strerror(int code) {
@@ -205,7 +312,7 @@ const char* selscan_strerror(int code) {
         case SELSCAN_ERR_ALLOC: return "workspace allocation failed";
         case SELSCAN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case SELSCAN_ERR_ALIAS: return "an output overlaps an input or another output";
-        case SELSCAN_ERR_CONFIG: return "launch options out of range";
+        case SELSCAN_ERR_CONFIG: return "options out of range, or workspace too small or misaligned";
         default: return "unknown error code";
     }
 }

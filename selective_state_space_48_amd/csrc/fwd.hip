@@ -455,12 +455,13 @@ __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, c
 }
 
 // Carry pass: for each (row, n), compose the segments in order,
-//   H_{s+1} = 2^(A_n * lsum_s) H_s + state_s,  H_0 = 0,
+//   H_{s+1} = 2^(A_n * lsum_s) H_s + state_s,  H_0 = h0 (or 0),
 // and write the state entering every segment. 2^(A * sum of l) is the
 // product of the per-token decays of the segment.
 __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
                                                     const float* __restrict__ seg_state,
                                                     const double* __restrict__ seg_lsum,
+                                                    const float* __restrict__ h0,
                                                     float* __restrict__ carry, int64_t rows,
                                                     int64_t dim, int32_t segments) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -468,8 +469,8 @@ __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
     const int64_t r = i / kN;
     const int n = int(i % kN);
     const double An = A[(r % dim) * kN + n];
-    float H = 0.0f;
-    carry[i] = 0.0f;
+    float H = h0 ? h0[i] : 0.0f;
+    carry[i] = H;
     constexpr int U = 8;
     int s = 0;
     for (; s + U <= segments - 1; s += U) {
@@ -543,6 +544,16 @@ hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, in
     return hipGetLastError();
 }
 
+// The output pass, bracketed by the plan's timing events when it has them.
+hipError_t output_pass(DType dt, const FwdKArgs& k, const FwdPlan& p, bool gate, int64_t blocks,
+                       hipStream_t st) {
+    if (p.ev_begin && hipEventRecord(p.ev_begin, st) != hipSuccess) return hipGetLastError();
+    const hipError_t e = dispatch_dtype<0>(dt, k, p.groups, gate, p.vec, blocks, st);
+    if (e != hipSuccess) return e;
+    if (p.ev_end && hipEventRecord(p.ev_end, st) != hipSuccess) return hipGetLastError();
+    return hipSuccess;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Padded token count of the packed B/C: whole chunks.
@@ -553,12 +564,24 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
     if (i < n) p[i] = 0.0f;
 }
 
+__global__ __launch_bounds__(256) void copy_f32_kernel(float* __restrict__ dst,
+                                                      const float* __restrict__ src, int64_t n) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
 }  // namespace
 
 // A fill kernel rather than a memset, so that the call stays capturable.
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t st) {
+    if (n <= 0 || dst == src) return hipSuccess;
+    hipLaunchKernelGGL(copy_f32_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
     return hipGetLastError();
 }
 
@@ -594,8 +617,8 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     const int64_t per_seg = int64_t(k.row_blocks) * s.batch;
 
     if (p.segments <= 1) {
-        k.h0 = nullptr;
-        return dispatch_dtype<0>(s.dtype, k, p.groups, gate, p.vec, per_seg, stream);
+        k.h0 = t.h0;
+        return output_pass(s.dtype, k, p, gate, per_seg, stream);
     }
     const size_t rows = size_t(s.batch) * size_t(s.dim);
     const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
@@ -613,12 +636,12 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     // 2) carries
     const int64_t nthreads = int64_t(rows) * kN;
     hipLaunchKernelGGL(carry_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream,
-                       t.A, seg_state, seg_lsum, carry, int64_t(rows), s.dim, p.segments);
+                       t.A, seg_state, seg_lsum, t.h0, carry, int64_t(rows), s.dim, p.segments);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 3) output pass from the carried-in states
     k.h0 = carry;
-    return dispatch_dtype<0>(s.dtype, k, p.groups, gate, p.vec, per_seg * p.segments, stream);
+    return output_pass(s.dtype, k, p, gate, per_seg * p.segments, stream);
 }
 
 }  // namespace selscan

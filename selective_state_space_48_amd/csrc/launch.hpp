@@ -21,6 +21,7 @@ struct FwdTensors {
     const float* dt_bias;  // null: 0
     void* y;
     float* last_state;  // null: not wanted
+    const float* h0;    // [batch, dim, N] state entering token 0; null: zeros
 };
 
 struct FwdShape {
@@ -36,6 +37,9 @@ struct FwdPlan {
     int64_t seg_len;
     int32_t groups;
     bool vec;  // 16-byte vector access to rows is valid (L * elem_size % 16 == 0)
+    // When set, recorded on the stream right before and after the output-pass
+    // kernel (measurement only).
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
 };
 
 // Time tile (tokens per chunk) of the forward kernels.
@@ -62,6 +66,7 @@ struct StepTensors {
 };
 
 hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType dtype,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t ev_begin = nullptr,
+                       hipEvent_t ev_end = nullptr);
 
 }  // namespace selscan

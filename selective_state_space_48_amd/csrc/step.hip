@@ -105,10 +105,14 @@ hipError_t launch_t(const StepTensors& t, int64_t rows, int64_t dim, hipStream_t
 }  // namespace
 
 hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType dtype,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
     const int64_t rows = batch * dim;
-    return dtype == DType::BF16 ? launch_t<bf16_bits>(t, rows, dim, stream)
-                                : launch_t<float>(t, rows, dim, stream);
+    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return hipGetLastError();
+    const hipError_t e = dtype == DType::BF16 ? launch_t<bf16_bits>(t, rows, dim, stream)
+                                              : launch_t<float>(t, rows, dim, stream);
+    if (e != hipSuccess) return e;
+    if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace selscan

@@ -33,6 +33,12 @@ class Dims(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32)]
 
 
+class FwdOpts(ctypes.Structure):
+    _fields_ = [("h0", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_uint64), ("segments", ctypes.c_int32),
+                ("groups", ctypes.c_int32)]
+
+
 class SelscanError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libselscan error {code}: {msg}")
@@ -48,8 +54,15 @@ def _load() -> ctypes.CDLL:
     dims_p = ctypes.POINTER(Dims)
     lib.selscan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, dims_p, vp]
     lib.selscan_fwd.restype = ctypes.c_int
-    lib.selscan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, dims_p, i32, i32, vp]
+    opts_p = ctypes.POINTER(FwdOpts)
+    lib.selscan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, dims_p, opts_p, vp]
     lib.selscan_fwd_ex.restype = ctypes.c_int
+    lib.selscan_fwd_workspace_size.argtypes = [dims_p, opts_p, ctypes.POINTER(ctypes.c_uint64)]
+    lib.selscan_fwd_workspace_size.restype = ctypes.c_int
+    lib.selscan_timing_start.argtypes = [i32]
+    lib.selscan_timing_start.restype = ctypes.c_int
+    lib.selscan_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    lib.selscan_timing_stop.restype = ctypes.c_int
     lib.selscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, dims_p, vp]
     lib.selscan_step.restype = ctypes.c_int
     lib.selscan_strerror.argtypes = [ctypes.c_int]
@@ -98,15 +111,42 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def workspace_size(batch: int, L: int, dim: int, dtype: torch.dtype, N: int = 16, *,
+                   segments: int = 0, groups: int = 0) -> int:
+    """Bytes of device workspace a forward call of this shape needs."""
+    dims = Dims(batch, L, dim, N, _DTYPES[dtype])
+    opts = FwdOpts(None, None, 0, int(segments), int(groups))
+    out = ctypes.c_uint64(0)
+    _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out)))
+    return int(out.value)
+
+
+def timing_start(capacity: int) -> None:
+    """Record HIP events around the next ``capacity`` output-pass / step kernels."""
+    _check(lib.selscan_timing_start(int(capacity)))
+
+
+def timing_stop() -> Tuple[float, int]:
+    """Wait for the recorded kernels; return (summed milliseconds, launches)."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int32(0)
+    _check(lib.selscan_timing_stop(ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
+
+
 def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
         dt_bias: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
         last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
+        h0: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
         segments: int = 0, groups: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Selective-scan forward (selscan_fwd / selscan_fwd_ex). Returns (y, last_state).
+    """Selective-scan forward (selscan_fwd_ex). Returns (y, last_state).
 
     ``y`` and ``last_state`` may be passed in preallocated; otherwise they are
-    allocated here. ``segments``/``groups`` select the launch (0 = automatic).
+    allocated here. ``h0`` [batch, dim, N] fp32 is the state entering token 0
+    (None: zeros; it may be ``last_state`` itself). ``workspace`` is a uint8
+    device tensor of at least ``workspace_size(...)`` bytes; by default one is
+    taken from torch's caching allocator. ``segments``/``groups`` select the
+    launch (0 = automatic).
     """
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
@@ -129,10 +169,22 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _req(last_state, "last_state", torch.float32, (batch, dim, N), dev)
+    _req(h0, "h0", torch.float32, (batch, dim, N), dev)
     dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
+    opts = FwdOpts(None, None, 0, int(segments), int(groups))
+    need = ctypes.c_uint64(0)
+    _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(need)))
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _req(workspace, "workspace", torch.uint8, None, dev)
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel()
+    if h0 is not None:
+        opts.h0 = h0.data_ptr()
     rc = lib.selscan_fwd_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(dt_bias), _ptr(y), _ptr(last_state), ctypes.byref(dims),
-                            int(segments), int(groups), _stream(dev))
+                            ctypes.byref(opts), _stream(dev))
     _check(rc)
     return y, last_state
 

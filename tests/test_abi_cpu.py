@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_step", "selscan_strerror",
+    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
+            "selscan_timing_start", "selscan_timing_stop", "selscan_strerror",
             "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
@@ -41,7 +42,7 @@ def test_error_codes_match_header():
 
 
 def test_version():
-    assert S.version() == 10000
+    assert S.version() == 10100
 
 
 # Fake, 16-byte aligned, non-overlapping device addresses (never dereferenced:
@@ -54,10 +55,11 @@ def P(i):
     return ctypes.c_void_p(BASE + i * SPAN)
 
 
-def fwd_call(dims, ptrs=None, segments=0, groups=0):
+def fwd_call(dims, ptrs=None, segments=0, groups=0, h0=None, ws=None, ws_bytes=0):
     p = [P(i) for i in range(10)] if ptrs is None else ptrs
+    opts = S.FwdOpts(h0, ws, ws_bytes, segments, groups)
     return S.lib.selscan_fwd_ex(*p, ctypes.byref(dims) if dims is not None else None,
-                                segments, groups, None)
+                                ctypes.byref(opts), None)
 
 
 def step_call(dims, ptrs=None):
@@ -131,3 +133,72 @@ def test_step_alias():
     p = [P(i) for i in range(9)]
     p[0] = p[3]  # state == A
     assert step_call(D(), p) == S.ERR_ALIAS
+
+
+def test_fwd_h0_checks():
+    h0 = P(12)
+    assert fwd_call(D(), h0=ctypes.c_void_p(BASE + 12 * SPAN + 8)) == S.ERR_ALIGN
+    # h0 overlapping y, or inside last_state without being it
+    assert fwd_call(D(), h0=ctypes.c_void_p(BASE + 8 * SPAN)) == S.ERR_ALIAS
+    assert fwd_call(D(), h0=ctypes.c_void_p(BASE + 9 * SPAN + 16)) == S.ERR_ALIAS
+    # h0 == last_state is allowed: the call then gets as far as the workspace check
+    assert fwd_call(D(), h0=P(9), ws=P(13), ws_bytes=16) == S.ERR_CONFIG
+    assert fwd_call(D(), h0=h0, ws=P(13), ws_bytes=16) == S.ERR_CONFIG
+
+
+def workspace_size(dims, segments=0, groups=0):
+    out = ctypes.c_uint64(7)
+    opts = S.FwdOpts(None, None, 0, segments, groups)
+    rc = S.lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_size():
+    # packed B/C: batch * ceil(L/32)*32 * 2 * 16 fp32, rounded to 256 bytes
+    assert workspace_size(D(batch=8, L=2048, dim=4096, dtype=S.BF16)) == (S.OK, 8 * 2048 * 128)
+    assert workspace_size(D(batch=1, L=100, dim=64)) == (S.OK, 128 * 128)
+    assert workspace_size(D(L=0)) == (S.OK, 0)
+    assert workspace_size(D(dim=0)) == (S.OK, 0)
+    # a split sequence adds per-segment states (fp32) and step sums (fp64)
+    rc, b1 = workspace_size(D(batch=1, L=4096, dim=128), segments=1)
+    rc2, b4 = workspace_size(D(batch=1, L=4096, dim=128), segments=4)
+    assert rc == rc2 == S.OK and b1 == 4096 * 128
+    assert b4 == b1 + 2 * 4 * 128 * 16 * 4 + 4 * 128 * 8
+    assert workspace_size(D(), groups=3)[0] == S.ERR_CONFIG
+    assert workspace_size(D(N=4))[0] == S.ERR_DSTATE
+    assert S.lib.selscan_fwd_workspace_size(ctypes.byref(D()), None, None) == S.ERR_NULL
+    assert S.workspace_size(8, 2048, 4096, __import__("torch").bfloat16) == 8 * 2048 * 128
+
+
+def test_workspace_too_small_or_misaligned():
+    need = workspace_size(D())[1]
+    assert fwd_call(D(), ws=P(13), ws_bytes=need - 1) == S.ERR_CONFIG
+    assert fwd_call(D(), ws=ctypes.c_void_p(BASE + 13 * SPAN + 16), ws_bytes=need) == S.ERR_CONFIG
+
+
+def test_timing_argument_errors():
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    assert S.lib.selscan_timing_start(0) == S.ERR_CONFIG
+    assert S.lib.selscan_timing_start(70000) == S.ERR_CONFIG
+    assert S.lib.selscan_timing_stop(None, ctypes.byref(n)) == S.ERR_NULL
+    assert S.lib.selscan_timing_stop(ctypes.byref(ms), ctypes.byref(n)) == S.ERR_CONFIG
+
+
+def test_calibration_library_exports_and_checks():
+    from selective_state_space_48_amd import build as B
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "selscan_calib.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(selscan_\w+)\s*\(", text)))
+    lib = ctypes.CDLL(B.CALIB_LIB)
+    assert names == ["selscan_calib_copy"]
+    for n in names:
+        assert hasattr(lib, n)
+    f = lib.selscan_calib_copy
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, P(1), 1024, 0, None) == -1
+    assert f(P(0), P(1), 1000, 0, None) == -2
+    assert f(P(0), P(1), 0, 0, None) == -2
+    assert f(ctypes.c_void_p(BASE + 4), P(1), 1024, 0, None) == -7
+    assert f(P(0), P(1), 1024, 2, None) == -2      # row pattern needs whole 256 KiB blocks
+    assert f(P(0), P(1), 1024, 5, None) == -9
