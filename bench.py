@@ -37,7 +37,8 @@ TRANS_SLOTS = 2            # v_exp/v_log/v_rcp occupy a wave twice as long as an
 # counter reads for a copy of known size with the same access pattern
 # (profiles/ holds the runs). It is valid only for the device code it was
 # taken on, identified by the sha256 of the forward kernel's sources.
-TRAFFIC = None
+TRAFFIC = {"sources_sha256": "b5e9015566b7757315063de017b3b6573476dff7a23cb09df5349a0ba5467628",
+           "fetch_kib": 213316.0, "fetch_factor": 2.0, "write_kib": 138347.7, "write_factor": 1.0}
 
 
 def kernel_sources_sha256():
@@ -109,7 +110,7 @@ def device_inputs(w, torch, dev, inp=None):
                 B=t(inp["B"], td), C=t(inp["C"], td), D=t(inp["D"]), dt_bias=t(inp["dt_bias"]))
 
 
-def time_fwd(w, steps, warmup, torch, dev, inp=None):
+def time_fwd(w, steps, warmup, torch, dev, inp=None, distribution=False):
     from selective_state_space_48_amd import selscan
 
     d = device_inputs(w, torch, dev, inp)
@@ -138,8 +139,44 @@ def time_fwd(w, steps, warmup, torch, dev, inp=None):
     k_ms, k_n = selscan.timing_stop()
     assert k_n == steps, (k_n, steps)
     ms = e0.elapsed_time(e1) / steps
+    dist = per_call_distribution(run, torch, dev) if distribution else None
     del d, y, hs
-    return ms, wall, k_ms / k_n
+    return ms, wall, k_ms / k_n, dist
+
+
+def _pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def per_call_distribution(run, torch, dev, n=20, scratch_mb=512):
+    """Per-call times (µs) of ``n`` calls, each bracketed by its own events:
+    warm (right after an untimed call) and cold (right after a 512 MB scratch
+    buffer is written, which evicts the 256 MB last-level cache and the L2s)."""
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(scratch_mb << 18, dtype=torch.float32, device=dev)
+    out = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for i in range(n):
+            torch.cuda.synchronize(dev)
+            # The timed call is queued behind other work (a call, or the
+            # scratch fill), so the events measure its execution, not the
+            # launch latency of an idle GPU.
+            if mode == "cold":
+                scratch.fill_(float(i))
+            else:
+                run()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run()
+            b.record(stream)
+            torch.cuda.synchronize(dev)
+            ts.append(a.elapsed_time(b) * 1e3)
+        out[mode] = {"p10_us": round(_pct(ts, 0.1), 2), "p50_us": round(_pct(ts, 0.5), 2),
+                     "p90_us": round(_pct(ts, 0.9), 2)}
+    del scratch
+    return out
 
 
 def time_decode(w, steps, warmup, torch, dev):
@@ -167,15 +204,70 @@ def time_decode(w, steps, warmup, torch, dev):
     torch.cuda.synchronize(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    selscan.timing_start(steps)
     for i in range(steps):
         x, dl, B, C, z = ins[i % len(ins)]
         selscan.step(state, x, dl, A, B, C, D=D, z=z, y=y)
     e1.record(stream)
     torch.cuda.synchronize(dev)
+    back_to_back = e0.elapsed_time(e1) / steps
+    # again with the library's events around each step kernel
+    selscan.timing_start(steps)
+    for i in range(steps):
+        x, dl, B, C, z = ins[i % len(ins)]
+        selscan.step(state, x, dl, A, B, C, D=D, z=z, y=y)
     k_ms, k_n = selscan.timing_stop()
     assert k_n == steps, (k_n, steps)
-    return e0.elapsed_time(e1) / steps, k_ms / k_n
+    # each of the 64 distinct steps alone, warm and after evicting the caches
+    it = iter(range(10 ** 9))
+
+    def one():
+        i = next(it)
+        x, dl, B, C, z = ins[i % len(ins)]
+        selscan.step(state, x, dl, A, B, C, D=D, z=z, y=y)
+
+    dist = per_call_distribution(one, torch, dev, n=len(ins))
+    return back_to_back, k_ms / k_n, dist
+
+
+def measured_ceilings(torch, dev):
+    """Measured ceilings on this GPU: the device-copy rate (torch copy of
+    1 GiB each way, bytes read + written per second) and the rate of the
+    forward kernel's inner-loop instruction mix alone (VALU slots per second,
+    8 waves per SIMD, from the calibration library)."""
+    import ctypes
+
+    from selective_state_space_48_amd import build as Bld
+
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    copy_bps = 2 * n * 4 * 5 / (e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    lib = ctypes.CDLL(Bld.CALIB_LIB)
+    lib.selscan_calib_scan_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p]
+    blocks, nsub = 256 * 8, 512
+    rec = torch.zeros(8192, dtype=torch.float32, device=dev)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    best = None
+    for _ in range(4):
+        e0.record()
+        assert lib.selscan_calib_scan_mix(rec.data_ptr(), out.data_ptr(), blocks, nsub, stream) == 0
+        e1.record()
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    slots = blocks * 256 * nsub * 16 * (4 + TRANS_SLOTS)
+    return {"copy_GBps": round(copy_bps / 1e9, 1), "scan_mix_T_slot_per_s": round(slots / (best * 1e-3) / 1e12, 3)}
 
 
 def cpu_baseline(w, inp, reps=3):
@@ -190,10 +282,21 @@ def cpu_baseline(w, inp, reps=3):
         oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
                    dt_bias=inp["dt_bias"], nthreads=nt)
     dt = (time.perf_counter() - t0) / reps
+    # one thread, on the first 1/8 of the rows
+    nrows = w.rows // 8
+    t0 = time.perf_counter()
+    sl = slice(0, max(1, nrows // w.dim))
+    oracle.fwd(inp["x"][sl], inp["delta"][sl], inp["A"], inp["B"][sl], inp["C"][sl], D=inp["D"],
+               z=inp["z"][sl], dt_bias=inp["dt_bias"], nthreads=1)
+    dt1 = time.perf_counter() - t0
+    e1 = (sl.stop - sl.start) * w.dim * w.seqlen
     return {"value": round(w.elements / dt / 1e9, 6), "unit": "Gelem/s", "cores": nt,
             "kind": "oracle",
             "sample": f"the whole {w.name} workload ({w.rows} rows x {w.seqlen} tokens), fp64, "
-                      f"{reps} runs, {dt:.2f} s wall each on {nt} threads"}
+                      f"{reps} runs, {dt:.2f} s wall each on {nt} threads",
+            "single_thread": {"value": round(e1 / dt1 / 1e9, 6), "unit": "Gelem/s",
+                              "sample": f"{sl.stop - sl.start} batch entries ({e1:,} elements), "
+                                        f"{dt1:.2f} s on 1 thread"}}
 
 
 def copy_calibration(torch, dev, gib=1, reps=3):
@@ -254,7 +357,9 @@ def main():
     if args.only in (None, "fwd"):
         inp = W.fwd_inputs(w)
         log(f"[bench] {w.name}: {args.warmup} warmup + {args.steps} timed forward calls")
-        ms, wall, k_ms = time_fwd(w, args.steps, args.warmup, torch, dev, inp)
+        ceil = measured_ceilings(torch, dev)
+        log(f"[bench] measured ceilings: {ceil}")
+        ms, wall, k_ms, dist = time_fwd(w, args.steps, args.warmup, torch, dev, inp, distribution=True)
         E = w.elements
         gelem = E / (ms * 1e-3) / 1e9
         bytes_ = algorithmic_bytes(w)
@@ -285,10 +390,15 @@ def main():
                          "peak": round(SLOT_PEAK / 1e12, 3), "unit": "T VALU-slot/s",
                          "frac": round(alu / SLOT_PEAK, 4), "traffic": traffic,
                          "kernel": "fwd_kernel<bf16, 4 waves, gate, 16-byte rows, output pass>",
-                         "kernel_us": round(k_ms * 1e3, 2), "slots_per_launch": slots},
+                         "kernel_us": round(k_ms * 1e3, 2), "slots_per_launch": slots,
+                         "measured_peak": ceil["scan_mix_T_slot_per_s"],
+                         "frac_of_measured_peak": round(alu / 1e12 / ceil["scan_mix_T_slot_per_s"], 4)},
             "hbm": {"achieved": round(hbm / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                     "frac": round(hbm / HBM_PEAK, 4), "bytes_per_launch": bytes_,
-                    "traffic_over_algorithmic": None if traffic is None else round(traffic / bytes_, 3)},
+                    "traffic_over_algorithmic": None if traffic is None else round(traffic / bytes_, 3),
+                    "copy_GBps": ceil["copy_GBps"],
+                    "frac_of_copy": round(hbm / 1e9 / ceil["copy_GBps"], 4)},
+            "per_call": dist,
             "wall_s_timed": round(wall, 4),
         })
 
@@ -296,20 +406,23 @@ def main():
     if not args.no_extras and args.only in (None, "decode"):
         wd = W.get(W.DECODE)
         log(f"[bench] {wd.name}: decode steps")
-        ms_step, k_ms = time_decode(wd, 256, 16, torch, dev)
+        ms_step, k_ms, ddist = time_decode(wd, 256, 16, torch, dev)
         us, kus = ms_step * 1e3, k_ms * 1e3
         gbs = step_bytes(wd) / (kus * 1e-6) / 1e9
-        log(f"[bench] decode: {us:.2f} us/step ({kus:.2f} us kernel), kernel at {gbs:.0f} GB/s")
+        cold = ddist["cold"]["p50_us"]
+        log(f"[bench] decode: {us:.2f} us/step back to back ({kus:.2f} us kernel, {gbs:.0f} GB/s); "
+            f"cold median {cold:.2f} us")
         extras["decode"] = {"workload": wd.name, "us_per_step": round(us, 3),
                             "kernel_us": round(kus, 3), "achieved_GBps": round(gbs, 1),
                             "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
-                            "bytes_per_step": step_bytes(wd)}
+                            "cold_p50_GBps": round(step_bytes(wd) / (cold * 1e-6) / 1e9, 1),
+                            "bytes_per_step": step_bytes(wd), "per_step": ddist}
     for key, name in (("long", "long_f32_b1_l1048576_d128"), ("m130m", "m130m_f32_b8_l2048_d1536")):
         if args.no_extras or args.only not in (None, key):
             continue
         wx = W.get(name)
         log(f"[bench] {name}: forward")
-        ms, _, k_ms = time_fwd(wx, 10, 2, torch, dev)
+        ms, _, k_ms, _ = time_fwd(wx, 10, 2, torch, dev)
         extras[key] = {"workload": name, "ms_per_call": round(ms, 4),
                        "output_pass_ms": round(k_ms, 4),
                        "Gelem_per_s": round(wx.elements / (ms * 1e-3) / 1e9, 2),

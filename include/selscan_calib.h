@@ -27,6 +27,20 @@ extern "C" {
 
 int selscan_calib_copy(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream);
 
+/*
+ * selscan_calib_scan_mix runs the forward kernel's inner loop alone (per lane
+ * 4 states; per token and state: l*A, v_exp_f32, w*B with B a scalar
+ * operand, the state FMA and the readout FMA; B/C by s_load_dwordx16 from a
+ * hot 32 KiB buffer, (l, w) from LDS) for nsub 4-token sub-blocks in
+ * `blocks` workgroups of 256 threads, with no HBM traffic and no barriers. Its
+ * rate is the measured ceiling of that instruction mix: (lane, token, state)
+ * updates = blocks * 256 * nsub * 4 * 4, at 6 VALU slots each.
+ *   rec : >= 8192 floats of device memory (contents irrelevant, read only)
+ *   out : blocks * 256 floats of device memory (written)
+ * Returns 0, -1 (NULL), -2 (blocks < 1, or nsub not even and >= 2), -5.
+ */
+int selscan_calib_scan_mix(const float* rec, float* out, int32_t blocks, int32_t nsub, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

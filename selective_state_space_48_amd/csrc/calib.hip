@@ -38,7 +38,78 @@ __global__ __launch_bounds__(256) void copy_rows(const unsigned char* __restrict
     }
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 sload64(const float* p) {
+    using CP = const __attribute__((address_space(4))) f32x16*;
+    return *(CP)(reinterpret_cast<uintptr_t>(p));
+}
+
+// The forward kernel's inner loop alone, from on-chip operands: per lane 4
+// states, per token and state one multiply (l*A), one v_exp_f32, one multiply
+// (w*B, B a scalar operand) and two FMAs (state, readout). B and C come from
+// a small hot buffer by s_load_dwordx16 one 4-token sub-block ahead, (l, w)
+// from LDS, exactly as in the forward kernel; no HBM traffic, no barriers.
+// Its rate is the measured ceiling of this instruction mix.
+__global__ __launch_bounds__(256) void scan_mix(const float* __restrict__ rec, float* __restrict__ out,
+                                                int32_t nsub) {
+    constexpr int NG = 4, SB = 4;
+    __shared__ float2 lw[16][64];
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+    if (tid < 64)
+        for (int e = 0; e < 16; ++e)
+            lw[e][lane] = make_float2(-0.01f * float(1 + (e + lane) % 7), 0.001f * float(e + 1));
+    __syncthreads();
+    float An[NG], h[NG];
+    for (int j = 0; j < NG; ++j) {
+        An[j] = -1.0f - float(j) - float(lane) * 1e-3f;
+        h[j] = 0.0f;
+    }
+    f32x16 B0 = sload64(rec + wv * 32), C0 = sload64(rec + wv * 32 + 16), B1, C1;
+    float2 l0[SB], l1[SB];
+    for (int e = 0; e < SB; ++e) l0[e] = lw[e][lane];
+    float tot = 0.0f;
+    auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float2* lc, f32x16& Bn,
+                    f32x16& Cn, float2* ln) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        const float* nr = rec + ((sb + 1) & 63) * 128 + wv * 32;
+        Bn = sload64(nr);
+        Cn = sload64(nr + 16);
+        for (int e = 0; e < SB; ++e) ln[e] = lw[((sb + 1) * SB + e) & 15][lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < SB; ++e) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const float dA = __builtin_amdgcn_exp2f(lc[e].x * An[j]);
+                h[j] = fmaf(dA, h[j], lc[e].y * Bc[j * SB + e]);
+                acc = fmaf(Cc[j * SB + e], h[j], acc);
+            }
+            tot += acc;
+        }
+    };
+#pragma unroll 1
+    for (int sb = 0; sb < nsub; sb += 2) {
+        half(sb, B0, C0, l0, B1, C1, l1);
+        half(sb + 1, B1, C1, l1, B0, C0, l0);
+    }
+    float s = tot;
+    for (int j = 0; j < NG; ++j) s += h[j];
+    out[int64_t(blockIdx.x) * 256 + tid] = s;
+}
+
 }  // namespace
+
+extern "C" int selscan_calib_scan_mix(const float* rec, float* out, int32_t blocks, int32_t nsub,
+                                      void* stream) {
+    if (!rec || !out) return -1;
+    if (blocks < 1 || nsub < 2 || nsub % 2) return -2;
+    hipLaunchKernelGGL(scan_mix, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       rec, out, nsub);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int selscan_calib_copy(const void* src, void* dst, int64_t bytes, int32_t mode,
                                   void* stream) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace selscan {
 
 using bf16_bits = uint16_t;  // bfloat16 storage: the upper half of an fp32
@@ -41,20 +43,21 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(u) / ln 2 = max(u, 0)/ln 2 + log2(1 + e^{-|u|}).
+// softplus(u) / ln 2 = max(u, 0)/ln 2 + log2(1 + e^{-|u|}), from ul = u / ln 2.
 // log2(1 + e) is taken from w = fl(1 + e) plus a first-order correction for
-// the rounding of w: with c = e - (w - 1) (exact), log(1 + e) = log(w) + c/w
-// + O(c^2), and 1/w is replaced by 2 - w, whose error only matters when c is
-// already below half an ulp of the result. This keeps the relative accuracy
-// of small step sizes (u very negative), where 1 + e rounds to 1.
-__device__ __forceinline__ float softplus_log2(float u) {
-    const float ul = u * kLog2e;
+// the rounding of w: with c = e - (w - 1) (exact), ln(1 + e) = ln(w) + c/w
+// + O(c^2). The factor 1/w is dropped: the term it changes is below
+// 2^-24 * log2(e) * (1 - 1/w), under one ulp of the result whether e is near
+// 1 (result >= 1) or small (then 1 - 1/w is about e, a relative 2^-24). This
+// keeps the relative accuracy of small step sizes (u very negative), where
+// 1 + e rounds to 1.
+__device__ __forceinline__ float softplus_log2_of(float ul) {
     const float e = exp2_hw(-fabsf(ul));
     const float w = 1.0f + e;
     const float c = e - (w - 1.0f);
-    const float corr = c * (2.0f - w) * kLog2e;
-    return fmaxf(ul, 0.0f) + (log2_hw(w) + corr);
+    return fmaxf(ul, 0.0f) + fmaf(c, kLog2e, log2_hw(w));
 }
+__device__ __forceinline__ float softplus_log2(float u) { return softplus_log2_of(u * kLog2e); }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z}); saturates cleanly at both ends.
 __device__ __forceinline__ float silu(float z) {

@@ -98,7 +98,7 @@ __device__ __forceinline__ f32x16 sload64(const float* p) {
     return *(CP)(reinterpret_cast<uintptr_t>(p));
 }
 
-// Packed operand layout (fp32): P[b][s][g][k][j][e] = (k ? C : B)[b, g*NG + j, s*G + e]
+// Packed operand layout (fp32): P[b][s][g][k][j][e] = (k ? C : B ln 2)[b, g*NG + j, s*G + e]
 // for sub-block s of G tokens, wave group g, state j < NG = 16/G, token e < G;
 // zero for tokens >= L. One (b, s, g) record is 2 x 16 floats.
 constexpr int kRec = 32;  // floats per (b, s, g) record
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const int64_t dp = d0 + pr;
     const bool prow_ok = dp < a.dim;
     const int64_t prow = b * a.dim + (prow_ok ? dp : d0);  // clamped for safe reads
-    const float bias = (a.dt_bias && prow_ok) ? a.dt_bias[dp] : 0.0f;
+    const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;  // bias / ln 2
     const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
     float An[NG], h[NG];
 #pragma unroll
@@ -196,21 +196,24 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 
     // ---- thread (pr, pq)'s token slice [pq*TS, pq*TS+TS) of a chunk, straight from HBM ----
     // The G threads of a row read adjacent slices, so a wave's load covers
-    // 64/G rows with CH contiguous tokens each.
-    // Two register sets, alternating by chunk parity: the loads of chunk c+2
-    // are in flight while chunks c and c+1 are processed.
+    // 64/G rows with CH contiguous tokens each. Two register sets alternate by
+    // chunk parity.
     struct Slice {
         uint4 x[SV], d[SV], z[LOADZ ? SV : 1];
     };
     Slice sl0, sl1;
+    // Whole 16-byte vectors are in or out (L and the segment ends are
+    // multiples of V when VEC); chunks wholly inside the segment load without
+    // any test.
     auto load_slice = [&](int c, Slice& sl) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
         const int64_t off = prow * a.L + ts;
+        const bool whole = t_begin + int64_t(c + 1) * CH <= t_end;
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             const int64_t tk = ts + k * V;
             if constexpr (VEC) {
-                const bool ok = tk < t_end;  // whole vector in or out (L, t_end multiples of V)
+                const bool ok = whole || tk < t_end;
                 sl.x[k] = ok ? ldg_stream(X + off + k * V) : make_uint4(0, 0, 0, 0);
                 sl.d[k] = ok ? ldg_stream(DL + off + k * V) : make_uint4(0, 0, 0, 0);
                 if constexpr (LOADZ) sl.z[k] = ok ? ldg_stream(Z + off + k * V) : make_uint4(0, 0, 0, 0);
@@ -229,18 +232,43 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             }
         }
     };
+    // Two consecutive chunks at once, tensor by tensor, so that when a row's
+    // chunk is only half a 128-byte line (bf16: 32 tokens = 64 bytes) both
+    // halves are requested back to back and the line is fetched once.
+    auto load_pair = [&](int c, Slice& s0, Slice& s1) {
+        const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
+        const int64_t off = prow * a.L + ts;
+        if (VEC && t_begin + int64_t(c + 2) * CH <= t_end) {
+#pragma unroll
+            for (int k = 0; k < SV; ++k) {
+                s0.x[k] = ldg_stream(X + off + k * V);
+                s1.x[k] = ldg_stream(X + off + CH + k * V);
+            }
+#pragma unroll
+            for (int k = 0; k < SV; ++k) {
+                s0.d[k] = ldg_stream(DL + off + k * V);
+                s1.d[k] = ldg_stream(DL + off + CH + k * V);
+            }
+            if constexpr (LOADZ) {
+#pragma unroll
+                for (int k = 0; k < SV; ++k) {
+                    s0.z[k] = ldg_stream(Z + off + k * V);
+                    s1.z[k] = ldg_stream(Z + off + CH + k * V);
+                }
+            }
+        } else {
+            if (c < nchunks) load_slice(c, s0);
+            if (c + 1 < nchunks) load_slice(c + 1, s1);
+        }
+    };
 
     // ---- per-token phase before the scan ----
     // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this thread's
     // registers until its epilogue of the same slice. Tokens past the segment
-    // end get l = w = 0, which makes their scan step the identity. The body is
-    // straight-line (the tail is masked with a uniform 0/1 factor, not
-    // branched around), so the TS independent softplus chains interleave.
-    float dx[TS], gz[TS];      // current chunk (for its epilogue)
-    float dxn[TS], gzn[TS];    // next chunk (written by its prologue)
-    auto prologue = [&](int c, const Slice& sl) {
+    // end get l = w = 0, which makes their scan step the identity. B was
+    // scaled by ln 2 when packed, so w = l * x with l in log2 units.
+    auto prologue = [&](int c, const Slice& sl, float* dxo, float* gzo) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
-        const int nvalid = int(min(int64_t(TS), max(int64_t(0), t_end - ts)));
         float xs[TS], ds[TS], zs[TS];
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
@@ -249,32 +277,29 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             if constexpr (LOADZ) unpack16<T>(sl.z[k], zs + k * V);
         }
         float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]) + pq * TS / 2;
+        auto body = [&](auto masked) {
+            const int nvalid = masked ? int(min(int64_t(TS), max(int64_t(0), t_end - ts))) : TS;
 #pragma unroll
-        for (int j = 0; j < TS; j += 2) {
-            float l[2], w[2];
+            for (int j = 0; j < TS; j += 2) {
+                float l[2], w[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const float keep = (j + u < nvalid) ? 1.0f : 0.0f;  // padded inputs are 0
-                l[u] = softplus_log2(ds[j + u] + bias) * keep;
-                w[u] = l[u] * kLn2 * xs[j + u];
-                if constexpr (MODE == 1) lsum_acc += double(l[u]);
-                if constexpr (MODE == 0) {
-                    dxn[j + u] = Dd * xs[j + u];
-                    gzn[j + u] = 1.0f;
-                    if constexpr (LOADZ) gzn[j + u] = silu(zs[j + u]);
+                for (int u = 0; u < 2; ++u) {
+                    l[u] = softplus_log2_of(fmaf(ds[j + u], kLog2e, biasl));
+                    if (masked && j + u >= nvalid) l[u] = 0.0f;  // padded inputs are 0
+                    w[u] = l[u] * xs[j + u];
+                    if constexpr (MODE == 1) lsum_acc += double(l[u]);
+                    if constexpr (MODE == 0) {
+                        dxo[j + u] = Dd * xs[j + u];
+                        gzo[j + u] = 1.0f;
+                        if constexpr (LOADZ) gzo[j + u] = silu(zs[j + u]);
+                    }
                 }
+                lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
             }
-            lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
-        }
+        };
+        if (t_begin + int64_t(c + 1) * CH <= t_end) body(std::false_type{});
+        else body(std::true_type{});
     };
-    auto take_next = [&]() {
-#pragma unroll
-        for (int j = 0; j < TS; ++j) {
-            dx[j] = dxn[j];
-            gz[j] = gzn[j];
-        }
-    };
-
     // ---- the scan over one chunk: this wave's NG states, all CH tokens ----
     // Software pipeline, one sub-block ahead: wait for the previous loads,
     // issue the next sub-block's B/C record (scalar) and (l, w) (LDS) loads,
@@ -337,7 +362,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     };
 
     // ---- per-token phase after the scan: sum partial readouts, D skip, gate, store ----
-    auto epilogue = [&](int c) {
+    auto epilogue = [&](int c, const float* dx, const float* gz) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
         float yv[TS];
 #pragma unroll
@@ -366,32 +391,43 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         }
     };
 
-    // Per chunk: scan | barrier | prologue(c+1), loads of c+3, epilogue(c) | barrier.
-    // Loads run two chunks ahead, in the register set chunk c+1 just freed.
-    // The epilogue's y stores come last, so no wait for loads (vmcnt, which on
-    // this chip also counts stores) ever waits for freshly issued stores.
-    auto step = [&](int c, Slice& next, Slice& other) {
-        // next holds chunk c+1's inputs; other holds chunk c+2's (in flight)
+    // Per chunk: scan | barrier | prologue(c+1), loads, epilogue(c) | barrier.
+    // Loads: with PAIR, chunks c+2 and c+3 at even c (one and two chunks of
+    // lead); otherwise chunk c+3 at every c (two chunks of lead). The
+    // epilogue's y stores come after the loads, so no wait for loads (vmcnt,
+    // which on this chip also counts stores) waits for fresh stores.
+    // Register sets: chunk c+1's inputs are in `next`; the D*x and gate
+    // values alternate between two arrays by chunk parity (no copies).
+    constexpr bool PAIR = VEC && sizeof(T) * CH < 128;
+    float dxA[TS], gzA[TS], dxB[TS], gzB[TS];
+    auto step = [&](int c, Slice& next, Slice& other, const float* dxc, const float* gzc,
+                    float* dxn, float* gzn) {
         scan_chunk(c);
         __syncthreads();
-        if (c + 1 < nchunks) prologue(c + 1, next);
-        if (c + 3 < nchunks) load_slice(c + 3, next);
-        if constexpr (MODE == 0) epilogue(c);
-        take_next();
+        if (c + 1 < nchunks) prologue(c + 1, next, dxn, gzn);
+        if constexpr (PAIR) {
+            if ((c & 1) == 0 && c + 2 < nchunks) load_pair(c + 2, other, next);
+        } else {
+            if (c + 3 < nchunks) load_slice(c + 3, next);
+        }
+        if constexpr (MODE == 0) epilogue(c, dxc, gzc);
         __syncthreads();
-        (void)other;
     };
     if (nchunks > 0) {
-        load_slice(0, sl0);
-        if (nchunks > 1) load_slice(1, sl1);
-        prologue(0, sl0);
-        take_next();
-        if (nchunks > 2) load_slice(2, sl0);
+        if constexpr (PAIR) {
+            load_pair(0, sl0, sl1);
+            prologue(0, sl0, dxA, gzA);
+        } else {
+            load_slice(0, sl0);
+            if (nchunks > 1) load_slice(1, sl1);
+            prologue(0, sl0, dxA, gzA);
+            if (nchunks > 2) load_slice(2, sl0);
+        }
         __syncthreads();
         // chunk c+1's inputs are in sl1 for even c, sl0 for odd c
         for (int c = 0; c < nchunks; c += 2) {
-            step(c, sl1, sl0);
-            if (c + 1 < nchunks) step(c + 1, sl0, sl1);
+            step(c, sl1, sl0, dxA, gzA, dxB, gzB);
+            if (c + 1 < nchunks) step(c + 1, sl0, sl1, dxB, gzB, dxA, gzA);
         }
     }
 
@@ -441,13 +477,16 @@ __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, c
     const int64_t s = (i / (2 * G)) % psub;
     const int64_t b = i / (2 * G * psub);
     const T* src = (k ? C : B) + (b * kN + g * NG) * L;
+    // B is stored times ln 2, so that the scan's input term is (l x) B' with
+    // l the step size in log2 units (l ln 2 x B = l x (B ln 2)).
+    const float scale = k ? 1.0f : kLn2;
     float v[16];
 #pragma unroll
     for (int j = 0; j < NG; ++j)
 #pragma unroll
         for (int e = 0; e < G; ++e) {
             const int64_t t = s * G + e;
-            v[j * G + e] = t < L ? to_f32(src[j * L + t]) : 0.0f;
+            v[j * G + e] = t < L ? to_f32(src[j * L + t]) * scale : 0.0f;
         }
     float4* dst = reinterpret_cast<float4*>(P + i * 16);
 #pragma unroll

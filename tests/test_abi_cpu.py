@@ -191,7 +191,7 @@ def test_calibration_library_exports_and_checks():
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(selscan_\w+)\s*\(", text)))
     lib = ctypes.CDLL(B.CALIB_LIB)
-    assert names == ["selscan_calib_copy"]
+    assert names == ["selscan_calib_copy", "selscan_calib_scan_mix"]
     for n in names:
         assert hasattr(lib, n)
     f = lib.selscan_calib_copy
@@ -202,3 +202,8 @@ def test_calibration_library_exports_and_checks():
     assert f(ctypes.c_void_p(BASE + 4), P(1), 1024, 0, None) == -7
     assert f(P(0), P(1), 1024, 2, None) == -2      # row pattern needs whole 256 KiB blocks
     assert f(P(0), P(1), 1024, 5, None) == -9
+    g = lib.selscan_calib_scan_mix
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert g(None, P(1), 4, 8, None) == -1
+    assert g(P(0), P(1), 0, 8, None) == -2
+    assert g(P(0), P(1), 4, 7, None) == -2
