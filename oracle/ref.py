@@ -76,8 +76,55 @@ class Oracle:
             [_dp] * 4 + [ctypes.c_int]
         lib.ssm_ref_step.restype = ctypes.c_int
         lib.ssm_ref_step.argtypes = [_dp] * 9 + [ctypes.c_int64] * 3 + [_dp] * 2
+        lib.ssm_ref_conv1d.restype = ctypes.c_int
+        lib.ssm_ref_conv1d.argtypes = [_dp] * 4 + [ctypes.c_int64] * 4 + [_dp] * 3
+        lib.ssm_ref_conv1d_step.restype = ctypes.c_int
+        lib.ssm_ref_conv1d_step.argtypes = [_dp] * 4 + [ctypes.c_int64] * 3 + [_dp] * 2
         self.lib = lib
         self.path = path
+
+    def conv1d(self, x, w, bias=None, x_prev=None):
+        """Causal depthwise convolution of width K = w.shape[1], then SiLU.
+
+        ``x``: ``[batch, dim, seqlen]``; ``w``: ``[dim, K]``; ``bias``: ``[dim]``;
+        ``x_prev``: ``[batch, dim, K-1]``, the inputs before token 0 (zeros if
+        None). Returns a dict with ``out`` and ``out_scale`` (``[batch, dim,
+        seqlen]``) and ``x_last`` (``[batch, dim, K-1]``), all float64.
+        """
+        x, w, bias, x_prev = map(_f64, (x, w, bias, x_prev))
+        batch, dim, L = x.shape
+        K = w.shape[1]
+        assert w.shape == (dim, K)
+        if bias is not None:
+            assert bias.shape == (dim,)
+        if x_prev is not None:
+            assert x_prev.shape == (batch, dim, K - 1)
+        out = np.empty((batch, dim, L), np.float64)
+        sc = np.empty((batch, dim, L), np.float64)
+        last = np.empty((batch, dim, K - 1), np.float64)
+        rc = self.lib.ssm_ref_conv1d(_ptr(x), _ptr(w), _ptr(bias), _ptr(x_prev), batch, L, dim, K,
+                                     _ptr(out), _ptr(sc), _ptr(last))
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_conv1d failed with code {rc}")
+        return {"out": out, "out_scale": sc, "x_last": last}
+
+    def conv1d_step(self, conv_state, x, w, bias=None):
+        """One decode step of the convolution from ``conv_state`` ``[batch, dim,
+        K-1]`` (oldest first) and ``x`` ``[batch, dim]``. Returns a dict with
+        ``out``, ``out_scale`` and the new ``conv_state`` (float64); the inputs
+        are not modified."""
+        st = _f64(conv_state).copy()
+        x, w, bias = map(_f64, (x, w, bias))
+        batch, dim = x.shape
+        K = w.shape[1]
+        assert st.shape == (batch, dim, K - 1) and w.shape == (dim, K)
+        out = np.empty((batch, dim), np.float64)
+        sc = np.empty((batch, dim), np.float64)
+        rc = self.lib.ssm_ref_conv1d_step(_ptr(st), _ptr(x), _ptr(w), _ptr(bias), batch, dim, K,
+                                          _ptr(out), _ptr(sc))
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_conv1d_step failed with code {rc}")
+        return {"out": out, "out_scale": sc, "conv_state": st}
 
     def fwd(self, x, delta, A, B, C, D=None, z=None, dt_bias=None, h0=None, h0_scale=None,
             rows: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
@@ -171,6 +218,16 @@ def fwd(*args, **kw):
 def step(*args, **kw):
     """One decode step through the built oracle; see ``Oracle.step``."""
     return default().step(*args, **kw)
+
+
+def conv1d(*args, **kw):
+    """Causal depthwise conv + SiLU through the built oracle; see ``Oracle.conv1d``."""
+    return default().conv1d(*args, **kw)
+
+
+def conv1d_step(*args, **kw):
+    """One convolution decode step; see ``Oracle.conv1d_step``."""
+    return default().conv1d_step(*args, **kw)
 
 
 def scaled_error(got, ref, scale, floor: float = 1e-30) -> float:

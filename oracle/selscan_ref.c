@@ -232,3 +232,99 @@ int ssm_ref_step(double *state, double *state_scale,
     }
     return 0;
 }
+
+/*
+ * The short causal convolution in front of the selective SSM, and its decode
+ * step.
+ *
+ * "State Space Models and Mamba" (multigrid.ai), section "What a Mamba block
+ * actually contains": the SSM branch is a depthwise conv1d of kernel width 4,
+ * then SiLU, then the selective SSM; the four-position convolution gives the
+ * block direct access to the few tokens just before the current one. "Mamba:
+ * Linear-Time Sequence Modeling with Selective State Spaces" (azimuth.plus),
+ * the block architecture: projection, then a short 1D convolution (kernel
+ * size 4), then SiLU, then the selective SSM. Depthwise: each channel d has
+ * its own K taps w[d, 0..K-1] (and bias[d]). It must be causal, since the
+ * same block runs one token at a time at inference: token t sees inputs
+ * t-K+1 .. t only. For each row (b, d) and token t:
+ *
+ *   pre = bias[d] + sum_{k=0}^{K-1} w[d,k] * xx(t - (K-1) + k)
+ *   out[b,d,t] = silu(pre) = pre / (1 + exp(-pre))
+ *
+ * with xx(s) = x[b,d,s] for s >= 0 and, for s < 0, x_prev[b,d,K-1+s]: the
+ * K-1 inputs that came before token 0 (zeros when x_prev is null). x_last
+ * receives the last K-1 entries of the sequence x_prev ++ x, i.e. the x_prev
+ * of a call that continues where this one stops.
+ *
+ * Error scale: out_scale = |bias| + sum_k |w[d,k] * xx(...)|, the magnitude
+ * sum of the terms of pre; silu is 1.1-Lipschitz, so it bounds the rounding
+ * error of out for any evaluation order.
+ *
+ * Layouts: x, out, out_scale: [batch, dim, seqlen]; w: [dim, K]; bias: [dim];
+ * x_prev, x_last: [batch, dim, K-1].
+ */
+int ssm_ref_conv1d(const double *x, const double *w, const double *bias, const double *x_prev,
+                   int64_t batch, int64_t seqlen, int64_t dim, int64_t K,
+                   double *out, double *out_scale, double *x_last)
+{
+    if (!x || !w || !out) return -1;
+    if (batch < 0 || seqlen < 0 || dim < 0 || K < 1) return -2;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t row = b * dim + d;
+            const double *xr = x + row * seqlen;
+            const double *pr = x_prev ? x_prev + row * (K - 1) : NULL;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                double sc = fabs(pre);
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t s = t - (K - 1) + k;
+                    const double xv = s >= 0 ? xr[s] : (pr ? pr[K - 1 + s] : 0.0);
+                    pre += w[d * K + k] * xv;
+                    sc += fabs(w[d * K + k] * xv);
+                }
+                out[row * seqlen + t] = silu(pre);
+                if (out_scale) out_scale[row * seqlen + t] = sc;
+            }
+            if (x_last) {
+                for (int64_t k = 0; k < K - 1; ++k) {
+                    const int64_t s = seqlen - (K - 1) + k;
+                    x_last[row * (K - 1) + k] = s >= 0 ? xr[s] : (pr ? pr[K - 1 + s] : 0.0);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * One decode step of the convolution: the same formula for a single token x
+ * [batch, dim] with the K-1 previous inputs held in conv_state [batch, dim,
+ * K-1] (oldest first), which is then shifted by one and takes x as its
+ * newest entry.
+ */
+int ssm_ref_conv1d_step(double *conv_state, const double *x, const double *w, const double *bias,
+                        int64_t batch, int64_t dim, int64_t K, double *out, double *out_scale)
+{
+    if (!conv_state || !x || !w || !out) return -1;
+    if (batch < 0 || dim < 0 || K < 1) return -2;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t row = b * dim + d;
+            double *st = conv_state + row * (K - 1);
+            double pre = bias ? bias[d] : 0.0;
+            double sc = fabs(pre);
+            for (int64_t k = 0; k < K - 1; ++k) {
+                pre += w[d * K + k] * st[k];
+                sc += fabs(w[d * K + k] * st[k]);
+            }
+            pre += w[d * K + K - 1] * x[row];
+            sc += fabs(w[d * K + K - 1] * x[row]);
+            out[row] = silu(pre);
+            if (out_scale) out_scale[row] = sc;
+            for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];
+            if (K > 1) st[K - 2] = x[row];
+        }
+    }
+    return 0;
+}

@@ -439,4 +439,101 @@ def pin_nan_propagation(O):
     assert np.all(np.isnan(r["last_state"][1, 2]))
 
 
+# ----------------------------------------------------------------------------
+# The short causal convolution (depthwise, width K) + SiLU, and its step
+# ----------------------------------------------------------------------------
+
+def _conv_problem(seed, batch, dim, L, K=4, with_bias=True, with_prev=True):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.standard_normal((batch, dim, L)),
+                w=rng.standard_normal((dim, K)) * 0.7,
+                bias=rng.standard_normal(dim) * 0.3 if with_bias else None,
+                x_prev=rng.standard_normal((batch, dim, K - 1)) if with_prev else None)
+
+
+def pin_conv1d_library_filter(O):
+    """Each row against scipy's FIR filter (lfilter with the taps reversed is
+    the causal sum over the last K inputs), then torch's silu; the inputs
+    before token 0 are prepended explicitly (or zeros)."""
+    for with_prev in (False, True):
+        p = _conv_problem(31, 2, 5, 23, with_prev=with_prev)
+        r = O.conv1d(p["x"], p["w"], p["bias"], p["x_prev"])
+        K = p["w"].shape[1]
+        for b in range(2):
+            for d in range(5):
+                prev = p["x_prev"][b, d] if with_prev else np.zeros(K - 1)
+                seq = np.concatenate([prev, p["x"][b, d]])
+                pre = scipy.signal.lfilter(p["w"][d, ::-1], [1.0], seq)[K - 1:] + p["bias"][d]
+                _close(r["out"][b, d], silu_lib(pre), 1e-12, what=f"conv lfilter prev={with_prev}")
+                _close(r["x_last"][b, d], seq[-(K - 1):], 0.0, what="conv x_last")
+
+
+def pin_conv1d_torch_grouped(O):
+    """Against torch's grouped conv1d in fp64 (groups = channels, left padding
+    K-1, first L outputs): the layer the pages name, from a library."""
+    p = _conv_problem(32, 3, 7, 40, with_prev=False)
+    K = p["w"].shape[1]
+    xt = torch.from_numpy(p["x"])
+    ref = torch.nn.functional.conv1d(xt, torch.from_numpy(p["w"])[:, None, :],
+                                     torch.from_numpy(p["bias"]), padding=K - 1, groups=7)
+    ref = torch.nn.functional.silu(ref[..., :40]).numpy()
+    _close(O.conv1d(p["x"], p["w"], p["bias"])["out"], ref, 1e-12, what="conv torch grouped")
+
+
+def pin_conv1d_one_hot_taps(O):
+    """A single tap k = K-1-j gives out[t] = silu(x[t-j]) (zero before the
+    start): fixes the causal direction and the tap order."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((1, 4, 12))
+    for j in range(4):
+        w = np.zeros((4, 4)); w[:, 3 - j] = 1.0
+        out = O.conv1d(x, w)["out"]
+        shifted = np.concatenate([np.zeros((1, 4, j)), x[..., :12 - j]], axis=-1)
+        _close(out, silu_lib(shifted), 1e-14, what=f"conv one-hot shift {j}")
+
+
+def pin_conv1d_streaming(O):
+    """Feeding [0, t) then [t, L) with x_prev = the first call's x_last equals
+    one call, for splits shorter and longer than the window."""
+    p = _conv_problem(34, 2, 3, 30)
+    whole = O.conv1d(p["x"], p["w"], p["bias"], p["x_prev"])
+    for t in (1, 2, 3, 11):
+        a = O.conv1d(p["x"][..., :t], p["w"], p["bias"], p["x_prev"])
+        b = O.conv1d(p["x"][..., t:], p["w"], p["bias"], a["x_last"])
+        _close(np.concatenate([a["out"], b["out"]], -1), whole["out"], 0.0, what=f"conv split {t}")
+        _close(b["x_last"], whole["x_last"], 0.0, what="conv split x_last")
+
+
+def pin_conv1d_steps_equal_call(O):
+    """L decode steps from conv_state = x_prev give the call's outputs, and
+    the final conv_state is its x_last."""
+    p = _conv_problem(35, 2, 3, 9)
+    whole = O.conv1d(p["x"], p["w"], p["bias"], p["x_prev"])
+    st = p["x_prev"]
+    for t in range(9):
+        r = O.conv1d_step(st, p["x"][..., t], p["w"], p["bias"])
+        _close(r["out"], whole["out"][..., t], 0.0, what=f"conv step {t}")
+        _close(r["out_scale"], whole["out_scale"][..., t], 0.0, what=f"conv step scale {t}")
+        st = r["conv_state"]
+    _close(st, whole["x_last"], 0.0, what="conv step final state")
+
+
+def pin_conv1d_scale(O):
+    """With every term nonnegative the scale is the pre-activation itself
+    (and out = silu(scale)); with mixed signs it is the sum of |terms|,
+    brute-forced here."""
+    rng = np.random.default_rng(36)
+    x = rng.uniform(0.1, 1.0, (1, 3, 10)); w = rng.uniform(0.1, 1.0, (3, 4))
+    bias = rng.uniform(0.0, 0.5, 3); prev = rng.uniform(0.1, 1.0, (1, 3, 3))
+    r = O.conv1d(x, w, bias, prev)
+    _close(r["out"], silu_lib(r["out_scale"]), 1e-14, what="conv positive scale")
+    p = _conv_problem(37, 1, 2, 6)
+    r = O.conv1d(p["x"], p["w"], p["bias"], p["x_prev"])
+    seq = np.concatenate([p["x_prev"], p["x"]], -1)
+    for d in range(2):
+        for t in range(6):
+            want = abs(p["bias"][d]) + sum(abs(p["w"][d, k] * seq[0, d, t + k]) for k in range(4))
+            _close(r["out_scale"][0, d, t], want, 1e-14, what="conv mixed scale")
+
+
 PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -47,6 +47,19 @@ MUTANTS = [
      "sv *= fabs(g);\n            }\n            y[row] = yv;"),
     ("step_softplus_dropped", "const double dl = softplus(delta[row]);",
      "const double dl = delta[row];"),
+    ("conv_taps_reversed", "pre += w[d * K + k] * xv;", "pre += w[d * K + (K - 1 - k)] * xv;"),
+    ("conv_window_off_by_one", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t - K + k;"),
+    ("conv_not_causal", "const int64_t s = t - (K - 1) + k;", "const int64_t s = t + k;"),
+    ("conv_prev_order", "(pr ? pr[K - 1 + s] : 0.0);\n                    pre +=",
+     "(pr ? pr[-1 - s] : 0.0);\n                    pre +="),
+    ("conv_bias_dropped", "double pre = bias ? bias[d] : 0.0;\n                double sc",
+     "double pre = 0.0;\n                double sc"),
+    ("conv_no_silu", "out[row * seqlen + t] = silu(pre);", "out[row * seqlen + t] = pre;"),
+    ("conv_scale_signed", "sc += fabs(w[d * K + k] * xv);", "sc += w[d * K + k] * xv;"),
+    ("conv_last_wrong", "x_last[row * (K - 1) + k] = s >= 0 ? xr[s]", "x_last[row * (K - 1) + k] = s > 0 ? xr[s]"),
+    ("conv_step_shift_wrong", "for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];",
+     "for (int64_t k = 0; k + 1 < K - 1; ++k) st[k + 1] = st[k];"),
+    ("conv_step_newest_tap", "pre += w[d * K + K - 1] * x[row];", "pre += w[d * K] * x[row];"),
 ]
 
 
