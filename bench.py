@@ -229,6 +229,64 @@ def time_decode(w, steps, warmup, torch, dev):
     return back_to_back, k_ms / k_n, dist
 
 
+def time_conv(torch, dev, reps=20):
+    """The causal conv1d (width 4) + SiLU over the headline-shaped input
+    (bf16, x_last returned), and its decode step on the decode shape. Kernel
+    times from the library's own events are not taken here: the whole call is
+    one kernel (plus a one-thread-per-row x_last kernel)."""
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    def t(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+
+    out = {}
+    w = W.get(W.HEADLINE)
+    p = W.conv_inputs(w)
+    x, cw, cb = t(p["x"], torch.bfloat16), t(p["w"]), t(p["bias"])
+    y = torch.empty_like(x)
+    last = torch.empty((w.batch, w.dim, 3), dtype=torch.float32, device=dev)
+    run = lambda: selscan.conv1d(x, cw, cb, None, out=y, x_last=last)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 2 * w.elements * 2 + w.rows * 12 + w.dim * 20
+    out["conv1d"] = {"workload": f"conv1d on {w.name}", "us_per_call": round(us, 2),
+                     "Gelem_per_s": round(w.elements / (us * 1e-6) / 1e9, 1),
+                     "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4), "bytes_per_call": nbytes}
+    del x, y, last
+    wd = W.get(W.DECODE)
+    pd = W.conv_inputs(W.scaled(wd, seqlen=1))
+    st = t(pd["x_prev"])
+    cw, cb = t(pd["w"]), t(pd["bias"])
+    xs = [t(W.conv_step_inputs(wd, s), torch.bfloat16) for s in range(16)]
+    yo = torch.empty_like(xs[0])
+    for i in range(4):
+        selscan.conv1d_step(st, xs[i], cw, cb, out=yo)
+    torch.cuda.synchronize(dev)
+    e0.record()
+    for i in range(256):
+        selscan.conv1d_step(st, xs[i % 16], cw, cb, out=yo)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) / 256 * 1e3
+    nbytes = wd.rows * (12 + 12 + 2 + 2) + wd.dim * 20
+    out["conv1d_step"] = {"workload": f"conv1d step on {wd.name}", "us_per_step": round(us, 2),
+                          "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
+                          "bytes_per_step": nbytes}
+    log(f"[bench] conv1d: {out['conv1d']}; step: {out['conv1d_step']}")
+    return out
+
+
 def measured_ceilings(torch, dev):
     """Measured ceilings on this GPU: the device-copy rate (torch copy of
     1 GiB each way, bytes read + written per second) and the rate of the
@@ -334,7 +392,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "copy"], default=None,
                     help="run just one workload (for profiling); copy = counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -417,6 +475,9 @@ def main():
                             "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
                             "cold_p50_GBps": round(step_bytes(wd) / (cold * 1e-6) / 1e9, 1),
                             "bytes_per_step": step_bytes(wd), "per_step": ddist}
+    if not args.no_extras and args.only in (None, "conv"):
+        log("[bench] conv1d: headline shape and decode steps")
+        extras.update(time_conv(torch, dev))
     for key, name in (("long", "long_f32_b1_l1048576_d128"), ("m130m", "m130m_f32_b8_l2048_d1536")):
         if args.no_extras or args.only not in (None, key):
             continue

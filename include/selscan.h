@@ -171,6 +171,52 @@ int selscan_step(float* state, const void* x, const void* delta, const float* A,
                  const selscan_dims_t* dims, void* stream);
 
 /*
+ * selscan_conv1d — the short causal convolution in front of the scan: a
+ * depthwise conv1d of width SELSCAN_CONV_WIDTH (4), then SiLU.
+ *
+ * Defined by: "State Space Models and Mamba" (multigrid.ai), section "What a
+ * Mamba block actually contains" (the SSM branch is a depthwise conv1d of
+ * kernel 4, SiLU, then the selective SSM; the short convolution gives direct
+ * access to the last few tokens) and "Mamba: Linear-Time Sequence Modeling
+ * with Selective State Spaces" (azimuth.plus), the block architecture
+ * (projection, 1D convolution of kernel size 4, SiLU, selective SSM). Causal,
+ * since the block also runs one token at a time (selscan_conv1d_step).
+ *
+ * For every row (b, d) and token t:
+ *   out[b,d,t] = silu(bias[d] + sum_{k=0..3} w[d,k] * xx(t - 3 + k))
+ *   xx(s) = x[b,d,s] for s >= 0, x_prev[b,d,3+s] for s < 0
+ *   x_last[b,d,0..2] = the last three entries of x_prev[b,d,:] ++ x[b,d,:]
+ *
+ * Arguments (device pointers):
+ *   x, out  : [B, d, L] of dtype (L contiguous)
+ *   w       : [d, 4] fp32 (tap k multiplies the input 3 - k tokens back)
+ *   bias    : [d] fp32; NULL means 0
+ *   x_prev  : [B, d, 3] fp32, the three inputs before token 0 (oldest first);
+ *             NULL means zeros (the start of a sequence)
+ *   x_last  : [B, d, 3] fp32 output, NULL means not wanted; it is the x_prev
+ *             of a call that continues this sequence, and the conv_state of
+ *             selscan_conv1d_step. It may be x_prev itself.
+ * dims->dstate is ignored. out must not overlap any input or x_last. No
+ * workspace. Errors as selscan_fwd.
+ */
+#define SELSCAN_CONV_WIDTH 4
+int selscan_conv1d(const void* x, const float* w, const float* bias, const float* x_prev,
+                   void* out, float* x_last, const selscan_dims_t* dims, void* stream);
+
+/*
+ * selscan_conv1d_step — one decode step of the convolution, with the three
+ * previous inputs of every row in conv_state [B, d, 3] fp32 (oldest first),
+ * updated in place (shifted by one, x appended). Same sources as
+ * selscan_conv1d. For every row (b, d):
+ *   out[b,d] = silu(bias[d] + w[d,0]*s0 + w[d,1]*s1 + w[d,2]*s2 + w[d,3]*x[b,d])
+ *   conv_state[b,d,:] = (s1, s2, x[b,d])
+ * x, out: [B, d] of dtype. dims->seqlen and dims->dstate are ignored. Running
+ * L steps from conv_state = x_prev equals selscan_conv1d over the L tokens.
+ */
+int selscan_conv1d_step(float* conv_state, const void* x, const float* w, const float* bias,
+                        void* out, const selscan_dims_t* dims, void* stream);
+
+/*
  * Kernel timing for measurement harnesses. selscan_timing_start(capacity)
  * creates capacity pairs of HIP events (once, reused) and from then on every
  * selscan_fwd / selscan_fwd_ex call records one pair on its stream around its

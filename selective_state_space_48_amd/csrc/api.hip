@@ -19,7 +19,7 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10200;  // 1.2.0
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -299,6 +299,65 @@ int selscan_timing_stop(double* total_ms, int32_t* launches) {
     *total_ms = sum;
     *launches = g_timing.used;
     return SELSCAN_OK;
+}
+
+int selscan_conv1d(const void* x, const float* w, const float* bias, const float* x_prev,
+                   void* out, float* x_last, const selscan_dims_t* dims, void* stream) {
+    if (!dims) return SELSCAN_ERR_NULL;
+    if (dims->batch < 0 || dims->dim < 0 || dims->seqlen < 0) return SELSCAN_ERR_DIMS;
+    if (dims->dtype != SELSCAN_F32 && dims->dtype != SELSCAN_BF16) return SELSCAN_ERR_DTYPE;
+    int64_t rows, seq, t;
+    if (!mul_ok(dims->batch, dims->dim, &rows) || !mul_ok(rows, dims->seqlen, &seq) ||
+        !mul_ok(seq, 4, &t) || !mul_ok(rows, 12, &t) || !mul_ok(dims->dim, 16, &t))
+        return SELSCAN_ERR_DIMS;
+    // grid: one thread per 16-byte vector, blocks of 256, at most 2^32 blocks
+    if (rows > (int64_t(1) << 36) || seq >= (int64_t(1) << 42)) return SELSCAN_ERR_DIMS;
+    if ((seq > 0 && (!x || !out)) || (dims->dim > 0 && !w)) return SELSCAN_ERR_NULL;
+    for (const void* p : {x, (const void*)w, (const void*)bias, (const void*)x_prev, (const void*)out,
+                          (const void*)x_last})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span o = span(out, seq * es), xl = span(x_last, rows * 12);
+    const Span ins[] = {span(x, seq * es), span(w, dims->dim * 16), span(bias, dims->dim * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, o) || overlaps(s, xl)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(o, xl)) return SELSCAN_ERR_ALIAS;
+    const Span xp = span(x_prev, rows * 12);
+    if (overlaps(xp, o)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(xp, xl) && static_cast<const void*>(x_prev) != static_cast<const void*>(x_last))
+        return SELSCAN_ERR_ALIAS;
+    if (rows == 0) return SELSCAN_OK;
+    ConvTensors ct{x, w, bias, x_prev, out, x_last};
+    const hipError_t e = launch_conv(ct, rows, dims->seqlen, dims->dim,
+                                     dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+int selscan_conv1d_step(float* conv_state, const void* x, const float* w, const float* bias,
+                        void* out, const selscan_dims_t* dims, void* stream) {
+    if (!dims) return SELSCAN_ERR_NULL;
+    if (dims->batch < 0 || dims->dim < 0) return SELSCAN_ERR_DIMS;
+    if (dims->dtype != SELSCAN_F32 && dims->dtype != SELSCAN_BF16) return SELSCAN_ERR_DTYPE;
+    int64_t rows, t;
+    if (!mul_ok(dims->batch, dims->dim, &rows) || !mul_ok(rows, 12, &t) || !mul_ok(dims->dim, 16, &t))
+        return SELSCAN_ERR_DIMS;
+    if (rows > (int64_t(1) << 36)) return SELSCAN_ERR_DIMS;
+    if (rows > 0 && (!conv_state || !x || !out || !w)) return SELSCAN_ERR_NULL;
+    for (const void* p : {(const void*)conv_state, x, (const void*)w, (const void*)bias, (const void*)out})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span o = span(out, rows * es), st = span(conv_state, rows * 12);
+    const Span ins[] = {span(x, rows * es), span(w, dims->dim * 16), span(bias, dims->dim * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, o) || overlaps(s, st)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(o, st)) return SELSCAN_ERR_ALIAS;
+    if (rows == 0) return SELSCAN_OK;
+    ConvStepTensors ct{conv_state, x, w, bias, out};
+    const hipError_t e = launch_conv_step(ct, rows, dims->dim,
+                                          dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 
 const char* selscan_strerror(int code) {

@@ -1,0 +1,209 @@
+// Causal depthwise convolution of width 4 followed by SiLU, and its one-token
+// decode step, for gfx950.
+//
+// "State Space Models and Mamba" (multigrid.ai), section "What a Mamba block
+// actually contains": in front of the selective SSM sits a depthwise conv1d of
+// kernel width 4 and a SiLU, which gives the block direct access to the last
+// few tokens; "Mamba: Linear-Time Sequence Modeling with Selective State
+// Spaces" (azimuth.plus), the block architecture (projection, short 1D
+// convolution of size 4, SiLU, selective SSM). Causal, so that the same block
+// can run one token at a time. Per (b, d) row and token t:
+//     out[t] = silu(bias_d + sum_{k<4} w[d,k] * xx(t - 3 + k))
+// where xx(s) is x[s] for s >= 0 and the carried-in input x_prev[3 + s] before
+// the start of the call.
+//
+// The whole operation moves 2 x (element size) bytes per element and does 4
+// FMAs and a sigmoid: it is bound by HBM. Each thread takes one 16-byte
+// vector of consecutive tokens of one row; consecutive lanes take consecutive
+// vectors of the same row, so a wave reads and writes 1 KiB contiguous runs
+// with non-temporal 16-byte accesses. The three inputs before a thread's
+// first token are the last three of the lane below (one cross-lane shift);
+// only lane 0 of a wave and the first vector of a row fetch them otherwise.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace selscan {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct CElem;
+template <> struct CElem<float> { static constexpr int kPer16 = 4; };
+template <> struct CElem<bf16_bits> { static constexpr int kPer16 = 8; };
+
+template <typename T>
+__device__ __forceinline__ void unpack_vec(const u32x4& v, float* o) {
+    if constexpr (sizeof(T) == 4) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    } else {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack_vec(const float* f) {
+    u32x4 v;
+    if constexpr (sizeof(T) == 4) {
+        v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+        v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
+    } else {
+        auto p = [](float a, float b) {
+            return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
+        };
+        v.x = p(f[0], f[1]); v.y = p(f[2], f[3]); v.z = p(f[4], f[5]); v.w = p(f[6], f[7]);
+    }
+    return v;
+}
+
+__device__ __forceinline__ float conv4(const float4& w, float b, float x0, float x1, float x2,
+                                       float x3) {
+    return fmaf(w.w, x3, fmaf(w.z, x2, fmaf(w.y, x1, fmaf(w.x, x0, b))));
+}
+
+// One thread = V consecutive tokens (one 16-byte vector) of one row.
+// VEC: L is a multiple of V, so every vector is whole and 16-byte aligned.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void conv1d_kernel(const T* __restrict__ x,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ bias,
+                                                     const float* __restrict__ x_prev,
+                                                     T* __restrict__ out, int64_t rows, int64_t L,
+                                                     int64_t dim, int64_t nvec) {
+    constexpr int V = CElem<T>::kPer16;
+    const int64_t total = rows * nvec;
+    const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const bool active = gid < total;
+    const int64_t g = active ? gid : total - 1;  // clamped: every lane reads valid memory
+    const int64_t r = g / nvec;
+    const int64_t v = g - r * nvec;
+    const int64_t t0 = v * V;
+    const int64_t d = r % dim;
+    const T* xr = x + r * L;
+
+    float xs[V + 3];  // xs[0..2]: the three inputs before t0; xs[3 + e]: token t0 + e
+    if constexpr (VEC) {
+        unpack_vec<T>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + t0)), xs + 3);
+    } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) xs[3 + e] = t0 + e < L ? to_f32(xr[t0 + e]) : 0.0f;
+    }
+    // The lane below holds the previous vector of the same row whenever v > 0
+    // (only a row's last vector can be partial, and it is never "previous").
+    const float p0 = __shfl_up(xs[V], 1, 64);
+    const float p1 = __shfl_up(xs[V + 1], 1, 64);
+    const float p2 = __shfl_up(xs[V + 2], 1, 64);
+    const int lane = threadIdx.x % 64;
+    if (v == 0) {
+        xs[0] = x_prev ? x_prev[r * 3 + 0] : 0.0f;
+        xs[1] = x_prev ? x_prev[r * 3 + 1] : 0.0f;
+        xs[2] = x_prev ? x_prev[r * 3 + 2] : 0.0f;
+    } else if (lane == 0) {
+        xs[0] = to_f32(xr[t0 - 3]);
+        xs[1] = to_f32(xr[t0 - 2]);
+        xs[2] = to_f32(xr[t0 - 1]);
+    } else {
+        xs[0] = p0; xs[1] = p1; xs[2] = p2;
+    }
+    const float4 wd = *reinterpret_cast<const float4*>(w + d * 4);
+    const float bd = bias ? bias[d] : 0.0f;
+    float o[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[e] = silu(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]));
+    if (!active) return;
+    T* orow = out + r * L;
+    if constexpr (VEC) {
+        __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
+    } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+    }
+}
+
+// x_last[r] = the last three entries of x_prev[r] ++ x[r]; one thread per row.
+// Reads everything before writing, so x_last may be x_prev itself.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_last_kernel(const T* __restrict__ x,
+                                                        const float* x_prev, float* x_last,
+                                                        int64_t rows, int64_t L) {
+    const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (r >= rows) return;
+    float s[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int64_t t = L - 3 + k;
+        s[k] = t >= 0 ? to_f32(x[r * L + t]) : (x_prev ? x_prev[r * 3 + 3 + t] : 0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) x_last[r * 3 + k] = s[k];
+}
+
+// One token per row: out = silu(bias + w . (s0, s1, s2, x)), state <- (s1, s2, x).
+template <typename T>
+__global__ __launch_bounds__(256) void conv_step_kernel(float* __restrict__ state,
+                                                        const T* __restrict__ x,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ bias,
+                                                        T* __restrict__ out, int64_t rows,
+                                                        int64_t dim) {
+    const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const int64_t d = r % dim;
+    const float s0 = state[r * 3 + 0], s1 = state[r * 3 + 1], s2 = state[r * 3 + 2];
+    const float xv = to_f32(x[r]);
+    const float4 wd = *reinterpret_cast<const float4*>(w + d * 4);
+    out[r] = from_f32<T>(silu(conv4(wd, bias ? bias[d] : 0.0f, s0, s1, s2, xv)));
+    state[r * 3 + 0] = s1;
+    state[r * 3 + 1] = s2;
+    state[r * 3 + 2] = xv;
+}
+
+template <typename T>
+hipError_t conv_t(const ConvTensors& t, int64_t rows, int64_t L, int64_t dim, hipStream_t st) {
+    constexpr int V = CElem<T>::kPer16;
+    const T* x = static_cast<const T*>(t.x);
+    if (L > 0) {
+        const int64_t nvec = (L + V - 1) / V;
+        const int64_t blocks = (rows * nvec + 255) / 256;
+        if (L % V == 0)
+            hipLaunchKernelGGL((conv1d_kernel<T, true>), dim3(unsigned(blocks)), dim3(256), 0, st, x,
+                               t.w, t.bias, t.x_prev, static_cast<T*>(t.out), rows, L, dim, nvec);
+        else
+            hipLaunchKernelGGL((conv1d_kernel<T, false>), dim3(unsigned(blocks)), dim3(256), 0, st, x,
+                               t.w, t.bias, t.x_prev, static_cast<T*>(t.out), rows, L, dim, nvec);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (t.x_last) {
+        hipLaunchKernelGGL((conv_last_kernel<T>), dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st,
+                           x, t.x_prev, t.x_last, rows, L);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t conv_step_t(const ConvStepTensors& t, int64_t rows, int64_t dim, hipStream_t st) {
+    hipLaunchKernelGGL((conv_step_kernel<T>), dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st,
+                       t.state, static_cast<const T*>(t.x), t.w, t.bias, static_cast<T*>(t.out),
+                       rows, dim);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvTensors& t, int64_t rows, int64_t L, int64_t dim, DType dtype,
+                       hipStream_t stream) {
+    return dtype == DType::BF16 ? conv_t<bf16_bits>(t, rows, L, dim, stream)
+                                : conv_t<float>(t, rows, L, dim, stream);
+}
+
+hipError_t launch_conv_step(const ConvStepTensors& t, int64_t rows, int64_t dim, DType dtype,
+                            hipStream_t stream) {
+    return dtype == DType::BF16 ? conv_step_t<bf16_bits>(t, rows, dim, stream)
+                                : conv_step_t<float>(t, rows, dim, stream);
+}
+
+}  // namespace selscan

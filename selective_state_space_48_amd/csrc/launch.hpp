@@ -69,4 +69,27 @@ hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType d
                        hipStream_t stream, hipEvent_t ev_begin = nullptr,
                        hipEvent_t ev_end = nullptr);
 
+// Causal depthwise conv (width 4) + SiLU. x/out: [rows, L]; w: [dim, 4];
+// bias: [dim] or null; x_prev/x_last: [rows, 3] fp32 or null.
+struct ConvTensors {
+    const void* x;
+    const float* w;
+    const float* bias;
+    const float* x_prev;
+    void* out;
+    float* x_last;
+};
+hipError_t launch_conv(const ConvTensors& t, int64_t rows, int64_t L, int64_t dim, DType dtype,
+                       hipStream_t stream);
+
+struct ConvStepTensors {
+    float* state;  // [rows, 3], oldest first, updated in place
+    const void* x;
+    const float* w;
+    const float* bias;
+    void* out;
+};
+hipError_t launch_conv_step(const ConvStepTensors& t, int64_t rows, int64_t dim, DType dtype,
+                            hipStream_t stream);
+
 }  // namespace selscan

@@ -65,6 +65,10 @@ def _load() -> ctypes.CDLL:
     lib.selscan_timing_stop.restype = ctypes.c_int
     lib.selscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, dims_p, vp]
     lib.selscan_step.restype = ctypes.c_int
+    lib.selscan_conv1d.argtypes = [vp, fp, fp, fp, vp, fp, dims_p, vp]
+    lib.selscan_conv1d.restype = ctypes.c_int
+    lib.selscan_conv1d_step.argtypes = [fp, vp, fp, fp, vp, dims_p, vp]
+    lib.selscan_conv1d_step.restype = ctypes.c_int
     lib.selscan_strerror.argtypes = [ctypes.c_int]
     lib.selscan_strerror.restype = ctypes.c_char_p
     lib.selscan_version.argtypes = []
@@ -218,3 +222,63 @@ def step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Ten
                           _ptr(z), _ptr(y), ctypes.byref(dims), _stream(dev))
     _check(rc)
     return y
+
+
+CONV_WIDTH = 4
+
+
+def conv1d(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+           x_prev: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
+           x_last: Optional[torch.Tensor] = None,
+           return_x_last: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Causal depthwise conv1d of width 4 + SiLU (selscan_conv1d). Returns (out, x_last).
+
+    ``x`` [batch, dim, L] (float32 or bfloat16); ``w`` [dim, 4] fp32; ``bias``
+    [dim] fp32; ``x_prev`` [batch, dim, 3] fp32, the inputs before token 0
+    (None: zeros). ``x_last`` [batch, dim, 3] fp32 receives the last three
+    inputs (it may be ``x_prev`` itself).
+    """
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    _req(x, "x", x.dtype, (batch, dim, L), dev)
+    _req(w, "w", torch.float32, (dim, CONV_WIDTH), dev)
+    _req(bias, "bias", torch.float32, (dim,), dev)
+    _req(x_prev, "x_prev", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", x.dtype, (batch, dim, L), dev)
+    if x_last is None and return_x_last:
+        x_last = torch.empty((batch, dim, CONV_WIDTH - 1), dtype=torch.float32, device=dev)
+    _req(x_last, "x_last", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
+    dims = Dims(batch, L, dim, 0, _DTYPES[x.dtype])
+    _check(lib.selscan_conv1d(_ptr(x), _ptr(w), _ptr(bias), _ptr(x_prev), _ptr(out), _ptr(x_last),
+                              ctypes.byref(dims), _stream(dev)))
+    return out, x_last
+
+
+def conv1d_step(conv_state: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
+                bias: Optional[torch.Tensor] = None, *,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of the convolution (selscan_conv1d_step): updates
+    ``conv_state`` [batch, dim, 3] fp32 in place and returns out [batch, dim]."""
+    if conv_state.dim() != 3:
+        raise ValueError("conv_state must be [batch, dim, 3]")
+    batch, dim, _ = conv_state.shape
+    dev = conv_state.device
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    _req(conv_state, "conv_state", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
+    _req(x, "x", x.dtype, (batch, dim), dev)
+    _req(w, "w", torch.float32, (dim, CONV_WIDTH), dev)
+    _req(bias, "bias", torch.float32, (dim,), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", x.dtype, (batch, dim), dev)
+    dims = Dims(batch, 1, dim, 0, _DTYPES[x.dtype])
+    _check(lib.selscan_conv1d_step(_ptr(conv_state), _ptr(x), _ptr(w), _ptr(bias), _ptr(out),
+                                   ctypes.byref(dims), _stream(dev)))
+    return out

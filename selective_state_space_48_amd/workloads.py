@@ -14,6 +14,9 @@ discussion; no dataset is involved):
   ``[delta_lo, delta_hi]``: the inverse map ``log(expm1(v))`` is part of this
   input recipe only.
 * ``D`` is 1, or U[0.5, 1.5] where the workload says so.
+* The short convolution in front of the scan: taps ``w[d, k]`` ~ N(0, 0.5^2),
+  ``bias[d]`` ~ N(0, 0.1^2); its input is the workload's ``x``; the carried-in
+  inputs ``x_prev`` [batch, dim, 3] ~ N(0, 1).
 * For bfloat16 workloads every float input is rounded to bfloat16
   (round-to-nearest-even, by torch) before either side sees it; the arrays
   returned here hold those rounded values in float32, which represents them
@@ -30,6 +33,8 @@ import numpy as np
 TID_X, TID_DELTA, TID_Z, TID_B, TID_C, TID_DT_BIAS, TID_D = 0, 1, 2, 3, 4, 5, 6
 TID_PRE_X, TID_PRE_DELTA, TID_PRE_B = 7, 8, 9
 TID_STEP0 = 10  # decode step s uses ids TID_STEP0 + s (sub-stream k = tensor)
+TID_CONV_W, TID_CONV_BIAS, TID_CONV_PREV = 200, 201, 202
+TID_CONV_STEP0 = 300  # convolution decode step s uses id TID_CONV_STEP0 + s
 
 
 @dataclass(frozen=True)
@@ -195,3 +200,28 @@ def random_state(w: Workload, scale: float = 0.1) -> np.ndarray:
         out[b] = _rng(w.seed, TID_PRE_X + 100, b).standard_normal(
             (w.dim, w.dstate), dtype=np.float32) * np.float32(scale)
     return out
+
+
+def conv_inputs(w: Workload, batches: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the causal convolution over the workload's sequence: x [b, dim, L]
+    (the forward's x stream), taps w [dim, 4], bias [dim] and x_prev [b, dim, 3]
+    (bf16-rounded values for bf16 workloads; taps and bias are fp32)."""
+    bs = list(range(w.batch)) if batches is None else list(batches)
+    d, L = w.dim, w.seqlen
+    x = np.empty((len(bs), d, L), np.float32)
+    prev = np.empty((len(bs), d, 3), np.float32)
+    for i, b in enumerate(bs):
+        x[i] = _rng(w.seed, TID_X, b).standard_normal((d, L), dtype=np.float32)
+        prev[i] = _rng(w.seed, TID_CONV_PREV, b).standard_normal((d, 3), dtype=np.float32)
+    return {
+        "x": _maybe_bf16(w, x),
+        "x_prev": _maybe_bf16(w, prev),
+        "w": (_rng(w.seed, TID_CONV_W, 0).standard_normal((d, 4), dtype=np.float32) * 0.5),
+        "bias": (_rng(w.seed, TID_CONV_BIAS, 0).standard_normal(d, dtype=np.float32) * 0.1),
+    }
+
+
+def conv_step_inputs(w: Workload, s: int) -> np.ndarray:
+    """The input token of convolution decode step ``s``: x [batch, dim]."""
+    x = _rng(w.seed, TID_CONV_STEP0 + s, 0).standard_normal((w.batch, w.dim), dtype=np.float32)
+    return _maybe_bf16(w, x)

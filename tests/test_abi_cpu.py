@@ -22,8 +22,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
-            "selscan_timing_start", "selscan_timing_stop", "selscan_strerror",
-            "selscan_version"} <= set(names)
+            "selscan_conv1d", "selscan_conv1d_step", "selscan_timing_start",
+            "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in selscan.h but not exported"
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 def test_error_codes_match_header():
     text = open(HEADER).read()
-    codes = dict((k, int(v)) for k, v in re.findall(r"#define SELSCAN_(\w+) \(?(-?\d+)\)?", text))
+    codes = dict((k, int(v)) for k, v in re.findall(r"#define SELSCAN_(OK|ERR_\w+) \(?(-?\d+)\)?", text))
     assert codes["OK"] == S.OK and codes["ERR_NULL"] == S.ERR_NULL
     assert codes["ERR_DIMS"] == S.ERR_DIMS and codes["ERR_DSTATE"] == S.ERR_DSTATE
     assert codes["ERR_DTYPE"] == S.ERR_DTYPE and codes["ERR_LAUNCH"] == S.ERR_LAUNCH
@@ -42,7 +42,7 @@ def test_error_codes_match_header():
 
 
 def test_version():
-    assert S.version() == 10100
+    assert S.version() == 10200
 
 
 # Fake, 16-byte aligned, non-overlapping device addresses (never dereferenced:
@@ -207,3 +207,55 @@ def test_calibration_library_exports_and_checks():
     assert g(None, P(1), 4, 8, None) == -1
     assert g(P(0), P(1), 0, 8, None) == -2
     assert g(P(0), P(1), 4, 7, None) == -2
+
+
+def conv_call(dims, ptrs=None):
+    p = [P(i) for i in range(6)] if ptrs is None else ptrs
+    return S.lib.selscan_conv1d(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def conv_step_call(dims, ptrs=None):
+    p = [P(i) for i in range(5)] if ptrs is None else ptrs
+    return S.lib.selscan_conv1d_step(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+@pytest.mark.parametrize("call", [conv_call, conv_step_call])
+def test_conv_bad_args(call):
+    assert call(None) == S.ERR_NULL
+    assert call(D(batch=-1)) == S.ERR_DIMS
+    assert call(D(dtype=5)) == S.ERR_DTYPE
+    assert call(D(batch=1 << 40, dim=1 << 40)) == S.ERR_DIMS
+    assert call(D(N=3)) != S.ERR_DSTATE          # dstate is ignored by the convolution
+
+
+def test_conv_null_align_alias():
+    assert conv_call(D(L=-1)) == S.ERR_DIMS
+    for idx in (0, 1, 4):                          # x, w, out are required
+        p = [P(i) for i in range(6)]
+        p[idx] = None
+        assert conv_call(D(), p) == S.ERR_NULL
+    for idx in range(6):
+        p = [P(i) for i in range(6)]
+        p[idx] = ctypes.c_void_p(BASE + idx * SPAN + 8)
+        assert conv_call(D(), p) == S.ERR_ALIGN
+    p = [P(i) for i in range(6)]
+    p[4] = p[0]                                    # out == x
+    assert conv_call(D(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(6)]
+    p[5] = ctypes.c_void_p(BASE + 4 * SPAN + 32)   # x_last inside out
+    assert conv_call(D(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(6)]
+    p[3] = ctypes.c_void_p(BASE + 5 * SPAN + 16)   # x_prev overlapping x_last, not equal
+    assert conv_call(D(), p) == S.ERR_ALIAS
+    for idx in (0, 1, 2, 4):                       # state, x, w, out are required
+        p = [P(i) for i in range(5)]
+        p[idx] = None
+        assert conv_step_call(D(), p) == S.ERR_NULL
+    p = [P(i) for i in range(5)]
+    p[4] = p[1]                                    # out == x
+    assert conv_step_call(D(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(5)]
+    p[0] = p[2]                                    # state == w
+    assert conv_step_call(D(), p) == S.ERR_ALIAS
+    assert conv_call(D(batch=0)) == S.OK           # nothing to do, nothing enqueued
+    assert conv_step_call(D(dim=0)) == S.OK

@@ -57,3 +57,16 @@ def test_step_inputs_shapes():
     assert not np.array_equal(s["x"], s2["x"])
     pre = W.prefill_inputs(w, 2)
     assert pre["x"].shape == (1, 64, 512) and pre["B"].shape == (1, 16, 512)
+
+
+def test_conv_inputs():
+    w = W.scaled(W.get(W.HEADLINE), seqlen=40, dim=16, batch=3)
+    a = W.conv_inputs(w)
+    assert a["x"].shape == (3, 16, 40) and a["x_prev"].shape == (3, 16, 3)
+    assert a["w"].shape == (16, 4) and a["bias"].shape == (16,)
+    assert np.array_equal(a["x"], W.fwd_inputs(w)["x"])      # the forward's x stream
+    part = W.conv_inputs(w, batches=[1])
+    assert np.array_equal(part["x_prev"][0], a["x_prev"][1])
+    t = torch.from_numpy(a["x_prev"])
+    assert torch.equal(t.to(torch.bfloat16).float(), t)
+    assert W.conv_step_inputs(W.get(W.DECODE), 3).shape == (256, 5120)
