@@ -76,12 +76,51 @@ class Oracle:
             [_dp] * 4 + [ctypes.c_int]
         lib.ssm_ref_step.restype = ctypes.c_int
         lib.ssm_ref_step.argtypes = [_dp] * 9 + [ctypes.c_int64] * 3 + [_dp] * 2
+        lib.ssm_ref_bwd.restype = ctypes.c_int
+        lib.ssm_ref_bwd.argtypes = [_dp] * 9 + [ctypes.c_int64] * 4 + [_dp] * 16 + [ctypes.c_int]
         lib.ssm_ref_conv1d.restype = ctypes.c_int
         lib.ssm_ref_conv1d.argtypes = [_dp] * 4 + [ctypes.c_int64] * 4 + [_dp] * 3
         lib.ssm_ref_conv1d_step.restype = ctypes.c_int
         lib.ssm_ref_conv1d_step.argtypes = [_dp] * 4 + [ctypes.c_int64] * 3 + [_dp] * 2
         self.lib = lib
         self.path = path
+
+    def bwd(self, x, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy,
+            nthreads: Optional[int] = None):
+        """Gradients of the forward pass (from a zero state) for an output
+        gradient ``dy`` ``[batch, dim, seqlen]``.
+
+        Returns a dict with ``dx, ddelta, dA, dB, dC`` and, when the matching
+        input is given, ``dD``, ``dz``, ``ddt_bias``; each with a ``<name>_scale``
+        (the same computation on magnitudes). Shapes follow the inputs; dA is
+        ``[dim, dstate]``, dD and ddt_bias ``[dim]``. All float64.
+        """
+        x, delta, A, B, C, dy = map(_f64, (x, delta, A, B, C, dy))
+        D, z, dt_bias = map(_f64, (D, z, dt_bias))
+        batch, dim, L = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and dy.shape == x.shape and A.shape == (dim, N)
+        assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
+        e = lambda *shape: np.zeros(shape, np.float64)
+        out = {k: e(batch, dim, L) for k in ("dx", "ddelta", "dx_scale", "ddelta_scale")}
+        out.update({k: e(batch, N, L) for k in ("dB", "dC", "dB_scale", "dC_scale")})
+        out.update({"dA": e(dim, N), "dA_scale": e(dim, N)})
+        if D is not None:
+            out.update({"dD": e(dim), "dD_scale": e(dim)})
+        if z is not None:
+            out.update({"dz": e(batch, dim, L), "dz_scale": e(batch, dim, L)})
+        if dt_bias is not None:
+            out.update({"ddt_bias": e(dim), "ddt_bias_scale": e(dim)})
+        g = lambda k: _ptr(out.get(k))
+        rc = self.lib.ssm_ref_bwd(
+            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+            _ptr(dy), batch, L, dim, N,
+            g("dx"), g("ddelta"), g("dA"), g("dB"), g("dC"), g("dD"), g("dz"), g("ddt_bias"),
+            g("dx_scale"), g("ddelta_scale"), g("dA_scale"), g("dB_scale"), g("dC_scale"),
+            g("dD_scale"), g("dz_scale"), g("ddt_bias_scale"), nthreads or default_threads())
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_bwd failed with code {rc}")
+        return out
 
     def conv1d(self, x, w, bias=None, x_prev=None):
         """Causal depthwise convolution of width K = w.shape[1], then SiLU.
@@ -218,6 +257,11 @@ def fwd(*args, **kw):
 def step(*args, **kw):
     """One decode step through the built oracle; see ``Oracle.step``."""
     return default().step(*args, **kw)
+
+
+def bwd(*args, **kw):
+    """Backward pass through the built oracle; see ``Oracle.bwd``."""
+    return default().bwd(*args, **kw)
 
 
 def conv1d(*args, **kw):

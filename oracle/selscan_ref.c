@@ -328,3 +328,218 @@ int ssm_ref_conv1d_step(double *conv_state, const double *x, const double *w, co
     }
     return 0;
 }
+
+/*
+ * Backward pass: gradients of a scalar loss whose gradient with respect to y
+ * is dy, through the forward pass defined above (from h = 0).
+ *
+ * "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ * (azimuth.plus), hardware-aware algorithm, recomputation: the backward pass
+ * does not keep the per-token states of the forward pass but recomputes
+ * them; "Mamba State Space Models: Fixed State, Linear Time" (deepnoodle.ai)
+ * likewise. Here the oracle simply recomputes the forward states of a row
+ * into a buffer and walks back through them; the gradients are the chain
+ * rule applied to the definition, written out:
+ *
+ *   g = silu(z), s_t = sum_n C h + D x, y = s g
+ *   dz   = dy * s * silu'(z),  silu'(z) = sig(z) (1 + z (1 - sig(z)))
+ *   ds   = dy * g;  dD += ds * x
+ *   going back in t, with carry[n] = 0 after the last token:
+ *     dh[n] = ds * C[n,t] + carry[n]           (total gradient of h_t[n])
+ *     abar  = exp(dl * A[n]);  q = dh * abar * h_{t-1}[n]
+ *     dA[n] += q * dl;   ddl += q * A[n]        (through the decay)
+ *     dB[n,t] += dh * dl * x;  ddl += dh * B x;  dx += dh * dl * B   (input term)
+ *     dC[n,t] += ds * h_t[n]
+ *     carry[n] = abar * dh
+ *   dx += ds * D;  ddelta = ddl * sig(u)  (softplus' = sigmoid);  ddt_bias += ddelta
+ * dA, dD and ddt_bias sum over batch and time; dB and dC sum over channels.
+ *
+ * Error scales: the same computation on magnitudes (|dy|, |x|, the forward
+ * habs, ...), one per output, as for the forward outputs.
+ *
+ * Layouts as the forward; dA: [dim, dstate]; dD, ddt_bias: [dim];
+ * dB, dC: [batch, dstate, seqlen]. D, z, dt_bias may be null (then dD, dz,
+ * ddt_bias are not written). Batch entries are split over threads; the
+ * per-channel sums are added in batch order afterwards.
+ */
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *D, *z, *dt_bias, *dy;
+    int64_t batch, L, dim, N;
+    double *dx, *ddelta, *dA, *dB, *dC, *dD, *dz, *ddt;       /* values */
+    double *sdx, *sddelta, *sdA, *sdB, *sdC, *sdD, *sdz, *sddt; /* scales */
+    double *pA, *psA, *pD, *psD, *pT, *psT;                    /* per-batch partials */
+    int64_t b0, b1;
+    int rc;
+} bwd_job;
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+static void bwd_batches(bwd_job *j)
+{
+    const int64_t L = j->L, N = j->N, dim = j->dim;
+    double *H = malloc(sizeof(double) * (size_t)(L + 1) * (size_t)N);
+    double *HA = malloc(sizeof(double) * (size_t)(L + 1) * (size_t)N);
+    double *carry = malloc(sizeof(double) * (size_t)N * 2);
+    if (!H || !HA || !carry) { j->rc = -3; free(H); free(HA); free(carry); return; }
+    double *carry_abs = carry + N;
+    for (int64_t b = j->b0; b < j->b1; ++b) {
+        const double *Bb = j->B + b * N * L, *Cb = j->C + b * N * L;
+        double *dBb = j->dB + b * N * L, *dCb = j->dC + b * N * L;
+        double *sdBb = j->sdB + b * N * L, *sdCb = j->sdC + b * N * L;
+        for (int64_t i = 0; i < N * L; ++i) dBb[i] = dCb[i] = sdBb[i] = sdCb[i] = 0.0;
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t row = b * dim + d;
+            const double *x = j->x + row * L, *dr = j->delta + row * L, *dy = j->dy + row * L;
+            const double *z = j->z ? j->z + row * L : NULL;
+            const double *Ad = j->A + d * N;
+            const double bias = j->dt_bias ? j->dt_bias[d] : 0.0;
+            const double Dd = j->D ? j->D[d] : 0.0;
+            /* forward: H[t+1] = h_t, H[0] = h_{-1} = 0 */
+            for (int64_t n = 0; n < N; ++n) H[n] = HA[n] = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const double dl = softplus(dr[t] + bias);
+                for (int64_t n = 0; n < N; ++n) {
+                    const double abar = exp(dl * Ad[n]);
+                    const double bx = dl * Bb[n * L + t] * x[t];
+                    H[(t + 1) * N + n] = abar * H[t * N + n] + bx;
+                    HA[(t + 1) * N + n] = abar * HA[t * N + n] + fabs(bx);
+                }
+            }
+            double dD = 0.0, sD = 0.0, dT = 0.0, sT = 0.0;
+            for (int64_t n = 0; n < N; ++n) carry[n] = carry_abs[n] = 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const double u = dr[t] + bias;
+                const double dl = softplus(u);
+                const double *h = H + (t + 1) * N, *hp = H + t * N;
+                const double *ha = HA + (t + 1) * N, *hpa = HA + t * N;
+                double s = 0.0, sabs = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    s += Cb[n * L + t] * h[n];
+                    sabs += fabs(Cb[n * L + t]) * ha[n];
+                }
+                s += Dd * x[t];
+                sabs += fabs(Dd * x[t]);
+                double g = 1.0;
+                if (z) {
+                    const double sz = sigmoid(z[t]);
+                    const double gp = sz * (1.0 + z[t] * (1.0 - sz));
+                    g = silu(z[t]);
+                    if (j->dz) {
+                        j->dz[row * L + t] = dy[t] * s * gp;
+                        j->sdz[row * L + t] = fabs(dy[t]) * sabs * fabs(gp);
+                    }
+                }
+                const double ds = dy[t] * g, dsa = fabs(ds);
+                dD += ds * x[t];
+                sD += fabs(ds * x[t]);
+                double ddl = 0.0, ddla = 0.0, accB = 0.0, accBa = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double Bv = Bb[n * L + t], Cv = Cb[n * L + t];
+                    const double dh = ds * Cv + carry[n];
+                    const double dha = dsa * fabs(Cv) + carry_abs[n];
+                    const double abar = exp(dl * Ad[n]);
+                    const double q = dh * abar * hp[n];
+                    const double qa = dha * abar * hpa[n];
+                    j->pA[(b * dim + d) * N + n] += q * dl;
+                    j->psA[(b * dim + d) * N + n] += qa * dl;
+                    ddl += q * Ad[n];
+                    ddla += qa * fabs(Ad[n]);
+                    dBb[n * L + t] += dh * dl * x[t];
+                    sdBb[n * L + t] += dha * fabs(dl * x[t]);
+                    accB += dh * Bv;
+                    accBa += dha * fabs(Bv);
+                    dCb[n * L + t] += ds * h[n];
+                    sdCb[n * L + t] += dsa * ha[n];
+                    carry[n] = abar * dh;
+                    carry_abs[n] = abar * dha;
+                }
+                ddl += accB * x[t];
+                ddla += accBa * fabs(x[t]);
+                j->dx[row * L + t] = ds * Dd + dl * accB;
+                j->sdx[row * L + t] = fabs(ds * Dd) + dl * accBa;
+                const double sg = sigmoid(u);
+                j->ddelta[row * L + t] = ddl * sg;
+                j->sddelta[row * L + t] = ddla * sg;
+                dT += ddl * sg;
+                sT += ddla * sg;
+            }
+            j->pD[b * dim + d] = dD;
+            j->psD[b * dim + d] = sD;
+            j->pT[b * dim + d] = dT;
+            j->psT[b * dim + d] = sT;
+        }
+    }
+    free(H); free(HA); free(carry);
+}
+
+static void *bwd_thread(void *p)
+{
+    bwd_batches((bwd_job *)p);
+    return NULL;
+}
+
+int ssm_ref_bwd(const double *x, const double *delta, const double *A, const double *B,
+                const double *C, const double *D, const double *z, const double *dt_bias,
+                const double *dy, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                double *dx, double *ddelta, double *dA, double *dB, double *dC, double *dD,
+                double *dz, double *ddt_bias,
+                double *sdx, double *sddelta, double *sdA, double *sdB, double *sdC, double *sdD,
+                double *sdz, double *sddt_bias, int nthreads)
+{
+    if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return -1;
+    if (!sdx || !sddelta || !sdA || !sdB || !sdC) return -1;
+    if (D && (!dD || !sdD)) return -1;
+    if (dt_bias && (!ddt_bias || !sddt_bias)) return -1;
+    if (z && (!dz || !sdz)) return -1;
+    if (batch < 0 || seqlen < 0 || dim < 0 || dstate <= 0) return -2;
+    const int64_t N = dstate;
+    const size_t nb = (size_t)(batch * dim);
+    double *part = calloc(nb * (size_t)(2 * N + 4) + 1, sizeof(double));
+    if (!part) return -3;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > batch) nthreads = (int)(batch > 0 ? batch : 1);
+    bwd_job proto = {x, delta, A, B, C, D, z, dt_bias, dy, batch, seqlen, dim, N,
+                     dx, ddelta, dA, dB, dC, dD, dz, ddt_bias,
+                     sdx, sddelta, sdA, sdB, sdC, sdD, sdz, sddt_bias,
+                     part, part + nb * N, part + 2 * nb * N, part + 2 * nb * N + nb,
+                     part + 2 * nb * N + 2 * nb, part + 2 * nb * N + 3 * nb, 0, 0, 0};
+    bwd_job *jobs = malloc(sizeof(bwd_job) * (size_t)nthreads);
+    pthread_t *th = malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!jobs || !th) { free(part); free(jobs); free(th); return -3; }
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = proto;
+        jobs[i].b0 = batch * i / nthreads;
+        jobs[i].b1 = batch * (i + 1) / nthreads;
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, bwd_thread, &jobs[i]) != 0) { rc = -3; break; }
+        started = i;
+    }
+    if (rc == 0) bwd_batches(&jobs[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    for (int i = 0; i <= started && rc == 0; ++i)
+        if (jobs[i].rc) rc = jobs[i].rc;
+    /* per-channel sums over batch, in batch order */
+    for (int64_t d = 0; d < dim; ++d) {
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0, s = 0.0;
+            for (int64_t b = 0; b < batch; ++b) {
+                v += proto.pA[(b * dim + d) * N + n];
+                s += proto.psA[(b * dim + d) * N + n];
+            }
+            dA[d * N + n] = v;
+            sdA[d * N + n] = s;
+        }
+        double vD = 0.0, sD = 0.0, vT = 0.0, sT = 0.0;
+        for (int64_t b = 0; b < batch; ++b) {
+            vD += proto.pD[b * dim + d]; sD += proto.psD[b * dim + d];
+            vT += proto.pT[b * dim + d]; sT += proto.psT[b * dim + d];
+        }
+        if (D) { dD[d] = vD; sdD[d] = sD; }
+        if (dt_bias) { ddt_bias[d] = vT; sddt_bias[d] = sT; }
+    }
+    free(part); free(jobs); free(th);
+    return rc;
+}

@@ -536,4 +536,98 @@ def pin_conv1d_scale(O):
             _close(r["out_scale"][0, d, t], want, 1e-14, what="conv mixed scale")
 
 
+# ----------------------------------------------------------------------------
+# Backward pass
+# ----------------------------------------------------------------------------
+
+def _bwd_problem(seed, batch, dim, N, L, gate=True, with_D=True, with_bias=True):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.standard_normal((batch, dim, L)), delta=rng.standard_normal((batch, dim, L)),
+                A=-rng.uniform(0.3, 2.0, (dim, N)), B=rng.standard_normal((batch, N, L)),
+                C=rng.standard_normal((batch, N, L)),
+                D=rng.standard_normal(dim) if with_D else None,
+                z=rng.standard_normal((batch, dim, L)) if gate else None,
+                dt_bias=rng.standard_normal(dim) * 0.5 if with_bias else None,
+                dy=rng.standard_normal((batch, dim, L)))
+
+
+_GRAD_OF = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+            "dt_bias": "ddt_bias"}
+
+
+def _torch_grads(p):
+    """Gradients from torch autograd (fp64) of the forward written with torch
+    ops: a library's chain rule, not the oracle's."""
+    T = {k: (torch.tensor(v, dtype=torch.float64, requires_grad=True) if v is not None else None)
+         for k, v in p.items() if k != "dy"}
+    x, dl, A, B, C = T["x"], T["delta"], T["A"], T["B"], T["C"]
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    u = dl + (T["dt_bias"][None, :, None] if T["dt_bias"] is not None else 0.0)
+    delta = torch.nn.functional.softplus(u)
+    h = torch.zeros((batch, dim, N), dtype=torch.float64)
+    ys = []
+    for t in range(L):
+        abar = torch.exp(delta[:, :, t, None] * A[None])
+        h = abar * h + delta[:, :, t, None] * B[:, None, :, t] * x[:, :, t, None]
+        yt = (h * C[:, None, :, t]).sum(-1)
+        if T["D"] is not None:
+            yt = yt + T["D"][None] * x[:, :, t]
+        ys.append(yt)
+    y = torch.stack(ys, -1)
+    if T["z"] is not None:
+        y = y * torch.nn.functional.silu(T["z"])
+    y.backward(torch.tensor(p["dy"]))
+    return {_GRAD_OF[k]: v.grad.numpy() for k, v in T.items() if v is not None}
+
+
+def pin_bwd_torch_autograd(O):
+    """Every gradient against torch autograd of the same forward in fp64, with
+    and without the optional inputs."""
+    for kw in (dict(), dict(gate=False, with_D=False, with_bias=False)):
+        p = _bwd_problem(41, 2, 3, 4, 17, **kw)
+        r = O.bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"],
+                  dy=p["dy"])
+        ref = _torch_grads(p)
+        for k, v in ref.items():
+            _close(r[k], v, 1e-10, scale=r[k + "_scale"] + 1e-300, what=f"bwd autograd {k} {kw}")
+        for k in ("dD", "dz", "ddt_bias"):
+            assert (k in r) == (k in ref), k
+
+
+def pin_bwd_finite_differences(O):
+    """Central differences of the loss sum(dy * y) through the oracle's own
+    forward pass, every element of every input, on a tiny problem."""
+    p = _bwd_problem(42, 2, 2, 3, 5)
+    r = O.bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"], dy=p["dy"])
+
+    def loss(q):
+        y = O.fwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"], q["dt_bias"])["y"]
+        return float(np.sum(p["dy"] * y))
+
+    for name, gname in _GRAD_OF.items():
+        base = p[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[idx]))
+            q = dict(p); arr = base.copy(); arr[idx] += eps; q[name] = arr
+            lp = loss(q)
+            arr = base.copy(); arr[idx] -= eps; q[name] = arr
+            lm = loss(q)
+            fd[idx] = (lp - lm) / (2 * eps)
+        _close(r[gname], fd, 1e-6, scale=np.maximum(np.abs(fd), 1.0), what=f"bwd finite diff {gname}")
+
+
+def pin_bwd_scales_bound_values(O):
+    """Each error scale is at least the magnitude of its value, and the
+    gradients are linear in dy (doubling dy doubles every gradient exactly)."""
+    p = _bwd_problem(43, 2, 3, 5, 11)
+    args = (p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"])
+    r = O.bwd(*args, dy=p["dy"])
+    r2 = O.bwd(*args, dy=2.0 * p["dy"])
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias"):
+        assert np.all(r[k + "_scale"] >= np.abs(r[k]) * (1 - 1e-12)), k
+        _close(r2[k], 2.0 * r[k], 0.0, what=f"bwd linear in dy {k}")
+
+
 PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -60,6 +60,19 @@ MUTANTS = [
     ("conv_step_shift_wrong", "for (int64_t k = 0; k + 1 < K - 1; ++k) st[k] = st[k + 1];",
      "for (int64_t k = 0; k + 1 < K - 1; ++k) st[k + 1] = st[k];"),
     ("conv_step_newest_tap", "pre += w[d * K + K - 1] * x[row];", "pre += w[d * K] * x[row];"),
+    ("bwd_dA_sign", "j->pA[(b * dim + d) * N + n] += q * dl;", "j->pA[(b * dim + d) * N + n] -= q * dl;"),
+    ("bwd_carry_no_decay", "carry[n] = abar * dh;", "carry[n] = dh;"),
+    ("bwd_q_uses_h_t", "const double q = dh * abar * hp[n];", "const double q = dh * abar * h[n];"),
+    ("bwd_dB_no_dl", "dBb[n * L + t] += dh * dl * x[t];", "dBb[n * L + t] += dh * x[t];"),
+    ("bwd_dC_prev_state", "dCb[n * L + t] += ds * h[n];", "dCb[n * L + t] += ds * hp[n];"),
+    ("bwd_ddelta_no_sigmoid", "j->ddelta[row * L + t] = ddl * sg;", "j->ddelta[row * L + t] = ddl;"),
+    ("bwd_dx_no_D", "j->dx[row * L + t] = ds * Dd + dl * accB;", "j->dx[row * L + t] = dl * accB;"),
+    ("bwd_dz_uses_silu", "j->dz[row * L + t] = dy[t] * s * gp;", "j->dz[row * L + t] = dy[t] * s * g;"),
+    ("bwd_ds_no_gate", "const double ds = dy[t] * g, dsa = fabs(ds);", "const double ds = dy[t], dsa = fabs(ds);"),
+    ("bwd_decay_term_dropped", "ddl += q * Ad[n];", "ddl += 0.0 * Ad[n];"),
+    ("bwd_dD_ungated", "dD += ds * x[t];", "dD += dy[t] * x[t];"),
+    ("bwd_dt_bias_no_sigmoid", "dT += ddl * sg;", "dT += ddl;"),
+    ("bwd_dx_scale_no_D", "j->sdx[row * L + t] = fabs(ds * Dd) + dl * accBa;", "j->sdx[row * L + t] = dl * accBa;"),
 ]
 
 
