@@ -425,8 +425,12 @@ static void bwd_batches(bwd_job *j)
                     const double gp = sz * (1.0 + z[t] * (1.0 - sz));
                     g = silu(z[t]);
                     if (j->dz) {
+                        /* silu'(z) is formed as sig + z sig (1 - sig), a sum that
+                           crosses zero (near z = -1.28): its scale is the sum of
+                           the magnitudes of those two terms. */
+                        const double gpa = sz * (1.0 + fabs(z[t]) * (1.0 - sz));
                         j->dz[row * L + t] = dy[t] * s * gp;
-                        j->sdz[row * L + t] = fabs(dy[t]) * sabs * fabs(gp);
+                        j->sdz[row * L + t] = fabs(dy[t]) * sabs * gpa;
                     }
                 }
                 const double ds = dy[t] * g, dsa = fabs(ds);
