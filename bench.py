@@ -229,6 +229,37 @@ def time_decode(w, steps, warmup, torch, dev):
     return back_to_back, k_ms / k_n, dist
 
 
+def time_bwd(torch, dev, reps=5):
+    """The backward pass on the headline shape (bf16, gate, D, dt_bias): all
+    eight gradients for a synthetic dy, whole call (checkpoint pass, reverse
+    pass, fixed-order reductions, workspace on the stream)."""
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    w = W.get(W.HEADLINE)
+    d = device_inputs(w, torch, dev)
+    dy = torch.randn(d["x"].shape, generator=torch.Generator().manual_seed(8)).to(dev).to(torch.bfloat16)
+    run = lambda: selscan.bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                              dt_bias=d["dt_bias"], dy=dy)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / reps
+    # algorithmic bytes: read x, delta, z, dy, B, C; write dx, ddelta, dz, dB, dC
+    nbytes = 7 * w.elements * 2 + 4 * w.batch * w.dstate * w.seqlen * 2
+    del d, dy
+    return {"workload": f"backward on {w.name}", "ms_per_call": round(ms, 4),
+            "Gelem_per_s": round(w.elements / (ms * 1e-3) / 1e9, 2),
+            "ratio_to_forward": None, "algorithmic_bytes": nbytes,
+            "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
+
+
 def time_conv(torch, dev, reps=20):
     """The causal conv1d (width 4) + SiLU over the headline-shaped input
     (bf16, x_last returned), and its decode step on the decode shape. Kernel
@@ -392,7 +423,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "bwd", "copy"],
+                    default=None,
                     help="run just one workload (for profiling); copy = counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -475,6 +507,10 @@ def main():
                             "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
                             "cold_p50_GBps": round(step_bytes(wd) / (cold * 1e-6) / 1e9, 1),
                             "bytes_per_step": step_bytes(wd), "per_step": ddist}
+    if not args.no_extras and args.only in (None, "bwd"):
+        log("[bench] backward: headline shape")
+        extras["bwd"] = time_bwd(torch, dev)
+        log(f"[bench] backward: {extras['bwd']}")
     if not args.no_extras and args.only in (None, "conv"):
         log("[bench] conv1d: headline shape and decode steps")
         extras.update(time_conv(torch, dev))

@@ -171,6 +171,44 @@ int selscan_step(float* state, const void* x, const void* delta, const float* A,
                  const selscan_dims_t* dims, void* stream);
 
 /*
+ * selscan_bwd — gradients of the forward pass (from a zero state) for an
+ * output gradient dy.
+ *
+ * Defined by: the chain rule through the recurrence of selscan_fwd ("State
+ * Space Models and Mamba" (multigrid.ai), section "Selective state: the
+ * change that made it work on text"), evaluated as "Mamba: Linear-Time
+ * Sequence Modeling with Selective State Spaces" (azimuth.plus), hardware-
+ * aware algorithm, prescribes: the per-token states are recomputed in the
+ * backward pass rather than stored (here from a checkpoint every 16 tokens).
+ * With g = silu(z), s = sum_n C h + D x, y = s g, and going back in time with
+ * dh[n] = dy g C[n,t] + exp(delta_{t+1} A[n]) dh_{t+1}[n]:
+ *   dz      = dy * s * silu'(z)
+ *   dx      = dy g D + delta sum_n dh[n] B[n,t]
+ *   ddelta  = (x sum_n dh[n] B[n,t] + sum_n dh[n] exp(delta A[n]) h_{t-1}[n] A[n])
+ *             * sigmoid(delta_raw + dt_bias)             (gradient of delta_raw)
+ *   dA[d,n] = sum_{b,t} dh[n] exp(delta A[n]) h_{t-1}[n] delta
+ *   dB[b,n,t] = sum_d dh[n] delta x;   dC[b,n,t] = sum_d dy g h_t[n]
+ *   dD[d]   = sum_{b,t} dy g x;   ddt_bias[d] = sum_{b,t} ddelta
+ *
+ * Arguments (device pointers), inputs exactly as selscan_fwd, plus:
+ *   dy                 : [B, d, L] of dtype
+ *   dx, ddelta         : [B, d, L] of dtype (outputs)
+ *   dz                 : [B, d, L] of dtype, required when z is given, else NULL
+ *   dB, dC             : [B, N, L] of dtype (outputs)
+ *   dA                 : [d, N] fp32 (output)
+ *   dD, ddt_bias       : [d] fp32 outputs, NULL when not wanted (computed
+ *                        whether or not D / dt_bias are given)
+ * Workspace: about (B d ceil(L/16) + 2 B ceil(d/64) ceil(L/16) 16) * 64 bytes
+ * (checkpoints and per-row-block partial sums; 0.4 GB at B 8, L 2048, d 4096),
+ * taken with hipMallocAsync on the stream and returned with hipFreeAsync.
+ * Outputs must not overlap inputs or each other. Deterministic.
+ */
+int selscan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,
+                void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias,
+                const selscan_dims_t* dims, void* stream);
+
+/*
  * selscan_conv1d — the short causal convolution in front of the scan: a
  * depthwise conv1d of width SELSCAN_CONV_WIDTH (4), then SiLU.
  *

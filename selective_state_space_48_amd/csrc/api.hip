@@ -19,7 +19,7 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
 
 namespace {
 
-constexpr int kVersion = 10200;  // 1.2.0
+constexpr int kVersion = 10300;  // 1.3.0
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -299,6 +299,59 @@ int selscan_timing_stop(double* total_ms, int32_t* launches) {
     *total_ms = sum;
     *launches = g_timing.used;
     return SELSCAN_OK;
+}
+
+int selscan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,
+                void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias,
+                const selscan_dims_t* dims, void* stream) {
+    Sizes sz;
+    int rc = check_fwd_dims(dims, &sz);
+    if (rc != SELSCAN_OK) return rc;
+    const int64_t L = dims->seqlen;
+    if ((sz.seq > 0 && (!x || !delta || !dy || !dx || !ddelta)) || (sz.bc > 0 && (!B || !C || !dB || !dC)) ||
+        (sz.param > 0 && (!A || !dA)))
+        return SELSCAN_ERR_NULL;
+    if (z && sz.seq > 0 && !dz) return SELSCAN_ERR_NULL;
+    if (!z && dz) return SELSCAN_ERR_NULL;  // dz has no meaning without a gate
+    for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, dy,
+                          (const void*)dx, (const void*)ddelta, (const void*)dA, (const void*)dB,
+                          (const void*)dC, (const void*)dD, (const void*)dz, (const void*)ddt_bias})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span outs[] = {span(dx, sz.seq * es), span(ddelta, sz.seq * es), span(dz, sz.seq * es),
+                         span(dB, sz.bc * es),  span(dC, sz.bc * es),     span(dA, sz.param * 4),
+                         span(dD, dims->dim * 4), span(ddt_bias, dims->dim * 4)};
+    const Span ins[] = {span(x, sz.seq * es), span(delta, sz.seq * es), span(z, sz.seq * es),
+                        span(dy, sz.seq * es), span(B, sz.bc * es),     span(C, sz.bc * es),
+                        span(A, sz.param * 4), span(D, dims->dim * 4),  span(dt_bias, dims->dim * 4)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span& s : ins)
+            if (overlaps(s, outs[i])) return SELSCAN_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlaps(outs[i], outs[j])) return SELSCAN_ERR_ALIAS;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sz.rows == 0 || L == 0) {  // no terms: the per-channel sums are zero
+        if (launch_fill_zero(dA, sz.param, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        if (dD && launch_fill_zero(dD, dims->dim, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        if (ddt_bias && launch_fill_zero(ddt_bias, dims->dim, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        return SELSCAN_OK;
+    }
+    if ((L + 15) / 16 * ((dims->dim + kWave - 1) / kWave) > INT32_MAX ||
+        ((dims->dim + kWave - 1) / kWave) * dims->batch > INT32_MAX)
+        return SELSCAN_ERR_DIMS;
+    const size_t ws_bytes = bwd_workspace_bytes(dims->batch, L, dims->dim);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return SELSCAN_ERR_ALLOC;
+    }
+    BwdTensors t{x, delta, A, B, C, D, z, dt_bias, dy, dx, ddelta, dA, dB, dC, dD, dz, ddt_bias};
+    const hipError_t e = launch_bwd(t, dims->batch, L, dims->dim,
+                                    dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32, ws, st);
+    (void)hipFreeAsync(ws, st);
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 
 int selscan_conv1d(const void* x, const float* w, const float* bias, const float* x_prev,

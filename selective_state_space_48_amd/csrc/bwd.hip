@@ -1,0 +1,557 @@
+// Backward pass of the selective scan (S6) for gfx950.
+//
+// The gradients of the forward pass (from a zero state) for an output
+// gradient dy, by the chain rule through the recurrence of "State Space
+// Models and Mamba" (multigrid.ai), section "Selective state: the change that
+// made it work on text". Following "Mamba: Linear-Time Sequence Modeling with
+// Selective State Spaces" (azimuth.plus), hardware-aware algorithm,
+// recomputation, the per-token states are never stored: a checkpoint pass
+// (the forward kernel's third mode) keeps the state before every 16th token
+// (1/16 of the states) and computes dz; this file's reverse pass then walks
+// the 16-token chunks from last to first, recomputing each chunk's states and
+// decays into registers from its checkpoint and sweeping back through them.
+//
+// Per (b, d) row, going back in t with carry[n] = 0 after the last token:
+//     ds = dy * silu(z)
+//     dh[n] = ds C[n,t] + carry[n];   carry[n] = abar[n,t] dh[n]
+//     q = carry[n] h_{t-1}[n]                  (= dh * abar * h_{t-1})
+//     dA[n] += q delta;  ddelta_t += q A[n] + x dh[n] B[n,t]
+//     dx_t  += dh[n] delta B[n,t];  dB[n,t] += dh[n] delta x;  dC[n,t] += ds h_t[n]
+//     dx_t  += ds D;  draw_t = ddelta_t * sigmoid(delta_raw + dt_bias);  ddt_bias += draw_t
+//
+// Mapping, as in the forward kernel: a workgroup owns 64 rows of one batch
+// entry, one lane per row, and its 4 waves own 4 states each. B and C
+// (packed by the checkpoint pass, B times ln 2) are staged per chunk in LDS
+// and read as broadcasts (scalar operands would need more SGPRs than the
+// reverse sweep leaves). The
+// per-token work (softplus, the gate, the sums over states into dx and
+// ddelta) is spread over all 256 threads by token slices and shared through
+// LDS. dB and dC sum over the 64 rows of a wave: each 4-token sub-block's 16
+// values per lane are reduced across the wave with the gfx950 lane-swap
+// instructions (v_permlane32_swap, v_permlane16_swap) and row rotations
+// (DPP), then the row blocks' partial sums are added in a fixed order by a
+// second kernel, as are the per-channel sums (dA, dD, ddt_bias) over the
+// batch. Every sum has a fixed order: the results are deterministic.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace selscan {
+namespace {
+
+constexpr int kBCH = 16;                // tokens per reverse chunk (= checkpoint spacing)
+constexpr int kBG = 4;                  // waves per 64-row block
+constexpr int kBNG = kN / kBG;          // states per wave
+constexpr int kBSB = 4;                 // tokens per packed sub-block (= waves)
+constexpr int kBNSB = kBCH / kBSB;      // sub-blocks per chunk
+constexpr int kBTS = kBCH / kBG;        // tokens per thread in the per-token phases
+constexpr int kRecF = 32;               // floats per packed (b, sub-block, wave) record
+
+struct BwdKArgs {
+    const void* x;
+    const void* delta;
+    const void* z;
+    const void* dy;
+    const float* A;
+    const float* P;      // packed B (times ln 2) / C records, as in the forward
+    const float* D;
+    const float* dt_bias;
+    const float* ckpt;   // [nck][batch*dim][N]
+    void* dx;
+    void* ddelta;
+    float* pB;           // [row_blocks][batch][Lp][N]: sum over the block's rows of dh * l x
+    float* pC;           // [row_blocks][batch][Lp][N]: sum over the block's rows of ds * h
+    float* pA;           // [batch*dim][N]: sum over t of q * l
+    float* pD;           // [batch*dim]
+    float* pT;           // [batch*dim]
+    int64_t batch, L, dim, Lp, psub;
+    int32_t row_blocks, nck;
+};
+
+// LDS: per-token (l, w) and ds of the chunk for the scan waves, and the
+// waves' per-token partial sums over their states (sum q A, sum dh B').
+// Row strides are odd multiples of 16 bytes.
+struct alignas(16) BwdSmem {
+    static constexpr int kLW = kBCH * 8 + 16;
+    static constexpr int kDS = kBCH * 4 + 16;
+    unsigned char lw[kWave * kLW];
+    unsigned char ds[kWave * kDS];
+    unsigned char part[kBG][kWave * kLW];
+    float bc[kBNSB * kBG * kRecF];  // the chunk's packed B/C records, as laid out in P
+};
+
+// 4 consecutive tokens of type T as one load: 16 bytes (fp32) or 8 (bf16).
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+    using V = uint4;
+    static __device__ __forceinline__ V load(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ void unpack(const V& v, float* o) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+    static __device__ __forceinline__ V pack(const float* f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
+    }
+    static __device__ __forceinline__ void store(float* p, const V& v) { *reinterpret_cast<uint4*>(p) = v; }
+};
+template <> struct Quad<bf16_bits> {
+    using V = uint2;
+    static __device__ __forceinline__ V load(const bf16_bits* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ void unpack(const V& v, float* o) {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    }
+    static __device__ __forceinline__ V pack(const float* f) {
+        auto p = [](float a, float b) {
+            return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
+        };
+        return make_uint2(p(f[0], f[1]), p(f[2], f[3]));
+    }
+    static __device__ __forceinline__ void store(bf16_bits* p, const V& v) { *reinterpret_cast<uint2*>(p) = v; }
+};
+
+// Sum of a over lanes {l, l^32} in lanes 0..31 and of b in lanes 32..63.
+__device__ __forceinline__ float fold32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum of a over lanes {l, l^16} in even 16-lane rows and of b in odd rows.
+__device__ __forceinline__ float fold16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum over the 16 lanes of a row, in every lane of it (rotations by 8, 4, 2, 1).
+__device__ __forceinline__ float rowsum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));
+    return v;
+}
+// v[4e + j] (token e, state j) summed over the 64 lanes of the wave. Lane l
+// returns, in o[0..3], the sums of token e = l / 16 for states 0..3.
+__device__ __forceinline__ void wave_sum16(const float* v, float* o) {
+    float u[8], w[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = fold32(v[i], v[i + 8]);   // index i + 8*(l/32)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = fold16(u[i], u[i + 4]);   // index i + 4*((l/16)%2) + 8*(l/32)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = rowsum16(w[i]);
+}
+
+template <typename T, bool GATE, bool VEC>
+__global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
+    using Q = Quad<T>;
+    using S = BwdSmem;
+    __shared__ S sm;
+    const T* __restrict__ X = static_cast<const T*>(a.x);
+    const T* __restrict__ DL = static_cast<const T*>(a.delta);
+    const T* __restrict__ Z = static_cast<const T*>(a.z);
+    const T* __restrict__ DY = static_cast<const T*>(a.dy);
+
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int rb = int(blockIdx.x % unsigned(a.row_blocks));
+    const int64_t b = int64_t(blockIdx.x / unsigned(a.row_blocks));
+    const int64_t rows = a.batch * a.dim;
+
+    // scan mapping: lane = row, wave = 4 states
+    const int64_t d0 = int64_t(rb) * kWave;
+    const int64_t d = d0 + lane;
+    const bool row_ok = d < a.dim;
+    const int64_t row = b * a.dim + (row_ok ? d : d0);
+    const int n0 = wv * kBNG;
+    float An[kBNG];
+#pragma unroll
+    for (int j = 0; j < kBNG; ++j) An[j] = row_ok ? a.A[d * kN + n0 + j] : 0.0f;
+
+    // per-token mapping: thread (pr, pq) = row pr, tokens [4 pq, 4 pq + 4) of a chunk
+    const int pr = tid / kBG, pq = tid % kBG;
+    const int64_t dp = d0 + pr;
+    const bool prow_ok = dp < a.dim;
+    const int64_t prow = b * a.dim + (prow_ok ? dp : d0);
+    const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;
+    const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
+
+    struct In {
+        typename Q::V x, d, z, g;
+        float2 bc;  // 8 bytes of the chunk's packed B/C records
+    };
+    // The chunk's records are one contiguous 2 KiB block of P: 8 bytes a thread.
+    const float* Pb = a.P + b * a.psub * kBG * kRecF;
+    auto load = [&](int c, In& in) {
+        in.bc = reinterpret_cast<const float2*>(Pb + int64_t(c) * (kBNSB * kBG * kRecF))[tid];
+        const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
+        const int64_t off = prow * a.L + t0;
+        if (VEC && t0 + kBTS <= a.L) {
+            in.x = Q::load(X + off);
+            in.d = Q::load(DL + off);
+            if constexpr (GATE) in.z = Q::load(Z + off);
+            in.g = Q::load(DY + off);
+        } else {
+            float fx[4], fd[4], fz[4], fg[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = t0 + e < a.L;
+                fx[e] = ok ? to_f32(X[off + e]) : 0.0f;
+                fd[e] = ok ? to_f32(DL[off + e]) : 0.0f;
+                fz[e] = (GATE && ok) ? to_f32(Z[off + e]) : 0.0f;
+                fg[e] = ok ? to_f32(DY[off + e]) : 0.0f;
+            }
+            in.x = Q::pack(fx);
+            in.d = Q::pack(fd);
+            in.z = Q::pack(fz);
+            in.g = Q::pack(fg);
+        }
+    };
+    // Values a per-token thread keeps from its prologue to its epilogue of the
+    // same chunk: x, ds, sigmoid(u), l.
+    struct Keep {
+        float x[kBTS], ds[kBTS], sg[kBTS], l[kBTS];
+    };
+    // ---- per-token prologue of chunk c: (l, w) and ds to LDS ----
+    auto prologue = [&](int c, const In& in, Keep& k) {
+        const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
+        float xs[4], us[4], zs[4], gs[4];
+        Q::unpack(in.x, xs);
+        Q::unpack(in.d, us);
+        Q::unpack(in.g, gs);
+        if constexpr (GATE) Q::unpack(in.z, zs);
+        float l[4], w[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = prow_ok && t0 + e < a.L;
+            const float ul = fmaf(us[e], kLog2e, biasl);
+            const float lv = softplus_log2_of(ul);
+            l[e] = ok ? lv : 0.0f;
+            w[e] = l[e] * xs[e];
+            const float g = GATE ? silu(zs[e]) : 1.0f;
+            dsv[e] = ok ? gs[e] * g : 0.0f;
+            k.x[e] = xs[e];
+            k.ds[e] = dsv[e];
+            k.sg[e] = exp2_hw(ul - lv);  // sigmoid(u) = e^u / (1 + e^u)
+            k.l[e] = l[e];
+        }
+        float4* lwr = reinterpret_cast<float4*>(&sm.lw[pr * S::kLW]) + pq * 2;
+        lwr[0] = make_float4(l[0], w[0], l[1], w[1]);
+        lwr[1] = make_float4(l[2], w[2], l[3], w[3]);
+        *(reinterpret_cast<float4*>(&sm.ds[pr * S::kDS]) + pq) = make_float4(dsv[0], dsv[1], dsv[2], dsv[3]);
+        reinterpret_cast<float2*>(sm.bc)[tid] = in.bc;
+    };
+
+    float carry[kBNG], dAacc[kBNG];
+#pragma unroll
+    for (int j = 0; j < kBNG; ++j) carry[j] = dAacc[j] = 0.0f;
+
+    // ---- the scan waves on chunk c: recompute, then sweep back ----
+    // The states of the chunk are recomputed from its checkpoint into
+    // registers (h_t for the 16 tokens); the decays are recomputed again on
+    // the way back rather than kept. B and C come from LDS (broadcast reads).
+    auto scan_chunk = [&](int c) {
+        const float4 hs4 = *reinterpret_cast<const float4*>(a.ckpt + (int64_t(c) * rows + row) * kN + n0);
+        const float hs[kBNG] = {hs4.x, hs4.y, hs4.z, hs4.w};
+        const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kLW]);
+        const float* dsr = reinterpret_cast<const float*>(&sm.ds[lane * S::kDS]);
+        auto rec = [&](int sb) { return reinterpret_cast<const float4*>(sm.bc + (sb * kBG + wv) * kRecF); };
+        float H[kBCH][kBNG];
+        float h[kBNG] = {hs[0], hs[1], hs[2], hs[3]};
+#pragma unroll
+        for (int sb = 0; sb < kBNSB; ++sb) {
+            float Bv[16];
+            const float4* r = rec(sb);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = r[q];
+                Bv[4 * q] = v.x; Bv[4 * q + 1] = v.y; Bv[4 * q + 2] = v.z; Bv[4 * q + 3] = v.w;
+            }
+#pragma unroll
+            for (int e = 0; e < kBSB; ++e) {
+                const int t = sb * kBSB + e;
+                const float2 lw = lw2[t];
+#pragma unroll
+                for (int j = 0; j < kBNG; ++j) {
+                    h[j] = fmaf(exp2_hw(lw.x * An[j]), h[j], lw.y * Bv[j * kBSB + e]);
+                    H[t][j] = h[j];
+                }
+            }
+        }
+        float2* prt = reinterpret_cast<float2*>(&sm.part[wv][lane * S::kLW]);
+#pragma unroll
+        for (int sb = kBNSB - 1; sb >= 0; --sb) {
+            float Bv[16], Cv[16];
+            const float4* r = rec(sb);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = r[q], w = r[4 + q];
+                Bv[4 * q] = v.x; Bv[4 * q + 1] = v.y; Bv[4 * q + 2] = v.z; Bv[4 * q + 3] = v.w;
+                Cv[4 * q] = w.x; Cv[4 * q + 1] = w.y; Cv[4 * q + 2] = w.z; Cv[4 * q + 3] = w.w;
+            }
+            float vB[16], vC[16];
+#pragma unroll
+            for (int e = kBSB - 1; e >= 0; --e) {
+                const int t = sb * kBSB + e;
+                const float2 lw = lw2[t];
+                const float ds = dsr[t];
+                float accA = 0.0f, accB = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kBNG; ++j) {
+                    const float dh = fmaf(ds, Cv[j * kBSB + e], carry[j]);
+                    carry[j] = exp2_hw(lw.x * An[j]) * dh;
+                    const float q = carry[j] * (t > 0 ? H[t - 1][j] : hs[j]);
+                    accA = fmaf(q, An[j], accA);
+                    dAacc[j] = fmaf(q, lw.x, dAacc[j]);
+                    accB = fmaf(dh, Bv[j * kBSB + e], accB);
+                    vB[e * 4 + j] = dh * lw.y;
+                    vC[e * 4 + j] = ds * H[t][j];
+                }
+                prt[t] = make_float2(accA, accB);
+            }
+            float sB[4], sC[4];
+            wave_sum16(vB, sB);
+            wave_sum16(vC, sC);
+            if ((lane & 15) == 0) {
+                const int64_t t = int64_t(c) * kBCH + sb * kBSB + (lane >> 4);
+                const int64_t o = ((int64_t(rb) * a.batch + b) * a.Lp + t) * kN + n0;
+                *reinterpret_cast<float4*>(a.pB + o) = make_float4(sB[0], sB[1], sB[2], sB[3]);
+                *reinterpret_cast<float4*>(a.pC + o) = make_float4(sC[0], sC[1], sC[2], sC[3]);
+            }
+        }
+    };
+
+    float dDacc = 0.0f, dTacc = 0.0f;
+    // ---- per-token epilogue of chunk c: sums over the waves, dx, ddelta ----
+    auto epilogue = [&](int c, const Keep& k) {
+        const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
+        float dxv[4], ddv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float AA = 0.0f, BB = 0.0f;
+#pragma unroll
+            for (int g = 0; g < kBG; ++g) {
+                const float2 p = reinterpret_cast<const float2*>(&sm.part[g][pr * S::kLW])[pq * kBTS + e];
+                AA += p.x;
+                BB += p.y;
+            }
+            // B was packed times ln 2: BB = ln2 * sum dh B, and delta = l ln 2.
+            const float ddl = fmaf(k.x[e] * BB, kLog2e, AA);
+            dxv[e] = fmaf(k.l[e], BB, k.ds[e] * Dd);
+            ddv[e] = ddl * k.sg[e];
+            if (t0 + e < a.L) {
+                dDacc = fmaf(k.ds[e], k.x[e], dDacc);
+                dTacc += ddv[e];
+            }
+        }
+        if (!prow_ok) return;
+        const int64_t off = prow * a.L + t0;
+        T* DXo = static_cast<T*>(a.dx);
+        T* DDo = static_cast<T*>(a.ddelta);
+        if (VEC && t0 + kBTS <= a.L) {
+            Q::store(DXo + off, Q::pack(dxv));
+            Q::store(DDo + off, Q::pack(ddv));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (t0 + e < a.L) {
+                    DXo[off + e] = from_f32<T>(dxv[e]);
+                    DDo[off + e] = from_f32<T>(ddv[e]);
+                }
+        }
+    };
+
+    // Chunks from last to first. Inputs are loaded two chunks ahead; the
+    // per-token values of chunk c live in the Keep set of its parity.
+    const int nck = a.nck;
+    In in0, in1;
+    Keep k0, k1;
+    auto step = [&](int c, Keep& kc, Keep& kn, In& inn) {
+        // kc: chunk c (prologue done); inn holds chunk c-1's inputs
+        scan_chunk(c);
+        __syncthreads();
+        epilogue(c, kc);
+        if (c >= 1) prologue(c - 1, inn, kn);
+        if (c >= 3) load(c - 3, inn);
+        __syncthreads();
+    };
+    const int last = nck - 1;
+    // in[p] holds the chunk of parity p's inputs
+    if (last & 1) {
+        load(last, in1);
+        if (last >= 1) load(last - 1, in0);
+        prologue(last, in1, k1);
+        if (last >= 2) load(last - 2, in1);
+    } else {
+        load(last, in0);
+        if (last >= 1) load(last - 1, in1);
+        prologue(last, in0, k0);
+        if (last >= 2) load(last - 2, in0);
+    }
+    __syncthreads();
+    int c = last;
+    if (c & 1) {
+        step(c, k1, k0, in0);
+        --c;
+    }
+    for (; c >= 0; c -= 2) {
+        step(c, k0, k1, in1);
+        if (c >= 1) step(c - 1, k1, k0, in0);
+    }
+
+    // ---- per-row sums: dA over t (this wave's states), dD and ddt_bias ----
+    if (row_ok) {
+        *reinterpret_cast<float4*>(a.pA + row * kN + n0) =
+            make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
+    }
+    float2* red = reinterpret_cast<float2*>(&sm.part[0][0]);
+    red[pq * kWave + pr] = make_float2(dDacc, dTacc);
+    __syncthreads();
+    if (wv == 0 && row_ok) {
+        float sD = 0.0f, sT = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kBG; ++g) {
+            const float2 v = red[g * kWave + lane];
+            sD += v.x;
+            sT += v.y;
+        }
+        a.pD[row] = sD;
+        a.pT[row] = sT;
+    }
+}
+
+// dB[b,n,t] = ln 2 * sum_rb pB[rb,b,t,n] and dC[b,n,t] = sum_rb pC[rb,b,t,n],
+// row blocks in order; one thread per (b, t).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ pB,
+                                                     const float* __restrict__ pC, T* __restrict__ dB,
+                                                     T* __restrict__ dC, int64_t batch, int64_t L,
+                                                     int64_t Lp, int32_t row_blocks) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= batch * L) return;
+    const int64_t b = i / L, t = i % L;
+    float sb[kN], sc[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) sb[n] = sc[n] = 0.0f;
+    for (int r = 0; r < row_blocks; ++r) {
+        const int64_t o = ((int64_t(r) * batch + b) * Lp + t) * kN;
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q) {
+            const float4 vb = reinterpret_cast<const float4*>(pB + o)[q];
+            const float4 vc = reinterpret_cast<const float4*>(pC + o)[q];
+            sb[4 * q] += vb.x; sb[4 * q + 1] += vb.y; sb[4 * q + 2] += vb.z; sb[4 * q + 3] += vb.w;
+            sc[4 * q] += vc.x; sc[4 * q + 1] += vc.y; sc[4 * q + 2] += vc.z; sc[4 * q + 3] += vc.w;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+        dB[(b * kN + n) * L + t] = from_f32<T>(sb[n] * kLn2);
+        dC[(b * kN + n) * L + t] = from_f32<T>(sc[n]);
+    }
+}
+
+// dA[d,n] = ln 2 * sum_b pA[b,d,n]; dD[d] = sum_b pD[b,d]; ddt_bias[d] = sum_b pT[b,d].
+__global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ pA,
+                                                         const float* __restrict__ pD,
+                                                         const float* __restrict__ pT,
+                                                         float* __restrict__ dA, float* dD,
+                                                         float* ddt, int64_t batch, int64_t dim) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= dim * kN) return;
+    const int64_t d = i / kN;
+    const int n = int(i % kN);
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += pA[(b * dim + d) * kN + n];
+    dA[i] = s * kLn2;
+    if (n == 0) {
+        float sD = 0.0f, sT = 0.0f;
+        for (int64_t b = 0; b < batch; ++b) {
+            sD += pD[b * dim + d];
+            sT += pT[b * dim + d];
+        }
+        if (dD) dD[d] = sD;
+        if (ddt) ddt[d] = sT;
+    }
+}
+
+size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct BwdLayout {
+    size_t packed, ckpt, pB, pC, pA, pD, pT, total;
+};
+BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim) {
+    const size_t rows = size_t(batch) * size_t(dim);
+    const size_t nck = size_t((L + kBCH - 1) / kBCH);
+    const size_t Lp = nck * kBCH;
+    const size_t Lp32 = size_t((L + kChunk - 1) / kChunk) * kChunk;
+    const size_t rbk = size_t((dim + kWave - 1) / kWave);
+    BwdLayout o{};
+    size_t off = 0;
+    o.packed = off; off += al256(size_t(batch) * Lp32 * 2 * kN * 4);
+    o.ckpt = off;   off += al256(nck * rows * kN * 4);
+    o.pB = off;     off += al256(rbk * size_t(batch) * Lp * kN * 4);
+    o.pC = off;     off += al256(rbk * size_t(batch) * Lp * kN * 4);
+    o.pA = off;     off += al256(rows * kN * 4);
+    o.pD = off;     off += al256(rows * 4);
+    o.pT = off;     off += al256(rows * 4);
+    o.total = off;
+    return o;
+}
+
+template <typename T>
+hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, void* ws,
+                 hipStream_t st) {
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    const BwdLayout lo = bwd_layout(batch, L, dim);
+    FwdTensors ft{t.x, t.delta, t.z, t.A, t.B, t.C, t.D, t.dt_bias, nullptr, nullptr, nullptr};
+    FwdShape fs{batch, L, dim, sizeof(T) == 2 ? DType::BF16 : DType::F32};
+    float* packed = reinterpret_cast<float*>(w + lo.packed);
+    float* ckpt = reinterpret_cast<float*>(w + lo.ckpt);
+    hipError_t e = launch_fwd_ckpt(ft, t.dy, t.dz, ckpt, fs, packed, st);
+    if (e != hipSuccess) return e;
+
+    BwdKArgs k{};
+    k.x = t.x; k.delta = t.delta; k.z = t.z; k.dy = t.dy; k.A = t.A; k.P = packed;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.ckpt = ckpt; k.dx = t.dx; k.ddelta = t.ddelta;
+    k.pB = reinterpret_cast<float*>(w + lo.pB);
+    k.pC = reinterpret_cast<float*>(w + lo.pC);
+    k.pA = reinterpret_cast<float*>(w + lo.pA);
+    k.pD = reinterpret_cast<float*>(w + lo.pD);
+    k.pT = reinterpret_cast<float*>(w + lo.pT);
+    k.batch = batch; k.L = L; k.dim = dim;
+    k.nck = int32_t((L + kBCH - 1) / kBCH);
+    k.Lp = int64_t(k.nck) * kBCH;
+    k.psub = ((L + kChunk - 1) / kChunk * kChunk) / kBG;
+    k.row_blocks = int32_t((dim + kWave - 1) / kWave);
+    const dim3 grid(unsigned(int64_t(k.row_blocks) * batch)), block(256);
+    const bool vec = L % 4 == 0;
+    if (t.z) {
+        if (vec) hipLaunchKernelGGL((bwd_kernel<T, true, true>), grid, block, 0, st, k);
+        else hipLaunchKernelGGL((bwd_kernel<T, true, false>), grid, block, 0, st, k);
+    } else {
+        if (vec) hipLaunchKernelGGL((bwd_kernel<T, false, true>), grid, block, 0, st, k);
+        else hipLaunchKernelGGL((bwd_kernel<T, false, false>), grid, block, 0, st, k);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * L + 255) / 256)), dim3(256), 0, st,
+                       k.pB, k.pC, static_cast<T*>(t.dB), static_cast<T*>(t.dC), batch, L, k.Lp,
+                       k.row_blocks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_params, dim3(unsigned((dim * kN + 255) / 256)), dim3(256), 0, st,
+                       k.pA, k.pD, k.pT, t.dA, t.dD, t.ddt_bias, batch, dim);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim) {
+    return bwd_layout(batch, L, dim).total;
+}
+
+hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,
+                      void* workspace, hipStream_t stream) {
+    return dtype == DType::BF16 ? bwd_t<bf16_bits>(t, batch, L, dim, workspace, stream)
+                                : bwd_t<float>(t, batch, L, dim, workspace, stream);
+}
+
+}  // namespace selscan

@@ -64,4 +64,10 @@ __device__ __forceinline__ float silu(float z) {
     return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
 }
 
+// silu'(z) = sig(z) (1 + z (1 - sig(z))), sig(z) = 1 / (1 + e^{-z}).
+__device__ __forceinline__ float silu_grad(float z) {
+    const float sg = rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+    return sg * fmaf(z, 1.0f - sg, 1.0f);
+}
+
 }  // namespace selscan

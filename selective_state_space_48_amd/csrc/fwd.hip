@@ -112,7 +112,7 @@ struct alignas(16) Smem {
     static constexpr int kPairB = CH * 8 + 16;  // float2-per-token row stride (bytes)
     static constexpr int kYB = CH * 4 + 16;     // float-per-token row stride (bytes)
     unsigned char lw[kWave * kPairB];
-    unsigned char yp[MODE == 0 ? G : 1][MODE == 0 ? kWave * kYB : 16];
+    unsigned char yp[MODE != 1 ? G : 1][MODE != 1 ? kWave * kYB : 16];
     double lsum[MODE == 1 ? G : 1][kWave];
 };
 
@@ -132,10 +132,16 @@ struct FwdKArgs {
     int64_t batch, L, dim, seg_len;
     int64_t psub;      // sub-blocks per batch entry in P
     int32_t segments, row_blocks;
+    // checkpoint pass of the backward (MODE 2) only:
+    const void* dy;    // [batch, dim, L] output gradient (read when gated)
+    float* ckpt;       // [ceil(L/16)][batch*dim][N]: the state before every 16th token
 };
 
 // MODE 0: output pass (y, and last_state from the final segment).
 // MODE 1: state pass (each segment's end state from zero, and its summed l).
+// MODE 2: checkpoint pass of the backward: the same recurrence and readout,
+//         storing the state before every 16th token, and in place of y the
+//         gate gradient dz = dy * (C.h + D x) * silu'(z) (one segment only).
 template <typename T, int G, bool GATE, bool VEC, int MODE>
 __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int CH = kChunk;
@@ -145,7 +151,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int TS = CH / G;              // tokens per wave in the per-token phases
     constexpr int V = Elem<T>::kPer16;      // elements per 16-byte vector
     constexpr int SV = TS / V;              // 16-byte vectors per row slice
-    constexpr bool LOADZ = GATE && MODE == 0;
+    constexpr bool LOADZ = GATE && MODE != 1;
+    constexpr bool LOADDY = GATE && MODE == 2;
+    constexpr bool READOUT = MODE == 0 || LOADDY;
+    static_assert(MODE != 2 || G == 4, "the checkpoint pass runs 4 waves of 4 states");
     static_assert(TS % V == 0 && SV >= 1, "tile shape");
     using S = Smem<G, CH, MODE>;
     __shared__ S sm;
@@ -153,6 +162,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const T* __restrict__ X = static_cast<const T*>(a.x);
     const T* __restrict__ DL = static_cast<const T*>(a.delta);
     const T* __restrict__ Z = static_cast<const T*>(a.z);
+    const T* __restrict__ DY = static_cast<const T*>(a.dy);
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; saying so lets every address
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // 64/G rows with CH contiguous tokens each. Two register sets alternate by
     // chunk parity.
     struct Slice {
-        uint4 x[SV], d[SV], z[LOADZ ? SV : 1];
+        uint4 x[SV], d[SV], z[LOADZ ? SV : 1], g[LOADDY ? SV : 1];
     };
     Slice sl0, sl1;
     // Whole 16-byte vectors are in or out (L and the segment ends are
@@ -217,18 +227,21 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 sl.x[k] = ok ? ldg_stream(X + off + k * V) : make_uint4(0, 0, 0, 0);
                 sl.d[k] = ok ? ldg_stream(DL + off + k * V) : make_uint4(0, 0, 0, 0);
                 if constexpr (LOADZ) sl.z[k] = ok ? ldg_stream(Z + off + k * V) : make_uint4(0, 0, 0, 0);
+                if constexpr (LOADDY) sl.g[k] = ok ? ldg_stream(DY + off + k * V) : make_uint4(0, 0, 0, 0);
             } else {
-                float fx[V], fd[V], fz[V];
+                float fx[V], fd[V], fz[V], fg[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     const bool ok = tk + e < t_end;
                     fx[e] = ok ? to_f32(X[off + k * V + e]) : 0.0f;
                     fd[e] = ok ? to_f32(DL[off + k * V + e]) : 0.0f;
                     fz[e] = (LOADZ && ok) ? to_f32(Z[off + k * V + e]) : 0.0f;
+                    fg[e] = (LOADDY && ok) ? to_f32(DY[off + k * V + e]) : 0.0f;
                 }
                 sl.x[k] = pack16<T>(fx);
                 sl.d[k] = pack16<T>(fd);
                 if constexpr (LOADZ) sl.z[k] = pack16<T>(fz);
+                if constexpr (LOADDY) sl.g[k] = pack16<T>(fg);
             }
         }
     };
@@ -256,6 +269,13 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                     s1.z[k] = ldg_stream(Z + off + CH + k * V);
                 }
             }
+            if constexpr (LOADDY) {
+#pragma unroll
+                for (int k = 0; k < SV; ++k) {
+                    s0.g[k] = ldg_stream(DY + off + k * V);
+                    s1.g[k] = ldg_stream(DY + off + CH + k * V);
+                }
+            }
         } else {
             if (c < nchunks) load_slice(c, s0);
             if (c + 1 < nchunks) load_slice(c + 1, s1);
@@ -269,12 +289,13 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // scaled by ln 2 when packed, so w = l * x with l in log2 units.
     auto prologue = [&](int c, const Slice& sl, float* dxo, float* gzo) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
-        float xs[TS], ds[TS], zs[TS];
+        float xs[TS], ds[TS], zs[TS], gs[TS];
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             unpack16<T>(sl.x[k], xs + k * V);
             unpack16<T>(sl.d[k], ds + k * V);
             if constexpr (LOADZ) unpack16<T>(sl.z[k], zs + k * V);
+            if constexpr (LOADDY) unpack16<T>(sl.g[k], gs + k * V);
         }
         float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]) + pq * TS / 2;
         auto body = [&](auto masked) {
@@ -293,6 +314,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                         gzo[j + u] = 1.0f;
                         if constexpr (LOADZ) gzo[j + u] = silu(zs[j + u]);
                     }
+                    if constexpr (LOADDY) {  // dz = (C.h + D x) * (dy * silu'(z))
+                        dxo[j + u] = Dd * xs[j + u];
+                        gzo[j + u] = gs[j + u] * silu_grad(zs[j + u]);
+                    }
                 }
                 lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
             }
@@ -309,22 +334,29 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         const int64_t s0 = (t_begin + int64_t(c) * CH) / SB;          // first sub-block
         const float* rec = a.P + ((b * a.psub + s0) * G + wv) * kRec;  // this wave's record
         const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kPairB]);
-        float* yrow = reinterpret_cast<float*>(&sm.yp[MODE == 0 ? wv : 0][lane * S::kYB]);
+        float* yrow = reinterpret_cast<float*>(&sm.yp[READOUT ? wv : 0][lane * S::kYB]);
         // Ping-pong operand buffers (two sub-blocks per loop trip), so that no
         // register has to be copied at the loop back-edge.
         f32x16 B0 = sload64(rec), C0, B1, C1;
-        if constexpr (MODE == 0) C0 = sload64(rec + 16);
+        if constexpr (READOUT) C0 = sload64(rec + 16);
         float2 l0[SB], l1[SB];
 #pragma unroll
         for (int e = 0; e < SB; ++e) l0[e] = lw2[e];
         auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float2* lc, f32x16& Bn,
                         f32x16& Cn, float2* ln) {
             const int sbn = sb + 1 < NSB ? sb + 1 : sb;  // stays inside the chunk
+            if constexpr (MODE == 2) {
+                // the state before tokens 0 and 16 of the chunk
+                const int64_t k = (t_begin + int64_t(c) * CH + sb * SB) / 16;
+                if ((sb * SB) % 16 == 0 && row_ok && k * 16 < t_end)
+                    *reinterpret_cast<float4*>(a.ckpt + (k * a.batch * a.dim + row) * kN + n0) =
+                        make_float4(h[0], h[1], h[2], h[3]);
+            }
             __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): current operands ready
             __builtin_amdgcn_sched_barrier(0);
             const float* nrec = rec + int64_t(sbn) * (G * kRec);
             Bn = sload64(nrec);
-            if constexpr (MODE == 0) Cn = sload64(nrec + 16);
+            if constexpr (READOUT) Cn = sload64(nrec + 16);
 #pragma unroll
             for (int e = 0; e < SB; ++e) ln[e] = lw2[sbn * SB + e];
             __builtin_amdgcn_sched_barrier(0);
@@ -336,11 +368,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 for (int j = 0; j < NG; ++j) {
                     const float dA = exp2_hw(lc[e].x * An[j]);
                     h[j] = fmaf(dA, h[j], lc[e].y * Bc[j * SB + e]);
-                    if constexpr (MODE == 0) acc = fmaf(Cc[j * SB + e], h[j], acc);
+                    if constexpr (READOUT) acc = fmaf(Cc[j * SB + e], h[j], acc);
                 }
                 yv[e] = acc;
             }
-            if constexpr (MODE == 0) {
+            if constexpr (READOUT) {
                 if constexpr (SB >= 4) {
 #pragma unroll
                     for (int k = 0; k < SB / 4; ++k)
@@ -410,7 +442,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         } else {
             if (c + 3 < nchunks) load_slice(c + 3, next);
         }
-        if constexpr (MODE == 0) epilogue(c, dxc, gzc);
+        if constexpr (READOUT) epilogue(c, dxc, gzc);
         __syncthreads();
     };
     if (nchunks > 0) {
@@ -438,7 +470,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             for (int k = 0; k < NG / 4; ++k)
                 dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
         }
-    } else {
+    } else if constexpr (MODE == 1) {
         const int64_t so = (int64_t(seg) * a.batch * a.dim + b * a.dim + d);
         if (row_ok) {
             float4* dst = reinterpret_cast<float4*>(a.seg_state + so * kN + n0);
@@ -542,6 +574,7 @@ hipError_t launch_one(const FwdKArgs& k, int64_t blocks, hipStream_t st) {
 
 template <typename T, int G, int MODE>
 hipError_t dispatch_gv(const FwdKArgs& k, bool gate, bool vec, int64_t blocks, hipStream_t st) {
+    static_assert(MODE != 2 || G == 4, "checkpoint pass: 4 waves");
     if (MODE == 1) gate = false;  // the state pass never reads z
     if (gate) return vec ? launch_one<T, G, true, true, MODE>(k, blocks, st)
                          : launch_one<T, G, true, false, MODE>(k, blocks, st);
@@ -681,6 +714,28 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     // 3) output pass from the carried-in states
     k.h0 = carry;
     return output_pass(s.dtype, k, p, gate, per_seg * p.segments, stream);
+}
+
+hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float* ckpt,
+                           const FwdShape& s, float* packed, hipStream_t stream) {
+    const int64_t Lp = padded_len(s.L);
+    constexpr int G = 4;
+    hipError_t e = s.dtype == DType::BF16
+                       ? launch_pack<bf16_bits>(t.B, t.C, packed, s.batch, s.L, Lp, G, stream)
+                       : launch_pack<float>(t.B, t.C, packed, s.batch, s.L, Lp, G, stream);
+    if (e != hipSuccess) return e;
+    FwdKArgs k{};
+    k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = packed;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.y = dz; k.last_state = nullptr; k.h0 = nullptr;
+    k.batch = s.batch; k.L = s.L; k.dim = s.dim; k.seg_len = s.L;
+    k.psub = Lp / G; k.segments = 1;
+    k.row_blocks = int32_t((s.dim + kWave - 1) / kWave);
+    k.dy = dy; k.ckpt = ckpt;
+    const int64_t blocks = int64_t(k.row_blocks) * s.batch;
+    const bool vec = (s.L * (s.dtype == DType::BF16 ? 2 : 4)) % 16 == 0;
+    const bool gate = t.z != nullptr;
+    return s.dtype == DType::BF16 ? dispatch_gv<bf16_bits, G, 2>(k, gate, vec, blocks, stream)
+                                  : dispatch_gv<float, G, 2>(k, gate, vec, blocks, stream);
 }
 
 }  // namespace selscan

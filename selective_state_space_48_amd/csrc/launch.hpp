@@ -53,6 +53,14 @@ size_t fwd_workspace_bytes(const FwdShape& s, const FwdPlan& p);
 hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, void* workspace,
                       hipStream_t stream);
 
+// Checkpoint pass of the backward: packs B/C into `packed` (the forward's
+// record layout, fwd_workspace_bytes of a one-segment plan), then runs the
+// forward recurrence storing the state before every 16th token in
+// ckpt [ceil(L/16)][batch*dim][N], and, when t.z is set, dz = dy * (C.h + D x)
+// * silu'(z) into dz ([batch, dim, L] of the dtype). One segment, 4 waves.
+hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float* ckpt,
+                           const FwdShape& s, float* packed, hipStream_t stream);
+
 struct StepTensors {
     float* state;
     const void* x;
@@ -68,6 +76,32 @@ struct StepTensors {
 hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType dtype,
                        hipStream_t stream, hipEvent_t ev_begin = nullptr,
                        hipEvent_t ev_end = nullptr);
+
+// Backward pass. x/delta/z/dy and dx/ddelta/dz: [batch, dim, L]; B/C and
+// dB/dC: [batch, N, L] (all of the dtype); A/dA: [dim, N]; D/dD, dt_bias/ddt_bias:
+// [dim] fp32. z/dz, D/dD, dt_bias/ddt_bias are null together.
+struct BwdTensors {
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* dt_bias;
+    const void* dy;
+    void* dx;
+    void* ddelta;
+    float* dA;
+    void* dB;
+    void* dC;
+    float* dD;
+    void* dz;
+    float* ddt_bias;
+};
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim);
+hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,
+                      void* workspace, hipStream_t stream);
 
 // Causal depthwise conv (width 4) + SiLU. x/out: [rows, L]; w: [dim, 4];
 // bias: [dim] or null; x_prev/x_last: [rows, 3] fp32 or null.

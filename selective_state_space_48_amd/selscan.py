@@ -65,6 +65,9 @@ def _load() -> ctypes.CDLL:
     lib.selscan_timing_stop.restype = ctypes.c_int
     lib.selscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, dims_p, vp]
     lib.selscan_step.restype = ctypes.c_int
+    lib.selscan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, vp, vp, fp, vp, vp, fp, vp, fp,
+                                dims_p, vp]
+    lib.selscan_bwd.restype = ctypes.c_int
     lib.selscan_conv1d.argtypes = [vp, fp, fp, fp, vp, fp, dims_p, vp]
     lib.selscan_conv1d.restype = ctypes.c_int
     lib.selscan_conv1d_step.argtypes = [fp, vp, fp, fp, vp, dims_p, vp]
@@ -222,6 +225,45 @@ def step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Ten
                           _ptr(z), _ptr(y), ctypes.byref(dims), _stream(dev))
     _check(rc)
     return y
+
+
+def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+        D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+        dt_bias: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
+        want_dD: bool = True, want_ddt_bias: bool = True) -> dict:
+    """Backward pass (selscan_bwd): gradients for the output gradient ``dy``.
+
+    Returns a dict with dx, ddelta, dB, dC (input dtype), dA [dim, N] fp32, and
+    dz (when z is given), dD and ddt_bias ([dim] fp32, when wanted).
+    """
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    N = A.shape[-1] if A.dim() == 2 else -1
+    for t, name, dt, shape in ((x, "x", x.dtype, (batch, dim, L)), (delta, "delta", x.dtype, (batch, dim, L)),
+                               (z, "z", x.dtype, (batch, dim, L)), (dy, "dy", x.dtype, (batch, dim, L)),
+                               (A, "A", torch.float32, (dim, N)), (B, "B", x.dtype, (batch, N, L)),
+                               (C, "C", x.dtype, (batch, N, L)), (D, "D", torch.float32, (dim,)),
+                               (dt_bias, "dt_bias", torch.float32, (dim,))):
+        _req(t, name, dt, shape, dev)
+    out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty_like(B),
+           "dC": torch.empty_like(C), "dA": torch.empty_like(A)}
+    if z is not None:
+        out["dz"] = torch.empty_like(x)
+    if want_dD:
+        out["dD"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    if want_ddt_bias:
+        out["ddt_bias"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
+    _check(lib.selscan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                           _ptr(dt_bias), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]),
+                           _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
+                           _ptr(out.get("dz")), _ptr(out.get("ddt_bias")), ctypes.byref(dims),
+                           _stream(dev)))
+    return out
 
 
 CONV_WIDTH = 4

@@ -22,7 +22,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
-            "selscan_conv1d", "selscan_conv1d_step", "selscan_timing_start",
+            "selscan_bwd", "selscan_conv1d", "selscan_conv1d_step", "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_error_codes_match_header():
 
 
 def test_version():
-    assert S.version() == 10200
+    assert S.version() == 10300
 
 
 # Fake, 16-byte aligned, non-overlapping device addresses (never dereferenced:
@@ -259,3 +259,37 @@ def test_conv_null_align_alias():
     assert conv_step_call(D(), p) == S.ERR_ALIAS
     assert conv_call(D(batch=0)) == S.OK           # nothing to do, nothing enqueued
     assert conv_step_call(D(dim=0)) == S.OK
+
+
+def bwd_call(dims, ptrs=None):
+    p = [P(i) for i in range(17)] if ptrs is None else ptrs
+    return S.lib.selscan_bwd(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_bwd_argument_checks():
+    assert bwd_call(None) == S.ERR_NULL
+    assert bwd_call(D(batch=-1)) == S.ERR_DIMS
+    assert bwd_call(D(N=8)) == S.ERR_DSTATE
+    assert bwd_call(D(dtype=3)) == S.ERR_DTYPE
+    assert bwd_call(D(L=1 << 27)) == S.ERR_DIMS
+    # x, delta, A, B, C, dy, dx, ddelta, dA, dB, dC are required
+    for idx in (0, 1, 2, 3, 4, 8, 9, 10, 11, 12, 13):
+        p = [P(i) for i in range(17)]
+        p[idx] = None
+        assert bwd_call(D(), p) == S.ERR_NULL, idx
+    p = [P(i) for i in range(17)]
+    p[15] = None                                   # z given, dz missing
+    assert bwd_call(D(), p) == S.ERR_NULL
+    p = [P(i) for i in range(17)]
+    p[6] = None                                    # dz without z
+    assert bwd_call(D(), p) == S.ERR_NULL
+    for idx in range(17):
+        p = [P(i) for i in range(17)]
+        p[idx] = ctypes.c_void_p(BASE + idx * SPAN + 4)
+        assert bwd_call(D(), p) == S.ERR_ALIGN, idx
+    p = [P(i) for i in range(17)]
+    p[9] = p[0]                                    # dx == x
+    assert bwd_call(D(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(17)]
+    p[13] = ctypes.c_void_p(BASE + 12 * SPAN + 64)  # dC inside dB
+    assert bwd_call(D(), p) == S.ERR_ALIAS
