@@ -212,22 +212,27 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         uint4 x[SV], d[SV], z[LOADZ ? SV : 1], g[LOADDY ? SV : 1];
     };
     Slice sl0, sl1;
-    // Whole 16-byte vectors are in or out (L and the segment ends are
-    // multiples of V when VEC); chunks wholly inside the segment load without
-    // any test.
+    // With 16-byte rows (VEC) the loads are issued without any condition: a
+    // vector past the end of the row is read from the row's last vector
+    // instead (always valid memory) and its values are discarded by the
+    // prologue's masked path. Branch-free loads keep the compiler from
+    // merging differently-allocated register sets after the loads, which
+    // would make it wait for them there. Without VEC, element loads test
+    // each token.
+    auto load_vec = [&](const T* base, int64_t tk) {
+        return ldg_stream(base + prow * a.L + min(tk, a.L - V));
+    };
     auto load_slice = [&](int c, Slice& sl) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
         const int64_t off = prow * a.L + ts;
-        const bool whole = t_begin + int64_t(c + 1) * CH <= t_end;
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             const int64_t tk = ts + k * V;
             if constexpr (VEC) {
-                const bool ok = whole || tk < t_end;
-                sl.x[k] = ok ? ldg_stream(X + off + k * V) : make_uint4(0, 0, 0, 0);
-                sl.d[k] = ok ? ldg_stream(DL + off + k * V) : make_uint4(0, 0, 0, 0);
-                if constexpr (LOADZ) sl.z[k] = ok ? ldg_stream(Z + off + k * V) : make_uint4(0, 0, 0, 0);
-                if constexpr (LOADDY) sl.g[k] = ok ? ldg_stream(DY + off + k * V) : make_uint4(0, 0, 0, 0);
+                sl.x[k] = load_vec(X, tk);
+                sl.d[k] = load_vec(DL, tk);
+                if constexpr (LOADZ) sl.z[k] = load_vec(Z, tk);
+                if constexpr (LOADDY) sl.g[k] = load_vec(DY, tk);
             } else {
                 float fx[V], fd[V], fz[V], fg[V];
 #pragma unroll
@@ -250,35 +255,29 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // halves are requested back to back and the line is fetched once.
     auto load_pair = [&](int c, Slice& s0, Slice& s1) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
-        const int64_t off = prow * a.L + ts;
-        if (VEC && t_begin + int64_t(c + 2) * CH <= t_end) {
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            s0.x[k] = load_vec(X, ts + k * V);
+            s1.x[k] = load_vec(X, ts + CH + k * V);
+        }
+#pragma unroll
+        for (int k = 0; k < SV; ++k) {
+            s0.d[k] = load_vec(DL, ts + k * V);
+            s1.d[k] = load_vec(DL, ts + CH + k * V);
+        }
+        if constexpr (LOADZ) {
 #pragma unroll
             for (int k = 0; k < SV; ++k) {
-                s0.x[k] = ldg_stream(X + off + k * V);
-                s1.x[k] = ldg_stream(X + off + CH + k * V);
+                s0.z[k] = load_vec(Z, ts + k * V);
+                s1.z[k] = load_vec(Z, ts + CH + k * V);
             }
+        }
+        if constexpr (LOADDY) {
 #pragma unroll
             for (int k = 0; k < SV; ++k) {
-                s0.d[k] = ldg_stream(DL + off + k * V);
-                s1.d[k] = ldg_stream(DL + off + CH + k * V);
+                s0.g[k] = load_vec(DY, ts + k * V);
+                s1.g[k] = load_vec(DY, ts + CH + k * V);
             }
-            if constexpr (LOADZ) {
-#pragma unroll
-                for (int k = 0; k < SV; ++k) {
-                    s0.z[k] = ldg_stream(Z + off + k * V);
-                    s1.z[k] = ldg_stream(Z + off + CH + k * V);
-                }
-            }
-            if constexpr (LOADDY) {
-#pragma unroll
-                for (int k = 0; k < SV; ++k) {
-                    s0.g[k] = ldg_stream(DY + off + k * V);
-                    s1.g[k] = ldg_stream(DY + off + CH + k * V);
-                }
-            }
-        } else {
-            if (c < nchunks) load_slice(c, s0);
-            if (c + 1 < nchunks) load_slice(c + 1, s1);
         }
     };
 
@@ -306,7 +305,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     l[u] = softplus_log2_of(fmaf(ds[j + u], kLog2e, biasl));
-                    if (masked && j + u >= nvalid) l[u] = 0.0f;  // padded inputs are 0
+                    if (masked && j + u >= nvalid) {  // past the end: an identity step
+                        l[u] = 0.0f;
+                        xs[j + u] = 0.0f;
+                    }
                     w[u] = l[u] * xs[j + u];
                     if constexpr (MODE == 1) lsum_acc += double(l[u]);
                     if constexpr (MODE == 0) {
@@ -437,10 +439,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         scan_chunk(c);
         __syncthreads();
         if (c + 1 < nchunks) prologue(c + 1, next, dxn, gzn);
+        // (VEC loads of chunks past the end read valid memory and are never used)
         if constexpr (PAIR) {
-            if ((c & 1) == 0 && c + 2 < nchunks) load_pair(c + 2, other, next);
+            if ((c & 1) == 0) load_pair(c + 2, other, next);
         } else {
-            if (c + 3 < nchunks) load_slice(c + 3, next);
+            if (VEC || c + 3 < nchunks) load_slice(c + 3, next);
         }
         if constexpr (READOUT) epilogue(c, dxc, gzc);
         __syncthreads();
