@@ -78,6 +78,8 @@ class Oracle:
         lib.ssm_ref_step.argtypes = [_dp] * 9 + [ctypes.c_int64] * 3 + [_dp] * 2
         lib.ssm_ref_bwd.restype = ctypes.c_int
         lib.ssm_ref_bwd.argtypes = [_dp] * 9 + [ctypes.c_int64] * 4 + [_dp] * 16 + [ctypes.c_int]
+        lib.ssm_ref_ssd.restype = ctypes.c_int
+        lib.ssm_ref_ssd.argtypes = [_dp] * 7 + [ctypes.c_int64] * 5 + [_dp] * 4 + [ctypes.c_int]
         lib.ssm_ref_conv1d.restype = ctypes.c_int
         lib.ssm_ref_conv1d.argtypes = [_dp] * 4 + [ctypes.c_int64] * 4 + [_dp] * 3
         lib.ssm_ref_conv1d_step.restype = ctypes.c_int
@@ -121,6 +123,30 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"ssm_ref_bwd failed with code {rc}")
         return out
+
+    def ssd(self, x, delta, A, B, C, D=None, dt_bias=None, nthreads: Optional[int] = None):
+        """Mamba-2's SSD layer (scalar decay per head), from a zero state.
+
+        ``x``: ``[batch, seqlen, heads, headdim]``; ``delta`` (raw):
+        ``[batch, seqlen, heads]``; ``A, D, dt_bias``: ``[heads]``; ``B, C``:
+        ``[batch, seqlen, dstate]``. Returns ``y``, ``y_scale`` (like x) and
+        ``last_state``, ``state_scale`` (``[batch, heads, dstate, headdim]``).
+        """
+        x, delta, A, B, C, D, dt_bias = map(_f64, (x, delta, A, B, C, D, dt_bias))
+        batch, L, H, P = x.shape
+        N = B.shape[2]
+        assert delta.shape == (batch, L, H) and A.shape == (H,)
+        assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        y = np.empty_like(x)
+        ys = np.empty_like(x)
+        hs = np.empty((batch, H, N, P), np.float64)
+        hss = np.empty((batch, H, N, P), np.float64)
+        rc = self.lib.ssm_ref_ssd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(dt_bias), batch, L, H, P, N, _ptr(y), _ptr(ys), _ptr(hs),
+                                  _ptr(hss), nthreads or default_threads())
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_ssd failed with code {rc}")
+        return {"y": y, "y_scale": ys, "last_state": hs, "state_scale": hss}
 
     def conv1d(self, x, w, bias=None, x_prev=None):
         """Causal depthwise convolution of width K = w.shape[1], then SiLU.
@@ -262,6 +288,11 @@ def step(*args, **kw):
 def bwd(*args, **kw):
     """Backward pass through the built oracle; see ``Oracle.bwd``."""
     return default().bwd(*args, **kw)
+
+
+def ssd(*args, **kw):
+    """Mamba-2 SSD layer through the built oracle; see ``Oracle.ssd``."""
+    return default().ssd(*args, **kw)
 
 
 def conv1d(*args, **kw):

@@ -547,3 +547,123 @@ int ssm_ref_bwd(const double *x, const double *delta, const double *A, const dou
     free(part); free(jobs); free(th);
     return rc;
 }
+
+/*
+ * The state space dual (SSD) layer of Mamba-2: the selective SSM restricted
+ * so that the decay is one scalar per head and token.
+ *
+ * "State Space Models Explained: How Mamba Works and How It Compares to
+ * Transformers" (mernstackdev.com), section "From S4 to Mamba": Mamba-2's
+ * state space duality shows a restricted kind of SSM and a form of linear
+ * attention to be two views of one computation, which lets it use matrix
+ * multiplications; "State space models and Mamba: reading long sequences
+ * without attention" (ai-trend.me), section "How it developed: from S4 to
+ * Mamba and Mamba-2": the link is the decomposition of a semiseparable
+ * matrix; "Mamba State Space Models: Fixed State, Linear Time"
+ * (deepnoodle.ai): the duality through decompositions of structured
+ * matrices. The restriction read here is the one under which the sequence
+ * map is such a matrix: A_t = exp(delta_t A_h) times the identity, one
+ * scalar per (token, head); the P channels of a head share delta_t, and B_t,
+ * C_t (N entries) are shared by all heads. Per batch entry b and head h, from
+ * a zero state S (N x P):
+ *
+ *   delta_t = softplus(delta_raw[b,t,h] + dt_bias[h])
+ *   S[n,p]  = exp(delta_t A_h) S[n,p] + delta_t B[b,t,n] x[b,t,h,p]
+ *   y[b,t,h,p] = sum_n C[b,t,n] S[n,p] + D_h x[b,t,h,p]
+ *   last_state[b,h,n,p] = S[n,p] after the last token
+ *
+ * (This is the recurrence; the duality is that y = (Lmask o C B^T)(delta x)
+ * + D x with Lmask[t,s] = exp(A_h sum_{s<k<=t} delta_k) for s <= t, which the
+ * tests check it against.) Scales as for the selective scan: the same
+ * recurrence on magnitudes.
+ *
+ * Layouts: x, y: [batch, seqlen, heads, headdim]; delta_raw: [batch, seqlen,
+ * heads]; A, D, dt_bias: [heads]; B, C: [batch, seqlen, dstate];
+ * last_state: [batch, heads, dstate, headdim]. (b, h) pairs are split over
+ * threads.
+ */
+typedef struct {
+    const double *x, *delta, *A, *B, *C, *D, *dt_bias;
+    int64_t batch, L, H, P, N;
+    double *y, *ys, *hs, *hss;
+    int64_t i0, i1;
+} ssd_job;
+
+static void ssd_pairs(const ssd_job *j)
+{
+    const int64_t L = j->L, H = j->H, P = j->P, N = j->N;
+    double *S = malloc(sizeof(double) * (size_t)(N * P) * 2);
+    if (!S) return;
+    double *Sa = S + N * P;
+    for (int64_t i = j->i0; i < j->i1; ++i) {
+        const int64_t b = i / H, h = i % H;
+        for (int64_t k = 0; k < N * P; ++k) S[k] = Sa[k] = 0.0;
+        const double Ah = j->A[h], Dh = j->D ? j->D[h] : 0.0, bias = j->dt_bias ? j->dt_bias[h] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double dl = softplus(j->delta[(b * L + t) * H + h] + bias);
+            const double a = exp(dl * Ah);
+            const double *xt = j->x + ((b * L + t) * H + h) * P;
+            const double *Bt = j->B + (b * L + t) * N, *Ct = j->C + (b * L + t) * N;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t p = 0; p < P; ++p) {
+                    const double in = dl * Bt[n] * xt[p];
+                    S[n * P + p] = a * S[n * P + p] + in;
+                    Sa[n * P + p] = a * Sa[n * P + p] + fabs(in);
+                }
+            double *yt = j->y + ((b * L + t) * H + h) * P;
+            double *yst = j->ys ? j->ys + ((b * L + t) * H + h) * P : NULL;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0, accs = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    acc += Ct[n] * S[n * P + p];
+                    accs += fabs(Ct[n]) * Sa[n * P + p];
+                }
+                yt[p] = acc + Dh * xt[p];
+                if (yst) yst[p] = accs + fabs(Dh * xt[p]);
+            }
+        }
+        if (j->hs)
+            for (int64_t k = 0; k < N * P; ++k) j->hs[i * N * P + k] = S[k];
+        if (j->hss)
+            for (int64_t k = 0; k < N * P; ++k) j->hss[i * N * P + k] = Sa[k];
+    }
+    free(S);
+}
+
+static void *ssd_thread(void *p)
+{
+    ssd_pairs((const ssd_job *)p);
+    return NULL;
+}
+
+int ssm_ref_ssd(const double *x, const double *delta, const double *A, const double *B,
+                const double *C, const double *D, const double *dt_bias,
+                int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
+                double *y, double *y_scale, double *last_state, double *state_scale, int nthreads)
+{
+    if (!x || !delta || !A || !B || !C || !y) return -1;
+    if (batch < 0 || seqlen < 0 || heads < 0 || headdim <= 0 || dstate <= 0) return -2;
+    const int64_t pairs = batch * heads;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > pairs) nthreads = pairs > 0 ? (int)pairs : 1;
+    ssd_job base = {x, delta, A, B, C, D, dt_bias, batch, seqlen, heads, headdim, dstate,
+                    y, y_scale, last_state, state_scale, 0, 0};
+    ssd_job *jobs = calloc((size_t)nthreads, sizeof(ssd_job));
+    pthread_t *tid = calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tid) { free(jobs); free(tid); return -3; }
+    int rc = 0, started = 0;
+    for (int k = 0; k < nthreads; ++k) {
+        jobs[k] = base;
+        jobs[k].i0 = pairs * k / nthreads;
+        jobs[k].i1 = pairs * (k + 1) / nthreads;
+    }
+    for (int k = 1; k < nthreads; ++k) {
+        if (pthread_create(&tid[k], NULL, ssd_thread, &jobs[k]) != 0) { rc = -3; break; }
+        started = k;
+    }
+    if (rc == 0) ssd_pairs(&jobs[0]);
+    for (int k = 1; k <= started; ++k) pthread_join(tid[k], NULL);
+    free(jobs);
+    free(tid);
+    return rc;
+}

@@ -630,4 +630,66 @@ def pin_bwd_scales_bound_values(O):
         _close(r2[k], 2.0 * r[k], 0.0, what=f"bwd linear in dy {k}")
 
 
+# ----------------------------------------------------------------------------
+# Mamba-2 SSD layer
+# ----------------------------------------------------------------------------
+
+def _ssd_problem(seed, batch, L, H, P, N, with_D=True, with_bias=True):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.standard_normal((batch, L, H, P)), delta=rng.standard_normal((batch, L, H)),
+                A=-rng.uniform(0.2, 2.0, H), B=rng.standard_normal((batch, L, N)),
+                C=rng.standard_normal((batch, L, N)),
+                D=rng.standard_normal(H) if with_D else None,
+                dt_bias=rng.standard_normal(H) * 0.5 if with_bias else None)
+
+
+def pin_ssd_equals_restricted_selective_scan(O):
+    """SSD is the selective scan with A[d, n] = A_h for every state n, one step
+    size per head and B, C shared: run the (separately pinned) selective-scan
+    definition on the channels of every head and compare y and the state."""
+    p = _ssd_problem(51, 2, 23, 3, 4, 5)
+    r = O.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"])
+    batch, L, H, P = p["x"].shape
+    N = p["B"].shape[2]
+    x = p["x"].transpose(0, 2, 3, 1).reshape(batch, H * P, L)          # channel d = h*P + p
+    delta = np.repeat(p["delta"].transpose(0, 2, 1), P, axis=1)
+    A = np.repeat(p["A"], P)[:, None] * np.ones((1, N))
+    s6 = O.fwd(x, delta, A, p["B"].transpose(0, 2, 1), p["C"].transpose(0, 2, 1),
+               D=np.repeat(p["D"], P), dt_bias=np.repeat(p["dt_bias"], P))
+    _close(r["y"], s6["y"].reshape(batch, H, P, L).transpose(0, 3, 1, 2), 1e-12, what="ssd vs S6 y")
+    _close(r["last_state"], s6["last_state"].reshape(batch, H, P, N).transpose(0, 1, 3, 2), 1e-12,
+           what="ssd vs S6 state")
+    _close(r["y_scale"], s6["y_scale"].reshape(batch, H, P, L).transpose(0, 3, 1, 2), 1e-12,
+           what="ssd vs S6 scale")
+
+
+def pin_ssd_dual_quadratic_form(O):
+    """The attention-like dual: y = (Lmask o C B^T)(delta x) + D x with
+    Lmask[t,s] = exp(A_h sum_{s<k<=t} delta_k) (s <= t), by numpy matrix
+    products; and the last state sum_s exp(A_h sum_{k>s} delta_k) delta_s
+    B_s x_s^T."""
+    for kw in (dict(), dict(with_D=False, with_bias=False)):
+        p = _ssd_problem(52, 2, 31, 2, 3, 4, **kw)
+        r = O.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"])
+        batch, L, H, P = p["x"].shape
+        bias = p["dt_bias"] if p["dt_bias"] is not None else np.zeros(H)
+        for b in range(batch):
+            CBt = p["C"][b] @ p["B"][b].T                                  # [L, L]
+            for h in range(H):
+                dl = softplus_lib(p["delta"][b, :, h] + bias[h])
+                cum = np.cumsum(dl)
+                seg = cum[:, None] - cum[None, :]                            # sum_{s<k<=t}
+                Lmask = np.where(np.tril(np.ones((L, L))) > 0, np.exp(p["A"][h] * seg), 0.0)
+                xs = p["x"][b, :, h, :]
+                y = (Lmask * CBt) @ (dl[:, None] * xs)
+                if p["D"] is not None:
+                    y = y + p["D"][h] * xs
+                _close(r["y"][b, :, h, :], y, 1e-11, scale=r["y_scale"][b, :, h, :] + 1e-300,
+                       what=f"ssd dual form {kw}")
+                w = np.exp(p["A"][h] * (cum[-1] - cum)) * dl
+                S = p["B"][b].T @ (w[:, None] * xs)                          # [N, P]
+                _close(r["last_state"][b, h], S, 1e-11, scale=r["state_scale"][b, h] + 1e-300,
+                       what="ssd dual last state")
+
+
 PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

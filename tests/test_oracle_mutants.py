@@ -72,6 +72,13 @@ MUTANTS = [
     ("bwd_decay_term_dropped", "ddl += q * Ad[n];", "ddl += 0.0 * Ad[n];"),
     ("bwd_dD_ungated", "dD += ds * x[t];", "dD += dy[t] * x[t];"),
     ("bwd_dt_bias_no_sigmoid", "dT += ddl * sg;", "dT += ddl;"),
+    ("ssd_decay_no_delta", "const double a = exp(dl * Ah);", "const double a = exp(Ah);"),
+    ("ssd_input_no_delta", "const double in = dl * Bt[n] * xt[p];", "const double in = Bt[n] * xt[p];"),
+    ("ssd_readout_B", "acc += Ct[n] * S[n * P + p];", "acc += Bt[n] * S[n * P + p];"),
+    ("ssd_no_D", "yt[p] = acc + Dh * xt[p];", "yt[p] = acc;"),
+    ("ssd_head_index", "const double dl = softplus(j->delta[(b * L + t) * H + h] + bias);",
+     "const double dl = softplus(j->delta[(b * L + t) * H] + bias);"),
+    ("ssd_state_transposed", "S[n * P + p] = a * S[n * P + p] + in;", "S[n * P + p] = a * S[p * N + n % P] + in;"),
     ("bwd_dx_scale_no_D", "j->sdx[row * L + t] = fabs(ds * Dd) + dl * accBa;", "j->sdx[row * L + t] = dl * accBa;"),
 ]
 
