@@ -260,6 +260,49 @@ def time_bwd(torch, dev, reps=5):
             "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
 
 
+def time_ssd(torch, dev, reps=10):
+    """Mamba-2 SSD layer, batch 8, L 2048, 64 heads of 64, state 128, bf16:
+    whole call (chunk states, state passing, chunk outputs; workspace on the
+    stream). Roofline terms: the chunked algorithm's matrix-product flops
+    (64-token chunks) against the 2.5 PFLOP/s bf16 peak, and the algorithmic
+    bytes (inputs once, y and the final state once) against 8 TB/s."""
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    s = W.SSD_HEADLINE
+    p = W.ssd_inputs(s["batch"], s["seqlen"], s["heads"], s["headdim"], s["dstate"], s["seed"])
+
+    def t(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+
+    bf = torch.bfloat16
+    x, dl, B, C = t(p["x"], bf), t(p["delta"], bf), t(p["B"], bf), t(p["C"], bf)
+    A, D, bias = t(p["A"]), t(p["D"]), t(p["dt_bias"])
+    y = torch.empty_like(x)
+    hs = torch.empty((s["batch"], s["heads"], s["dstate"], s["headdim"]), device=dev)
+    run = lambda: selscan.ssd_fwd(x, dl, A, B, C, D=D, dt_bias=bias, y=y, last_state=hs)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) / reps * 1e3
+    Bb, L, H, P, N = s["batch"], s["seqlen"], s["heads"], s["headdim"], s["dstate"]
+    Q = 64
+    chunks = Bb * H * ((L + Q - 1) // Q)
+    flops = chunks * 2 * Q * (P * N + Q * N + Q * P + N * P)
+    nbytes = 2 * (2 * Bb * L * H * P) + 2 * Bb * L * H + 2 * 2 * Bb * L * N + 4 * Bb * H * N * P
+    E = Bb * L * H * P
+    return {"workload": f"ssd_bf16_b{Bb}_l{L}_h{H}_p{P}_n{N}", "us_per_call": round(us, 2),
+            "Gelem_per_s": round(E / (us * 1e-6) / 1e9, 1),
+            "mfma_TFLOPs": round(flops / (us * 1e-6) / 1e12, 2), "frac_mfma_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
+            "algorithmic_bytes": nbytes, "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4)}
+
+
 def time_conv(torch, dev, reps=20):
     """The causal conv1d (width 4) + SiLU over the headline-shaped input
     (bf16, x_last returned), and its decode step on the decode shape. Kernel
@@ -423,7 +466,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "bwd", "copy"],
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "bwd", "ssd", "copy"],
                     default=None,
                     help="run just one workload (for profiling); copy = counter calibration")
     args = ap.parse_args()
@@ -511,6 +554,10 @@ def main():
         log("[bench] backward: headline shape")
         extras["bwd"] = time_bwd(torch, dev)
         log(f"[bench] backward: {extras['bwd']}")
+    if not args.no_extras and args.only in (None, "ssd"):
+        log("[bench] SSD layer")
+        extras["ssd"] = time_ssd(torch, dev)
+        log(f"[bench] ssd: {extras['ssd']}")
     if not args.no_extras and args.only in (None, "conv"):
         log("[bench] conv1d: headline shape and decode steps")
         extras.update(time_conv(torch, dev))

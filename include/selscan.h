@@ -209,6 +209,49 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
                 const selscan_dims_t* dims, void* stream);
 
 /*
+ * selscan_ssd_fwd — Mamba-2's state space dual (SSD) layer: the selective SSM
+ * restricted to one scalar decay per token and head, evaluated chunk-wise
+ * with matrix products.
+ *
+ * Defined by: "State Space Models Explained: How Mamba Works and How It
+ * Compares to Transformers" (mernstackdev.com), section "From S4 to Mamba"
+ * (a restricted SSM and a form of linear attention are two views of one
+ * computation, which lets Mamba-2 use matrix multiplications) and "State
+ * space models and Mamba: reading long sequences without attention"
+ * (ai-trend.me), section "How it developed: from S4 to Mamba and Mamba-2"
+ * (the link is a decomposition of a semiseparable matrix). Per batch entry b
+ * and head h, from a zero state S (dstate x headdim):
+ *   delta_t = softplus(delta[b,t,h] + dt_bias[h])
+ *   S = exp(delta_t A[h]) S + delta_t B[b,t,:]^T x[b,t,h,:]
+ *   y[b,t,h,:] = C[b,t,:] S + D[h] x[b,t,h,:];   last_state[b,h] = S at the end
+ *
+ * Arguments (device pointers; bfloat16 only in this version):
+ *   x, y       : [B, L, H, P] bf16 (token-major, as a projection writes them)
+ *   delta      : [B, L, H] bf16 (before softplus; dt_bias is added first)
+ *   A          : [H] fp32, negative; D, dt_bias: [H] fp32 or NULL (0)
+ *   B, C       : [B, L, N] bf16, shared by all heads
+ *   last_state : [B, H, N, P] fp32 output or NULL
+ * dims: batch B, seqlen L (< 2^27), heads H, headdim P (64), dstate N (64 or
+ * 128), dtype SELSCAN_BF16 (anything else: SELSCAN_ERR_DTYPE; other P or N:
+ * SELSCAN_ERR_DSTATE). Workspace: B H ceil(L/64) P N 6 bytes (chunk states),
+ * taken with hipMallocAsync on the stream. Outputs must not overlap inputs.
+ * Products in bf16 with fp32 sums (the within-chunk scores and the scaled C
+ * are rounded to bf16 as matrix-core operands). Deterministic.
+ */
+typedef struct {
+    int64_t batch;
+    int64_t seqlen;
+    int64_t heads;
+    int64_t headdim;
+    int64_t dstate;
+    int32_t dtype;
+} selscan_ssd_dims_t;
+
+int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D, const float* dt_bias, void* y, float* last_state,
+                    const selscan_ssd_dims_t* dims, void* stream);
+
+/*
  * selscan_conv1d — the short causal convolution in front of the scan: a
  * depthwise conv1d of width SELSCAN_CONV_WIDTH (4), then SiLU.
  *

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libselscan.so")
-SOURCES = ["api.hip", "fwd.hip", "step.hip", "conv.hip", "bwd.hip"]
+SOURCES = ["api.hip", "fwd.hip", "step.hip", "conv.hip", "bwd.hip", "ssd.hip"]
 # Counter-calibration copies (measurement only), a library of their own.
 CALIB_LIB = os.path.join(PKG, "libselscan_calib.so")
 CALIB_SOURCES = ["calib.hip"]

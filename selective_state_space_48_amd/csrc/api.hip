@@ -19,7 +19,7 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
 
 namespace {
 
-constexpr int kVersion = 10300;  // 1.3.0
+constexpr int kVersion = 10400;  // 1.4.0
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -351,6 +351,55 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
     const hipError_t e = launch_bwd(t, dims->batch, L, dims->dim,
                                     dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32, ws, st);
     (void)hipFreeAsync(ws, st);
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D, const float* dt_bias, void* y, float* last_state,
+                    const selscan_ssd_dims_t* dims, void* stream) {
+    if (!dims) return SELSCAN_ERR_NULL;
+    if (dims->batch < 0 || dims->seqlen < 0 || dims->heads < 0 || dims->headdim < 0 || dims->dstate < 0)
+        return SELSCAN_ERR_DIMS;
+    if (dims->dtype != SELSCAN_BF16) return SELSCAN_ERR_DTYPE;
+    if (dims->headdim != 64 || (dims->dstate != 64 && dims->dstate != 128)) return SELSCAN_ERR_DSTATE;
+    if (dims->seqlen >= (int64_t(1) << 27)) return SELSCAN_ERR_DIMS;
+    int64_t bl, seq, bh, st, t;
+    if (!mul_ok(dims->batch, dims->seqlen, &bl) || !mul_ok(bl, dims->heads * 64, &seq) ||
+        !mul_ok(seq, 4, &t) || !mul_ok(dims->batch, dims->heads, &bh) ||
+        !mul_ok(bh, 64 * dims->dstate, &st) || !mul_ok(st, 4, &t) || bh > (int64_t(1) << 31) ||
+        dims->heads > (int64_t(1) << 20))
+        return SELSCAN_ERR_DIMS;
+    const int64_t nc = (dims->seqlen + 63) / 64;
+    if (bh * nc > INT32_MAX) return SELSCAN_ERR_DIMS;
+    const int64_t nbc = bl * dims->dstate;  // elements of B, C
+    if ((seq > 0 && (!x || !y)) || (bl * dims->heads > 0 && !delta) || (nbc > 0 && (!B || !C)) ||
+        (dims->heads > 0 && !A))
+        return SELSCAN_ERR_NULL;
+    for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, (const void*)dt_bias, (const void*)y,
+                          (const void*)last_state})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const Span oy = span(y, seq * 2), os = span(last_state, st * 4);
+    const Span ins[] = {span(x, seq * 2), span(delta, bl * dims->heads * 2), span(A, dims->heads * 4),
+                        span(B, nbc * 2), span(C, nbc * 2), span(D, dims->heads * 4),
+                        span(dt_bias, dims->heads * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, oy) || overlaps(s, os)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(oy, os)) return SELSCAN_ERR_ALIAS;
+    hipStream_t stm = static_cast<hipStream_t>(stream);
+    if (bh == 0) return SELSCAN_OK;
+    if (dims->seqlen == 0) {
+        if (last_state && launch_fill_zero(last_state, st, stm) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        return SELSCAN_OK;
+    }
+    const size_t ws_bytes = ssd_workspace_bytes(dims->batch, dims->seqlen, dims->heads, dims->dstate);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, ws_bytes, stm) != hipSuccess || !ws) {
+        (void)hipGetLastError();
+        return SELSCAN_ERR_ALLOC;
+    }
+    SsdTensors tt{x, delta, A, B, C, D, dt_bias, y, last_state};
+    const hipError_t e = launch_ssd(tt, dims->batch, dims->seqlen, dims->heads, dims->dstate, ws, stm);
+    (void)hipFreeAsync(ws, stm);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 

@@ -103,6 +103,24 @@ size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim);
 hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,
                       void* workspace, hipStream_t stream);
 
+// Mamba-2 SSD layer (bf16). x/y: [batch, L, heads, 64]; delta: [batch, L, heads];
+// A, D, dt_bias: [heads] fp32; B, C: [batch, L, dstate]; last_state:
+// [batch, heads, dstate, 64] fp32 or null. dstate 64 or 128.
+struct SsdTensors {
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* dt_bias;
+    void* y;
+    float* last_state;
+};
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t heads, int64_t dstate);
+hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t heads, int64_t dstate,
+                      void* workspace, hipStream_t stream);
+
 // Causal depthwise conv (width 4) + SiLU. x/out: [rows, L]; w: [dim, 4];
 // bias: [dim] or null; x_prev/x_last: [rows, 3] fp32 or null.
 struct ConvTensors {

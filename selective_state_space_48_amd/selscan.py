@@ -39,6 +39,11 @@ class FwdOpts(ctypes.Structure):
                 ("groups", ctypes.c_int32)]
 
 
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
 class SelscanError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libselscan error {code}: {msg}")
@@ -68,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.selscan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, vp, vp, fp, vp, vp, fp, vp, fp,
                                 dims_p, vp]
     lib.selscan_bwd.restype = ctypes.c_int
+    lib.selscan_ssd_fwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, ctypes.POINTER(SsdDims), vp]
+    lib.selscan_ssd_fwd.restype = ctypes.c_int
     lib.selscan_conv1d.argtypes = [vp, fp, fp, fp, vp, fp, dims_p, vp]
     lib.selscan_conv1d.restype = ctypes.c_int
     lib.selscan_conv1d_step.argtypes = [fp, vp, fp, fp, vp, dims_p, vp]
@@ -264,6 +271,43 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
                            _ptr(out.get("dz")), _ptr(out.get("ddt_bias")), ctypes.byref(dims),
                            _stream(dev)))
     return out
+
+
+def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+            C: torch.Tensor, D: Optional[torch.Tensor] = None,
+            dt_bias: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
+            last_state: Optional[torch.Tensor] = None,
+            return_last_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Mamba-2 SSD layer (selscan_ssd_fwd), bfloat16. Returns (y, last_state).
+
+    ``x`` [batch, L, heads, 64]; ``delta`` [batch, L, heads] (before softplus);
+    ``A``, ``D``, ``dt_bias`` [heads] fp32; ``B``, ``C`` [batch, L, dstate];
+    last_state [batch, heads, dstate, 64] fp32.
+    """
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, L, heads, headdim]")
+    batch, L, H, P = x.shape
+    N = B.shape[-1] if B.dim() == 3 else -1
+    dev = x.device
+    bf = torch.bfloat16
+    _req(x, "x", bf, (batch, L, H, P), dev)
+    _req(delta, "delta", bf, (batch, L, H), dev)
+    _req(A, "A", torch.float32, (H,), dev)
+    _req(B, "B", bf, (batch, L, N), dev)
+    _req(C, "C", bf, (batch, L, N), dev)
+    _req(D, "D", torch.float32, (H,), dev)
+    _req(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, "y", bf, (batch, L, H, P), dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, H, N, P), dtype=torch.float32, device=dev)
+    _req(last_state, "last_state", torch.float32, (batch, H, N, P), dev)
+    dims = SsdDims(batch, L, H, P, N, BF16)
+    _check(lib.selscan_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(dt_bias), _ptr(y), _ptr(last_state), ctypes.byref(dims),
+                               _stream(dev)))
+    return y, last_state
 
 
 CONV_WIDTH = 4

@@ -35,6 +35,7 @@ TID_PRE_X, TID_PRE_DELTA, TID_PRE_B = 7, 8, 9
 TID_STEP0 = 10  # decode step s uses ids TID_STEP0 + s (sub-stream k = tensor)
 TID_CONV_W, TID_CONV_BIAS, TID_CONV_PREV = 200, 201, 202
 TID_CONV_STEP0 = 300  # convolution decode step s uses id TID_CONV_STEP0 + s
+TID_SSD = 400          # SSD layer: ids TID_SSD + 0..6
 
 
 @dataclass(frozen=True)
@@ -225,3 +226,33 @@ def conv_step_inputs(w: Workload, s: int) -> np.ndarray:
     """The input token of convolution decode step ``s``: x [batch, dim]."""
     x = _rng(w.seed, TID_CONV_STEP0 + s, 0).standard_normal((w.batch, w.dim), dtype=np.float32)
     return _maybe_bf16(w, x)
+
+
+# Mamba-2 SSD layer: a 1.3B-shaped layer (d_inner 4096 = 64 heads of 64
+# channels, state 128, one B/C group), bf16.
+SSD_HEADLINE = dict(batch=8, seqlen=2048, heads=64, headdim=64, dstate=128, seed=5)
+
+
+def ssd_inputs(batch: int, seqlen: int, heads: int, headdim: int, dstate: int, seed: int,
+               batches: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the SSD layer (bf16-rounded values as float32): x [b, L, H, P],
+    delta_raw [b, L, H], B, C [b, L, N] ~ N(0, 1); per head A = -U[1, 16],
+    dt_bias with softplus(dt_bias) log-uniform in [1e-3, 1e-1], D ~ U[0.5, 1.5]."""
+    bs = list(range(batch)) if batches is None else list(batches)
+
+    def draw(k, shape):
+        out = np.empty((len(bs),) + shape, np.float32)
+        for i, b in enumerate(bs):
+            out[i] = _rng(seed, TID_SSD + k, b).standard_normal(shape, dtype=np.float32)
+        return _round_bf16(out)
+
+    v = np.exp(_rng(seed, TID_SSD + 5, 0).uniform(np.log(1e-3), np.log(1e-1), size=heads))
+    return {
+        "x": draw(0, (seqlen, heads, headdim)),
+        "delta": draw(1, (seqlen, heads)),
+        "B": draw(2, (seqlen, dstate)),
+        "C": draw(3, (seqlen, dstate)),
+        "A": -_rng(seed, TID_SSD + 4, 0).uniform(1.0, 16.0, size=heads).astype(np.float32),
+        "dt_bias": np.log(np.expm1(v)).astype(np.float32),
+        "D": _rng(seed, TID_SSD + 6, 0).uniform(0.5, 1.5, size=heads).astype(np.float32),
+    }

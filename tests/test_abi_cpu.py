@@ -22,7 +22,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
-            "selscan_bwd", "selscan_conv1d", "selscan_conv1d_step", "selscan_timing_start",
+            "selscan_bwd", "selscan_ssd_fwd", "selscan_conv1d", "selscan_conv1d_step",
+            "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
@@ -42,7 +43,7 @@ def test_error_codes_match_header():
 
 
 def test_version():
-    assert S.version() == 10300
+    assert S.version() == 10400
 
 
 # Fake, 16-byte aligned, non-overlapping device addresses (never dereferenced:
@@ -293,3 +294,33 @@ def test_bwd_argument_checks():
     p = [P(i) for i in range(17)]
     p[13] = ctypes.c_void_p(BASE + 12 * SPAN + 64)  # dC inside dB
     assert bwd_call(D(), p) == S.ERR_ALIAS
+
+
+def ssd_call(dims, ptrs=None):
+    p = [P(i) for i in range(9)] if ptrs is None else ptrs
+    return S.lib.selscan_ssd_fwd(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def SD(batch=2, L=64, heads=4, P=64, N=128, dtype=S.BF16):
+    return S.SsdDims(batch, L, heads, P, N, dtype)
+
+
+def test_ssd_argument_checks():
+    assert ssd_call(None) == S.ERR_NULL
+    assert ssd_call(SD(batch=-1)) == S.ERR_DIMS
+    assert ssd_call(SD(dtype=S.F32)) == S.ERR_DTYPE
+    assert ssd_call(SD(P=32)) == S.ERR_DSTATE
+    assert ssd_call(SD(N=16)) == S.ERR_DSTATE
+    assert ssd_call(SD(L=1 << 27)) == S.ERR_DIMS
+    for idx in (0, 1, 2, 3, 4, 7):            # x, delta, A, B, C, y are required
+        p = [P(i) for i in range(9)]
+        p[idx] = None
+        assert ssd_call(SD(), p) == S.ERR_NULL, idx
+    for idx in range(9):
+        p = [P(i) for i in range(9)]
+        p[idx] = ctypes.c_void_p(BASE + idx * SPAN + 2)
+        assert ssd_call(SD(), p) == S.ERR_ALIGN, idx
+    p = [P(i) for i in range(9)]
+    p[7] = p[0]                                # y == x
+    assert ssd_call(SD(), p) == S.ERR_ALIAS
+    assert ssd_call(SD(batch=0)) == S.OK
