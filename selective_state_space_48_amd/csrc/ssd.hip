@@ -45,6 +45,19 @@ __device__ __forceinline__ bf16x8 lds8(const bf16_bits* p) {
 }
 __device__ __forceinline__ bf16_bits tobf(float v) { return from_f32<bf16_bits>(v); }
 
+// 8 bf16 (16 bytes) from global memory, or zeros.
+__device__ __forceinline__ uint4 ld8(const bf16_bits* p, bool ok) {
+    return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+}
+__device__ __forceinline__ bf16_bits lo16(uint32_t w) { return bf16_bits(w & 0xffffu); }
+__device__ __forceinline__ bf16_bits hi16(uint32_t w) { return bf16_bits(w >> 16); }
+// The 8 values of a 16-byte piece, as bf16 bits, in order.
+__device__ __forceinline__ void split8(const uint4& v, bf16_bits* o) {
+    o[0] = lo16(v.x); o[1] = hi16(v.x); o[2] = lo16(v.y); o[3] = hi16(v.y);
+    o[4] = lo16(v.z); o[5] = hi16(v.z); o[6] = lo16(v.w); o[7] = hi16(v.w);
+}
+__device__ __forceinline__ float bfval(bf16_bits v) { return __uint_as_float(uint32_t(v) << 16); }
+
 struct SsdArgs {
     const bf16_bits* x;     // [batch, L, H, P]
     const bf16_bits* delta; // [batch, L, H]
@@ -100,24 +113,27 @@ __global__ __launch_bounds__(256) void ssd_chunk_state(SsdArgs a) {
     chunk_decays<N>(a, b, h, c, dts, cum);
     __syncthreads();
     const float cend = cum[kQ - 1];
-    // stage: thread -> token s = tid / 4, quarter q = tid % 4 of the row
-    {
-        const int s = tid / 4, q = tid % 4;
+    // Stage B^T and (w x)^T, both transposed: a thread loads a 16-byte piece
+    // (8 consecutive n, or p) of one token's row and writes it down a column;
+    // consecutive threads take consecutive tokens, so the 2-byte LDS writes
+    // of a wave fall in distinct banks.
+    for (int i = tid; i < kQ * (N / 8); i += 256) {
+        const int s = i % kQ, q8 = i / kQ;
+        const int64_t t = int64_t(c) * kQ + s;
+        bf16_bits v[8];
+        split8(ld8(a.B + (b * a.L + t) * N + q8 * 8, t < a.L), v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Bt[(q8 * 8 + e) * QR + s] = v[e];
+    }
+    for (int i = tid; i < kQ * (kP / 8); i += 256) {
+        const int s = i % kQ, q8 = i / kQ;
         const int64_t t = int64_t(c) * kQ + s;
         const bool ok = t < a.L;
         const float w = ok ? exp2_hw(cend - cum[s]) * dts[s] : 0.0f;
-        // B row: N elements, this thread N/4 of them
+        bf16_bits v[8];
+        split8(ld8(a.x + ((b * a.L + t) * a.H + h) * kP + q8 * 8, ok), v);
 #pragma unroll
-        for (int k = 0; k < N / 4; ++k) {
-            const int n = q * (N / 4) + k;
-            Bt[n * QR + s] = ok ? a.B[(b * a.L + t) * N + n] : bf16_bits(0);
-        }
-#pragma unroll
-        for (int k = 0; k < kP / 4; ++k) {
-            const int p = q * (kP / 4) + k;
-            const float xv = ok ? to_f32(a.x[((b * a.L + t) * a.H + h) * kP + p]) : 0.0f;
-            Xt[p * QR + s] = tobf(w * xv);
-        }
+        for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = tobf(w * bfval(v[e]));
     }
     __syncthreads();
     // S^T [P x N] = Xt [P x Q] . Bt^T [Q x N]; tiles of 32 x 32: (P/32) x (N/32), split over 4 waves
@@ -193,24 +209,32 @@ __global__ __launch_bounds__(256) void ssd_chunk_scan(SsdArgs a) {
     const int64_t b = bh / a.H, h = bh % a.H;
     chunk_decays<N>(a, b, h, c, dts, cum);
     __syncthreads();
-    {
-        const int s = tid / 4, q = tid % 4;
+    // C and B rows as they are (16-byte pieces, consecutive threads on
+    // consecutive pieces of a row), C scaled by 2^cum_t as well; x transposed
+    // (consecutive threads on consecutive tokens).
+    for (int i = tid; i < kQ * (N / 8); i += 256) {
+        const int s = i / (N / 8), q8 = i % (N / 8);
         const int64_t t = int64_t(c) * kQ + s;
         const bool ok = t < a.L;
+        const uint4 cv = ld8(a.C + (b * a.L + t) * N + q8 * 8, ok);
+        *reinterpret_cast<uint4*>(&Cs[s * NR + q8 * 8]) = cv;
+        *reinterpret_cast<uint4*>(&Bs[s * NR + q8 * 8]) = ld8(a.B + (b * a.L + t) * N + q8 * 8, ok);
         const float gw = exp2_hw(cum[s]);
+        bf16_bits v[8];
+        split8(cv, v);
+        uint32_t wv4[4];
 #pragma unroll
-        for (int k = 0; k < N / 4; ++k) {
-            const int n = q * (N / 4) + k;
-            const bf16_bits cv = ok ? a.C[(b * a.L + t) * N + n] : bf16_bits(0);
-            Cs[s * NR + n] = cv;
-            Cw[s * NR + n] = tobf(gw * to_f32(cv));
-            Bs[s * NR + n] = ok ? a.B[(b * a.L + t) * N + n] : bf16_bits(0);
-        }
+        for (int e = 0; e < 4; ++e)
+            wv4[e] = uint32_t(tobf(gw * bfval(v[2 * e]))) | (uint32_t(tobf(gw * bfval(v[2 * e + 1]))) << 16);
+        *reinterpret_cast<uint4*>(&Cw[s * NR + q8 * 8]) = make_uint4(wv4[0], wv4[1], wv4[2], wv4[3]);
+    }
+    for (int i = tid; i < kQ * (kP / 8); i += 256) {
+        const int s = i % kQ, q8 = i / kQ;
+        const int64_t t = int64_t(c) * kQ + s;
+        bf16_bits v[8];
+        split8(ld8(a.x + ((b * a.L + t) * a.H + h) * kP + q8 * 8, t < a.L), v);
 #pragma unroll
-        for (int k = 0; k < kP / 4; ++k) {
-            const int p = q * (kP / 4) + k;
-            Xt[p * QR + s] = ok ? a.x[((b * a.L + t) * a.H + h) * kP + p] : bf16_bits(0);
-        }
+        for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = v[e];
     }
     __syncthreads();
     // scores G = C B^T [Q x Q], one 32 x 32 tile per wave: (t block, s block)
