@@ -330,8 +330,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // ---- the scan over one chunk: this wave's NG states, all CH tokens ----
     // Software pipeline, one sub-block ahead: wait for the previous loads,
     // issue the next sub-block's B/C record (scalar) and (l, w) (LDS) loads,
-    // then compute from registers only. lgkmcnt covers both kinds of load, so
-    // the wait must come before the next loads are issued.
+    // then compute from registers only. lgkmcnt covers both kinds of load (and
+    // LDS writes), so the wait must come before the next loads are issued; for
+    // the same reason a sub-block's partial readouts are written to LDS one
+    // sub-block later, right after those loads, so that the next wait does not
+    // wait for a write issued just before it.
     auto scan_chunk = [&](int c) {
         const int64_t s0 = (t_begin + int64_t(c) * CH) / SB;          // first sub-block
         const float* rec = a.P + ((b * a.psub + s0) * G + wv) * kRec;  // this wave's record
@@ -344,8 +347,21 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         float2 l0[SB], l1[SB];
 #pragma unroll
         for (int e = 0; e < SB; ++e) l0[e] = lw2[e];
+        float yA[SB], yB[SB];
+        auto put = [&](int sb, const float* yv) {  // partial readouts of sub-block sb
+            if constexpr (SB >= 4) {
+#pragma unroll
+                for (int k = 0; k < SB / 4; ++k)
+                    *reinterpret_cast<float4*>(yrow + sb * SB + 4 * k) =
+                        make_float4(yv[4 * k], yv[4 * k + 1], yv[4 * k + 2], yv[4 * k + 3]);
+            } else if constexpr (SB == 2) {
+                *reinterpret_cast<float2*>(yrow + sb * SB) = make_float2(yv[0], yv[1]);
+            } else {
+                yrow[sb] = yv[0];
+            }
+        };
         auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float2* lc, f32x16& Bn,
-                        f32x16& Cn, float2* ln) {
+                        f32x16& Cn, float2* ln, const float* yprev, float* yv) {
             const int sbn = sb + 1 < NSB ? sb + 1 : sb;  // stays inside the chunk
             if constexpr (MODE == 2) {
                 // the state before tokens 0 and 16 of the chunk
@@ -361,38 +377,43 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             if constexpr (READOUT) Cn = sload64(nrec + 16);
 #pragma unroll
             for (int e = 0; e < SB; ++e) ln[e] = lw2[sbn * SB + e];
+            // The previous sub-block's readouts. At sb = 0 there is none: the
+            // write goes to the chunk's last slot, which the final write below
+            // overwrites (same wave, LDS accesses in order).
+            if constexpr (READOUT) put((sb + NSB - 1) % NSB, yprev);
             __builtin_amdgcn_sched_barrier(0);
-            float yv[SB];
+            // All decays and input terms first, then the dependent FMAs, so
+            // that no FMA is scheduled right behind the exponential it uses.
+            float dA[SB][NG], u[SB][NG];
+#pragma unroll
+            for (int e = 0; e < SB; ++e)
+#pragma unroll
+                for (int j = 0; j < NG; ++j) dA[e][j] = exp2_hw(lc[e].x * An[j]);
+#pragma unroll
+            for (int e = 0; e < SB; ++e)
+#pragma unroll
+                for (int j = 0; j < NG; ++j) u[e][j] = lc[e].y * Bc[j * SB + e];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < SB; ++e) {
                 float acc = 0.0f;
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
-                    const float dA = exp2_hw(lc[e].x * An[j]);
-                    h[j] = fmaf(dA, h[j], lc[e].y * Bc[j * SB + e]);
+                    h[j] = fmaf(dA[e][j], h[j], u[e][j]);
                     if constexpr (READOUT) acc = fmaf(Cc[j * SB + e], h[j], acc);
                 }
                 yv[e] = acc;
             }
-            if constexpr (READOUT) {
-                if constexpr (SB >= 4) {
-#pragma unroll
-                    for (int k = 0; k < SB / 4; ++k)
-                        *reinterpret_cast<float4*>(yrow + sb * SB + 4 * k) =
-                            make_float4(yv[4 * k], yv[4 * k + 1], yv[4 * k + 2], yv[4 * k + 3]);
-                } else if constexpr (SB == 2) {
-                    *reinterpret_cast<float2*>(yrow + sb * SB) = make_float2(yv[0], yv[1]);
-                } else {
-                    yrow[sb] = yv[0];
-                }
-            }
         };
         static_assert(NSB % 2 == 0, "sub-blocks per chunk must be even");
+#pragma unroll
+        for (int e = 0; e < SB; ++e) yB[e] = 0.0f;
 #pragma unroll 1
         for (int sb = 0; sb < NSB; sb += 2) {
-            half(sb, B0, C0, l0, B1, C1, l1);
-            half(sb + 1, B1, C1, l1, B0, C0, l0);
+            half(sb, B0, C0, l0, B1, C1, l1, yB, yA);
+            half(sb + 1, B1, C1, l1, B0, C0, l0, yA, yB);
         }
+        if constexpr (READOUT) put(NSB - 1, yB);
     };
 
     // ---- per-token phase after the scan: sum partial readouts, D skip, gate, store ----
