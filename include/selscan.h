@@ -233,10 +233,11 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
  *   last_state : [B, H, N, P] fp32 output or NULL
  * dims: batch B, seqlen L (< 2^27), heads H, headdim P (64), dstate N (64 or
  * 128), dtype SELSCAN_BF16 (anything else: SELSCAN_ERR_DTYPE; other P or N:
- * SELSCAN_ERR_DSTATE). Workspace: B H ceil(L/64) P N 6 bytes (chunk states),
- * taken with hipMallocAsync on the stream. Outputs must not overlap inputs.
- * Products in bf16 with fp32 sums (the within-chunk scores and the scaled C
- * are rounded to bf16 as matrix-core operands). Deterministic.
+ * SELSCAN_ERR_DSTATE). No workspace: one workgroup per (batch, head) walks
+ * the 64-token chunks in order with the state on chip. Outputs must not
+ * overlap inputs. Products in bf16 with fp32 sums (the within-chunk scores,
+ * the decay-weighted B and the carried state are rounded to bf16 as
+ * matrix-core operands; the state is accumulated in fp32). Deterministic.
  */
 typedef struct {
     int64_t batch;

@@ -391,15 +391,8 @@ int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void
         if (last_state && launch_fill_zero(last_state, st, stm) != hipSuccess) return SELSCAN_ERR_LAUNCH;
         return SELSCAN_OK;
     }
-    const size_t ws_bytes = ssd_workspace_bytes(dims->batch, dims->seqlen, dims->heads, dims->dstate);
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, ws_bytes, stm) != hipSuccess || !ws) {
-        (void)hipGetLastError();
-        return SELSCAN_ERR_ALLOC;
-    }
     SsdTensors tt{x, delta, A, B, C, D, dt_bias, y, last_state};
-    const hipError_t e = launch_ssd(tt, dims->batch, dims->seqlen, dims->heads, dims->dstate, ws, stm);
-    (void)hipFreeAsync(ws, stm);
+    const hipError_t e = launch_ssd(tt, dims->batch, dims->seqlen, dims->heads, dims->dstate, stm);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 

@@ -117,9 +117,8 @@ struct SsdTensors {
     void* y;
     float* last_state;
 };
-size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t heads, int64_t dstate);
 hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t heads, int64_t dstate,
-                      void* workspace, hipStream_t stream);
+                      hipStream_t stream);
 
 // Causal depthwise conv (width 4) + SiLU. x/out: [rows, L]; w: [dim, 4];
 // bias: [dim] or null; x_prev/x_last: [rows, 3] fp32 or null.

@@ -11,19 +11,25 @@
 // Its dual is a masked matrix product, y = (L o C B^T)(delta x) + D x with
 // L[t,s] = a_{s+1} ... a_t, a semiseparable matrix; cutting the sequence into
 // chunks of Q tokens splits it into diagonal blocks (small dense products)
-// and low-rank off-diagonal parts carried by the chunk states. That is what
-// makes the layer matrix-multiply work:
-//   chunk_state: S_c = sum_{s in c} exp(cum_end - cum_s) delta_s B_s x_s^T
-//   state_pass:  H_{c+1} = exp(cum_end(c)) H_c + S_c       (sequential in c)
-//   chunk_scan:  y_t = sum_{s<=t in c} [C_t.B_s] exp(cum_t - cum_s) delta_s x_s
-//                      + exp(cum_t) C_t^T H_c + D x_t
-// with cum the running sum of delta A within the chunk (base 2 here). The
-// products run on v_mfma_f32_32x32x16_bf16: bf16 operands (the inputs, and
-// the masked-and-scaled score and scaled C rounded to bf16), fp32 sums.
+// and low-rank off-diagonal parts carried by the state between chunks. Per
+// chunk, with cum_t the running sum of log2-decays inside the chunk and
+// H the state entering it:
+//   y_t   = sum_{s<=t} [C_t . B_s] 2^(cum_t - cum_s) delta_s x_s      (scores)
+//         + 2^(cum_t) C_t^T H + D x_t                                  (carry-in)
+//   H'    = 2^(cum_end) H + sum_s 2^(cum_end - cum_s) delta_s B_s x_s^T
+// Every product is a v_mfma_f32_32x32x16_bf16: bf16 operands (the inputs,
+// the masked and scaled scores, the scaled B and the carried state rounded
+// to bf16 as operands), fp32 sums; the state itself is accumulated in fp32.
 //
-// One workgroup (4 waves) per (batch, head, chunk of 64 tokens); headdim 64,
-// dstate 64 or 128. Tiles are staged in LDS with rows padded by 16 bytes so
-// that the 16-byte operand reads of 32 lanes on 32 rows spread over the banks.
+// One workgroup (4 waves) per (batch, head) walks the chunks in order and
+// keeps the state in matrix-core accumulators, so no chunk state ever goes
+// to HBM: x, delta, B and C are read once (B and C, shared by the heads, from
+// L2 after the first head) and y is written once. Wave w owns the 32 x 32
+// output tile (t block w/2, p block w%2) and the state tiles of p block w%2
+// for half of the state rows; the state crosses waves through LDS as bf16.
+// Tiles are staged in LDS with rows padded by 16 bytes so that the 16-byte
+// operand reads of 32 lanes on 32 rows spread over the banks. The next
+// chunk's inputs are loaded into registers while the current one computes.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,27 +42,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kQ = 64;   // tokens per chunk
 constexpr int kP = 64;   // headdim
 
+// acc[r] of a 32 x 32 MFMA tile is element (row, col) = (8*(r/4) + 4*(lane/32) + r%4, lane%32);
+// operands: lane holds 8 consecutive K of row lane%32 (A) or column lane%32 (B), K offset 8*(lane/32).
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r / 4) + 4 * (lane / 32) + r % 4; }
 // 8 consecutive bf16 from LDS (16 bytes, aligned).
 __device__ __forceinline__ bf16x8 lds8(const bf16_bits* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 __device__ __forceinline__ bf16_bits tobf(float v) { return from_f32<bf16_bits>(v); }
-
-// 8 bf16 (16 bytes) from global memory, or zeros.
-__device__ __forceinline__ uint4 ld8(const bf16_bits* p, bool ok) {
-    return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-}
-__device__ __forceinline__ bf16_bits lo16(uint32_t w) { return bf16_bits(w & 0xffffu); }
-__device__ __forceinline__ bf16_bits hi16(uint32_t w) { return bf16_bits(w >> 16); }
-// The 8 values of a 16-byte piece, as bf16 bits, in order.
-__device__ __forceinline__ void split8(const uint4& v, bf16_bits* o) {
-    o[0] = lo16(v.x); o[1] = hi16(v.x); o[2] = lo16(v.y); o[3] = hi16(v.y);
-    o[4] = lo16(v.z); o[5] = hi16(v.z); o[6] = lo16(v.w); o[7] = hi16(v.w);
-}
 __device__ __forceinline__ float bfval(bf16_bits v) { return __uint_as_float(uint32_t(v) << 16); }
+// The 8 bf16 of a 16-byte piece, in order.
+__device__ __forceinline__ void split8(const uint4& v, bf16_bits* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o[2 * k] = bf16_bits(w[k] & 0xffffu);
+        o[2 * k + 1] = bf16_bits(w[k] >> 16);
+    }
+}
 
 struct SsdArgs {
     const bf16_bits* x;     // [batch, L, H, P]
@@ -68,249 +74,206 @@ struct SsdArgs {
     const float* dt_bias;   // [H] or null
     bf16_bits* y;           // [batch, L, H, P]
     float* last_state;      // [batch, H, N, P] or null
-    float* S;               // [batch*H*nc][P][N] chunk states (transposed)
-    float* tot;             // [batch*H*nc] base-2 log of the chunk's total decay
-    bf16_bits* Hin;         // [batch*H*nc][P][N] state entering each chunk (transposed)
     int64_t batch, L, H;
-    int32_t nc;
 };
 
-// delta_t and the running sum of log2-decays of the chunk's tokens, into LDS;
-// tokens past L get delta 0 (an identity step). One wave computes the scan.
+// One chunk's inputs as this thread loads them: token s = lane of B, C and x
+// pieces (16 bytes each; B and C pieces wv + 4k of N/8, x pieces wv + 4k of
+// 8) and the raw step of token lane.
 template <int N>
-__device__ __forceinline__ void chunk_decays(const SsdArgs& a, int64_t b, int64_t h, int c, float* dts,
-                                             float* cum) {
-    const int tid = threadIdx.x;
-    if (tid < kQ) {
-        const int64_t t = int64_t(c) * kQ + tid;
-        float dt = 0.0f;
-        if (t < a.L) {
-            const float u = to_f32(a.delta[(b * a.L + t) * a.H + h]) + (a.dt_bias ? a.dt_bias[h] : 0.0f);
-            dt = softplus_log2(u) * kLn2;
+struct ChunkRegs {
+    static constexpr int NB = N / 8 / 4;  // 16-byte pieces of a B (or C) row per thread
+    uint4 b[NB], c[NB], x[2];
+    float dl;
+    bool ok;  // token lane exists (tokens past the end take step 0: an identity step)
+};
+
+template <int N>
+__global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
+    constexpr int NR = N + 8;        // row stride (bf16) of [.][n] tiles
+    constexpr int QR = kQ + 8;       // row stride of [.][s] tiles
+    constexpr int NT = N / 32;       // 32-row tiles of the state
+    constexpr int NTW = NT / 2;      // state tiles per wave
+    using R = ChunkRegs<N>;
+    __shared__ alignas(16) bf16_bits Cs[kQ * NR];      // C rows [t][n]
+    __shared__ alignas(16) bf16_bits BsMs[kQ * NR];    // B rows [s][n]; later the masked scores [t][s]
+    __shared__ alignas(16) bf16_bits Bw[N * QR];       // 2^(cum_end - cum_s) delta_s B^T: [n][s]
+    __shared__ alignas(16) bf16_bits Xt[kP * QR];      // x^T [p][s]
+    __shared__ alignas(16) bf16_bits Ht[kP * NR];      // the state entering the chunk, bf16, [p][n]
+    __shared__ float cums[kQ], dts[kQ];                // running log2-decay and step of the chunk's tokens
+    bf16_bits* Ms = BsMs;
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int pb = wv % 2, tb = wv / 2;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int nc = int((a.L + kQ - 1) / kQ);
+    const float Ah = a.A[h] * kLog2e;                      // log2 decay per unit step
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float Dh = a.D ? a.D[h] : 0.0f;
+
+    // Loads are unconditional (a token past the end reads the last token's
+    // row: valid memory) so that they need no branches; staging zeroes such
+    // tokens, whose step is 0 (an identity step).
+    auto load = [&](int c, R& r) {
+        const int64_t t = int64_t(c) * kQ + lane;
+        r.ok = t < a.L;
+        const int64_t tt = r.ok ? t : a.L - 1;
+#pragma unroll
+        for (int k = 0; k < R::NB; ++k) {
+            const int q8 = wv + 4 * k;
+            r.b[k] = *reinterpret_cast<const uint4*>(a.B + (b * a.L + tt) * N + q8 * 8);
+            r.c[k] = *reinterpret_cast<const uint4*>(a.C + (b * a.L + tt) * N + q8 * 8);
         }
-        float v = dt * a.A[h] * kLog2e;  // log2 of this token's decay
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            r.x[k] = *reinterpret_cast<const uint4*>(a.x + ((b * a.L + tt) * a.H + h) * kP + (wv + 4 * k) * 8);
+        r.dl = to_f32(a.delta[(b * a.L + tt) * a.H + h]);
+    };
+
+    // State tiles (fp32 accumulators): H^T rows p = 32 pb + acc_row, columns
+    // n = 32 (tb NTW + j) + lane % 32.
+    f32x16 H[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
+    for (int i = tid; i < kP * NR; i += 256) Ht[i] = 0;
+
+    R cur;
+    load(0, cur);
+    for (int c = 0; c < nc; ++c) {
+        // ---- per-token: step size and running log2-decay, token = lane (every wave) ----
+        const float dt = cur.ok ? softplus_log2(cur.dl + bias) * kLn2 : 0.0f;
+        float cum = dt * Ah;
 #pragma unroll
         for (int o = 1; o < kQ; o <<= 1) {
-            const float w = __shfl_up(v, o, kQ);
-            if (tid >= o) v += w;
+            const float w = __shfl_up(cum, o, kQ);
+            if (lane >= o) cum += w;
         }
-        dts[tid] = dt;
-        cum[tid] = v;
-    }
-}
+        const float cend = __shfl(cum, kQ - 1, kQ);
+        // ---- stage chunk c ----
+        {
+            const int s = lane;
+            if (wv == 0) {
+                cums[s] = cum;
+                dts[s] = dt;
+            }
+            const float ws = exp2_hw(cend - cum) * dt;  // weight of token s in the state update
+            const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < R::NB; ++k)
+                if (!cur.ok) cur.b[k] = cur.c[k] = zero;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                if (!cur.ok) cur.x[k] = zero;
+#pragma unroll
+            for (int k = 0; k < R::NB; ++k) {
+                const int q8 = wv + 4 * k;
+                *reinterpret_cast<uint4*>(&Cs[s * NR + q8 * 8]) = cur.c[k];
+                *reinterpret_cast<uint4*>(&BsMs[s * NR + q8 * 8]) = cur.b[k];
+                bf16_bits v[8];
+                split8(cur.b[k], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) Bw[(q8 * 8 + e) * QR + s] = tobf(ws * bfval(v[e]));
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int q8 = wv + 4 * k;
+                bf16_bits v[8];
+                split8(cur.x[k], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = v[e];
+            }
+        }
+        load(c + 1, cur);  // next chunk's inputs, in flight during this chunk
+        __syncthreads();
 
-// ---- chunk_state: S_c^T[p][n] = sum_s x[s][p] w_s B[s][n], w_s = 2^(cum_end - cum_s) delta_s ----
-template <int N>
-__global__ __launch_bounds__(256) void ssd_chunk_state(SsdArgs a) {
-    constexpr int QR = kQ + 8;
-    __shared__ alignas(16) bf16_bits Bt[N * QR];    // B^T: [n][s]
-    __shared__ alignas(16) bf16_bits Xt[kP * QR];   // (w x)^T: [p][s]
-    __shared__ float dts[kQ], cum[kQ];
-    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
-    const int c = int(blockIdx.x % unsigned(a.nc));
-    const int64_t bh = blockIdx.x / unsigned(a.nc);
-    const int64_t b = bh / a.H, h = bh % a.H;
-    chunk_decays<N>(a, b, h, c, dts, cum);
-    __syncthreads();
-    const float cend = cum[kQ - 1];
-    // Stage B^T and (w x)^T, both transposed: a thread loads a 16-byte piece
-    // (8 consecutive n, or p) of one token's row and writes it down a column;
-    // consecutive threads take consecutive tokens, so the 2-byte LDS writes
-    // of a wave fall in distinct banks.
-    for (int i = tid; i < kQ * (N / 8); i += 256) {
-        const int s = i % kQ, q8 = i / kQ;
-        const int64_t t = int64_t(c) * kQ + s;
-        bf16_bits v[8];
-        split8(ld8(a.B + (b * a.L + t) * N + q8 * 8, t < a.L), v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Bt[(q8 * 8 + e) * QR + s] = v[e];
-    }
-    for (int i = tid; i < kQ * (kP / 8); i += 256) {
-        const int s = i % kQ, q8 = i / kQ;
-        const int64_t t = int64_t(c) * kQ + s;
-        const bool ok = t < a.L;
-        const float w = ok ? exp2_hw(cend - cum[s]) * dts[s] : 0.0f;
-        bf16_bits v[8];
-        split8(ld8(a.x + ((b * a.L + t) * a.H + h) * kP + q8 * 8, ok), v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = tobf(w * bfval(v[e]));
-    }
-    __syncthreads();
-    // S^T [P x N] = Xt [P x Q] . Bt^T [Q x N]; tiles of 32 x 32: (P/32) x (N/32), split over 4 waves
-    constexpr int TI = kP / 32, TJ = N / 32, TILES = TI * TJ, PER = TILES / 4;
-    const int64_t base = (bh * a.nc + c) * int64_t(kP) * N;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int tile = wv * PER + u;
-        const int ti = tile / TJ, tj = tile % TJ;
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < kQ / 16; ++ks) {
-            const int k0 = ks * 16 + 8 * (lane / 32);
-            const bf16x8 av = lds8(&Xt[(ti * 32 + lane % 32) * QR + k0]);
-            const bf16x8 bv = lds8(&Bt[(tj * 32 + lane % 32) * QR + k0]);
-            acc = mfma(av, bv, acc);
-        }
-        // acc[r] = S^T[ti*32 + 8*(r/4) + 4*(lane/32) + r%4][tj*32 + lane%32]
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = ti * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-            const int n = tj * 32 + lane % 32;
-            a.S[base + int64_t(p) * N + n] = acc[r];
-        }
-    }
-    if (tid == 0) a.tot[bh * a.nc + c] = cend;
-}
-
-// ---- state_pass: H_in[c] = state entering chunk c; H <- 2^tot_c H + S_c ----
-template <int N>
-__global__ __launch_bounds__(256) void ssd_state_pass(SsdArgs a) {
-    constexpr int E = kP * N / 256;  // elements per thread
-    const int64_t bh = blockIdx.x;
-    const int tid = threadIdx.x;
-    float H[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) H[e] = 0.0f;
-    for (int c = 0; c < a.nc; ++c) {
-        const int64_t base = (bh * a.nc + c) * int64_t(kP) * N;
-        const float g = exp2_hw(a.tot[bh * a.nc + c]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int64_t i = int64_t(e) * 256 + tid;
-            a.Hin[base + i] = tobf(H[e]);
-            H[e] = fmaf(g, H[e], a.S[base + i]);
-        }
-    }
-    if (a.last_state) {
-        const int64_t b = bh / a.H, h = bh % a.H;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int i = e * 256 + tid;      // = p * N + n
-            const int p = i / N, n = i % N;
-            a.last_state[((b * a.H + h) * N + n) * kP + p] = H[e];
-        }
-    }
-}
-
-// ---- chunk_scan: y = (L o C B^T)(delta x) + (2^cum o C) H_in + D x ----
-template <int N>
-__global__ __launch_bounds__(256) void ssd_chunk_scan(SsdArgs a) {
-    constexpr int NR = N + 8;
-    constexpr int QR = kQ + 8;
-    __shared__ alignas(16) bf16_bits Cs[kQ * NR];   // C rows [t][n]
-    __shared__ alignas(16) bf16_bits Cw[kQ * NR];   // 2^cum_t C rows [t][n]
-    __shared__ alignas(16) bf16_bits Bs[kQ * NR];   // B rows [s][n]
-    __shared__ alignas(16) bf16_bits Xt[kP * QR];   // x^T [p][s]
-    __shared__ alignas(16) bf16_bits Ms[kQ * QR];   // masked, scaled scores [t][s]
-    __shared__ float dts[kQ], cum[kQ];
-    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
-    const int c = int(blockIdx.x % unsigned(a.nc));
-    const int64_t bh = blockIdx.x / unsigned(a.nc);
-    const int64_t b = bh / a.H, h = bh % a.H;
-    chunk_decays<N>(a, b, h, c, dts, cum);
-    __syncthreads();
-    // C and B rows as they are (16-byte pieces, consecutive threads on
-    // consecutive pieces of a row), C scaled by 2^cum_t as well; x transposed
-    // (consecutive threads on consecutive tokens).
-    for (int i = tid; i < kQ * (N / 8); i += 256) {
-        const int s = i / (N / 8), q8 = i % (N / 8);
-        const int64_t t = int64_t(c) * kQ + s;
-        const bool ok = t < a.L;
-        const uint4 cv = ld8(a.C + (b * a.L + t) * N + q8 * 8, ok);
-        *reinterpret_cast<uint4*>(&Cs[s * NR + q8 * 8]) = cv;
-        *reinterpret_cast<uint4*>(&Bs[s * NR + q8 * 8]) = ld8(a.B + (b * a.L + t) * N + q8 * 8, ok);
-        const float gw = exp2_hw(cum[s]);
-        bf16_bits v[8];
-        split8(cv, v);
-        uint32_t wv4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            wv4[e] = uint32_t(tobf(gw * bfval(v[2 * e]))) | (uint32_t(tobf(gw * bfval(v[2 * e + 1]))) << 16);
-        *reinterpret_cast<uint4*>(&Cw[s * NR + q8 * 8]) = make_uint4(wv4[0], wv4[1], wv4[2], wv4[3]);
-    }
-    for (int i = tid; i < kQ * (kP / 8); i += 256) {
-        const int s = i % kQ, q8 = i / kQ;
-        const int64_t t = int64_t(c) * kQ + s;
-        bf16_bits v[8];
-        split8(ld8(a.x + ((b * a.L + t) * a.H + h) * kP + q8 * 8, t < a.L), v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = v[e];
-    }
-    __syncthreads();
-    // scores G = C B^T [Q x Q], one 32 x 32 tile per wave: (t block, s block)
-    {
-        const int tb = wv / 2, sb = wv % 2;
-        f32x16 g = {};
-        if (sb <= tb) {
+        // ---- scores of the lower block triangle: wave 0 (0,0), wave 1 (1,0), wave 2 (1,1) ----
+        const int gt = wv == 0 ? 0 : 1, gs = wv == 2 ? 1 : 0;
+        f32x16 G = {};
+        if (wv < 3) {
 #pragma unroll
             for (int ks = 0; ks < N / 16; ++ks) {
                 const int k0 = ks * 16 + 8 * (lane / 32);
-                g = mfma(lds8(&Cs[(tb * 32 + lane % 32) * NR + k0]), lds8(&Bs[(sb * 32 + lane % 32) * NR + k0]), g);
+                G = mfma(lds8(&Cs[(gt * 32 + lane % 32) * NR + k0]), lds8(&BsMs[(gs * 32 + lane % 32) * NR + k0]), G);
             }
         }
-        // M[t][s] = G[t][s] 2^(cum_t - cum_s) delta_s for s <= t, else 0
-        const int s = sb * 32 + lane % 32;
+        __syncthreads();  // every read of B rows is done: the scores take their place
+        if (wv < 3) {
+            const int s = gs * 32 + lane % 32;
+            const float cs = cums[s], ds = dts[s];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = tb * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-            const float m = s <= t ? g[r] * exp2_hw(cum[t] - cum[s]) * dts[s] : 0.0f;
-            Ms[t * QR + s] = tobf(m);
+            for (int r = 0; r < 16; ++r) {
+                const int t = gt * 32 + acc_row(r, lane);
+                const float m = s <= t ? G[r] * exp2_hw(cums[t] - cs) * ds : 0.0f;
+                Ms[t * QR + s] = tobf(m);
+            }
+        }
+        __syncthreads();
+
+        // ---- output tile (tb, pb): scores x x  +  2^cum_t (C H)  +  D x ----
+        {
+            f32x16 y1 = {}, y2 = {};
+#pragma unroll
+            for (int ks = 0; ks < kQ / 16; ++ks) {
+                if (ks < 2 * (tb + 1)) {  // s blocks above the diagonal are all masked
+                    const int k0 = ks * 16 + 8 * (lane / 32);
+                    y1 = mfma(lds8(&Ms[(tb * 32 + lane % 32) * QR + k0]), lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), y1);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < N / 16; ++ks) {
+                const int k0 = ks * 16 + 8 * (lane / 32);
+                y2 = mfma(lds8(&Cs[(tb * 32 + lane % 32) * NR + k0]), lds8(&Ht[(pb * 32 + lane % 32) * NR + k0]), y2);
+            }
+            const int p = pb * 32 + lane % 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tl = tb * 32 + acc_row(r, lane);
+                const float g = exp2_hw(cums[tl]);
+                const float v = fmaf(g, y2[r], y1[r]) + Dh * bfval(Xt[p * QR + tl]);
+                const int64_t t = int64_t(c) * kQ + tl;
+                if (t < a.L) a.y[((b * a.L + t) * a.H + h) * kP + p] = tobf(v);
+            }
+        }
+        // ---- state: H^T <- 2^cum_end H^T + x^T (w B) over this wave's tiles ----
+        {
+            const float gend = exp2_hw(cend);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int nb = tb * NTW + j;
+                f32x16 acc = H[j] * gend;
+#pragma unroll
+                for (int ks = 0; ks < kQ / 16; ++ks) {
+                    const int k0 = ks * 16 + 8 * (lane / 32);
+                    acc = mfma(lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), lds8(&Bw[(nb * 32 + lane % 32) * QR + k0]), acc);
+                }
+                H[j] = acc;
+            }
+        }
+        __syncthreads();  // every read of this chunk's tiles and of Ht is done
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int n = (tb * NTW + j) * 32 + lane % 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ht[(pb * 32 + acc_row(r, lane)) * NR + n] = tobf(H[j][r]);
         }
     }
-    __syncthreads();
-    // y [Q x P]: one 32 x 32 tile per wave (t block, p block)
-    const int tb = wv / 2, pb = wv % 2;
-    f32x16 acc = {};
+    if (a.last_state) {
+        float* dst = a.last_state + (b * a.H + h) * int64_t(N) * kP;
 #pragma unroll
-    for (int ks = 0; ks < kQ / 16; ++ks) {   // + M x
-        const int k0 = ks * 16 + 8 * (lane / 32);
-        acc = mfma(lds8(&Ms[(tb * 32 + lane % 32) * QR + k0]), lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), acc);
-    }
-    const bf16_bits* Hc = a.Hin + (bh * a.nc + c) * int64_t(kP) * N + int64_t(pb * 32 + lane % 32) * N;
+        for (int j = 0; j < NTW; ++j) {
+            const int n = (tb * NTW + j) * 32 + lane % 32;
 #pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) {    // + (2^cum o C) H_in
-        const int k0 = ks * 16 + 8 * (lane / 32);
-        acc = mfma(lds8(&Cw[(tb * 32 + lane % 32) * NR + k0]), *reinterpret_cast<const bf16x8*>(Hc + k0), acc);
-    }
-    const float Dh = a.D ? a.D[h] : 0.0f;
-    const int p = pb * 32 + lane % 32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int tl = tb * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-        const int64_t t = int64_t(c) * kQ + tl;
-        if (t < a.L) {
-            const int64_t o = ((b * a.L + t) * a.H + h) * kP + p;
-            a.y[o] = tobf(fmaf(Dh, to_f32(Xt[p * QR + tl]), acc[r]));
+            for (int r = 0; r < 16; ++r) dst[int64_t(n) * kP + pb * 32 + acc_row(r, lane)] = H[j][r];
         }
     }
 }
-
-template <int N>
-hipError_t ssd_n(const SsdArgs& k, hipStream_t st) {
-    const int64_t pairs = k.batch * k.H;
-    const dim3 block(256);
-    hipLaunchKernelGGL((ssd_chunk_state<N>), dim3(unsigned(pairs * k.nc)), block, 0, st, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ssd_state_pass<N>), dim3(unsigned(pairs)), block, 0, st, k);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ssd_chunk_scan<N>), dim3(unsigned(pairs * k.nc)), block, 0, st, k);
-    return hipGetLastError();
-}
-
-size_t al256s(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace
 
-size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t heads, int64_t dstate) {
-    const size_t blocks = size_t(batch) * size_t(heads) * size_t((L + kQ - 1) / kQ);
-    return al256s(blocks * kP * size_t(dstate) * 4) + al256s(blocks * 4) +
-           al256s(blocks * kP * size_t(dstate) * 2);
-}
-
 hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t heads, int64_t dstate,
-                      void* workspace, hipStream_t stream) {
+                      hipStream_t stream) {
     SsdArgs k{};
     k.x = static_cast<const bf16_bits*>(t.x);
     k.delta = static_cast<const bf16_bits*>(t.delta);
@@ -322,15 +285,10 @@ hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t hea
     k.y = static_cast<bf16_bits*>(t.y);
     k.last_state = t.last_state;
     k.batch = batch; k.L = L; k.H = heads;
-    k.nc = int32_t((L + kQ - 1) / kQ);
-    const size_t blocks = size_t(batch) * size_t(heads) * size_t(k.nc);
-    unsigned char* w = static_cast<unsigned char*>(workspace);
-    k.S = reinterpret_cast<float*>(w);
-    w += al256s(blocks * kP * size_t(dstate) * 4);
-    k.tot = reinterpret_cast<float*>(w);
-    w += al256s(blocks * 4);
-    k.Hin = reinterpret_cast<bf16_bits*>(w);
-    return dstate == 64 ? ssd_n<64>(k, stream) : ssd_n<128>(k, stream);
+    const dim3 grid(unsigned(batch * heads)), block(256);
+    if (dstate == 64) hipLaunchKernelGGL((ssd_fused<64>), grid, block, 0, stream, k);
+    else hipLaunchKernelGGL((ssd_fused<128>), grid, block, 0, stream, k);
+    return hipGetLastError();
 }
 
 }  // namespace selscan
