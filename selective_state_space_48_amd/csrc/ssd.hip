@@ -64,6 +64,24 @@ __device__ __forceinline__ void split8(const uint4& v, bf16_bits* o) {
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps by
+// DPP row shifts inside each row of 16 lanes (zero-filled), then the row
+// totals carried across rows by the row broadcasts of lanes 15 and 31.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shifted(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v += dpp_shifted<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_shifted<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_shifted<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_shifted<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_shifted<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_shifted<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 struct SsdArgs {
     const bf16_bits* x;     // [batch, L, H, P]
     const bf16_bits* delta; // [batch, L, H]
@@ -143,14 +161,10 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     load(0, cur);
     for (int c = 0; c < nc; ++c) {
         // ---- per-token: step size and running log2-decay, token = lane (every wave) ----
-        const float dt = cur.ok ? softplus_log2(cur.dl + bias) * kLn2 : 0.0f;
-        float cum = dt * Ah;
-#pragma unroll
-        for (int o = 1; o < kQ; o <<= 1) {
-            const float w = __shfl_up(cum, o, kQ);
-            if (lane >= o) cum += w;
-        }
-        const float cend = __shfl(cum, kQ - 1, kQ);
+        const float sp = softplus_log2(cur.dl + bias) * kLn2;
+        const float dt = cur.ok ? sp : 0.0f;
+        const float cum = wave_prefix_sum(dt * Ah);
+        const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), kQ - 1));
         // ---- stage chunk c ----
         {
             const int s = lane;
@@ -200,13 +214,18 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         }
         __syncthreads();  // every read of B rows is done: the scores take their place
         if (wv < 3) {
+            // Branch-free: every lane forms its 16 values and keeps those on
+            // or below the diagonal (the exponent is clamped at 0 above it).
             const int s = gs * 32 + lane % 32;
             const float cs = cums[s], ds = dts[s];
+            const int t0 = gt * 32 + 4 * (lane / 32);  // row of G[0]
+            const float* crow = &cums[t0];
+            bf16_bits* mrow = &Ms[t0 * QR + s];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int t = gt * 32 + acc_row(r, lane);
-                const float m = s <= t ? G[r] * exp2_hw(cums[t] - cs) * ds : 0.0f;
-                Ms[t * QR + s] = tobf(m);
+                const int dr = 8 * (r / 4) + r % 4;
+                const float m = G[r] * exp2_hw(fminf(crow[dr] - cs, 0.0f)) * ds;
+                mrow[dr * QR] = tobf(t0 + dr >= s ? m : 0.0f);
             }
         }
         __syncthreads();
@@ -227,13 +246,32 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 y2 = mfma(lds8(&Cs[(tb * 32 + lane % 32) * NR + k0]), lds8(&Ht[(pb * 32 + lane % 32) * NR + k0]), y2);
             }
             const int p = pb * 32 + lane % 32;
+            const int t0 = tb * 32 + 4 * (lane / 32);  // chunk row of y1[0]
+            const float* crow = &cums[t0];
+            const bf16_bits* xcol = &Xt[p * QR + t0];
+            float v[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int tl = tb * 32 + acc_row(r, lane);
-                const float g = exp2_hw(cums[tl]);
-                const float v = fmaf(g, y2[r], y1[r]) + Dh * bfval(Xt[p * QR + tl]);
-                const int64_t t = int64_t(c) * kQ + tl;
-                if (t < a.L) a.y[((b * a.L + t) * a.H + h) * kP + p] = tobf(v);
+                const int dr = 8 * (r / 4) + r % 4;
+                v[r] = fmaf(exp2_hw(crow[dr]), y2[r], y1[r]) + Dh * bfval(xcol[dr]);
+            }
+            // Stores of two adjacent columns at once: of each pair of rows
+            // (dr, dr+1), the even lane of a lane pair stores row dr and the
+            // odd lane row dr+1, swapping one value through a DPP quad
+            // permutation (lanes 0<->1, 2<->3).
+            const bool odd = lane & 1;
+            const int64_t tg0 = int64_t(c) * kQ + t0 + (odd ? 1 : 0);
+            bf16_bits* yrow = a.y + ((b * a.L + tg0) * a.H + h) * kP + (p & ~1);
+            const int64_t rs = a.H * kP;  // elements from one token to the next
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int dr = 8 * (r / 4) + r % 4;  // rows dr and dr + 1
+                const float send = odd ? v[r] : v[r + 1];
+                const float recv = __builtin_bit_cast(
+                    float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xb1, 0xf, 0xf, false));
+                const float lo = odd ? recv : v[r], hi = odd ? v[r + 1] : recv;
+                const uint32_t w = uint32_t(tobf(lo)) | (uint32_t(tobf(hi)) << 16);
+                if (tg0 + dr < a.L) *reinterpret_cast<uint32_t*>(yrow + dr * rs) = w;
             }
         }
         // ---- state: H^T <- 2^cum_end H^T + x^T (w B) over this wave's tiles ----
