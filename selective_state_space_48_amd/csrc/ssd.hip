@@ -157,6 +157,24 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
     for (int i = tid; i < kP * NR; i += 256) Ht[i] = 0;
 
+    // The output of a chunk is stored in the next iteration, once that
+    // iteration's prefetched inputs have been consumed and before the next
+    // prefetch is issued: vector-memory waits count stores too, in issue
+    // order, so a store issued after a prefetch would hold up the wait for it.
+    uint32_t ypend[8];  // two adjacent columns (bf16) for each pair of rows
+    auto store_y = [&](int c) {
+        const bool odd = lane & 1;
+        const int p = pb * 32 + lane % 32;
+        const int64_t tg0 = int64_t(c) * kQ + tb * 32 + 4 * (lane / 32) + (odd ? 1 : 0);
+        bf16_bits* yrow = a.y + ((b * a.L + tg0) * a.H + h) * kP + (p & ~1);
+        const int64_t rs = a.H * kP;  // elements from one token to the next
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int dr = 8 * (k / 2) + 2 * (k % 2);  // rows dr and dr + 1 of the pair
+            if (tg0 + dr < a.L) *reinterpret_cast<uint32_t*>(yrow + dr * rs) = ypend[k];
+        }
+    };
+
     R cur;
     load(0, cur);
     for (int c = 0; c < nc; ++c) {
@@ -199,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = v[e];
             }
         }
+        if (c > 0) store_y(c - 1);
         load(c + 1, cur);  // next chunk's inputs, in flight during this chunk
         __syncthreads();
 
@@ -260,18 +279,13 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             // odd lane row dr+1, swapping one value through a DPP quad
             // permutation (lanes 0<->1, 2<->3).
             const bool odd = lane & 1;
-            const int64_t tg0 = int64_t(c) * kQ + t0 + (odd ? 1 : 0);
-            bf16_bits* yrow = a.y + ((b * a.L + tg0) * a.H + h) * kP + (p & ~1);
-            const int64_t rs = a.H * kP;  // elements from one token to the next
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const int dr = 8 * (r / 4) + r % 4;  // rows dr and dr + 1
                 const float send = odd ? v[r] : v[r + 1];
                 const float recv = __builtin_bit_cast(
                     float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xb1, 0xf, 0xf, false));
                 const float lo = odd ? recv : v[r], hi = odd ? v[r + 1] : recv;
-                const uint32_t w = uint32_t(tobf(lo)) | (uint32_t(tobf(hi)) << 16);
-                if (tg0 + dr < a.L) *reinterpret_cast<uint32_t*>(yrow + dr * rs) = w;
+                ypend[r / 2] = uint32_t(tobf(lo)) | (uint32_t(tobf(hi)) << 16);
             }
         }
         // ---- state: H^T <- 2^cum_end H^T + x^T (w B) over this wave's tiles ----
@@ -297,6 +311,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             for (int r = 0; r < 16; ++r) Ht[(pb * 32 + acc_row(r, lane)) * NR + n] = tobf(H[j][r]);
         }
     }
+    store_y(nc - 1);
     if (a.last_state) {
         float* dst = a.last_state + (b * a.H + h) * int64_t(N) * kP;
 #pragma unroll
