@@ -37,8 +37,8 @@ TRANS_SLOTS = 2            # v_exp/v_log/v_rcp occupy a wave twice as long as an
 # counter reads for a copy of known size with the same access pattern
 # (profiles/ holds the runs). It is valid only for the device code it was
 # taken on, identified by the sha256 of the forward kernel's sources.
-TRAFFIC = {"sources_sha256": "b5e9015566b7757315063de017b3b6573476dff7a23cb09df5349a0ba5467628",
-           "fetch_kib": 213316.0, "fetch_factor": 2.0, "write_kib": 138347.7, "write_factor": 1.0}
+TRAFFIC = {"sources_sha256": "6fed44419bbd79080678bf9d6264ccc5c97fcd651e86e8ff79adff42eb18d8bf",
+           "fetch_kib": 220067.5, "fetch_factor": 2.0, "write_kib": 148437.5, "write_factor": 1.0}
 
 
 def kernel_sources_sha256():
@@ -262,10 +262,11 @@ def time_bwd(torch, dev, reps=5):
 
 def time_ssd(torch, dev, reps=10):
     """Mamba-2 SSD layer, batch 8, L 2048, 64 heads of 64, state 128, bf16:
-    whole call (chunk states, state passing, chunk outputs; workspace on the
-    stream). Roofline terms: the chunked algorithm's matrix-product flops
-    (64-token chunks) against the 2.5 PFLOP/s bf16 peak, and the algorithmic
-    bytes (inputs once, y and the final state once) against 8 TB/s."""
+    whole call (one fused kernel: per (batch, head) the 64-token chunks in
+    order, state on chip). Roofline terms: the chunked algorithm's
+    matrix-product flops (64-token chunks) against the 2.5 PFLOP/s bf16 peak,
+    and the algorithmic bytes (inputs once, y and the final state once)
+    against 8 TB/s."""
     from selective_state_space_48_amd import selscan
     from selective_state_space_48_amd import workloads as W
 
