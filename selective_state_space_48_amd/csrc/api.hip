@@ -82,10 +82,12 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
     if (S == 0) {
         // Segmenting adds a state pass (about 0.7 of an output pass) over all
         // but the last segment, so it only pays when the one-pass grid leaves
-        // SIMDs without a wave (1024 SIMDs). Then aim at ~3 waves per SIMD.
+        // most SIMDs (1024) without a wave. Then aim at exactly two waves per
+        // SIMD: two workgroups per CU are resident at once (LDS), and a grid
+        // of more than one such round leaves a partial last round.
         S = 1;
-        if (waves < 1024 && L >= 16 * kChunk) {
-            const int64_t target = 3072;
+        if (waves < 512 && L >= 16 * kChunk) {
+            const int64_t target = 2048;
             S = (target + waves - 1) / waves;
             const int64_t max_by_len = L / (8 * kChunk);
             if (S > max_by_len) S = max_by_len;
