@@ -364,10 +364,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     const int nck = a.nck;
     In in0, in1;
     Keep k0, k1;
+    // As in the forward kernel, the sweep runs at a raised wave priority and
+    // the per-token phases at the base one (about 3.5% less time).
     auto step = [&](int c, Keep& kc, Keep& kn, In& inn) {
         // kc: chunk c (prologue done); inn holds chunk c-1's inputs
+        __builtin_amdgcn_s_setprio(1);
         scan_chunk(c);
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
         epilogue(c, kc);
         if (c >= 1) prologue(c - 1, inn, kn);
         if (c >= 3) load(c - 3, inn);

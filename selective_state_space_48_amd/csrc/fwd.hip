@@ -455,10 +455,17 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // values alternate between two arrays by chunk parity (no copies).
     constexpr bool PAIR = VEC && sizeof(T) * CH < 128;
     float dxA[TS], gzA[TS], dxB[TS], gzB[TS];
+    // The scan runs at a raised wave priority and the per-token phases at the
+    // base one: with two waves per SIMD from different workgroups, the
+    // VALU-bound scan of one then issues ahead of the latency-bound loads,
+    // LDS traffic and stores of the other, which fill the gaps (measured:
+    // about 7% less time than equal priorities).
     auto step = [&](int c, Slice& next, Slice& other, const float* dxc, const float* gzc,
                     float* dxn, float* gzn) {
+        __builtin_amdgcn_s_setprio(1);
         scan_chunk(c);
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
         if (c + 1 < nchunks) prologue(c + 1, next, dxn, gzn);
         // (VEC loads of chunks past the end read valid memory and are never used)
         if constexpr (PAIR) {
