@@ -178,6 +178,11 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     R cur;
     load(0, cur);
     for (int c = 0; c < nc; ++c) {
+        // Staging (and the stores and prefetch issued with it) runs at a
+        // raised wave priority, the matrix products at the base one: the
+        // other workgroup's waves on the same SIMDs then reach their next
+        // chunk's products sooner (measured: about 8% less time).
+        __builtin_amdgcn_s_setprio(1);
         // ---- per-token: step size and running log2-decay, token = lane (every wave) ----
         const float sp = softplus_log2(cur.dl + bias) * kLn2;
         const float dt = cur.ok ? sp : 0.0f;
@@ -220,6 +225,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         if (c > 0) store_y(c - 1);
         load(c + 1, cur);  // next chunk's inputs, in flight during this chunk
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- scores of the lower block triangle: wave 0 (0,0), wave 1 (1,0), wave 2 (1,1) ----
         const int gt = wv == 0 ? 0 : 1, gs = wv == 2 ? 1 : 0;
