@@ -429,26 +429,44 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ p
                                                      const float* __restrict__ pC, T* __restrict__ dB,
                                                      T* __restrict__ dC, int64_t batch, int64_t L,
                                                      int64_t Lp, int32_t row_blocks) {
+    // One thread per (b, 4 states, t), t fastest: the output rows are written
+    // contiguously, and the four threads reading one 64-byte partial record
+    // (one per state quad) share it through L2. The row blocks are summed in
+    // order (deterministic), eight loads in flight at a time.
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= batch * L) return;
-    const int64_t b = i / L, t = i % L;
-    float sb[kN], sc[kN];
+    if (i >= batch * 4 * L) return;
+    const int64_t t = i % L, bq = i / L;
+    const int q = int(bq % 4);
+    const int64_t b = bq / 4;
+    float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
+    const int64_t step = batch * Lp * kN;  // floats from one row block to the next
+    const float* ob = pB + (b * Lp + t) * kN + 4 * q;
+    const float* oc = pC + (b * Lp + t) * kN + 4 * q;
+    int r = 0;
+    for (; r + 8 <= row_blocks; r += 8) {
+        float4 vb[8], vc[8];
 #pragma unroll
-    for (int n = 0; n < kN; ++n) sb[n] = sc[n] = 0.0f;
-    for (int r = 0; r < row_blocks; ++r) {
-        const int64_t o = ((int64_t(r) * batch + b) * Lp + t) * kN;
+        for (int u = 0; u < 8; ++u) {
+            vb[u] = *reinterpret_cast<const float4*>(ob + (r + u) * step);
+            vc[u] = *reinterpret_cast<const float4*>(oc + (r + u) * step);
+        }
 #pragma unroll
-        for (int q = 0; q < kN / 4; ++q) {
-            const float4 vb = reinterpret_cast<const float4*>(pB + o)[q];
-            const float4 vc = reinterpret_cast<const float4*>(pC + o)[q];
-            sb[4 * q] += vb.x; sb[4 * q + 1] += vb.y; sb[4 * q + 2] += vb.z; sb[4 * q + 3] += vb.w;
-            sc[4 * q] += vc.x; sc[4 * q + 1] += vc.y; sc[4 * q + 2] += vc.z; sc[4 * q + 3] += vc.w;
+        for (int u = 0; u < 8; ++u) {
+            sb.x += vb[u].x; sb.y += vb[u].y; sb.z += vb[u].z; sb.w += vb[u].w;
+            sc.x += vc[u].x; sc.y += vc[u].y; sc.z += vc[u].z; sc.w += vc[u].w;
         }
     }
+    for (; r < row_blocks; ++r) {
+        const float4 vb = *reinterpret_cast<const float4*>(ob + r * step);
+        const float4 vc = *reinterpret_cast<const float4*>(oc + r * step);
+        sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+        sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+    }
+    const float vb4[4] = {sb.x, sb.y, sb.z, sb.w}, vc4[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-    for (int n = 0; n < kN; ++n) {
-        dB[(b * kN + n) * L + t] = from_f32<T>(sb[n] * kLn2);
-        dC[(b * kN + n) * L + t] = from_f32<T>(sc[n]);
+    for (int j = 0; j < 4; ++j) {
+        dB[(b * kN + 4 * q + j) * L + t] = from_f32<T>(vb4[j] * kLn2);
+        dC[(b * kN + 4 * q + j) * L + t] = from_f32<T>(vc4[j]);
     }
 }
 
@@ -536,7 +554,7 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, voi
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * L + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * 4 * L + 255) / 256)), dim3(256), 0, st,
                        k.pB, k.pC, static_cast<T*>(t.dB), static_cast<T*>(t.dC), batch, L, k.Lp,
                        k.row_blocks);
     e = hipGetLastError();
