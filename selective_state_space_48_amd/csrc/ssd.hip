@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     __shared__ alignas(16) bf16_bits Bw[N * QR];       // 2^(cum_end - cum_s) delta_s B^T: [n][s]
     __shared__ alignas(16) bf16_bits Xt[kP * QR];      // x^T [p][s]
     __shared__ alignas(16) bf16_bits Ht[kP * NR];      // the state entering the chunk, bf16, [p][n]
-    __shared__ float cums[kQ], dts[kQ];                // running log2-decay and step of the chunk's tokens
+    __shared__ float cums[kQ], dts[kQ], gcum[kQ];      // running log2-decay, step and 2^cum of the chunk's tokens
     bf16_bits* Ms = BsMs;
 
     const int tid = threadIdx.x, lane = tid % 64;
@@ -192,17 +192,20 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         {
             const int s = lane;
             if (wv == 0) {
+                gcum[s] = exp2_hw(cum);
                 cums[s] = cum;
                 dts[s] = dt;
             }
             const float ws = exp2_hw(cend - cum) * dt;  // weight of token s in the state update
-            const uint4 zero = make_uint4(0, 0, 0, 0);
+            if (int64_t(c + 1) * kQ > a.L) {  // the last chunk is partial (a uniform branch)
+                const uint4 zero = make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int k = 0; k < R::NB; ++k)
-                if (!cur.ok) cur.b[k] = cur.c[k] = zero;
+                for (int k = 0; k < R::NB; ++k)
+                    if (!cur.ok) cur.b[k] = cur.c[k] = zero;
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                if (!cur.ok) cur.x[k] = zero;
+                for (int k = 0; k < 2; ++k)
+                    if (!cur.ok) cur.x[k] = zero;
+            }
 #pragma unroll
             for (int k = 0; k < R::NB; ++k) {
                 const int q8 = wv + 4 * k;
@@ -272,13 +275,13 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             }
             const int p = pb * 32 + lane % 32;
             const int t0 = tb * 32 + 4 * (lane / 32);  // chunk row of y1[0]
-            const float* crow = &cums[t0];
+            const float* grow = &gcum[t0];
             const bf16_bits* xcol = &Xt[p * QR + t0];
             float v[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int dr = 8 * (r / 4) + r % 4;
-                v[r] = fmaf(exp2_hw(crow[dr]), y2[r], y1[r]) + Dh * bfval(xcol[dr]);
+                v[r] = fmaf(grow[dr], y2[r], y1[r]) + Dh * bfval(xcol[dr]);
             }
             // Stores of two adjacent columns at once: of each pair of rows
             // (dr, dr+1), the even lane of a lane pair stores row dr and the
