@@ -571,7 +571,12 @@ def main():
         extras[key] = {"workload": name, "ms_per_call": round(ms, 4),
                        "output_pass_ms": round(k_ms, 4),
                        "Gelem_per_s": round(wx.elements / (ms * 1e-3) / 1e9, 2),
-                       "frac_hbm": round(algorithmic_bytes(wx) / (ms * 1e-3) / HBM_PEAK, 4)}
+                       "frac_hbm": round(algorithmic_bytes(wx) / (ms * 1e-3) / HBM_PEAK, 4),
+                       # the method's slots (one pass) against the slot peak: over the
+                       # output pass alone, and over the whole call (which adds the
+                       # state pass of a segmented plan)
+                       "output_pass_frac_alu": round(method_slots(wx) / (k_ms * 1e-3) / SLOT_PEAK, 4),
+                       "call_frac_alu": round(method_slots(wx) / (ms * 1e-3) / SLOT_PEAK, 4)}
     if extras:
         out["extras"] = extras
 
