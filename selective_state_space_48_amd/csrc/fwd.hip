@@ -524,17 +524,19 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 
 // Pack B and C ([batch, 16, L] of T) into the fp32 record layout above, for
 // Lp >= L tokens (a multiple of the chunk), zero past L. One thread writes one
-// 16-float half-record (B or C of one (b, s, g)), so a wave writes 4 KiB
-// contiguously; its reads are G consecutive tokens of NG rows, and the 8
-// sub-blocks a wave covers make them 8*G contiguous tokens per row.
+// float4 of a 16-float half-record (B or C of one (b, s, g)), so a wave
+// writes 1 KiB contiguously; with G = 4 a float4 is 4 consecutive tokens of
+// one row, read as one 8-byte (bf16) or 16-byte (fp32) load when whole.
 template <typename T, int G>
 __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, const T* __restrict__ C,
                                                       float* __restrict__ P, int64_t batch, int64_t L,
                                                       int64_t Lp) {
     constexpr int NG = kN / G;
     const int64_t psub = Lp / G;
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;  // half-record index
-    if (i >= batch * psub * G * 2) return;
+    const int64_t f = int64_t(blockIdx.x) * 256 + threadIdx.x;  // float4 index
+    if (f >= batch * psub * G * 2 * 4) return;
+    const int q = int(f % 4);
+    const int64_t i = f / 4;                                      // half-record index
     const int k = int(i % 2);
     const int g = int((i / 2) % G);
     const int64_t s = (i / (2 * G)) % psub;
@@ -543,17 +545,28 @@ __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, c
     // B is stored times ln 2, so that the scan's input term is (l x) B' with
     // l the step size in log2 units (l ln 2 x B = l x (B ln 2)).
     const float scale = k ? 1.0f : kLn2;
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < NG; ++j)
-#pragma unroll
-        for (int e = 0; e < G; ++e) {
-            const int64_t t = s * G + e;
-            v[j * G + e] = t < L ? to_f32(src[j * L + t]) * scale : 0.0f;
+    float v[4];
+    if (G == 4 && L % 4 == 0 && s * 4 + 3 < L) {  // row q, tokens 4s..4s+3, aligned and whole
+        const T* p = src + q * L + s * 4;
+        if constexpr (sizeof(T) == 4) {
+            const float4 u = *reinterpret_cast<const float4*>(p);
+            v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(p);
+            v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
         }
-    float4* dst = reinterpret_cast<float4*>(P + i * 16);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        for (int e = 0; e < 4; ++e) v[e] *= scale;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = 4 * q + e;  // element of the half-record: state row j, token within sub-block
+            const int j = idx / G;
+            const int64_t t = s * G + idx % G;
+            v[e] = t < L ? to_f32(src[j * L + t]) * scale : 0.0f;
+        }
+    }
+    reinterpret_cast<float4*>(P)[f] = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // Carry pass: for each (row, n), compose the segments in order,
@@ -634,7 +647,7 @@ hipError_t dispatch_dtype(DType dt, const FwdKArgs& k, int groups, bool gate, bo
 template <typename T>
 hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, int64_t L,
                        int64_t Lp, int groups, hipStream_t st) {
-    const int64_t n = batch * Lp * 2;  // half-records: batch * (Lp / G) * G * 2
+    const int64_t n = batch * Lp * 2 * 4;  // float4s: batch * (Lp / G) * G * 2 half-records of 4
     const dim3 grid(unsigned((n + 255) / 256)), block(256);
     const T* b = static_cast<const T*>(B);
     const T* c = static_cast<const T*>(C);
