@@ -260,6 +260,35 @@ def time_bwd(torch, dev, reps=5):
             "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
 
 
+def time_bwd_long(torch, dev, reps=3):
+    """The backward pass on the long-memory workload (fp32, batch 1, L 2^20,
+    d_inner 128, no gate): two 64-row blocks, so the sweep is cut into
+    sequence segments (automatic choice); whole call."""
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    w = W.get("long_f32_b1_l1048576_d128")
+    d = device_inputs(w, torch, dev)
+    dy = torch.randn(d["x"].shape, generator=torch.Generator().manual_seed(9)).to(dev)
+    run = lambda: selscan.bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d.get("z"),
+                              dt_bias=d["dt_bias"], dy=dy)
+    run()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / reps
+    # read x, delta, dy, B, C; write dx, ddelta, dB, dC (fp32)
+    nbytes = 4 * w.elements * 4 + 4 * w.batch * w.dstate * w.seqlen * 4
+    del d, dy
+    return {"workload": f"backward on {w.name}", "ms_per_call": round(ms, 4),
+            "Gelem_per_s": round(w.elements / (ms * 1e-3) / 1e9, 2),
+            "algorithmic_bytes": nbytes, "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
+
+
 def time_ssd(torch, dev, reps=10):
     """Mamba-2 SSD layer, batch 8, L 2048, 64 heads of 64, state 128, bf16:
     whole call (one fused kernel: per (batch, head) the 64-token chunks in
@@ -555,6 +584,9 @@ def main():
         log("[bench] backward: headline shape")
         extras["bwd"] = time_bwd(torch, dev)
         log(f"[bench] backward: {extras['bwd']}")
+        log("[bench] backward: long-memory workload")
+        extras["bwd_long"] = time_bwd_long(torch, dev)
+        log(f"[bench] backward long: {extras['bwd_long']}")
     if not args.no_extras and args.only in (None, "ssd"):
         log("[bench] SSD layer")
         extras["ssd"] = time_ssd(torch, dev)

@@ -209,6 +209,35 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
                 const selscan_dims_t* dims, void* stream);
 
 /*
+ * Options of selscan_bwd_ex (zero-initialise, then set what is wanted).
+ *   segments : sequence segments swept in parallel. 1 = one reverse sweep per
+ *              row; > 1 = the states entering the segments (a forward state
+ *              pass and carries), the checkpoint pass over all segments, a
+ *              reverse carry sweep of every segment but the first and its
+ *              composition, then the reverse sweep of all segments at once;
+ *              0 = automatic (segments only when rows are too few to fill the
+ *              chip). At most 65536; the segment length is rounded up to 32
+ *              tokens, so fewer segments may run. Results agree to rounding;
+ *              each choice is deterministic.
+ */
+typedef struct {
+    int32_t segments;
+} selscan_bwd_opts_t;
+
+/*
+ * selscan_bwd_ex — selscan_bwd with explicit launch choices (opts may be
+ * NULL: automatic, which is selscan_bwd). A segmented call takes, beyond the
+ * workspace above, 2 S B d 16 fp32 states, S B d doubles and S-fold dA/dD/
+ * ddt_bias partial sums. Errors as selscan_bwd, plus SELSCAN_ERR_CONFIG for
+ * segments out of range.
+ */
+int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,
+                   void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                   float* ddt_bias, const selscan_dims_t* dims, const selscan_bwd_opts_t* opts,
+                   void* stream);
+
+/*
  * selscan_ssd_fwd — Mamba-2's state space dual (SSD) layer: the selective SSM
  * restricted to one scalar decay per token and head, evaluated chunk-wise
  * with matrix products.

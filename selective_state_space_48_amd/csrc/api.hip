@@ -203,6 +203,33 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 
+// Segments of a backward call: the same rule as the forward's (the reverse
+// sweep runs 4 waves per 64-row block, two blocks per CU); a segmented call
+// adds a state pass and a carry sweep, each over all but one segment.
+void bwd_segments(const selscan_dims_t* dims, int32_t requested, int32_t* segments,
+                  int64_t* seg_len) {
+    const int64_t L = dims->seqlen;
+    const int64_t waves = (dims->dim + kWave - 1) / kWave * dims->batch * 4;
+    int64_t S = requested;
+    if (S == 0) {
+        S = 1;
+        if (waves < 512 && L >= 16 * kChunk) {
+            S = (2048 + waves - 1) / waves;
+            const int64_t max_by_len = L / (8 * kChunk);
+            if (S > max_by_len) S = max_by_len;
+            if (S < 1) S = 1;
+        }
+    }
+    *seg_len = L;
+    if (S > 1 && L > 0) {
+        int64_t len = (L + S - 1) / S;
+        len = (len + kChunk - 1) / kChunk * kChunk;
+        S = (L + len - 1) / len;
+        *seg_len = S > 1 ? len : L;
+    }
+    *segments = int32_t(S > 1 ? S : 1);
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,6 +334,17 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
                 const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,
                 void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddt_bias,
                 const selscan_dims_t* dims, void* stream) {
+    return selscan_bwd_ex(x, delta, A, B, C, D, z, dt_bias, dy, dx, ddelta, dA, dB, dC, dD, dz,
+                          ddt_bias, dims, nullptr, stream);
+}
+
+int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,
+                   void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                   float* ddt_bias, const selscan_dims_t* dims, const selscan_bwd_opts_t* opts,
+                   void* stream) {
+    const selscan_bwd_opts_t o = opts ? *opts : selscan_bwd_opts_t{};
+    if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
     Sizes sz;
     int rc = check_fwd_dims(dims, &sz);
     if (rc != SELSCAN_OK) return rc;
@@ -340,10 +378,13 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
         if (ddt_bias && launch_fill_zero(ddt_bias, dims->dim, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
         return SELSCAN_OK;
     }
+    int32_t segments = 1;
+    int64_t seg_len = L;
+    bwd_segments(dims, o.segments, &segments, &seg_len);
     if ((L + 15) / 16 * ((dims->dim + kWave - 1) / kWave) > INT32_MAX ||
-        ((dims->dim + kWave - 1) / kWave) * dims->batch > INT32_MAX)
+        ((dims->dim + kWave - 1) / kWave) * dims->batch * segments > INT32_MAX)
         return SELSCAN_ERR_DIMS;
-    const size_t ws_bytes = bwd_workspace_bytes(dims->batch, L, dims->dim);
+    const size_t ws_bytes = bwd_workspace_bytes(dims->batch, L, dims->dim, segments);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
         (void)hipGetLastError();
@@ -351,7 +392,8 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
     }
     BwdTensors t{x, delta, A, B, C, D, z, dt_bias, dy, dx, ddelta, dA, dB, dC, dD, dz, ddt_bias};
     const hipError_t e = launch_bwd(t, dims->batch, L, dims->dim,
-                                    dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32, ws, st);
+                                    dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
+                                    segments, seg_len, ws, st);
     (void)hipFreeAsync(ws, st);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }

@@ -60,11 +60,19 @@ struct BwdKArgs {
     void* ddelta;
     float* pB;           // [row_blocks][batch][Lp][N]: sum over the block's rows of dh * l x
     float* pC;           // [row_blocks][batch][Lp][N]: sum over the block's rows of ds * h
-    float* pA;           // [batch*dim][N]: sum over t of q * l
-    float* pD;           // [batch*dim]
-    float* pT;           // [batch*dim]
-    int64_t batch, L, dim, Lp, psub;
-    int32_t row_blocks, nck;
+    float* pA;           // [segments][batch*dim][N]: sum over the segment's t of q * l
+    float* pD;           // [segments][batch*dim]
+    float* pT;           // [segments][batch*dim]
+    // Segments along t (a multiple of 32 tokens each). In the reverse pass,
+    // carry_in[S-1-k] is the carry entering segment k from the right (null:
+    // zero; one segment). The carry pass writes, for segment k, the carry a
+    // sweep over it from zero leaves at its start to rc_state[S-1-k] and its
+    // summed log2 step sizes to rc_lsum[S-1-k], both [S][batch*dim](*N).
+    const float* carry_in;
+    float* rc_state;
+    double* rc_lsum;
+    int64_t batch, L, dim, Lp, psub, seg_len;
+    int32_t row_blocks, nck, segments, seg0;
 };
 
 // LDS: per-token (l, w) and ds of the chunk for the scan waves, and the
@@ -139,7 +147,9 @@ __device__ __forceinline__ void wave_sum16(const float* v, float* o) {
     for (int i = 0; i < 4; ++i) o[i] = rowsum16(w[i]);
 }
 
-template <typename T, bool GATE, bool VEC>
+// CARRY: the carry pass of a segmented backward (only the adjoint carry,
+// swept back over the segment from zero, and the summed step sizes).
+template <typename T, bool GATE, bool VEC, bool CARRY>
 __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     using Q = Quad<T>;
     using S = BwdSmem;
@@ -152,9 +162,16 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
-    const int rb = int(blockIdx.x % unsigned(a.row_blocks));
-    const int64_t b = int64_t(blockIdx.x / unsigned(a.row_blocks));
+    // block -> (segment, batch entry, 64-row block)
+    int64_t blk = blockIdx.x;
+    const int rb = int(blk % a.row_blocks);
+    blk /= a.row_blocks;
+    const int64_t b = blk % a.batch;
+    const int seg = a.seg0 + int(blk / a.batch);
     const int64_t rows = a.batch * a.dim;
+    // this segment's 16-token chunks [c_lo, c_hi)
+    const int c_lo = int(int64_t(seg) * a.seg_len / kBCH);
+    const int c_hi = int(min(int64_t(a.nck), (int64_t(seg) + 1) * a.seg_len / kBCH));
 
     // scan mapping: lane = row, wave = 4 states
     const int64_t d0 = int64_t(rb) * kWave;
@@ -210,6 +227,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     struct Keep {
         float x[kBTS], ds[kBTS], sg[kBTS], l[kBTS];
     };
+    double lsum_acc = 0.0;  // carry pass: this thread's tokens' summed step sizes
     // ---- per-token prologue of chunk c: (l, w) and ds to LDS ----
     auto prologue = [&](int c, const In& in, Keep& k) {
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
@@ -232,6 +250,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
             k.ds[e] = dsv[e];
             k.sg[e] = exp2_hw(ul - lv);  // sigmoid(u) = e^u / (1 + e^u)
             k.l[e] = l[e];
+            if constexpr (CARRY) lsum_acc += double(l[e]);
         }
         float4* lwr = reinterpret_cast<float4*>(&sm.lw[pr * S::kLW]) + pq * 2;
         lwr[0] = make_float4(l[0], w[0], l[1], w[1]);
@@ -242,13 +261,44 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
 
     float carry[kBNG], dAacc[kBNG];
 #pragma unroll
-    for (int j = 0; j < kBNG; ++j) carry[j] = dAacc[j] = 0.0f;
+    for (int j = 0; j < kBNG; ++j) {
+        carry[j] = (a.carry_in && row_ok)
+                       ? a.carry_in[((int64_t(a.segments) - 1 - seg) * rows + row) * kN + n0 + j]
+                       : 0.0f;
+        dAacc[j] = 0.0f;
+    }
 
     // ---- the scan waves on chunk c: recompute, then sweep back ----
     // The states of the chunk are recomputed from its checkpoint into
     // registers (h_t for the 16 tokens); the decays are recomputed again on
     // the way back rather than kept. B and C come from LDS (broadcast reads).
     auto scan_chunk = [&](int c) {
+        if constexpr (CARRY) {
+            // only the adjoint carry: dh = ds C + carry, carry = exp(delta A) dh
+            const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kLW]);
+            const float* dsr = reinterpret_cast<const float*>(&sm.ds[lane * S::kDS]);
+#pragma unroll
+            for (int sb = kBNSB - 1; sb >= 0; --sb) {
+                float Cv[16];
+                const float4* r = reinterpret_cast<const float4*>(sm.bc + (sb * kBG + wv) * kRecF);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 w = r[4 + q];
+                    Cv[4 * q] = w.x; Cv[4 * q + 1] = w.y; Cv[4 * q + 2] = w.z; Cv[4 * q + 3] = w.w;
+                }
+#pragma unroll
+                for (int e = kBSB - 1; e >= 0; --e) {
+                    const int t = sb * kBSB + e;
+                    const float lx = lw2[t].x, ds = dsr[t];
+#pragma unroll
+                    for (int j = 0; j < kBNG; ++j) {
+                        const float dh = fmaf(ds, Cv[j * kBSB + e], carry[j]);
+                        carry[j] = exp2_hw(lx * An[j]) * dh;
+                    }
+                }
+            }
+            return;
+        }
         const float4 hs4 = *reinterpret_cast<const float4*>(a.ckpt + (int64_t(c) * rows + row) * kN + n0);
         const float hs[kBNG] = {hs4.x, hs4.y, hs4.z, hs4.w};
         const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kLW]);
@@ -322,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     float dDacc = 0.0f, dTacc = 0.0f;
     // ---- per-token epilogue of chunk c: sums over the waves, dx, ddelta ----
     auto epilogue = [&](int c, const Keep& k) {
+        if constexpr (CARRY) return;
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
         float dxv[4], ddv[4];
 #pragma unroll
@@ -359,9 +410,9 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         }
     };
 
-    // Chunks from last to first. Inputs are loaded two chunks ahead; the
-    // per-token values of chunk c live in the Keep set of its parity.
-    const int nck = a.nck;
+    // The segment's chunks from last to first. Inputs are loaded two chunks
+    // ahead; the per-token values of chunk c live in the Keep set of its
+    // parity.
     In in0, in1;
     Keep k0, k1;
     // As in the forward kernel, the sweep runs at a raised wave priority and
@@ -373,22 +424,22 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
         epilogue(c, kc);
-        if (c >= 1) prologue(c - 1, inn, kn);
-        if (c >= 3) load(c - 3, inn);
+        if (c - 1 >= c_lo) prologue(c - 1, inn, kn);
+        if (c - 3 >= c_lo) load(c - 3, inn);
         __syncthreads();
     };
-    const int last = nck - 1;
+    const int last = c_hi - 1;
     // in[p] holds the chunk of parity p's inputs
     if (last & 1) {
         load(last, in1);
-        if (last >= 1) load(last - 1, in0);
+        if (last - 1 >= c_lo) load(last - 1, in0);
         prologue(last, in1, k1);
-        if (last >= 2) load(last - 2, in1);
+        if (last - 2 >= c_lo) load(last - 2, in1);
     } else {
         load(last, in0);
-        if (last >= 1) load(last - 1, in1);
+        if (last - 1 >= c_lo) load(last - 1, in1);
         prologue(last, in0, k0);
-        if (last >= 2) load(last - 2, in0);
+        if (last - 2 >= c_lo) load(last - 2, in0);
     }
     __syncthreads();
     int c = last;
@@ -396,14 +447,33 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         step(c, k1, k0, in0);
         --c;
     }
-    for (; c >= 0; c -= 2) {
+    for (; c >= c_lo; c -= 2) {
         step(c, k0, k1, in1);
-        if (c >= 1) step(c - 1, k1, k0, in0);
+        if (c - 1 >= c_lo) step(c - 1, k1, k0, in0);
     }
 
-    // ---- per-row sums: dA over t (this wave's states), dD and ddt_bias ----
+    if constexpr (CARRY) {
+        // this segment's carry from zero, and its summed step sizes (the four
+        // token slices of a row added in order)
+        const int64_t ri = int64_t(a.segments) - 1 - seg;
+        if (row_ok)
+            *reinterpret_cast<float4*>(a.rc_state + (ri * rows + row) * kN + n0) =
+                make_float4(carry[0], carry[1], carry[2], carry[3]);
+        double* red = reinterpret_cast<double*>(&sm.part[0][0]);
+        red[pq * kWave + pr] = lsum_acc;
+        __syncthreads();
+        if (wv == 0 && row_ok) {
+            double sL = 0.0;
+#pragma unroll
+            for (int g = 0; g < kBG; ++g) sL += red[g * kWave + lane];
+            a.rc_lsum[ri * rows + row] = sL;
+        }
+        return;
+    }
+    // ---- per-row sums over the segment: dA (this wave's states), dD and ddt_bias ----
+    const int64_t so = int64_t(seg) * rows + row;
     if (row_ok) {
-        *reinterpret_cast<float4*>(a.pA + row * kN + n0) =
+        *reinterpret_cast<float4*>(a.pA + so * kN + n0) =
             make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
     }
     float2* red = reinterpret_cast<float2*>(&sm.part[0][0]);
@@ -417,8 +487,8 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
             sD += v.x;
             sT += v.y;
         }
-        a.pD[row] = sD;
-        a.pT[row] = sT;
+        a.pD[so] = sD;
+        a.pT[so] = sT;
     }
 }
 
@@ -470,7 +540,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ p
     }
 }
 
-// dA[d,n] = ln 2 * sum_b pA[b,d,n]; dD[d] = sum_b pD[b,d]; ddt_bias[d] = sum_b pT[b,d].
+// dA[d,n] = ln 2 * sum_b pA[b,d,n]; dD[d] = sum_b pD[b,d]; ddt_bias[d] = sum_b pT[b,d]
+// (b runs over segments x batch entries, in order).
 __global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ pA,
                                                          const float* __restrict__ pD,
                                                          const float* __restrict__ pT,
@@ -497,10 +568,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct BwdLayout {
-    size_t packed, ckpt, pB, pC, pA, pD, pT, total;
+    size_t packed, ckpt, pB, pC, pA, pD, pT, seg_state, carry, seg_lsum, total;
 };
-BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim) {
+BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int32_t segments) {
     const size_t rows = size_t(batch) * size_t(dim);
+    const size_t S = size_t(segments);
     const size_t nck = size_t((L + kBCH - 1) / kBCH);
     const size_t Lp = nck * kBCH;
     const size_t Lp32 = size_t((L + kChunk - 1) / kChunk) * kChunk;
@@ -511,23 +583,55 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim) {
     o.ckpt = off;   off += al256(nck * rows * kN * 4);
     o.pB = off;     off += al256(rbk * size_t(batch) * Lp * kN * 4);
     o.pC = off;     off += al256(rbk * size_t(batch) * Lp * kN * 4);
-    o.pA = off;     off += al256(rows * kN * 4);
-    o.pD = off;     off += al256(rows * 4);
-    o.pT = off;     off += al256(rows * 4);
+    o.pA = off;     off += al256(S * rows * kN * 4);
+    o.pD = off;     off += al256(S * rows * 4);
+    o.pT = off;     off += al256(S * rows * 4);
+    // segmented runs: per-segment states and carries (forward, then reused
+    // for the reverse carries) and summed step sizes
+    const size_t segb = S > 1 ? S : 0;
+    o.seg_state = off; off += al256(segb * rows * kN * 4);
+    o.carry = off;     off += al256(segb * rows * kN * 4);
+    o.seg_lsum = off;  off += al256(segb * rows * 8);
     o.total = off;
     return o;
 }
 
+template <typename T, bool CARRY>
+hipError_t launch_bwd_kernel(const BwdKArgs& k, bool gate, bool vec, int64_t blocks, hipStream_t st) {
+    const dim3 grid{unsigned(blocks)}, block{256};
+    if (gate) {
+        if (vec) hipLaunchKernelGGL((bwd_kernel<T, true, true, CARRY>), grid, block, 0, st, k);
+        else hipLaunchKernelGGL((bwd_kernel<T, true, false, CARRY>), grid, block, 0, st, k);
+    } else {
+        if (vec) hipLaunchKernelGGL((bwd_kernel<T, false, true, CARRY>), grid, block, 0, st, k);
+        else hipLaunchKernelGGL((bwd_kernel<T, false, false, CARRY>), grid, block, 0, st, k);
+    }
+    return hipGetLastError();
+}
+
+// A segmented backward (S > 1) runs: the forward state pass and carries
+// (states entering each segment), the checkpoint pass over all segments from
+// those states, the reverse carry pass over segments 1..S-1 (the adjoint
+// carry each leaves from zero) and its right-to-left composition (the same
+// associative pair as the forward carries: the carry a sweep leaves is
+// prod(decays) * carry in + carry from zero), and the reverse pass over all
+// segments from the carries entering them from the right. Every per-token
+// gradient belongs to one segment; dA, dD and ddt_bias are per-segment
+// partial sums added in a fixed order.
 template <typename T>
-hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, void* ws,
-                 hipStream_t st) {
+hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int32_t segments,
+                 int64_t seg_len, void* ws, hipStream_t st) {
     unsigned char* w = static_cast<unsigned char*>(ws);
-    const BwdLayout lo = bwd_layout(batch, L, dim);
+    const BwdLayout lo = bwd_layout(batch, L, dim, segments);
     FwdTensors ft{t.x, t.delta, t.z, t.A, t.B, t.C, t.D, t.dt_bias, nullptr, nullptr, nullptr};
     FwdShape fs{batch, L, dim, sizeof(T) == 2 ? DType::BF16 : DType::F32};
     float* packed = reinterpret_cast<float*>(w + lo.packed);
     float* ckpt = reinterpret_cast<float*>(w + lo.ckpt);
-    hipError_t e = launch_fwd_ckpt(ft, t.dy, t.dz, ckpt, fs, packed, st);
+    float* seg_state = segments > 1 ? reinterpret_cast<float*>(w + lo.seg_state) : nullptr;
+    float* carry = segments > 1 ? reinterpret_cast<float*>(w + lo.carry) : nullptr;
+    double* seg_lsum = segments > 1 ? reinterpret_cast<double*>(w + lo.seg_lsum) : nullptr;
+    hipError_t e = launch_fwd_ckpt(ft, t.dy, t.dz, ckpt, fs, packed, segments, seg_len, seg_state,
+                                   seg_lsum, carry, st);
     if (e != hipSuccess) return e;
 
     BwdKArgs k{};
@@ -543,16 +647,25 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, voi
     k.Lp = int64_t(k.nck) * kBCH;
     k.psub = ((L + kChunk - 1) / kChunk * kChunk) / kBG;
     k.row_blocks = int32_t((dim + kWave - 1) / kWave);
-    const dim3 grid(unsigned(int64_t(k.row_blocks) * batch)), block(256);
+    k.segments = segments;
+    k.seg_len = segments > 1 ? seg_len : int64_t(k.nck) * kBCH;
+    const int64_t per_seg = int64_t(k.row_blocks) * batch;
     const bool vec = L % 4 == 0;
-    if (t.z) {
-        if (vec) hipLaunchKernelGGL((bwd_kernel<T, true, true>), grid, block, 0, st, k);
-        else hipLaunchKernelGGL((bwd_kernel<T, true, false>), grid, block, 0, st, k);
-    } else {
-        if (vec) hipLaunchKernelGGL((bwd_kernel<T, false, true>), grid, block, 0, st, k);
-        else hipLaunchKernelGGL((bwd_kernel<T, false, false>), grid, block, 0, st, k);
+    const bool gate = t.z != nullptr;
+    const int64_t rows = batch * dim;
+    if (segments > 1) {
+        // reverse carries: the forward state buffers are free again
+        BwdKArgs kc = k;
+        kc.seg0 = 1;
+        kc.rc_state = seg_state;
+        kc.rc_lsum = seg_lsum;
+        e = launch_bwd_kernel<T, true>(kc, gate, vec, per_seg * (segments - 1), st);
+        if (e != hipSuccess) return e;
+        e = launch_carry(t.A, seg_state, seg_lsum, nullptr, carry, rows, dim, segments, st);
+        if (e != hipSuccess) return e;
+        k.carry_in = carry;
     }
-    e = hipGetLastError();
+    e = launch_bwd_kernel<T, false>(k, gate, vec, per_seg * segments, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * 4 * L + 255) / 256)), dim3(256), 0, st,
                        k.pB, k.pC, static_cast<T*>(t.dB), static_cast<T*>(t.dC), batch, L, k.Lp,
@@ -560,20 +673,20 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_reduce_params, dim3(unsigned((dim * kN + 255) / 256)), dim3(256), 0, st,
-                       k.pA, k.pD, k.pT, t.dA, t.dD, t.ddt_bias, batch, dim);
+                       k.pA, k.pD, k.pT, t.dA, t.dD, t.ddt_bias, batch * segments, dim);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim) {
-    return bwd_layout(batch, L, dim).total;
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int32_t segments) {
+    return bwd_layout(batch, L, dim, segments).total;
 }
 
 hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,
-                      void* workspace, hipStream_t stream) {
-    return dtype == DType::BF16 ? bwd_t<bf16_bits>(t, batch, L, dim, workspace, stream)
-                                : bwd_t<float>(t, batch, L, dim, workspace, stream);
+                      int32_t segments, int64_t seg_len, void* workspace, hipStream_t stream) {
+    return dtype == DType::BF16 ? bwd_t<bf16_bits>(t, batch, L, dim, segments, seg_len, workspace, stream)
+                                : bwd_t<float>(t, batch, L, dim, segments, seg_len, workspace, stream);
 }
 
 }  // namespace selscan

@@ -760,8 +760,18 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     return output_pass(s.dtype, k, p, gate, per_seg * p.segments, stream);
 }
 
+hipError_t launch_carry(const float* A, const float* seg_state, const double* seg_lsum,
+                        const float* h0, float* carry, int64_t rows, int64_t dim, int32_t segments,
+                        hipStream_t stream) {
+    const int64_t nthreads = rows * kN;
+    hipLaunchKernelGGL(carry_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream,
+                       A, seg_state, seg_lsum, h0, carry, rows, dim, segments);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float* ckpt,
-                           const FwdShape& s, float* packed, hipStream_t stream) {
+                           const FwdShape& s, float* packed, int32_t segments, int64_t seg_len,
+                           float* seg_state, double* seg_lsum, float* carry, hipStream_t stream) {
     const int64_t Lp = padded_len(s.L);
     constexpr int G = 4;
     hipError_t e = s.dtype == DType::BF16
@@ -771,13 +781,33 @@ hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float*
     FwdKArgs k{};
     k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = packed;
     k.D = t.D; k.dt_bias = t.dt_bias; k.y = dz; k.last_state = nullptr; k.h0 = nullptr;
-    k.batch = s.batch; k.L = s.L; k.dim = s.dim; k.seg_len = s.L;
-    k.psub = Lp / G; k.segments = 1;
+    k.batch = s.batch; k.L = s.L; k.dim = s.dim;
+    k.seg_len = segments > 1 ? seg_len : s.L;
+    k.psub = Lp / G; k.segments = segments > 1 ? segments : 1;
     k.row_blocks = int32_t((s.dim + kWave - 1) / kWave);
     k.dy = dy; k.ckpt = ckpt;
-    const int64_t blocks = int64_t(k.row_blocks) * s.batch;
+    const int64_t per_seg = int64_t(k.row_blocks) * s.batch;
     const bool vec = (s.L * (s.dtype == DType::BF16 ? 2 : 4)) % 16 == 0;
     const bool gate = t.z != nullptr;
+    if (segments > 1) {
+        // the states entering the segments: state pass over all but the last,
+        // then the carries
+        FwdKArgs k1 = k;
+        k1.seg_state = seg_state;
+        k1.seg_lsum = seg_lsum;
+        k1.y = nullptr;
+        k1.dy = nullptr;
+        k1.ckpt = nullptr;
+        e = s.dtype == DType::BF16
+                ? dispatch_gv<bf16_bits, G, 1>(k1, false, vec, per_seg * (segments - 1), stream)
+                : dispatch_gv<float, G, 1>(k1, false, vec, per_seg * (segments - 1), stream);
+        if (e != hipSuccess) return e;
+        e = launch_carry(t.A, seg_state, seg_lsum, nullptr, carry, s.batch * s.dim, s.dim, segments,
+                         stream);
+        if (e != hipSuccess) return e;
+        k.h0 = carry;
+    }
+    const int64_t blocks = per_seg * k.segments;
     return s.dtype == DType::BF16 ? dispatch_gv<bf16_bits, G, 2>(k, gate, vec, blocks, stream)
                                   : dispatch_gv<float, G, 2>(k, gate, vec, blocks, stream);
 }

@@ -57,9 +57,19 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
 // record layout, fwd_workspace_bytes of a one-segment plan), then runs the
 // forward recurrence storing the state before every 16th token in
 // ckpt [ceil(L/16)][batch*dim][N], and, when t.z is set, dz = dy * (C.h + D x)
-// * silu'(z) into dz ([batch, dim, L] of the dtype). One segment, 4 waves.
+// * silu'(z) into dz ([batch, dim, L] of the dtype). 4 waves. With segments > 1
+// (seg_len a multiple of kChunk, every segment non-empty) the states entering
+// the segments come first, from a state pass into seg_state [segments][rows][N]
+// and seg_lsum [segments][rows] and the carries into carry [segments][rows][N].
 hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float* ckpt,
-                           const FwdShape& s, float* packed, hipStream_t stream);
+                           const FwdShape& s, float* packed, int32_t segments, int64_t seg_len,
+                           float* seg_state, double* seg_lsum, float* carry, hipStream_t stream);
+
+// Carries of a segmented scan, per (row, n): carry[0] = h0 (or 0),
+// carry[s+1] = 2^(A[row % dim, n] * seg_lsum[s]) carry[s] + seg_state[s].
+hipError_t launch_carry(const float* A, const float* seg_state, const double* seg_lsum,
+                        const float* h0, float* carry, int64_t rows, int64_t dim, int32_t segments,
+                        hipStream_t stream);
 
 struct StepTensors {
     float* state;
@@ -99,9 +109,11 @@ struct BwdTensors {
     void* dz;
     float* ddt_bias;
 };
-size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim);
+// segments > 1: the sequence is cut into segments of seg_len tokens (a
+// multiple of kChunk, every segment non-empty), swept in parallel.
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int32_t segments);
 hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,
-                      void* workspace, hipStream_t stream);
+                      int32_t segments, int64_t seg_len, void* workspace, hipStream_t stream);
 
 // Mamba-2 SSD layer (bf16). x/y: [batch, L, heads, 64]; delta: [batch, L, heads];
 // A, D, dt_bias: [heads] fp32; B, C: [batch, L, dstate]; last_state:

@@ -39,6 +39,10 @@ class FwdOpts(ctypes.Structure):
                 ("groups", ctypes.c_int32)]
 
 
+class BwdOpts(ctypes.Structure):
+    _fields_ = [("segments", ctypes.c_int32)]
+
+
 class SsdDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32)]
@@ -73,6 +77,9 @@ def _load() -> ctypes.CDLL:
     lib.selscan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, vp, vp, fp, vp, vp, fp, vp, fp,
                                 dims_p, vp]
     lib.selscan_bwd.restype = ctypes.c_int
+    lib.selscan_bwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, vp, vp, fp, vp, vp, fp, vp,
+                                   fp, dims_p, ctypes.POINTER(BwdOpts), vp]
+    lib.selscan_bwd_ex.restype = ctypes.c_int
     lib.selscan_ssd_fwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, ctypes.POINTER(SsdDims), vp]
     lib.selscan_ssd_fwd.restype = ctypes.c_int
     lib.selscan_conv1d.argtypes = [vp, fp, fp, fp, vp, fp, dims_p, vp]
@@ -237,11 +244,13 @@ def step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Ten
 def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
         dt_bias: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
-        want_dD: bool = True, want_ddt_bias: bool = True) -> dict:
+        want_dD: bool = True, want_ddt_bias: bool = True, segments: int = 0) -> dict:
     """Backward pass (selscan_bwd): gradients for the output gradient ``dy``.
 
     Returns a dict with dx, ddelta, dB, dC (input dtype), dA [dim, N] fp32, and
     dz (when z is given), dD and ddt_bias ([dim] fp32, when wanted).
+    ``segments`` other than 0 (automatic) calls selscan_bwd_ex with that
+    many sequence segments.
     """
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
@@ -265,11 +274,15 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     if want_ddt_bias:
         out["ddt_bias"] = torch.empty((dim,), dtype=torch.float32, device=dev)
     dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
-    _check(lib.selscan_bwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                           _ptr(dt_bias), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]),
-                           _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
-                           _ptr(out.get("dz")), _ptr(out.get("ddt_bias")), ctypes.byref(dims),
-                           _stream(dev)))
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+            _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+            _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out.get("ddt_bias")),
+            ctypes.byref(dims))
+    if segments == 0:
+        _check(lib.selscan_bwd(*args, _stream(dev)))
+    else:
+        opts = BwdOpts(segments)
+        _check(lib.selscan_bwd_ex(*args, ctypes.byref(opts), _stream(dev)))
     return out
 
 

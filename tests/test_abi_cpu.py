@@ -22,7 +22,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
-            "selscan_bwd", "selscan_ssd_fwd", "selscan_conv1d", "selscan_conv1d_step",
+            "selscan_bwd", "selscan_bwd_ex", "selscan_ssd_fwd", "selscan_conv1d", "selscan_conv1d_step",
             "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
@@ -294,6 +294,20 @@ def test_bwd_argument_checks():
     p = [P(i) for i in range(17)]
     p[13] = ctypes.c_void_p(BASE + 12 * SPAN + 64)  # dC inside dB
     assert bwd_call(D(), p) == S.ERR_ALIAS
+
+
+def test_bwd_ex_option_checks():
+    p = [P(i) for i in range(17)]
+    for seg in (-1, 65537):
+        o = S.BwdOpts(seg)
+        assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_CONFIG, seg
+    o = S.BwdOpts(4)
+    assert S.lib.selscan_bwd_ex(*p, None, ctypes.byref(o), None) == S.ERR_NULL
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D(batch=-1)), ctypes.byref(o), None) == S.ERR_DIMS
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D(N=8)), None, None) == S.ERR_DSTATE
+    q = list(p)
+    q[9] = q[0]                                    # dx == x
+    assert S.lib.selscan_bwd_ex(*q, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
 
 
 def ssd_call(dims, ptrs=None):

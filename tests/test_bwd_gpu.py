@@ -1,8 +1,8 @@
 """GPU parity of the backward pass (selscan_bwd) against the fp64 oracle's
 gradients on the same seeded inputs: every gradient, several shapes (ragged
 rows and lengths around the 16-token chunks and 64-row blocks), with and
-without the optional inputs, determinism, a long sequence, and the full
-headline-shaped layer. Error measure: |gpu - ref| over the oracle's
+without the optional inputs, determinism, forced and automatic sequence
+segments, a long sequence, and the full headline-shaped layer. Error measure: |gpu - ref| over the oracle's
 magnitude-sum scale of each gradient (same limits as the forward)."""
 import numpy as np
 import pytest
@@ -106,6 +106,54 @@ def test_bwd_long_sequence_small_steps():
     dy = _dy((1, 64, 4096), 7)
     case("bwd long f32 L4096")
     _check(_run(inp, "f32", dy, use_z=False), _ref(inp, dy, use_z=False), "f32", "long memory")
+
+
+SEGMENTED = [
+    # (batch, L, dim, dtype, segments requested)
+    (1, 300, 64, "f32", 2),
+    (1, 300, 64, "f32", 3),     # 128 + 128 + 44 tokens
+    (1, 33, 64, "f32", 2),      # 32 + 1 tokens
+    (2, 1000, 65, "bf16", 7),   # six of 160 and a last of 40, ragged rows
+    (1, 100, 40, "bf16", 10),   # rounds to 32-token segments: 4 run
+    (3, 520, 130, "f32", 5),
+]
+
+
+@pytest.mark.parametrize("batch,L,dim,dtype,segments", SEGMENTED)
+def test_bwd_segmented(batch, L, dim, dtype, segments):
+    """Forced sequence segments: the carries in both directions and the
+    per-segment partial sums of dA, dD and ddt_bias."""
+    inp = small(M14 if dtype == "bf16" else M130, batch=batch, seqlen=L, dim=dim)
+    dy = _dy((batch, dim, L), L + segments)
+    if dtype == "bf16":
+        dy = W._maybe_bf16(W.get(M14), dy)
+    case(f"bwd segments={segments} b{batch} L{L} d{dim} {dtype}")
+    td = TDT[dtype]
+    g = selscan.bwd(dev(inp["x"], td), dev(inp["delta"], td), dev(inp["A"]), dev(inp["B"], td),
+                    dev(inp["C"], td), D=dev(inp["D"]), z=dev(inp["z"], td),
+                    dt_bias=dev(inp["dt_bias"]), dy=dev(dy, td), segments=segments)
+    _check(g, _ref(inp, dy), dtype, f"segments={segments} b{batch} L{L} d{dim} {dtype}")
+
+
+def test_bwd_segmented_deterministic_and_close_to_one_sweep():
+    inp = small(M130, batch=1, seqlen=2048, dim=64)
+    dy = _dy((1, 64, 2048), 11)
+    case("bwd segments 1 vs 16, determinism")
+    args = (dev(inp["x"]), dev(inp["delta"]), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]))
+    kw = dict(D=dev(inp["D"]), z=dev(inp["z"]), dt_bias=dev(inp["dt_bias"]), dy=dev(dy))
+    one = selscan.bwd(*args, **kw, segments=1)
+    s1 = selscan.bwd(*args, **kw, segments=16)
+    s2 = selscan.bwd(*args, **kw, segments=16)
+    torch.cuda.synchronize()
+    for k in s1:
+        assert torch.equal(s1[k], s2[k]), k
+    ref = _ref(inp, dy)
+    for k in GRADS:
+        if k in ref:
+            e1 = oracle.scaled_error(to_np(one[k]), ref[k], ref[k + "_scale"])
+            e16 = oracle.scaled_error(to_np(s1[k]), ref[k], ref[k + "_scale"])
+            print(f"[parity] {k}: one sweep {e1:.2e}, 16 segments {e16:.2e}", flush=True)
+            assert e1 <= TOL["f32"] and e16 <= TOL["f32"], k
 
 
 def test_bwd_empty():
