@@ -77,7 +77,7 @@ class Oracle:
         lib.ssm_ref_step.restype = ctypes.c_int
         lib.ssm_ref_step.argtypes = [_dp] * 9 + [ctypes.c_int64] * 3 + [_dp] * 2
         lib.ssm_ref_bwd.restype = ctypes.c_int
-        lib.ssm_ref_bwd.argtypes = [_dp] * 9 + [ctypes.c_int64] * 4 + [_dp] * 16 + [ctypes.c_int]
+        lib.ssm_ref_bwd.argtypes = [_dp] * 11 + [ctypes.c_int64] * 4 + [_dp] * 18 + [ctypes.c_int]
         lib.ssm_ref_ssd.restype = ctypes.c_int
         lib.ssm_ref_ssd.argtypes = [_dp] * 7 + [ctypes.c_int64] * 5 + [_dp] * 4 + [ctypes.c_int]
         lib.ssm_ref_conv1d.restype = ctypes.c_int
@@ -87,18 +87,21 @@ class Oracle:
         self.lib = lib
         self.path = path
 
-    def bwd(self, x, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy,
-            nthreads: Optional[int] = None):
-        """Gradients of the forward pass (from a zero state) for an output
-        gradient ``dy`` ``[batch, dim, seqlen]``.
+    def bwd(self, x, delta, A, B, C, D=None, z=None, dt_bias=None, *, dy, h0=None,
+            dlast_state=None, want_dh0: bool = False, nthreads: Optional[int] = None):
+        """Gradients of the forward pass for an output gradient ``dy``
+        ``[batch, dim, seqlen]``: the forward starts from ``h0`` (``[batch,
+        dim, dstate]``, zero when None) and ``dlast_state`` (same shape) is the
+        gradient flowing into the final state (zero when None).
 
         Returns a dict with ``dx, ddelta, dA, dB, dC`` and, when the matching
-        input is given, ``dD``, ``dz``, ``ddt_bias``; each with a ``<name>_scale``
-        (the same computation on magnitudes). Shapes follow the inputs; dA is
-        ``[dim, dstate]``, dD and ddt_bias ``[dim]``. All float64.
+        input is given, ``dD``, ``dz``, ``ddt_bias``, and ``dh0`` when wanted;
+        each with a ``<name>_scale`` (the same computation on magnitudes).
+        Shapes follow the inputs; dA is ``[dim, dstate]``, dD and ddt_bias
+        ``[dim]``. All float64.
         """
         x, delta, A, B, C, dy = map(_f64, (x, delta, A, B, C, dy))
-        D, z, dt_bias = map(_f64, (D, z, dt_bias))
+        D, z, dt_bias, h0, dlast_state = map(_f64, (D, z, dt_bias, h0, dlast_state))
         batch, dim, L = x.shape
         N = A.shape[1]
         assert delta.shape == x.shape and dy.shape == x.shape and A.shape == (dim, N)
@@ -113,13 +116,19 @@ class Oracle:
             out.update({"dz": e(batch, dim, L), "dz_scale": e(batch, dim, L)})
         if dt_bias is not None:
             out.update({"ddt_bias": e(dim), "ddt_bias_scale": e(dim)})
+        for st in (h0, dlast_state):
+            assert st is None or st.shape == (batch, dim, N)
+        if want_dh0:
+            out.update({"dh0": e(batch, dim, N), "dh0_scale": e(batch, dim, N)})
         g = lambda k: _ptr(out.get(k))
         rc = self.lib.ssm_ref_bwd(
             _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-            _ptr(dy), batch, L, dim, N,
+            _ptr(dy), _ptr(h0), _ptr(dlast_state), batch, L, dim, N,
             g("dx"), g("ddelta"), g("dA"), g("dB"), g("dC"), g("dD"), g("dz"), g("ddt_bias"),
+            g("dh0"),
             g("dx_scale"), g("ddelta_scale"), g("dA_scale"), g("dB_scale"), g("dC_scale"),
-            g("dD_scale"), g("dz_scale"), g("ddt_bias_scale"), nthreads or default_threads())
+            g("dD_scale"), g("dz_scale"), g("ddt_bias_scale"), g("dh0_scale"),
+            nthreads or default_threads())
         if rc != 0:
             raise RuntimeError(f"ssm_ref_bwd failed with code {rc}")
         return out

@@ -344,7 +344,8 @@ int ssm_ref_conv1d_step(double *conv_state, const double *x, const double *w, co
  *   g = silu(z), s_t = sum_n C h + D x, y = s g
  *   dz   = dy * s * silu'(z),  silu'(z) = sig(z) (1 + z (1 - sig(z)))
  *   ds   = dy * g;  dD += ds * x
- *   going back in t, with carry[n] = 0 after the last token:
+ *   going back in t, with carry[n] = dlast[n] after the last token (the
+ *   gradient flowing into the final state; 0 when none is given):
  *     dh[n] = ds * C[n,t] + carry[n]           (total gradient of h_t[n])
  *     abar  = exp(dl * A[n]);  q = dh * abar * h_{t-1}[n]
  *     dA[n] += q * dl;   ddl += q * A[n]        (through the decay)
@@ -352,6 +353,8 @@ int ssm_ref_conv1d_step(double *conv_state, const double *x, const double *w, co
  *     dC[n,t] += ds * h_t[n]
  *     carry[n] = abar * dh
  *   dx += ds * D;  ddelta = ddl * sig(u)  (softplus' = sigmoid);  ddt_bias += ddelta
+ *   dh0[n] = carry[n] after the first token (h_{-1} = h0, the initial state;
+ *   0 when none is given)
  * dA, dD and ddt_bias sum over batch and time; dB and dC sum over channels.
  *
  * Error scales: the same computation on magnitudes (|dy|, |x|, the forward
@@ -359,11 +362,13 @@ int ssm_ref_conv1d_step(double *conv_state, const double *x, const double *w, co
  *
  * Layouts as the forward; dA: [dim, dstate]; dD, ddt_bias: [dim];
  * dB, dC: [batch, dstate, seqlen]. D, z, dt_bias may be null (then dD, dz,
- * ddt_bias are not written). Batch entries are split over threads; the
+ * ddt_bias are not written). h0, dlast and dh0: [batch, dim, dstate], each
+ * may be null. Batch entries are split over threads; the
  * per-channel sums are added in batch order afterwards.
  */
 typedef struct {
-    const double *x, *delta, *A, *B, *C, *D, *z, *dt_bias, *dy;
+    const double *x, *delta, *A, *B, *C, *D, *z, *dt_bias, *dy, *h0, *dlast;
+    double *dh0, *sdh0;
     int64_t batch, L, dim, N;
     double *dx, *ddelta, *dA, *dB, *dC, *dD, *dz, *ddt;       /* values */
     double *sdx, *sddelta, *sdA, *sdB, *sdC, *sdD, *sdz, *sddt; /* scales */
@@ -394,8 +399,11 @@ static void bwd_batches(bwd_job *j)
             const double *Ad = j->A + d * N;
             const double bias = j->dt_bias ? j->dt_bias[d] : 0.0;
             const double Dd = j->D ? j->D[d] : 0.0;
-            /* forward: H[t+1] = h_t, H[0] = h_{-1} = 0 */
-            for (int64_t n = 0; n < N; ++n) H[n] = HA[n] = 0.0;
+            /* forward: H[t+1] = h_t, H[0] = h_{-1} = h0 (or 0) */
+            for (int64_t n = 0; n < N; ++n) {
+                H[n] = j->h0 ? j->h0[row * N + n] : 0.0;
+                HA[n] = fabs(H[n]);
+            }
             for (int64_t t = 0; t < L; ++t) {
                 const double dl = softplus(dr[t] + bias);
                 for (int64_t n = 0; n < N; ++n) {
@@ -406,7 +414,10 @@ static void bwd_batches(bwd_job *j)
                 }
             }
             double dD = 0.0, sD = 0.0, dT = 0.0, sT = 0.0;
-            for (int64_t n = 0; n < N; ++n) carry[n] = carry_abs[n] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                carry[n] = j->dlast ? j->dlast[row * N + n] : 0.0;
+                carry_abs[n] = fabs(carry[n]);
+            }
             for (int64_t t = L - 1; t >= 0; --t) {
                 const double u = dr[t] + bias;
                 const double dl = softplus(u);
@@ -467,6 +478,11 @@ static void bwd_batches(bwd_job *j)
                 dT += ddl * sg;
                 sT += ddla * sg;
             }
+            if (j->dh0)
+                for (int64_t n = 0; n < N; ++n) {
+                    j->dh0[row * N + n] = carry[n];
+                    j->sdh0[row * N + n] = carry_abs[n];
+                }
             j->pD[b * dim + d] = dD;
             j->psD[b * dim + d] = sD;
             j->pT[b * dim + d] = dT;
@@ -484,17 +500,19 @@ static void *bwd_thread(void *p)
 
 int ssm_ref_bwd(const double *x, const double *delta, const double *A, const double *B,
                 const double *C, const double *D, const double *z, const double *dt_bias,
-                const double *dy, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                const double *dy, const double *h0, const double *dlast,
+                int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                 double *dx, double *ddelta, double *dA, double *dB, double *dC, double *dD,
-                double *dz, double *ddt_bias,
+                double *dz, double *ddt_bias, double *dh0,
                 double *sdx, double *sddelta, double *sdA, double *sdB, double *sdC, double *sdD,
-                double *sdz, double *sddt_bias, int nthreads)
+                double *sdz, double *sddt_bias, double *sdh0, int nthreads)
 {
     if (!x || !delta || !A || !B || !C || !dy || !dx || !ddelta || !dA || !dB || !dC) return -1;
     if (!sdx || !sddelta || !sdA || !sdB || !sdC) return -1;
     if (D && (!dD || !sdD)) return -1;
     if (dt_bias && (!ddt_bias || !sddt_bias)) return -1;
     if (z && (!dz || !sdz)) return -1;
+    if (dh0 && !sdh0) return -1;
     if (batch < 0 || seqlen < 0 || dim < 0 || dstate <= 0) return -2;
     const int64_t N = dstate;
     const size_t nb = (size_t)(batch * dim);
@@ -502,7 +520,8 @@ int ssm_ref_bwd(const double *x, const double *delta, const double *A, const dou
     if (!part) return -3;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > batch) nthreads = (int)(batch > 0 ? batch : 1);
-    bwd_job proto = {x, delta, A, B, C, D, z, dt_bias, dy, batch, seqlen, dim, N,
+    bwd_job proto = {x, delta, A, B, C, D, z, dt_bias, dy, h0, dlast, dh0, sdh0,
+                     batch, seqlen, dim, N,
                      dx, ddelta, dA, dB, dC, dD, dz, ddt_bias,
                      sdx, sddelta, sdA, sdB, sdC, sdD, sdz, sddt_bias,
                      part, part + nb * N, part + 2 * nb * N, part + 2 * nb * N + nb,

@@ -552,20 +552,21 @@ def _bwd_problem(seed, batch, dim, N, L, gate=True, with_D=True, with_bias=True)
 
 
 _GRAD_OF = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
-            "dt_bias": "ddt_bias"}
+            "dt_bias": "ddt_bias", "h0": "dh0"}
 
 
 def _torch_grads(p):
     """Gradients from torch autograd (fp64) of the forward written with torch
-    ops: a library's chain rule, not the oracle's."""
+    ops: a library's chain rule, not the oracle's. With ``h0`` in p the
+    recurrence starts there; with ``dlast`` the loss adds sum(dlast * h_L)."""
     T = {k: (torch.tensor(v, dtype=torch.float64, requires_grad=True) if v is not None else None)
-         for k, v in p.items() if k != "dy"}
+         for k, v in p.items() if k not in ("dy", "dlast")}
     x, dl, A, B, C = T["x"], T["delta"], T["A"], T["B"], T["C"]
     batch, dim, L = x.shape
     N = A.shape[1]
     u = dl + (T["dt_bias"][None, :, None] if T["dt_bias"] is not None else 0.0)
     delta = torch.nn.functional.softplus(u)
-    h = torch.zeros((batch, dim, N), dtype=torch.float64)
+    h = T["h0"] if T.get("h0") is not None else torch.zeros((batch, dim, N), dtype=torch.float64)
     ys = []
     for t in range(L):
         abar = torch.exp(delta[:, :, t, None] * A[None])
@@ -577,7 +578,10 @@ def _torch_grads(p):
     y = torch.stack(ys, -1)
     if T["z"] is not None:
         y = y * torch.nn.functional.silu(T["z"])
-    y.backward(torch.tensor(p["dy"]))
+    loss = (y * torch.tensor(p["dy"])).sum()
+    if p.get("dlast") is not None:
+        loss = loss + (h * torch.tensor(p["dlast"])).sum()
+    loss.backward()
     return {_GRAD_OF[k]: v.grad.numpy() for k, v in T.items() if v is not None}
 
 
@@ -595,15 +599,44 @@ def pin_bwd_torch_autograd(O):
             assert (k in r) == (k in ref), k
 
 
+def pin_bwd_initial_and_final_state_autograd(O):
+    """With an initial state h0 and a gradient flowing into the final state:
+    every gradient and dh0 against torch autograd (fp64) of the same forward,
+    the loss being sum(dy * y) + sum(dlast * h_L)."""
+    for kw in (dict(), dict(gate=False, with_D=False, with_bias=False)):
+        p = _bwd_problem(44, 2, 3, 4, 13, **kw)
+        rng = np.random.default_rng(45)
+        p["h0"] = rng.standard_normal((2, 3, 4))
+        p["dlast"] = rng.standard_normal((2, 3, 4))
+        r = O.bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"],
+                  dy=p["dy"], h0=p["h0"], dlast_state=p["dlast"], want_dh0=True)
+        ref = _torch_grads(p)
+        assert "dh0" in ref
+        for k, v in ref.items():
+            _close(r[k], v, 1e-10, scale=r[k + "_scale"] + 1e-300, what=f"bwd h0/dlast autograd {k} {kw}")
+    # No tokens: last_state = h0, so dh0 = dlast and every other gradient is zero.
+    p = _bwd_problem(46, 1, 2, 3, 0)
+    h0 = np.random.default_rng(47).standard_normal((1, 2, 3))
+    dl = np.random.default_rng(48).standard_normal((1, 2, 3))
+    r = O.bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"],
+              dy=p["dy"], h0=h0, dlast_state=dl, want_dh0=True)
+    assert np.array_equal(r["dh0"], dl)
+    assert not np.any(r["dA"]) and not np.any(r["dD"]) and not np.any(r["ddt_bias"])
+
+
 def pin_bwd_finite_differences(O):
     """Central differences of the loss sum(dy * y) through the oracle's own
     forward pass, every element of every input, on a tiny problem."""
     p = _bwd_problem(42, 2, 2, 3, 5)
-    r = O.bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"], dy=p["dy"])
+    rng = np.random.default_rng(49)
+    p["h0"] = rng.standard_normal((2, 2, 3))
+    dlast = rng.standard_normal((2, 2, 3))
+    r = O.bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["dt_bias"], dy=p["dy"],
+              h0=p["h0"], dlast_state=dlast, want_dh0=True)
 
     def loss(q):
-        y = O.fwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"], q["dt_bias"])["y"]
-        return float(np.sum(p["dy"] * y))
+        o = O.fwd(q["x"], q["delta"], q["A"], q["B"], q["C"], q["D"], q["z"], q["dt_bias"], h0=q["h0"])
+        return float(np.sum(p["dy"] * o["y"]) + np.sum(dlast * o["last_state"]))
 
     for name, gname in _GRAD_OF.items():
         base = p[name]

@@ -79,6 +79,9 @@ MUTANTS = [
     ("ssd_head_index", "const double dl = softplus(j->delta[(b * L + t) * H + h] + bias);",
      "const double dl = softplus(j->delta[(b * L + t) * H] + bias);"),
     ("ssd_state_transposed", "S[n * P + p] = a * S[n * P + p] + in;", "S[n * P + p] = a * S[p * N + n % P] + in;"),
+    ("bwd_h0_ignored", "H[n] = j->h0 ? j->h0[row * N + n] : 0.0;", "H[n] = 0.0;"),
+    ("bwd_dlast_ignored", "carry[n] = j->dlast ? j->dlast[row * N + n] : 0.0;", "carry[n] = 0.0;"),
+    ("bwd_dh0_scale_swap", "j->dh0[row * N + n] = carry[n];", "j->dh0[row * N + n] = carry_abs[n];"),
     ("bwd_dx_scale_no_D", "j->sdx[row * L + t] = fabs(ds * Dd) + dl * accBa;", "j->sdx[row * L + t] = dl * accBa;"),
 ]
 
