@@ -210,6 +210,14 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
 
 /*
  * Options of selscan_bwd_ex (zero-initialise, then set what is wanted).
+ *   h0          : [B, d, N] fp32, the state the forward started from (as
+ *                 selscan_fwd_ex's h0); NULL = zeros.
+ *   dlast_state : [B, d, N] fp32, the gradient flowing into the forward's
+ *                 last_state (a later chunk's dh0 when a sequence is trained
+ *                 in pieces); NULL = zeros. The adjoint carry starts from it.
+ *   dh0         : [B, d, N] fp32 output, the gradient of h0 (the adjoint
+ *                 carry leaving the first token); NULL = not wanted. With
+ *                 L = 0 it is dlast_state (or zeros).
  *   segments : sequence segments swept in parallel. 1 = one reverse sweep per
  *              row; > 1 = the states entering the segments (a forward state
  *              pass and carries), the checkpoint pass over all segments, a
@@ -221,15 +229,28 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
  *              each choice is deterministic.
  */
 typedef struct {
+    const float* h0;
+    const float* dlast_state;
+    float* dh0;
     int32_t segments;
 } selscan_bwd_opts_t;
 
 /*
- * selscan_bwd_ex — selscan_bwd with explicit launch choices (opts may be
- * NULL: automatic, which is selscan_bwd). A segmented call takes, beyond the
- * workspace above, 2 S B d 16 fp32 states, S B d doubles and S-fold dA/dD/
- * ddt_bias partial sums. Errors as selscan_bwd, plus SELSCAN_ERR_CONFIG for
- * segments out of range.
+ * selscan_bwd_ex — selscan_bwd with an initial state, a gradient flowing
+ * into the final state, the gradient of the initial state, and explicit
+ * launch choices (opts may be NULL: all defaults, which is selscan_bwd).
+ * Defined by the same chain rule as selscan_bwd with the loss adding
+ * sum(dlast_state * last_state) and the recurrence starting from h0: the
+ * adjoint carry after the last token is dlast_state, and dh0 is the carry
+ * after the first token. Splitting a sequence at a token, running the
+ * second part's backward with h0 = the first part's last_state and the first
+ * part's with dlast_state = the second part's dh0 gives the unsplit
+ * gradients (dA, dD, ddt_bias as the sum of the parts') up to rounding.
+ * h0, dlast_state and dh0 must be 16-byte aligned; dh0 must not overlap any
+ * input or other output. A segmented call takes, beyond the workspace above,
+ * 2 S B d 16 fp32 states, S B d doubles and S-fold dA/dD/ddt_bias partial
+ * sums. Errors as selscan_bwd, plus SELSCAN_ERR_CONFIG for segments out of
+ * range.
  */
 int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,

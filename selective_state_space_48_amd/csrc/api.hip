@@ -356,15 +356,18 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
     if (!z && dz) return SELSCAN_ERR_NULL;  // dz has no meaning without a gate
     for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, dy,
                           (const void*)dx, (const void*)ddelta, (const void*)dA, (const void*)dB,
-                          (const void*)dC, (const void*)dD, (const void*)dz, (const void*)ddt_bias})
+                          (const void*)dC, (const void*)dD, (const void*)dz, (const void*)ddt_bias,
+                          (const void*)o.h0, (const void*)o.dlast_state, (const void*)o.dh0})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
     const Span outs[] = {span(dx, sz.seq * es), span(ddelta, sz.seq * es), span(dz, sz.seq * es),
                          span(dB, sz.bc * es),  span(dC, sz.bc * es),     span(dA, sz.param * 4),
-                         span(dD, dims->dim * 4), span(ddt_bias, dims->dim * 4)};
+                         span(dD, dims->dim * 4), span(ddt_bias, dims->dim * 4),
+                         span(o.dh0, sz.state * 4)};
     const Span ins[] = {span(x, sz.seq * es), span(delta, sz.seq * es), span(z, sz.seq * es),
                         span(dy, sz.seq * es), span(B, sz.bc * es),     span(C, sz.bc * es),
-                        span(A, sz.param * 4), span(D, dims->dim * 4),  span(dt_bias, dims->dim * 4)};
+                        span(A, sz.param * 4), span(D, dims->dim * 4),  span(dt_bias, dims->dim * 4),
+                        span(o.h0, sz.state * 4), span(o.dlast_state, sz.state * 4)};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
         for (const Span& s : ins)
             if (overlaps(s, outs[i])) return SELSCAN_ERR_ALIAS;
@@ -376,6 +379,12 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
         if (launch_fill_zero(dA, sz.param, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
         if (dD && launch_fill_zero(dD, dims->dim, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
         if (ddt_bias && launch_fill_zero(ddt_bias, dims->dim, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        // the final state is h0 itself: its gradient passes straight through
+        if (o.dh0) {
+            const hipError_t e = o.dlast_state ? launch_copy_f32(o.dh0, o.dlast_state, sz.state, st)
+                                               : launch_fill_zero(o.dh0, sz.state, st);
+            if (e != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        }
         return SELSCAN_OK;
     }
     int32_t segments = 1;
@@ -390,7 +399,8 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
         (void)hipGetLastError();
         return SELSCAN_ERR_ALLOC;
     }
-    BwdTensors t{x, delta, A, B, C, D, z, dt_bias, dy, dx, ddelta, dA, dB, dC, dD, dz, ddt_bias};
+    BwdTensors t{x,  delta, A,  B,  C,  D,  z,        dt_bias, dy,
+                 dx, ddelta, dA, dB, dC, dD, dz, ddt_bias, o.h0, o.dlast_state, o.dh0};
     const hipError_t e = launch_bwd(t, dims->batch, L, dims->dim,
                                     dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
                                     segments, seg_len, ws, st);

@@ -65,12 +65,13 @@ struct BwdKArgs {
     float* pT;           // [segments][batch*dim]
     // Segments along t (a multiple of 32 tokens each). In the reverse pass,
     // carry_in[S-1-k] is the carry entering segment k from the right (null:
-    // zero; one segment). The carry pass writes, for segment k, the carry a
+    // zero). The carry pass writes, for segment k, the carry a
     // sweep over it from zero leaves at its start to rc_state[S-1-k] and its
     // summed log2 step sizes to rc_lsum[S-1-k], both [S][batch*dim](*N).
     const float* carry_in;
     float* rc_state;
     double* rc_lsum;
+    float* dh0;  // [batch*dim][N]: the carry leaving token 0 (null: not wanted)
     int64_t batch, L, dim, Lp, psub, seg_len;
     int32_t row_blocks, nck, segments, seg0;
 };
@@ -470,6 +471,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         }
         return;
     }
+    // the adjoint carry leaving the first token is the gradient of the initial state
+    if (a.dh0 && seg == 0 && row_ok)
+        *reinterpret_cast<float4*>(a.dh0 + row * kN + n0) =
+            make_float4(carry[0], carry[1], carry[2], carry[3]);
     // ---- per-row sums over the segment: dA (this wave's states), dD and ddt_bias ----
     const int64_t so = int64_t(seg) * rows + row;
     if (row_ok) {
@@ -623,7 +628,7 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
                  int64_t seg_len, void* ws, hipStream_t st) {
     unsigned char* w = static_cast<unsigned char*>(ws);
     const BwdLayout lo = bwd_layout(batch, L, dim, segments);
-    FwdTensors ft{t.x, t.delta, t.z, t.A, t.B, t.C, t.D, t.dt_bias, nullptr, nullptr, nullptr};
+    FwdTensors ft{t.x, t.delta, t.z, t.A, t.B, t.C, t.D, t.dt_bias, nullptr, nullptr, t.h0};
     FwdShape fs{batch, L, dim, sizeof(T) == 2 ? DType::BF16 : DType::F32};
     float* packed = reinterpret_cast<float*>(w + lo.packed);
     float* ckpt = reinterpret_cast<float*>(w + lo.ckpt);
@@ -661,10 +666,13 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
         kc.rc_lsum = seg_lsum;
         e = launch_bwd_kernel<T, true>(kc, gate, vec, per_seg * (segments - 1), st);
         if (e != hipSuccess) return e;
-        e = launch_carry(t.A, seg_state, seg_lsum, nullptr, carry, rows, dim, segments, st);
+        e = launch_carry(t.A, seg_state, seg_lsum, t.dlast, carry, rows, dim, segments, st);
         if (e != hipSuccess) return e;
         k.carry_in = carry;
+    } else {
+        k.carry_in = t.dlast;
     }
+    k.dh0 = t.dh0;
     e = launch_bwd_kernel<T, false>(k, gate, vec, per_seg * segments, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * 4 * L + 255) / 256)), dim3(256), 0, st,

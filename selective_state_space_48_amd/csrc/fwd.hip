@@ -780,7 +780,7 @@ hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float*
     if (e != hipSuccess) return e;
     FwdKArgs k{};
     k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = packed;
-    k.D = t.D; k.dt_bias = t.dt_bias; k.y = dz; k.last_state = nullptr; k.h0 = nullptr;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.y = dz; k.last_state = nullptr; k.h0 = t.h0;
     k.batch = s.batch; k.L = s.L; k.dim = s.dim;
     k.seg_len = segments > 1 ? seg_len : s.L;
     k.psub = Lp / G; k.segments = segments > 1 ? segments : 1;
@@ -795,6 +795,7 @@ hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float*
         FwdKArgs k1 = k;
         k1.seg_state = seg_state;
         k1.seg_lsum = seg_lsum;
+        k1.h0 = nullptr;  // every segment from zero; h0 enters through the carries
         k1.y = nullptr;
         k1.dy = nullptr;
         k1.ckpt = nullptr;
@@ -802,7 +803,7 @@ hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float*
                 ? dispatch_gv<bf16_bits, G, 1>(k1, false, vec, per_seg * (segments - 1), stream)
                 : dispatch_gv<float, G, 1>(k1, false, vec, per_seg * (segments - 1), stream);
         if (e != hipSuccess) return e;
-        e = launch_carry(t.A, seg_state, seg_lsum, nullptr, carry, s.batch * s.dim, s.dim, segments,
+        e = launch_carry(t.A, seg_state, seg_lsum, t.h0, carry, s.batch * s.dim, s.dim, segments,
                          stream);
         if (e != hipSuccess) return e;
         k.h0 = carry;

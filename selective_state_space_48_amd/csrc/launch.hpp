@@ -57,7 +57,8 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
 // record layout, fwd_workspace_bytes of a one-segment plan), then runs the
 // forward recurrence storing the state before every 16th token in
 // ckpt [ceil(L/16)][batch*dim][N], and, when t.z is set, dz = dy * (C.h + D x)
-// * silu'(z) into dz ([batch, dim, L] of the dtype). 4 waves. With segments > 1
+// * silu'(z) into dz ([batch, dim, L] of the dtype), from t.h0 (null: zeros).
+// 4 waves. With segments > 1
 // (seg_len a multiple of kChunk, every segment non-empty) the states entering
 // the segments come first, from a state pass into seg_state [segments][rows][N]
 // and seg_lsum [segments][rows] and the carries into carry [segments][rows][N].
@@ -89,7 +90,9 @@ hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType d
 
 // Backward pass. x/delta/z/dy and dx/ddelta/dz: [batch, dim, L]; B/C and
 // dB/dC: [batch, N, L] (all of the dtype); A/dA: [dim, N]; D/dD, dt_bias/ddt_bias:
-// [dim] fp32. z/dz, D/dD, dt_bias/ddt_bias are null together.
+// [dim] fp32. z/dz, D/dD, dt_bias/ddt_bias are null together. h0 (the
+// forward's initial state), dlast (the gradient flowing into its final state)
+// and dh0: [batch, dim, N] fp32, each may be null.
 struct BwdTensors {
     const void* x;
     const void* delta;
@@ -108,6 +111,9 @@ struct BwdTensors {
     float* dD;
     void* dz;
     float* ddt_bias;
+    const float* h0;
+    const float* dlast;
+    float* dh0;
 };
 // segments > 1: the sequence is cut into segments of seg_len tokens (a
 // multiple of kChunk, every segment non-empty), swept in parallel.

@@ -40,7 +40,8 @@ class FwdOpts(ctypes.Structure):
 
 
 class BwdOpts(ctypes.Structure):
-    _fields_ = [("segments", ctypes.c_int32)]
+    _fields_ = [("h0", ctypes.c_void_p), ("dlast_state", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
+                ("segments", ctypes.c_int32)]
 
 
 class SsdDims(ctypes.Structure):
@@ -244,13 +245,16 @@ def step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Ten
 def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
         dt_bias: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
-        want_dD: bool = True, want_ddt_bias: bool = True, segments: int = 0) -> dict:
+        want_dD: bool = True, want_ddt_bias: bool = True, segments: int = 0,
+        h0: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
+        want_dh0: bool = False) -> dict:
     """Backward pass (selscan_bwd): gradients for the output gradient ``dy``.
 
     Returns a dict with dx, ddelta, dB, dC (input dtype), dA [dim, N] fp32, and
     dz (when z is given), dD and ddt_bias ([dim] fp32, when wanted).
-    ``segments`` other than 0 (automatic) calls selscan_bwd_ex with that
-    many sequence segments.
+    ``h0`` (the forward's initial state), ``dlast_state`` (the gradient into
+    its final state), ``want_dh0`` (adds dh0 [batch, dim, N] fp32) and
+    ``segments`` other than 0 (automatic) call selscan_bwd_ex.
     """
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
@@ -263,7 +267,9 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
                                (z, "z", x.dtype, (batch, dim, L)), (dy, "dy", x.dtype, (batch, dim, L)),
                                (A, "A", torch.float32, (dim, N)), (B, "B", x.dtype, (batch, N, L)),
                                (C, "C", x.dtype, (batch, N, L)), (D, "D", torch.float32, (dim,)),
-                               (dt_bias, "dt_bias", torch.float32, (dim,))):
+                               (dt_bias, "dt_bias", torch.float32, (dim,)),
+                               (h0, "h0", torch.float32, (batch, dim, N)),
+                               (dlast_state, "dlast_state", torch.float32, (batch, dim, N))):
         _req(t, name, dt, shape, dev)
     out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty_like(B),
            "dC": torch.empty_like(C), "dA": torch.empty_like(A)}
@@ -273,15 +279,17 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
         out["dD"] = torch.empty((dim,), dtype=torch.float32, device=dev)
     if want_ddt_bias:
         out["ddt_bias"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    if want_dh0:
+        out["dh0"] = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
     args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
             _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
             _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out.get("ddt_bias")),
             ctypes.byref(dims))
-    if segments == 0:
+    if segments == 0 and h0 is None and dlast_state is None and not want_dh0:
         _check(lib.selscan_bwd(*args, _stream(dev)))
     else:
-        opts = BwdOpts(segments)
+        opts = BwdOpts(_ptr(h0), _ptr(dlast_state), _ptr(out.get("dh0")), segments)
         _check(lib.selscan_bwd_ex(*args, ctypes.byref(opts), _stream(dev)))
     return out
 

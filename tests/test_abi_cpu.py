@@ -299,9 +299,20 @@ def test_bwd_argument_checks():
 def test_bwd_ex_option_checks():
     p = [P(i) for i in range(17)]
     for seg in (-1, 65537):
-        o = S.BwdOpts(seg)
+        o = S.BwdOpts(segments=seg)
         assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_CONFIG, seg
-    o = S.BwdOpts(4)
+    # h0, dlast_state and dh0: 16-byte aligned; dh0 is an output
+    for field in ("h0", "dlast_state", "dh0"):
+        o = S.BwdOpts(segments=1)
+        setattr(o, field, BASE + 17 * SPAN + 4)
+        assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIGN, field
+    o = S.BwdOpts(h0=BASE + 17 * SPAN, dlast_state=BASE + 18 * SPAN, dh0=BASE + 0 * SPAN)  # dh0 == x
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
+    o = S.BwdOpts(h0=BASE + 17 * SPAN, dh0=BASE + 17 * SPAN)                            # dh0 == h0
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
+    o = S.BwdOpts(dh0=BASE + 9 * SPAN)                                                 # dh0 == dx
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
+    o = S.BwdOpts(segments=4)
     assert S.lib.selscan_bwd_ex(*p, None, ctypes.byref(o), None) == S.ERR_NULL
     assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D(batch=-1)), ctypes.byref(o), None) == S.ERR_DIMS
     assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D(N=8)), None, None) == S.ERR_DSTATE

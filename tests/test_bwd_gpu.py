@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 M14 = W.HEADLINE
 M130 = "m130m_f32_b8_l2048_d1536"
-GRADS = ("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddt_bias")
+GRADS = ("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddt_bias", "dh0")
 
 
 def case(msg):
@@ -154,6 +154,83 @@ def test_bwd_segmented_deterministic_and_close_to_one_sweep():
             e16 = oracle.scaled_error(to_np(s1[k]), ref[k], ref[k + "_scale"])
             print(f"[parity] {k}: one sweep {e1:.2e}, 16 segments {e16:.2e}", flush=True)
             assert e1 <= TOL["f32"] and e16 <= TOL["f32"], k
+
+
+STATE_CASES = [
+    # (batch, L, dim, dtype, segments)
+    (2, 100, 130, "bf16", 0),
+    (1, 300, 64, "f32", 1),
+    (1, 300, 64, "f32", 3),
+    (2, 47, 65, "f32", 0),
+    (1, 1000, 64, "bf16", 0),    # automatic: segmented
+]
+
+
+@pytest.mark.parametrize("batch,L,dim,dtype,segments", STATE_CASES)
+def test_bwd_initial_and_final_state(batch, L, dim, dtype, segments):
+    """The forward starts from h0, a gradient flows into its final state, and
+    dh0 is returned: every gradient against the oracle."""
+    inp = small(M14 if dtype == "bf16" else M130, batch=batch, seqlen=L, dim=dim)
+    rng = np.random.default_rng([L, dim, 5])
+    h0 = rng.standard_normal((batch, dim, 16)).astype(np.float32)
+    dlast = rng.standard_normal((batch, dim, 16)).astype(np.float32)
+    dy = _dy((batch, dim, L), L + 3)
+    if dtype == "bf16":
+        dy = W._maybe_bf16(W.get(M14), dy)
+    case(f"bwd h0+dlast+dh0 segments={segments} b{batch} L{L} d{dim} {dtype}")
+    td = TDT[dtype]
+    g = selscan.bwd(dev(inp["x"], td), dev(inp["delta"], td), dev(inp["A"]), dev(inp["B"], td),
+                    dev(inp["C"], td), D=dev(inp["D"]), z=dev(inp["z"], td),
+                    dt_bias=dev(inp["dt_bias"]), dy=dev(dy, td), segments=segments,
+                    h0=dev(h0), dlast_state=dev(dlast), want_dh0=True)
+    ref = oracle.bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                     inp["dt_bias"], dy=dy, h0=h0, dlast_state=dlast, want_dh0=True)
+    _check(g, ref, dtype, f"h0/dlast segments={segments} b{batch} L{L} d{dim} {dtype}")
+
+
+def test_bwd_split_sequence_matches_unsplit():
+    """Training a sequence in two pieces: the second piece's backward from
+    h0 = the first piece's final state gives dh0, fed to the first piece as
+    the gradient of its final state. The pieces' gradients equal the unsplit
+    backward's (dA, dD, ddt_bias as sums)."""
+    batch, L, dim, cut = 2, 600, 64, 237
+    inp = small(M130, batch=batch, seqlen=L, dim=dim)
+    dy = _dy((batch, dim, L), 12)
+    case(f"bwd split at {cut} of L{L}")
+    ref = _ref(inp, dy)
+    part = lambda a, lo, hi: np.ascontiguousarray(a[..., lo:hi])
+    args = lambda lo, hi: (dev(part(inp["x"], lo, hi)), dev(part(inp["delta"], lo, hi)),
+                           dev(inp["A"]), dev(part(inp["B"], lo, hi)), dev(part(inp["C"], lo, hi)))
+    kw = lambda lo, hi: dict(D=dev(inp["D"]), z=dev(part(inp["z"], lo, hi)),
+                             dt_bias=dev(inp["dt_bias"]), dy=dev(part(dy, lo, hi)))
+    # the state entering the second piece, from the oracle's forward of the first
+    h_mid = oracle.fwd(part(inp["x"], 0, cut), part(inp["delta"], 0, cut), inp["A"],
+                       part(inp["B"], 0, cut), part(inp["C"], 0, cut), inp["D"],
+                       part(inp["z"], 0, cut), inp["dt_bias"])["last_state"].astype(np.float32)
+    g2 = selscan.bwd(*args(cut, L), **kw(cut, L), h0=dev(h_mid), want_dh0=True)
+    g1 = selscan.bwd(*args(0, cut), **kw(0, cut), dlast_state=g2["dh0"])
+    torch.cuda.synchronize()
+    joined = {k: np.concatenate([to_np(g1[k]), to_np(g2[k])], axis=-1)
+              for k in ("dx", "ddelta", "dz", "dB", "dC")}
+    for k in ("dA", "dD", "ddt_bias"):
+        joined[k] = to_np(g1[k]) + to_np(g2[k])
+    worst = {k: oracle.scaled_error(v, ref[k], ref[k + "_scale"]) for k, v in joined.items()}
+    print("[parity] split: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    bad = {k: v for k, v in worst.items() if not v <= TOL["f32"]}
+    assert not bad, bad
+
+
+def test_bwd_empty_passes_dlast_to_dh0():
+    case("bwd L = 0 with dlast_state")
+    x = torch.empty((2, 64, 0), device="cuda")
+    A = -torch.ones((64, 16), device="cuda")
+    B = torch.empty((2, 16, 0), device="cuda")
+    dl = torch.randn((2, 64, 16), device="cuda")
+    g = selscan.bwd(x, x.clone(), A, B, B.clone(), dy=x.clone(), h0=torch.ones_like(dl),
+                    dlast_state=dl, want_dh0=True)
+    g0 = selscan.bwd(x, x.clone(), A, B, B.clone(), dy=x.clone(), want_dh0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dl) and torch.all(g0["dh0"] == 0)
 
 
 def test_bwd_empty():
