@@ -497,43 +497,59 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     }
 }
 
-// dB[b,n,t] = ln 2 * sum_rb pB[rb,b,t,n] and dC[b,n,t] = sum_rb pC[rb,b,t,n],
-// row blocks in order; one thread per (b, t).
+// dB[b,n,t] = ln 2 * sum_rb pB[rb,b,t,n] and dC[b,n,t] = sum_rb pC[rb,b,t,n].
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ pB,
                                                      const float* __restrict__ pC, T* __restrict__ dB,
                                                      T* __restrict__ dC, int64_t batch, int64_t L,
                                                      int64_t Lp, int32_t row_blocks) {
-    // One thread per (b, 4 states, t), t fastest: the output rows are written
-    // contiguously, and the four threads reading one 64-byte partial record
-    // (one per state quad) share it through L2. The row blocks are summed in
-    // order (deterministic), eight loads in flight at a time.
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= batch * 4 * L) return;
-    const int64_t t = i % L, bq = i / L;
-    const int q = int(bq % 4);
-    const int64_t b = bq / 4;
+    // A lane takes one (b, t, 4 states), the state quad fastest, so a wave
+    // reads 16 whole 64-byte partial records (1 KiB contiguous) from each row
+    // block; the block's 4 waves take a quarter of the row blocks each, summed
+    // in order, and wave 0 adds the quarters in order (deterministic).
+    __shared__ float4 part[2][3][kWave];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t i = int64_t(blockIdx.x) * kWave + lane;
+    const bool ok = i < batch * L * 4;
+    const int q = int(i % 4);
+    const int64_t bt = ok ? i / 4 : 0;
+    const int64_t t = bt % L, b = bt / L;
+    const int r_lo = int(int64_t(row_blocks) * w / 4), r_hi = int(int64_t(row_blocks) * (w + 1) / 4);
     float4 sb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sc = sb;
     const int64_t step = batch * Lp * kN;  // floats from one row block to the next
     const float* ob = pB + (b * Lp + t) * kN + 4 * q;
     const float* oc = pC + (b * Lp + t) * kN + 4 * q;
-    int r = 0;
-    for (; r + 8 <= row_blocks; r += 8) {
-        float4 vb[8], vc[8];
+    int r = r_lo;
+    if (ok) {
+        for (; r + 8 <= r_hi; r += 8) {
+            float4 vb[8], vc[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            vb[u] = *reinterpret_cast<const float4*>(ob + (r + u) * step);
-            vc[u] = *reinterpret_cast<const float4*>(oc + (r + u) * step);
+            for (int u = 0; u < 8; ++u) {
+                vb[u] = *reinterpret_cast<const float4*>(ob + (r + u) * step);
+                vc[u] = *reinterpret_cast<const float4*>(oc + (r + u) * step);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                sb.x += vb[u].x; sb.y += vb[u].y; sb.z += vb[u].z; sb.w += vb[u].w;
+                sc.x += vc[u].x; sc.y += vc[u].y; sc.z += vc[u].z; sc.w += vc[u].w;
+            }
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            sb.x += vb[u].x; sb.y += vb[u].y; sb.z += vb[u].z; sb.w += vb[u].w;
-            sc.x += vc[u].x; sc.y += vc[u].y; sc.z += vc[u].z; sc.w += vc[u].w;
+        for (; r < r_hi; ++r) {
+            const float4 vb = *reinterpret_cast<const float4*>(ob + r * step);
+            const float4 vc = *reinterpret_cast<const float4*>(oc + r * step);
+            sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+            sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
         }
     }
-    for (; r < row_blocks; ++r) {
-        const float4 vb = *reinterpret_cast<const float4*>(ob + r * step);
-        const float4 vc = *reinterpret_cast<const float4*>(oc + r * step);
+    if (w > 0) {
+        part[0][w - 1][lane] = sb;
+        part[1][w - 1][lane] = sc;
+    }
+    __syncthreads();
+    if (w > 0 || !ok) return;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        const float4 vb = part[0][g][lane], vc = part[1][g][lane];
         sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
         sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
     }
@@ -545,26 +561,55 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ p
     }
 }
 
-// dA[d,n] = ln 2 * sum_b pA[b,d,n]; dD[d] = sum_b pD[b,d]; ddt_bias[d] = sum_b pT[b,d]
-// (b runs over segments x batch entries, in order).
+// dA[d,n] = ln 2 * sum_e pA[e,d,n]; dD[d] = sum_e pD[e,d]; ddt_bias[d] = sum_e pT[e,d],
+// e over the entries (segment x batch entry). A block takes 64 outputs
+// (4 channels x 16 states); each of its waves a quarter of the entries,
+// summed in order; wave 0 adds the quarters in order (deterministic).
 __global__ __launch_bounds__(256) void bwd_reduce_params(const float* __restrict__ pA,
                                                          const float* __restrict__ pD,
                                                          const float* __restrict__ pT,
                                                          float* __restrict__ dA, float* dD,
-                                                         float* ddt, int64_t batch, int64_t dim) {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= dim * kN) return;
+                                                         float* ddt, int64_t entries, int64_t dim) {
+    __shared__ float part[3][3][kWave];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t i = int64_t(blockIdx.x) * kWave + lane;  // d * N + n
+    const bool ok = i < dim * kN;
     const int64_t d = i / kN;
-    const int n = int(i % kN);
-    float s = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) s += pA[(b * dim + d) * kN + n];
-    dA[i] = s * kLn2;
-    if (n == 0) {
-        float sD = 0.0f, sT = 0.0f;
-        for (int64_t b = 0; b < batch; ++b) {
-            sD += pD[b * dim + d];
-            sT += pT[b * dim + d];
+    const bool first = ok && i % kN == 0;  // this lane also sums dD and ddt_bias of channel d
+    const int64_t e_lo = entries * w / 4, e_hi = entries * (w + 1) / 4;
+    const int64_t sA = dim * kN;  // floats from one entry to the next
+    float s = 0.0f, sD = 0.0f, sT = 0.0f;
+    if (ok) {
+        int64_t e = e_lo;
+        for (; e + 8 <= e_hi; e += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = pA[(e + u) * sA + i];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
         }
+        for (; e < e_hi; ++e) s += pA[e * sA + i];
+        if (first)
+            for (e = e_lo; e < e_hi; ++e) {
+                sD += pD[e * dim + d];
+                sT += pT[e * dim + d];
+            }
+    }
+    if (w > 0) {
+        part[0][w - 1][lane] = s;
+        part[1][w - 1][lane] = sD;
+        part[2][w - 1][lane] = sT;
+    }
+    __syncthreads();
+    if (w > 0 || !ok) return;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        s += part[0][g][lane];
+        sD += part[1][g][lane];
+        sT += part[2][g][lane];
+    }
+    dA[i] = s * kLn2;
+    if (first) {
         if (dD) dD[d] = sD;
         if (ddt) ddt[d] = sT;
     }
@@ -675,12 +720,12 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
     k.dh0 = t.dh0;
     e = launch_bwd_kernel<T, false>(k, gate, vec, per_seg * segments, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * 4 * L + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * 4 * L + kWave - 1) / kWave)), dim3(256), 0, st,
                        k.pB, k.pC, static_cast<T*>(t.dB), static_cast<T*>(t.dC), batch, L, k.Lp,
                        k.row_blocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_reduce_params, dim3(unsigned((dim * kN + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(bwd_reduce_params, dim3(unsigned((dim * kN + kWave - 1) / kWave)), dim3(256), 0, st,
                        k.pA, k.pD, k.pT, t.dA, t.dD, t.ddt_bias, batch * segments, dim);
     return hipGetLastError();
 }
