@@ -232,32 +232,48 @@ def time_decode(w, steps, warmup, torch, dev):
 def time_bwd(torch, dev, reps=5):
     """The backward pass on the headline shape (bf16, gate, D, dt_bias): all
     eight gradients for a synthetic dy, whole call (checkpoint pass, reverse
-    pass, fixed-order reductions, workspace on the stream)."""
+    pass, fixed-order reductions, workspace on the stream). Also timed: the
+    forward that stores checkpoints and the backward that takes them (no
+    checkpoint pass), i.e. a training step's two calls each way."""
     from selective_state_space_48_amd import selscan
     from selective_state_space_48_amd import workloads as W
 
     w = W.get(W.HEADLINE)
     d = device_inputs(w, torch, dev)
     dy = torch.randn(d["x"].shape, generator=torch.Generator().manual_seed(8)).to(dev).to(torch.bfloat16)
-    run = lambda: selscan.bwd(d["x"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
-                              dt_bias=d["dt_bias"], dy=dy)
-    for _ in range(2):
-        run()
-    torch.cuda.synchronize(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        run()
-    e1.record()
-    torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1) / reps
+    y = torch.empty_like(d["x"])
+    ck = torch.empty(selscan.ckpt_shape(w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
+    args = (d["x"], d["delta"], d["A"], d["B"], d["C"])
+    kw = dict(D=d["D"], z=d["z"], dt_bias=d["dt_bias"])
+
+    def timed(run):
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(lambda: selscan.bwd(*args, **kw, dy=dy))
+    fwd_ms = timed(lambda: selscan.fwd(*args, **kw, y=y))
+    fwd_ck_ms = timed(lambda: selscan.fwd(*args, **kw, y=y, ckpt=ck))
+    bwd_ck_ms = timed(lambda: selscan.bwd(*args, **kw, dy=dy, ckpt=ck))
     # algorithmic bytes: read x, delta, z, dy, B, C; write dx, ddelta, dz, dB, dC
     nbytes = 7 * w.elements * 2 + 4 * w.batch * w.dstate * w.seqlen * 2
-    del d, dy
+    del d, dy, y, ck
     return {"workload": f"backward on {w.name}", "ms_per_call": round(ms, 4),
             "Gelem_per_s": round(w.elements / (ms * 1e-3) / 1e9, 2),
-            "ratio_to_forward": None, "algorithmic_bytes": nbytes,
-            "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4)}
+            "ratio_to_forward": round(ms / fwd_ms, 2), "algorithmic_bytes": nbytes,
+            "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 4),
+            "forward_ms": round(fwd_ms, 4),
+            "forward_storing_checkpoints_ms": round(fwd_ck_ms, 4),
+            "backward_from_checkpoints_ms": round(bwd_ck_ms, 4),
+            "training_step_ms": {"recompute": round(fwd_ms + ms, 4),
+                                 "checkpoints": round(fwd_ck_ms + bwd_ck_ms, 4)}}
 
 
 def time_bwd_long(torch, dev, reps=3):

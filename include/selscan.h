@@ -112,6 +112,14 @@ int selscan_fwd(const void* x, const void* delta, const float* A, const void* B,
  *               up to the kernels' 32-token tile. Results agree to rounding.
  *   groups    : waves per 64-row block, each taking N/groups states: 1, 2 or
  *               4; 0 = automatic. Results agree to rounding.
+ *   ckpt      : NULL, or a [ceil(L/16), B, d, N] fp32 output: the state
+ *               entering tokens 0, 16, 32, ... of every row (token 0's is h0
+ *               or zeros), for a later selscan_bwd_ex over the same inputs,
+ *               which then need not recompute them ("Mamba: Linear-Time
+ *               Sequence Modeling with Selective State Spaces" (azimuth.plus),
+ *               hardware-aware algorithm: the backward recomputes states
+ *               rather than storing all L of them; these are 1/16 of them).
+ *               Requires groups 0 or 4. Must not overlap any input or output.
  */
 typedef struct {
     const float* h0;
@@ -119,6 +127,7 @@ typedef struct {
     uint64_t workspace_bytes;
     int32_t segments;
     int32_t groups;
+    float* ckpt;
 } selscan_fwd_opts_t;
 
 /*
@@ -218,6 +227,10 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
  *   dh0         : [B, d, N] fp32 output, the gradient of h0 (the adjoint
  *                 carry leaving the first token); NULL = not wanted. With
  *                 L = 0 it is dlast_state (or zeros).
+ *   ckpt        : [ceil(L/16), B, d, N] fp32, the checkpoints a
+ *                 selscan_fwd_ex over the same inputs (and h0) wrote; the
+ *                 call then skips recomputing them (and takes no workspace
+ *                 for them). NULL = recompute.
  *   segments : sequence segments swept in parallel. 1 = one reverse sweep per
  *              row; > 1 = the states entering the segments (a forward state
  *              pass and carries), the checkpoint pass over all segments, a
@@ -233,6 +246,7 @@ typedef struct {
     const float* dlast_state;
     float* dh0;
     int32_t segments;
+    const float* ckpt;
 } selscan_bwd_opts_t;
 
 /*
@@ -246,8 +260,8 @@ typedef struct {
  * second part's backward with h0 = the first part's last_state and the first
  * part's with dlast_state = the second part's dh0 gives the unsplit
  * gradients (dA, dD, ddt_bias as the sum of the parts') up to rounding.
- * h0, dlast_state and dh0 must be 16-byte aligned; dh0 must not overlap any
- * input or other output. A segmented call takes, beyond the workspace above,
+ * h0, dlast_state, dh0 and ckpt must be 16-byte aligned; dh0 must not
+ * overlap any input or other output. A segmented call takes, beyond the workspace above,
  * 2 S B d 16 fp32 states, S B d doubles and S-fold dA/dD/ddt_bias partial
  * sums. Errors as selscan_bwd, plus SELSCAN_ERR_CONFIG for segments out of
  * range.

@@ -111,6 +111,7 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
 int check_opts(const selscan_fwd_opts_t& o) {
     if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
     if (o.groups != 0 && o.groups != 1 && o.groups != 2 && o.groups != 4) return SELSCAN_ERR_CONFIG;
+    if (o.ckpt && o.groups != 0 && o.groups != 4) return SELSCAN_ERR_CONFIG;  // 4 waves store them
     return SELSCAN_OK;
 }
 
@@ -154,7 +155,7 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     if ((sz.seq > 0 && (!x || !delta || !y)) || (sz.bc > 0 && (!B || !C)) || (sz.param > 0 && !A))
         return SELSCAN_ERR_NULL;
     for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, (const void*)y,
-                          (const void*)last_state, (const void*)o.h0})
+                          (const void*)last_state, (const void*)o.h0, (const void*)o.ckpt})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u)) return SELSCAN_ERR_CONFIG;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
@@ -170,6 +171,14 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     const Span in_h0 = span(o.h0, sz.state * 4);
     if (overlaps(in_h0, out_y)) return SELSCAN_ERR_ALIAS;
     if (overlaps(in_h0, out_s) && static_cast<const void*>(o.h0) != static_cast<const void*>(last_state))
+        return SELSCAN_ERR_ALIAS;
+    // checkpoints: an output of ceil(L/16) states per row
+    int64_t ck_bytes = 0;
+    if (o.ckpt && !mul_ok((L + 15) / 16, sz.state * 4, &ck_bytes)) return SELSCAN_ERR_DIMS;
+    const Span out_c = span(o.ckpt, ck_bytes);
+    for (const Span& s : ins)
+        if (overlaps(s, out_c)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_c, out_y) || overlaps(out_c, out_s) || overlaps(out_c, in_h0))
         return SELSCAN_ERR_ALIAS;
 
     FwdPlan plan{};
@@ -188,7 +197,7 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
         return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
     }
 
-    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state, o.h0};
+    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state, o.h0, o.ckpt};
     next_events(&plan.ev_begin, &plan.ev_end);
     void* ws = o.workspace;
     const bool own = ws == nullptr;
@@ -348,6 +357,9 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
     Sizes sz;
     int rc = check_fwd_dims(dims, &sz);
     if (rc != SELSCAN_OK) return rc;
+    int64_t ck_bytes = 0;
+    if (o.ckpt && !mul_ok((dims->seqlen + 15) / 16, sz.state * 4, &ck_bytes)) rc = SELSCAN_ERR_DIMS;
+    if (rc != SELSCAN_OK) return rc;
     const int64_t L = dims->seqlen;
     if ((sz.seq > 0 && (!x || !delta || !dy || !dx || !ddelta)) || (sz.bc > 0 && (!B || !C || !dB || !dC)) ||
         (sz.param > 0 && (!A || !dA)))
@@ -357,7 +369,8 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
     for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, dy,
                           (const void*)dx, (const void*)ddelta, (const void*)dA, (const void*)dB,
                           (const void*)dC, (const void*)dD, (const void*)dz, (const void*)ddt_bias,
-                          (const void*)o.h0, (const void*)o.dlast_state, (const void*)o.dh0})
+                          (const void*)o.h0, (const void*)o.dlast_state, (const void*)o.dh0,
+                          (const void*)o.ckpt})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
     const Span outs[] = {span(dx, sz.seq * es), span(ddelta, sz.seq * es), span(dz, sz.seq * es),
@@ -367,7 +380,8 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
     const Span ins[] = {span(x, sz.seq * es), span(delta, sz.seq * es), span(z, sz.seq * es),
                         span(dy, sz.seq * es), span(B, sz.bc * es),     span(C, sz.bc * es),
                         span(A, sz.param * 4), span(D, dims->dim * 4),  span(dt_bias, dims->dim * 4),
-                        span(o.h0, sz.state * 4), span(o.dlast_state, sz.state * 4)};
+                        span(o.h0, sz.state * 4), span(o.dlast_state, sz.state * 4),
+                        span(o.ckpt, ck_bytes)};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
         for (const Span& s : ins)
             if (overlaps(s, outs[i])) return SELSCAN_ERR_ALIAS;
@@ -393,14 +407,14 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
     if ((L + 15) / 16 * ((dims->dim + kWave - 1) / kWave) > INT32_MAX ||
         ((dims->dim + kWave - 1) / kWave) * dims->batch * segments > INT32_MAX)
         return SELSCAN_ERR_DIMS;
-    const size_t ws_bytes = bwd_workspace_bytes(dims->batch, L, dims->dim, segments);
+    const size_t ws_bytes = bwd_workspace_bytes(dims->batch, L, dims->dim, segments, o.ckpt != nullptr);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
         (void)hipGetLastError();
         return SELSCAN_ERR_ALLOC;
     }
     BwdTensors t{x,  delta, A,  B,  C,  D,  z,        dt_bias, dy,
-                 dx, ddelta, dA, dB, dC, dD, dz, ddt_bias, o.h0, o.dlast_state, o.dh0};
+                 dx, ddelta, dA, dB, dC, dD, dz, ddt_bias, o.h0, o.dlast_state, o.dh0, o.ckpt};
     const hipError_t e = launch_bwd(t, dims->batch, L, dims->dim,
                                     dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
                                     segments, seg_len, ws, st);

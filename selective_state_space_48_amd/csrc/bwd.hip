@@ -58,6 +58,7 @@ struct BwdKArgs {
     const float* ckpt;   // [nck][batch*dim][N]
     void* dx;
     void* ddelta;
+    void* dz;            // [batch, dim, L] (gated only)
     float* pB;           // [row_blocks][batch][Lp][N]: sum over the block's rows of dh * l x
     float* pC;           // [row_blocks][batch][Lp][N]: sum over the block's rows of ds * h
     float* pA;           // [segments][batch*dim][N]: sum over the segment's t of q * l
@@ -77,14 +78,15 @@ struct BwdKArgs {
 };
 
 // LDS: per-token (l, w) and ds of the chunk for the scan waves, and the
-// waves' per-token partial sums over their states (sum q A, sum dh B').
-// Row strides are odd multiples of 16 bytes.
+// waves' per-token partial sums over their states (sum q A, sum dh B', and,
+// gated, sum C h). Row strides are odd multiples of 16 bytes.
 struct alignas(16) BwdSmem {
     static constexpr int kLW = kBCH * 8 + 16;
     static constexpr int kDS = kBCH * 4 + 16;
     unsigned char lw[kWave * kLW];
     unsigned char ds[kWave * kDS];
     unsigned char part[kBG][kWave * kLW];
+    unsigned char py[kBG][kWave * kDS];
     float bc[kBNSB * kBG * kRecF];  // the chunk's packed B/C records, as laid out in P
 };
 
@@ -224,9 +226,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         }
     };
     // Values a per-token thread keeps from its prologue to its epilogue of the
-    // same chunk: x, ds, sigmoid(u), l.
+    // same chunk: x, sigmoid(u), and (gated) dy silu'(z). Its l and ds are
+    // read back from LDS, where they stay for the scan until the next prologue.
     struct Keep {
-        float x[kBTS], ds[kBTS], sg[kBTS], l[kBTS];
+        float x[kBTS], sg[kBTS], dzf[GATE ? kBTS : 1];
     };
     double lsum_acc = 0.0;  // carry pass: this thread's tokens' summed step sizes
     // ---- per-token prologue of chunk c: (l, w) and ds to LDS ----
@@ -245,12 +248,16 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
             const float lv = softplus_log2_of(ul);
             l[e] = ok ? lv : 0.0f;
             w[e] = l[e] * xs[e];
-            const float g = GATE ? silu(zs[e]) : 1.0f;
+            float g = 1.0f;
+            if constexpr (GATE) {
+                // silu(z) = z sig(z); silu'(z) = sig(z) (1 + z (1 - sig(z)))
+                const float sz = rcp_hw(1.0f + exp2_hw(-zs[e] * kLog2e));
+                g = zs[e] * sz;
+                k.dzf[e] = ok ? gs[e] * (sz * fmaf(zs[e], 1.0f - sz, 1.0f)) : 0.0f;
+            }
             dsv[e] = ok ? gs[e] * g : 0.0f;
             k.x[e] = xs[e];
-            k.ds[e] = dsv[e];
             k.sg[e] = exp2_hw(ul - lv);  // sigmoid(u) = e^u / (1 + e^u)
-            k.l[e] = l[e];
             if constexpr (CARRY) lsum_acc += double(l[e]);
         }
         float4* lwr = reinterpret_cast<float4*>(&sm.lw[pr * S::kLW]) + pq * 2;
@@ -328,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
             }
         }
         float2* prt = reinterpret_cast<float2*>(&sm.part[wv][lane * S::kLW]);
+        float4* pyt = reinterpret_cast<float4*>(&sm.py[wv][lane * S::kDS]);
 #pragma unroll
         for (int sb = kBNSB - 1; sb >= 0; --sb) {
             float Bv[16], Cv[16];
@@ -338,13 +346,13 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
                 Bv[4 * q] = v.x; Bv[4 * q + 1] = v.y; Bv[4 * q + 2] = v.z; Bv[4 * q + 3] = v.w;
                 Cv[4 * q] = w.x; Cv[4 * q + 1] = w.y; Cv[4 * q + 2] = w.z; Cv[4 * q + 3] = w.w;
             }
-            float vB[16], vC[16];
+            float vB[16], vC[16], yv[kBSB];
 #pragma unroll
             for (int e = kBSB - 1; e >= 0; --e) {
                 const int t = sb * kBSB + e;
                 const float2 lw = lw2[t];
                 const float ds = dsr[t];
-                float accA = 0.0f, accB = 0.0f;
+                float accA = 0.0f, accB = 0.0f, accY = 0.0f;
 #pragma unroll
                 for (int j = 0; j < kBNG; ++j) {
                     const float dh = fmaf(ds, Cv[j * kBSB + e], carry[j]);
@@ -355,9 +363,12 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
                     accB = fmaf(dh, Bv[j * kBSB + e], accB);
                     vB[e * 4 + j] = dh * lw.y;
                     vC[e * 4 + j] = ds * H[t][j];
+                    if constexpr (GATE) accY = fmaf(Cv[j * kBSB + e], H[t][j], accY);
                 }
                 prt[t] = make_float2(accA, accB);
+                yv[e] = accY;
             }
+            if constexpr (GATE) pyt[sb] = make_float4(yv[0], yv[1], yv[2], yv[3]);
             float sB[4], sC[4];
             wave_sum16(vB, sB);
             wave_sum16(vC, sC);
@@ -375,7 +386,24 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     auto epilogue = [&](int c, const Keep& k) {
         if constexpr (CARRY) return;
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
-        float dxv[4], ddv[4];
+        const float4* lwr = reinterpret_cast<const float4*>(&sm.lw[pr * S::kLW]) + pq * 2;
+        const float4 lw01 = lwr[0], lw23 = lwr[1];
+        const float4 ds4 = *(reinterpret_cast<const float4*>(&sm.ds[pr * S::kDS]) + pq);
+        const float kl[4] = {lw01.x, lw01.z, lw23.x, lw23.z};
+        const float kds[4] = {ds4.x, ds4.y, ds4.z, ds4.w};
+        float dxv[4], ddv[4], dzv[4];
+        if constexpr (GATE) {
+            // dz = dy silu'(z) (C.h + D x), the waves' partial sums added in order
+            float4 y4 = reinterpret_cast<const float4*>(&sm.py[0][pr * S::kDS])[pq];
+#pragma unroll
+            for (int g = 1; g < kBG; ++g) {
+                const float4 v = reinterpret_cast<const float4*>(&sm.py[g][pr * S::kDS])[pq];
+                y4.x += v.x; y4.y += v.y; y4.z += v.z; y4.w += v.w;
+            }
+            const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dzv[e] = fmaf(Dd, k.x[e], yv[e]) * k.dzf[e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float AA = 0.0f, BB = 0.0f;
@@ -387,10 +415,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
             }
             // B was packed times ln 2: BB = ln2 * sum dh B, and delta = l ln 2.
             const float ddl = fmaf(k.x[e] * BB, kLog2e, AA);
-            dxv[e] = fmaf(k.l[e], BB, k.ds[e] * Dd);
+            dxv[e] = fmaf(kl[e], BB, kds[e] * Dd);
             ddv[e] = ddl * k.sg[e];
             if (t0 + e < a.L) {
-                dDacc = fmaf(k.ds[e], k.x[e], dDacc);
+                dDacc = fmaf(kds[e], k.x[e], dDacc);
                 dTacc += ddv[e];
             }
         }
@@ -398,15 +426,18 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         const int64_t off = prow * a.L + t0;
         T* DXo = static_cast<T*>(a.dx);
         T* DDo = static_cast<T*>(a.ddelta);
+        T* DZo = static_cast<T*>(a.dz);
         if (VEC && t0 + kBTS <= a.L) {
             Q::store(DXo + off, Q::pack(dxv));
             Q::store(DDo + off, Q::pack(ddv));
+            if constexpr (GATE) Q::store(DZo + off, Q::pack(dzv));
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (t0 + e < a.L) {
                     DXo[off + e] = from_f32<T>(dxv[e]);
                     DDo[off + e] = from_f32<T>(ddv[e]);
+                    if constexpr (GATE) DZo[off + e] = from_f32<T>(dzv[e]);
                 }
         }
     };
@@ -620,7 +651,7 @@ size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 struct BwdLayout {
     size_t packed, ckpt, pB, pC, pA, pD, pT, seg_state, carry, seg_lsum, total;
 };
-BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int32_t segments) {
+BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int32_t segments, bool ckpt_given) {
     const size_t rows = size_t(batch) * size_t(dim);
     const size_t S = size_t(segments);
     const size_t nck = size_t((L + kBCH - 1) / kBCH);
@@ -630,7 +661,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int32_t segments) {
     BwdLayout o{};
     size_t off = 0;
     o.packed = off; off += al256(size_t(batch) * Lp32 * 2 * kN * 4);
-    o.ckpt = off;   off += al256(nck * rows * kN * 4);
+    o.ckpt = off;   off += ckpt_given ? 0 : al256(nck * rows * kN * 4);
     o.pB = off;     off += al256(rbk * size_t(batch) * Lp * kN * 4);
     o.pC = off;     off += al256(rbk * size_t(batch) * Lp * kN * 4);
     o.pA = off;     off += al256(S * rows * kN * 4);
@@ -672,21 +703,22 @@ template <typename T>
 hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int32_t segments,
                  int64_t seg_len, void* ws, hipStream_t st) {
     unsigned char* w = static_cast<unsigned char*>(ws);
-    const BwdLayout lo = bwd_layout(batch, L, dim, segments);
-    FwdTensors ft{t.x, t.delta, t.z, t.A, t.B, t.C, t.D, t.dt_bias, nullptr, nullptr, t.h0};
+    const bool given = t.ckpt != nullptr;
+    const BwdLayout lo = bwd_layout(batch, L, dim, segments, given);
+    FwdTensors ft{t.x, t.delta, t.z, t.A, t.B, t.C, t.D, t.dt_bias, nullptr, nullptr, t.h0, nullptr};
     FwdShape fs{batch, L, dim, sizeof(T) == 2 ? DType::BF16 : DType::F32};
     float* packed = reinterpret_cast<float*>(w + lo.packed);
-    float* ckpt = reinterpret_cast<float*>(w + lo.ckpt);
+    float* ckpt = given ? nullptr : reinterpret_cast<float*>(w + lo.ckpt);
     float* seg_state = segments > 1 ? reinterpret_cast<float*>(w + lo.seg_state) : nullptr;
     float* carry = segments > 1 ? reinterpret_cast<float*>(w + lo.carry) : nullptr;
     double* seg_lsum = segments > 1 ? reinterpret_cast<double*>(w + lo.seg_lsum) : nullptr;
-    hipError_t e = launch_fwd_ckpt(ft, t.dy, t.dz, ckpt, fs, packed, segments, seg_len, seg_state,
-                                   seg_lsum, carry, st);
+    hipError_t e = launch_fwd_ckpt(ft, ckpt, fs, packed, segments, seg_len, seg_state, seg_lsum,
+                                   carry, !given, st);
     if (e != hipSuccess) return e;
 
     BwdKArgs k{};
     k.x = t.x; k.delta = t.delta; k.z = t.z; k.dy = t.dy; k.A = t.A; k.P = packed;
-    k.D = t.D; k.dt_bias = t.dt_bias; k.ckpt = ckpt; k.dx = t.dx; k.ddelta = t.ddelta;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.ckpt = given ? t.ckpt : ckpt; k.dx = t.dx; k.ddelta = t.ddelta; k.dz = t.dz;
     k.pB = reinterpret_cast<float*>(w + lo.pB);
     k.pC = reinterpret_cast<float*>(w + lo.pC);
     k.pA = reinterpret_cast<float*>(w + lo.pA);
@@ -732,8 +764,9 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int32_t segments) {
-    return bwd_layout(batch, L, dim, segments).total;
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int32_t segments,
+                           bool ckpt_given) {
+    return bwd_layout(batch, L, dim, segments, ckpt_given).total;
 }
 
 hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,

@@ -112,7 +112,8 @@ struct alignas(16) Smem {
     static constexpr int kPairB = CH * 8 + 16;  // float2-per-token row stride (bytes)
     static constexpr int kYB = CH * 4 + 16;     // float-per-token row stride (bytes)
     unsigned char lw[kWave * kPairB];
-    unsigned char yp[MODE != 1 ? G : 1][MODE != 1 ? kWave * kYB : 16];
+    static constexpr bool kReadout = MODE == 0 || MODE == 3;
+    unsigned char yp[kReadout ? G : 1][kReadout ? kWave * kYB : 16];
     double lsum[MODE == 1 ? G : 1][kWave];
 };
 
@@ -132,16 +133,16 @@ struct FwdKArgs {
     int64_t batch, L, dim, seg_len;
     int64_t psub;      // sub-blocks per batch entry in P
     int32_t segments, row_blocks;
-    // checkpoint pass of the backward (MODE 2) only:
-    const void* dy;    // [batch, dim, L] output gradient (read when gated)
+    // MODE 2 and 3 only:
     float* ckpt;       // [ceil(L/16)][batch*dim][N]: the state before every 16th token
 };
 
 // MODE 0: output pass (y, and last_state from the final segment).
 // MODE 1: state pass (each segment's end state from zero, and its summed l).
-// MODE 2: checkpoint pass of the backward: the same recurrence and readout,
-//         storing the state before every 16th token, and in place of y the
-//         gate gradient dz = dy * (C.h + D x) * silu'(z) (one segment only).
+// MODE 2: checkpoint pass of the backward: the recurrence alone, storing the
+//         state before every 16th token.
+// MODE 3: output pass that also stores those checkpoints (a forward whose
+//         backward follows).
 template <typename T, int G, bool GATE, bool VEC, int MODE>
 __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int CH = kChunk;
@@ -151,10 +152,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int TS = CH / G;              // tokens per wave in the per-token phases
     constexpr int V = Elem<T>::kPer16;      // elements per 16-byte vector
     constexpr int SV = TS / V;              // 16-byte vectors per row slice
-    constexpr bool LOADZ = GATE && MODE != 1;
-    constexpr bool LOADDY = GATE && MODE == 2;
-    constexpr bool READOUT = MODE == 0 || LOADDY;
-    static_assert(MODE != 2 || G == 4, "the checkpoint pass runs 4 waves of 4 states");
+    constexpr bool READOUT = MODE == 0 || MODE == 3;  // y = C.h + D x, gated
+    constexpr bool CKPT = MODE == 2 || MODE == 3;     // states every 16 tokens
+    constexpr bool LOADZ = GATE && READOUT;
+    static_assert(!CKPT || G == 4, "checkpoints: 4 waves of 4 states");
     static_assert(TS % V == 0 && SV >= 1, "tile shape");
     using S = Smem<G, CH, MODE>;
     __shared__ S sm;
@@ -162,7 +163,6 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const T* __restrict__ X = static_cast<const T*>(a.x);
     const T* __restrict__ DL = static_cast<const T*>(a.delta);
     const T* __restrict__ Z = static_cast<const T*>(a.z);
-    const T* __restrict__ DY = static_cast<const T*>(a.dy);
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; saying so lets every address
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // 64/G rows with CH contiguous tokens each. Two register sets alternate by
     // chunk parity.
     struct Slice {
-        uint4 x[SV], d[SV], z[LOADZ ? SV : 1], g[LOADDY ? SV : 1];
+        uint4 x[SV], d[SV], z[LOADZ ? SV : 1];
     };
     Slice sl0, sl1;
     // With 16-byte rows (VEC) the loads are issued without any condition: a
@@ -232,21 +232,18 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 sl.x[k] = load_vec(X, tk);
                 sl.d[k] = load_vec(DL, tk);
                 if constexpr (LOADZ) sl.z[k] = load_vec(Z, tk);
-                if constexpr (LOADDY) sl.g[k] = load_vec(DY, tk);
             } else {
-                float fx[V], fd[V], fz[V], fg[V];
+                float fx[V], fd[V], fz[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     const bool ok = tk + e < t_end;
                     fx[e] = ok ? to_f32(X[off + k * V + e]) : 0.0f;
                     fd[e] = ok ? to_f32(DL[off + k * V + e]) : 0.0f;
                     fz[e] = (LOADZ && ok) ? to_f32(Z[off + k * V + e]) : 0.0f;
-                    fg[e] = (LOADDY && ok) ? to_f32(DY[off + k * V + e]) : 0.0f;
                 }
                 sl.x[k] = pack16<T>(fx);
                 sl.d[k] = pack16<T>(fd);
                 if constexpr (LOADZ) sl.z[k] = pack16<T>(fz);
-                if constexpr (LOADDY) sl.g[k] = pack16<T>(fg);
             }
         }
     };
@@ -272,13 +269,6 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 s1.z[k] = load_vec(Z, ts + CH + k * V);
             }
         }
-        if constexpr (LOADDY) {
-#pragma unroll
-            for (int k = 0; k < SV; ++k) {
-                s0.g[k] = load_vec(DY, ts + k * V);
-                s1.g[k] = load_vec(DY, ts + CH + k * V);
-            }
-        }
     };
 
     // ---- per-token phase before the scan ----
@@ -288,13 +278,12 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // scaled by ln 2 when packed, so w = l * x with l in log2 units.
     auto prologue = [&](int c, const Slice& sl, float* dxo, float* gzo) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
-        float xs[TS], ds[TS], zs[TS], gs[TS];
+        float xs[TS], ds[TS], zs[TS];
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             unpack16<T>(sl.x[k], xs + k * V);
             unpack16<T>(sl.d[k], ds + k * V);
             if constexpr (LOADZ) unpack16<T>(sl.z[k], zs + k * V);
-            if constexpr (LOADDY) unpack16<T>(sl.g[k], gs + k * V);
         }
         float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]) + pq * TS / 2;
         auto body = [&](auto masked) {
@@ -311,14 +300,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                     }
                     w[u] = l[u] * xs[j + u];
                     if constexpr (MODE == 1) lsum_acc += double(l[u]);
-                    if constexpr (MODE == 0) {
+                    if constexpr (READOUT) {
                         dxo[j + u] = Dd * xs[j + u];
                         gzo[j + u] = 1.0f;
                         if constexpr (LOADZ) gzo[j + u] = silu(zs[j + u]);
-                    }
-                    if constexpr (LOADDY) {  // dz = (C.h + D x) * (dy * silu'(z))
-                        dxo[j + u] = Dd * xs[j + u];
-                        gzo[j + u] = gs[j + u] * silu_grad(zs[j + u]);
                     }
                 }
                 lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
@@ -363,7 +348,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float2* lc, f32x16& Bn,
                         f32x16& Cn, float2* ln, const float* yprev, float* yv) {
             const int sbn = sb + 1 < NSB ? sb + 1 : sb;  // stays inside the chunk
-            if constexpr (MODE == 2) {
+            if constexpr (CKPT) {
                 // the state before tokens 0 and 16 of the chunk
                 const int64_t k = (t_begin + int64_t(c) * CH + sb * SB) / 16;
                 if ((sb * SB) % 16 == 0 && row_ok && k * 16 < t_end)
@@ -494,7 +479,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         }
     }
 
-    if constexpr (MODE == 0) {
+    if constexpr (READOUT) {
         if (a.last_state && row_ok && seg == a.segments - 1) {
             float4* dst = reinterpret_cast<float4*>(a.last_state + (b * a.dim + d) * kN + n0);
 #pragma unroll
@@ -618,8 +603,8 @@ hipError_t launch_one(const FwdKArgs& k, int64_t blocks, hipStream_t st) {
 
 template <typename T, int G, int MODE>
 hipError_t dispatch_gv(const FwdKArgs& k, bool gate, bool vec, int64_t blocks, hipStream_t st) {
-    static_assert(MODE != 2 || G == 4, "checkpoint pass: 4 waves");
-    if (MODE == 1) gate = false;  // the state pass never reads z
+    static_assert(MODE < 2 || G == 4, "checkpoints: 4 waves");
+    if (MODE == 1 || MODE == 2) gate = false;  // no readout: z is never read
     if (gate) return vec ? launch_one<T, G, true, true, MODE>(k, blocks, st)
                          : launch_one<T, G, true, false, MODE>(k, blocks, st);
     return vec ? launch_one<T, G, false, true, MODE>(k, blocks, st)
@@ -660,11 +645,19 @@ hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, in
     return hipGetLastError();
 }
 
-// The output pass, bracketed by the plan's timing events when it has them.
+// The output pass, bracketed by the plan's timing events when it has them;
+// with checkpoints wanted (k.ckpt), the 4-wave variant that also stores them.
 hipError_t output_pass(DType dt, const FwdKArgs& k, const FwdPlan& p, bool gate, int64_t blocks,
                        hipStream_t st) {
     if (p.ev_begin && hipEventRecord(p.ev_begin, st) != hipSuccess) return hipGetLastError();
-    const hipError_t e = dispatch_dtype<0>(dt, k, p.groups, gate, p.vec, blocks, st);
+    hipError_t e;
+    if (k.ckpt) {
+        if (p.groups != 4) return hipErrorInvalidValue;
+        e = dt == DType::BF16 ? dispatch_gv<bf16_bits, 4, 3>(k, gate, p.vec, blocks, st)
+                              : dispatch_gv<float, 4, 3>(k, gate, p.vec, blocks, st);
+    } else {
+        e = dispatch_dtype<0>(dt, k, p.groups, gate, p.vec, blocks, st);
+    }
     if (e != hipSuccess) return e;
     if (p.ev_end && hipEventRecord(p.ev_end, st) != hipSuccess) return hipGetLastError();
     return hipSuccess;
@@ -723,7 +716,7 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
 
     FwdKArgs k{};
     k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = P;
-    k.D = t.D; k.dt_bias = t.dt_bias; k.y = t.y; k.last_state = t.last_state;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.y = t.y; k.last_state = t.last_state; k.ckpt = t.ckpt;
     k.batch = s.batch; k.L = s.L; k.dim = s.dim;
     k.seg_len = p.segments > 1 ? p.seg_len : s.L;
     k.psub = Lp / p.groups;
@@ -747,6 +740,7 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     k1.seg_state = seg_state;
     k1.seg_lsum = seg_lsum;
     k1.h0 = nullptr;
+    k1.ckpt = nullptr;
     e = dispatch_dtype<1>(s.dtype, k1, p.groups, false, p.vec, per_seg * (p.segments - 1), stream);
     if (e != hipSuccess) return e;
     // 2) carries
@@ -769,26 +763,26 @@ hipError_t launch_carry(const float* A, const float* seg_state, const double* se
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float* ckpt,
-                           const FwdShape& s, float* packed, int32_t segments, int64_t seg_len,
-                           float* seg_state, double* seg_lsum, float* carry, hipStream_t stream) {
+hipError_t launch_fwd_ckpt(const FwdTensors& t, float* ckpt, const FwdShape& s, float* packed,
+                           int32_t segments, int64_t seg_len, float* seg_state, double* seg_lsum,
+                           float* carry, bool recompute, hipStream_t stream) {
     const int64_t Lp = padded_len(s.L);
     constexpr int G = 4;
     hipError_t e = s.dtype == DType::BF16
                        ? launch_pack<bf16_bits>(t.B, t.C, packed, s.batch, s.L, Lp, G, stream)
                        : launch_pack<float>(t.B, t.C, packed, s.batch, s.L, Lp, G, stream);
     if (e != hipSuccess) return e;
+    if (!recompute) return hipSuccess;
     FwdKArgs k{};
     k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = packed;
-    k.D = t.D; k.dt_bias = t.dt_bias; k.y = dz; k.last_state = nullptr; k.h0 = t.h0;
+    k.D = t.D; k.dt_bias = t.dt_bias; k.y = nullptr; k.last_state = nullptr; k.h0 = t.h0;
     k.batch = s.batch; k.L = s.L; k.dim = s.dim;
     k.seg_len = segments > 1 ? seg_len : s.L;
     k.psub = Lp / G; k.segments = segments > 1 ? segments : 1;
     k.row_blocks = int32_t((s.dim + kWave - 1) / kWave);
-    k.dy = dy; k.ckpt = ckpt;
+    k.ckpt = ckpt;
     const int64_t per_seg = int64_t(k.row_blocks) * s.batch;
     const bool vec = (s.L * (s.dtype == DType::BF16 ? 2 : 4)) % 16 == 0;
-    const bool gate = t.z != nullptr;
     if (segments > 1) {
         // the states entering the segments: state pass over all but the last,
         // then the carries
@@ -796,8 +790,6 @@ hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float*
         k1.seg_state = seg_state;
         k1.seg_lsum = seg_lsum;
         k1.h0 = nullptr;  // every segment from zero; h0 enters through the carries
-        k1.y = nullptr;
-        k1.dy = nullptr;
         k1.ckpt = nullptr;
         e = s.dtype == DType::BF16
                 ? dispatch_gv<bf16_bits, G, 1>(k1, false, vec, per_seg * (segments - 1), stream)
@@ -809,8 +801,8 @@ hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float*
         k.h0 = carry;
     }
     const int64_t blocks = per_seg * k.segments;
-    return s.dtype == DType::BF16 ? dispatch_gv<bf16_bits, G, 2>(k, gate, vec, blocks, stream)
-                                  : dispatch_gv<float, G, 2>(k, gate, vec, blocks, stream);
+    return s.dtype == DType::BF16 ? dispatch_gv<bf16_bits, G, 2>(k, false, vec, blocks, stream)
+                                  : dispatch_gv<float, G, 2>(k, false, vec, blocks, stream);
 }
 
 }  // namespace selscan

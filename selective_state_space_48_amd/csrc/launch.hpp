@@ -22,6 +22,7 @@ struct FwdTensors {
     void* y;
     float* last_state;  // null: not wanted
     const float* h0;    // [batch, dim, N] state entering token 0; null: zeros
+    float* ckpt;        // [ceil(L/16)][batch*dim][N] states before every 16th token; null: none
 };
 
 struct FwdShape {
@@ -55,16 +56,15 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
 
 // Checkpoint pass of the backward: packs B/C into `packed` (the forward's
 // record layout, fwd_workspace_bytes of a one-segment plan), then runs the
-// forward recurrence storing the state before every 16th token in
-// ckpt [ceil(L/16)][batch*dim][N], and, when t.z is set, dz = dy * (C.h + D x)
-// * silu'(z) into dz ([batch, dim, L] of the dtype), from t.h0 (null: zeros).
-// 4 waves. With segments > 1
+// forward recurrence from t.h0 (null: zeros) storing the state before every
+// 16th token in ckpt [ceil(L/16)][batch*dim][N] (recompute = false: the pack
+// only, the checkpoints being given). 4 waves. With segments > 1
 // (seg_len a multiple of kChunk, every segment non-empty) the states entering
 // the segments come first, from a state pass into seg_state [segments][rows][N]
 // and seg_lsum [segments][rows] and the carries into carry [segments][rows][N].
-hipError_t launch_fwd_ckpt(const FwdTensors& t, const void* dy, void* dz, float* ckpt,
-                           const FwdShape& s, float* packed, int32_t segments, int64_t seg_len,
-                           float* seg_state, double* seg_lsum, float* carry, hipStream_t stream);
+hipError_t launch_fwd_ckpt(const FwdTensors& t, float* ckpt, const FwdShape& s, float* packed,
+                           int32_t segments, int64_t seg_len, float* seg_state, double* seg_lsum,
+                           float* carry, bool recompute, hipStream_t stream);
 
 // Carries of a segmented scan, per (row, n): carry[0] = h0 (or 0),
 // carry[s+1] = 2^(A[row % dim, n] * seg_lsum[s]) carry[s] + seg_state[s].
@@ -114,10 +114,12 @@ struct BwdTensors {
     const float* h0;
     const float* dlast;
     float* dh0;
+    const float* ckpt;  // checkpoints from the forward (null: recomputed)
 };
 // segments > 1: the sequence is cut into segments of seg_len tokens (a
 // multiple of kChunk, every segment non-empty), swept in parallel.
-size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int32_t segments);
+size_t bwd_workspace_bytes(int64_t batch, int64_t L, int64_t dim, int32_t segments,
+                           bool ckpt_given);
 hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, DType dtype,
                       int32_t segments, int64_t seg_len, void* workspace, hipStream_t stream);
 

@@ -36,12 +36,12 @@ class Dims(ctypes.Structure):
 class FwdOpts(ctypes.Structure):
     _fields_ = [("h0", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_uint64), ("segments", ctypes.c_int32),
-                ("groups", ctypes.c_int32)]
+                ("groups", ctypes.c_int32), ("ckpt", ctypes.c_void_p)]
 
 
 class BwdOpts(ctypes.Structure):
     _fields_ = [("h0", ctypes.c_void_p), ("dlast_state", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
-                ("segments", ctypes.c_int32)]
+                ("segments", ctypes.c_int32), ("ckpt", ctypes.c_void_p)]
 
 
 class SsdDims(ctypes.Structure):
@@ -155,13 +155,22 @@ def timing_stop() -> Tuple[float, int]:
     return float(ms.value), int(n.value)
 
 
+def ckpt_shape(batch: int, dim: int, L: int, N: int = 16) -> Tuple[int, int, int, int]:
+    """Shape of the forward's checkpoints: the state before every 16th token."""
+    return ((L + 15) // 16, batch, dim, N)
+
+
 def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
         dt_bias: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
         last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
         h0: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-        segments: int = 0, groups: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        segments: int = 0, groups: int = 0,
+        ckpt: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective-scan forward (selscan_fwd_ex). Returns (y, last_state).
+
+    ``ckpt`` (shape ``ckpt_shape(batch, dim, L)``, fp32) receives the state
+    entering every 16th token, for ``bwd(..., ckpt=ckpt)``.
 
     ``y`` and ``last_state`` may be passed in preallocated; otherwise they are
     allocated here. ``h0`` [batch, dim, N] fp32 is the state entering token 0
@@ -192,8 +201,9 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _req(last_state, "last_state", torch.float32, (batch, dim, N), dev)
     _req(h0, "h0", torch.float32, (batch, dim, N), dev)
+    _req(ckpt, "ckpt", torch.float32, ckpt_shape(batch, dim, L, N), dev)
     dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
-    opts = FwdOpts(None, None, 0, int(segments), int(groups))
+    opts = FwdOpts(None, None, 0, int(segments), int(groups), _ptr(ckpt))
     need = ctypes.c_uint64(0)
     _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value > 0:
@@ -247,13 +257,14 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
         dt_bias: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
         want_dD: bool = True, want_ddt_bias: bool = True, segments: int = 0,
         h0: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
-        want_dh0: bool = False) -> dict:
+        want_dh0: bool = False, ckpt: Optional[torch.Tensor] = None) -> dict:
     """Backward pass (selscan_bwd): gradients for the output gradient ``dy``.
 
     Returns a dict with dx, ddelta, dB, dC (input dtype), dA [dim, N] fp32, and
     dz (when z is given), dD and ddt_bias ([dim] fp32, when wanted).
     ``h0`` (the forward's initial state), ``dlast_state`` (the gradient into
-    its final state), ``want_dh0`` (adds dh0 [batch, dim, N] fp32) and
+    its final state), ``want_dh0`` (adds dh0 [batch, dim, N] fp32), ``ckpt``
+    (the checkpoints a ``fwd(..., ckpt=...)`` over the same inputs wrote) and
     ``segments`` other than 0 (automatic) call selscan_bwd_ex.
     """
     if x.dim() != 3:
@@ -269,7 +280,8 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
                                (C, "C", x.dtype, (batch, N, L)), (D, "D", torch.float32, (dim,)),
                                (dt_bias, "dt_bias", torch.float32, (dim,)),
                                (h0, "h0", torch.float32, (batch, dim, N)),
-                               (dlast_state, "dlast_state", torch.float32, (batch, dim, N))):
+                               (dlast_state, "dlast_state", torch.float32, (batch, dim, N)),
+                               (ckpt, "ckpt", torch.float32, ckpt_shape(batch, dim, L, N))):
         _req(t, name, dt, shape, dev)
     out = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dB": torch.empty_like(B),
            "dC": torch.empty_like(C), "dA": torch.empty_like(A)}
@@ -286,10 +298,10 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
             _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
             _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out.get("ddt_bias")),
             ctypes.byref(dims))
-    if segments == 0 and h0 is None and dlast_state is None and not want_dh0:
+    if segments == 0 and h0 is None and dlast_state is None and not want_dh0 and ckpt is None:
         _check(lib.selscan_bwd(*args, _stream(dev)))
     else:
-        opts = BwdOpts(_ptr(h0), _ptr(dlast_state), _ptr(out.get("dh0")), segments)
+        opts = BwdOpts(_ptr(h0), _ptr(dlast_state), _ptr(out.get("dh0")), segments, _ptr(ckpt))
         _check(lib.selscan_bwd_ex(*args, ctypes.byref(opts), _stream(dev)))
     return out
 

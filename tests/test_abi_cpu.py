@@ -56,9 +56,9 @@ def P(i):
     return ctypes.c_void_p(BASE + i * SPAN)
 
 
-def fwd_call(dims, ptrs=None, segments=0, groups=0, h0=None, ws=None, ws_bytes=0):
+def fwd_call(dims, ptrs=None, segments=0, groups=0, h0=None, ws=None, ws_bytes=0, ckpt=None):
     p = [P(i) for i in range(10)] if ptrs is None else ptrs
-    opts = S.FwdOpts(h0, ws, ws_bytes, segments, groups)
+    opts = S.FwdOpts(h0, ws, ws_bytes, segments, groups, ckpt)
     return S.lib.selscan_fwd_ex(*p, ctypes.byref(dims) if dims is not None else None,
                                 ctypes.byref(opts), None)
 
@@ -145,6 +145,18 @@ def test_fwd_h0_checks():
     # h0 == last_state is allowed: the call then gets as far as the workspace check
     assert fwd_call(D(), h0=P(9), ws=P(13), ws_bytes=16) == S.ERR_CONFIG
     assert fwd_call(D(), h0=h0, ws=P(13), ws_bytes=16) == S.ERR_CONFIG
+
+
+def test_fwd_checkpoint_option_checks():
+    ck = BASE + 20 * SPAN
+    assert fwd_call(D(), ckpt=ck + 4) == S.ERR_ALIGN
+    assert fwd_call(D(), ckpt=P(8).value) == S.ERR_ALIAS      # ckpt == y
+    assert fwd_call(D(), ckpt=P(0).value) == S.ERR_ALIAS      # ckpt == x
+    assert fwd_call(D(), h0=ck, ckpt=ck) == S.ERR_ALIAS       # ckpt == h0
+    for g in (1, 2):                                          # only 4 waves store them
+        assert fwd_call(D(), groups=g, ckpt=ck) == S.ERR_CONFIG
+    # valid otherwise: the call gets as far as the workspace check
+    assert fwd_call(D(), groups=4, ckpt=ck, ws=P(13), ws_bytes=16) == S.ERR_CONFIG
 
 
 def workspace_size(dims, segments=0, groups=0):
@@ -311,6 +323,10 @@ def test_bwd_ex_option_checks():
     o = S.BwdOpts(h0=BASE + 17 * SPAN, dh0=BASE + 17 * SPAN)                            # dh0 == h0
     assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
     o = S.BwdOpts(dh0=BASE + 9 * SPAN)                                                 # dh0 == dx
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
+    o = S.BwdOpts(ckpt=BASE + 20 * SPAN + 8)
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIGN
+    o = S.BwdOpts(ckpt=BASE + 10 * SPAN)                                               # ckpt == ddelta
     assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
     o = S.BwdOpts(segments=4)
     assert S.lib.selscan_bwd_ex(*p, None, ctypes.byref(o), None) == S.ERR_NULL
