@@ -79,7 +79,7 @@ class Oracle:
         lib.ssm_ref_bwd.restype = ctypes.c_int
         lib.ssm_ref_bwd.argtypes = [_dp] * 11 + [ctypes.c_int64] * 4 + [_dp] * 18 + [ctypes.c_int]
         lib.ssm_ref_ssd.restype = ctypes.c_int
-        lib.ssm_ref_ssd.argtypes = [_dp] * 7 + [ctypes.c_int64] * 5 + [_dp] * 4 + [ctypes.c_int]
+        lib.ssm_ref_ssd.argtypes = [_dp] * 8 + [ctypes.c_int64] * 5 + [_dp] * 4 + [ctypes.c_int]
         lib.ssm_ref_conv1d.restype = ctypes.c_int
         lib.ssm_ref_conv1d.argtypes = [_dp] * 4 + [ctypes.c_int64] * 4 + [_dp] * 3
         lib.ssm_ref_conv1d_step.restype = ctypes.c_int
@@ -133,29 +133,43 @@ class Oracle:
             raise RuntimeError(f"ssm_ref_bwd failed with code {rc}")
         return out
 
-    def ssd(self, x, delta, A, B, C, D=None, dt_bias=None, nthreads: Optional[int] = None):
-        """Mamba-2's SSD layer (scalar decay per head), from a zero state.
+    def ssd(self, x, delta, A, B, C, D=None, dt_bias=None, h0=None,
+            nthreads: Optional[int] = None):
+        """Mamba-2's SSD layer (scalar decay per head), from the state ``h0``
+        (``[batch, heads, dstate, headdim]``; zeros when None).
 
         ``x``: ``[batch, seqlen, heads, headdim]``; ``delta`` (raw):
         ``[batch, seqlen, heads]``; ``A, D, dt_bias``: ``[heads]``; ``B, C``:
         ``[batch, seqlen, dstate]``. Returns ``y``, ``y_scale`` (like x) and
         ``last_state``, ``state_scale`` (``[batch, heads, dstate, headdim]``).
         """
-        x, delta, A, B, C, D, dt_bias = map(_f64, (x, delta, A, B, C, D, dt_bias))
+        x, delta, A, B, C, D, dt_bias, h0 = map(_f64, (x, delta, A, B, C, D, dt_bias, h0))
         batch, L, H, P = x.shape
         N = B.shape[2]
         assert delta.shape == (batch, L, H) and A.shape == (H,)
         assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        assert h0 is None or h0.shape == (batch, H, N, P)
         y = np.empty_like(x)
         ys = np.empty_like(x)
         hs = np.empty((batch, H, N, P), np.float64)
         hss = np.empty((batch, H, N, P), np.float64)
         rc = self.lib.ssm_ref_ssd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                  _ptr(dt_bias), batch, L, H, P, N, _ptr(y), _ptr(ys), _ptr(hs),
+                                  _ptr(dt_bias), _ptr(h0), batch, L, H, P, N, _ptr(y), _ptr(ys), _ptr(hs),
                                   _ptr(hss), nthreads or default_threads())
         if rc != 0:
             raise RuntimeError(f"ssm_ref_ssd failed with code {rc}")
         return {"y": y, "y_scale": ys, "last_state": hs, "state_scale": hss}
+
+    def ssd_step(self, state, x, delta, A, B, C, D=None, dt_bias=None):
+        """One decode step of the SSD layer: the layer over a single token
+        from ``state`` ``[batch, heads, dstate, headdim]``. ``x``: ``[batch,
+        heads, headdim]``; ``delta`` (raw): ``[batch, heads]``; ``B, C``:
+        ``[batch, dstate]``. Returns ``y`` ``[batch, heads, headdim]``,
+        ``y_scale``, ``state`` (the new state) and ``state_scale``."""
+        x, delta, B, C = (np.asarray(v, np.float64) for v in (x, delta, B, C))
+        r = self.ssd(x[:, None], delta[:, None], A, B[:, None], C[:, None], D, dt_bias, h0=state)
+        return {"y": r["y"][:, 0], "y_scale": r["y_scale"][:, 0], "state": r["last_state"],
+                "state_scale": r["state_scale"]}
 
     def conv1d(self, x, w, bias=None, x_prev=None):
         """Causal depthwise convolution of width K = w.shape[1], then SiLU.
@@ -302,6 +316,10 @@ def bwd(*args, **kw):
 def ssd(*args, **kw):
     """Mamba-2 SSD layer through the built oracle; see ``Oracle.ssd``."""
     return default().ssd(*args, **kw)
+
+
+def ssd_step(*args, **kw):
+    return default().ssd_step(*args, **kw)
 
 
 def conv1d(*args, **kw):

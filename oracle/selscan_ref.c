@@ -584,7 +584,7 @@ int ssm_ref_bwd(const double *x, const double *delta, const double *A, const dou
  * map is such a matrix: A_t = exp(delta_t A_h) times the identity, one
  * scalar per (token, head); the P channels of a head share delta_t, and B_t,
  * C_t (N entries) are shared by all heads. Per batch entry b and head h, from
- * a zero state S (N x P):
+ * the state S = h0[b,h] (N x P; zero when h0 is null):
  *
  *   delta_t = softplus(delta_raw[b,t,h] + dt_bias[h])
  *   S[n,p]  = exp(delta_t A_h) S[n,p] + delta_t B[b,t,n] x[b,t,h,p]
@@ -598,11 +598,11 @@ int ssm_ref_bwd(const double *x, const double *delta, const double *A, const dou
  *
  * Layouts: x, y: [batch, seqlen, heads, headdim]; delta_raw: [batch, seqlen,
  * heads]; A, D, dt_bias: [heads]; B, C: [batch, seqlen, dstate];
- * last_state: [batch, heads, dstate, headdim]. (b, h) pairs are split over
- * threads.
+ * last_state, h0: [batch, heads, dstate, headdim]. (b, h) pairs are split
+ * over threads. One token from a given state is the layer's decode step.
  */
 typedef struct {
-    const double *x, *delta, *A, *B, *C, *D, *dt_bias;
+    const double *x, *delta, *A, *B, *C, *D, *dt_bias, *h0;
     int64_t batch, L, H, P, N;
     double *y, *ys, *hs, *hss;
     int64_t i0, i1;
@@ -616,7 +616,10 @@ static void ssd_pairs(const ssd_job *j)
     double *Sa = S + N * P;
     for (int64_t i = j->i0; i < j->i1; ++i) {
         const int64_t b = i / H, h = i % H;
-        for (int64_t k = 0; k < N * P; ++k) S[k] = Sa[k] = 0.0;
+        for (int64_t k = 0; k < N * P; ++k) {
+            S[k] = j->h0 ? j->h0[i * N * P + k] : 0.0;
+            Sa[k] = fabs(S[k]);
+        }
         const double Ah = j->A[h], Dh = j->D ? j->D[h] : 0.0, bias = j->dt_bias ? j->dt_bias[h] : 0.0;
         for (int64_t t = 0; t < L; ++t) {
             const double dl = softplus(j->delta[(b * L + t) * H + h] + bias);
@@ -656,7 +659,7 @@ static void *ssd_thread(void *p)
 }
 
 int ssm_ref_ssd(const double *x, const double *delta, const double *A, const double *B,
-                const double *C, const double *D, const double *dt_bias,
+                const double *C, const double *D, const double *dt_bias, const double *h0,
                 int64_t batch, int64_t seqlen, int64_t heads, int64_t headdim, int64_t dstate,
                 double *y, double *y_scale, double *last_state, double *state_scale, int nthreads)
 {
@@ -665,7 +668,7 @@ int ssm_ref_ssd(const double *x, const double *delta, const double *A, const dou
     const int64_t pairs = batch * heads;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > pairs) nthreads = pairs > 0 ? (int)pairs : 1;
-    ssd_job base = {x, delta, A, B, C, D, dt_bias, batch, seqlen, heads, headdim, dstate,
+    ssd_job base = {x, delta, A, B, C, D, dt_bias, h0, batch, seqlen, heads, headdim, dstate,
                     y, y_scale, last_state, state_scale, 0, 0};
     ssd_job *jobs = calloc((size_t)nthreads, sizeof(ssd_job));
     pthread_t *tid = calloc((size_t)nthreads, sizeof(pthread_t));

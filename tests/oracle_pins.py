@@ -696,6 +696,34 @@ def pin_ssd_equals_restricted_selective_scan(O):
            what="ssd vs S6 scale")
 
 
+def pin_ssd_initial_state_and_step(O):
+    """From an initial state: SSD equals the (separately pinned) selective scan
+    started from the same state laid out per channel (d = h*P + p, state
+    [d, n]); and one decode step is the layer over one token from the state,
+    so L steps give the L-token call."""
+    p = _ssd_problem(53, 2, 19, 3, 4, 5)
+    batch, L, H, P = p["x"].shape
+    N = p["B"].shape[2]
+    h0 = np.random.default_rng(54).standard_normal((batch, H, N, P))
+    r = O.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"], h0=h0)
+    x = p["x"].transpose(0, 2, 3, 1).reshape(batch, H * P, L)
+    delta = np.repeat(p["delta"].transpose(0, 2, 1), P, axis=1)
+    A = np.repeat(p["A"], P)[:, None] * np.ones((1, N))
+    s6 = O.fwd(x, delta, A, p["B"].transpose(0, 2, 1), p["C"].transpose(0, 2, 1),
+               D=np.repeat(p["D"], P), dt_bias=np.repeat(p["dt_bias"], P),
+               h0=h0.transpose(0, 1, 3, 2).reshape(batch, H * P, N))
+    _close(r["y"], s6["y"].reshape(batch, H, P, L).transpose(0, 3, 1, 2), 1e-12, what="ssd h0 vs S6 y")
+    _close(r["last_state"], s6["last_state"].reshape(batch, H, P, N).transpose(0, 1, 3, 2), 1e-12,
+           what="ssd h0 vs S6 state")
+    st = h0
+    for t in range(L):
+        o = O.ssd_step(st, p["x"][:, t], p["delta"][:, t], p["A"], p["B"][:, t], p["C"][:, t],
+                       p["D"], p["dt_bias"])
+        _close(o["y"], r["y"][:, t], 1e-12, what=f"ssd step {t} y")
+        st = o["state"]
+    _close(st, r["last_state"], 1e-12, what="ssd steps final state")
+
+
 def pin_ssd_dual_quadratic_form(O):
     """The attention-like dual: y = (Lmask o C B^T)(delta x) + D x with
     Lmask[t,s] = exp(A_h sum_{s<k<=t} delta_k) (s <= t), by numpy matrix

@@ -74,6 +74,7 @@ MUTANTS = [
     ("bwd_dt_bias_no_sigmoid", "dT += ddl * sg;", "dT += ddl;"),
     ("ssd_decay_no_delta", "const double a = exp(dl * Ah);", "const double a = exp(Ah);"),
     ("ssd_input_no_delta", "const double in = dl * Bt[n] * xt[p];", "const double in = Bt[n] * xt[p];"),
+    ("ssd_h0_ignored", "S[k] = j->h0 ? j->h0[i * N * P + k] : 0.0;", "S[k] = 0.0;"),
     ("ssd_readout_B", "acc += Ct[n] * S[n * P + p];", "acc += Bt[n] * S[n * P + p];"),
     ("ssd_no_D", "yt[p] = acc + Dh * xt[p];", "yt[p] = acc;"),
     ("ssd_head_index", "const double dl = softplus(j->delta[(b * L + t) * H + h] + bias);",
