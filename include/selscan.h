@@ -317,6 +317,40 @@ int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void
                     const selscan_ssd_dims_t* dims, void* stream);
 
 /*
+ * selscan_ssd_fwd_ex — selscan_ssd_fwd from a given state: S starts as
+ * h0[b,h] ([B, H, N, P] fp32; NULL means zeros) instead of zero. A state is
+ * all the layer keeps between tokens ("State Space Models and Mamba"
+ * (multigrid.ai), section "The state, in bytes, against a KV cache"), so a
+ * sequence run in two pieces, the second from the first's last_state, gives
+ * the unsplit result up to rounding (the state enters the first chunk's
+ * products as bf16, like the carried state between chunks). h0 may be
+ * last_state itself, but must not overlap y. With L = 0, last_state = h0.
+ */
+int selscan_ssd_fwd_ex(const void* x, const void* delta, const float* A, const void* B,
+                       const void* C, const float* D, const float* dt_bias, const float* h0,
+                       void* y, float* last_state, const selscan_ssd_dims_t* dims, void* stream);
+
+/*
+ * selscan_ssd_step — one decode step of the SSD layer, the state updated in
+ * place: the recurrence of selscan_ssd_fwd for a single token ("State Space
+ * Models and Mamba" (multigrid.ai), section "Why a linear recurrence can be
+ * trained in parallel": at inference the layer runs the recurrence one token
+ * at a time on a fixed-size state). Per (b, h):
+ *   delta = softplus(delta[b,h] + dt_bias[h])
+ *   state[b,h] = exp(delta A[h]) state[b,h] + delta B[b,:]^T x[b,h,:]
+ *   y[b,h,:] = C[b,:] state[b,h] + D[h] x[b,h,:]
+ * Arguments (device pointers): state [B, H, N, P] fp32 (read and written);
+ * x, y [B, H, P] bf16; delta [B, H] bf16; B, C [B, N] bf16; A [H] fp32; D,
+ * dt_bias [H] fp32 or NULL. dims->seqlen is ignored; P 64, N 64 or 128, bf16.
+ * Fully fp32 arithmetic (no matrix-core rounding). y and state must not
+ * overlap any input or each other. Running L steps equals selscan_ssd_fwd_ex
+ * over the L tokens up to that call's bf16 operand rounding.
+ */
+int selscan_ssd_step(float* state, const void* x, const void* delta, const float* A, const void* B,
+                     const void* C, const float* D, const float* dt_bias, void* y,
+                     const selscan_ssd_dims_t* dims, void* stream);
+
+/*
  * selscan_conv1d — the short causal convolution in front of the scan: a
  * depthwise conv1d of width SELSCAN_CONV_WIDTH (4), then SiLU.
  *

@@ -425,6 +425,12 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
 int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                     const float* D, const float* dt_bias, void* y, float* last_state,
                     const selscan_ssd_dims_t* dims, void* stream) {
+    return selscan_ssd_fwd_ex(x, delta, A, B, C, D, dt_bias, nullptr, y, last_state, dims, stream);
+}
+
+int selscan_ssd_fwd_ex(const void* x, const void* delta, const float* A, const void* B,
+                       const void* C, const float* D, const float* dt_bias, const float* h0,
+                       void* y, float* last_state, const selscan_ssd_dims_t* dims, void* stream) {
     if (!dims) return SELSCAN_ERR_NULL;
     if (dims->batch < 0 || dims->seqlen < 0 || dims->heads < 0 || dims->headdim < 0 || dims->dstate < 0)
         return SELSCAN_ERR_DIMS;
@@ -444,9 +450,14 @@ int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void
         (dims->heads > 0 && !A))
         return SELSCAN_ERR_NULL;
     for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, (const void*)dt_bias, (const void*)y,
-                          (const void*)last_state})
+                          (const void*)last_state, (const void*)h0})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     const Span oy = span(y, seq * 2), os = span(last_state, st * 4);
+    // h0 may be last_state itself (each (b, h) reads it before writing it)
+    const Span ih = span(h0, st * 4);
+    if (overlaps(ih, oy)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(ih, os) && static_cast<const void*>(h0) != static_cast<const void*>(last_state))
+        return SELSCAN_ERR_ALIAS;
     const Span ins[] = {span(x, seq * 2), span(delta, bl * dims->heads * 2), span(A, dims->heads * 4),
                         span(B, nbc * 2), span(C, nbc * 2), span(D, dims->heads * 4),
                         span(dt_bias, dims->heads * 4)};
@@ -456,11 +467,43 @@ int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void
     hipStream_t stm = static_cast<hipStream_t>(stream);
     if (bh == 0) return SELSCAN_OK;
     if (dims->seqlen == 0) {
-        if (last_state && launch_fill_zero(last_state, st, stm) != hipSuccess) return SELSCAN_ERR_LAUNCH;
-        return SELSCAN_OK;
+        if (!last_state) return SELSCAN_OK;
+        const hipError_t e = h0 ? launch_copy_f32(last_state, h0, st, stm) : launch_fill_zero(last_state, st, stm);
+        return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
     }
-    SsdTensors tt{x, delta, A, B, C, D, dt_bias, y, last_state};
+    SsdTensors tt{x, delta, A, B, C, D, dt_bias, y, last_state, h0};
     const hipError_t e = launch_ssd(tt, dims->batch, dims->seqlen, dims->heads, dims->dstate, stm);
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+int selscan_ssd_step(float* state, const void* x, const void* delta, const float* A, const void* B,
+                     const void* C, const float* D, const float* dt_bias, void* y,
+                     const selscan_ssd_dims_t* dims, void* stream) {
+    if (!dims) return SELSCAN_ERR_NULL;
+    if (dims->batch < 0 || dims->heads < 0 || dims->headdim < 0 || dims->dstate < 0)
+        return SELSCAN_ERR_DIMS;
+    if (dims->dtype != SELSCAN_BF16) return SELSCAN_ERR_DTYPE;
+    if (dims->headdim != 64 || (dims->dstate != 64 && dims->dstate != 128)) return SELSCAN_ERR_DSTATE;
+    int64_t bh, xe, st, t, bn;
+    if (!mul_ok(dims->batch, dims->heads, &bh) || !mul_ok(bh, 64, &xe) ||
+        !mul_ok(xe, dims->dstate, &st) || !mul_ok(st, 4, &t) || !mul_ok(dims->batch, dims->dstate, &bn) ||
+        bh > INT32_MAX)
+        return SELSCAN_ERR_DIMS;
+    if (bh > 0 && (!state || !x || !delta || !A || !y)) return SELSCAN_ERR_NULL;
+    if (bn > 0 && (!B || !C)) return SELSCAN_ERR_NULL;
+    for (const void* p : {(const void*)state, x, delta, (const void*)A, B, C, (const void*)D,
+                          (const void*)dt_bias, (const void*)y})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const Span os = span(state, st * 4), oy = span(y, xe * 2);
+    const Span ins[] = {span(x, xe * 2), span(delta, bh * 2), span(A, dims->heads * 4), span(B, bn * 2),
+                        span(C, bn * 2), span(D, dims->heads * 4), span(dt_bias, dims->heads * 4)};
+    for (const Span& s : ins)
+        if (overlaps(s, oy) || overlaps(s, os)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(oy, os)) return SELSCAN_ERR_ALIAS;
+    if (bh == 0) return SELSCAN_OK;
+    SsdStepTensors tt{state, x, delta, A, B, C, D, dt_bias, y};
+    const hipError_t e = launch_ssd_step(tt, dims->batch, dims->heads, dims->dstate,
+                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 

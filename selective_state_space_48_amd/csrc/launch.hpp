@@ -124,8 +124,9 @@ hipError_t launch_bwd(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim
                       int32_t segments, int64_t seg_len, void* workspace, hipStream_t stream);
 
 // Mamba-2 SSD layer (bf16). x/y: [batch, L, heads, 64]; delta: [batch, L, heads];
-// A, D, dt_bias: [heads] fp32; B, C: [batch, L, dstate]; last_state:
-// [batch, heads, dstate, 64] fp32 or null. dstate 64 or 128.
+// A, D, dt_bias: [heads] fp32; B, C: [batch, L, dstate]; last_state and h0
+// (the state entering token 0): [batch, heads, dstate, 64] fp32 or null.
+// dstate 64 or 128.
 struct SsdTensors {
     const void* x;
     const void* delta;
@@ -136,9 +137,27 @@ struct SsdTensors {
     const float* dt_bias;
     void* y;
     float* last_state;
+    const float* h0;
 };
 hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t heads, int64_t dstate,
                       hipStream_t stream);
+
+// One decode step of the SSD layer: state [batch, heads, dstate, 64] fp32 in
+// place; x/y: [batch, heads, 64], delta: [batch, heads], B/C: [batch, dstate]
+// (bf16); A, D, dt_bias: [heads] fp32 (D, dt_bias may be null).
+struct SsdStepTensors {
+    float* state;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* dt_bias;
+    void* y;
+};
+hipError_t launch_ssd_step(const SsdStepTensors& t, int64_t batch, int64_t heads, int64_t dstate,
+                           hipStream_t stream);
 
 // Causal depthwise conv (width 4) + SiLU. x/out: [rows, L]; w: [dim, 4];
 // bias: [dim] or null; x_prev/x_last: [rows, 3] fp32 or null.

@@ -38,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = 64;   // tokens per chunk
 constexpr int kP = 64;   // headdim
@@ -92,6 +93,7 @@ struct SsdArgs {
     const float* dt_bias;   // [H] or null
     bf16_bits* y;           // [batch, L, H, P]
     float* last_state;      // [batch, H, N, P] or null
+    const float* h0;        // [batch, H, N, P] state entering token 0, or null (zeros)
     int64_t batch, L, H;
 };
 
@@ -151,11 +153,25 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     };
 
     // State tiles (fp32 accumulators): H^T rows p = 32 pb + acc_row, columns
-    // n = 32 (tb NTW + j) + lane % 32.
+    // n = 32 (tb NTW + j) + lane % 32; from h0 (with its bf16 copy for the
+    // first chunk's C H), or zero. Both cover every element a product reads.
     f32x16 H[NTW];
+    if (a.h0) {
+        const float* src = a.h0 + (b * a.H + h) * int64_t(N) * kP;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
-    for (int i = tid; i < kP * NR; i += 256) Ht[i] = 0;
+        for (int j = 0; j < NTW; ++j) {
+            const int n = (tb * NTW + j) * 32 + lane % 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                H[j][r] = src[int64_t(n) * kP + pb * 32 + acc_row(r, lane)];
+                Ht[(pb * 32 + acc_row(r, lane)) * NR + n] = tobf(H[j][r]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
+        for (int i = tid; i < kP * NR; i += 256) Ht[i] = 0;
+    }
 
     // The output of a chunk is stored in the next iteration, once that
     // iteration's prefetched inputs have been consumed and before the next
@@ -332,7 +348,83 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     }
 }
 
+struct SsdStepArgs {
+    float* state;           // [batch, H, N, P], updated in place
+    const bf16_bits* x;     // [batch, H, P]
+    const bf16_bits* delta; // [batch, H]
+    const float* A;         // [H]
+    const bf16_bits* B;     // [batch, N]
+    const bf16_bits* C;     // [batch, N]
+    const float* D;         // [H] or null
+    const float* dt_bias;   // [H] or null
+    bf16_bits* y;           // [batch, H, P]
+    int64_t H;
+};
+
+// One decode step of the layer: per (batch entry, head) the N x P state is
+// read and written once (the step is bound by that traffic). Thread (nq, p4)
+// takes the 4 channels 4 p4.. and the state rows n = nq + 16 k, so a wave
+// moves four whole 256-byte rows per access; the readout's partial sums over
+// n meet in LDS and are added in order.
+template <int N>
+__global__ __launch_bounds__(256) void ssd_step_kernel(SsdStepArgs a) {
+    constexpr int K = N / 16;
+    __shared__ float red[16][kP];
+    const int tid = threadIdx.x, p4 = tid % 16, nq = tid / 16;
+    const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+    const float l = softplus_log2(to_f32(a.delta[bh]) + (a.dt_bias ? a.dt_bias[h] : 0.0f));
+    const float decay = exp2_hw(l * a.A[h]);  // exp(delta A), delta = l ln 2
+    const float dl = l * kLn2;
+    const uint2 xr = *reinterpret_cast<const uint2*>(a.x + bh * kP + 4 * p4);
+    const float xs[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
+    float* S = a.state + bh * int64_t(N) * kP + 4 * p4;
+    f32x4v s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        s[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(S + (nq + 16 * k) * kP));
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int n = nq + 16 * k;
+        const float u = dl * to_f32(a.B[b * N + n]), c = to_f32(a.C[b * N + n]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[k][i] = fmaf(decay, s[k][i], u * xs[i]);
+            acc[i] = fmaf(c, s[k][i], acc[i]);
+        }
+        __builtin_nontemporal_store(s[k], reinterpret_cast<f32x4v*>(S + n * kP));
+    }
+    *reinterpret_cast<float4*>(&red[nq][4 * p4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (tid < kP) {
+        float y = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) y += red[q][tid];
+        const float Dh = a.D ? a.D[h] : 0.0f;
+        a.y[bh * kP + tid] = tobf(fmaf(Dh, to_f32(a.x[bh * kP + tid]), y));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ssd_step(const SsdStepTensors& t, int64_t batch, int64_t heads, int64_t dstate,
+                           hipStream_t stream) {
+    SsdStepArgs k{};
+    k.state = t.state;
+    k.x = static_cast<const bf16_bits*>(t.x);
+    k.delta = static_cast<const bf16_bits*>(t.delta);
+    k.A = t.A;
+    k.B = static_cast<const bf16_bits*>(t.B);
+    k.C = static_cast<const bf16_bits*>(t.C);
+    k.D = t.D;
+    k.dt_bias = t.dt_bias;
+    k.y = static_cast<bf16_bits*>(t.y);
+    k.H = heads;
+    const dim3 grid(unsigned(batch * heads)), block(256);
+    if (dstate == 64) hipLaunchKernelGGL((ssd_step_kernel<64>), grid, block, 0, stream, k);
+    else hipLaunchKernelGGL((ssd_step_kernel<128>), grid, block, 0, stream, k);
+    return hipGetLastError();
+}
 
 hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t heads, int64_t dstate,
                       hipStream_t stream) {
@@ -346,6 +438,7 @@ hipError_t launch_ssd(const SsdTensors& t, int64_t batch, int64_t L, int64_t hea
     k.dt_bias = t.dt_bias;
     k.y = static_cast<bf16_bits*>(t.y);
     k.last_state = t.last_state;
+    k.h0 = t.h0;
     k.batch = batch; k.L = L; k.H = heads;
     const dim3 grid(unsigned(batch * heads)), block(256);
     if (dstate == 64) hipLaunchKernelGGL((ssd_fused<64>), grid, block, 0, stream, k);

@@ -83,6 +83,10 @@ def _load() -> ctypes.CDLL:
     lib.selscan_bwd_ex.restype = ctypes.c_int
     lib.selscan_ssd_fwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, ctypes.POINTER(SsdDims), vp]
     lib.selscan_ssd_fwd.restype = ctypes.c_int
+    lib.selscan_ssd_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, fp, fp, vp, fp, ctypes.POINTER(SsdDims), vp]
+    lib.selscan_ssd_fwd_ex.restype = ctypes.c_int
+    lib.selscan_ssd_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, fp, vp, ctypes.POINTER(SsdDims), vp]
+    lib.selscan_ssd_step.restype = ctypes.c_int
     lib.selscan_conv1d.argtypes = [vp, fp, fp, fp, vp, fp, dims_p, vp]
     lib.selscan_conv1d.restype = ctypes.c_int
     lib.selscan_conv1d_step.argtypes = [fp, vp, fp, fp, vp, dims_p, vp]
@@ -309,13 +313,14 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
 def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             C: torch.Tensor, D: Optional[torch.Tensor] = None,
             dt_bias: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
-            last_state: Optional[torch.Tensor] = None,
-            return_last_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
+            h0: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Mamba-2 SSD layer (selscan_ssd_fwd), bfloat16. Returns (y, last_state).
 
     ``x`` [batch, L, heads, 64]; ``delta`` [batch, L, heads] (before softplus);
     ``A``, ``D``, ``dt_bias`` [heads] fp32; ``B``, ``C`` [batch, L, dstate];
-    last_state [batch, heads, dstate, 64] fp32.
+    last_state [batch, heads, dstate, 64] fp32. ``h0`` (same shape) is the
+    state entering token 0 (selscan_ssd_fwd_ex; None: zeros).
     """
     if x.dim() != 4:
         raise ValueError("x must be [batch, L, heads, headdim]")
@@ -336,11 +341,47 @@ def ssd_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tens
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, H, N, P), dtype=torch.float32, device=dev)
     _req(last_state, "last_state", torch.float32, (batch, H, N, P), dev)
+    _req(h0, "h0", torch.float32, (batch, H, N, P), dev)
     dims = SsdDims(batch, L, H, P, N, BF16)
-    _check(lib.selscan_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                               _ptr(dt_bias), _ptr(y), _ptr(last_state), ctypes.byref(dims),
-                               _stream(dev)))
+    if h0 is None:
+        _check(lib.selscan_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(dt_bias), _ptr(y), _ptr(last_state), ctypes.byref(dims),
+                                   _stream(dev)))
+    else:
+        _check(lib.selscan_ssd_fwd_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(last_state),
+                                      ctypes.byref(dims), _stream(dev)))
     return y, last_state
+
+
+def ssd_step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+             B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+             dt_bias: Optional[torch.Tensor] = None, *,
+             y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of the SSD layer (selscan_ssd_step): updates ``state``
+    [batch, heads, dstate, 64] fp32 in place and returns y [batch, heads, 64].
+    ``x`` [batch, heads, 64], ``delta`` [batch, heads], ``B``, ``C`` [batch,
+    dstate] bf16; ``A``, ``D``, ``dt_bias`` [heads] fp32."""
+    if state.dim() != 4:
+        raise ValueError("state must be [batch, heads, dstate, headdim]")
+    batch, H, N, P = state.shape
+    dev = state.device
+    bf = torch.bfloat16
+    _req(state, "state", torch.float32, (batch, H, N, P), dev)
+    _req(x, "x", bf, (batch, H, P), dev)
+    _req(delta, "delta", bf, (batch, H), dev)
+    _req(A, "A", torch.float32, (H,), dev)
+    _req(B, "B", bf, (batch, N), dev)
+    _req(C, "C", bf, (batch, N), dev)
+    _req(D, "D", torch.float32, (H,), dev)
+    _req(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, "y", bf, (batch, H, P), dev)
+    dims = SsdDims(batch, 1, H, P, N, BF16)
+    _check(lib.selscan_ssd_step(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(dt_bias), _ptr(y), ctypes.byref(dims), _stream(dev)))
+    return y
 
 
 CONV_WIDTH = 4

@@ -231,6 +231,9 @@ def conv_step_inputs(w: Workload, s: int) -> np.ndarray:
 # Mamba-2 SSD layer: a 1.3B-shaped layer (d_inner 4096 = 64 heads of 64
 # channels, state 128, one B/C group), bf16.
 SSD_HEADLINE = dict(batch=8, seqlen=2048, heads=64, headdim=64, dstate=128, seed=5)
+# Decode of a Mamba-2-2.7B-shaped layer (d_inner 5120: 80 heads of 64, state
+# 128), 256 sequences at once: an fp32 state of 671 MB read and written per step.
+SSD_DECODE = dict(batch=256, heads=80, headdim=64, dstate=128, seed=6)
 
 
 def ssd_inputs(batch: int, seqlen: int, heads: int, headdim: int, dstate: int, seed: int,

@@ -22,7 +22,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
-            "selscan_bwd", "selscan_bwd_ex", "selscan_ssd_fwd", "selscan_conv1d", "selscan_conv1d_step",
+            "selscan_bwd", "selscan_bwd_ex", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
             "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
@@ -365,3 +365,42 @@ def test_ssd_argument_checks():
     p[7] = p[0]                                # y == x
     assert ssd_call(SD(), p) == S.ERR_ALIAS
     assert ssd_call(SD(batch=0)) == S.OK
+
+
+def test_ssd_ex_initial_state_checks():
+    def call(h0, ls=P(8)):
+        p = [P(i) for i in range(7)] + [h0, P(7), ls]
+        return S.lib.selscan_ssd_fwd_ex(*p, ctypes.byref(SD()), None)
+    assert call(ctypes.c_void_p(BASE + 20 * SPAN + 4)) == S.ERR_ALIGN
+    assert call(P(7)) == S.ERR_ALIAS                  # h0 overlapping y
+    assert call(ctypes.c_void_p(BASE + 8 * SPAN + 64)) == S.ERR_ALIAS   # inside last_state, not equal
+    # h0 == last_state is allowed: with no (batch, head) pairs nothing is launched
+    p = [P(i) for i in range(7)] + [P(8), P(7), P(8)]
+    assert S.lib.selscan_ssd_fwd_ex(*p, ctypes.byref(SD(batch=0)), None) == S.OK
+
+
+def ssd_step_call(dims, ptrs=None):
+    p = [P(i) for i in range(9)] if ptrs is None else ptrs
+    return S.lib.selscan_ssd_step(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_ssd_step_argument_checks():
+    assert ssd_step_call(None) == S.ERR_NULL
+    assert ssd_step_call(SD(heads=-1)) == S.ERR_DIMS
+    assert ssd_step_call(SD(dtype=S.F32)) == S.ERR_DTYPE
+    assert ssd_step_call(SD(N=32)) == S.ERR_DSTATE
+    for idx in (0, 1, 2, 3, 4, 5, 8):          # state, x, delta, A, B, C, y are required
+        p = [P(i) for i in range(9)]
+        p[idx] = None
+        assert ssd_step_call(SD(), p) == S.ERR_NULL, idx
+    for idx in range(9):
+        p = [P(i) for i in range(9)]
+        p[idx] = ctypes.c_void_p(BASE + idx * SPAN + 2)
+        assert ssd_step_call(SD(), p) == S.ERR_ALIGN, idx
+    p = [P(i) for i in range(9)]
+    p[8] = p[1]                                # y == x
+    assert ssd_step_call(SD(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(9)]
+    p[0] = p[4]                                # state == B
+    assert ssd_step_call(SD(), p) == S.ERR_ALIAS
+    assert ssd_step_call(SD(batch=0)) == S.OK

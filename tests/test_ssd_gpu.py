@@ -93,3 +93,114 @@ def test_ssd_headline_shape():
     case("ssd full b8 L2048 H64 P64 N128")
     y, hs = _gpu(p)
     _check(y, hs, p, "headline shape")
+
+
+def _state(batch, H, N, seed, scale=0.5):
+    return (np.random.default_rng(seed).standard_normal((batch, H, N, 64)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("batch,L,heads,N", [(2, 65, 3, 128), (1, 130, 2, 64), (2, 7, 1, 128)])
+def test_ssd_from_initial_state(batch, L, heads, N):
+    """selscan_ssd_fwd_ex: the recurrence starts from h0."""
+    p = W.ssd_inputs(batch, L, heads, 64, N, seed=L + 100)
+    h0 = _state(batch, heads, N, L)
+    case(f"ssd from h0 b{batch} L{L} H{heads} N{N}")
+    y, hs = selscan.ssd_fwd(dev(p["x"], BF), dev(p["delta"], BF), dev(p["A"]), dev(p["B"], BF),
+                            dev(p["C"], BF), D=dev(p["D"]), dt_bias=dev(p["dt_bias"]), h0=dev(h0))
+    torch.cuda.synchronize()
+    r = oracle.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"], h0=h0)
+    ey = oracle.scaled_error(to_np(y), r["y"], r["y_scale"])
+    es = oracle.scaled_error(to_np(hs), r["last_state"], r["state_scale"])
+    print(f"[parity] ssd h0 b{batch} L{L} H{heads} N{N}: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_ssd_split_sequence_matches_unsplit():
+    """A sequence in two pieces, the second from the first's last state (in
+    place: h0 is last_state), against the unsplit oracle."""
+    batch, L, H, N, cut = 2, 300, 3, 128, 137
+    p = W.ssd_inputs(batch, L, H, 64, N, seed=77)
+    case(f"ssd split at {cut} of {L}")
+    part = lambda a, lo, hi: np.ascontiguousarray(a[:, lo:hi])
+    run = lambda lo, hi, **kw: selscan.ssd_fwd(
+        dev(part(p["x"], lo, hi), BF), dev(part(p["delta"], lo, hi), BF), dev(p["A"]),
+        dev(part(p["B"], lo, hi), BF), dev(part(p["C"], lo, hi), BF), D=dev(p["D"]),
+        dt_bias=dev(p["dt_bias"]), **kw)
+    y1, st = run(0, cut)
+    y2, st2 = run(cut, L, h0=st, last_state=st)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == st.data_ptr()
+    r = oracle.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"])
+    y = np.concatenate([to_np(y1), to_np(y2)], axis=1)
+    ey = oracle.scaled_error(y, r["y"], r["y_scale"])
+    es = oracle.scaled_error(to_np(st), r["last_state"], r["state_scale"])
+    print(f"[parity] ssd split: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_ssd_decode_steps(N):
+    """selscan_ssd_step: several tokens one at a time from a given state. Each
+    step against the oracle's step from the same state (the GPU's previous
+    one), and the chain against the oracle's layer over those tokens from the
+    first state (whose error scales carry the whole history)."""
+    batch, H, T = 3, 5, 6
+    p = W.ssd_inputs(batch, T, H, 64, N, seed=N + 7)
+    st0 = _state(batch, H, N, N)
+    st = dev(st0)
+    case(f"ssd decode N{N}: {T} steps")
+    worst_y = worst_s = 0.0
+    ys = []
+    for t in range(T):
+        xt, dt = np.ascontiguousarray(p["x"][:, t]), np.ascontiguousarray(p["delta"][:, t])
+        Bt, Ct = np.ascontiguousarray(p["B"][:, t]), np.ascontiguousarray(p["C"][:, t])
+        prev = to_np(st)
+        y = selscan.ssd_step(st, dev(xt, BF), dev(dt, BF), dev(p["A"]), dev(Bt, BF), dev(Ct, BF),
+                             D=dev(p["D"]), dt_bias=dev(p["dt_bias"]))
+        torch.cuda.synchronize()
+        r = oracle.ssd_step(prev, xt, dt, p["A"], Bt, Ct, p["D"], p["dt_bias"])
+        ys.append(to_np(y))
+        worst_y = max(worst_y, oracle.scaled_error(ys[-1], r["y"], r["y_scale"]))
+        worst_s = max(worst_s, oracle.scaled_error(to_np(st), r["state"], r["state_scale"]))
+    full = oracle.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"], h0=st0)
+    ey = oracle.scaled_error(np.stack(ys, 1), full["y"], full["y_scale"])
+    es = oracle.scaled_error(to_np(st), full["last_state"], full["state_scale"])
+    print(f"[parity] ssd decode N{N}: per step err_y={worst_y:.3e} err_state={worst_s:.3e}; "
+          f"chain err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    # y is bf16; the state is fp32 arithmetic throughout: held to the fp32 limit
+    assert worst_y <= TOL["bf16"] and ey <= TOL["bf16"]
+    assert worst_s <= TOL["f32"] and es <= TOL["f32"]
+
+
+def test_ssd_decode_continues_prefill():
+    """Prefill with selscan_ssd_fwd, then decode with selscan_ssd_step from its
+    last state: the decoded tokens match the oracle over the whole sequence."""
+    batch, L, H, N, T = 2, 100, 3, 128, 4
+    p = W.ssd_inputs(batch, L + T, H, 64, N, seed=5)
+    case("ssd prefill then decode")
+    part = lambda a, lo, hi: np.ascontiguousarray(a[:, lo:hi])
+    _, st = selscan.ssd_fwd(dev(part(p["x"], 0, L), BF), dev(part(p["delta"], 0, L), BF),
+                            dev(p["A"]), dev(part(p["B"], 0, L), BF), dev(part(p["C"], 0, L), BF),
+                            D=dev(p["D"]), dt_bias=dev(p["dt_bias"]))
+    ys = []
+    for t in range(L, L + T):
+        ys.append(to_np(selscan.ssd_step(st, dev(p["x"][:, t], BF), dev(p["delta"][:, t], BF),
+                                         dev(p["A"]), dev(p["B"][:, t], BF), dev(p["C"][:, t], BF),
+                                         D=dev(p["D"]), dt_bias=dev(p["dt_bias"]))))
+    torch.cuda.synchronize()
+    r = oracle.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["dt_bias"])
+    ey = oracle.scaled_error(np.stack(ys, 1), r["y"][:, L:], r["y_scale"][:, L:])
+    es = oracle.scaled_error(to_np(st), r["last_state"], r["state_scale"])
+    print(f"[parity] ssd prefill+decode: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_ssd_empty_from_initial_state():
+    case("ssd L = 0 from h0")
+    x = torch.empty((2, 0, 3, 64), dtype=BF, device="cuda")
+    h0 = torch.randn((2, 3, 64, 64), device="cuda")
+    _, hs = selscan.ssd_fwd(x, torch.empty((2, 0, 3), dtype=BF, device="cuda"),
+                            -torch.ones(3, device="cuda"), torch.empty((2, 0, 64), dtype=BF, device="cuda"),
+                            torch.empty((2, 0, 64), dtype=BF, device="cuda"), h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(hs, h0)
