@@ -81,14 +81,19 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
     int64_t S = segments;
     if (S == 0) {
         // Segmenting adds a state pass (about 0.7 of an output pass) over all
-        // but the last segment, so it only pays when the one-pass grid leaves
-        // most SIMDs (1024) without a wave. Then aim at exactly two waves per
-        // SIMD: two workgroups per CU are resident at once (LDS), and a grid
-        // of more than one such round leaves a partial last round.
+        // but the last segment, so it pays only when the one-pass grid leaves
+        // SIMDs (1024 of them, two resident waves each) idle. Below 512 waves,
+        // aim at two waves per SIMD (2048). Between 512 and 832 the counts
+        // below were the fastest of 1..6 in a sweep (L 2048, bf16): a grid
+        // just over one round of 2048 waves leaves a small, slow last round,
+        // so 3 segments at 640 waves (1,920) but 5 at 704 or 768. From 832
+        // waves on, one pass was fastest.
         S = 1;
-        if (waves < 512 && L >= 16 * kChunk) {
-            const int64_t target = 2048;
-            S = (target + waves - 1) / waves;
+        if (L >= 16 * kChunk) {
+            if (waves < 512) S = (2048 + waves - 1) / waves;
+            else if (waves <= 544) S = 4;
+            else if (waves <= 682) S = 3;
+            else if (waves < 832) S = 5;
             const int64_t max_by_len = L / (8 * kChunk);
             if (S > max_by_len) S = max_by_len;
             if (S < 1) S = 1;
@@ -212,9 +217,13 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 
-// Segments of a backward call: the same rule as the forward's (the reverse
-// sweep runs 4 waves per 64-row block, two blocks per CU); a segmented call
-// adds a state pass and a carry sweep, each over all but one segment.
+// Segments of a backward call (the reverse sweep runs 4 waves per 64-row
+// block, two blocks per CU); a segmented call adds a state pass and a carry
+// sweep, each over all but one segment, which cost less against the reverse
+// pass than the forward's state pass does against its output pass, so
+// segments pay up to larger grids. Below 512 waves: two waves per SIMD;
+// from 512 to 1279 the fastest counts of a sweep (L 2048, bf16); from 1280
+// waves on, one sweep.
 void bwd_segments(const selscan_dims_t* dims, int32_t requested, int32_t* segments,
                   int64_t* seg_len) {
     const int64_t L = dims->seqlen;
@@ -222,8 +231,13 @@ void bwd_segments(const selscan_dims_t* dims, int32_t requested, int32_t* segmen
     int64_t S = requested;
     if (S == 0) {
         S = 1;
-        if (waves < 512 && L >= 16 * kChunk) {
-            S = (2048 + waves - 1) / waves;
+        if (L >= 16 * kChunk) {
+            if (waves < 512) S = (2048 + waves - 1) / waves;
+            else if (waves <= 544) S = 4;
+            else if (waves < 736) S = 5;
+            else if (waves < 960) S = 6;
+            else if (waves < 1152) S = 2;
+            else if (waves < 1280) S = 3;
             const int64_t max_by_len = L / (8 * kChunk);
             if (S > max_by_len) S = max_by_len;
             if (S < 1) S = 1;

@@ -183,6 +183,33 @@ def test_workspace_size():
     assert S.workspace_size(8, 2048, 4096, __import__("torch").bfloat16) == 8 * 2048 * 128
 
 
+def _segments_from_workspace(batch, L, dim):
+    """The automatic segment count, read back from the workspace size."""
+    rows = batch * dim
+    packed = batch * ((L + 31) // 32 * 32) * 128
+    rc, total = workspace_size(D(batch=batch, L=L, dim=dim, dtype=S.BF16))
+    assert rc == S.OK
+    if total == packed:
+        return 1
+    al = lambda v: (v + 255) // 256 * 256
+    for seg in range(2, 4097):
+        if total == packed + 2 * al(seg * rows * 64) + al(seg * rows * 8):
+            return seg
+    raise AssertionError(total)
+
+
+def test_automatic_segments_follow_grid_size():
+    # waves = ceil(dim / 64) * batch * 4
+    assert _segments_from_workspace(8, 2048, 4096) == 1       # 2048 waves: one pass
+    assert _segments_from_workspace(8, 2048, 1664) == 1       # 832
+    assert _segments_from_workspace(8, 2048, 1536) == 5       # 768
+    assert _segments_from_workspace(4, 2048, 2560) == 3       # 640
+    assert _segments_from_workspace(8, 2048, 1024) == 4       # 512
+    assert _segments_from_workspace(1, 2048, 128) == 8        # 8 waves: two per SIMD, capped by L / 256
+    assert _segments_from_workspace(1, 1 << 20, 128) == 256   # 8 waves, long: 2048 waves
+    assert _segments_from_workspace(1, 511, 128) == 1         # too short to split
+
+
 def test_workspace_too_small_or_misaligned():
     need = workspace_size(D())[1]
     assert fwd_call(D(), ws=P(13), ws_bytes=need - 1) == S.ERR_CONFIG
