@@ -37,6 +37,7 @@ namespace selscan {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     __shared__ alignas(16) bf16_bits BsMs[kQ * NR];    // B rows [s][n]; later the masked scores [t][s]
     __shared__ alignas(16) bf16_bits Bw[N * QR];       // 2^(cum_end - cum_s) delta_s B^T: [n][s]
     __shared__ alignas(16) bf16_bits Xt[kP * QR];      // x^T [p][s]
-    __shared__ alignas(16) bf16_bits Ht[kP * NR];      // the state entering the chunk, bf16, [p][n]
+    __shared__ alignas(16) float4 Yx[4][4][64];       // carry-in partial sums for the partner wave
     __shared__ float cums[kQ], dts[kQ], gcum[kQ];      // running log2-decay, step and 2^cum of the chunk's tokens
     bf16_bits* Ms = BsMs;
 
@@ -152,25 +153,22 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         r.dl = to_f32(a.delta[(b * a.L + tt) * a.H + h]);
     };
 
-    // State tiles (fp32 accumulators): H^T rows p = 32 pb + acc_row, columns
-    // n = 32 (tb NTW + j) + lane % 32; from h0 (with its bf16 copy for the
-    // first chunk's C H), or zero. Both cover every element a product reads.
+    // State tiles (fp32 accumulators), from h0 or zero: rows
+    // n = 32 (tb NTW + j) + acc_row, columns p = 32 pb + lane % 32. The wave
+    // keeps its own rows of the state for its p block from chunk to chunk;
+    // the carry-in product C H is summed over n in two halves, one per wave
+    // of the p block, which swap partial sums through LDS.
     f32x16 H[NTW];
     if (a.h0) {
         const float* src = a.h0 + (b * a.H + h) * int64_t(N) * kP;
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int n = (tb * NTW + j) * 32 + lane % 32;
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                H[j][r] = src[int64_t(n) * kP + pb * 32 + acc_row(r, lane)];
-                Ht[(pb * 32 + acc_row(r, lane)) * NR + n] = tobf(H[j][r]);
-            }
-        }
+            for (int r = 0; r < 16; ++r)
+                H[j][r] = src[int64_t((tb * NTW + j) * 32 + acc_row(r, lane)) * kP + pb * 32 + lane % 32];
     } else {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
-        for (int i = tid; i < kP * NR; i += 256) Ht[i] = 0;
     }
 
     // The output of a chunk is stored in the next iteration, once that
@@ -246,6 +244,39 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
 
+        // ---- carry-in partials: C (both t blocks) times this wave's state rows ----
+        // The state's accumulator layout is the B operand of this product
+        // once the contraction index runs in a permuted order: registers
+        // 8 kb .. 8 kb + 7 of a lane hold state rows 16 kb + 4 (lane / 32) +
+        // {0..3, 8..11} of the tile, so the C operand is read in the same
+        // order (two 8-byte pieces per lane).
+        f32x16 Yp[2] = {f32x16{}, f32x16{}};
+        {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    bf16x8 hb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hb[e] = __bf16(H[j][8 * kb + e]);
+                    const int n0 = (tb * NTW + j) * 32 + 16 * kb + 4 * (lane / 32);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const bf16_bits* crow = &Cs[(tt * 32 + lane % 32) * NR + n0];
+                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(crow);
+                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(crow + 8);
+                        Yp[tt] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), hb, Yp[tt]);
+                    }
+                }
+            }
+            // the partner wave (same p block, other t block) gets its tile's half
+            const f32x16& give = Yp[1 - tb];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                Yx[pb * 2 + (1 - tb)][q][lane] =
+                    make_float4(give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]);
+        }
+
         // ---- scores of the lower block triangle: wave 0 (0,0), wave 1 (1,0), wave 2 (1,1) ----
         const int gt = wv == 0 ? 0 : 1, gs = wv == 2 ? 1 : 0;
         f32x16 G = {};
@@ -276,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
 
         // ---- output tile (tb, pb): scores x x  +  2^cum_t (C H)  +  D x ----
         {
-            f32x16 y1 = {}, y2 = {};
+            f32x16 y1 = {};
 #pragma unroll
             for (int ks = 0; ks < kQ / 16; ++ks) {
                 if (ks < 2 * (tb + 1)) {  // s blocks above the diagonal are all masked
@@ -284,10 +315,12 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                     y1 = mfma(lds8(&Ms[(tb * 32 + lane % 32) * QR + k0]), lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), y1);
                 }
             }
+            // C H: this wave's half plus the partner's (written before the last barrier)
+            f32x16 y2 = Yp[tb];
 #pragma unroll
-            for (int ks = 0; ks < N / 16; ++ks) {
-                const int k0 = ks * 16 + 8 * (lane / 32);
-                y2 = mfma(lds8(&Cs[(tb * 32 + lane % 32) * NR + k0]), lds8(&Ht[(pb * 32 + lane % 32) * NR + k0]), y2);
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = Yx[pb * 2 + tb][q][lane];
+                y2[4 * q] += v.x; y2[4 * q + 1] += v.y; y2[4 * q + 2] += v.z; y2[4 * q + 3] += v.w;
             }
             const int p = pb * 32 + lane % 32;
             const int t0 = tb * 32 + 4 * (lane / 32);  // chunk row of y1[0]
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 ypend[r / 2] = uint32_t(tobf(lo)) | (uint32_t(tobf(hi)) << 16);
             }
         }
-        // ---- state: H^T <- 2^cum_end H^T + x^T (w B) over this wave's tiles ----
+        // ---- state: H <- 2^cum_end H + (w B)^T x over this wave's tiles ----
         {
             const float gend = exp2_hw(cend);
 #pragma unroll
@@ -323,28 +356,21 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < kQ / 16; ++ks) {
                     const int k0 = ks * 16 + 8 * (lane / 32);
-                    acc = mfma(lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), lds8(&Bw[(nb * 32 + lane % 32) * QR + k0]), acc);
+                    acc = mfma(lds8(&Bw[(nb * 32 + lane % 32) * QR + k0]), lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), acc);
                 }
                 H[j] = acc;
             }
         }
-        __syncthreads();  // every read of this chunk's tiles and of Ht is done
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int n = (tb * NTW + j) * 32 + lane % 32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Ht[(pb * 32 + acc_row(r, lane)) * NR + n] = tobf(H[j][r]);
-        }
+        __syncthreads();  // every read of this chunk's tiles is done
     }
     store_y(nc - 1);
     if (a.last_state) {
         float* dst = a.last_state + (b * a.H + h) * int64_t(N) * kP;
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int n = (tb * NTW + j) * 32 + lane % 32;
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[int64_t(n) * kP + pb * 32 + acc_row(r, lane)] = H[j][r];
-        }
+            for (int r = 0; r < 16; ++r)
+                dst[int64_t((tb * NTW + j) * 32 + acc_row(r, lane)) * kP + pb * 32 + lane % 32] = H[j][r];
     }
 }
 
