@@ -388,6 +388,49 @@ def time_ssd_decode(torch, dev, steps=8):
             "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4)}
 
 
+def time_fused_conv(torch, dev, reps=10):
+    """The block's convolution + SiLU and the scan on the headline shape, as two
+    calls (conv1d writes its output, the scan reads it) and as one (the
+    convolution formed in the scan's per-token phase)."""
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    w = W.get(W.HEADLINE)
+    d = device_inputs(w, torch, dev)
+    c = W.conv_inputs(w)
+    cw = torch.from_numpy(c["w"]).to(dev)
+    cb = torch.from_numpy(c["bias"]).to(dev)
+    y = torch.empty_like(d["x"])
+    xc = torch.empty_like(d["x"])
+    kw = dict(D=d["D"], z=d["z"], dt_bias=d["dt_bias"], y=y)
+
+    def timed(run):
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    def separate():
+        selscan.conv1d(d["x"], cw, cb, out=xc, return_x_last=False)
+        selscan.fwd(xc, d["delta"], d["A"], d["B"], d["C"], **kw)
+
+    sep = timed(separate)
+    fused = timed(lambda: selscan.fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], **kw,
+                                      conv_w=cw, conv_b=cb))
+    scan = timed(lambda: selscan.fwd(d["x"], d["delta"], d["A"], d["B"], d["C"], **kw))
+    del d, y, xc
+    return {"workload": f"conv1d + scan on {w.name}", "separate_us": round(sep, 2),
+            "fused_us": round(fused, 2), "scan_alone_us": round(scan, 2),
+            "speedup": round(sep / fused, 3),
+            "fused_Gelem_per_s": round(w.elements / (fused * 1e-6) / 1e9, 1)}
+
+
 def time_conv(torch, dev, reps=20):
     """The causal conv1d (width 4) + SiLU over the headline-shaped input
     (bf16, x_last returned), and its decode step on the decode shape. Kernel
@@ -652,6 +695,9 @@ def main():
     if not args.no_extras and args.only in (None, "conv"):
         log("[bench] conv1d: headline shape and decode steps")
         extras.update(time_conv(torch, dev))
+        log("[bench] conv1d fused into the scan")
+        extras["conv_fused"] = time_fused_conv(torch, dev)
+        log(f"[bench] conv fused: {extras['conv_fused']}")
     for key, name in (("long", "long_f32_b1_l1048576_d128"), ("m130m", "m130m_f32_b8_l2048_d1536")):
         if args.no_extras or args.only not in (None, key):
             continue

@@ -120,6 +120,16 @@ int selscan_fwd(const void* x, const void* delta, const float* A, const void* B,
  *               hardware-aware algorithm: the backward recomputes states
  *               rather than storing all L of them; these are 1/16 of them).
  *               Requires groups 0 or 4. Must not overlap any input or output.
+ *   conv_w    : NULL, or [d, 4] fp32 taps of the block's causal depthwise
+ *               convolution + SiLU (the definition of selscan_conv1d), which
+ *               is then applied to x on the fly: the scan's input is
+ *               silu(conv_b[d] + sum_k conv_w[d,k] xx(t - 3 + k)), never
+ *               written to memory (x is the convolution's input, and D
+ *               multiplies the convolved input). Requires groups 0 or 4 and
+ *               no ckpt.
+ *   conv_b    : [d] fp32 or NULL (0); only with conv_w.
+ *   conv_x_prev, conv_x_last : [B, d, 3] fp32 or NULL, as selscan_conv1d's
+ *               x_prev and x_last; only with conv_w. x_last may be x_prev.
  */
 typedef struct {
     const float* h0;
@@ -128,6 +138,10 @@ typedef struct {
     int32_t segments;
     int32_t groups;
     float* ckpt;
+    const float* conv_w;
+    const float* conv_b;
+    const float* conv_x_prev;
+    float* conv_x_last;
 } selscan_fwd_opts_t;
 
 /*

@@ -117,6 +117,9 @@ int check_opts(const selscan_fwd_opts_t& o) {
     if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
     if (o.groups != 0 && o.groups != 1 && o.groups != 2 && o.groups != 4) return SELSCAN_ERR_CONFIG;
     if (o.ckpt && o.groups != 0 && o.groups != 4) return SELSCAN_ERR_CONFIG;  // 4 waves store them
+    // the convolution in front: 4 waves, not with checkpoints, its other inputs only with taps
+    if (o.conv_w && ((o.groups != 0 && o.groups != 4) || o.ckpt)) return SELSCAN_ERR_CONFIG;
+    if (!o.conv_w && (o.conv_b || o.conv_x_prev || o.conv_x_last)) return SELSCAN_ERR_CONFIG;
     return SELSCAN_OK;
 }
 
@@ -160,7 +163,9 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     if ((sz.seq > 0 && (!x || !delta || !y)) || (sz.bc > 0 && (!B || !C)) || (sz.param > 0 && !A))
         return SELSCAN_ERR_NULL;
     for (const void* p : {x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)dt_bias, (const void*)y,
-                          (const void*)last_state, (const void*)o.h0, (const void*)o.ckpt})
+                          (const void*)last_state, (const void*)o.h0, (const void*)o.ckpt,
+                          (const void*)o.conv_w, (const void*)o.conv_b, (const void*)o.conv_x_prev,
+                          (const void*)o.conv_x_last})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u)) return SELSCAN_ERR_CONFIG;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
@@ -185,6 +190,19 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
         if (overlaps(s, out_c)) return SELSCAN_ERR_ALIAS;
     if (overlaps(out_c, out_y) || overlaps(out_c, out_s) || overlaps(out_c, in_h0))
         return SELSCAN_ERR_ALIAS;
+    // the convolution: x_last is an output (it may be x_prev itself)
+    const Span in_cw = span(o.conv_w, dims->dim * 16), in_cb = span(o.conv_b, dims->dim * 4);
+    const Span in_cp = span(o.conv_x_prev, sz.rows * 12), out_cl = span(o.conv_x_last, sz.rows * 12);
+    for (const Span& s : {in_cw, in_cb, in_cp})
+        if (overlaps(s, out_y) || overlaps(s, out_s) || overlaps(s, out_c)) return SELSCAN_ERR_ALIAS;
+    for (const Span& s : ins)
+        if (overlaps(s, out_cl)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_cl, out_y) || overlaps(out_cl, out_s) || overlaps(out_cl, in_h0) ||
+        overlaps(out_cl, in_cw) || overlaps(out_cl, in_cb))
+        return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_cl, in_cp) &&
+        static_cast<const void*>(o.conv_x_last) != static_cast<const void*>(o.conv_x_prev))
+        return SELSCAN_ERR_ALIAS;
 
     FwdPlan plan{};
     rc = make_plan(dims, o.segments, o.groups, &plan);
@@ -196,13 +214,19 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (sz.rows == 0) return SELSCAN_OK;
     if (L == 0) {
+        if (o.conv_x_last) {  // no new inputs: the last three are the previous ones
+            const hipError_t e = o.conv_x_prev ? launch_copy_f32(o.conv_x_last, o.conv_x_prev, sz.rows * 3, st)
+                                               : launch_fill_zero(o.conv_x_last, sz.rows * 3, st);
+            if (e != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        }
         if (!last_state) return SELSCAN_OK;
         const hipError_t e = o.h0 ? launch_copy_f32(last_state, o.h0, sz.state, st)
                                   : launch_fill_zero(last_state, sz.state, st);
         return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
     }
 
-    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state, o.h0, o.ckpt};
+    FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state, o.h0, o.ckpt,
+                 o.conv_w, o.conv_b, o.conv_x_prev, o.conv_x_last};
     next_events(&plan.ev_begin, &plan.ev_end);
     void* ws = o.workspace;
     const bool own = ws == nullptr;

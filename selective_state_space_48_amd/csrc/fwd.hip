@@ -112,9 +112,10 @@ struct alignas(16) Smem {
     static constexpr int kPairB = CH * 8 + 16;  // float2-per-token row stride (bytes)
     static constexpr int kYB = CH * 4 + 16;     // float-per-token row stride (bytes)
     unsigned char lw[kWave * kPairB];
-    static constexpr bool kReadout = MODE == 0 || MODE == 3;
+    static constexpr int kBase = MODE >= 4 ? MODE - 4 : MODE;  // 4, 5: 0, 1 with the conv
+    static constexpr bool kReadout = kBase == 0 || kBase == 3;
     unsigned char yp[kReadout ? G : 1][kReadout ? kWave * kYB : 16];
-    double lsum[MODE == 1 ? G : 1][kWave];
+    double lsum[kBase == 1 ? G : 1][kWave];
 };
 
 struct FwdKArgs {
@@ -135,6 +136,10 @@ struct FwdKArgs {
     int32_t segments, row_blocks;
     // MODE 2 and 3 only:
     float* ckpt;       // [ceil(L/16)][batch*dim][N]: the state before every 16th token
+    // MODE 4 and 5 only: x is the convolution's input (see below)
+    const float* cw;      // [dim][4] taps, tap k on the input 3 - k tokens back
+    const float* cb;      // [dim] or null
+    const float* cx_prev; // [batch*dim][3] inputs before token 0 (oldest first), or null
 };
 
 // MODE 0: output pass (y, and last_state from the final segment).
@@ -143,6 +148,10 @@ struct FwdKArgs {
 //         state before every 16th token.
 // MODE 3: output pass that also stores those checkpoints (a forward whose
 //         backward follows).
+// MODE 4, 5: MODE 0, 1 with the block's causal depthwise convolution (width
+//         4) and SiLU applied to x on the fly, in the per-token phase: the
+//         scan's input is silu(cb + sum_k cw[k] x[t - 3 + k]), which is never
+//         written to memory.
 template <typename T, int G, bool GATE, bool VEC, int MODE>
 __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int CH = kChunk;
@@ -152,10 +161,13 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int TS = CH / G;              // tokens per wave in the per-token phases
     constexpr int V = Elem<T>::kPer16;      // elements per 16-byte vector
     constexpr int SV = TS / V;              // 16-byte vectors per row slice
-    constexpr bool READOUT = MODE == 0 || MODE == 3;  // y = C.h + D x, gated
-    constexpr bool CKPT = MODE == 2 || MODE == 3;     // states every 16 tokens
+    constexpr bool CONV = MODE >= 4;                  // convolution + SiLU in front
+    constexpr int BASE = CONV ? MODE - 4 : MODE;
+    constexpr bool READOUT = BASE == 0 || BASE == 3;  // y = C.h + D x, gated
+    constexpr bool CKPT = BASE == 2 || BASE == 3;     // states every 16 tokens
     constexpr bool LOADZ = GATE && READOUT;
     static_assert(!CKPT || G == 4, "checkpoints: 4 waves of 4 states");
+    static_assert(!CONV || (G == 4 && BASE < 2), "the convolution: 4 waves, output or state pass");
     static_assert(TS % V == 0 && SV >= 1, "tile shape");
     using S = Smem<G, CH, MODE>;
     __shared__ S sm;
@@ -195,6 +207,12 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const int64_t prow = b * a.dim + (prow_ok ? dp : d0);  // clamped for safe reads
     const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;  // bias / ln 2
     const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
+    float4 cw4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float cbias = 0.0f;
+    if constexpr (CONV) {
+        if (prow_ok) cw4 = *reinterpret_cast<const float4*>(a.cw + dp * 4);
+        cbias = (a.cb && prow_ok) ? a.cb[dp] : 0.0f;
+    }
     float An[NG], h[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -210,6 +228,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // chunk parity.
     struct Slice {
         uint4 x[SV], d[SV], z[LOADZ ? SV : 1];
+        uint4 xp[1];  // with the convolution: the 16 bytes of x before the slice
     };
     Slice sl0, sl1;
     // With 16-byte rows (VEC) the loads are issued without any condition: a
@@ -222,9 +241,28 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     auto load_vec = [&](const T* base, int64_t tk) {
         return ldg_stream(base + prow * a.L + min(tk, a.L - V));
     };
+    // The convolution's history of a slice: the V inputs before it (real
+    // data also across a segment boundary; at token 0 the prologue takes the
+    // caller's previous inputs instead).
+    auto load_hist = [&](int64_t ts, Slice& sl) {
+        if constexpr (CONV) {
+            if constexpr (VEC) {
+                sl.xp[0] = ldg_stream(X + prow * a.L + max(int64_t(0), min(ts - V, a.L - V)));
+            } else {
+                float f[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const int64_t tk = ts - V + e;
+                    f[e] = (tk >= 0 && tk < a.L) ? to_f32(X[prow * a.L + tk]) : 0.0f;
+                }
+                sl.xp[0] = pack16<T>(f);
+            }
+        }
+    };
     auto load_slice = [&](int c, Slice& sl) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
         const int64_t off = prow * a.L + ts;
+        load_hist(ts, sl);
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             const int64_t tk = ts + k * V;
@@ -252,6 +290,8 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // halves are requested back to back and the line is fetched once.
     auto load_pair = [&](int c, Slice& s0, Slice& s1) {
         const int64_t ts = t_begin + int64_t(c) * CH + pq * TS;
+        load_hist(ts, s0);
+        load_hist(ts + CH, s1);
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
             s0.x[k] = load_vec(X, ts + k * V);
@@ -285,6 +325,24 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             unpack16<T>(sl.d[k], ds + k * V);
             if constexpr (LOADZ) unpack16<T>(sl.z[k], zs + k * V);
         }
+        if constexpr (CONV) {
+            // x <- silu(cb + sum_k cw[k] x[t - 3 + k]) over the window of the
+            // 3 inputs before the slice and the slice itself
+            float hp[V], win[TS + 3];
+            unpack16<T>(sl.xp[0], hp);
+#pragma unroll
+            for (int e = 0; e < 3; ++e) win[e] = hp[V - 3 + e];
+            if (ts == 0) {
+#pragma unroll
+                for (int e = 0; e < 3; ++e) win[e] = a.cx_prev ? a.cx_prev[prow * 3 + e] : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < TS; ++e) win[3 + e] = xs[e];
+#pragma unroll
+            for (int e = 0; e < TS; ++e)
+                xs[e] = silu(fmaf(cw4.w, win[e + 3], fmaf(cw4.z, win[e + 2],
+                             fmaf(cw4.y, win[e + 1], fmaf(cw4.x, win[e], cbias)))));
+        }
         float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]) + pq * TS / 2;
         auto body = [&](auto masked) {
             const int nvalid = masked ? int(min(int64_t(TS), max(int64_t(0), t_end - ts))) : TS;
@@ -299,7 +357,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                         xs[j + u] = 0.0f;
                     }
                     w[u] = l[u] * xs[j + u];
-                    if constexpr (MODE == 1) lsum_acc += double(l[u]);
+                    if constexpr (BASE == 1) lsum_acc += double(l[u]);
                     if constexpr (READOUT) {
                         dxo[j + u] = Dd * xs[j + u];
                         gzo[j + u] = 1.0f;
@@ -486,7 +544,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             for (int k = 0; k < NG / 4; ++k)
                 dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
         }
-    } else if constexpr (MODE == 1) {
+    } else if constexpr (BASE == 1) {
         const int64_t so = (int64_t(seg) * a.batch * a.dim + b * a.dim + d);
         if (row_ok) {
             float4* dst = reinterpret_cast<float4*>(a.seg_state + so * kN + n0);
@@ -604,7 +662,7 @@ hipError_t launch_one(const FwdKArgs& k, int64_t blocks, hipStream_t st) {
 template <typename T, int G, int MODE>
 hipError_t dispatch_gv(const FwdKArgs& k, bool gate, bool vec, int64_t blocks, hipStream_t st) {
     static_assert(MODE < 2 || G == 4, "checkpoints: 4 waves");
-    if (MODE == 1 || MODE == 2) gate = false;  // no readout: z is never read
+    if (MODE == 1 || MODE == 2 || MODE == 5) gate = false;  // no readout: z is never read
     if (gate) return vec ? launch_one<T, G, true, true, MODE>(k, blocks, st)
                          : launch_one<T, G, true, false, MODE>(k, blocks, st);
     return vec ? launch_one<T, G, false, true, MODE>(k, blocks, st)
@@ -651,7 +709,11 @@ hipError_t output_pass(DType dt, const FwdKArgs& k, const FwdPlan& p, bool gate,
                        hipStream_t st) {
     if (p.ev_begin && hipEventRecord(p.ev_begin, st) != hipSuccess) return hipGetLastError();
     hipError_t e;
-    if (k.ckpt) {
+    if (k.cw) {
+        if (p.groups != 4 || k.ckpt) return hipErrorInvalidValue;
+        e = dt == DType::BF16 ? dispatch_gv<bf16_bits, 4, 4>(k, gate, p.vec, blocks, st)
+                              : dispatch_gv<float, 4, 4>(k, gate, p.vec, blocks, st);
+    } else if (k.ckpt) {
         if (p.groups != 4) return hipErrorInvalidValue;
         e = dt == DType::BF16 ? dispatch_gv<bf16_bits, 4, 3>(k, gate, p.vec, blocks, st)
                               : dispatch_gv<float, 4, 3>(k, gate, p.vec, blocks, st);
@@ -667,6 +729,20 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Padded token count of the packed B/C: whole chunks.
 int64_t padded_len(int64_t L) { return (L + kChunk - 1) / kChunk * kChunk; }
+
+// The convolution's last three inputs of every row (oldest first): the
+// x_prev of a call that continues the sequence. One thread per row, entries
+// in order, so x_last may be x_prev itself (entry k reads entry k + L >= k).
+template <typename T>
+__global__ __launch_bounds__(256) void conv_last_kernel(const T* __restrict__ x, const float* x_prev,
+                                                        float* x_last, int64_t rows, int64_t L) {
+    const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (r >= rows) return;
+    for (int k = 0; k < 3; ++k) {
+        const int64_t s = L - 3 + k;
+        x_last[r * 3 + k] = s >= 0 ? to_f32(x[r * L + s]) : (x_prev ? x_prev[r * 3 + 3 + s] : 0.0f);
+    }
+}
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -717,6 +793,7 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     FwdKArgs k{};
     k.x = t.x; k.delta = t.delta; k.z = t.z; k.A = t.A; k.P = P;
     k.D = t.D; k.dt_bias = t.dt_bias; k.y = t.y; k.last_state = t.last_state; k.ckpt = t.ckpt;
+    k.cw = t.conv_w; k.cb = t.conv_b; k.cx_prev = t.conv_x_prev;
     k.batch = s.batch; k.L = s.L; k.dim = s.dim;
     k.seg_len = p.segments > 1 ? p.seg_len : s.L;
     k.psub = Lp / p.groups;
@@ -725,9 +802,23 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     const bool gate = t.z != nullptr;
     const int64_t per_seg = int64_t(k.row_blocks) * s.batch;
 
+    // the convolution's last inputs, after the pass that reads x_prev
+    auto conv_last = [&]() -> hipError_t {
+        if (!t.conv_w || !t.conv_x_last) return hipSuccess;
+        const int64_t rows = s.batch * s.dim;
+        const dim3 grid(unsigned((rows + 255) / 256)), block(256);
+        if (s.dtype == DType::BF16)
+            hipLaunchKernelGGL((conv_last_kernel<bf16_bits>), grid, block, 0, stream,
+                               static_cast<const bf16_bits*>(t.x), t.conv_x_prev, t.conv_x_last, rows, s.L);
+        else
+            hipLaunchKernelGGL((conv_last_kernel<float>), grid, block, 0, stream,
+                               static_cast<const float*>(t.x), t.conv_x_prev, t.conv_x_last, rows, s.L);
+        return hipGetLastError();
+    };
     if (p.segments <= 1) {
         k.h0 = t.h0;
-        return output_pass(s.dtype, k, p, gate, per_seg, stream);
+        e = output_pass(s.dtype, k, p, gate, per_seg, stream);
+        return e != hipSuccess ? e : conv_last();
     }
     const size_t rows = size_t(s.batch) * size_t(s.dim);
     const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
@@ -741,7 +832,14 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     k1.seg_lsum = seg_lsum;
     k1.h0 = nullptr;
     k1.ckpt = nullptr;
-    e = dispatch_dtype<1>(s.dtype, k1, p.groups, false, p.vec, per_seg * (p.segments - 1), stream);
+    if (t.conv_w) {
+        if (p.groups != 4) return hipErrorInvalidValue;
+        e = s.dtype == DType::BF16
+                ? dispatch_gv<bf16_bits, 4, 5>(k1, false, p.vec, per_seg * (p.segments - 1), stream)
+                : dispatch_gv<float, 4, 5>(k1, false, p.vec, per_seg * (p.segments - 1), stream);
+    } else {
+        e = dispatch_dtype<1>(s.dtype, k1, p.groups, false, p.vec, per_seg * (p.segments - 1), stream);
+    }
     if (e != hipSuccess) return e;
     // 2) carries
     const int64_t nthreads = int64_t(rows) * kN;
@@ -751,7 +849,8 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     if (e != hipSuccess) return e;
     // 3) output pass from the carried-in states
     k.h0 = carry;
-    return output_pass(s.dtype, k, p, gate, per_seg * p.segments, stream);
+    e = output_pass(s.dtype, k, p, gate, per_seg * p.segments, stream);
+    return e != hipSuccess ? e : conv_last();
 }
 
 hipError_t launch_carry(const float* A, const float* seg_state, const double* seg_lsum,

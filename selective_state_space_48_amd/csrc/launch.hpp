@@ -23,6 +23,14 @@ struct FwdTensors {
     float* last_state;  // null: not wanted
     const float* h0;    // [batch, dim, N] state entering token 0; null: zeros
     float* ckpt;        // [ceil(L/16)][batch*dim][N] states before every 16th token; null: none
+    // The block's causal depthwise convolution (width 4) + SiLU applied to x
+    // first (null conv_w: none): taps [dim, 4], bias [dim] or null, the 3
+    // inputs before token 0 [batch*dim, 3] or null (zeros), and the last 3
+    // inputs out [batch*dim, 3] or null.
+    const float* conv_w = nullptr;
+    const float* conv_b = nullptr;
+    const float* conv_x_prev = nullptr;
+    float* conv_x_last = nullptr;
 };
 
 struct FwdShape {

@@ -36,7 +36,9 @@ class Dims(ctypes.Structure):
 class FwdOpts(ctypes.Structure):
     _fields_ = [("h0", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_uint64), ("segments", ctypes.c_int32),
-                ("groups", ctypes.c_int32), ("ckpt", ctypes.c_void_p)]
+                ("groups", ctypes.c_int32), ("ckpt", ctypes.c_void_p),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+                ("conv_x_prev", ctypes.c_void_p), ("conv_x_last", ctypes.c_void_p)]
 
 
 class BwdOpts(ctypes.Structure):
@@ -170,11 +172,16 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
         last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
         h0: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
         segments: int = 0, groups: int = 0,
-        ckpt: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        ckpt: Optional[torch.Tensor] = None, conv_w: Optional[torch.Tensor] = None,
+        conv_b: Optional[torch.Tensor] = None, conv_x_prev: Optional[torch.Tensor] = None,
+        conv_x_last: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective-scan forward (selscan_fwd_ex). Returns (y, last_state).
 
     ``ckpt`` (shape ``ckpt_shape(batch, dim, L)``, fp32) receives the state
-    entering every 16th token, for ``bwd(..., ckpt=ckpt)``.
+    entering every 16th token, for ``bwd(..., ckpt=ckpt)``. With ``conv_w``
+    [dim, 4] fp32 the block's causal conv1d + SiLU (as ``conv1d``) is applied
+    to ``x`` inside the scan; ``conv_b`` [dim], ``conv_x_prev`` and
+    ``conv_x_last`` [batch, dim, 3] fp32 as for ``conv1d``.
 
     ``y`` and ``last_state`` may be passed in preallocated; otherwise they are
     allocated here. ``h0`` [batch, dim, N] fp32 is the state entering token 0
@@ -206,8 +213,13 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     _req(last_state, "last_state", torch.float32, (batch, dim, N), dev)
     _req(h0, "h0", torch.float32, (batch, dim, N), dev)
     _req(ckpt, "ckpt", torch.float32, ckpt_shape(batch, dim, L, N), dev)
+    _req(conv_w, "conv_w", torch.float32, (dim, CONV_WIDTH), dev)
+    _req(conv_b, "conv_b", torch.float32, (dim,), dev)
+    _req(conv_x_prev, "conv_x_prev", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
+    _req(conv_x_last, "conv_x_last", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
     dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
-    opts = FwdOpts(None, None, 0, int(segments), int(groups), _ptr(ckpt))
+    opts = FwdOpts(None, None, 0, int(segments), int(groups), _ptr(ckpt), _ptr(conv_w), _ptr(conv_b),
+                   _ptr(conv_x_prev), _ptr(conv_x_last))
     need = ctypes.c_uint64(0)
     _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value > 0:

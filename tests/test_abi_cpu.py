@@ -159,6 +159,26 @@ def test_fwd_checkpoint_option_checks():
     assert fwd_call(D(), groups=4, ckpt=ck, ws=P(13), ws_bytes=16) == S.ERR_CONFIG
 
 
+def test_fwd_fused_conv_option_checks():
+    def call(groups=0, ckpt=None, cw=None, cb=None, cp=None, cl=None, ws=None, ws_bytes=0):
+        p = [P(i) for i in range(10)]
+        o = S.FwdOpts(None, ws, ws_bytes, 0, groups, ckpt, cw, cb, cp, cl)
+        return S.lib.selscan_fwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None)
+    cw, cb, cp, cl = (BASE + (20 + i) * SPAN for i in range(4))
+    assert call(cb=cb) == S.ERR_CONFIG                      # bias without taps
+    assert call(cp=cp) == S.ERR_CONFIG
+    assert call(cl=cl) == S.ERR_CONFIG
+    assert call(cw=cw, groups=2) == S.ERR_CONFIG            # 4 waves only
+    assert call(cw=cw, ckpt=BASE + 25 * SPAN) == S.ERR_CONFIG
+    assert call(cw=cw + 4) == S.ERR_ALIGN
+    assert call(cw=cw, cl=P(0).value) == S.ERR_ALIAS        # x_last == x
+    assert call(cw=cw, cl=P(8).value) == S.ERR_ALIAS        # x_last == y
+    assert call(cw=P(8).value) == S.ERR_ALIAS               # taps inside y
+    assert call(cw=cw, cp=cp, cl=cp + 16) == S.ERR_ALIAS    # overlapping, not equal
+    # x_last == x_prev is allowed: the call gets as far as the workspace check
+    assert call(cw=cw, cb=cb, cp=cp, cl=cp, ws=P(13), ws_bytes=16) == S.ERR_CONFIG
+
+
 def workspace_size(dims, segments=0, groups=0):
     out = ctypes.c_uint64(7)
     opts = S.FwdOpts(None, None, 0, segments, groups)
