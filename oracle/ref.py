@@ -82,6 +82,8 @@ class Oracle:
         lib.ssm_ref_ssd.argtypes = [_dp] * 8 + [ctypes.c_int64] * 5 + [_dp] * 4 + [ctypes.c_int]
         lib.ssm_ref_conv1d.restype = ctypes.c_int
         lib.ssm_ref_conv1d.argtypes = [_dp] * 4 + [ctypes.c_int64] * 4 + [_dp] * 3
+        lib.ssm_ref_conv1d_bwd.restype = ctypes.c_int
+        lib.ssm_ref_conv1d_bwd.argtypes = [_dp] * 5 + [ctypes.c_int64] * 4 + [_dp] * 8
         lib.ssm_ref_conv1d_step.restype = ctypes.c_int
         lib.ssm_ref_conv1d_step.argtypes = [_dp] * 4 + [ctypes.c_int64] * 3 + [_dp] * 2
         self.lib = lib
@@ -195,6 +197,28 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"ssm_ref_conv1d failed with code {rc}")
         return {"out": out, "out_scale": sc, "x_last": last}
+
+    def conv1d_bwd(self, x, w, bias=None, x_prev=None, *, dout):
+        """Gradients of ``conv1d`` for an output gradient ``dout`` ``[batch, dim,
+        seqlen]``. Returns a dict with ``dx`` (like x), ``dx_prev`` (``[batch,
+        dim, K-1]``), ``dw`` (``[dim, K]``) and ``dbias`` (``[dim]``), each with a
+        ``<name>_scale``, all float64."""
+        x, w, bias, x_prev, dout = map(_f64, (x, w, bias, x_prev, dout))
+        batch, dim, L = x.shape
+        K = w.shape[1]
+        assert w.shape == (dim, K) and dout.shape == x.shape
+        e = lambda *shape: np.zeros(shape, np.float64)
+        out = {"dx": e(batch, dim, L), "dx_scale": e(batch, dim, L), "dx_prev": e(batch, dim, K - 1),
+               "dx_prev_scale": e(batch, dim, K - 1), "dw": e(dim, K), "dw_scale": e(dim, K),
+               "dbias": e(dim), "dbias_scale": e(dim)}
+        g = lambda k: _ptr(out[k])
+        rc = self.lib.ssm_ref_conv1d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(x_prev), _ptr(dout),
+                                         batch, L, dim, K, g("dx"), g("dx_prev"), g("dw"), g("dbias"),
+                                         g("dx_scale"), g("dx_prev_scale"), g("dw_scale"),
+                                         g("dbias_scale"))
+        if rc != 0:
+            raise RuntimeError(f"ssm_ref_conv1d_bwd failed with code {rc}")
+        return out
 
     def conv1d_step(self, conv_state, x, w, bias=None):
         """One decode step of the convolution from ``conv_state`` ``[batch, dim,
@@ -325,6 +349,11 @@ def ssd_step(*args, **kw):
 def conv1d(*args, **kw):
     """Causal depthwise conv + SiLU through the built oracle; see ``Oracle.conv1d``."""
     return default().conv1d(*args, **kw)
+
+
+def conv1d_bwd(*args, **kw):
+    """Gradients of the convolution; see ``Oracle.conv1d_bwd``."""
+    return default().conv1d_bwd(*args, **kw)
 
 
 def conv1d_step(*args, **kw):

@@ -298,6 +298,71 @@ int ssm_ref_conv1d(const double *x, const double *w, const double *bias, const d
 }
 
 /*
+ * Gradients of the convolution + SiLU above for an output gradient dout
+ * [batch, dim, seqlen]: the chain rule through its definition, written out.
+ *   pre[t] = bias + sum_k w[k] xx(t - (K-1) + k),   out[t] = silu(pre[t])
+ *   g[t]   = dout[t] * silu'(pre[t]),  silu'(u) = sig(u) (1 + u (1 - sig(u)))
+ *   dxx(s) = sum_k w[k] g[s + (K-1) - k]   over the t = s + (K-1) - k in [0, L)
+ *   dx[t] = dxx(t) (t >= 0);  dx_prev[j] = dxx(j - (K-1))  (j < K-1)
+ *   dw[d,k] = sum_{b,t} g[t] xx(t - (K-1) + k);   dbias[d] = sum_{b,t} g[t]
+ * Scales: the same sums on magnitudes, silu' taken as the sum of its two
+ * terms' magnitudes, sig(u) (1 + |u| (1 - sig(u))), and pre as its terms'.
+ * dx_prev, dbias and their scales may be null (not wanted). dw, dbias: sums
+ * over batch entries in order.
+ */
+int ssm_ref_conv1d_bwd(const double *x, const double *w, const double *bias, const double *x_prev,
+                       const double *dout, int64_t batch, int64_t seqlen, int64_t dim, int64_t K,
+                       double *dx, double *dx_prev, double *dw, double *dbias,
+                       double *sdx, double *sdx_prev, double *sdw, double *sdbias)
+{
+    if (!x || !w || !dout || !dx || !dw || !sdx || !sdw) return -1;
+    if ((dx_prev && !sdx_prev) || (dbias && !sdbias)) return -1;
+    if (batch < 0 || seqlen < 0 || dim < 0 || K < 1) return -2;
+    const int64_t L = seqlen, H = K - 1;
+    double *g = malloc(sizeof(double) * (size_t)(2 * (L + 1)));
+    if (!g) return -3;
+    double *ga = g + L + 1;
+    for (int64_t i = 0; i < dim * K; ++i) dw[i] = sdw[i] = 0.0;
+    if (dbias) for (int64_t d = 0; d < dim; ++d) dbias[d] = sdbias[d] = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t row = b * dim + d;
+            const double *xr = x + row * L, *dr = dout + row * L;
+            const double *pr = x_prev ? x_prev + row * H : NULL;
+            const double *wd = w + d * K;
+            #define XX(s) ((s) >= 0 ? xr[s] : (pr ? pr[H + (s)] : 0.0))
+            for (int64_t t = 0; t < L; ++t) {
+                double pre = bias ? bias[d] : 0.0, pa = fabs(pre);
+                for (int64_t k = 0; k < K; ++k) {
+                    pre += wd[k] * XX(t - H + k);
+                    pa += fabs(wd[k] * XX(t - H + k));
+                }
+                const double sg = 1.0 / (1.0 + exp(-pre));
+                g[t] = dr[t] * sg * (1.0 + pre * (1.0 - sg));
+                ga[t] = fabs(dr[t]) * sg * (1.0 + pa * (1.0 - sg));
+                for (int64_t k = 0; k < K; ++k) {
+                    dw[d * K + k] += g[t] * XX(t - H + k);
+                    sdw[d * K + k] += ga[t] * fabs(XX(t - H + k));
+                }
+                if (dbias) { dbias[d] += g[t]; sdbias[d] += ga[t]; }
+            }
+            for (int64_t s = -H; s < L; ++s) {
+                double v = 0.0, va = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t t = s + H - k;
+                    if (t >= 0 && t < L) { v += wd[k] * g[t]; va += fabs(wd[k]) * ga[t]; }
+                }
+                if (s >= 0) { dx[row * L + s] = v; sdx[row * L + s] = va; }
+                else if (dx_prev) { dx_prev[row * H + H + s] = v; sdx_prev[row * H + H + s] = va; }
+            }
+            #undef XX
+        }
+    }
+    free(g);
+    return 0;
+}
+
+/*
  * One decode step of the convolution: the same formula for a single token x
  * [batch, dim] with the K-1 previous inputs held in conv_state [batch, dim,
  * K-1] (oldest first), which is then shifted by one and takes x as its

@@ -480,6 +480,51 @@ def pin_conv1d_torch_grouped(O):
     _close(O.conv1d(p["x"], p["w"], p["bias"])["out"], ref, 1e-12, what="conv torch grouped")
 
 
+def pin_conv1d_bwd_torch_autograd(O):
+    """Every gradient of the convolution (x, the inputs before token 0, taps,
+    bias) against torch autograd in fp64 of the grouped conv1d (the
+    library's chain rule) over the previous inputs prepended, then silu."""
+    for with_bias in (True, False):
+        p = _conv_problem(35, 2, 5, 19, with_bias=with_bias)
+        dout = np.random.default_rng(36).standard_normal((2, 5, 19))
+        r = O.conv1d_bwd(p["x"], p["w"], p["bias"], p["x_prev"], dout=dout)
+        K = p["w"].shape[1]
+        T = {k: torch.tensor(p[k], requires_grad=True) for k in ("x", "w", "x_prev")}
+        bias = torch.tensor(p["bias"], requires_grad=True) if with_bias else None
+        seq = torch.cat([T["x_prev"], T["x"]], dim=-1)
+        pre = torch.nn.functional.conv1d(seq, T["w"][:, None, :], bias, groups=5)
+        (torch.nn.functional.silu(pre) * torch.from_numpy(dout)).sum().backward()
+        for k, g in (("x", "dx"), ("w", "dw"), ("x_prev", "dx_prev")):
+            _close(r[g], T[k].grad.numpy(), 1e-12, scale=r[g + "_scale"] + 1e-300,
+                   what=f"conv bwd autograd {g} bias={with_bias}")
+        if with_bias:
+            _close(r["dbias"], bias.grad.numpy(), 1e-12, scale=r["dbias_scale"] + 1e-300,
+                   what="conv bwd autograd dbias")
+        assert np.all(r["dx_scale"] >= np.abs(r["dx"]) * (1 - 1e-12))
+
+
+def pin_conv1d_bwd_finite_differences(O):
+    """Central differences of sum(dout * out) through the oracle's own
+    convolution, every element of every input, on a tiny problem."""
+    p = _conv_problem(37, 2, 2, 6)
+    dout = np.random.default_rng(38).standard_normal((2, 2, 6))
+    r = O.conv1d_bwd(p["x"], p["w"], p["bias"], p["x_prev"], dout=dout)
+
+    def loss(q):
+        return float(np.sum(dout * O.conv1d(q["x"], q["w"], q["bias"], q["x_prev"])["out"]))
+
+    for name, gname in (("x", "dx"), ("w", "dw"), ("bias", "dbias"), ("x_prev", "dx_prev")):
+        base = p[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[idx]))
+            q = dict(p); arr = base.copy(); arr[idx] += eps; q[name] = arr
+            lp = loss(q)
+            arr = base.copy(); arr[idx] -= eps; q[name] = arr
+            fd[idx] = (lp - loss(q)) / (2 * eps)
+        _close(r[gname], fd, 1e-6, scale=np.maximum(np.abs(fd), 1.0), what=f"conv bwd finite diff {gname}")
+
+
 def pin_conv1d_one_hot_taps(O):
     """A single tap k = K-1-j gives out[t] = silu(x[t-j]) (zero before the
     start): fixes the causal direction and the tap order."""

@@ -72,6 +72,9 @@ MUTANTS = [
     ("bwd_decay_term_dropped", "ddl += q * Ad[n];", "ddl += 0.0 * Ad[n];"),
     ("bwd_dD_ungated", "dD += ds * x[t];", "dD += dy[t] * x[t];"),
     ("bwd_dt_bias_no_sigmoid", "dT += ddl * sg;", "dT += ddl;"),
+    ("conv_bwd_no_silu_grad", "g[t] = dr[t] * sg * (1.0 + pre * (1.0 - sg));", "g[t] = dr[t] * sg;"),
+    ("conv_bwd_tap_reversed", "if (t >= 0 && t < L) { v += wd[k] * g[t];", "if (t >= 0 && t < L) { v += wd[K - 1 - k] * g[t];"),
+    ("conv_bwd_dw_shift", "dw[d * K + k] += g[t] * XX(t - H + k);", "dw[d * K + k] += g[t] * XX(t - H + k - 1);"),
     ("ssd_decay_no_delta", "const double a = exp(dl * Ah);", "const double a = exp(Ah);"),
     ("ssd_input_no_delta", "const double in = dl * Bt[n] * xt[p];", "const double in = Bt[n] * xt[p];"),
     ("ssd_h0_ignored", "S[k] = j->h0 ? j->h0[i * N * P + k] : 0.0;", "S[k] = 0.0;"),
