@@ -464,7 +464,23 @@ def time_conv(torch, dev, reps=20):
                      "Gelem_per_s": round(w.elements / (us * 1e-6) / 1e9, 1),
                      "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4), "bytes_per_call": nbytes}
-    del x, y, last
+    # the gradients of the same convolution: read x and dout, write dx
+    dout = torch.randn(x.shape, generator=torch.Generator().manual_seed(3)).to(dev).to(torch.bfloat16)
+    runb = lambda: selscan.conv1d_bwd(x, cw, cb, None, dout=dout)
+    for _ in range(3):
+        runb()
+    torch.cuda.synchronize(dev)
+    e0.record()
+    for _ in range(reps):
+        runb()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 3 * w.elements * 2 + w.rows * 12 + w.dim * 40
+    out["conv1d_bwd"] = {"workload": f"conv1d gradients on {w.name}", "us_per_call": round(us, 2),
+                         "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4), "bytes_per_call": nbytes}
+    del x, y, last, dout
     wd = W.get(W.DECODE)
     pd = W.conv_inputs(W.scaled(wd, seqlen=1))
     st = t(pd["x_prev"])
@@ -485,7 +501,7 @@ def time_conv(torch, dev, reps=20):
                           "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                           "frac_hbm": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
                           "bytes_per_step": nbytes}
-    log(f"[bench] conv1d: {out['conv1d']}; step: {out['conv1d_step']}")
+    log(f"[bench] conv1d: {out['conv1d']}; gradients: {out['conv1d_bwd']}; step: {out['conv1d_step']}")
     return out
 
 

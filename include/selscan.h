@@ -398,6 +398,26 @@ int selscan_conv1d(const void* x, const float* w, const float* bias, const float
                    void* out, float* x_last, const selscan_dims_t* dims, void* stream);
 
 /*
+ * selscan_conv1d_bwd — gradients of selscan_conv1d for an output gradient
+ * dout: the chain rule through its definition (the training face of the
+ * block's convolution; same sources as selscan_conv1d). With
+ * pre[t] = bias + sum_k w[k] xx(t - 3 + k) and g[t] = dout[t] silu'(pre[t]):
+ *   dx[b,d,s]      = sum_k w[d,k] g[s + 3 - k]   (terms with 0 <= s + 3 - k < L)
+ *   dx_prev[b,d,j] = the same sum for s = j - 3 (the inputs before token 0)
+ *   dw[d,k] = sum_{b,t} g[t] xx(t - 3 + k);   dbias[d] = sum_{b,t} g[t]
+ * Arguments (device pointers): x, dout, dx [B, d, L] of dtype; w [d, 4] fp32;
+ * bias [d] fp32 or NULL; x_prev [B, d, 3] fp32 or NULL (zeros); dw [d, 4]
+ * fp32 (output); dbias [d], dx_prev [B, d, 3] fp32 outputs or NULL (not
+ * wanted). dims->dstate is ignored. Outputs must not overlap inputs or each
+ * other. A workspace of 20 bytes per row (more for long rows split into
+ * pieces) is taken with hipMallocAsync on the stream. dw and dbias are sums in
+ * a fixed order: deterministic.
+ */
+int selscan_conv1d_bwd(const void* x, const float* w, const float* bias, const float* x_prev,
+                       const void* dout, void* dx, float* dw, float* dbias, float* dx_prev,
+                       const selscan_dims_t* dims, void* stream);
+
+/*
  * selscan_conv1d_step — one decode step of the convolution, with the three
  * previous inputs of every row in conv_state [B, d, 3] fp32 (oldest first),
  * updated in place (shifted by one, x appended). Same sources as

@@ -578,6 +578,54 @@ int selscan_conv1d(const void* x, const float* w, const float* bias, const float
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }
 
+int selscan_conv1d_bwd(const void* x, const float* w, const float* bias, const float* x_prev,
+                       const void* dout, void* dx, float* dw, float* dbias, float* dx_prev,
+                       const selscan_dims_t* dims, void* stream) {
+    if (!dims) return SELSCAN_ERR_NULL;
+    if (dims->batch < 0 || dims->dim < 0 || dims->seqlen < 0) return SELSCAN_ERR_DIMS;
+    if (dims->dtype != SELSCAN_F32 && dims->dtype != SELSCAN_BF16) return SELSCAN_ERR_DTYPE;
+    int64_t rows, seq, t;
+    if (!mul_ok(dims->batch, dims->dim, &rows) || !mul_ok(rows, dims->seqlen, &seq) ||
+        !mul_ok(seq, 4, &t) || !mul_ok(rows, 12, &t) || !mul_ok(dims->dim, 16, &t))
+        return SELSCAN_ERR_DIMS;
+    const DType dt = dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32;
+    const int32_t nseg = conv_bwd_pieces(dims->batch, dims->seqlen, dims->dim, dt);
+    if (rows * nseg > INT32_MAX) return SELSCAN_ERR_DIMS;
+    if ((seq > 0 && (!x || !dout || !dx)) || (dims->dim > 0 && (!w || !dw))) return SELSCAN_ERR_NULL;
+    for (const void* p : {x, (const void*)w, (const void*)bias, (const void*)x_prev, dout, (const void*)dx,
+                          (const void*)dw, (const void*)dbias, (const void*)dx_prev})
+        if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
+    const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
+    const Span outs[] = {span(dx, seq * es), span(dw, dims->dim * 16), span(dbias, dims->dim * 4),
+                         span(dx_prev, rows * 12)};
+    const Span ins[] = {span(x, seq * es), span(w, dims->dim * 16), span(bias, dims->dim * 4),
+                        span(x_prev, rows * 12), span(dout, seq * es)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span& s : ins)
+            if (overlaps(s, outs[i])) return SELSCAN_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlaps(outs[i], outs[j])) return SELSCAN_ERR_ALIAS;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dims->dim == 0) return SELSCAN_OK;
+    if (rows == 0 || dims->seqlen == 0) {  // no terms
+        if (launch_fill_zero(dw, dims->dim * 4, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        if (dbias && launch_fill_zero(dbias, dims->dim, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        if (dx_prev && launch_fill_zero(dx_prev, rows * 3, st) != hipSuccess) return SELSCAN_ERR_LAUNCH;
+        return SELSCAN_OK;
+    }
+    void* part = nullptr;
+    if (hipMallocAsync(&part, size_t(rows) * nseg * 5 * sizeof(float), st) != hipSuccess || !part) {
+        (void)hipGetLastError();
+        return SELSCAN_ERR_ALLOC;
+    }
+    ConvBwdTensors ct{x, w, bias, x_prev, dout, dx, dw, dbias, dx_prev};
+    const hipError_t e = launch_conv_bwd(ct, dims->batch, dims->seqlen, dims->dim, dt,
+                                         static_cast<float*>(part), nseg, st);
+    (void)hipFreeAsync(part, st);
+    return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
 int selscan_conv1d_step(float* conv_state, const void* x, const float* w, const float* bias,
                         void* out, const selscan_dims_t* dims, void* stream) {
     if (!dims) return SELSCAN_ERR_NULL;

@@ -160,6 +160,180 @@ __global__ __launch_bounds__(256) void conv_step_kernel(float* __restrict__ stat
     state[r * 3 + 2] = xv;
 }
 
+// ---- gradients ----
+//   g[t] = dout[t] silu'(pre[t]),  dx(s) = sum_k w[k] g[s + 3 - k],
+//   dw[k] = sum_t g[t] xx(t - 3 + k),  dbias = sum_t g[t]
+// A workgroup takes a contiguous range of one row's 16-byte vectors (a whole
+// row, or one of nseg pieces of it), 256 consecutive vectors per trip, one
+// per thread. A thread needs the 3 inputs before its vector (lane below, as in
+// the forward) and g of the 3 tokens after it (lane above); lanes at a wave's
+// edge, or next to an idle lane, compute those from memory instead. Its sums
+// for dw and dbias are added over the workgroup in a fixed order into one
+// partial per (row, piece); conv1d_bwd_reduce adds the partials of a channel
+// over the batch and the pieces, in order.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ bias,
+                                                         const float* __restrict__ x_prev,
+                                                         const T* __restrict__ dout,
+                                                         T* __restrict__ dx, float* __restrict__ dx_prev,
+                                                         float* __restrict__ part, int64_t L,
+                                                         int64_t dim, int64_t nvec, int32_t nseg) {
+    constexpr int V = CElem<T>::kPer16;
+    __shared__ float red[5][4];
+    const int64_t r = blockIdx.x / nseg;
+    const int sg = int(blockIdx.x % nseg);
+    const int64_t d = r % dim;
+    const int64_t v_lo = nvec * sg / nseg, v_hi = nvec * (sg + 1) / nseg;
+    const int lane = threadIdx.x % 64;
+    const T* xr = x + r * L;
+    const T* dr = dout + r * L;
+    const float4 wd = *reinterpret_cast<const float4*>(w + d * 4);
+    const float bd = bias ? bias[d] : 0.0f;
+    auto gof = [&](float pre, float dy) {  // dy * silu'(pre)
+        const float s = rcp_hw(1.0f + exp2_hw(-pre * kLog2e));
+        return dy * s * fmaf(pre, 1.0f - s, 1.0f);
+    };
+    float aw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ab = 0.0f;
+    for (int64_t base = v_lo; base < v_hi; base += 256) {  // a uniform trip count
+        const int64_t v = base + threadIdx.x;
+        const bool active = v < v_hi;
+        const int64_t vc = active ? v : v_hi - 1;  // clamped: every lane reads valid memory
+        const int64_t t0 = vc * V;
+        float xs[V + 3], dy[V], gs[V + 3];
+        if constexpr (VEC) {
+            unpack_vec<T>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + t0)), xs + 3);
+            unpack_vec<T>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + t0)), dy);
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const bool ok = t0 + e < L;
+                xs[3 + e] = ok ? to_f32(xr[t0 + e]) : 0.0f;
+                dy[e] = ok ? to_f32(dr[t0 + e]) : 0.0f;
+            }
+        }
+        // the 3 inputs before the vector
+        const float p0 = __shfl_up(xs[V], 1, 64), p1 = __shfl_up(xs[V + 1], 1, 64),
+                    p2 = __shfl_up(xs[V + 2], 1, 64);
+        if (vc == 0) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) xs[e] = x_prev ? x_prev[r * 3 + e] : 0.0f;
+        } else if (lane == 0 || v == v_lo) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) xs[e] = to_f32(xr[t0 - 3 + e]);
+        } else {
+            xs[0] = p0; xs[1] = p1; xs[2] = p2;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            gs[e] = t0 + e < L ? gof(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]), dy[e]) : 0.0f;
+        // g of the 3 tokens after the vector
+        const float q0 = __shfl_down(gs[0], 1, 64), q1 = __shfl_down(gs[1], 1, 64),
+                    q2 = __shfl_down(gs[2], 1, 64);
+        if (vc == nvec - 1) {
+            gs[V] = gs[V + 1] = gs[V + 2] = 0.0f;  // past the end of the row
+        } else if (lane == 63 || v + 1 >= v_hi) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int64_t t = t0 + V + j;
+                float pre = bd;
+                if (t < L) {
+                    float win[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int i = V + j - 3 + k;  // index into xs of token t - 3 + k, minus 3
+                        win[k] = i + 3 < V + 3 ? xs[i + 3] : to_f32(xr[t - 3 + k]);
+                    }
+                    pre = conv4(wd, bd, win[0], win[1], win[2], win[3]);
+                }
+                gs[V + j] = t < L ? gof(pre, to_f32(dr[t])) : 0.0f;
+            }
+        } else {
+            gs[V] = q0; gs[V + 1] = q1; gs[V + 2] = q2;
+        }
+        if (!active) continue;
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            o[e] = fmaf(wd.x, gs[e + 3], fmaf(wd.y, gs[e + 2], fmaf(wd.z, gs[e + 1], wd.w * gs[e])));
+        T* orow = dx + r * L;
+        if constexpr (VEC) {
+            __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            aw[0] = fmaf(gs[e], xs[e], aw[0]);
+            aw[1] = fmaf(gs[e], xs[e + 1], aw[1]);
+            aw[2] = fmaf(gs[e], xs[e + 2], aw[2]);
+            aw[3] = fmaf(gs[e], xs[e + 3], aw[3]);
+            ab += gs[e];
+        }
+        if (vc == 0 && dx_prev) {  // the inputs before token 0: dxx(j - 3) = sum_{k <= j} w[k] g[j - k]
+            dx_prev[r * 3 + 0] = wd.x * gs[0];
+            dx_prev[r * 3 + 1] = fmaf(wd.x, gs[1], wd.y * gs[0]);
+            dx_prev[r * 3 + 2] = fmaf(wd.x, gs[2], fmaf(wd.y, gs[1], wd.z * gs[0]));
+        }
+    }
+    // a fixed tree over the wave's lanes, then the four waves in order
+    float v5[5] = {aw[0], aw[1], aw[2], aw[3], ab};
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v5[i] += __shfl_xor(v5[i], off, 64);
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) red[i][threadIdx.x / 64] = v5[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < 5)
+        part[(r * nseg + sg) * 5 + threadIdx.x] =
+            ((red[threadIdx.x][0] + red[threadIdx.x][1]) + red[threadIdx.x][2]) + red[threadIdx.x][3];
+}
+
+// dw[d,k] = sum over (batch entry, piece) of part[(b dim + d) nseg + piece][k],
+// in order; dbias likewise from entry 4.
+__global__ __launch_bounds__(256) void conv1d_bwd_reduce(const float* __restrict__ part,
+                                                         float* __restrict__ dw, float* dbias,
+                                                         int64_t batch, int64_t dim, int32_t nseg) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= dim * 5) return;
+    const int64_t d = i / 5;
+    const int k = int(i % 5);
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int sg = 0; sg < nseg; ++sg) s += part[((b * dim + d) * nseg + sg) * 5 + k];
+    if (k < 4) dw[d * 4 + k] = s;
+    else if (dbias) dbias[d] = s;
+}
+
+template <typename T>
+hipError_t conv_bwd_t(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim, float* part,
+                      int32_t nseg, hipStream_t st) {
+    constexpr int V = CElem<T>::kPer16;
+    const int64_t rows = batch * dim;
+    const int64_t nvec = (L + V - 1) / V;
+    const dim3 grid(unsigned(rows * nseg)), block(256);
+    const T* x = static_cast<const T*>(t.x);
+    const T* dy = static_cast<const T*>(t.dout);
+    T* dx = static_cast<T*>(t.dx);
+    if (L % V == 0)
+        hipLaunchKernelGGL((conv1d_bwd_kernel<T, true>), grid, block, 0, st, x, t.w, t.bias, t.x_prev,
+                           dy, dx, t.dx_prev, part, L, dim, nvec, nseg);
+    else
+        hipLaunchKernelGGL((conv1d_bwd_kernel<T, false>), grid, block, 0, st, x, t.w, t.bias, t.x_prev,
+                           dy, dx, t.dx_prev, part, L, dim, nvec, nseg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(conv1d_bwd_reduce, dim3(unsigned((dim * 5 + 255) / 256)), dim3(256), 0, st, part,
+                       t.dw, t.dbias, batch, dim, nseg);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t conv_t(const ConvTensors& t, int64_t rows, int64_t L, int64_t dim, hipStream_t st) {
     constexpr int V = CElem<T>::kPer16;
@@ -198,6 +372,23 @@ hipError_t launch_conv(const ConvTensors& t, int64_t rows, int64_t L, int64_t di
                        hipStream_t stream) {
     return dtype == DType::BF16 ? conv_t<bf16_bits>(t, rows, L, dim, stream)
                                 : conv_t<float>(t, rows, L, dim, stream);
+}
+
+int32_t conv_bwd_pieces(int64_t batch, int64_t L, int64_t dim, DType dtype) {
+    const int64_t V = dtype == DType::BF16 ? 8 : 4;
+    const int64_t rows = batch * dim, nvec = (L + V - 1) / V;
+    // enough workgroups to fill the chip (4096), none with under 256 vectors
+    int64_t nseg = rows > 0 ? (4096 + rows - 1) / rows : 1;
+    const int64_t max_by_len = nvec / 256;
+    if (nseg > max_by_len) nseg = max_by_len;
+    if (nseg < 1) nseg = 1;
+    return int32_t(nseg);
+}
+
+hipError_t launch_conv_bwd(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim,
+                           DType dtype, float* part, int32_t nseg, hipStream_t stream) {
+    return dtype == DType::BF16 ? conv_bwd_t<bf16_bits>(t, batch, L, dim, part, nseg, stream)
+                                : conv_bwd_t<float>(t, batch, L, dim, part, nseg, stream);
 }
 
 hipError_t launch_conv_step(const ConvStepTensors& t, int64_t rows, int64_t dim, DType dtype,

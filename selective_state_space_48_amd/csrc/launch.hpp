@@ -180,6 +180,24 @@ struct ConvTensors {
 hipError_t launch_conv(const ConvTensors& t, int64_t rows, int64_t L, int64_t dim, DType dtype,
                        hipStream_t stream);
 
+// Gradients of the convolution + SiLU for dout: dx [rows, L] of the dtype,
+// dw [dim, 4] fp32, dbias [dim] fp32 or null, dx_prev [rows, 3] fp32 or null
+// (the inputs before token 0). part: nseg * rows * 5 floats of workspace.
+struct ConvBwdTensors {
+    const void* x;
+    const float* w;
+    const float* bias;
+    const float* x_prev;
+    const void* dout;
+    void* dx;
+    float* dw;
+    float* dbias;
+    float* dx_prev;
+};
+int32_t conv_bwd_pieces(int64_t batch, int64_t L, int64_t dim, DType dtype);
+hipError_t launch_conv_bwd(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim,
+                           DType dtype, float* part, int32_t nseg, hipStream_t stream);
+
 struct ConvStepTensors {
     float* state;  // [rows, 3], oldest first, updated in place
     const void* x;

@@ -92,6 +92,8 @@ def _load() -> ctypes.CDLL:
     lib.selscan_conv1d.argtypes = [vp, fp, fp, fp, vp, fp, dims_p, vp]
     lib.selscan_conv1d.restype = ctypes.c_int
     lib.selscan_conv1d_step.argtypes = [fp, vp, fp, fp, vp, dims_p, vp]
+    lib.selscan_conv1d_bwd.argtypes = [vp, fp, fp, fp, vp, vp, fp, fp, fp, dims_p, vp]
+    lib.selscan_conv1d_bwd.restype = ctypes.c_int
     lib.selscan_conv1d_step.restype = ctypes.c_int
     lib.selscan_strerror.argtypes = [ctypes.c_int]
     lib.selscan_strerror.restype = ctypes.c_char_p
@@ -430,6 +432,34 @@ def conv1d(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
     _check(lib.selscan_conv1d(_ptr(x), _ptr(w), _ptr(bias), _ptr(x_prev), _ptr(out), _ptr(x_last),
                               ctypes.byref(dims), _stream(dev)))
     return out, x_last
+
+
+def conv1d_bwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+               x_prev: Optional[torch.Tensor] = None, *, dout: torch.Tensor,
+               want_dbias: bool = True, want_dx_prev: bool = True) -> dict:
+    """Gradients of ``conv1d`` (selscan_conv1d_bwd) for ``dout``: a dict with dx
+    (like x), dw [dim, 4] fp32, and dbias [dim], dx_prev [batch, dim, 3] fp32
+    when wanted."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    for t, name, dt, shape in ((x, "x", x.dtype, (batch, dim, L)), (dout, "dout", x.dtype, (batch, dim, L)),
+                               (w, "w", torch.float32, (dim, CONV_WIDTH)), (bias, "bias", torch.float32, (dim,)),
+                               (x_prev, "x_prev", torch.float32, (batch, dim, CONV_WIDTH - 1))):
+        _req(t, name, dt, shape, dev)
+    out = {"dx": torch.empty_like(x), "dw": torch.empty((dim, CONV_WIDTH), dtype=torch.float32, device=dev)}
+    if want_dbias:
+        out["dbias"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    if want_dx_prev:
+        out["dx_prev"] = torch.empty((batch, dim, CONV_WIDTH - 1), dtype=torch.float32, device=dev)
+    dims = Dims(batch, L, dim, 0, _DTYPES[x.dtype])
+    _check(lib.selscan_conv1d_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(x_prev), _ptr(dout), _ptr(out["dx"]),
+                                  _ptr(out["dw"]), _ptr(out.get("dbias")), _ptr(out.get("dx_prev")),
+                                  ctypes.byref(dims), _stream(dev)))
+    return out
 
 
 def conv1d_step(conv_state: torch.Tensor, x: torch.Tensor, w: torch.Tensor,

@@ -22,7 +22,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
-            "selscan_bwd", "selscan_bwd_ex", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
+            "selscan_bwd", "selscan_bwd_ex", "selscan_conv1d_bwd", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
             "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
@@ -451,3 +451,32 @@ def test_ssd_step_argument_checks():
     p[0] = p[4]                                # state == B
     assert ssd_step_call(SD(), p) == S.ERR_ALIAS
     assert ssd_step_call(SD(batch=0)) == S.OK
+
+
+def conv_bwd_call(dims, ptrs=None):
+    p = [P(i) for i in range(9)] if ptrs is None else ptrs
+    return S.lib.selscan_conv1d_bwd(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_conv1d_bwd_argument_checks():
+    assert conv_bwd_call(None) == S.ERR_NULL
+    assert conv_bwd_call(D(batch=-1)) == S.ERR_DIMS
+    assert conv_bwd_call(D(dtype=3)) == S.ERR_DTYPE
+    for idx in (0, 1, 4, 5, 6):                   # x, w, dout, dx, dw are required
+        p = [P(i) for i in range(9)]
+        p[idx] = None
+        assert conv_bwd_call(D(), p) == S.ERR_NULL, idx
+    for idx in range(9):
+        p = [P(i) for i in range(9)]
+        p[idx] = ctypes.c_void_p(BASE + idx * SPAN + 4)
+        assert conv_bwd_call(D(), p) == S.ERR_ALIGN, idx
+    p = [P(i) for i in range(9)]
+    p[5] = p[0]                                    # dx == x
+    assert conv_bwd_call(D(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(9)]
+    p[8] = p[3]                                    # dx_prev == x_prev
+    assert conv_bwd_call(D(), p) == S.ERR_ALIAS
+    p = [P(i) for i in range(9)]
+    p[7] = ctypes.c_void_p(BASE + 6 * SPAN + 16)   # dbias inside dw
+    assert conv_bwd_call(D(), p) == S.ERR_ALIAS
+    assert conv_bwd_call(D(dim=0)) == S.OK         # nothing to do, nothing enqueued

@@ -154,3 +154,54 @@ def test_conv_decode_shape_steps():
         assert oracle.scaled_error(to_np(out), r["out"], r["out_scale"]) <= TOL["bf16"]
         assert np.array_equal(to_np(st), r["conv_state"])
         ref_state = r["conv_state"]
+
+
+CONV_BWD_SHAPES = [
+    # (batch, L, dim, dtype)
+    (1, 1, 1, "f32"),
+    (1, 2, 64, "f32"),       # fewer tokens than the window
+    (2, 17, 65, "bf16"),     # element rows
+    (2, 64, 40, "f32"),      # 16-byte rows
+    (3, 100, 130, "bf16"),
+    (2, 2048, 64, "bf16"),   # several 256-vector trips
+    (1, 40000, 8, "f32"),    # long rows split into pieces
+]
+
+
+@pytest.mark.parametrize("batch,L,dim,dtype", CONV_BWD_SHAPES)
+@pytest.mark.parametrize("with_bias,with_prev", [(True, True), (False, False)])
+def test_conv1d_bwd(batch, L, dim, dtype, with_bias, with_prev):
+    """selscan_conv1d_bwd against the oracle's gradients of the convolution."""
+    p = _inputs(batch, L, dim, dtype, seed=L + dim)
+    dout = np.random.default_rng([L, dim, 3]).standard_normal((batch, dim, L)).astype(np.float32)
+    if dtype == "bf16":
+        dout = W._maybe_bf16(W.get(W.HEADLINE), dout)
+    case(f"conv bwd b{batch} L{L} d{dim} {dtype} bias={with_bias} prev={with_prev}")
+    td = TDT[dtype]
+    g = selscan.conv1d_bwd(dev(p["x"], td), dev(p["w"]), dev(p["bias"]) if with_bias else None,
+                           dev(p["x_prev"]) if with_prev else None, dout=dev(dout, td))
+    torch.cuda.synchronize()
+    ref = oracle.conv1d_bwd(p["x"], p["w"], p["bias"] if with_bias else None,
+                            p["x_prev"] if with_prev else None, dout=dout)
+    errs = {k: oracle.scaled_error(to_np(g[k]), ref[k], ref[k + "_scale"])
+            for k in ("dx", "dw", "dbias", "dx_prev")}
+    print(f"[parity] conv bwd b{batch} L{L} d{dim} {dtype}: " +
+          " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= TOL[dtype] for v in errs.values()), errs
+
+
+def test_conv1d_bwd_deterministic_and_empty():
+    p = _inputs(2, 500, 96, "bf16", seed=4)
+    dout = dev(np.random.default_rng(5).standard_normal((2, 96, 500)), TDT["bf16"])
+    args = (dev(p["x"], TDT["bf16"]), dev(p["w"]), dev(p["bias"]), dev(p["x_prev"]))
+    case("conv bwd determinism")
+    g1 = selscan.conv1d_bwd(*args, dout=dout)
+    g2 = selscan.conv1d_bwd(*args, dout=dout)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+    case("conv bwd L = 0")
+    x = torch.empty((2, 8, 0), device="cuda")
+    g = selscan.conv1d_bwd(x, torch.ones((8, 4), device="cuda"), dout=x.clone())
+    torch.cuda.synchronize()
+    assert torch.all(g["dw"] == 0) and torch.all(g["dbias"] == 0) and torch.all(g["dx_prev"] == 0)
