@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (automatic plan). The oracle runs on sampled rows where all
-rows would take it minutes, and on every row of the long-sequence workload.
-pytest -m gpu."""
+rows would take it minutes, and on every row of the long-sequence workload,
+the headline backward (from the forward's checkpoints) and the convolution's
+gradients. pytest -m gpu."""
 import numpy as np
 import pytest
 import torch
@@ -107,3 +108,103 @@ def test_full_decode_steps(dtype):
     print(f"[parity] decode {dtype} 64 steps: err_y={worst[0]:.3e} err_state={worst[1]:.3e}",
           flush=True)
     assert worst[0] <= TOL[dtype] and worst[1] <= TOL[dtype]
+
+
+def test_full_fused_conv_sampled():
+    """The headline-shaped layer with the block's convolution fused in front
+    (selscan_fwd_ex's conv_w), sampled rows against the oracle's convolution
+    then scan (the scales of the composition as in test_fused_conv_gpu)."""
+    w = W.get(W.HEADLINE)
+    print("[case] full fused conv: generating", flush=True)
+    inp = W.fwd_inputs(w)
+    c = W.conv_inputs(w)
+    td = TDT[w.dtype]
+    print("[case] full fused conv: GPU", flush=True)
+    y, hs = selscan.fwd(dev(c["x"], td), dev(inp["delta"], td), dev(inp["A"]), dev(inp["B"], td),
+                        dev(inp["C"], td), D=dev(inp["D"]), z=dev(inp["z"], td),
+                        dt_bias=dev(inp["dt_bias"]), conv_w=dev(c["w"]), conv_b=dev(c["bias"]),
+                        conv_x_prev=dev(c["x_prev"]))
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 96, seed=3)
+    print(f"[case] full fused conv: oracle on {len(rows)} rows", flush=True)
+    b_idx, d_idx = rows // w.dim, rows % w.dim
+    conv = oracle.conv1d(c["x"][b_idx, d_idx][None], c["w"][d_idx], c["bias"][d_idx], c["x_prev"][b_idx, d_idx][None])
+    xs = inp["x"].copy()
+    xm = np.zeros_like(inp["x"])
+    xs[b_idx, d_idx] = conv["out"][0]
+    xm[b_idx, d_idx] = np.abs(conv["out"][0]) + 1.1 * conv["out_scale"][0]
+    ref = oracle_fwd(dict(inp, x=xs), use_z=True, rows=rows)
+    mag = oracle_fwd(dict(inp, x=xm), use_z=True, rows=rows)
+    yr, hr = to_np(y).reshape(w.rows, w.seqlen)[rows], to_np(hs).reshape(w.rows, w.dstate)[rows]
+    ey = oracle.scaled_error(yr, ref["y"], mag["y_scale"])
+    es = oracle.scaled_error(hr, ref["last_state"], mag["state_scale"])
+    print(f"[parity] full fused conv: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    assert ey <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_full_backward_from_forward_checkpoints():
+    """The headline-shaped layer's backward given the forward's checkpoints
+    (the training path bench.py times), every gradient against the oracle."""
+    w = W.get(W.HEADLINE)
+    print("[case] full bwd from checkpoints: generating", flush=True)
+    inp = W.fwd_inputs(w)
+    dy = W._maybe_bf16(w, np.random.default_rng([8, 99]).standard_normal((w.batch, w.dim, w.seqlen)).astype(np.float32))
+    td = TDT[w.dtype]
+    args = (dev(inp["x"], td), dev(inp["delta"], td), dev(inp["A"]), dev(inp["B"], td), dev(inp["C"], td))
+    kw = dict(D=dev(inp["D"]), z=dev(inp["z"], td), dt_bias=dev(inp["dt_bias"]))
+    ck = torch.empty(selscan.ckpt_shape(w.batch, w.dim, w.seqlen), device="cuda")
+    print("[case] full bwd from checkpoints: GPU", flush=True)
+    selscan.fwd(*args, **kw, ckpt=ck)
+    g = selscan.bwd(*args, **kw, dy=dev(dy, td), ckpt=ck)
+    torch.cuda.synchronize()
+    print("[case] full bwd from checkpoints: oracle", flush=True)
+    ref = oracle.bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                     inp["dt_bias"], dy=dy)
+    errs = {k: oracle.scaled_error(to_np(g[k]), ref[k], ref[k + "_scale"])
+            for k in ("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddt_bias")}
+    print("[parity] full bwd from checkpoints: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= TOL[w.dtype] for v in errs.values()), errs
+
+
+def test_full_conv_gradients():
+    """The convolution's gradients on the headline-shaped tensor, every output
+    against the oracle."""
+    w = W.get(W.HEADLINE)
+    print("[case] full conv gradients: generating", flush=True)
+    c = W.conv_inputs(w)
+    dout = W._maybe_bf16(w, np.random.default_rng([9, 99]).standard_normal((w.batch, w.dim, w.seqlen)).astype(np.float32))
+    td = TDT[w.dtype]
+    print("[case] full conv gradients: GPU", flush=True)
+    g = selscan.conv1d_bwd(dev(c["x"], td), dev(c["w"]), dev(c["bias"]), dev(c["x_prev"]), dout=dev(dout, td))
+    torch.cuda.synchronize()
+    print("[case] full conv gradients: oracle", flush=True)
+    ref = oracle.conv1d_bwd(c["x"], c["w"], c["bias"], c["x_prev"], dout=dout)
+    errs = {k: oracle.scaled_error(to_np(g[k]), ref[k], ref[k + "_scale"]) for k in ("dx", "dw", "dbias", "dx_prev")}
+    print("[parity] full conv gradients: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= TOL[w.dtype] for v in errs.values()), errs
+
+
+def test_full_ssd_decode_sampled():
+    """The SSD decode step at the benchmark's shape (256 sequences, 80 heads
+    of 64, state 128): two steps on the full state, sampled batch entries
+    against the oracle's step from the same state."""
+    s = W.SSD_DECODE
+    Bb, H, P, N = s["batch"], s["heads"], s["headdim"], s["dstate"]
+    p = W.ssd_inputs(Bb, 2, H, P, N, s["seed"])
+    st0 = (np.random.default_rng(7).standard_normal((Bb, H, N, P)) * 0.3).astype(np.float32)
+    st = dev(st0)
+    bf = TDT["bf16"]
+    sample = np.array([0, 77, 128, 255])
+    prev = st0[sample].astype(np.float64)
+    for t in range(2):
+        y = selscan.ssd_step(st, dev(p["x"][:, t], bf), dev(p["delta"][:, t], bf), dev(p["A"]),
+                             dev(p["B"][:, t], bf), dev(p["C"][:, t], bf), D=dev(p["D"]), dt_bias=dev(p["dt_bias"]))
+        torch.cuda.synchronize()
+        r = oracle.ssd_step(prev, p["x"][sample, t], p["delta"][sample, t], p["A"], p["B"][sample, t],
+                            p["C"][sample, t], p["D"], p["dt_bias"])
+        cur = to_np(st)[sample]
+        ey = oracle.scaled_error(to_np(y)[sample], r["y"], r["y_scale"])
+        es = oracle.scaled_error(cur, r["state"], r["state_scale"])
+        print(f"[parity] full ssd decode step {t}: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+        assert ey <= TOL["bf16"] and es <= TOL["f32"]
+        prev = cur
