@@ -391,6 +391,18 @@ hipError_t launch_conv_bwd(const ConvBwdTensors& t, int64_t batch, int64_t L, in
                                 : conv_bwd_t<float>(t, batch, L, dim, part, nseg, stream);
 }
 
+hipError_t launch_conv_last(const void* x, const float* x_prev, float* x_last, int64_t rows,
+                            int64_t L, DType dtype, hipStream_t stream) {
+    const dim3 grid(unsigned((rows + 255) / 256)), block(256);
+    if (dtype == DType::BF16)
+        hipLaunchKernelGGL((conv_last_kernel<bf16_bits>), grid, block, 0, stream,
+                           static_cast<const bf16_bits*>(x), x_prev, x_last, rows, L);
+    else
+        hipLaunchKernelGGL((conv_last_kernel<float>), grid, block, 0, stream,
+                           static_cast<const float*>(x), x_prev, x_last, rows, L);
+    return hipGetLastError();
+}
+
 hipError_t launch_conv_step(const ConvStepTensors& t, int64_t rows, int64_t dim, DType dtype,
                             hipStream_t stream) {
     return dtype == DType::BF16 ? conv_step_t<bf16_bits>(t, rows, dim, stream)

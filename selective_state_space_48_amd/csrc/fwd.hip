@@ -730,20 +730,6 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // Padded token count of the packed B/C: whole chunks.
 int64_t padded_len(int64_t L) { return (L + kChunk - 1) / kChunk * kChunk; }
 
-// The convolution's last three inputs of every row (oldest first): the
-// x_prev of a call that continues the sequence. One thread per row, entries
-// in order, so x_last may be x_prev itself (entry k reads entry k + L >= k).
-template <typename T>
-__global__ __launch_bounds__(256) void conv_last_kernel(const T* __restrict__ x, const float* x_prev,
-                                                        float* x_last, int64_t rows, int64_t L) {
-    const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (r >= rows) return;
-    for (int k = 0; k < 3; ++k) {
-        const int64_t s = L - 3 + k;
-        x_last[r * 3 + k] = s >= 0 ? to_f32(x[r * L + s]) : (x_prev ? x_prev[r * 3 + 3 + s] : 0.0f);
-    }
-}
-
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (i < n) p[i] = 0.0f;
@@ -805,15 +791,7 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     // the convolution's last inputs, after the pass that reads x_prev
     auto conv_last = [&]() -> hipError_t {
         if (!t.conv_w || !t.conv_x_last) return hipSuccess;
-        const int64_t rows = s.batch * s.dim;
-        const dim3 grid(unsigned((rows + 255) / 256)), block(256);
-        if (s.dtype == DType::BF16)
-            hipLaunchKernelGGL((conv_last_kernel<bf16_bits>), grid, block, 0, stream,
-                               static_cast<const bf16_bits*>(t.x), t.conv_x_prev, t.conv_x_last, rows, s.L);
-        else
-            hipLaunchKernelGGL((conv_last_kernel<float>), grid, block, 0, stream,
-                               static_cast<const float*>(t.x), t.conv_x_prev, t.conv_x_last, rows, s.L);
-        return hipGetLastError();
+        return launch_conv_last(t.x, t.conv_x_prev, t.conv_x_last, s.batch * s.dim, s.L, s.dtype, stream);
     };
     if (p.segments <= 1) {
         k.h0 = t.h0;

@@ -198,6 +198,11 @@ int32_t conv_bwd_pieces(int64_t batch, int64_t L, int64_t dim, DType dtype);
 hipError_t launch_conv_bwd(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim,
                            DType dtype, float* part, int32_t nseg, hipStream_t stream);
 
+// x_last[r] = the last three entries of x_prev[r] ++ x[r] (x: [rows, L] of the
+// dtype; x_prev, x_last: [rows, 3] fp32, x_prev may be null, x_last may be x_prev).
+hipError_t launch_conv_last(const void* x, const float* x_prev, float* x_last, int64_t rows,
+                            int64_t L, DType dtype, hipStream_t stream);
+
 struct ConvStepTensors {
     float* state;  // [rows, 3], oldest first, updated in place
     const void* x;
