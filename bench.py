@@ -620,8 +620,9 @@ def main():
                     help="run just one workload (for profiling); copy = counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the selective scan here "
-              "is built and measured on a single MI355X; see DESIGN.md for how it would shard.",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}). Across GPUs the rows "
+              "would be split, or a long sequence's segments, each GPU passing on its segments' "
+              "end states and summed step sizes for the carries; that is not measured here.",
               file=sys.stderr)
         sys.exit(2)
 
