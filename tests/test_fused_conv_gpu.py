@@ -147,3 +147,36 @@ def test_fused_conv_empty_sequence():
                 conv_x_prev=prev, conv_x_last=last)
     torch.cuda.synchronize()
     assert torch.equal(last, prev)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_prefill_then_decode(dtype):
+    """The block's inference path end to end: a prefill with the convolution
+    fused (its last inputs and the scan's last state out), then decode steps
+    with the convolution's step and the scan's step from those; the decoded
+    outputs against the oracle's convolution then scan over the whole
+    sequence (the decode step takes the step size with the channel bias
+    already added)."""
+    batch, L, T, dim = 2, 150, 6, 128
+    p = _inputs(batch, L + T, dim, dtype)
+    td = TDT[dtype]
+    case(f"block prefill {L} then {T} decode steps {dtype}")
+    cut = lambda a: np.ascontiguousarray(a[..., :L])
+    cst = torch.empty((batch, dim, 3), device="cuda")
+    _, st = selscan.fwd(dev(cut(p["x"]), td), dev(cut(p["delta"]), td), dev(p["A"]), dev(cut(p["B"]), td),
+                        dev(cut(p["C"]), td), D=dev(p["D"]), z=dev(cut(p["z"]), td), dt_bias=dev(p["dt_bias"]),
+                        conv_w=dev(p["cw"]), conv_b=dev(p["cb"]), conv_x_prev=dev(p["x_prev"]),
+                        conv_x_last=cst)
+    ys = []
+    for t in range(L, L + T):
+        xa = selscan.conv1d_step(cst, dev(p["x"][..., t], td), dev(p["cw"]), dev(p["cb"]))
+        dl = (p["delta"][..., t] + p["dt_bias"][None]).astype(np.float32)
+        ys.append(to_np(selscan.step(st, xa, dev(dl, td), dev(p["A"]), dev(p["B"][..., t], td),
+                                     dev(p["C"][..., t], td), D=dev(p["D"]), z=dev(p["z"][..., t], td))))
+    torch.cuda.synchronize()
+    ref = _ref(p)
+    ey = oracle.scaled_error(np.stack(ys, -1), ref["y"][..., L:], ref["y_scale"][..., L:])
+    es = oracle.scaled_error(to_np(st), ref["last_state"], ref["state_scale"])
+    print(f"[parity] block prefill+decode {dtype}: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    assert np.array_equal(to_np(cst), ref["x_last"])
