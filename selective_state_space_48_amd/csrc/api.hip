@@ -589,8 +589,9 @@ int selscan_conv1d_bwd(const void* x, const float* w, const float* bias, const f
         !mul_ok(seq, 4, &t) || !mul_ok(rows, 12, &t) || !mul_ok(dims->dim, 16, &t))
         return SELSCAN_ERR_DIMS;
     const DType dt = dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32;
-    const int32_t nseg = conv_bwd_pieces(dims->batch, dims->seqlen, dims->dim, dt);
-    if (rows * nseg > INT32_MAX) return SELSCAN_ERR_DIMS;
+    const ConvBwdPlan plan = conv_bwd_plan(dims->batch, dims->seqlen, dims->dim, dt);
+    const int64_t nparts = int64_t(plan.bgroups) * plan.pieces;
+    if (dims->dim * nparts > INT32_MAX) return SELSCAN_ERR_DIMS;
     if ((seq > 0 && (!x || !dout || !dx)) || (dims->dim > 0 && (!w || !dw))) return SELSCAN_ERR_NULL;
     for (const void* p : {x, (const void*)w, (const void*)bias, (const void*)x_prev, dout, (const void*)dx,
                           (const void*)dw, (const void*)dbias, (const void*)dx_prev})
@@ -615,13 +616,13 @@ int selscan_conv1d_bwd(const void* x, const float* w, const float* bias, const f
         return SELSCAN_OK;
     }
     void* part = nullptr;
-    if (hipMallocAsync(&part, size_t(rows) * nseg * 5 * sizeof(float), st) != hipSuccess || !part) {
+    if (hipMallocAsync(&part, size_t(dims->dim) * nparts * 5 * sizeof(float), st) != hipSuccess || !part) {
         (void)hipGetLastError();
         return SELSCAN_ERR_ALLOC;
     }
     ConvBwdTensors ct{x, w, bias, x_prev, dout, dx, dw, dbias, dx_prev};
     const hipError_t e = launch_conv_bwd(ct, dims->batch, dims->seqlen, dims->dim, dt,
-                                         static_cast<float*>(part), nseg, st);
+                                         static_cast<float*>(part), plan, st);
     (void)hipFreeAsync(part, st);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
 }

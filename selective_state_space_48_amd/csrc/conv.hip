@@ -163,14 +163,85 @@ __global__ __launch_bounds__(256) void conv_step_kernel(float* __restrict__ stat
 // ---- gradients ----
 //   g[t] = dout[t] silu'(pre[t]),  dx(s) = sum_k w[k] g[s + 3 - k],
 //   dw[k] = sum_t g[t] xx(t - 3 + k),  dbias = sum_t g[t]
-// A workgroup takes a contiguous range of one row's 16-byte vectors (a whole
-// row, or one of nseg pieces of it), 256 consecutive vectors per trip, one
-// per thread. A thread needs the 3 inputs before its vector (lane below, as in
-// the forward) and g of the 3 tokens after it (lane above); lanes at a wave's
-// edge, or next to an idle lane, compute those from memory instead. Its sums
-// for dw and dbias are added over the workgroup in a fixed order into one
-// partial per (row, piece); conv1d_bwd_reduce adds the partials of a channel
-// over the batch and the pieces, in order.
+// A workgroup takes one channel d, a group of batch entries and a piece of
+// the sequence (a contiguous range of 16-byte vectors), and walks the rows of
+// its batch entries 256 vectors per trip, one vector per thread, with the
+// next trip's loads in flight while it computes the current one. Each thread
+// loads, beside its vector, the 4 inputs before it and the 4 inputs and
+// output gradients after it (cache hits: the neighbouring lanes' vectors),
+// so that it forms g of the 3 tokens after its vector itself; no lane waits
+// for another. The thread's sums for dw and dbias, added over its trips in
+// order, then over the workgroup in a fixed order, give one partial per
+// (channel, batch group, piece); conv1d_bwd_reduce adds a channel's partials
+// in order.
+template <typename T> struct Halo;  // 4 tokens
+template <> struct Halo<float> { typedef u32x4 type; };
+template <> struct Halo<bf16_bits> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
+
+template <typename T>
+__device__ __forceinline__ void unpack_halo(const typename Halo<T>::type& v, float* o) {
+    if constexpr (sizeof(T) == 4) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    } else {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    }
+}
+
+// The raw loads of one trip of one thread (t0 = its vector's first token).
+// VEC: x and dout at t0 .. t0+V-1, x at t0-4 .. t0-1 (zero for the row's
+// first vector), x and dout at t0+V .. t0+V+3 (zero for its last vector).
+// Otherwise element by element: x at t0-3 .. t0+V+2, dout at t0 .. t0+V+2,
+// zero outside the row.
+template <typename T, bool VEC> struct Trip;
+template <typename T> struct Trip<T, true> {
+    static constexpr int V = CElem<T>::kPer16;
+    u32x4 x, dy;
+    typename Halo<T>::type xb, xa, da;
+    __device__ __forceinline__ void load(const T* xr, const T* dr, int64_t t0, int64_t, bool first,
+                                         bool last) {
+        typedef typename Halo<T>::type H;
+        x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + t0));
+        dy = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + t0));
+        xb = first ? H{} : *reinterpret_cast<const H*>(xr + t0 - 4);
+        xa = last ? H{} : *reinterpret_cast<const H*>(xr + t0 + V);
+        da = last ? H{} : *reinterpret_cast<const H*>(dr + t0 + V);
+    }
+    __device__ __forceinline__ void unpack(float* xs, float* dys) const {
+        float b4[4];
+        unpack_halo<T>(xb, b4);
+        xs[0] = b4[1]; xs[1] = b4[2]; xs[2] = b4[3];
+        unpack_vec<T>(x, xs + 3);
+        unpack_vec<T>(dy, dys);
+        float a4[4];
+        unpack_halo<T>(xa, a4);
+        xs[V + 3] = a4[0]; xs[V + 4] = a4[1]; xs[V + 5] = a4[2];
+        unpack_halo<T>(da, a4);
+        dys[V] = a4[0]; dys[V + 1] = a4[1]; dys[V + 2] = a4[2];
+    }
+};
+template <typename T> struct Trip<T, false> {
+    static constexpr int V = CElem<T>::kPer16;
+    T x[V + 6], dy[V + 3];
+    __device__ __forceinline__ void load(const T* xr, const T* dr, int64_t t0, int64_t L, bool, bool) {
+#pragma unroll
+        for (int i = 0; i < V + 6; ++i) {
+            const int64_t t = t0 - 3 + i;
+            x[i] = t >= 0 && t < L ? xr[t] : T{};
+        }
+#pragma unroll
+        for (int i = 0; i < V + 3; ++i) dy[i] = t0 + i < L ? dr[t0 + i] : T{};
+    }
+    __device__ __forceinline__ void unpack(float* xs, float* dys) const {
+#pragma unroll
+        for (int i = 0; i < V + 6; ++i) xs[i] = to_f32(x[i]);
+#pragma unroll
+        for (int i = 0; i < V + 3; ++i) dys[i] = to_f32(dy[i]);
+    }
+};
+
+// Grid: dim * bgroups * pieces workgroups of 256 threads, blockIdx =
+// (d * bgroups + bg) * pieces + piece. part: 5 floats per workgroup.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x,
                                                          const float* __restrict__ w,
@@ -178,108 +249,89 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
                                                          const float* __restrict__ x_prev,
                                                          const T* __restrict__ dout,
                                                          T* __restrict__ dx, float* __restrict__ dx_prev,
-                                                         float* __restrict__ part, int64_t L,
-                                                         int64_t dim, int64_t nvec, int32_t nseg) {
+                                                         float* __restrict__ part, int64_t batch,
+                                                         int64_t L, int64_t dim, int64_t nvec,
+                                                         int32_t bgroups, int32_t pieces) {
     constexpr int V = CElem<T>::kPer16;
     __shared__ float red[5][4];
-    const int64_t r = blockIdx.x / nseg;
-    const int sg = int(blockIdx.x % nseg);
-    const int64_t d = r % dim;
-    const int64_t v_lo = nvec * sg / nseg, v_hi = nvec * (sg + 1) / nseg;
-    const int lane = threadIdx.x % 64;
-    const T* xr = x + r * L;
-    const T* dr = dout + r * L;
+    const int64_t d = blockIdx.x / (int64_t(bgroups) * pieces);
+    const int bg = int(blockIdx.x / pieces % bgroups);
+    const int sg = int(blockIdx.x % pieces);
+    const int64_t b_lo = batch * bg / bgroups, b_hi = batch * (bg + 1) / bgroups;
+    const int64_t v_lo = nvec * sg / pieces, v_hi = nvec * (sg + 1) / pieces;
+    const int64_t per_row = (v_hi - v_lo + 255) / 256;  // trips per row, uniform over the workgroup
+    const int64_t trips = (b_hi - b_lo) * per_row;
     const float4 wd = *reinterpret_cast<const float4*>(w + d * 4);
     const float bd = bias ? bias[d] : 0.0f;
     auto gof = [&](float pre, float dy) {  // dy * silu'(pre)
         const float s = rcp_hw(1.0f + exp2_hw(-pre * kLog2e));
         return dy * s * fmaf(pre, 1.0f - s, 1.0f);
     };
+    // trip i: row (b_lo + i / per_row) * dim + d, vector v_lo + (i % per_row) * 256 + thread
+    auto where = [&](int64_t i, int64_t& r, int64_t& v, int64_t& vc) {
+        r = (b_lo + i / per_row) * dim + d;
+        v = v_lo + (i % per_row) * 256 + threadIdx.x;
+        vc = v < v_hi ? v : v_hi - 1;  // clamped: every lane reads valid memory
+    };
     float aw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ab = 0.0f;
-    for (int64_t base = v_lo; base < v_hi; base += 256) {  // a uniform trip count
-        const int64_t v = base + threadIdx.x;
-        const bool active = v < v_hi;
-        const int64_t vc = active ? v : v_hi - 1;  // clamped: every lane reads valid memory
-        const int64_t t0 = vc * V;
-        float xs[V + 3], dy[V], gs[V + 3];
-        if constexpr (VEC) {
-            unpack_vec<T>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + t0)), xs + 3);
-            unpack_vec<T>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + t0)), dy);
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const bool ok = t0 + e < L;
-                xs[3 + e] = ok ? to_f32(xr[t0 + e]) : 0.0f;
-                dy[e] = ok ? to_f32(dr[t0 + e]) : 0.0f;
-            }
+    Trip<T, VEC> cur;
+    if (trips > 0) {
+        int64_t r, v, vc;
+        where(0, r, v, vc);
+        cur.load(x + r * L, dout + r * L, vc * V, L, vc == 0, vc == nvec - 1);
+    }
+    for (int64_t i = 0; i < trips; ++i) {
+        int64_t r, v, vc;
+        where(i, r, v, vc);
+        Trip<T, VEC> nxt;
+        if (i + 1 < trips) {
+            int64_t r1, v1, vc1;
+            where(i + 1, r1, v1, vc1);
+            nxt.load(x + r1 * L, dout + r1 * L, vc1 * V, L, vc1 == 0, vc1 == nvec - 1);
         }
-        // the 3 inputs before the vector
-        const float p0 = __shfl_up(xs[V], 1, 64), p1 = __shfl_up(xs[V + 1], 1, 64),
-                    p2 = __shfl_up(xs[V + 2], 1, 64);
+        const int64_t t0 = vc * V;
+        float xs[V + 6], dys[V + 3], gs[V + 3];
+        cur.unpack(xs, dys);
         if (vc == 0) {
 #pragma unroll
             for (int e = 0; e < 3; ++e) xs[e] = x_prev ? x_prev[r * 3 + e] : 0.0f;
-        } else if (lane == 0 || v == v_lo) {
-#pragma unroll
-            for (int e = 0; e < 3; ++e) xs[e] = to_f32(xr[t0 - 3 + e]);
-        } else {
-            xs[0] = p0; xs[1] = p1; xs[2] = p2;
         }
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            gs[e] = t0 + e < L ? gof(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]), dy[e]) : 0.0f;
-        // g of the 3 tokens after the vector
-        const float q0 = __shfl_down(gs[0], 1, 64), q1 = __shfl_down(gs[1], 1, 64),
-                    q2 = __shfl_down(gs[2], 1, 64);
-        if (vc == nvec - 1) {
-            gs[V] = gs[V + 1] = gs[V + 2] = 0.0f;  // past the end of the row
-        } else if (lane == 63 || v + 1 >= v_hi) {
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const int64_t t = t0 + V + j;
-                float pre = bd;
-                if (t < L) {
-                    float win[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int i = V + j - 3 + k;  // index into xs of token t - 3 + k, minus 3
-                        win[k] = i + 3 < V + 3 ? xs[i + 3] : to_f32(xr[t - 3 + k]);
-                    }
-                    pre = conv4(wd, bd, win[0], win[1], win[2], win[3]);
-                }
-                gs[V + j] = t < L ? gof(pre, to_f32(dr[t])) : 0.0f;
-            }
-        } else {
-            gs[V] = q0; gs[V + 1] = q1; gs[V + 2] = q2;
+        for (int e = 0; e < V + 3; ++e) {
+            const bool in_row = VEC ? (e < V || vc != nvec - 1) : t0 + e < L;
+            gs[e] = in_row ? gof(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]), dys[e]) : 0.0f;
         }
-        if (!active) continue;
-        float o[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e)
-            o[e] = fmaf(wd.x, gs[e + 3], fmaf(wd.y, gs[e + 2], fmaf(wd.z, gs[e + 1], wd.w * gs[e])));
-        T* orow = dx + r * L;
-        if constexpr (VEC) {
-            __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
-        } else {
+        if (v < v_hi) {
+            float o[V];
 #pragma unroll
             for (int e = 0; e < V; ++e)
-                if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
-        }
+                o[e] = fmaf(wd.x, gs[e + 3], fmaf(wd.y, gs[e + 2], fmaf(wd.z, gs[e + 1], wd.w * gs[e])));
+            T* orow = dx + r * L;
+            if constexpr (VEC) {
+                __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
+            } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            aw[0] = fmaf(gs[e], xs[e], aw[0]);
-            aw[1] = fmaf(gs[e], xs[e + 1], aw[1]);
-            aw[2] = fmaf(gs[e], xs[e + 2], aw[2]);
-            aw[3] = fmaf(gs[e], xs[e + 3], aw[3]);
-            ab += gs[e];
+                for (int e = 0; e < V; ++e)
+                    if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                aw[0] = fmaf(gs[e], xs[e], aw[0]);
+                aw[1] = fmaf(gs[e], xs[e + 1], aw[1]);
+                aw[2] = fmaf(gs[e], xs[e + 2], aw[2]);
+                aw[3] = fmaf(gs[e], xs[e + 3], aw[3]);
+                ab += gs[e];
+            }
+            if (vc == 0 && dx_prev) {  // the inputs before token 0: dxx(j - 3) = sum_{k <= j} w[k] g[j - k]
+                dx_prev[r * 3 + 0] = wd.x * gs[0];
+                dx_prev[r * 3 + 1] = fmaf(wd.x, gs[1], wd.y * gs[0]);
+                dx_prev[r * 3 + 2] = fmaf(wd.x, gs[2], fmaf(wd.y, gs[1], wd.z * gs[0]));
+            }
         }
-        if (vc == 0 && dx_prev) {  // the inputs before token 0: dxx(j - 3) = sum_{k <= j} w[k] g[j - k]
-            dx_prev[r * 3 + 0] = wd.x * gs[0];
-            dx_prev[r * 3 + 1] = fmaf(wd.x, gs[1], wd.y * gs[0]);
-            dx_prev[r * 3 + 2] = fmaf(wd.x, gs[2], fmaf(wd.y, gs[1], wd.z * gs[0]));
-        }
+        cur = nxt;
     }
     // a fixed tree over the wave's lanes, then the four waves in order
+    const int lane = threadIdx.x % 64;
     float v5[5] = {aw[0], aw[1], aw[2], aw[3], ab};
 #pragma unroll
     for (int i = 0; i < 5; ++i)
@@ -291,46 +343,44 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
     }
     __syncthreads();
     if (threadIdx.x < 5)
-        part[(r * nseg + sg) * 5 + threadIdx.x] =
+        part[int64_t(blockIdx.x) * 5 + threadIdx.x] =
             ((red[threadIdx.x][0] + red[threadIdx.x][1]) + red[threadIdx.x][2]) + red[threadIdx.x][3];
 }
 
-// dw[d,k] = sum over (batch entry, piece) of part[(b dim + d) nseg + piece][k],
-// in order; dbias likewise from entry 4.
+// dw[d,k] = sum over the channel's nparts partials part[d nparts + j][k], in
+// order of j; dbias likewise from entry 4.
 __global__ __launch_bounds__(256) void conv1d_bwd_reduce(const float* __restrict__ part,
                                                          float* __restrict__ dw, float* dbias,
-                                                         int64_t batch, int64_t dim, int32_t nseg) {
+                                                         int64_t dim, int32_t nparts) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (i >= dim * 5) return;
     const int64_t d = i / 5;
     const int k = int(i % 5);
     float s = 0.0f;
-    for (int64_t b = 0; b < batch; ++b)
-        for (int sg = 0; sg < nseg; ++sg) s += part[((b * dim + d) * nseg + sg) * 5 + k];
+    for (int j = 0; j < nparts; ++j) s += part[(d * nparts + j) * 5 + k];
     if (k < 4) dw[d * 4 + k] = s;
     else if (dbias) dbias[d] = s;
 }
 
 template <typename T>
 hipError_t conv_bwd_t(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim, float* part,
-                      int32_t nseg, hipStream_t st) {
+                      ConvBwdPlan plan, hipStream_t st) {
     constexpr int V = CElem<T>::kPer16;
-    const int64_t rows = batch * dim;
     const int64_t nvec = (L + V - 1) / V;
-    const dim3 grid(unsigned(rows * nseg)), block(256);
+    const dim3 grid(unsigned(dim * plan.bgroups * plan.pieces)), block(256);
     const T* x = static_cast<const T*>(t.x);
     const T* dy = static_cast<const T*>(t.dout);
     T* dx = static_cast<T*>(t.dx);
     if (L % V == 0)
         hipLaunchKernelGGL((conv1d_bwd_kernel<T, true>), grid, block, 0, st, x, t.w, t.bias, t.x_prev,
-                           dy, dx, t.dx_prev, part, L, dim, nvec, nseg);
+                           dy, dx, t.dx_prev, part, batch, L, dim, nvec, plan.bgroups, plan.pieces);
     else
         hipLaunchKernelGGL((conv1d_bwd_kernel<T, false>), grid, block, 0, st, x, t.w, t.bias, t.x_prev,
-                           dy, dx, t.dx_prev, part, L, dim, nvec, nseg);
+                           dy, dx, t.dx_prev, part, batch, L, dim, nvec, plan.bgroups, plan.pieces);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(conv1d_bwd_reduce, dim3(unsigned((dim * 5 + 255) / 256)), dim3(256), 0, st, part,
-                       t.dw, t.dbias, batch, dim, nseg);
+                       t.dw, t.dbias, dim, plan.bgroups * plan.pieces);
     return hipGetLastError();
 }
 
@@ -374,21 +424,26 @@ hipError_t launch_conv(const ConvTensors& t, int64_t rows, int64_t L, int64_t di
                                 : conv_t<float>(t, rows, L, dim, stream);
 }
 
-int32_t conv_bwd_pieces(int64_t batch, int64_t L, int64_t dim, DType dtype) {
+ConvBwdPlan conv_bwd_plan(int64_t batch, int64_t L, int64_t dim, DType dtype) {
     const int64_t V = dtype == DType::BF16 ? 8 : 4;
-    const int64_t rows = batch * dim, nvec = (L + V - 1) / V;
-    // enough workgroups to fill the chip (4096), none with under 256 vectors
-    int64_t nseg = rows > 0 ? (4096 + rows - 1) / rows : 1;
-    const int64_t max_by_len = nvec / 256;
-    if (nseg > max_by_len) nseg = max_by_len;
-    if (nseg < 1) nseg = 1;
-    return int32_t(nseg);
+    const int64_t nvec = (L + V - 1) / V;
+    // Workgroups to fill the chip (kFill): batch groups first (a workgroup
+    // keeps at least 2 rows while the batch allows), then pieces of the
+    // sequence of at least 256 vectors.
+    constexpr int64_t kFill = 8192;
+    ConvBwdPlan p{1, 1};
+    while (dim * p.bgroups * p.pieces < kFill) {
+        if (int64_t(p.bgroups) * 4 <= batch) p.bgroups *= 2;
+        else if (nvec / (int64_t(p.pieces) * 2) >= 256) p.pieces *= 2;
+        else break;
+    }
+    return p;
 }
 
 hipError_t launch_conv_bwd(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim,
-                           DType dtype, float* part, int32_t nseg, hipStream_t stream) {
-    return dtype == DType::BF16 ? conv_bwd_t<bf16_bits>(t, batch, L, dim, part, nseg, stream)
-                                : conv_bwd_t<float>(t, batch, L, dim, part, nseg, stream);
+                           DType dtype, float* part, ConvBwdPlan plan, hipStream_t stream) {
+    return dtype == DType::BF16 ? conv_bwd_t<bf16_bits>(t, batch, L, dim, part, plan, stream)
+                                : conv_bwd_t<float>(t, batch, L, dim, part, plan, stream);
 }
 
 hipError_t launch_conv_last(const void* x, const float* x_prev, float* x_last, int64_t rows,

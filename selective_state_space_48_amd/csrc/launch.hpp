@@ -182,7 +182,7 @@ hipError_t launch_conv(const ConvTensors& t, int64_t rows, int64_t L, int64_t di
 
 // Gradients of the convolution + SiLU for dout: dx [rows, L] of the dtype,
 // dw [dim, 4] fp32, dbias [dim] fp32 or null, dx_prev [rows, 3] fp32 or null
-// (the inputs before token 0). part: nseg * rows * 5 floats of workspace.
+// (the inputs before token 0).
 struct ConvBwdTensors {
     const void* x;
     const float* w;
@@ -194,9 +194,15 @@ struct ConvBwdTensors {
     float* dbias;
     float* dx_prev;
 };
-int32_t conv_bwd_pieces(int64_t batch, int64_t L, int64_t dim, DType dtype);
+// Work split of the gradient kernel: per channel, `bgroups` groups of batch
+// entries times `pieces` pieces of the sequence, one workgroup each.
+struct ConvBwdPlan {
+    int32_t bgroups, pieces;
+};
+ConvBwdPlan conv_bwd_plan(int64_t batch, int64_t L, int64_t dim, DType dtype);
+// part: dim * bgroups * pieces * 5 floats of workspace.
 hipError_t launch_conv_bwd(const ConvBwdTensors& t, int64_t batch, int64_t L, int64_t dim,
-                           DType dtype, float* part, int32_t nseg, hipStream_t stream);
+                           DType dtype, float* part, ConvBwdPlan plan, hipStream_t stream);
 
 // x_last[r] = the last three entries of x_prev[r] ++ x[r] (x: [rows, L] of the
 // dtype; x_prev, x_last: [rows, 3] fp32, x_prev may be null, x_last may be x_prev).

@@ -165,6 +165,8 @@ CONV_BWD_SHAPES = [
     (3, 100, 130, "bf16"),
     (2, 2048, 64, "bf16"),   # several 256-vector trips
     (1, 40000, 8, "f32"),    # long rows split into pieces
+    (5, 700, 24, "bf16"),    # element rows, batch entries in two uneven groups
+    (8, 4096, 16, "bf16"),   # four batch groups of two rows, two pieces per row
 ]
 
 
