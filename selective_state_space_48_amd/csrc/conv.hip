@@ -16,9 +16,9 @@
 // FMAs and a sigmoid: it is bound by HBM. Each thread takes one 16-byte
 // vector of consecutive tokens of one row; consecutive lanes take consecutive
 // vectors of the same row, so a wave reads and writes 1 KiB contiguous runs
-// with non-temporal 16-byte accesses. The three inputs before a thread's
-// first token are the last three of the lane below (one cross-lane shift);
-// only lane 0 of a wave and the first vector of a row fetch them otherwise.
+// with non-temporal 16-byte accesses. A thread also loads the 4 inputs before
+// its vector (a hit in cache: the lane below's vector), so that no lane
+// waits for another.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -62,6 +62,21 @@ __device__ __forceinline__ float conv4(const float4& w, float b, float x0, float
     return fmaf(w.w, x3, fmaf(w.z, x2, fmaf(w.y, x1, fmaf(w.x, x0, b))));
 }
 
+// 4 consecutive tokens (8 bytes of bf16, 16 of fp32).
+template <typename T> struct Halo;  // 4 tokens
+template <> struct Halo<float> { typedef u32x4 type; };
+template <> struct Halo<bf16_bits> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
+
+template <typename T>
+__device__ __forceinline__ void unpack_halo(const typename Halo<T>::type& v, float* o) {
+    if constexpr (sizeof(T) == 4) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    } else {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    }
+}
+
 // One thread = V consecutive tokens (one 16-byte vector) of one row.
 // VEC: L is a multiple of V, so every vector is whole and 16-byte aligned.
 template <typename T, bool VEC>
@@ -84,27 +99,34 @@ __global__ __launch_bounds__(256) void conv1d_kernel(const T* __restrict__ x,
 
     float xs[V + 3];  // xs[0..2]: the three inputs before t0; xs[3 + e]: token t0 + e
     if constexpr (VEC) {
+        // the vector and the 4 inputs before it (cache hits: the lane below's vector)
+        typedef typename Halo<T>::type H;
+        const H hb = v == 0 ? H{} : *reinterpret_cast<const H*>(xr + t0 - 4);
         unpack_vec<T>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + t0)), xs + 3);
+        float b4[4];
+        unpack_halo<T>(hb, b4);
+        xs[0] = b4[1]; xs[1] = b4[2]; xs[2] = b4[3];
     } else {
+        // element loads; the 3 inputs before t0 are the last 3 of the lane
+        // below whenever v > 0 (only a row's last vector can be partial, and
+        // it is never "previous"); lane 0 of a wave loads them itself
 #pragma unroll
         for (int e = 0; e < V; ++e) xs[3 + e] = t0 + e < L ? to_f32(xr[t0 + e]) : 0.0f;
+        const float p0 = __shfl_up(xs[V], 1, 64);
+        const float p1 = __shfl_up(xs[V + 1], 1, 64);
+        const float p2 = __shfl_up(xs[V + 2], 1, 64);
+        if (v != 0 && threadIdx.x % 64 == 0) {
+            xs[0] = to_f32(xr[t0 - 3]);
+            xs[1] = to_f32(xr[t0 - 2]);
+            xs[2] = to_f32(xr[t0 - 1]);
+        } else {
+            xs[0] = p0; xs[1] = p1; xs[2] = p2;
+        }
     }
-    // The lane below holds the previous vector of the same row whenever v > 0
-    // (only a row's last vector can be partial, and it is never "previous").
-    const float p0 = __shfl_up(xs[V], 1, 64);
-    const float p1 = __shfl_up(xs[V + 1], 1, 64);
-    const float p2 = __shfl_up(xs[V + 2], 1, 64);
-    const int lane = threadIdx.x % 64;
     if (v == 0) {
         xs[0] = x_prev ? x_prev[r * 3 + 0] : 0.0f;
         xs[1] = x_prev ? x_prev[r * 3 + 1] : 0.0f;
         xs[2] = x_prev ? x_prev[r * 3 + 2] : 0.0f;
-    } else if (lane == 0) {
-        xs[0] = to_f32(xr[t0 - 3]);
-        xs[1] = to_f32(xr[t0 - 2]);
-        xs[2] = to_f32(xr[t0 - 1]);
-    } else {
-        xs[0] = p0; xs[1] = p1; xs[2] = p2;
     }
     const float4 wd = *reinterpret_cast<const float4*>(w + d * 4);
     const float bd = bias ? bias[d] : 0.0f;
@@ -174,20 +196,6 @@ __global__ __launch_bounds__(256) void conv_step_kernel(float* __restrict__ stat
 // order, then over the workgroup in a fixed order, give one partial per
 // (channel, batch group, piece); conv1d_bwd_reduce adds a channel's partials
 // in order.
-template <typename T> struct Halo;  // 4 tokens
-template <> struct Halo<float> { typedef u32x4 type; };
-template <> struct Halo<bf16_bits> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
-
-template <typename T>
-__device__ __forceinline__ void unpack_halo(const typename Halo<T>::type& v, float* o) {
-    if constexpr (sizeof(T) == 4) {
-        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
-        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
-    } else {
-        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
-    }
-}
-
 // The raw loads of one trip of one thread (t0 = its vector's first token).
 // VEC: x and dout at t0 .. t0+V-1, x at t0-4 .. t0-1 (zero for the row's
 // first vector), x and dout at t0+V .. t0+V+3 (zero for its last vector).
