@@ -234,6 +234,73 @@ def time_decode(w, steps, warmup, torch, dev):
     return back_to_back, k_ms / k_n, dist
 
 
+def time_block_decode(w, torch, dev, per_graph=16, replays=16):
+    """The Mamba block's decode step on the decode shape, two ways: the
+    convolution's step then the scan's (two launches per token), and the
+    scan's step with the convolution fused in front (one). Each back to back
+    from Python, and captured as a HIP graph of ``per_graph`` consecutive
+    tokens (distinct inputs, the states updated in place) replayed ``replays``
+    times; the gap between the two is the host's cost of the launches."""
+    from selective_state_space_48_amd import selscan
+    from selective_state_space_48_amd import workloads as W
+
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    p = W.params(w)
+
+    def t(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+
+    state = t(W.random_state(w))
+    A, D = t(p["A"]), t(p["D"])
+    c = W.conv_inputs(W.scaled(w, seqlen=1))
+    cst, cw, cb = t(c["x_prev"]), t(c["w"]), t(c["bias"])
+    ins = []
+    for s in range(per_graph):
+        si = W.step_inputs(w, s)
+        ins.append((t(si["x"], td), t(si["delta"], td), t(si["B"], td), t(si["C"], td),
+                    t(si["z"], td)))
+    xa = torch.empty((w.batch, w.dim), dtype=td, device=dev)
+    ys = [torch.empty_like(xa) for _ in range(per_graph)]
+
+    def two_calls():
+        for i, (x, dl, B, C, z) in enumerate(ins):
+            selscan.conv1d_step(cst, x, cw, cb, out=xa)
+            selscan.step(state, xa, dl, A, B, C, D=D, z=z, y=ys[i])
+
+    def fused():
+        for i, (x, dl, B, C, z) in enumerate(ins):
+            selscan.step(state, x, dl, A, B, C, D=D, z=z, y=ys[i], conv_w=cw, conv_b=cb, conv_state=cst)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def per_token(run):
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize(dev)
+        e0.record()
+        for _ in range(replays):
+            run()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e3 / (replays * per_graph)
+
+    res = {"workload": f"block decode step on {w.name}", "tokens_per_graph": per_graph}
+    for name, run in (("two_calls", two_calls), ("fused", fused)):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        res[f"us_per_token_{name}_eager"] = round(per_token(run), 2)
+        res[f"us_per_token_{name}_graph"] = round(per_token(graph.replay), 2)
+    # fused: the scan's step bytes with the raw input in place of the convolved
+    # one, plus the convolution's state (read, written), taps and bias
+    nbytes = step_bytes(w) + w.rows * 24 + w.dim * 20
+    us = res["us_per_token_fused_graph"]
+    res.update({"achieved_GBps_fused_graph": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "frac_hbm_fused_graph": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
+                "bytes_per_token_fused": nbytes})
+    return res
+
+
 def time_bwd(torch, dev, reps=5):
     """The backward pass on the headline shape (bf16, gate, D, dt_bias): all
     eight gradients for a synthetic dy, whole call (checkpoint pass, reverse
@@ -700,6 +767,11 @@ def main():
                             "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
                             "cold_p50_GBps": round(step_bytes(wd) / (cold * 1e-6) / 1e9, 1),
                             "bytes_per_step": step_bytes(wd), "per_step": ddist}
+        # the same at one sequence, where the launches rather than the bytes set the rate
+        extras["block_decode"] = [time_block_decode(wd, torch, dev),
+                                  time_block_decode(W.scaled(wd, batch=1, name=wd.name.replace("b256", "b1")),
+                                                    torch, dev)]
+        log(f"[bench] block decode step: {extras['block_decode']}")
     if not args.no_extras and args.only in (None, "bwd"):
         log("[bench] backward: headline shape")
         extras["bwd"] = time_bwd(torch, dev)

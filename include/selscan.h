@@ -194,6 +194,40 @@ int selscan_step(float* state, const void* x, const void* delta, const float* A,
                  const selscan_dims_t* dims, void* stream);
 
 /*
+ * Options of selscan_step_ex. Zero-initialise and set what is wanted.
+ *   conv_w     : NULL, or [d, 4] fp32 taps of the block's causal depthwise
+ *                convolution + SiLU (the definition of selscan_conv1d_step),
+ *                applied to x first in the same kernel: x is then the
+ *                convolution's input, and the step's input (also the one D
+ *                multiplies) is u = silu(conv_b[d] + conv_w[d,0..2] .
+ *                conv_state[b,d,0..2] + conv_w[d,3] x[b,d]), kept in fp32
+ *                (never rounded to the dtype or written to memory).
+ *   conv_b     : [d] fp32 or NULL (0); only with conv_w.
+ *   conv_state : [B, d, 3] fp32, the three previous inputs of every row
+ *                (oldest first), read and shifted in place with x appended;
+ *                required with conv_w, which it must not overlap, nor any
+ *                other argument.
+ * The fields exist for "State Space Models and Mamba" (multigrid.ai),
+ * section "What a Mamba block actually contains": in the block the
+ * convolution sits right in front of the selective SSM, so a decode step of
+ * the block is one launch instead of two.
+ */
+typedef struct {
+    const float* conv_w;
+    const float* conv_b;
+    float* conv_state;
+} selscan_step_opts_t;
+
+/*
+ * selscan_step_ex — selscan_step with options (opts may be NULL: selscan_step).
+ * Errors as selscan_step, plus SELSCAN_ERR_CONFIG for conv_b or conv_state
+ * without conv_w, or conv_w without conv_state.
+ */
+int selscan_step_ex(float* state, const void* x, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, void* y,
+                    const selscan_dims_t* dims, const selscan_step_opts_t* opts, void* stream);
+
+/*
  * selscan_bwd — gradients of the forward pass (from a zero state) for an
  * output gradient dy.
  *
@@ -409,9 +443,9 @@ int selscan_conv1d(const void* x, const float* w, const float* bias, const float
  * bias [d] fp32 or NULL; x_prev [B, d, 3] fp32 or NULL (zeros); dw [d, 4]
  * fp32 (output); dbias [d], dx_prev [B, d, 3] fp32 outputs or NULL (not
  * wanted). dims->dstate is ignored. Outputs must not overlap inputs or each
- * other. A workspace of 20 bytes per row (more for long rows split into
- * pieces) is taken with hipMallocAsync on the stream. dw and dbias are sums in
- * a fixed order: deterministic.
+ * other. A workspace of 20 bytes per workgroup of the gradient kernel (at
+ * most 20 * max(d, 16384) bytes) is taken with hipMallocAsync on the stream.
+ * dw and dbias are sums in a fixed order: deterministic.
  */
 int selscan_conv1d_bwd(const void* x, const float* w, const float* bias, const float* x_prev,
                        const void* dout, void* dx, float* dw, float* dbias, float* dx_prev,

@@ -315,26 +315,39 @@ int selscan_fwd_workspace_size(const selscan_dims_t* dims, const selscan_fwd_opt
 int selscan_step(float* state, const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, void* y,
                  const selscan_dims_t* dims, void* stream) {
+    return selscan_step_ex(state, x, delta, A, B, C, D, z, y, dims, nullptr, stream);
+}
+
+int selscan_step_ex(float* state, const void* x, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, void* y,
+                    const selscan_dims_t* dims, const selscan_step_opts_t* opts, void* stream) {
     int rc = check_common(dims, false);
     if (rc != SELSCAN_OK) return rc;
     Sizes sz;
     if (!sizes(*dims, 1, &sz)) return SELSCAN_ERR_DIMS;
+    const selscan_step_opts_t o = opts ? *opts : selscan_step_opts_t{};
+    if ((o.conv_b && !o.conv_w) || (o.conv_w && !o.conv_state && sz.rows > 0) ||
+        (o.conv_state && !o.conv_w))
+        return SELSCAN_ERR_CONFIG;
     // A tensor with no elements may come with a null pointer (torch gives one).
     if ((sz.rows > 0 && (!state || !x || !delta || !y)) || (dims->batch > 0 && (!B || !C)) ||
         (sz.param > 0 && !A))
         return SELSCAN_ERR_NULL;
-    for (const void* p : {(const void*)state, x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)y})
+    for (const void* p : {(const void*)state, x, delta, (const void*)A, B, C, (const void*)D, z, (const void*)y,
+                          (const void*)o.conv_w, (const void*)o.conv_b, (const void*)o.conv_state})
         if (!aligned16(p)) return SELSCAN_ERR_ALIGN;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
-    const Span out_y = span(y, sz.rows * es), io_s = span(state, sz.state * 4);
+    const Span out_y = span(y, sz.rows * es), io_s = span(state, sz.state * 4),
+               io_c = span(o.conv_state, sz.rows * 12);
     const Span ins[] = {span(x, sz.rows * es), span(delta, sz.rows * es), span(z, sz.rows * es),
                         span(B, dims->batch * kN * es), span(C, dims->batch * kN * es),
-                        span(A, sz.param * 4), span(D, dims->dim * 4)};
+                        span(A, sz.param * 4), span(D, dims->dim * 4),
+                        span(o.conv_w, dims->dim * 16), span(o.conv_b, dims->dim * 4)};
     for (const Span& s : ins)
-        if (overlaps(s, out_y) || overlaps(s, io_s)) return SELSCAN_ERR_ALIAS;
-    if (overlaps(out_y, io_s)) return SELSCAN_ERR_ALIAS;
+        if (overlaps(s, out_y) || overlaps(s, io_s) || overlaps(s, io_c)) return SELSCAN_ERR_ALIAS;
+    if (overlaps(out_y, io_s) || overlaps(out_y, io_c) || overlaps(io_s, io_c)) return SELSCAN_ERR_ALIAS;
     if (sz.rows == 0) return SELSCAN_OK;
-    StepTensors t{state, x, delta, A, B, C, D, z, y};
+    StepTensors t{state, x, delta, A, B, C, D, z, y, o.conv_w, o.conv_b, o.conv_state};
     hipEvent_t eb, ee;
     next_events(&eb, &ee);
     const hipError_t e = launch_step(t, dims->batch, dims->dim,

@@ -90,6 +90,12 @@ struct StepTensors {
     const float* D;  // null: 0
     const void* z;   // null: no gate
     void* y;
+    // The block's convolution (width 4) + SiLU applied to x first (null
+    // conv_w: none): taps [dim, 4], bias [dim] or null, and the three previous
+    // inputs of every row [rows, 3], shifted in place.
+    const float* conv_w = nullptr;
+    const float* conv_b = nullptr;
+    float* conv_state = nullptr;
 };
 
 hipError_t launch_step(const StepTensors& t, int64_t batch, int64_t dim, DType dtype,

@@ -17,6 +17,13 @@
 // quad with two cross-lane adds. Each thread takes two quads (measured against
 // one and four: 38 and 40 us per step at batch 256 x d_inner 5120 with cached
 // state accesses, 35 us non-temporal at two).
+//
+// With the block's convolution fused in front ("State Space Models and
+// Mamba" (multigrid.ai), section "What a Mamba block actually contains": a
+// width-4 causal depthwise conv1d and a SiLU feed the selective SSM), the
+// step's input is u = silu(b_d + w_d . (s0, s1, s2, x)) from the row's three
+// previous inputs s, which lane 0 of the quad then shifts (s1, s2, x); u is
+// kept in fp32 and D multiplies it.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,7 +35,7 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // Each thread owns R quads (a quad = 4 states of one row), R*256 quads per
 // block; all of a thread's loads are issued before any arithmetic so that a
 // wave has R KiB of state in flight.
-template <typename T, bool GATE, int R>
+template <typename T, bool GATE, bool CONV, int R>
 __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ state,
                                                    const T* __restrict__ x,
                                                    const T* __restrict__ delta,
@@ -37,9 +44,12 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ state,
                                                    const T* __restrict__ C,
                                                    const float* __restrict__ D,
                                                    const T* __restrict__ z, T* __restrict__ y,
-                                                   int64_t rows, int64_t dim) {
-    float4 h[R], a4[R];
-    float bv[R][4], cv[R][4], xv[R], dv[R], zv[R];
+                                                   const float* __restrict__ conv_w,
+                                                   const float* __restrict__ conv_b,
+                                                   float* __restrict__ conv_state, int64_t rows,
+                                                   int64_t dim) {
+    float4 h[R], a4[R], cw[R];
+    float bv[R][4], cv[R][4], xv[R], dv[R], zv[R], cs[R][3], cb[R];
     int64_t rr[R];
     bool ok[R];
     int q[R];
@@ -68,9 +78,26 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ state,
         xv[k] = to_f32(x[r]);
         dv[k] = to_f32(delta[r]);
         zv[k] = GATE ? to_f32(z[r]) : 0.0f;
+        if constexpr (CONV) {
+            cs[k][0] = conv_state[r * 3 + 0];
+            cs[k][1] = conv_state[r * 3 + 1];
+            cs[k][2] = conv_state[r * 3 + 2];
+            cw[k] = *reinterpret_cast<const float4*>(conv_w + d * 4);
+            cb[k] = conv_b ? conv_b[d] : 0.0f;
+        }
     }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
+        if constexpr (CONV) {
+            const float xr = xv[k];
+            xv[k] = silu(fmaf(cw[k].w, xr, fmaf(cw[k].z, cs[k][2], fmaf(cw[k].y, cs[k][1],
+                                                                        fmaf(cw[k].x, cs[k][0], cb[k])))));
+            if (ok[k] && q[k] == 0) {
+                conv_state[rr[k] * 3 + 0] = cs[k][1];
+                conv_state[rr[k] * 3 + 1] = cs[k][2];
+                conv_state[rr[k] * 3 + 2] = xr;
+            }
+        }
         const float l = softplus_log2(dv[k]);
         const float w = l * kLn2 * xv[k];
         h[k].x = fmaf(exp2_hw(l * a4[k].x), h[k].x, w * bv[k][0]);
@@ -91,20 +118,22 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ state,
 
 constexpr int kStepR = 2;
 
+template <typename T, bool GATE, bool CONV>
+hipError_t launch_v(const StepTensors& t, int64_t rows, int64_t dim, hipStream_t st) {
+    const int64_t blocks = (rows * 4 + 256 * kStepR - 1) / (256 * kStepR);
+    hipLaunchKernelGGL((step_kernel<T, GATE, CONV, kStepR>), dim3(unsigned(blocks)), dim3(256), 0, st,
+                       t.state, static_cast<const T*>(t.x), static_cast<const T*>(t.delta), t.A,
+                       static_cast<const T*>(t.B), static_cast<const T*>(t.C), t.D,
+                       static_cast<const T*>(t.z), static_cast<T*>(t.y), t.conv_w, t.conv_b,
+                       t.conv_state, rows, dim);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_t(const StepTensors& t, int64_t rows, int64_t dim, hipStream_t st) {
-    const int64_t blocks = (rows * 4 + 256 * kStepR - 1) / (256 * kStepR);
-    if (t.z)
-        hipLaunchKernelGGL((step_kernel<T, true, kStepR>), dim3(unsigned(blocks)), dim3(256), 0, st,
-                           t.state, static_cast<const T*>(t.x), static_cast<const T*>(t.delta), t.A,
-                           static_cast<const T*>(t.B), static_cast<const T*>(t.C), t.D,
-                           static_cast<const T*>(t.z), static_cast<T*>(t.y), rows, dim);
-    else
-        hipLaunchKernelGGL((step_kernel<T, false, kStepR>), dim3(unsigned(blocks)), dim3(256), 0, st,
-                           t.state, static_cast<const T*>(t.x), static_cast<const T*>(t.delta), t.A,
-                           static_cast<const T*>(t.B), static_cast<const T*>(t.C), t.D,
-                           static_cast<const T*>(nullptr), static_cast<T*>(t.y), rows, dim);
-    return hipGetLastError();
+    if (t.conv_w)
+        return t.z ? launch_v<T, true, true>(t, rows, dim, st) : launch_v<T, false, true>(t, rows, dim, st);
+    return t.z ? launch_v<T, true, false>(t, rows, dim, st) : launch_v<T, false, false>(t, rows, dim, st);
 }
 
 }  // namespace

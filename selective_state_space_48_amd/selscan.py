@@ -41,6 +41,10 @@ class FwdOpts(ctypes.Structure):
                 ("conv_x_prev", ctypes.c_void_p), ("conv_x_last", ctypes.c_void_p)]
 
 
+class StepOpts(ctypes.Structure):
+    _fields_ = [("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p), ("conv_state", ctypes.c_void_p)]
+
+
 class BwdOpts(ctypes.Structure):
     _fields_ = [("h0", ctypes.c_void_p), ("dlast_state", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
                 ("segments", ctypes.c_int32), ("ckpt", ctypes.c_void_p)]
@@ -77,6 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.selscan_timing_stop.restype = ctypes.c_int
     lib.selscan_step.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, dims_p, vp]
     lib.selscan_step.restype = ctypes.c_int
+    lib.selscan_step_ex.argtypes = [fp, vp, vp, fp, vp, vp, fp, vp, vp, dims_p, ctypes.POINTER(StepOpts), vp]
+    lib.selscan_step_ex.restype = ctypes.c_int
     lib.selscan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, vp, vp, fp, vp, vp, fp, vp, fp,
                                 dims_p, vp]
     lib.selscan_bwd.restype = ctypes.c_int
@@ -241,10 +247,16 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
 
 def step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
          B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
-         z: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One decode step (selscan_step): updates ``state`` in place and returns y [batch, dim].
+         z: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
+         conv_w: Optional[torch.Tensor] = None, conv_b: Optional[torch.Tensor] = None,
+         conv_state: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step (selscan_step / selscan_step_ex): updates ``state`` in place and
+    returns y [batch, dim].
 
-    ``delta`` is the pre-activation with any channel bias already added.
+    ``delta`` is the pre-activation with any channel bias already added. With
+    ``conv_w`` [dim, 4] (and ``conv_b`` [dim], ``conv_state`` [batch, dim, 3]
+    fp32, shifted in place) the block's convolution + SiLU is applied to x
+    first, in the same kernel.
     """
     if state.dim() != 3:
         raise ValueError("state must be [batch, dim, N]")
@@ -260,12 +272,20 @@ def step(state: torch.Tensor, x: torch.Tensor, delta: torch.Tensor, A: torch.Ten
     _req(B, "B", x.dtype, (batch, N), dev)
     _req(C, "C", x.dtype, (batch, N), dev)
     _req(D, "D", torch.float32, (dim,), dev)
+    _req(conv_w, "conv_w", torch.float32, (dim, CONV_WIDTH), dev)
+    _req(conv_b, "conv_b", torch.float32, (dim,), dev)
+    _req(conv_state, "conv_state", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
     if y is None:
         y = torch.empty_like(x)
     _req(y, "y", x.dtype, (batch, dim), dev)
     dims = Dims(batch, 1, dim, N, _DTYPES[x.dtype])
-    rc = lib.selscan_step(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                          _ptr(z), _ptr(y), ctypes.byref(dims), _stream(dev))
+    if conv_w is None and conv_b is None and conv_state is None:
+        rc = lib.selscan_step(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                              _ptr(z), _ptr(y), ctypes.byref(dims), _stream(dev))
+    else:
+        opts = StepOpts(_ptr(conv_w), _ptr(conv_b), _ptr(conv_state))
+        rc = lib.selscan_step_ex(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                 _ptr(z), _ptr(y), ctypes.byref(dims), ctypes.byref(opts), _stream(dev))
     _check(rc)
     return y
 

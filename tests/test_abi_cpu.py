@@ -21,7 +21,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step",
+    assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step", "selscan_step_ex",
             "selscan_bwd", "selscan_bwd_ex", "selscan_conv1d_bwd", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
             "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
@@ -177,6 +177,28 @@ def test_fwd_fused_conv_option_checks():
     assert call(cw=cw, cp=cp, cl=cp + 16) == S.ERR_ALIAS    # overlapping, not equal
     # x_last == x_prev is allowed: the call gets as far as the workspace check
     assert call(cw=cw, cb=cb, cp=cp, cl=cp, ws=P(13), ws_bytes=16) == S.ERR_CONFIG
+
+
+def test_step_fused_conv_option_checks():
+    def call(cw=None, cb=None, cs=None, dims=None, opts=True):
+        p = [P(i) for i in range(9)]  # state, x, delta, A, B, C, D, z, y
+        o = S.StepOpts(cw, cb, cs)
+        return S.lib.selscan_step_ex(*p, ctypes.byref(dims or D()), ctypes.byref(o) if opts else None, None)
+    cw, cb, cs = (BASE + (20 + i) * SPAN for i in range(3))
+    assert call(cb=cb) == S.ERR_CONFIG                       # bias without taps
+    assert call(cs=cs) == S.ERR_CONFIG                       # state without taps
+    assert call(cw=cw) == S.ERR_CONFIG                       # taps without state
+    assert call(cw=cw + 4, cs=cs) == S.ERR_ALIGN
+    assert call(cw=cw, cs=cs + 4) == S.ERR_ALIGN
+    assert call(cw=cw, cs=P(0).value) == S.ERR_ALIAS         # the scan's state
+    assert call(cw=cw, cs=P(1).value) == S.ERR_ALIAS         # x
+    assert call(cw=cw, cs=P(8).value) == S.ERR_ALIAS         # y
+    assert call(cw=P(8).value, cs=cs) == S.ERR_ALIAS         # taps inside y
+    assert call(cw=cw, cb=P(0).value + 64, cs=cs) == S.ERR_ALIAS  # bias inside the state
+    assert call(cw=cw, cs=cs, dims=D(dim=-1)) == S.ERR_DIMS
+    # nothing to do: accepted, nothing enqueued
+    assert call(cw=cw, cb=cb, cs=cs, dims=D(batch=0)) == S.OK
+    assert call(dims=D(batch=0), opts=False) == S.OK
 
 
 def workspace_size(dims, segments=0, groups=0):

@@ -149,18 +149,20 @@ def test_fused_conv_empty_sequence():
     assert torch.equal(last, prev)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_block_prefill_then_decode(dtype):
+def test_block_prefill_then_decode(dtype, fused):
     """The block's inference path end to end: a prefill with the convolution
     fused (its last inputs and the scan's last state out), then decode steps
-    with the convolution's step and the scan's step from those; the decoded
-    outputs against the oracle's convolution then scan over the whole
+    from those, either the convolution's step then the scan's step, or the
+    scan's step with the convolution fused in front (selscan_step_ex); the
+    decoded outputs against the oracle's convolution then scan over the whole
     sequence (the decode step takes the step size with the channel bias
     already added)."""
     batch, L, T, dim = 2, 150, 6, 128
     p = _inputs(batch, L + T, dim, dtype)
     td = TDT[dtype]
-    case(f"block prefill {L} then {T} decode steps {dtype}")
+    case(f"block prefill {L} then {T} decode steps {dtype} fused={fused}")
     cut = lambda a: np.ascontiguousarray(a[..., :L])
     cst = torch.empty((batch, dim, 3), device="cuda")
     _, st = selscan.fwd(dev(cut(p["x"]), td), dev(cut(p["delta"]), td), dev(p["A"]), dev(cut(p["B"]), td),
@@ -169,14 +171,45 @@ def test_block_prefill_then_decode(dtype):
                         conv_x_last=cst)
     ys = []
     for t in range(L, L + T):
-        xa = selscan.conv1d_step(cst, dev(p["x"][..., t], td), dev(p["cw"]), dev(p["cb"]))
         dl = (p["delta"][..., t] + p["dt_bias"][None]).astype(np.float32)
-        ys.append(to_np(selscan.step(st, xa, dev(dl, td), dev(p["A"]), dev(p["B"][..., t], td),
-                                     dev(p["C"][..., t], td), D=dev(p["D"]), z=dev(p["z"][..., t], td))))
+        tok = (dev(dl, td), dev(p["A"]), dev(p["B"][..., t], td), dev(p["C"][..., t], td))
+        if fused:
+            y = selscan.step(st, dev(p["x"][..., t], td), *tok, D=dev(p["D"]), z=dev(p["z"][..., t], td),
+                             conv_w=dev(p["cw"]), conv_b=dev(p["cb"]), conv_state=cst)
+        else:
+            xa = selscan.conv1d_step(cst, dev(p["x"][..., t], td), dev(p["cw"]), dev(p["cb"]))
+            y = selscan.step(st, xa, *tok, D=dev(p["D"]), z=dev(p["z"][..., t], td))
+        ys.append(to_np(y))
     torch.cuda.synchronize()
     ref = _ref(p)
     ey = oracle.scaled_error(np.stack(ys, -1), ref["y"][..., L:], ref["y_scale"][..., L:])
     es = oracle.scaled_error(to_np(st), ref["last_state"], ref["state_scale"])
-    print(f"[parity] block prefill+decode {dtype}: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    print(f"[parity] block prefill+decode {dtype} fused={fused}: err_y={ey:.3e} err_state={es:.3e}", flush=True)
     assert ey <= TOL[dtype] and es <= TOL[dtype]
     assert np.array_equal(to_np(cst), ref["x_last"])
+
+
+@pytest.mark.parametrize("batch,dim", [(1, 1), (3, 77), (2, 256), (5, 1000)])
+def test_fused_conv_step_equals_two_calls(batch, dim):
+    """In fp32 the fused step's arithmetic is that of conv1d_step then step
+    (same operations in the same order; the convolved input is not rounded in
+    either), so y, the state and the convolution's state are equal bit for
+    bit over a few steps; ragged rows (not a multiple of the kernel's
+    2 x 256 quads) included, with and without bias and gate."""
+    N = 16
+    g = torch.Generator(device="cuda").manual_seed(batch * 1000 + dim)
+    rn = lambda *s: torch.randn(s, device="cuda", generator=g)
+    A, D, cw, cb = -torch.exp(0.5 * rn(dim, N)), rn(dim), 0.5 * rn(dim, 4), 0.1 * rn(dim)
+    for bias, gate in ((True, True), (False, False)):
+        case(f"fused conv step b{batch} d{dim} bias={bias} gate={gate}")
+        st1, cs1 = 0.1 * rn(batch, dim, N), rn(batch, dim, 3)
+        st2, cs2 = st1.clone(), cs1.clone()
+        for _ in range(3):
+            x, dl, z = rn(batch, dim), rn(batch, dim) - 1.0, rn(batch, dim) if gate else None
+            Bt, Ct = rn(batch, N), rn(batch, N)
+            xa = selscan.conv1d_step(cs1, x, cw, cb if bias else None)
+            y1 = selscan.step(st1, xa, dl, A, Bt, Ct, D=D, z=z)
+            y2 = selscan.step(st2, x, dl, A, Bt, Ct, D=D, z=z, conv_w=cw, conv_b=cb if bias else None,
+                              conv_state=cs2)
+            torch.cuda.synchronize()
+            assert torch.equal(y1, y2) and torch.equal(st1, st2) and torch.equal(cs1, cs2)
