@@ -74,9 +74,23 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
     const int64_t L = dims->seqlen;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
     *plan = FwdPlan{};
+    if (groups == 8 && dims->dtype != SELSCAN_F32) return SELSCAN_ERR_CONFIG;  // fp32 rows only
     plan->groups = groups ? groups : 4;
     plan->vec = (L * es) % 16 == 0;
     const int64_t row_blocks = (dims->dim + kWave - 1) / kWave;
+    // fp32 rows, 160 to 256 row blocks: 8 waves of 2 states per block in one
+    // pass. With 4 waves such a grid holds one wave per SIMD (a block per CU);
+    // with 8 it holds two, which hide each other's latency, still one block
+    // per CU (its LDS). Measured, L 2048: 191 against 205-211 us at 192
+    // blocks (best segmented 4-wave plan), 190 against 243 at 256; worse at
+    // 128 blocks (176 against 145, segmented) and at 512 (407 against 351).
+    const int64_t blocks = row_blocks * dims->batch;
+    if (groups == 0 && segments == 0 && dims->dtype == SELSCAN_F32 && blocks >= 160 && blocks <= 256) {
+        plan->groups = 8;
+        plan->segments = 1;
+        plan->seg_len = L;
+        return SELSCAN_OK;
+    }
     const int64_t waves = row_blocks * dims->batch * plan->groups;
     int64_t S = segments;
     if (S == 0) {
@@ -115,7 +129,8 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
 
 int check_opts(const selscan_fwd_opts_t& o) {
     if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
-    if (o.groups != 0 && o.groups != 1 && o.groups != 2 && o.groups != 4) return SELSCAN_ERR_CONFIG;
+    if (o.groups != 0 && o.groups != 1 && o.groups != 2 && o.groups != 4 && o.groups != 8)
+        return SELSCAN_ERR_CONFIG;
     if (o.ckpt && o.groups != 0 && o.groups != 4) return SELSCAN_ERR_CONFIG;  // 4 waves store them
     // the convolution in front: 4 waves, not with checkpoints, its other inputs only with taps
     if (o.conv_w && ((o.groups != 0 && o.groups != 4) || o.ckpt)) return SELSCAN_ERR_CONFIG;

@@ -221,6 +221,16 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                                 : 0.0f;
     }
     double lsum_acc = 0.0;
+    // this wave's NG states of a row, to 16-byte aligned memory
+    auto store_state = [&](float* dst, const float* hv) {
+        if constexpr (NG >= 4) {
+#pragma unroll
+            for (int k = 0; k < NG / 4; ++k)
+                reinterpret_cast<float4*>(dst)[k] = make_float4(hv[4 * k], hv[4 * k + 1], hv[4 * k + 2], hv[4 * k + 3]);
+        } else {
+            *reinterpret_cast<float2*>(dst) = make_float2(hv[0], hv[1]);
+        }
+    };
 
     // ---- thread (pr, pq)'s token slice [pq*TS, pq*TS+TS) of a chunk, straight from HBM ----
     // The G threads of a row read adjacent slices, so a wave's load covers
@@ -538,20 +548,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     }
 
     if constexpr (READOUT) {
-        if (a.last_state && row_ok && seg == a.segments - 1) {
-            float4* dst = reinterpret_cast<float4*>(a.last_state + (b * a.dim + d) * kN + n0);
-#pragma unroll
-            for (int k = 0; k < NG / 4; ++k)
-                dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
-        }
+        if (a.last_state && row_ok && seg == a.segments - 1)
+            store_state(a.last_state + (b * a.dim + d) * kN + n0, h);
     } else if constexpr (BASE == 1) {
         const int64_t so = (int64_t(seg) * a.batch * a.dim + b * a.dim + d);
-        if (row_ok) {
-            float4* dst = reinterpret_cast<float4*>(a.seg_state + so * kN + n0);
-#pragma unroll
-            for (int k = 0; k < NG / 4; ++k)
-                dst[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
-        }
+        if (row_ok) store_state(a.seg_state + so * kN + n0, h);
         // Step-size sums were accumulated per (row pr, slice pq); add the G
         // slices of each row in a fixed order.
         sm.lsum[pq][pr] = lsum_acc;
@@ -676,6 +677,9 @@ hipError_t dispatch(const FwdKArgs& k, int groups, bool gate, bool vec, int64_t 
         case 1: return dispatch_gv<T, 1, MODE>(k, gate, vec, blocks, st);
         case 2: return dispatch_gv<T, 2, MODE>(k, gate, vec, blocks, st);
         case 4: return dispatch_gv<T, 4, MODE>(k, gate, vec, blocks, st);
+        case 8:  // fp32 only: a wave's token slice (4 tokens) is one 16-byte vector
+            if constexpr (sizeof(T) == 4) return dispatch_gv<T, 8, MODE>(k, gate, vec, blocks, st);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -698,6 +702,7 @@ hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, in
         case 1: hipLaunchKernelGGL((pack_bc_kernel<T, 1>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
         case 2: hipLaunchKernelGGL((pack_bc_kernel<T, 2>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
         case 4: hipLaunchKernelGGL((pack_bc_kernel<T, 4>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
+        case 8: hipLaunchKernelGGL((pack_bc_kernel<T, 8>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
