@@ -111,8 +111,7 @@ int selscan_fwd(const void* x, const void* delta, const float* A, const void* B,
  *               0 = automatic. At most 65536; the segment length is rounded
  *               up to the kernels' 32-token tile. Results agree to rounding.
  *   groups    : waves per 64-row block, each taking N/groups states: 1, 2,
- *               4, or 8 (fp32 dtype only); 0 = automatic. Results agree to
- *               rounding.
+ *               4 or 8; 0 = automatic. Results agree to rounding.
  *   ckpt      : NULL, or a [ceil(L/16), B, d, N] fp32 output: the state
  *               entering tokens 0, 16, 32, ... of every row (token 0's is h0
  *               or zeros), for a later selscan_bwd_ex over the same inputs,

@@ -74,18 +74,19 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
     const int64_t L = dims->seqlen;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
     *plan = FwdPlan{};
-    if (groups == 8 && dims->dtype != SELSCAN_F32) return SELSCAN_ERR_CONFIG;  // fp32 rows only
     plan->groups = groups ? groups : 4;
     plan->vec = (L * es) % 16 == 0;
     const int64_t row_blocks = (dims->dim + kWave - 1) / kWave;
-    // fp32 rows, 160 to 256 row blocks: 8 waves of 2 states per block in one
-    // pass. With 4 waves such a grid holds one wave per SIMD (a block per CU);
-    // with 8 it holds two, which hide each other's latency, still one block
-    // per CU (its LDS). Measured, L 2048: 191 against 205-211 us at 192
-    // blocks (best segmented 4-wave plan), 190 against 243 at 256; worse at
-    // 128 blocks (176 against 145, segmented) and at 512 (407 against 351).
+    // 8 waves of 2 states per block in one pass, at 160 (fp32) or 208 (bf16)
+    // to 256 row blocks. With 4 waves such a grid holds one wave per SIMD (a
+    // block per CU); with 8 it holds two, which hide each other's latency,
+    // still one block per CU (its LDS). Measured, L 2048, against the 4-wave
+    // plan: fp32 191 vs 205-211 us at 192 blocks (segmented), 190 vs 243 at
+    // 256; bf16 187 vs 207 at 256, equal at 192 (segmented); worse for both
+    // at 128 blocks (segmented 4-wave plans win) and at 512.
     const int64_t blocks = row_blocks * dims->batch;
-    if (groups == 0 && segments == 0 && dims->dtype == SELSCAN_F32 && blocks >= 160 && blocks <= 256) {
+    const int64_t g8_from = dims->dtype == SELSCAN_F32 ? 160 : 208;
+    if (groups == 0 && segments == 0 && blocks >= g8_from && blocks <= 256) {
         plan->groups = 8;
         plan->segments = 1;
         plan->seg_len = L;

@@ -50,18 +50,22 @@ template <typename T> struct Elem;
 template <> struct Elem<float> { static constexpr int kPer16 = 4; };
 template <> struct Elem<bf16_bits> { static constexpr int kPer16 = 8; };
 
-template <typename T>
+// E elements of T in the low bytes of a 16-byte register quad: E = 4 or 8
+// for bf16 (8 or 16 bytes), 4 for fp32.
+template <typename T, int E = Elem<T>::kPer16>
 __device__ __forceinline__ void unpack16(const uint4& v, float* o) {
     if constexpr (sizeof(T) == 4) {
         o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
         o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
     } else {
         o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
-        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+        if constexpr (E == 8) {
+            o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+        }
     }
 }
 
-template <typename T>
+template <typename T, int E = Elem<T>::kPer16>
 __device__ __forceinline__ uint4 pack16(const float* f) {
     uint4 v;
     if constexpr (sizeof(T) == 4) {
@@ -71,21 +75,40 @@ __device__ __forceinline__ uint4 pack16(const float* f) {
         auto p = [](float a, float b) {
             return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
         };
-        v.x = p(f[0], f[1]); v.y = p(f[2], f[3]); v.z = p(f[4], f[5]); v.w = p(f[6], f[7]);
+        v.x = p(f[0], f[1]); v.y = p(f[2], f[3]);
+        if constexpr (E == 8) {
+            v.z = p(f[4], f[5]); v.w = p(f[6], f[7]);
+        } else {
+            v.z = v.w = 0u;
+        }
     }
     return v;
 }
 
-// Streaming 16-byte global accesses: x, delta and z are read exactly once and
-// y is written exactly once, so they are marked non-temporal (no reuse).
+// Streaming global accesses of 16 (or 8) bytes: x, delta and z are read
+// exactly once and y is written exactly once, so they are marked
+// non-temporal (no reuse).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <int BYTES = 16>
 __device__ __forceinline__ uint4 ldg_stream(const void* p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
+    if constexpr (BYTES == 16) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        return make_uint4(v.x, v.y, 0u, 0u);
+    }
 }
+template <int BYTES = 16>
 __device__ __forceinline__ void stg_stream(void* p, const uint4& v) {
-    u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    if constexpr (BYTES == 16) {
+        u32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    } else {
+        u32x2 w = {v.x, v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+    }
 }
 
 // 16 floats through the constant address space: with a wave-uniform address
@@ -159,8 +182,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     constexpr int SB = G;                   // tokens per sub-block (NG * SB = 16)
     constexpr int NSB = CH / SB;            // sub-blocks per chunk
     constexpr int TS = CH / G;              // tokens per wave in the per-token phases
-    constexpr int V = Elem<T>::kPer16;      // elements per 16-byte vector
-    constexpr int SV = TS / V;              // 16-byte vectors per row slice
+    // elements per vector access: 16 bytes, or 8 when the slice is shorter
+    // (bf16 with 8 waves: 4 tokens)
+    constexpr int V = Elem<T>::kPer16 < TS ? Elem<T>::kPer16 : TS;
+    constexpr int VB = V * int(sizeof(T));  // bytes per vector access
+    constexpr int SV = TS / V;              // vectors per row slice
     constexpr bool CONV = MODE >= 4;                  // convolution + SiLU in front
     constexpr int BASE = CONV ? MODE - 4 : MODE;
     constexpr bool READOUT = BASE == 0 || BASE == 3;  // y = C.h + D x, gated
@@ -249,7 +275,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // would make it wait for them there. Without VEC, element loads test
     // each token.
     auto load_vec = [&](const T* base, int64_t tk) {
-        return ldg_stream(base + prow * a.L + min(tk, a.L - V));
+        return ldg_stream<VB>(base + prow * a.L + min(tk, a.L - V));
     };
     // The convolution's history of a slice: the V inputs before it (real
     // data also across a segment boundary; at token 0 the prologue takes the
@@ -289,9 +315,9 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                     fd[e] = ok ? to_f32(DL[off + k * V + e]) : 0.0f;
                     fz[e] = (LOADZ && ok) ? to_f32(Z[off + k * V + e]) : 0.0f;
                 }
-                sl.x[k] = pack16<T>(fx);
-                sl.d[k] = pack16<T>(fd);
-                if constexpr (LOADZ) sl.z[k] = pack16<T>(fz);
+                sl.x[k] = pack16<T, V>(fx);
+                sl.d[k] = pack16<T, V>(fd);
+                if constexpr (LOADZ) sl.z[k] = pack16<T, V>(fz);
             }
         }
     };
@@ -331,9 +357,9 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         float xs[TS], ds[TS], zs[TS];
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
-            unpack16<T>(sl.x[k], xs + k * V);
-            unpack16<T>(sl.d[k], ds + k * V);
-            if constexpr (LOADZ) unpack16<T>(sl.z[k], zs + k * V);
+            unpack16<T, V>(sl.x[k], xs + k * V);
+            unpack16<T, V>(sl.d[k], ds + k * V);
+            if constexpr (LOADZ) unpack16<T, V>(sl.z[k], zs + k * V);
         }
         if constexpr (CONV) {
             // x <- silu(cb + sum_k cw[k] x[t - 3 + k]) over the window of the
@@ -491,7 +517,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         if (VEC && ts + TS <= t_end) {
 #pragma unroll
             for (int k = 0; k < SV; ++k)
-                stg_stream(Y + ts + k * V, pack16<T>(yv + k * V));
+                stg_stream<VB>(Y + ts + k * V, pack16<T, V>(yv + k * V));
         } else {
 #pragma unroll
             for (int j = 0; j < TS; ++j)
@@ -677,9 +703,7 @@ hipError_t dispatch(const FwdKArgs& k, int groups, bool gate, bool vec, int64_t 
         case 1: return dispatch_gv<T, 1, MODE>(k, gate, vec, blocks, st);
         case 2: return dispatch_gv<T, 2, MODE>(k, gate, vec, blocks, st);
         case 4: return dispatch_gv<T, 4, MODE>(k, gate, vec, blocks, st);
-        case 8:  // fp32 only: a wave's token slice (4 tokens) is one 16-byte vector
-            if constexpr (sizeof(T) == 4) return dispatch_gv<T, 8, MODE>(k, gate, vec, blocks, st);
-            return hipErrorInvalidValue;
+        case 8: return dispatch_gv<T, 8, MODE>(k, gate, vec, blocks, st);
         default: return hipErrorInvalidValue;
     }
 }

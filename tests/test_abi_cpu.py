@@ -220,8 +220,9 @@ def test_workspace_size():
     assert rc == rc2 == S.OK and b1 == 4096 * 128
     assert b4 == b1 + 2 * 4 * 128 * 16 * 4 + 4 * 128 * 8
     assert workspace_size(D(), groups=3)[0] == S.ERR_CONFIG
-    assert workspace_size(D(), groups=8)[0] == S.OK                      # 8 waves: fp32 rows
-    assert workspace_size(D(dtype=S.BF16), groups=8)[0] == S.ERR_CONFIG
+    assert workspace_size(D(), groups=8)[0] == S.OK
+    assert workspace_size(D(dtype=S.BF16), groups=8)[0] == S.OK
+    assert workspace_size(D(), groups=16)[0] == S.ERR_CONFIG
     assert workspace_size(D(N=4))[0] == S.ERR_DSTATE
     assert S.lib.selscan_fwd_workspace_size(ctypes.byref(D()), None, None) == S.ERR_NULL
     assert S.workspace_size(8, 2048, 4096, __import__("torch").bfloat16) == 8 * 2048 * 128

@@ -64,7 +64,7 @@ def test_every_launch_variant(dtype):
                 dim=130)
     ref = oracle_fwd(inp)
     ys = {}
-    for groups in (1, 2, 4, 8) if dtype == "f32" else (1, 2, 4):  # 8 waves: fp32 rows only
+    for groups in (1, 2, 4, 8):
         for segments in (1, 2, 5, 34):
             case(f"variant {dtype} groups={groups} segments={segments}")
             y, hs = gpu_fwd(inp, dtype, groups=groups, segments=segments)
@@ -75,17 +75,19 @@ def test_every_launch_variant(dtype):
     assert np.max(np.abs(a - b) / (np.abs(ref["y_scale"]) + 1e-30)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("L,dim,segments", [(1101, 130, 1), (1101, 130, 3), (37, 64, 1), (2048, 64, 0)])
-def test_eight_waves(L, dim, segments):
-    """8 waves of 2 states per row block (fp32 only): element rows (L * 4
-    not a multiple of 16), a segmented run (the 8-wave state pass), a short
-    sequence, and a shape whose automatic plan picks 8 waves (160 to 256
-    blocks of 64 rows: here 160 batch entries of one block each)."""
-    batch = 160 if segments == 0 else 2
-    case(f"8 waves b{batch} L{L} d{dim} segments={segments}")
-    inp = small("m130m_f32_b8_l2048_d1536", batch=batch, seqlen=L, dim=dim)
-    y, hs = gpu_fwd(inp, "f32", groups=8 if segments else 0, segments=segments)
-    assert_close(y, hs, oracle_fwd(inp), "f32", f"8 waves L{L} d{dim} segments={segments}")
+def test_eight_waves(dtype, L, dim, segments):
+    """8 waves of 2 states per row block (bf16: 8-byte token slices): element
+    rows (L * element size not a multiple of 16), a segmented run (the
+    8-wave state pass), a short sequence, and a shape whose automatic plan
+    picks 8 waves (blocks of 64 rows: 160 fp32 or 224 bf16 batch entries of
+    one block each)."""
+    batch = (160 if dtype == "f32" else 224) if segments == 0 else 2
+    case(f"8 waves {dtype} b{batch} L{L} d{dim} segments={segments}")
+    inp = small(M14 if dtype == "bf16" else "m130m_f32_b8_l2048_d1536", batch=batch, seqlen=L, dim=dim)
+    y, hs = gpu_fwd(inp, dtype, groups=8 if segments else 0, segments=segments)
+    assert_close(y, hs, oracle_fwd(inp), dtype, f"8 waves {dtype} L{L} d{dim} segments={segments}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
