@@ -111,6 +111,22 @@ __device__ __forceinline__ void stg_stream(void* p, const uint4& v) {
     }
 }
 
+// Bytes [sh, sh + 16) of the 32 bytes lo ++ hi (sh = 0..15): a row that
+// does not start on a 16-byte boundary is read with aligned loads and shifted
+// into place here.
+__device__ __forceinline__ uint4 extract16(const uint4& lo, const uint4& hi, int sh) {
+    // dwords sh/4 .. sh/4 + 4 of the 8, then the byte shift within them
+    const bool s4 = sh & 4, s8 = sh & 8;
+    const uint32_t e0 = s4 ? lo.y : lo.x, e1 = s4 ? lo.z : lo.y, e2 = s4 ? lo.w : lo.z,
+                   e3 = s4 ? hi.x : lo.w, e4 = s4 ? hi.y : hi.x, e5 = s4 ? hi.z : hi.y,
+                   e6 = s4 ? hi.w : hi.z;
+    const uint32_t f0 = s8 ? e2 : e0, f1 = s8 ? e3 : e1, f2 = s8 ? e4 : e2, f3 = s8 ? e5 : e3,
+                   f4 = s8 ? e6 : e4;
+    const uint32_t b = uint32_t(sh & 3);
+    return make_uint4(__builtin_amdgcn_alignbyte(f1, f0, b), __builtin_amdgcn_alignbyte(f2, f1, b),
+                      __builtin_amdgcn_alignbyte(f3, f2, b), __builtin_amdgcn_alignbyte(f4, f3, b));
+}
+
 // 16 floats through the constant address space: with a wave-uniform address
 // the compiler must use one scalar load (s_load_dwordx16) into SGPRs. Going
 // through an integer keeps address-space inference from turning it back into
@@ -201,6 +217,8 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const T* __restrict__ X = static_cast<const T*>(a.x);
     const T* __restrict__ DL = static_cast<const T*>(a.delta);
     const T* __restrict__ Z = static_cast<const T*>(a.z);
+    // byte offset of the last 16-byte block of x, delta and z (without VEC)
+    const int64_t last_block = (a.batch * a.dim * a.L * int64_t(sizeof(T)) - 1) & ~int64_t(15);
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave; saying so lets every address
@@ -262,8 +280,15 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // The G threads of a row read adjacent slices, so a wave's load covers
     // 64/G rows with CH contiguous tokens each. Two register sets alternate by
     // chunk parity.
+    // Without VEC, each vector is read as the two aligned 16-byte blocks
+    // that hold it and shifted into place in the prologue (RAW), so that the
+    // loads stay in flight a chunk ahead like the VEC ones. With 1 or 2 waves
+    // (long token slices) that would take too many registers: there the
+    // loads are element by element, converted on arrival.
+    constexpr bool RAW = !VEC && G >= 4;
+    constexpr int NR = RAW ? 2 : 1;  // 16-byte loads per vector
     struct Slice {
-        uint4 x[SV], d[SV], z[LOADZ ? SV : 1];
+        uint4 x[SV * NR], d[SV * NR], z[LOADZ ? SV * NR : 1];
         uint4 xp[1];  // with the convolution: the 16 bytes of x before the slice
     };
     Slice sl0, sl1;
@@ -306,6 +331,22 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 sl.x[k] = load_vec(X, tk);
                 sl.d[k] = load_vec(DL, tk);
                 if constexpr (LOADZ) sl.z[k] = load_vec(Z, tk);
+            } else if constexpr (RAW) {
+                // The 16-byte blocks at and after the vector's start. A block
+                // that starts past the tensor's last block is read from that
+                // last block instead (always valid memory): it holds only
+                // tokens past the row's end, whose values the prologue's
+                // masked path discards.
+                const int64_t b0 = ((off + k * V) * int64_t(sizeof(T))) & ~int64_t(15);
+                const int64_t b1 = min(b0 + 16, last_block), bb = min(b0, last_block);
+                sl.x[2 * k] = ldg_stream(reinterpret_cast<const char*>(X) + bb);
+                sl.x[2 * k + 1] = ldg_stream(reinterpret_cast<const char*>(X) + b1);
+                sl.d[2 * k] = ldg_stream(reinterpret_cast<const char*>(DL) + bb);
+                sl.d[2 * k + 1] = ldg_stream(reinterpret_cast<const char*>(DL) + b1);
+                if constexpr (LOADZ) {
+                    sl.z[2 * k] = ldg_stream(reinterpret_cast<const char*>(Z) + bb);
+                    sl.z[2 * k + 1] = ldg_stream(reinterpret_cast<const char*>(Z) + b1);
+                }
             } else {
                 float fx[V], fd[V], fz[V];
 #pragma unroll
@@ -357,9 +398,16 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         float xs[TS], ds[TS], zs[TS];
 #pragma unroll
         for (int k = 0; k < SV; ++k) {
-            unpack16<T, V>(sl.x[k], xs + k * V);
-            unpack16<T, V>(sl.d[k], ds + k * V);
-            if constexpr (LOADZ) unpack16<T, V>(sl.z[k], zs + k * V);
+            if constexpr (!RAW) {
+                unpack16<T, V>(sl.x[k], xs + k * V);
+                unpack16<T, V>(sl.d[k], ds + k * V);
+                if constexpr (LOADZ) unpack16<T, V>(sl.z[k], zs + k * V);
+            } else {
+                const int sh = int(((prow * a.L + ts + k * V) * int64_t(sizeof(T))) & 15);
+                unpack16<T, V>(extract16(sl.x[2 * k], sl.x[2 * k + 1], sh), xs + k * V);
+                unpack16<T, V>(extract16(sl.d[2 * k], sl.d[2 * k + 1], sh), ds + k * V);
+                if constexpr (LOADZ) unpack16<T, V>(extract16(sl.z[2 * k], sl.z[2 * k + 1], sh), zs + k * V);
+            }
         }
         if constexpr (CONV) {
             // x <- silu(cb + sum_k cw[k] x[t - 3 + k]) over the window of the
