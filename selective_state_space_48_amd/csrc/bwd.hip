@@ -194,8 +194,13 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;
     const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
 
+    // Without VEC the four tokens are loaded element by element, unconverted
+    // and from clamped addresses (no condition), so that the loads stay in
+    // flight until the prologue, which converts them and masks tokens past
+    // the row's end.
     struct In {
         typename Q::V x, d, z, g;
+        T xe[VEC ? 1 : 4], de[VEC ? 1 : 4], ze[VEC || !GATE ? 1 : 4], ge[VEC ? 1 : 4];
         float2 bc;  // 8 bytes of the chunk's packed B/C records
     };
     // The chunk's records are one contiguous 2 KiB block of P: 8 bytes a thread.
@@ -204,7 +209,17 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         in.bc = reinterpret_cast<const float2*>(Pb + int64_t(c) * (kBNSB * kBG * kRecF))[tid];
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
         const int64_t off = prow * a.L + t0;
-        if (VEC && t0 + kBTS <= a.L) {
+        if constexpr (!VEC) {
+            const int64_t last = prow * a.L + a.L - 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = min(off + e, last);
+                in.xe[e] = X[i];
+                in.de[e] = DL[i];
+                if constexpr (GATE) in.ze[e] = Z[i];
+                in.ge[e] = DY[i];
+            }
+        } else if (t0 + kBTS <= a.L) {
             in.x = Q::load(X + off);
             in.d = Q::load(DL + off);
             if constexpr (GATE) in.z = Q::load(Z + off);
@@ -236,10 +251,21 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     auto prologue = [&](int c, const In& in, Keep& k) {
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
         float xs[4], us[4], zs[4], gs[4];
-        Q::unpack(in.x, xs);
-        Q::unpack(in.d, us);
-        Q::unpack(in.g, gs);
-        if constexpr (GATE) Q::unpack(in.z, zs);
+        if constexpr (VEC) {
+            Q::unpack(in.x, xs);
+            Q::unpack(in.d, us);
+            Q::unpack(in.g, gs);
+            if constexpr (GATE) Q::unpack(in.z, zs);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = t0 + e < a.L;  // past the row's end: the clamped load's value
+                xs[e] = ok ? to_f32(in.xe[e]) : 0.0f;
+                us[e] = ok ? to_f32(in.de[e]) : 0.0f;
+                gs[e] = ok ? to_f32(in.ge[e]) : 0.0f;
+                zs[e] = (GATE && ok) ? to_f32(in.ze[e]) : 0.0f;
+            }
+        }
         float l[4], w[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
