@@ -337,15 +337,20 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 // last block instead (always valid memory): it holds only
                 // tokens past the row's end, whose values the prologue's
                 // masked path discards.
+                // Cached loads (not streaming): a row's chunk straddles cache
+                // lines that the next chunk's loads touch again.
                 const int64_t b0 = ((off + k * V) * int64_t(sizeof(T))) & ~int64_t(15);
                 const int64_t b1 = min(b0 + 16, last_block), bb = min(b0, last_block);
-                sl.x[2 * k] = ldg_stream(reinterpret_cast<const char*>(X) + bb);
-                sl.x[2 * k + 1] = ldg_stream(reinterpret_cast<const char*>(X) + b1);
-                sl.d[2 * k] = ldg_stream(reinterpret_cast<const char*>(DL) + bb);
-                sl.d[2 * k + 1] = ldg_stream(reinterpret_cast<const char*>(DL) + b1);
+                auto ld = [](const T* base, int64_t byte) {
+                    return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + byte);
+                };
+                sl.x[2 * k] = ld(X, bb);
+                sl.x[2 * k + 1] = ld(X, b1);
+                sl.d[2 * k] = ld(DL, bb);
+                sl.d[2 * k + 1] = ld(DL, b1);
                 if constexpr (LOADZ) {
-                    sl.z[2 * k] = ldg_stream(reinterpret_cast<const char*>(Z) + bb);
-                    sl.z[2 * k + 1] = ldg_stream(reinterpret_cast<const char*>(Z) + b1);
+                    sl.z[2 * k] = ld(Z, bb);
+                    sl.z[2 * k + 1] = ld(Z, b1);
                 }
             } else {
                 float fx[V], fd[V], fz[V];
@@ -560,8 +565,48 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < TS; ++j) yv[j] = (yv[j] + dx[j]) * gz[j];
-        if (!prow_ok) return;
         T* Y = static_cast<T*>(a.y) + prow * a.L;
+        // Rows off a 16-byte boundary (RAW, 16-byte vectors), chunk wholly
+        // inside the row: the chunk's bytes are written as the aligned
+        // 16-byte blocks inside them, each the tail of one vector and the head
+        // of the next (the next lane's first vector for a lane's last), and
+        // element stores for the part before the first block boundary (lane
+        // 0) and after the last (lane G-1). Cached stores: the lines at a
+        // chunk's ends are completed by the neighbouring chunks' stores.
+        if constexpr (RAW && VB == 16) {
+            if (t_begin + int64_t(c + 1) * CH <= t_end) {
+                uint4 v[SV];
+#pragma unroll
+                for (int k = 0; k < SV; ++k) v[k] = pack16<T, V>(yv + k * V);
+                uint4 nx;
+                nx.x = uint32_t(__shfl_down(int(v[0].x), 1, 64));
+                nx.y = uint32_t(__shfl_down(int(v[0].y), 1, 64));
+                nx.z = uint32_t(__shfl_down(int(v[0].z), 1, 64));
+                nx.w = uint32_t(__shfl_down(int(v[0].w), 1, 64));
+                if (!prow_ok) return;
+                const int64_t cb = (prow * a.L + t_begin + int64_t(c) * CH) * int64_t(sizeof(T));
+                const int s2 = int((16 - (cb & 15)) & 15);  // bytes before the first boundary
+                char* Yb = static_cast<char*>(a.y) + cb + s2 + int64_t(pq) * SV * 16;
+#pragma unroll
+                for (int k = 0; k < SV; ++k) {
+                    const bool last = pq == G - 1 && k == SV - 1;
+                    if (!last || s2 == 0) {
+                        *reinterpret_cast<uint4*>(Yb + 16 * k) = extract16(v[k], k + 1 < SV ? v[k + 1] : nx, s2);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < V; ++e)
+                            if (e * int(sizeof(T)) >= s2) Y[ts + k * V + e] = from_f32<T>(yv[k * V + e]);
+                    }
+                }
+                if (pq == 0) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+                        if (e * int(sizeof(T)) < s2) Y[ts + e] = from_f32<T>(yv[e]);
+                }
+                return;
+            }
+        }
+        if (!prow_ok) return;
         if (VEC && ts + TS <= t_end) {
 #pragma unroll
             for (int k = 0; k < SV; ++k)
