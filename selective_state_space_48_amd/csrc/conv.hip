@@ -77,6 +77,23 @@ __device__ __forceinline__ void unpack_halo(const typename Halo<T>::type& v, flo
     }
 }
 
+// Bytes [sh, sh + 16) of the 32 bytes lo ++ hi (sh = 0..15).
+__device__ __forceinline__ u32x4 bytes16_at(const u32x4& lo, const u32x4& hi, int sh) {
+    const bool s4 = sh & 4, s8 = sh & 8;
+    const uint32_t e0 = s4 ? lo.y : lo.x, e1 = s4 ? lo.z : lo.y, e2 = s4 ? lo.w : lo.z,
+                   e3 = s4 ? hi.x : lo.w, e4 = s4 ? hi.y : hi.x, e5 = s4 ? hi.z : hi.y,
+                   e6 = s4 ? hi.w : hi.z;
+    const uint32_t f0 = s8 ? e2 : e0, f1 = s8 ? e3 : e1, f2 = s8 ? e4 : e2, f3 = s8 ? e5 : e3,
+                   f4 = s8 ? e6 : e4;
+    const uint32_t b = uint32_t(sh & 3);
+    u32x4 r;
+    r.x = __builtin_amdgcn_alignbyte(f1, f0, b);
+    r.y = __builtin_amdgcn_alignbyte(f2, f1, b);
+    r.z = __builtin_amdgcn_alignbyte(f3, f2, b);
+    r.w = __builtin_amdgcn_alignbyte(f4, f3, b);
+    return r;
+}
+
 // One thread = V consecutive tokens (one 16-byte vector) of one row.
 // VEC: L is a multiple of V, so every vector is whole and 16-byte aligned.
 template <typename T, bool VEC>
@@ -107,21 +124,23 @@ __global__ __launch_bounds__(256) void conv1d_kernel(const T* __restrict__ x,
         unpack_halo<T>(hb, b4);
         xs[0] = b4[1]; xs[1] = b4[2]; xs[2] = b4[3];
     } else {
-        // element loads; the 3 inputs before t0 are the last 3 of the lane
-        // below whenever v > 0 (only a row's last vector can be partial, and
-        // it is never "previous"); lane 0 of a wave loads them itself
-#pragma unroll
-        for (int e = 0; e < V; ++e) xs[3 + e] = t0 + e < L ? to_f32(xr[t0 + e]) : 0.0f;
-        const float p0 = __shfl_up(xs[V], 1, 64);
-        const float p1 = __shfl_up(xs[V + 1], 1, 64);
-        const float p2 = __shfl_up(xs[V + 2], 1, 64);
-        if (v != 0 && threadIdx.x % 64 == 0) {
-            xs[0] = to_f32(xr[t0 - 3]);
-            xs[1] = to_f32(xr[t0 - 2]);
-            xs[2] = to_f32(xr[t0 - 1]);
-        } else {
-            xs[0] = p0; xs[1] = p1; xs[2] = p2;
-        }
+        // A row off a 16-byte boundary: the three aligned 16-byte blocks that
+        // hold the vector and the 16 bytes before it, shifted into place. A
+        // block past the tensor's last is read from that last one (it holds
+        // only tokens past the row's end, which feed no stored output); the
+        // block before the tensor is needed only for v = 0, whose history is
+        // x_prev.
+        const int64_t bo = (r * L + t0) * int64_t(sizeof(T));
+        const int sh = int(bo & 15);
+        const int64_t b0 = bo - sh, lastb = (rows * L * int64_t(sizeof(T)) - 1) & ~int64_t(15);
+        const char* xb = reinterpret_cast<const char*>(x);
+        const u32x4 bm = *reinterpret_cast<const u32x4*>(xb + max(b0 - 16, int64_t(0)));
+        const u32x4 bc = *reinterpret_cast<const u32x4*>(xb + min(b0, lastb));
+        const u32x4 bn = *reinterpret_cast<const u32x4*>(xb + min(b0 + 16, lastb));
+        float before[V];
+        unpack_vec<T>(bytes16_at(bm, bc, sh), before);
+        unpack_vec<T>(bytes16_at(bc, bn, sh), xs + 3);
+        xs[0] = before[V - 3]; xs[1] = before[V - 2]; xs[2] = before[V - 1];
     }
     if (v == 0) {
         xs[0] = x_prev ? x_prev[r * 3 + 0] : 0.0f;
@@ -133,14 +152,37 @@ __global__ __launch_bounds__(256) void conv1d_kernel(const T* __restrict__ x,
     float o[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) o[e] = silu(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]));
-    if (!active) return;
-    T* orow = out + r * L;
     if constexpr (VEC) {
-        __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
+        if (!active) return;
+        __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(out + r * L + t0));
     } else {
+        // A row off a 16-byte boundary: each thread writes the aligned 16-byte
+        // block that starts s2 bytes into its vector (its tail and the head of
+        // the next thread's vector) when that block lies inside the row, and
+        // element stores for what no block covers (a row's ends, a wave's
+        // last lane, a block that would leave the row).
+        const u32x4 mine = pack_vec<T>(o);
+        u32x4 next;
+        next.x = uint32_t(__shfl_down(int(mine.x), 1, 64));
+        next.y = uint32_t(__shfl_down(int(mine.y), 1, 64));
+        next.z = uint32_t(__shfl_down(int(mine.z), 1, 64));
+        next.w = uint32_t(__shfl_down(int(mine.w), 1, 64));
+        if (!active) return;
+        const int lane = threadIdx.x % 64;
+        const int64_t es = int64_t(sizeof(T));
+        const int64_t bo = (r * L + t0) * es, row_end = (r * L + L) * es;
+        const int s2 = int((16 - (bo & 15)) & 15);  // bytes before the first 16-byte boundary
+        const bool own_block = (s2 == 0 || lane != 63) && bo + s2 + 16 <= row_end;
+        const bool head_by_prev = s2 > 0 && lane != 0 && v > 0 && bo + s2 <= row_end;
+        if (own_block)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) + bo + s2) = bytes16_at(mine, next, s2);
+        T* orow = out + r * L;
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+        for (int e = 0; e < V; ++e) {
+            const bool in_head = e * es < s2;
+            const bool covered = in_head ? head_by_prev : own_block;
+            if (!covered && t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+        }
     }
 }
 

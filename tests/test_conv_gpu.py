@@ -53,10 +53,13 @@ SHAPES = [
     (1, 2, 3, "bf16"),       # shorter than the window: x_last reaches into x_prev
     (2, 3, 5, "f32"),
     (2, 64, 7, "bf16"),      # 16-byte rows
-    (3, 37, 70, "f32"),      # element rows, ragged
-    (2, 45, 66, "bf16"),     # element rows, ragged
-    (1, 1000, 130, "bf16"),  # many waves per row, lane-0 fetches across waves
+    (3, 37, 70, "f32"),      # rows off a 16-byte boundary: aligned blocks shifted
+    (2, 45, 66, "bf16"),     # rows off a 16-byte boundary
+    (1, 1000, 130, "bf16"),  # many waves per row
     (2, 516, 33, "f32"),
+    (3, 2047, 96, "bf16"),   # every byte offset of a row start, blocks across wave edges
+    (2, 1001, 70, "f32"),
+    (4, 7, 50, "bf16"),      # rows shorter than a vector
 ]
 
 
