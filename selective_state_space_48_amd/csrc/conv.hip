@@ -249,7 +249,7 @@ template <typename T> struct Trip<T, true> {
     u32x4 x, dy;
     typename Halo<T>::type xb, xa, da;
     __device__ __forceinline__ void load(const T* xr, const T* dr, int64_t t0, int64_t, bool first,
-                                         bool last) {
+                                         bool last, const T*, const T*, int64_t) {
         typedef typename Halo<T>::type H;
         x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + t0));
         dy = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + t0));
@@ -257,7 +257,7 @@ template <typename T> struct Trip<T, true> {
         xa = last ? H{} : *reinterpret_cast<const H*>(xr + t0 + V);
         da = last ? H{} : *reinterpret_cast<const H*>(dr + t0 + V);
     }
-    __device__ __forceinline__ void unpack(float* xs, float* dys) const {
+    __device__ __forceinline__ void unpack(float* xs, float* dys, int64_t, int64_t) const {
         float b4[4];
         unpack_halo<T>(xb, b4);
         xs[0] = b4[1]; xs[1] = b4[2]; xs[2] = b4[3];
@@ -271,22 +271,53 @@ template <typename T> struct Trip<T, true> {
     }
 };
 template <typename T> struct Trip<T, false> {
+    // A row off a 16-byte boundary: the aligned 16-byte blocks around the
+    // vector, x at -16, 0, +16, +32 bytes and dout at 0, +16, +32 from the
+    // block that holds the vector's first byte (sh bytes into it); a block
+    // outside the tensor is read from its first or last block instead (it
+    // holds only tokens outside the row, masked in unpack).
     static constexpr int V = CElem<T>::kPer16;
-    T x[V + 6], dy[V + 3];
-    __device__ __forceinline__ void load(const T* xr, const T* dr, int64_t t0, int64_t L, bool, bool) {
+    u32x4 xb[4], db[3];
+    int sh;
+    __device__ __forceinline__ void load(const T* xr, const T* dr, int64_t t0, int64_t, bool, bool,
+                                         const T* x, const T* dout, int64_t lastb) {
+        const int64_t bo = reinterpret_cast<const char*>(xr + t0) - reinterpret_cast<const char*>(x);
+        sh = int(bo & 15);
+        const int64_t b0 = bo - sh;
+        const char* xc = reinterpret_cast<const char*>(x);
+        const char* dc = reinterpret_cast<const char*>(dout);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t o = min(max(b0 + 16 * (i - 1), int64_t(0)), lastb);
+            xb[i] = *reinterpret_cast<const u32x4*>(xc + o);
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            db[i] = *reinterpret_cast<const u32x4*>(dc + min(b0 + 16 * i, lastb));
+        (void)dr;
+    }
+    __device__ __forceinline__ void unpack(float* xs, float* dys, int64_t t0, int64_t L) const {
+        float pre[V], cur[V], post[V];
+        unpack_vec<T>(bytes16_at(xb[0], xb[1], sh), pre);
+        unpack_vec<T>(bytes16_at(xb[1], xb[2], sh), cur);
+        unpack_vec<T>(bytes16_at(xb[2], xb[3], sh), post);
+        xs[0] = pre[V - 3]; xs[1] = pre[V - 2]; xs[2] = pre[V - 1];
+#pragma unroll
+        for (int e = 0; e < V; ++e) xs[3 + e] = cur[e];
+        xs[V + 3] = post[0]; xs[V + 4] = post[1]; xs[V + 5] = post[2];
+        unpack_vec<T>(bytes16_at(db[0], db[1], sh), cur);
+        unpack_vec<T>(bytes16_at(db[1], db[2], sh), post);
+#pragma unroll
+        for (int e = 0; e < V; ++e) dys[e] = cur[e];
+        dys[V] = post[0]; dys[V + 1] = post[1]; dys[V + 2] = post[2];
 #pragma unroll
         for (int i = 0; i < V + 6; ++i) {
             const int64_t t = t0 - 3 + i;
-            x[i] = t >= 0 && t < L ? xr[t] : T{};
+            if (t < 0 || t >= L) xs[i] = 0.0f;
         }
 #pragma unroll
-        for (int i = 0; i < V + 3; ++i) dy[i] = t0 + i < L ? dr[t0 + i] : T{};
-    }
-    __device__ __forceinline__ void unpack(float* xs, float* dys) const {
-#pragma unroll
-        for (int i = 0; i < V + 6; ++i) xs[i] = to_f32(x[i]);
-#pragma unroll
-        for (int i = 0; i < V + 3; ++i) dys[i] = to_f32(dy[i]);
+        for (int i = 0; i < V + 3; ++i)
+            if (t0 + i >= L) dys[i] = 0.0f;
     }
 };
 
@@ -311,6 +342,7 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
     const int64_t v_lo = nvec * sg / pieces, v_hi = nvec * (sg + 1) / pieces;
     const int64_t per_row = (v_hi - v_lo + 255) / 256;  // trips per row, uniform over the workgroup
     const int64_t trips = (b_hi - b_lo) * per_row;
+    const int64_t lastb = (batch * dim * L * int64_t(sizeof(T)) - 1) & ~int64_t(15);  // last 16-byte block
     const float4 wd = *reinterpret_cast<const float4*>(w + d * 4);
     const float bd = bias ? bias[d] : 0.0f;
     auto gof = [&](float pre, float dy) {  // dy * silu'(pre)
@@ -328,7 +360,7 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
     if (trips > 0) {
         int64_t r, v, vc;
         where(0, r, v, vc);
-        cur.load(x + r * L, dout + r * L, vc * V, L, vc == 0, vc == nvec - 1);
+        cur.load(x + r * L, dout + r * L, vc * V, L, vc == 0, vc == nvec - 1, x, dout, lastb);
     }
     for (int64_t i = 0; i < trips; ++i) {
         int64_t r, v, vc;
@@ -337,11 +369,11 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
         if (i + 1 < trips) {
             int64_t r1, v1, vc1;
             where(i + 1, r1, v1, vc1);
-            nxt.load(x + r1 * L, dout + r1 * L, vc1 * V, L, vc1 == 0, vc1 == nvec - 1);
+            nxt.load(x + r1 * L, dout + r1 * L, vc1 * V, L, vc1 == 0, vc1 == nvec - 1, x, dout, lastb);
         }
         const int64_t t0 = vc * V;
         float xs[V + 6], dys[V + 3], gs[V + 3];
-        cur.unpack(xs, dys);
+        cur.unpack(xs, dys, t0, L);
         if (vc == 0) {
 #pragma unroll
             for (int e = 0; e < 3; ++e) xs[e] = x_prev ? x_prev[r * 3 + e] : 0.0f;
@@ -351,18 +383,40 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
             const bool in_row = VEC ? (e < V || vc != nvec - 1) : t0 + e < L;
             gs[e] = in_row ? gof(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]), dys[e]) : 0.0f;
         }
-        if (v < v_hi) {
-            float o[V];
+        float o[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                o[e] = fmaf(wd.x, gs[e + 3], fmaf(wd.y, gs[e + 2], fmaf(wd.z, gs[e + 1], wd.w * gs[e])));
+        for (int e = 0; e < V; ++e)
+            o[e] = fmaf(wd.x, gs[e + 3], fmaf(wd.y, gs[e + 2], fmaf(wd.z, gs[e + 1], wd.w * gs[e])));
+        // Rows off a 16-byte boundary: as in the forward, the aligned block
+        // that starts s2 bytes into the vector (its tail and the next lane's
+        // head), where it lies inside the row and the trip's range; element
+        // stores for the rest.
+        u32x4 mine{}, next{};
+        if constexpr (!VEC) {
+            mine = pack_vec<T>(o);
+            next.x = uint32_t(__shfl_down(int(mine.x), 1, 64));
+            next.y = uint32_t(__shfl_down(int(mine.y), 1, 64));
+            next.z = uint32_t(__shfl_down(int(mine.z), 1, 64));
+            next.w = uint32_t(__shfl_down(int(mine.w), 1, 64));
+        }
+        if (v < v_hi) {
             T* orow = dx + r * L;
             if constexpr (VEC) {
                 __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
             } else {
+                const int lane = threadIdx.x % 64;
+                const int64_t es = int64_t(sizeof(T));
+                const int64_t bo = (r * L + t0) * es, row_end = (r * L + L) * es;
+                const int s2 = int((16 - (bo & 15)) & 15);
+                const bool own_block = (s2 == 0 || (lane != 63 && v + 1 < v_hi)) && bo + s2 + 16 <= row_end;
+                const bool head_by_prev = s2 > 0 && lane != 0 && bo + s2 <= row_end;
+                if (own_block)
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dx) + bo + s2) = bytes16_at(mine, next, s2);
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+                for (int e = 0; e < V; ++e) {
+                    const bool covered = e * es < s2 ? head_by_prev : own_block;
+                    if (!covered && t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+                }
             }
 #pragma unroll
             for (int e = 0; e < V; ++e) {

@@ -170,6 +170,8 @@ CONV_BWD_SHAPES = [
     (1, 40000, 8, "f32"),    # long rows split into pieces
     (5, 700, 24, "bf16"),    # element rows, batch entries in two uneven groups
     (8, 4096, 16, "bf16"),   # four batch groups of two rows, two pieces per row
+    (1, 40001, 8, "bf16"),   # rows off a 16-byte boundary split into pieces, several trips
+    (3, 2047, 96, "f32"),    # rows off a 16-byte boundary, blocks across wave edges
 ]
 
 
