@@ -309,6 +309,13 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         if constexpr (CONV) {
             if constexpr (VEC) {
                 sl.xp[0] = ldg_stream(X + prow * a.L + max(int64_t(0), min(ts - V, a.L - V)));
+            } else if constexpr (RAW) {
+                // the aligned block before the one that holds the slice's
+                // first byte: with that block, it holds the 16 bytes before
+                // the slice (shifted in the prologue)
+                const int64_t b0 = ((prow * a.L + ts) * int64_t(sizeof(T))) & ~int64_t(15);
+                sl.xp[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(X) +
+                                                           min(max(b0 - 16, int64_t(0)), last_block));
             } else {
                 float f[V];
 #pragma unroll
@@ -418,7 +425,12 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             // x <- silu(cb + sum_k cw[k] x[t - 3 + k]) over the window of the
             // 3 inputs before the slice and the slice itself
             float hp[V], win[TS + 3];
-            unpack16<T>(sl.xp[0], hp);
+            if constexpr (RAW) {
+                const int sh = int(((prow * a.L + ts) * int64_t(sizeof(T))) & 15);
+                unpack16<T>(extract16(sl.xp[0], sl.x[0], sh), hp);
+            } else {
+                unpack16<T>(sl.xp[0], hp);
+            }
 #pragma unroll
             for (int e = 0; e < 3; ++e) win[e] = hp[V - 3 + e];
             if (ts == 0) {
