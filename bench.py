@@ -8,7 +8,8 @@ forward workloads, and the fp64 CPU oracle timed on a bounded sample of the
 same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extras]
-                       [--no-cpu-baseline] [--only fwd|decode|long|m130m]
+                       [--no-cpu-baseline]
+                       [--only fwd|decode|long|m130m|conv|bwd|ssd|ragged|copy]
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -299,6 +300,55 @@ def time_block_decode(w, torch, dev, per_graph=16, replays=16):
                 "frac_hbm_fused_graph": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
                 "bytes_per_token_fused": nbytes})
     return res
+
+
+def time_ragged(torch, dev, reps=5):
+    """Rows whose length is not a multiple of the 16-byte vector: the headline
+    shape at L 2047 against L 2048 (bf16; synthetic N(0, 1) inputs, the step
+    size centred at -1), for the forward (plain and with the convolution
+    fused), the backward, and the convolution and its gradients."""
+    from selective_state_space_48_amd import selscan
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    out = {}
+    b, d, dt = 8, 4096, torch.bfloat16
+    A = -torch.arange(1, 17, device=dev, dtype=torch.float32).repeat(d, 1).contiguous()
+    D = torch.ones(d, device=dev)
+    bias = torch.full((d,), -4.0, device=dev)
+    cw = 0.5 * torch.randn((d, 4), device=dev, generator=g)
+    cb = 0.1 * torch.randn((d,), device=dev, generator=g)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def per_call(f):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize(dev)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return round(e0.elapsed_time(e1) * 1e3 / reps, 1)
+
+    for L in (2048, 2047):
+        r = lambda *sh: torch.randn(*sh, device=dev, generator=g)
+        x, z, dy = r(b, d, L).to(dt), r(b, d, L).to(dt), r(b, d, L).to(dt)
+        dl = (0.5 * r(b, d, L) - 1.0).to(dt)
+        B, C = r(b, 16, L).to(dt), r(b, 16, L).to(dt)
+        y = torch.empty_like(x)
+        res = {
+            "fwd_us": per_call(lambda: selscan.fwd(x, dl, A, B, C, D=D, z=z, dt_bias=bias, y=y)),
+            "fwd_fused_conv_us": per_call(lambda: selscan.fwd(x, dl, A, B, C, D=D, z=z, dt_bias=bias, y=y,
+                                                              conv_w=cw, conv_b=cb)),
+            "bwd_us": per_call(lambda: selscan.bwd(x, dl, A, B, C, D=D, z=z, dt_bias=bias, dy=dy)),
+            "conv1d_us": per_call(lambda: selscan.conv1d(x, cw, cb, None, out=y)),
+            "conv1d_bwd_us": per_call(lambda: selscan.conv1d_bwd(x, cw, cb, None, dout=dy)),
+        }
+        out[f"L{L}"] = res
+        del x, z, dy, dl, B, C, y
+    out["workload"] = "m1p4b_bf16_b8_d4096 at L 2048 and 2047 (rows off a 16-byte boundary)"
+    return out
 
 
 def time_bwd(torch, dev, reps=5):
@@ -682,7 +732,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "bwd", "ssd", "copy"],
+    ap.add_argument("--only", choices=["fwd", "decode", "long", "m130m", "conv", "bwd", "ssd", "ragged",
+                                       "copy"],
                     default=None,
                     help="run just one workload (for profiling); copy = counter calibration")
     args = ap.parse_args()
@@ -792,6 +843,10 @@ def main():
         log("[bench] conv1d fused into the scan")
         extras["conv_fused"] = time_fused_conv(torch, dev)
         log(f"[bench] conv fused: {extras['conv_fused']}")
+    if not args.no_extras and args.only in (None, "ragged"):
+        log("[bench] ragged rows (L 2047 against 2048)")
+        extras["ragged"] = time_ragged(torch, dev)
+        log(f"[bench] ragged: {extras['ragged']}")
     for key, name in (("long", "long_f32_b1_l1048576_d128"), ("m130m", "m130m_f32_b8_l2048_d1536")):
         if args.no_extras or args.only not in (None, key):
             continue
