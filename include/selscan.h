@@ -326,12 +326,13 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
  * with matrix products.
  *
  * Defined by: "State Space Models Explained: How Mamba Works and How It
- * Compares to Transformers" (mernstackdev.com), section "From S4 to Mamba"
- * (a restricted SSM and a form of linear attention are two views of one
- * computation, which lets Mamba-2 use matrix multiplications) and "State
- * space models and Mamba: reading long sequences without attention"
- * (ai-trend.me), section "How it developed: from S4 to Mamba and Mamba-2"
- * (the link is a decomposition of a semiseparable matrix). Per batch entry b
+ * Compares to Transformers" (mernstackdev.com), section "From S4 to Mamba",
+ * and "State space models and Mamba: reading long sequences without
+ * attention" (ai-trend.me), section "How it developed: from S4 to Mamba and
+ * Mamba-2". With one decay per token and head, the layer's output over a
+ * chunk equals y = (Lmask o C B^T)(delta x) + D x, Lmask[t,s] the product of
+ * the decays after s up to t (a semiseparable matrix), so it can be formed
+ * with matrix products instead of a token-by-token loop. Per batch entry b
  * and head h, from a zero state S (dstate x headdim):
  *   delta_t = softplus(delta[b,t,h] + dt_bias[h])
  *   S = exp(delta_t A[h]) S + delta_t B[b,t,:]^T x[b,t,h,:]

@@ -316,9 +316,12 @@ _default: Optional[Oracle] = None
 
 
 def default() -> Oracle:
+    """The oracle library: the built one, or the one named by the environment
+    variable SELSCAN_ORACLE_LIB (the sanitizer test loads an instrumented
+    build of the same source this way)."""
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get("SELSCAN_ORACLE_LIB") or None)
     return _default
 
 
@@ -366,11 +369,15 @@ def scaled_error(got, ref, scale, floor: float = 1e-30) -> float:
 
     Positions where ``ref`` is NaN must be NaN in ``got`` too (else the error
     is infinite); they are excluded from the maximum. Infinite references must
-    be matched exactly.
+    be matched exactly. The three arrays must have one shape: a comparison
+    that broadcast a smaller result over a larger reference would check less
+    than it claims.
     """
     got = _f64(got)
     ref = _f64(ref)
     scale = _f64(scale)
+    if got.shape != ref.shape or scale.shape != ref.shape:
+        raise ValueError(f"shape mismatch: got {got.shape}, ref {ref.shape}, scale {scale.shape}")
     nan_ref = np.isnan(ref)
     if np.any(np.isnan(got) != nan_ref):
         return float("inf")

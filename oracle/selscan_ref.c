@@ -637,15 +637,13 @@ int ssm_ref_bwd(const double *x, const double *delta, const double *A, const dou
  * so that the decay is one scalar per head and token.
  *
  * "State Space Models Explained: How Mamba Works and How It Compares to
- * Transformers" (mernstackdev.com), section "From S4 to Mamba": Mamba-2's
- * state space duality shows a restricted kind of SSM and a form of linear
- * attention to be two views of one computation, which lets it use matrix
- * multiplications; "State space models and Mamba: reading long sequences
- * without attention" (ai-trend.me), section "How it developed: from S4 to
- * Mamba and Mamba-2": the link is the decomposition of a semiseparable
- * matrix; "Mamba State Space Models: Fixed State, Linear Time"
- * (deepnoodle.ai): the duality through decompositions of structured
- * matrices. The restriction read here is the one under which the sequence
+ * Transformers" (mernstackdev.com), section "From S4 to Mamba"; "State
+ * space models and Mamba: reading long sequences without attention"
+ * (ai-trend.me), section "How it developed: from S4 to Mamba and Mamba-2";
+ * "Mamba State Space Models: Fixed State, Linear Time" (deepnoodle.ai). In
+ * short: when the decay is restricted enough, the layer's sequence map is a
+ * masked product y = (Lmask o C B^T)(delta x) + D x with a semiseparable
+ * mask, so matrix products can evaluate it. The restriction read here is the one under which the sequence
  * map is such a matrix: A_t = exp(delta_t A_h) times the identity, one
  * scalar per (token, head); the P channels of a head share delta_t, and B_t,
  * C_t (N entries) are shared by all heads. Per batch entry b and head h, from

@@ -70,7 +70,10 @@ int check_common(const selscan_dims_t* dims, bool fwd) {
 }
 
 // Launch plan of a forward call (shared by the call and the workspace query).
-int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdPlan* plan) {
+// `four_only`: the call asks for checkpoints or the fused convolution, which
+// only the 4-wave kernels provide, so the 8-wave choice below is skipped.
+int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, bool four_only,
+              FwdPlan* plan) {
     const int64_t L = dims->seqlen;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
     *plan = FwdPlan{};
@@ -86,7 +89,7 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, FwdP
     // at 128 blocks (segmented 4-wave plans win) and at 512.
     const int64_t blocks = row_blocks * dims->batch;
     const int64_t g8_from = dims->dtype == SELSCAN_F32 ? 160 : 208;
-    if (groups == 0 && segments == 0 && blocks >= g8_from && blocks <= 256) {
+    if (groups == 0 && segments == 0 && !four_only && blocks >= g8_from && blocks <= 256) {
         plan->groups = 8;
         plan->segments = 1;
         plan->seg_len = L;
@@ -221,7 +224,7 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
         return SELSCAN_ERR_ALIAS;
 
     FwdPlan plan{};
-    rc = make_plan(dims, o.segments, o.groups, &plan);
+    rc = make_plan(dims, o.segments, o.groups, o.ckpt || o.conv_w, &plan);
     if (rc != SELSCAN_OK) return rc;
     FwdShape shape{dims->batch, L, dims->dim, dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
     const size_t ws_bytes = (sz.rows > 0 && L > 0) ? fwd_workspace_bytes(shape, plan) : 0;
@@ -320,7 +323,7 @@ int selscan_fwd_workspace_size(const selscan_dims_t* dims, const selscan_fwd_opt
     rc = check_opts(o);
     if (rc != SELSCAN_OK) return rc;
     FwdPlan plan{};
-    rc = make_plan(dims, o.segments, o.groups, &plan);
+    rc = make_plan(dims, o.segments, o.groups, o.ckpt || o.conv_w, &plan);
     if (rc != SELSCAN_OK) return rc;
     FwdShape shape{dims->batch, dims->seqlen, dims->dim,
                    dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};

@@ -26,7 +26,10 @@
 // to HBM: x, delta, B and C are read once (B and C, shared by the heads, from
 // L2 after the first head) and y is written once. Wave w owns the 32 x 32
 // output tile (t block w/2, p block w%2) and the state tiles of p block w%2
-// for half of the state rows; the state crosses waves through LDS as bf16.
+// for half of the state rows. A wave's state rows stay in its accumulators
+// from chunk to chunk (never in LDS): each wave forms C.H over its half of
+// the state rows for both t blocks, and the two waves of a p block exchange
+// those partial products (4 KB per wave) through LDS.
 // Tiles are staged in LDS with rows padded by 16 bytes so that the 16-byte
 // operand reads of 32 lanes on 32 rows spread over the banks. The next
 // chunk's inputs are loaded into registers while the current one computes.

@@ -148,10 +148,17 @@ def _stream(device: torch.device):
 
 
 def workspace_size(batch: int, L: int, dim: int, dtype: torch.dtype, N: int = 16, *,
-                   segments: int = 0, groups: int = 0) -> int:
-    """Bytes of device workspace a forward call of this shape needs."""
+                   segments: int = 0, groups: int = 0, ckpt: bool = False,
+                   conv: bool = False) -> int:
+    """Bytes of device workspace a forward call of this shape needs; ``ckpt`` and
+    ``conv`` say whether the call passes checkpoints or the fused convolution's
+    taps (they restrict the automatic plan to 4-wave launches)."""
     dims = Dims(batch, L, dim, N, _DTYPES[dtype])
-    opts = FwdOpts(None, None, 0, int(segments), int(groups))
+    # The size query looks only at whether these options are set, never at
+    # the memory: a placeholder address stands for "set".
+    flag = ctypes.c_void_p(256)
+    opts = FwdOpts(None, None, 0, int(segments), int(groups), flag if ckpt else None,
+                   flag if conv else None)
     out = ctypes.c_uint64(0)
     _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out)))
     return int(out.value)

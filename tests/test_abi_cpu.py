@@ -228,6 +228,21 @@ def test_workspace_size():
     assert S.workspace_size(8, 2048, 4096, __import__("torch").bfloat16) == 8 * 2048 * 128
 
 
+def test_plan_with_checkpoints_or_conv_stays_four_waves():
+    """At 160-256 row blocks the automatic plan takes 8-wave blocks in one pass
+    (workspace = the packed B/C alone), but checkpoints and the fused
+    convolution exist only as 4-wave kernels: with either option the plan
+    must fall back to the 4-wave rule, which segments this grid (768 waves)."""
+    import torch
+    packed = 8 * 2048 * 128
+    assert S.workspace_size(8, 2048, 1536, torch.float32) == packed
+    with_ck = S.workspace_size(8, 2048, 1536, torch.float32, ckpt=True)
+    with_cv = S.workspace_size(8, 2048, 1536, torch.float32, conv=True)
+    assert with_ck == with_cv > packed
+    # explicit 4-wave plan with the same segment rule gives the same size
+    assert S.workspace_size(8, 2048, 1536, torch.float32, groups=4) == with_ck
+
+
 def _segments_from_workspace(batch, L, dim):
     """The automatic segment count, read back from the workspace size."""
     rows = batch * dim
@@ -505,3 +520,4 @@ def test_conv1d_bwd_argument_checks():
     p[7] = ctypes.c_void_p(BASE + 6 * SPAN + 16)   # dbias inside dw
     assert conv_bwd_call(D(), p) == S.ERR_ALIAS
     assert conv_bwd_call(D(dim=0)) == S.OK         # nothing to do, nothing enqueued
+

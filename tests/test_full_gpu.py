@@ -1,8 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (automatic plan). The oracle runs on sampled rows where all
-rows would take it minutes, and on every row of the long-sequence workload,
-the headline backward (from the forward's checkpoints) and the convolution's
-gradients. pytest -m gpu."""
+benchmark times (automatic plan): every row of the 130m-shaped and the
+headline forward, every row of the long-sequence workload, every sequence of
+the decode workload after every one of its 64 steps (from the oracle's
+512-token prefill), the headline backward (from the forward's checkpoints)
+and the convolution's gradients. pytest -m gpu."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -14,6 +17,8 @@ from selective_state_space_48_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
+M130 = "m130m_f32_b8_l2048_d1536"
+
 
 def sample_rows(w, n, seed=0):
     rng = np.random.default_rng(seed)
@@ -23,20 +28,73 @@ def sample_rows(w, n, seed=0):
     return np.unique(np.concatenate([rows, extra])).astype(np.int64)
 
 
-@pytest.mark.parametrize("name,nrows", [("m130m_f32_b8_l2048_d1536", 160),
-                                        (W.HEADLINE, 160)])
-def test_full_size_sampled(name, nrows):
+@pytest.mark.parametrize("name", [M130, W.HEADLINE])
+def test_full_size_all_rows(name):
+    """Every output of the 130m-shaped (fp32) and the headline (bf16) forward
+    against the oracle run over the whole workload."""
     w = W.get(name)
     print(f"[case] full {name}: generating", flush=True)
     inp = W.fwd_inputs(w)
     print(f"[case] full {name}: GPU", flush=True)
     y, hs = gpu_fwd(inp, w.dtype, use_z=w.gate)
-    rows = sample_rows(w, nrows)
-    print(f"[case] full {name}: oracle on {len(rows)} rows", flush=True)
-    ref = oracle_fwd(inp, use_z=w.gate, rows=rows)
-    assert_close(y, hs, ref, w.dtype, f"{name} sampled", rows=rows)
-    yn = to_np(y)
-    assert np.isfinite(yn).all()
+    print(f"[case] full {name}: oracle, all {w.rows} rows", flush=True)
+    ref = oracle_fwd(inp, use_z=w.gate)
+    assert_close(y, hs, ref, w.dtype, f"{name} all rows")
+    assert np.isfinite(to_np(y)).all()
+
+
+def test_m130m_with_checkpoints_and_conv():
+    """The 130m-shaped grid (192 row blocks), where the automatic plan takes
+    8-wave blocks, with checkpoints and with the fused convolution, which
+    only 4-wave kernels provide: the plan must fall back to them. Sampled
+    rows against the oracle; checkpoints at a few positions against the
+    oracle's state after that prefix."""
+    w = W.get(M130)
+    print("[case] m130m with ckpt / conv: generating", flush=True)
+    inp = W.fwd_inputs(w)
+    td = TDT[w.dtype]
+    args = (dev(inp["x"], td), dev(inp["delta"], td), dev(inp["A"]), dev(inp["B"], td), dev(inp["C"], td))
+    kw = dict(D=dev(inp["D"]), z=dev(inp["z"], td), dt_bias=dev(inp["dt_bias"]))
+    rows = sample_rows(w, 48, seed=5)
+    print("[case] m130m with ckpt: GPU", flush=True)
+    ck = torch.full(selscan.ckpt_shape(w.batch, w.dim, w.seqlen), float("nan"), device="cuda")
+    y, hs = selscan.fwd(*args, **kw, ckpt=ck)
+    y_plain, hs_plain = selscan.fwd(*args, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_fwd(inp, rows=rows)
+    assert_close(y, hs, ref, w.dtype, "m130m with ckpt", rows=rows)
+    assert_close(y_plain, hs_plain, ref, w.dtype, "m130m plain", rows=rows)
+    ck_np = to_np(ck).reshape(ck.shape[0], w.rows, 16)
+    b_idx, d_idx = rows // w.dim, rows % w.dim
+    worst = 0.0
+    for k in (1, 57, 127):
+        t = 16 * k
+        for i, row in enumerate(rows):
+            b, d = int(b_idx[i]), int(d_idx[i])
+            rr = oracle.fwd(inp["x"][b:b + 1, d:d + 1, :t], inp["delta"][b:b + 1, d:d + 1, :t],
+                            inp["A"][d:d + 1], inp["B"][b:b + 1, :, :t], inp["C"][b:b + 1, :, :t],
+                            D=inp["D"][d:d + 1], z=inp["z"][b:b + 1, d:d + 1, :t],
+                            dt_bias=inp["dt_bias"][d:d + 1])
+            worst = max(worst, oracle.scaled_error(ck_np[k, row][None, None], rr["last_state"], rr["state_scale"]))
+    print(f"[parity] m130m checkpoints: {worst:.2e}", flush=True)
+    assert worst <= TOL[w.dtype]
+    print("[case] m130m with conv: GPU", flush=True)
+    c = W.conv_inputs(w)
+    yc, hc = selscan.fwd(dev(c["x"], td), *args[1:], **kw, conv_w=dev(c["w"]), conv_b=dev(c["bias"]),
+                         conv_x_prev=dev(c["x_prev"]))
+    torch.cuda.synchronize()
+    conv = oracle.conv1d(c["x"][b_idx, d_idx][None], c["w"][d_idx], c["bias"][d_idx], c["x_prev"][b_idx, d_idx][None])
+    xs = inp["x"].copy()
+    xm = np.zeros_like(inp["x"])
+    xs[b_idx, d_idx] = conv["out"][0]
+    xm[b_idx, d_idx] = np.abs(conv["out"][0]) + 1.1 * conv["out_scale"][0]
+    refc = oracle_fwd(dict(inp, x=xs), rows=rows)
+    mag = oracle_fwd(dict(inp, x=xm), rows=rows)
+    yr, hr = to_np(yc).reshape(w.rows, w.seqlen)[rows], to_np(hc).reshape(w.rows, 16)[rows]
+    ey = oracle.scaled_error(yr, refc["y"], mag["y_scale"])
+    es = oracle.scaled_error(hr, refc["last_state"], mag["state_scale"])
+    print(f"[parity] m130m with conv: err_y={ey:.3e} err_state={es:.3e}", flush=True)
+    assert ey <= TOL[w.dtype] and es <= TOL[w.dtype]
 
 
 def test_full_long_sequence_all_rows():
@@ -55,58 +113,84 @@ def test_full_long_sequence_all_rows():
     assert ey <= TOL["f32"] and es <= TOL["f32"]
 
 
-def prefill_state(w, batches):
-    """Decode state for the given batch entries from a w.prefill-token oracle
-    forward pass (float64, rounded to float32)."""
+def prefill_state(w, group=8, workers=8):
+    """Decode state of every batch entry from the oracle's w.prefill-token
+    forward pass (float64; the GPU gets it rounded to float32), with the
+    oracle's state error scale. Batch entries are generated and run in groups
+    on a thread pool (the oracle releases the interpreter lock)."""
     p = W.params(w)
-    out = {}
-    for b in batches:
-        pre = W.prefill_inputs(w, b)
-        C = np.zeros_like(pre["B"])
-        r = oracle.fwd(pre["x"], pre["delta"], p["A"], pre["B"], C, D=p["D"],
-                       dt_bias=p["dt_bias"])
-        out[b] = (r["last_state"][0].astype(np.float32), r["state_scale"][0])
+    h = np.empty((w.batch, w.dim, w.dstate), np.float64)
+    hs = np.empty_like(h)
+
+    def run(g):
+        bs = range(g * group, min(w.batch, (g + 1) * group))
+        pre = [W.prefill_inputs(w, b) for b in bs]
+        x = np.concatenate([q["x"] for q in pre])
+        dl = np.concatenate([q["delta"] for q in pre])
+        B = np.concatenate([q["B"] for q in pre])
+        r = oracle.fwd(x, dl, p["A"], B, np.zeros_like(B), D=p["D"], dt_bias=p["dt_bias"])
+        h[bs.start:bs.stop] = r["last_state"]
+        hs[bs.start:bs.stop] = r["state_scale"]
+        return bs.stop
+
+    groups = (w.batch + group - 1) // group
+    with ThreadPoolExecutor(workers) as ex:
+        for i, done in enumerate(ex.map(run, range(groups))):
+            if (i + 1) % 8 == 0 or done == w.batch:
+                print(f"[case]   prefill: {done}/{w.batch} batch entries", flush=True)
+    return h, hs
+
+
+def oracle_step_all(h, hs, si, p, workers=8):
+    """oracle.step over every batch entry, split over a thread pool by batch
+    entry (rows are independent; each row's arithmetic is unchanged)."""
+    batch = h.shape[0]
+    parts = np.array_split(np.arange(batch), workers)
+
+    def run(idx):
+        sl = slice(int(idx[0]), int(idx[-1]) + 1)
+        return sl, oracle.step(h[sl], si["x"][sl], si["delta"][sl], p["A"], si["B"][sl], si["C"][sl],
+                               D=p["D"], z=None if si["z"] is None else si["z"][sl], state_scale=hs[sl])
+
+    out = {k: np.empty((batch,) + shape, np.float64) for k, shape in
+           (("y", h.shape[1:2]), ("y_scale", h.shape[1:2]), ("state", h.shape[1:]), ("state_scale", h.shape[1:]))}
+    with ThreadPoolExecutor(workers) as ex:
+        for sl, r in ex.map(run, [q for q in parts if len(q)]):
+            for k in out:
+                out[k][sl] = r[k]
     return out
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_full_decode_steps(dtype):
-    """The 2.8B-shaped decode workload: 64 steps on the full [256, 5120, 16]
-    state. Sampled batch entries start from the oracle's 512-token prefill and
-    are compared after every step; the others start from a synthetic state."""
+    """The 2.8B-shaped decode workload: every one of the 256 sequences starts
+    from the oracle's 512-token prefill state and is compared with the oracle
+    after every one of the 64 steps, on the full [256, 5120, 16] state."""
     w = W.get(W.DECODE)
     if dtype == "f32":
         w = W.scaled(w, dtype="f32")
-    batches = [0, 17, 128, 255]
-    print(f"[case] decode {dtype}: prefill {len(batches)} batch entries", flush=True)
-    pre = prefill_state(w, batches)
-    h0 = W.random_state(w)
-    for b in batches:
-        h0[b] = pre[b][0]
+    print(f"[case] decode {dtype}: oracle prefill of all {w.batch} sequences", flush=True)
+    ref_h, ref_s = prefill_state(w)
     p = W.params(w)
     td = TDT[dtype]
-    state = dev(h0)
+    state = dev(ref_h.astype(np.float32))
     A, D = dev(p["A"]), dev(p["D"])
-    ref_h = {b: h0[b].astype(np.float64) for b in batches}
-    ref_s = {b: pre[b][1] for b in batches}
     worst = (0.0, 0.0)
     for s in range(w.steps):
         si = W.step_inputs(w, s)
         y = selscan.step(state, dev(si["x"], td), dev(si["delta"], td), A, dev(si["B"], td),
                          dev(si["C"], td), D=D, z=dev(si["z"], td))
         torch.cuda.synchronize()
-        yn = to_np(y)
-        hn = to_np(state)
-        for b in batches:
-            sl = slice(b, b + 1)
-            r = oracle.step(ref_h[b][None], si["x"][sl], si["delta"][sl], p["A"], si["B"][sl],
-                            si["C"][sl], D=p["D"], z=si["z"][sl], state_scale=ref_s[b][None])
-            ref_h[b], ref_s[b] = r["state"][0], r["state_scale"][0]
-            ey = oracle.scaled_error(yn[sl], r["y"], r["y_scale"])
-            es = oracle.scaled_error(hn[sl], r["state"], r["state_scale"])
-            worst = (max(worst[0], ey), max(worst[1], es))
-    print(f"[parity] decode {dtype} 64 steps: err_y={worst[0]:.3e} err_state={worst[1]:.3e}",
-          flush=True)
+        r = oracle_step_all(ref_h, ref_s, si, p)
+        ref_h, ref_s = r["state"], r["state_scale"]
+        ey = oracle.scaled_error(to_np(y), r["y"], r["y_scale"])
+        es = oracle.scaled_error(to_np(state), r["state"], r["state_scale"])
+        worst = (max(worst[0], ey), max(worst[1], es))
+        if (s + 1) % 16 == 0:
+            print(f"[case]   decode {dtype}: step {s + 1}/{w.steps} err_y={worst[0]:.3e} "
+                  f"err_state={worst[1]:.3e}", flush=True)
+    print(f"[parity] decode {dtype} all sequences, 64 steps: err_y={worst[0]:.3e} "
+          f"err_state={worst[1]:.3e}", flush=True)
     assert worst[0] <= TOL[dtype] and worst[1] <= TOL[dtype]
 
 
