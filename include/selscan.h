@@ -49,6 +49,11 @@ typedef struct {
 #define SELSCAN_ERR_ALIGN (-7)  /* a pointer is not 16-byte aligned */
 #define SELSCAN_ERR_ALIAS (-8)  /* an output overlaps an input or another output */
 #define SELSCAN_ERR_CONFIG (-9) /* options out of range, or workspace too small */
+#define SELSCAN_ERR_SCRATCH (-10) /* selscan_fwd_noalloc: the call needs more workspace
+                                     than SELSCAN_NOALLOC_SCRATCH_BYTES */
+
+/* Size of the device scratch array behind selscan_fwd_noalloc (per GPU). */
+#define SELSCAN_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * selscan_fwd — the selective scan over whole sequences.
@@ -157,6 +162,30 @@ int selscan_fwd_ex(const void* x, const void* delta, const float* A, const void*
                    const float* D, const void* z, const float* dt_bias, void* y,
                    float* last_state, const selscan_dims_t* dims,
                    const selscan_fwd_opts_t* opts, void* stream);
+
+/*
+ * selscan_fwd_noalloc — selscan_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, results and errors as selscan_fwd, and
+ * the same kernels and launch plan; the workspace is a file-scope device array
+ * of SELSCAN_NOALLOC_SCRATCH_BYTES (64 MiB) instead of an allocation, so no
+ * hipMalloc, hipMallocAsync or hipFree is made. Each GPU the library runs on
+ * holds its own copy of the array from first use until the process ends; its
+ * device address is looked up on the first call on a device (that device
+ * current; the stream must belong to the current device).
+ * A call that needs more workspace than the array holds (selscan_fwd_workspace_size
+ * with NULL opts: B and C repacked as B * ceil(L/32)*32 * 128 bytes, plus
+ * per-segment states) returns SELSCAN_ERR_SCRATCH with nothing enqueued,
+ * e.g. batch * L above about 500,000 tokens.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from several threads without ordering on
+ * one stream) race on it and must not be made. Calls ordered on one stream
+ * are safe; nothing in the array needs to start at zero (each call writes
+ * every byte it reads before reading it).
+ */
+int selscan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* dt_bias,
+                        void* y, float* last_state, const selscan_dims_t* dims, void* stream);
 
 /*
  * Bytes of workspace selscan_fwd_ex needs for these dims and options (h0 and

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/selscan.h"
@@ -19,7 +20,7 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
 
 namespace {
 
-constexpr int kVersion = 10400;  // 1.4.0
+constexpr int kVersion = 10500;  // 1.5.0
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -168,9 +169,45 @@ void next_events(hipEvent_t* b, hipEvent_t* e) {
     ++g_timing.used;
 }
 
+// The no-allocation forward's scratch: a file-scope device array, one copy per
+// GPU, held until the process ends. Host code never uses the array's name as
+// an address (on the host it is only a stand-in for the symbol): the device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(SELSCAN_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchTable {
+    std::mutex m;
+    void* ptr[64] = {};  // per device ordinal; null until looked up
+};
+ScratchTable g_scratch;
+
+// The current device's copy of the scratch array, or null on failure.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch.m);
+    if (!g_scratch.ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch.ptr[dev] = p;
+    }
+    return g_scratch.ptr[dev];
+}
+
+// noalloc: the workspace is the device's scratch array (SELSCAN_ERR_SCRATCH
+// when the call needs more); nothing is allocated.
 int fwd_impl(const void* x, const void* delta, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, void* y, float* last_state,
-             const selscan_dims_t* dims, const selscan_fwd_opts_t* opts, void* stream) {
+             const selscan_dims_t* dims, const selscan_fwd_opts_t* opts, void* stream,
+             bool noalloc = false) {
     Sizes sz;
     int rc = check_fwd_dims(dims, &sz);
     if (rc != SELSCAN_OK) return rc;
@@ -229,6 +266,7 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     FwdShape shape{dims->batch, L, dims->dim, dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
     const size_t ws_bytes = (sz.rows > 0 && L > 0) ? fwd_workspace_bytes(shape, plan) : 0;
     if (o.workspace && o.workspace_bytes < ws_bytes) return SELSCAN_ERR_CONFIG;
+    if (noalloc && ws_bytes > kScratchBytes) return SELSCAN_ERR_SCRATCH;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (sz.rows == 0) return SELSCAN_OK;
@@ -246,8 +284,14 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
 
     FwdTensors t{x, delta, z, A, B, C, D, dt_bias, y, last_state, o.h0, o.ckpt,
                  o.conv_w, o.conv_b, o.conv_x_prev, o.conv_x_last};
-    next_events(&plan.ev_begin, &plan.ev_end);
     void* ws = o.workspace;
+    if (noalloc) {
+        // every byte of the workspace that a kernel reads is written first by
+        // an earlier kernel of the same call, so no clearing is needed
+        ws = scratch_for_current_device();
+        if (!ws) return SELSCAN_ERR_LAUNCH;
+    }
+    next_events(&plan.ev_begin, &plan.ev_end);
     const bool own = ws == nullptr;
     if (own) {
         if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
@@ -311,6 +355,12 @@ int selscan_fwd_ex(const void* x, const void* delta, const float* A, const void*
                    float* last_state, const selscan_dims_t* dims,
                    const selscan_fwd_opts_t* opts, void* stream) {
     return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, opts, stream);
+}
+
+int selscan_fwd_noalloc(const void* x, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* dt_bias,
+                        void* y, float* last_state, const selscan_dims_t* dims, void* stream) {
+    return fwd_impl(x, delta, A, B, C, D, z, dt_bias, y, last_state, dims, nullptr, stream, true);
 }
 
 int selscan_fwd_workspace_size(const selscan_dims_t* dims, const selscan_fwd_opts_t* opts,
@@ -697,6 +747,8 @@ const char* selscan_strerror(int code) {
         case SELSCAN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case SELSCAN_ERR_ALIAS: return "an output overlaps an input or another output";
         case SELSCAN_ERR_CONFIG: return "options out of range, or workspace too small or misaligned";
+        case SELSCAN_ERR_SCRATCH:
+            return "the call needs more workspace than the no-allocation scratch holds";
         default: return "unknown error code";
     }
 }

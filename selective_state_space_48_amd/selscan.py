@@ -25,7 +25,9 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 # Return codes (include/selscan.h)
 OK, ERR_NULL, ERR_DIMS, ERR_DSTATE, ERR_DTYPE, ERR_LAUNCH, ERR_ALLOC, ERR_ALIGN, ERR_ALIAS, \
-    ERR_CONFIG = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+    ERR_CONFIG, ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+# Bytes of the device scratch array behind fwd_noalloc (per GPU)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Dims(ctypes.Structure):
@@ -73,6 +75,8 @@ def _load() -> ctypes.CDLL:
     opts_p = ctypes.POINTER(FwdOpts)
     lib.selscan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, dims_p, opts_p, vp]
     lib.selscan_fwd_ex.restype = ctypes.c_int
+    lib.selscan_fwd_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, fp, dims_p, vp]
+    lib.selscan_fwd_noalloc.restype = ctypes.c_int
     lib.selscan_fwd_workspace_size.argtypes = [dims_p, opts_p, ctypes.POINTER(ctypes.c_uint64)]
     lib.selscan_fwd_workspace_size.restype = ctypes.c_int
     lib.selscan_timing_start.argtypes = [i32]
@@ -248,6 +252,36 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     rc = lib.selscan_fwd_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(dt_bias), _ptr(y), _ptr(last_state), ctypes.byref(dims),
                             ctypes.byref(opts), _stream(dev))
+    _check(rc)
+    return y, last_state
+
+
+def fwd_noalloc(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                dt_bias: Optional[torch.Tensor] = None, *, y: torch.Tensor,
+                last_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """selscan_fwd_noalloc: the forward with its workspace in the library's
+    static device scratch (NOALLOC_SCRATCH_BYTES per GPU) instead of an
+    allocation. ``y`` (and ``last_state``, if wanted) must be passed in: this
+    call allocates nothing, here or in the library. Calls that overlap in time
+    on one GPU share the scratch and must not be made."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    N = A.shape[-1] if A.dim() == 2 else -1
+    for t, name, dt, shape in ((x, "x", x.dtype, (batch, dim, L)), (delta, "delta", x.dtype, (batch, dim, L)),
+                               (z, "z", x.dtype, (batch, dim, L)), (A, "A", torch.float32, (dim, N)),
+                               (B, "B", x.dtype, (batch, N, L)), (C, "C", x.dtype, (batch, N, L)),
+                               (D, "D", torch.float32, (dim,)), (dt_bias, "dt_bias", torch.float32, (dim,)),
+                               (y, "y", x.dtype, (batch, dim, L)),
+                               (last_state, "last_state", torch.float32, (batch, dim, N))):
+        _req(t, name, dt, shape, dev)
+    dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
+    rc = lib.selscan_fwd_noalloc(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(dt_bias), _ptr(y), _ptr(last_state), ctypes.byref(dims), _stream(dev))
     _check(rc)
     return y, last_state
 

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step", "selscan_step_ex",
             "selscan_bwd", "selscan_bwd_ex", "selscan_conv1d_bwd", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
             "selscan_timing_start",
-            "selscan_timing_stop", "selscan_strerror", "selscan_version"} <= set(names)
+            "selscan_timing_stop", "selscan_strerror", "selscan_version", "selscan_fwd_noalloc"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in selscan.h but not exported"
@@ -38,12 +38,13 @@ def test_error_codes_match_header():
     assert codes["ERR_DTYPE"] == S.ERR_DTYPE and codes["ERR_LAUNCH"] == S.ERR_LAUNCH
     assert codes["ERR_ALLOC"] == S.ERR_ALLOC and codes["ERR_ALIGN"] == S.ERR_ALIGN
     assert codes["ERR_ALIAS"] == S.ERR_ALIAS and codes["ERR_CONFIG"] == S.ERR_CONFIG
+    assert codes["ERR_SCRATCH"] == S.ERR_SCRATCH
     for c in codes.values():
         assert isinstance(S.strerror(c), str) and S.strerror(c) != "unknown error code"
 
 
 def test_version():
-    assert S.version() == 10400
+    assert S.version() == 10500
 
 
 # Fake, 16-byte aligned, non-overlapping device addresses (never dereferenced:
@@ -521,3 +522,48 @@ def test_conv1d_bwd_argument_checks():
     assert conv_bwd_call(D(), p) == S.ERR_ALIAS
     assert conv_bwd_call(D(dim=0)) == S.OK         # nothing to do, nothing enqueued
 
+
+def noalloc_call(dims, ptrs=None):
+    p = [P(i) for i in range(10)] if ptrs is None else ptrs
+    return S.lib.selscan_fwd_noalloc(*p, ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SELSCAN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == S.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_argument_checks():
+    """The no-allocation forward checks its arguments like selscan_fwd, before
+    any HIP call."""
+    assert noalloc_call(None) == S.ERR_NULL
+    assert noalloc_call(D(batch=-1)) == S.ERR_DIMS
+    assert noalloc_call(D(N=8)) == S.ERR_DSTATE
+    assert noalloc_call(D(dtype=5)) == S.ERR_DTYPE
+    for idx in (0, 1, 2, 3, 4, 8):
+        p = [P(i) for i in range(10)]
+        p[idx] = None
+        assert noalloc_call(D(), p) == S.ERR_NULL
+    p = [P(i) for i in range(10)]
+    p[3] = ctypes.c_void_p(BASE + 3 * SPAN + 4)
+    assert noalloc_call(D(), p) == S.ERR_ALIGN
+    p = [P(i) for i in range(10)]
+    p[8] = P(0)  # y on x
+    assert noalloc_call(D(), p) == S.ERR_ALIAS
+    # nothing to do: accepted with nothing enqueued and no device touched
+    assert noalloc_call(D(batch=0)) == S.OK
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    """A call whose workspace exceeds the scratch array is refused with
+    SELSCAN_ERR_SCRATCH before any HIP call (the million-token forward needs
+    128 MiB of repacked B/C); the limit follows selscan_fwd_workspace_size."""
+    big = D(batch=1, L=1 << 20, dim=128)
+    assert workspace_size(big)[1] > S.NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(big) == S.ERR_SCRATCH
+    # just over the limit in batch * L (one segment, packed B/C alone)
+    tokens = S.NOALLOC_SCRATCH_BYTES // 128
+    assert workspace_size(D(batch=1, L=tokens + 32, dim=64))[1] > S.NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(D(batch=1, L=tokens + 32, dim=64)) == S.ERR_SCRATCH
+    assert "scratch" in S.strerror(S.ERR_SCRATCH)
