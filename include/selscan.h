@@ -135,6 +135,15 @@ int selscan_fwd(const void* x, const void* delta, const float* A, const void* B,
  *   conv_b    : [d] fp32 or NULL (0); only with conv_w.
  *   conv_x_prev, conv_x_last : [B, d, 3] fp32 or NULL, as selscan_conv1d's
  *               x_prev and x_last; only with conv_w. x_last may be x_prev.
+ *   variant   : which forward kernel: 0 = automatic; 1 = the per-wave kernel
+ *               (every wave both streams its tokens and scans); 2 = the
+ *               warp-specialised kernel (scan waves fed through LDS by io
+ *               waves that stream x, delta, z and store y), groups then
+ *               being its scan waves, 0 (automatic), 4 or 8; 3 = 2, with the
+ *               io waves also loading each chunk's B/C operands into the
+ *               scalar cache a chunk ahead of the scan waves. 2 and 3 need
+ *               L % 4 == 0 and no ckpt or conv_w.
+ *               Results agree to rounding.
  */
 typedef struct {
     const float* h0;
@@ -147,6 +156,7 @@ typedef struct {
     const float* conv_b;
     const float* conv_x_prev;
     float* conv_x_last;
+    int32_t variant;
 } selscan_fwd_opts_t;
 
 /*

@@ -73,14 +73,48 @@ int check_common(const selscan_dims_t* dims, bool fwd) {
 // Launch plan of a forward call (shared by the call and the workspace query).
 // `four_only`: the call asks for checkpoints or the fused convolution, which
 // only the 4-wave kernels provide, so the 8-wave choice below is skipped.
-int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, bool four_only,
-              FwdPlan* plan) {
+int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, int32_t variant,
+              bool four_only, FwdPlan* plan) {
     const int64_t L = dims->seqlen;
     const int64_t es = dims->dtype == SELSCAN_BF16 ? 2 : 4;
     *plan = FwdPlan{};
     plan->groups = groups ? groups : 4;
     plan->vec = (L * es) % 16 == 0;
     const int64_t row_blocks = (dims->dim + kWave - 1) / kWave;
+    const int64_t nblocks = row_blocks * dims->batch;
+    if (variant == 0 && groups == 0 && segments == 0 && !four_only && L % 4 == 0) {
+        // The warp-specialised kernel where it measured faster (L 2048 sweeps
+        // of batch x d_inner, whole call; fp32 32..1024 row blocks, bf16
+        // 48..1024, and long rows with few blocks): fp32 below 1024 blocks
+        // (e.g. 192 blocks: 159 against 197 us; 320: 270 against 302; 48 in
+        // segments: 85 against 95); bf16 at 160-256 blocks (192: 175 against
+        // 203 us) - elsewhere the per-wave kernel's 16-byte bf16 loads win
+        // (512 blocks: 294 against 319 us).
+        const bool f32 = dims->dtype == SELSCAN_F32;
+        if (f32 ? nblocks < 1024 : (nblocks >= 160 && nblocks <= 256)) {
+            plan->ws = true;
+            if (nblocks < 160) {
+                // few blocks: segments (the rule below), operand prefetch
+                plan->groups = 4;
+                plan->pref = true;
+            } else if (f32 && nblocks < 256) {
+                // one block per CU: 8 scan waves (two per SIMD), one pass
+                plan->groups = 8;
+                plan->pref = true;
+                segments = 1;
+            } else {
+                plan->groups = 4;
+                segments = 1;
+            }
+        }
+    }
+    if (variant >= 2) {
+        // the warp-specialised kernel: whole 4-token vectors per row
+        if (L % 4 != 0 || four_only) return SELSCAN_ERR_CONFIG;
+        plan->ws = true;
+        plan->pref = variant == 3;
+        if (groups == 0) plan->groups = nblocks <= 256 ? 8 : 4;
+    }
     // 8 waves of 2 states per block in one pass, at 160 (fp32) or 208 (bf16)
     // to 256 row blocks. With 4 waves such a grid holds one wave per SIMD (a
     // block per CU); with 8 it holds two, which hide each other's latency,
@@ -90,13 +124,16 @@ int make_plan(const selscan_dims_t* dims, int32_t segments, int32_t groups, bool
     // at 128 blocks (segmented 4-wave plans win) and at 512.
     const int64_t blocks = row_blocks * dims->batch;
     const int64_t g8_from = dims->dtype == SELSCAN_F32 ? 160 : 208;
-    if (groups == 0 && segments == 0 && !four_only && blocks >= g8_from && blocks <= 256) {
+    if (!plan->ws && groups == 0 && segments == 0 && variant < 2 && !four_only && blocks >= g8_from &&
+        blocks <= 256) {
         plan->groups = 8;
         plan->segments = 1;
         plan->seg_len = L;
         return SELSCAN_OK;
     }
-    const int64_t waves = row_blocks * dims->batch * plan->groups;
+    // (the specialised kernel counts like 4 waves per block: 4 or 8 scan
+    // waves sharing a block's rows)
+    const int64_t waves = row_blocks * dims->batch * (plan->ws ? 4 : plan->groups);
     int64_t S = segments;
     if (S == 0) {
         // Segmenting adds a state pass (about 0.7 of an output pass) over all
@@ -139,6 +176,10 @@ int check_opts(const selscan_fwd_opts_t& o) {
     if (o.ckpt && o.groups != 0 && o.groups != 4) return SELSCAN_ERR_CONFIG;  // 4 waves store them
     // the convolution in front: 4 waves, not with checkpoints, its other inputs only with taps
     if (o.conv_w && ((o.groups != 0 && o.groups != 4) || o.ckpt)) return SELSCAN_ERR_CONFIG;
+    if (o.variant < 0 || o.variant > 3) return SELSCAN_ERR_CONFIG;
+    // the specialised kernel: 4 or 8 scan waves, no checkpoints, no convolution
+    if (o.variant >= 2 && ((o.groups != 0 && o.groups != 4 && o.groups != 8) || o.ckpt || o.conv_w))
+        return SELSCAN_ERR_CONFIG;
     if (!o.conv_w && (o.conv_b || o.conv_x_prev || o.conv_x_last)) return SELSCAN_ERR_CONFIG;
     return SELSCAN_OK;
 }
@@ -261,7 +302,7 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
         return SELSCAN_ERR_ALIAS;
 
     FwdPlan plan{};
-    rc = make_plan(dims, o.segments, o.groups, o.ckpt || o.conv_w, &plan);
+    rc = make_plan(dims, o.segments, o.groups, o.variant, o.ckpt || o.conv_w, &plan);
     if (rc != SELSCAN_OK) return rc;
     FwdShape shape{dims->batch, L, dims->dim, dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
     const size_t ws_bytes = (sz.rows > 0 && L > 0) ? fwd_workspace_bytes(shape, plan) : 0;
@@ -373,7 +414,7 @@ int selscan_fwd_workspace_size(const selscan_dims_t* dims, const selscan_fwd_opt
     rc = check_opts(o);
     if (rc != SELSCAN_OK) return rc;
     FwdPlan plan{};
-    rc = make_plan(dims, o.segments, o.groups, o.ckpt || o.conv_w, &plan);
+    rc = make_plan(dims, o.segments, o.groups, o.variant, o.ckpt || o.conv_w, &plan);
     if (rc != SELSCAN_OK) return rc;
     FwdShape shape{dims->batch, dims->seqlen, dims->dim,
                    dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};

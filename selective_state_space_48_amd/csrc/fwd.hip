@@ -179,6 +179,9 @@ struct FwdKArgs {
     const float* cw;      // [dim][4] taps, tap k on the input 3 - k tokens back
     const float* cb;      // [dim] or null
     const float* cx_prev; // [batch*dim][3] inputs before token 0 (oldest first), or null
+    // warp-specialised kernel only: 256 bytes of workspace that the io lanes
+    // of rows past dim store to, so that every lane issues the same stores
+    void* dump;
 };
 
 // MODE 0: output pass (y, and last_state from the final segment).
@@ -697,6 +700,401 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialised forward: the output pass (MODE 0) and the state pass
+// (MODE 1) of fwd_kernel, computing the same recurrence from the same packed
+// B/C records, with the two kinds of work on different waves of a 64-row
+// block. NS scan waves (16/NS states of every row each) run only the
+// register recurrence, fed by the records through SGPRs and by (l, w) from
+// LDS; four io waves stream x, delta and z from HBM, form the per-token
+// values, sum the scan waves' partial readouts, gate and store y. LDS holds
+// two chunks of each hand-off, so one barrier per 16-token chunk separates
+// the roles: during chunk c the scan waves read (l, w) of c and write their
+// partial readouts of c, while the io waves write (l, w) of c+1 and read the
+// partial readouts of c-1. The scan waves never wait on global memory, and
+// the io waves' loads, LDS traffic and stores run beside the scans of other
+// waves on the same SIMD instead of between them.
+//
+// Rows must be whole 4-token vectors (L % 4 == 0): an io lane takes 4
+// consecutive tokens of one row per chunk (8 bytes of bf16, 16 of fp32), and
+// the lanes of a wave load QC consecutive chunks back to back, one 128-byte
+// line per row, tensor by tensor.
+constexpr int kWsChunk = 16;  // tokens per chunk of the warp-specialised kernel
+constexpr int kWsIo = 4;      // io waves per block
+
+// LDS of the warp-specialised kernel. (l, w): row stride 9 x 16 bytes, so the
+// scan lanes' 16-byte reads of one token pair on 8 consecutive rows, and the io
+// lanes' writes (4 lanes of a row at 32-byte steps, two rows per 8 lanes),
+// each fall in 8 distinct 16-byte bank groups. Partial readouts: 64 bytes per
+// row, the 16-byte piece k of row r stored at piece k ^ ((r >> 1) & 3), which
+// keeps both the scan lanes' writes (one piece, 8 rows) and the io lanes' reads
+// (4 pieces of 2 rows) free of bank conflicts.
+template <int NS, bool READOUT>
+struct alignas(16) WsSmem {
+    static constexpr int kLwB = kWsChunk * 8 + 16;
+    unsigned char lw[2][kWave * kLwB];
+    float yp[READOUT ? 2 : 1][READOUT ? NS : 1][READOUT ? kWave * kWsChunk : 4];
+};
+__device__ __forceinline__ int yp_index(int row, int piece) {
+    return row * kWsChunk + ((piece ^ ((row >> 1) & 3)) << 2);
+}
+
+template <typename T, int NS, bool GATE, int MODE, bool PREF>
+__global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) {
+    constexpr int CH = kWsChunk;
+    constexpr int NG = kN / NS;        // states per scan lane
+    constexpr int SB = NS;             // tokens per sub-block (NG * SB = 16)
+    constexpr int NSB = CH / SB;       // sub-blocks per chunk
+    constexpr bool READOUT = MODE == 0;
+    constexpr bool LOADZ = GATE && READOUT;
+    constexpr int EB = 4 * int(sizeof(T));          // bytes per io load: 4 tokens
+    constexpr int QC = 128 / (CH * int(sizeof(T)));  // chunks per load group (one line per row)
+    static_assert(NS == 4 || NS == 8, "4 or 8 scan waves");
+    static_assert(NSB % 2 == 0, "sub-blocks per chunk must be even");
+    using S = WsSmem<NS, READOUT>;
+    __shared__ S sm;
+
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+
+    int64_t blk = blockIdx.x;
+    const int rb = int(blk % a.row_blocks);
+    blk /= a.row_blocks;
+    const int64_t b = blk % a.batch;
+    const int seg = int(blk / a.batch);
+    const int64_t d0 = int64_t(rb) * kWave;
+    const int64_t t_begin = int64_t(seg) * a.seg_len;
+    const int64_t t_end = min(a.L, t_begin + a.seg_len);
+    const int nchunks = int((t_end - t_begin + CH - 1) / CH);
+    // Both roles run a whole number of io iterations (2 QC chunks each):
+    // chunks past the segment's end are identity steps (l = w = 0) whose
+    // outputs go to the dump area. The io loop then issues the same memory
+    // operations in every iteration, which lets the compiler count its
+    // waits for prefetched loads exactly.
+    const int nch = (nchunks + 2 * QC - 1) / (2 * QC) * (2 * QC);
+
+    if (wv < NS) {
+        // ---------------- scan wave: states n0 .. n0+NG-1 of every row ----------------
+        const int64_t d = d0 + lane;
+        const bool row_ok = d < a.dim;
+        const int n0 = wv * NG;
+        float An[NG], h[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            An[j] = row_ok ? a.A[d * kN + n0 + j] : 0.0f;
+            h[j] = (a.h0 && row_ok) ? a.h0[(int64_t(seg) * a.batch * a.dim + b * a.dim + d) * kN + n0 + j]
+                                    : 0.0f;
+        }
+        // this wave's records: sub-block s of the segment at rec0 + s * RS;
+        // consecutive sub-blocks (also across chunks) are RS floats apart
+        constexpr int RS = NS * kRec;
+        // With 4 scan waves the first records of a chunk are loaded during
+        // the chunk before; with 8 (one sub-block pair per chunk) that leaves
+        // the compiler short of SGPRs at the loop back-edge, so they are
+        // loaded at the top of each chunk instead.
+        constexpr bool XPF = NSB >= 4;
+        const float* rec0 = a.P + ((b * a.psub + t_begin / SB) * NS + wv) * kRec;
+        f32x16 B0, C0, B1, C1;
+        if constexpr (XPF) {
+            B0 = sload64(rec0);
+            if constexpr (READOUT) C0 = sload64(rec0 + 16);
+        }
+        float yA[SB], yB[SB];
+#pragma unroll
+        for (int e = 0; e < SB; ++e) yB[e] = 0.0f;
+        __syncthreads();  // (l, w) of chunk 0 written
+        for (int c = 0; c < nch; ++c) {
+            const int buf = c & 1;
+            const float4* lwrow = reinterpret_cast<const float4*>(&sm.lw[buf][lane * S::kLwB]);
+            float* yrow = READOUT ? &sm.yp[buf][wv][0] : nullptr;
+            // the chunk's records (past the segment's last chunk that one's:
+            // their steps are identities), and the furthest one to prefetch:
+            // the next chunk's first, or in the last chunk its own last
+            const float* recc = rec0 + int64_t(min(c, nchunks - 1)) * NSB * RS;
+            const int nmax = XPF && c + 1 < nchunks ? NSB : NSB - 1;
+            if constexpr (!XPF) {
+                B0 = sload64(recc);
+                if constexpr (READOUT) C0 = sload64(recc + 16);
+            }
+            float4 lq0[SB / 2], lq1[SB / 2];
+#pragma unroll
+            for (int e = 0; e < SB / 2; ++e) lq0[e] = lwrow[e];
+            auto put = [&](int sb, const float* yv) {  // partial readouts of sub-block sb
+#pragma unroll
+                for (int m = 0; m < SB / 4; ++m)
+                    *reinterpret_cast<float4*>(yrow + yp_index(lane, sb * (SB / 4) + m)) =
+                        make_float4(yv[4 * m], yv[4 * m + 1], yv[4 * m + 2], yv[4 * m + 3]);
+            };
+            auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float4* lc, f32x16& Bn,
+                            f32x16& Cn, float4* ln, const float* yprev, float* yv) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): current operands ready
+                __builtin_amdgcn_sched_barrier(0);
+                // Next sub-block's records (the next chunk's first after the
+                // last) and (l, w) (at the last sub-block the chunk's first
+                // again: harmless, reloaded after the barrier). The previous
+                // sub-block's partial readouts; at sb = 0 that write goes to
+                // the chunk's last slot, which the final write overwrites.
+                const float* nrec = recc + min(sb + 1, nmax) * RS;
+                Bn = sload64(nrec);
+                if constexpr (READOUT) Cn = sload64(nrec + 16);
+#pragma unroll
+                for (int e = 0; e < SB / 2; ++e) ln[e] = lwrow[((sb + 1) & (NSB - 1)) * (SB / 2) + e];
+                if constexpr (READOUT) put((sb + NSB - 1) & (NSB - 1), yprev);
+                __builtin_amdgcn_sched_barrier(0);
+                float dA[SB][NG], u[SB][NG];
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    const float l = (e & 1) ? lc[e / 2].z : lc[e / 2].x;
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) dA[e][j] = exp2_hw(l * An[j]);
+                }
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    const float w = (e & 1) ? lc[e / 2].w : lc[e / 2].y;
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) u[e][j] = w * Bc[j * SB + e];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NG; ++j) {
+                        h[j] = fmaf(dA[e][j], h[j], u[e][j]);
+                        if constexpr (READOUT) acc = fmaf(Cc[j * SB + e], h[j], acc);
+                    }
+                    yv[e] = acc;
+                }
+            };
+            // sub-blocks in pairs (ping-pong operand sets, no copies at the
+            // back-edge); a loop rather than a full unroll keeps the two
+            // record sets of each pair in fixed SGPRs
+#pragma unroll 1
+            for (int sb = 0; sb < NSB; sb += 2) {
+                half(sb, B0, C0, lq0, B1, C1, lq1, yB, yA);
+                half(sb + 1, B1, C1, lq1, B0, C0, lq0, yA, yB);
+            }
+            if constexpr (READOUT) put(NSB - 1, yB);
+            __syncthreads();  // partial readouts of c written; (l, w) of c+1 written
+        }
+        if constexpr (READOUT) {
+            if (a.last_state && row_ok && seg == a.segments - 1) {
+                float* dst = a.last_state + (b * a.dim + d) * kN + n0;
+#pragma unroll
+                for (int k = 0; k < NG / 2; ++k)
+                    reinterpret_cast<float2*>(dst)[k] = make_float2(h[2 * k], h[2 * k + 1]);
+            }
+        } else {
+            const int64_t so = int64_t(seg) * a.batch * a.dim + b * a.dim + d;
+            if (row_ok) {
+                float* dst = a.seg_state + so * kN + n0;
+#pragma unroll
+                for (int k = 0; k < NG / 2; ++k)
+                    reinterpret_cast<float2*>(dst)[k] = make_float2(h[2 * k], h[2 * k + 1]);
+            }
+        }
+        return;
+    }
+
+    // ---------------- io wave: 16 rows x 16 tokens per chunk ----------------
+    // At a raised priority: the scan waves wait at each chunk's barrier for
+    // the io waves' (l, w), so these latency-bound waves issue first and the
+    // VALU-bound scans fill their gaps.
+    __builtin_amdgcn_s_setprio(1);
+    const int io = tid - NS * kWave;  // 0..255
+    const int r = io >> 2, q = io & 3;
+    const int64_t dp = d0 + r;
+    const bool prow_ok = dp < a.dim;
+    const int64_t prow = b * a.dim + (prow_ok ? dp : d0);  // clamped for safe reads
+    const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;
+    const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
+    const T* __restrict__ X = static_cast<const T*>(a.x);
+    const T* __restrict__ DL = static_cast<const T*>(a.delta);
+    const T* __restrict__ Z = static_cast<const T*>(a.z);
+    using V = typename std::conditional<sizeof(T) == 4, uint4, uint2>::type;
+    struct Group {
+        V x[QC], d[QC], z[LOADZ ? QC : 1];
+    };
+    // The lane's 4 tokens of chunk c: a vector past the row's end is read
+    // from the row's last vector instead (valid memory, values discarded).
+    auto ld = [&](const T* base, int c) -> V {
+        const int64_t ts = t_begin + int64_t(c) * CH + q * 4;
+        const T* p = base + prow * a.L + min(ts, a.L - 4);
+        if constexpr (sizeof(T) == 4) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+            return make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+            return make_uint2(v.x, v.y);
+        }
+    };
+    auto load_group = [&](int k, Group& g) {
+#pragma unroll
+        for (int j = 0; j < QC; ++j) g.x[j] = ld(X, k * QC + j);
+#pragma unroll
+        for (int j = 0; j < QC; ++j) g.d[j] = ld(DL, k * QC + j);
+        if constexpr (LOADZ) {
+#pragma unroll
+            for (int j = 0; j < QC; ++j) g.z[j] = ld(Z, k * QC + j);
+        }
+    };
+    auto unpack4 = [](const V& v, float* o) {
+        if constexpr (sizeof(T) == 4) {
+            o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+            o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+        } else {
+            o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        }
+    };
+    double lsum_acc = 0.0;
+    uint32_t sink = 0;
+    // per-token phase of chunk c (tokens past the segment end: identity steps)
+    auto prologue = [&](int c, const V& xv, const V& dv, const V& zv, float* dxo, float* gzo) {
+        const int64_t ts = t_begin + int64_t(c) * CH + q * 4;
+        float xs[4], ds[4], zs[4];
+        unpack4(xv, xs);
+        unpack4(dv, ds);
+        if constexpr (LOADZ) unpack4(zv, zs);
+        const int nvalid = int(min(int64_t(4), max(int64_t(0), t_end - ts)));
+        float l[4], w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            l[e] = softplus_log2_of(fmaf(ds[e], kLog2e, biasl));
+            if (e >= nvalid) {
+                l[e] = 0.0f;
+                xs[e] = 0.0f;
+            }
+            w[e] = l[e] * xs[e];
+            if constexpr (MODE == 1) lsum_acc += double(l[e]);
+            if constexpr (READOUT) {
+                dxo[e] = Dd * xs[e];
+                gzo[e] = 1.0f;
+                if constexpr (LOADZ) gzo[e] = silu(zs[e]);
+            }
+        }
+        float4* dst = reinterpret_cast<float4*>(&sm.lw[c & 1][r * S::kLwB + q * 32]);
+        dst[0] = make_float4(l[0], w[0], l[1], w[1]);
+        dst[1] = make_float4(l[2], w[2], l[3], w[3]);
+    };
+    // The B/C records of chunk c (2 KB per block: NSB sub-blocks x NS scan
+    // waves x 128 bytes) are brought into the scalar data cache, which the
+    // CU's waves share, by scalar loads of one dword per 64-byte line from
+    // the io waves (a quarter each), one chunk ahead of the scan waves' own
+    // loads: those then hit that cache instead of waiting on L2.
+    auto prefetch_records = [&](int c) {
+        if constexpr (PREF) {
+            const int iw = wv - NS;
+            const float* base = a.P + ((b * a.psub + (t_begin + int64_t(c) * CH) / SB) * NS) * kRec + iw * 128;
+            using CP = const __attribute__((address_space(4))) uint32_t*;
+            uint32_t acc = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc ^= *(CP)(reinterpret_cast<uintptr_t>(base + 16 * k));
+            sink ^= acc;
+        }
+    };
+    // Chunk c's outputs: every lane issues exactly one vector store, to y
+    // when its 4 tokens are inside the segment (t_begin, t_end and ts are
+    // multiples of 4: they are all inside or all past it) and its row exists,
+    // else to the dump area. With a fixed number of memory operations per
+    // chunk the compiler's waits for the next chunks' loads count past the
+    // fresh stores instead of draining them.
+    auto epilogue = [&](int c, const float* dx, const float* gz) {
+        const int64_t ts = t_begin + int64_t(c) * CH + q * 4;
+        float4 acc = *reinterpret_cast<const float4*>(&sm.yp[c & 1][0][yp_index(r, q)]);
+#pragma unroll
+        for (int g = 1; g < NS; ++g) {
+            const float4 v = *reinterpret_cast<const float4*>(&sm.yp[c & 1][g][yp_index(r, q)]);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        float yv[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yv[e] = (yv[e] + dx[e]) * gz[e];
+        const bool real = prow_ok && c >= 0 && ts < t_end;
+        T* dst = real ? static_cast<T*>(a.y) + prow * a.L + ts : static_cast<T*>(a.dump) + 4 * (io & 15);
+        if constexpr (sizeof(T) == 4) {
+            u32x4 v = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]),
+                       __float_as_uint(yv[3])};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        } else {
+            const uint4 p = pack16<T, 4>(yv);
+            u32x2 v = {p.x, p.y};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(dst));
+        }
+    };
+
+    Group g0, g1;
+    float dx0[4], gz0[4], dx1[4], gz1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dx1[e] = gz1[e] = 0.0f;
+    prefetch_records(0);
+    load_group(0, g0);
+    load_group(1, g1);
+    prologue(0, g0.x[0], g0.d[0], LOADZ ? g0.z[0] : g0.x[0], dx0, gz0);
+    __syncthreads();
+    // Chunk c's inputs are slot c % QC of group (c / QC) % 2; group k + 2 is
+    // loaded into the set of group k once its last chunk has been formed
+    // (addresses past the row's end read its last vector). The loop is
+    // unrolled over 2 QC chunks so that every slot index is a compile-time
+    // constant, and every iteration issues the same loads and stores.
+    for (int c0 = 0; c0 < nch; c0 += 2 * QC) {
+#pragma unroll
+        for (int j = 0; j < 2 * QC; ++j) {
+            const int c = c0 + j;
+            prefetch_records(min(c + 1, nchunks - 1));
+            // chunk c - 1's outputs first (chunk -1: a store to the dump
+            // area): its D x and gate values share a buffer with chunk c + 1's,
+            // which the prologue below overwrites
+            if constexpr (READOUT)
+                epilogue(c - 1, j & 1 ? dx0 : dx1, j & 1 ? gz0 : gz1);
+            Group& gn = ((j + 1) / QC) % 2 == 0 ? g0 : g1;  // set of chunk c + 1
+            constexpr int QCc = QC;
+            const int sn = (j + 1) % QCc;
+            prologue(c + 1, gn.x[sn], gn.d[sn], LOADZ ? gn.z[sn] : gn.x[sn], j & 1 ? dx0 : dx1,
+                     j & 1 ? gz0 : gz1);
+            if (sn == QC - 1) load_group((c + 1) / QC + 2, gn);
+            __syncthreads();
+        }
+    }
+    if constexpr (READOUT) epilogue(nch - 1, dx1, gz1);
+    if constexpr (MODE == 1) {
+        // step-size sum of the row: the 4 lanes of a row (a quad) add their
+        // sums in a fixed order
+        double v = lsum_acc;
+        const double v1 = __shfl_xor(v, 1, 64);
+        v = q & 1 ? v1 + v : v + v1;          // (q0 + q1), (q2 + q3)
+        const double v2 = __shfl_xor(v, 2, 64);
+        v = q & 2 ? v2 + v : v + v2;          // (q0 + q1) + (q2 + q3)
+        if (q == 0 && prow_ok) a.seg_lsum[int64_t(seg) * a.batch * a.dim + b * a.dim + dp] = v;
+    }
+    if (PREF && a.dim < 0) static_cast<uint32_t*>(a.y)[0] = sink;  // never true: keeps the prefetch loads
+}
+
+template <typename T, int NS, int MODE, bool PREF>
+hipError_t launch_ws_t(const FwdKArgs& k, bool gate, int64_t blocks, hipStream_t st) {
+    const dim3 grid{unsigned(blocks)}, block{unsigned(kWave * (NS + kWsIo))};
+    if (gate && MODE == 0)
+        hipLaunchKernelGGL((fwd_ws_kernel<T, NS, true, MODE, PREF>), grid, block, 0, st, k);
+    else
+        hipLaunchKernelGGL((fwd_ws_kernel<T, NS, false, MODE, PREF>), grid, block, 0, st, k);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_ws(DType dt, const FwdKArgs& k, int ns, bool pref, bool gate, int64_t blocks,
+                     hipStream_t st) {
+    if (dt == DType::BF16) {
+        if (ns == 8) return pref ? launch_ws_t<bf16_bits, 8, MODE, true>(k, gate, blocks, st)
+                                 : launch_ws_t<bf16_bits, 8, MODE, false>(k, gate, blocks, st);
+        return pref ? launch_ws_t<bf16_bits, 4, MODE, true>(k, gate, blocks, st)
+                    : launch_ws_t<bf16_bits, 4, MODE, false>(k, gate, blocks, st);
+    }
+    if (ns == 8) return pref ? launch_ws_t<float, 8, MODE, true>(k, gate, blocks, st)
+                             : launch_ws_t<float, 8, MODE, false>(k, gate, blocks, st);
+    return pref ? launch_ws_t<float, 4, MODE, true>(k, gate, blocks, st)
+                : launch_ws_t<float, 4, MODE, false>(k, gate, blocks, st);
+}
+
 // Pack B and C ([batch, 16, L] of T) into the fp32 record layout above, for
 // Lp >= L tokens (a multiple of the chunk), zero past L. One thread writes one
 // float4 of a 16-float half-record (B or C of one (b, s, g)), so a wave
@@ -843,7 +1241,10 @@ hipError_t output_pass(DType dt, const FwdKArgs& k, const FwdPlan& p, bool gate,
                        hipStream_t st) {
     if (p.ev_begin && hipEventRecord(p.ev_begin, st) != hipSuccess) return hipGetLastError();
     hipError_t e;
-    if (k.cw) {
+    if (p.ws) {
+        if (k.cw || k.ckpt) return hipErrorInvalidValue;
+        e = launch_ws<0>(dt, k, p.groups, p.pref, gate, blocks, st);
+    } else if (k.cw) {
         if (p.groups != 4 || k.ckpt) return hipErrorInvalidValue;
         e = dt == DType::BF16 ? dispatch_gv<bf16_bits, 4, 4>(k, gate, p.vec, blocks, st)
                               : dispatch_gv<float, 4, 4>(k, gate, p.vec, blocks, st);
@@ -890,13 +1291,16 @@ hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t 
     return hipGetLastError();
 }
 
+// Workspace: packed B/C records; with segments, the segment states, carries
+// and step sums; with the warp-specialised kernel, 256 bytes of dump area.
 size_t fwd_workspace_bytes(const FwdShape& s, const FwdPlan& p) {
     const size_t packed = size_t(s.batch) * size_t(padded_len(s.L)) * 2 * kN * sizeof(float);
-    if (p.segments <= 1) return align256(packed);
+    const size_t dump = p.ws ? 256 : 0;
+    if (p.segments <= 1) return align256(packed) + dump;
     const size_t rows = size_t(s.batch) * size_t(s.dim);
     const size_t states = size_t(p.segments) * rows * kN * sizeof(float);
     return align256(packed) + 2 * align256(states) +
-           align256(size_t(p.segments) * rows * sizeof(double));
+           align256(size_t(p.segments) * rows * sizeof(double)) + dump;
 }
 
 hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, void* workspace,
@@ -919,6 +1323,7 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     k.psub = Lp / p.groups;
     k.segments = p.segments;
     k.row_blocks = int32_t((s.dim + kWave - 1) / kWave);
+    if (p.ws) k.dump = ws + fwd_workspace_bytes(s, p) - 256;
     const bool gate = t.z != nullptr;
     const int64_t per_seg = int64_t(k.row_blocks) * s.batch;
 
@@ -944,7 +1349,9 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     k1.seg_lsum = seg_lsum;
     k1.h0 = nullptr;
     k1.ckpt = nullptr;
-    if (t.conv_w) {
+    if (p.ws) {
+        e = launch_ws<1>(s.dtype, k1, p.groups, p.pref, false, per_seg * (p.segments - 1), stream);
+    } else if (t.conv_w) {
         if (p.groups != 4) return hipErrorInvalidValue;
         e = s.dtype == DType::BF16
                 ? dispatch_gv<bf16_bits, 4, 5>(k1, false, p.vec, per_seg * (p.segments - 1), stream)

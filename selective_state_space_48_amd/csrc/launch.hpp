@@ -44,8 +44,12 @@ struct FwdShape {
 struct FwdPlan {
     int32_t segments;
     int64_t seg_len;
-    int32_t groups;
+    int32_t groups;  // waves per block of the per-wave kernel; scan waves of the specialised one
     bool vec;  // 16-byte vector access to rows is valid (L * elem_size % 16 == 0)
+    // The warp-specialised kernel (scan waves and io waves) instead of the
+    // per-wave one; pref: its io waves also load the B/C records of the next
+    // chunk into the scalar cache.
+    bool ws = false, pref = false;
     // When set, recorded on the stream right before and after the output-pass
     // kernel (measurement only).
     hipEvent_t ev_begin = nullptr, ev_end = nullptr;

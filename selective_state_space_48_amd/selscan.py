@@ -40,7 +40,8 @@ class FwdOpts(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64), ("segments", ctypes.c_int32),
                 ("groups", ctypes.c_int32), ("ckpt", ctypes.c_void_p),
                 ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
-                ("conv_x_prev", ctypes.c_void_p), ("conv_x_last", ctypes.c_void_p)]
+                ("conv_x_prev", ctypes.c_void_p), ("conv_x_last", ctypes.c_void_p),
+                ("variant", ctypes.c_int32)]
 
 
 class StepOpts(ctypes.Structure):
@@ -153,7 +154,7 @@ def _stream(device: torch.device):
 
 def workspace_size(batch: int, L: int, dim: int, dtype: torch.dtype, N: int = 16, *,
                    segments: int = 0, groups: int = 0, ckpt: bool = False,
-                   conv: bool = False) -> int:
+                   conv: bool = False, variant: int = 0) -> int:
     """Bytes of device workspace a forward call of this shape needs; ``ckpt`` and
     ``conv`` say whether the call passes checkpoints or the fused convolution's
     taps (they restrict the automatic plan to 4-wave launches)."""
@@ -162,7 +163,7 @@ def workspace_size(batch: int, L: int, dim: int, dtype: torch.dtype, N: int = 16
     # the memory: a placeholder address stands for "set".
     flag = ctypes.c_void_p(256)
     opts = FwdOpts(None, None, 0, int(segments), int(groups), flag if ckpt else None,
-                   flag if conv else None)
+                   flag if conv else None, None, None, None, int(variant))
     out = ctypes.c_uint64(0)
     _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out)))
     return int(out.value)
@@ -190,7 +191,7 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
         dt_bias: Optional[torch.Tensor] = None, *, y: Optional[torch.Tensor] = None,
         last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
         h0: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-        segments: int = 0, groups: int = 0,
+        segments: int = 0, groups: int = 0, variant: int = 0,
         ckpt: Optional[torch.Tensor] = None, conv_w: Optional[torch.Tensor] = None,
         conv_b: Optional[torch.Tensor] = None, conv_x_prev: Optional[torch.Tensor] = None,
         conv_x_last: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -206,8 +207,8 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     allocated here. ``h0`` [batch, dim, N] fp32 is the state entering token 0
     (None: zeros; it may be ``last_state`` itself). ``workspace`` is a uint8
     device tensor of at least ``workspace_size(...)`` bytes; by default one is
-    taken from torch's caching allocator. ``segments``/``groups`` select the
-    launch (0 = automatic).
+    taken from torch's caching allocator. ``segments``/``groups``/``variant``
+    select the launch (0 = automatic; see selscan_fwd_opts_t).
     """
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
@@ -238,7 +239,7 @@ def fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     _req(conv_x_last, "conv_x_last", torch.float32, (batch, dim, CONV_WIDTH - 1), dev)
     dims = Dims(batch, L, dim, N, _DTYPES[x.dtype])
     opts = FwdOpts(None, None, 0, int(segments), int(groups), _ptr(ckpt), _ptr(conv_w), _ptr(conv_b),
-                   _ptr(conv_x_prev), _ptr(conv_x_last))
+                   _ptr(conv_x_prev), _ptr(conv_x_last), int(variant))
     need = ctypes.c_uint64(0)
     _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(need)))
     if workspace is None and need.value > 0:

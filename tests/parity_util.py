@@ -30,7 +30,7 @@ def to_np(t):
 
 
 def gpu_fwd(inp, dtype, *, use_D=True, use_bias=True, use_z=True, segments=0, groups=0,
-            last_state=True):
+            last_state=True, variant=0, h0=None):
     from selective_state_space_48_amd import selscan
 
     td = TDT[dtype]
@@ -39,7 +39,8 @@ def gpu_fwd(inp, dtype, *, use_D=True, use_bias=True, use_z=True, segments=0, gr
                         D=dev(inp["D"]) if use_D else None,
                         z=dev(inp["z"], td) if (use_z and inp.get("z") is not None) else None,
                         dt_bias=dev(inp["dt_bias"]) if use_bias else None,
-                        return_last_state=last_state, segments=segments, groups=groups)
+                        return_last_state=last_state, segments=segments, groups=groups,
+                        variant=variant, h0=None if h0 is None else dev(h0))
     torch.cuda.synchronize()
     return y, hs
 

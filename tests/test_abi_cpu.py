@@ -202,9 +202,9 @@ def test_step_fused_conv_option_checks():
     assert call(dims=D(batch=0), opts=False) == S.OK
 
 
-def workspace_size(dims, segments=0, groups=0):
+def workspace_size(dims, segments=0, groups=0, variant=0):
     out = ctypes.c_uint64(7)
-    opts = S.FwdOpts(None, None, 0, segments, groups)
+    opts = S.FwdOpts(None, None, 0, segments, groups, None, None, None, None, None, variant)
     rc = S.lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out))
     return rc, out.value
 
@@ -212,7 +212,9 @@ def workspace_size(dims, segments=0, groups=0):
 def test_workspace_size():
     # packed B/C: batch * ceil(L/32)*32 * 2 * 16 fp32, rounded to 256 bytes
     assert workspace_size(D(batch=8, L=2048, dim=4096, dtype=S.BF16)) == (S.OK, 8 * 2048 * 128)
-    assert workspace_size(D(batch=1, L=100, dim=64)) == (S.OK, 128 * 128)
+    assert workspace_size(D(batch=1, L=100, dim=64), variant=1) == (S.OK, 128 * 128)
+    # the warp-specialised kernel adds 256 bytes (the dump area of rows past dim)
+    assert workspace_size(D(batch=1, L=100, dim=64), variant=2, segments=1) == (S.OK, 128 * 128 + 256)
     assert workspace_size(D(L=0)) == (S.OK, 0)
     assert workspace_size(D(dim=0)) == (S.OK, 0)
     # a split sequence adds per-segment states (fp32) and step sums (fp64)
@@ -230,25 +232,61 @@ def test_workspace_size():
 
 
 def test_plan_with_checkpoints_or_conv_stays_four_waves():
-    """At 160-256 row blocks the automatic plan takes 8-wave blocks in one pass
-    (workspace = the packed B/C alone), but checkpoints and the fused
-    convolution exist only as 4-wave kernels: with either option the plan
-    must fall back to the 4-wave rule, which segments this grid (768 waves)."""
+    """At 192 row blocks (fp32) the automatic plan takes the warp-specialised
+    kernel in one pass (workspace = the packed B/C and its 256-byte dump
+    area), and the per-wave plan 8-wave blocks in one pass (the packed B/C
+    alone); checkpoints and the fused convolution exist only as 4-wave
+    per-wave kernels: with either option the plan must fall back to the
+    4-wave rule, which segments this grid (768 waves)."""
     import torch
     packed = 8 * 2048 * 128
-    assert S.workspace_size(8, 2048, 1536, torch.float32) == packed
+    assert S.workspace_size(8, 2048, 1536, torch.float32) == packed + 256
+    assert S.workspace_size(8, 2048, 1536, torch.float32, variant=1) == packed
     with_ck = S.workspace_size(8, 2048, 1536, torch.float32, ckpt=True)
     with_cv = S.workspace_size(8, 2048, 1536, torch.float32, conv=True)
-    assert with_ck == with_cv > packed
+    assert with_ck == with_cv > packed + 256
     # explicit 4-wave plan with the same segment rule gives the same size
     assert S.workspace_size(8, 2048, 1536, torch.float32, groups=4) == with_ck
 
 
+def test_automatic_kernel_choice():
+    """Where the automatic plan takes the warp-specialised kernel, read back
+    from the 256-byte dump area it adds to the workspace of the same segment
+    plan: fp32 below 1024 row blocks, bf16 at 160-256, never for rows that
+    are not whole 4-token vectors; and the variant option's checks."""
+    import torch
+
+    def chosen(batch, L, dim, dt):
+        blocks = (dim + 63) // 64 * batch
+        same_plan = S.workspace_size(batch, L, dim, dt, variant=1, groups=4,
+                                     segments=1 if blocks >= 160 else 0)
+        return S.workspace_size(batch, L, dim, dt) == same_plan + 256
+
+    f32, bf = torch.float32, torch.bfloat16
+    assert chosen(8, 2048, 1536, f32)          # 192 blocks
+    assert chosen(8, 2048, 2560, f32)          # 320
+    assert chosen(8, 2048, 1024, f32)          # 128, segmented
+    assert chosen(1, 1 << 20, 128, f32)        # 2 blocks, long: segmented
+    assert not chosen(8, 2048, 8192, f32)      # 1024: per-wave
+    assert chosen(8, 2048, 1536, bf)           # 192 blocks bf16
+    assert not chosen(8, 2048, 1024, bf)       # 128 blocks bf16: per-wave
+    assert not chosen(8, 2048, 4096, bf)       # 512 blocks bf16 (the headline shape): per-wave
+    assert not chosen(8, 2046, 1536, f32)      # rows not whole 4-token vectors
+    # variant checks
+    assert workspace_size(D(), variant=4)[0] == S.ERR_CONFIG
+    assert workspace_size(D(), variant=-1)[0] == S.ERR_CONFIG
+    assert workspace_size(D(), variant=2, groups=2)[0] == S.ERR_CONFIG
+    assert workspace_size(D(L=30), variant=2)[0] == S.ERR_CONFIG
+    assert workspace_size(D(), variant=2, groups=8)[0] == S.OK
+    assert workspace_size(D(), variant=3, groups=4)[0] == S.OK
+
+
 def _segments_from_workspace(batch, L, dim):
-    """The automatic segment count, read back from the workspace size."""
+    """The automatic segment count of the per-wave kernel, read back from the
+    workspace size."""
     rows = batch * dim
     packed = batch * ((L + 31) // 32 * 32) * 128
-    rc, total = workspace_size(D(batch=batch, L=L, dim=dim, dtype=S.BF16))
+    rc, total = workspace_size(D(batch=batch, L=L, dim=dim, dtype=S.BF16), variant=1)
     assert rc == S.OK
     if total == packed:
         return 1
