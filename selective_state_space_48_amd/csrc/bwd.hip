@@ -113,7 +113,7 @@ template <> struct Quad<bf16_bits> {
     }
     static __device__ __forceinline__ V pack(const float* f) {
         auto p = [](float a, float b) {
-            return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
+            return pack_bf16x2(a, b);
         };
         return make_uint2(p(f[0], f[1]), p(f[2], f[3]));
     }

@@ -28,6 +28,14 @@ template <> __device__ __forceinline__ bf16_bits from_f32<bf16_bits>(float v) {
     return __builtin_bit_cast(bf16_bits, (__bf16)v);
 }
 
+// Two floats rounded to bfloat16 (nearest even) and packed low, high into a
+// 32-bit word: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // The two bfloat16 halves of a 32-bit word, as fp32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -50,7 +50,7 @@ __device__ __forceinline__ u32x4 pack_vec(const float* f) {
         v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
     } else {
         auto p = [](float a, float b) {
-            return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
+            return pack_bf16x2(a, b);
         };
         v.x = p(f[0], f[1]); v.y = p(f[2], f[3]); v.z = p(f[4], f[5]); v.w = p(f[6], f[7]);
     }

@@ -73,7 +73,7 @@ __device__ __forceinline__ uint4 pack16(const float* f) {
         v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
     } else {
         auto p = [](float a, float b) {
-            return uint32_t(from_f32<bf16_bits>(a)) | (uint32_t(from_f32<bf16_bits>(b)) << 16);
+            return pack_bf16x2(a, b);
         };
         v.x = p(f[0], f[1]); v.y = p(f[2], f[3]);
         if constexpr (E == 8) {
@@ -145,7 +145,19 @@ constexpr int kRec = 32;  // floats per (b, s, g) record
 // LDS of one workgroup: the per-token pairs (l, w) of the current chunk and
 // the partial readouts of the G waves. Row strides are odd multiples of 16
 // bytes, so 16-byte accesses by consecutive lanes to consecutive rows do not
-// conflict.
+// conflict. The (l, w) of token pair k (16 bytes) sit at piece lw_swizzle(k)
+// of the row: the G threads of a row write their token slices in the same
+// instruction, and without the swizzle slices 64 bytes apart (G = 4) fall in
+// the same banks; the scan reads token pairs (16 bytes, 8 lanes per pass)
+// from 8 consecutive rows, conflict-free at the odd row stride.
+template <int G>
+__device__ __forceinline__ constexpr int lw_swizzle(int k) {
+    // flip a bit of the pair index in the upper half of the chunk's 16 pairs:
+    // the piece positions (mod 8 pieces = 32 banks) of the G threads of two
+    // rows then all differ
+    return k ^ (((k >> 3) & 1) * (G == 2 ? 4 : G == 4 ? 2 : 0));
+}
+
 template <int G, int CH, int MODE>
 struct alignas(16) Smem {
     static constexpr int kPairB = CH * 8 + 16;  // float2-per-token row stride (bytes)
@@ -403,6 +415,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         }
     };
 
+    // The swizzled pieces of this thread's token pairs: k = pq TS/2 + jj maps
+    // to pq TS/2 + (jj ^ X) with X < TS/2 fixed per thread.
+    int lw_piece[TS / 2];
+#pragma unroll
+    for (int jj = 0; jj < TS / 2; ++jj) lw_piece[jj] = lw_swizzle<G>(pq * (TS / 2) + jj);
     // ---- per-token phase before the scan ----
     // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this thread's
     // registers until its epilogue of the same slice. Tokens past the segment
@@ -447,7 +464,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 xs[e] = silu(fmaf(cw4.w, win[e + 3], fmaf(cw4.z, win[e + 2],
                              fmaf(cw4.y, win[e + 1], fmaf(cw4.x, win[e], cbias)))));
         }
-        float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]) + pq * TS / 2;
+        float4* lwrow = reinterpret_cast<float4*>(&sm.lw[pr * S::kPairB]);
         auto body = [&](auto masked) {
             const int nvalid = masked ? int(min(int64_t(TS), max(int64_t(0), t_end - ts))) : TS;
 #pragma unroll
@@ -468,7 +485,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                         if constexpr (LOADZ) gzo[j + u] = silu(zs[j + u]);
                     }
                 }
-                lwrow[j / 2] = make_float4(l[0], w[0], l[1], w[1]);
+                lwrow[lw_piece[j / 2]] = make_float4(l[0], w[0], l[1], w[1]);
             }
         };
         if (t_begin + int64_t(c + 1) * CH <= t_end) body(std::false_type{});
@@ -486,14 +503,29 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         const int64_t s0 = (t_begin + int64_t(c) * CH) / SB;          // first sub-block
         const float* rec = a.P + ((b * a.psub + s0) * G + wv) * kRec;  // this wave's record
         const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kPairB]);
+        // the (l, w) of the SB tokens of sub-block sb: SB/2 consecutive token
+        // pairs starting at piece lw_swizzle(sb * SB / 2) (the swizzle keeps the
+        // pairs of a sub-block together); single tokens for SB = 1
+        auto read_lw = [&](int sb, float2* out) {
+            if constexpr (SB >= 2) {
+                const float4* q4 = reinterpret_cast<const float4*>(lw2) + lw_swizzle<G>(sb * (SB / 2));
+#pragma unroll
+                for (int e = 0; e < SB / 2; ++e) {
+                    const float4 v = q4[e];
+                    out[2 * e] = make_float2(v.x, v.y);
+                    out[2 * e + 1] = make_float2(v.z, v.w);
+                }
+            } else {
+                out[0] = lw2[sb];
+            }
+        };
         float* yrow = reinterpret_cast<float*>(&sm.yp[READOUT ? wv : 0][lane * S::kYB]);
         // Ping-pong operand buffers (two sub-blocks per loop trip), so that no
         // register has to be copied at the loop back-edge.
         f32x16 B0 = sload64(rec), C0, B1, C1;
         if constexpr (READOUT) C0 = sload64(rec + 16);
         float2 l0[SB], l1[SB];
-#pragma unroll
-        for (int e = 0; e < SB; ++e) l0[e] = lw2[e];
+        read_lw(0, l0);
         float yA[SB], yB[SB];
         auto put = [&](int sb, const float* yv) {  // partial readouts of sub-block sb
             if constexpr (SB >= 4) {
@@ -522,8 +554,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             const float* nrec = rec + int64_t(sbn) * (G * kRec);
             Bn = sload64(nrec);
             if constexpr (READOUT) Cn = sload64(nrec + 16);
-#pragma unroll
-            for (int e = 0; e < SB; ++e) ln[e] = lw2[sbn * SB + e];
+            read_lw(sbn, ln);
             // The previous sub-block's readouts. At sb = 0 there is none: the
             // write goes to the chunk's last slot, which the final write below
             // overwrites (same wave, LDS accesses in order).

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 const float recv = __builtin_bit_cast(
                     float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xb1, 0xf, 0xf, false));
                 const float lo = odd ? recv : v[r], hi = odd ? v[r + 1] : recv;
-                ypend[r / 2] = uint32_t(tobf(lo)) | (uint32_t(tobf(hi)) << 16);
+                ypend[r / 2] = pack_bf16x2(lo, hi);
             }
         }
         // ---- state: H <- 2^cum_end H + (w B)^T x over this wave's tiles ----
