@@ -77,18 +77,30 @@ struct BwdKArgs {
     int32_t row_blocks, nck, segments, seg0;
 };
 
-// LDS: per-token (l, w) and ds of the chunk for the scan waves, and the
-// waves' per-token partial sums over their states (sum q A, sum dh B', and,
-// gated, sum C h). Row strides are odd multiples of 16 bytes.
+// LDS: per-token l, w and ds of the chunk for the scan waves, and the waves'
+// per-token partial sums over their states (sum q A, sum dh B', and, gated,
+// sum C h). Every array holds 4 tokens per 16-byte piece, 64 bytes per row,
+// and every access is a 16-byte one, at a piece index swizzled so that no
+// access conflicts. On gfx950 a 16-byte read is served 16 lanes at a time
+// from 64 banks (so 16 lanes must hit 16 distinct pieces mod 16) and a
+// 16-byte write 8 lanes at a time from 32 banks (8 distinct pieces mod 8):
+// * quad_in: written by the per-token threads (4 per row; 8 lanes = 2 rows x
+//   4 pieces), read by them (16 lanes = 4 rows x 4 pieces) and by the scan
+//   lanes (one row each, 16 rows, one piece);
+// * quad_out: written by the scan lanes (8 rows, one piece), read by the
+//   per-token threads.
 struct alignas(16) BwdSmem {
-    static constexpr int kLW = kBCH * 8 + 16;
-    static constexpr int kDS = kBCH * 4 + 16;
-    unsigned char lw[kWave * kLW];
-    unsigned char ds[kWave * kDS];
-    unsigned char part[kBG][kWave * kLW];
-    unsigned char py[kBG][kWave * kDS];
+    float ql[kWave * kBCH];        // l = log2-unit step size
+    float qw[kWave * kBCH];        // w = l x
+    float qd[kWave * kBCH];        // ds = dy silu(z)
+    float pa[kBG][kWave * kBCH];   // per wave: sum over its states of q A
+    float pb[kBG][kWave * kBCH];   // sum of dh B'
+    float py[kBG][kWave * kBCH];   // sum of C h (gated)
     float bc[kBNSB * kBG * kRecF];  // the chunk's packed B/C records, as laid out in P
 };
+__device__ __forceinline__ int quad_in(int row, int k) { return row * 4 + (k ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int quad_out(int row, int k) { return row * 4 + (k ^ ((row >> 1) & 3)); }
+__device__ __forceinline__ float4& piece(float* base, int i) { return reinterpret_cast<float4*>(base)[i]; }
 
 // 4 consecutive tokens of type T as one load: 16 bytes (fp32) or 8 (bf16).
 template <typename T> struct Quad;
@@ -155,8 +167,7 @@ __device__ __forceinline__ void wave_sum16(const float* v, float* o) {
 template <typename T, bool GATE, bool VEC, bool CARRY>
 __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     using Q = Quad<T>;
-    using S = BwdSmem;
-    __shared__ S sm;
+    __shared__ BwdSmem sm;
     const T* __restrict__ X = static_cast<const T*>(a.x);
     const T* __restrict__ DL = static_cast<const T*>(a.delta);
     const T* __restrict__ Z = static_cast<const T*>(a.z);
@@ -286,10 +297,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
             k.sg[e] = exp2_hw(ul - lv);  // sigmoid(u) = e^u / (1 + e^u)
             if constexpr (CARRY) lsum_acc += double(l[e]);
         }
-        float4* lwr = reinterpret_cast<float4*>(&sm.lw[pr * S::kLW]) + pq * 2;
-        lwr[0] = make_float4(l[0], w[0], l[1], w[1]);
-        lwr[1] = make_float4(l[2], w[2], l[3], w[3]);
-        *(reinterpret_cast<float4*>(&sm.ds[pr * S::kDS]) + pq) = make_float4(dsv[0], dsv[1], dsv[2], dsv[3]);
+        const int qi = quad_in(pr, pq);
+        piece(sm.ql, qi) = make_float4(l[0], l[1], l[2], l[3]);
+        piece(sm.qw, qi) = make_float4(w[0], w[1], w[2], w[3]);
+        piece(sm.qd, qi) = make_float4(dsv[0], dsv[1], dsv[2], dsv[3]);
         reinterpret_cast<float2*>(sm.bc)[tid] = in.bc;
     };
 
@@ -309,10 +320,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     auto scan_chunk = [&](int c) {
         if constexpr (CARRY) {
             // only the adjoint carry: dh = ds C + carry, carry = exp(delta A) dh
-            const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kLW]);
-            const float* dsr = reinterpret_cast<const float*>(&sm.ds[lane * S::kDS]);
 #pragma unroll
             for (int sb = kBNSB - 1; sb >= 0; --sb) {
+                const float4 L4 = piece(sm.ql, quad_in(lane, sb)), D4 = piece(sm.qd, quad_in(lane, sb));
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
                 float Cv[16];
                 const float4* r = reinterpret_cast<const float4*>(sm.bc + (sb * kBG + wv) * kRecF);
 #pragma unroll
@@ -322,8 +333,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
                 }
 #pragma unroll
                 for (int e = kBSB - 1; e >= 0; --e) {
-                    const int t = sb * kBSB + e;
-                    const float lx = lw2[t].x, ds = dsr[t];
+                    const float lx = Lv[e], ds = Dv[e];
 #pragma unroll
                     for (int j = 0; j < kBNG; ++j) {
                         const float dh = fmaf(ds, Cv[j * kBSB + e], carry[j]);
@@ -335,8 +345,6 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         }
         const float4 hs4 = *reinterpret_cast<const float4*>(a.ckpt + (int64_t(c) * rows + row) * kN + n0);
         const float hs[kBNG] = {hs4.x, hs4.y, hs4.z, hs4.w};
-        const float2* lw2 = reinterpret_cast<const float2*>(&sm.lw[lane * S::kLW]);
-        const float* dsr = reinterpret_cast<const float*>(&sm.ds[lane * S::kDS]);
         auto rec = [&](int sb) { return reinterpret_cast<const float4*>(sm.bc + (sb * kBG + wv) * kRecF); };
         float H[kBCH][kBNG];
         float h[kBNG] = {hs[0], hs[1], hs[2], hs[3]};
@@ -349,19 +357,18 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
                 const float4 v = r[q];
                 Bv[4 * q] = v.x; Bv[4 * q + 1] = v.y; Bv[4 * q + 2] = v.z; Bv[4 * q + 3] = v.w;
             }
+            const float4 L4 = piece(sm.ql, quad_in(lane, sb)), W4 = piece(sm.qw, quad_in(lane, sb));
+            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Wv[4] = {W4.x, W4.y, W4.z, W4.w};
 #pragma unroll
             for (int e = 0; e < kBSB; ++e) {
                 const int t = sb * kBSB + e;
-                const float2 lw = lw2[t];
 #pragma unroll
                 for (int j = 0; j < kBNG; ++j) {
-                    h[j] = fmaf(exp2_hw(lw.x * An[j]), h[j], lw.y * Bv[j * kBSB + e]);
+                    h[j] = fmaf(exp2_hw(Lv[e] * An[j]), h[j], Wv[e] * Bv[j * kBSB + e]);
                     H[t][j] = h[j];
                 }
             }
         }
-        float2* prt = reinterpret_cast<float2*>(&sm.part[wv][lane * S::kLW]);
-        float4* pyt = reinterpret_cast<float4*>(&sm.py[wv][lane * S::kDS]);
 #pragma unroll
         for (int sb = kBNSB - 1; sb >= 0; --sb) {
             float Bv[16], Cv[16];
@@ -372,12 +379,16 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
                 Bv[4 * q] = v.x; Bv[4 * q + 1] = v.y; Bv[4 * q + 2] = v.z; Bv[4 * q + 3] = v.w;
                 Cv[4 * q] = w.x; Cv[4 * q + 1] = w.y; Cv[4 * q + 2] = w.z; Cv[4 * q + 3] = w.w;
             }
-            float vB[16], vC[16], yv[kBSB];
+            const int qi = quad_in(lane, sb);
+            const float4 L4 = piece(sm.ql, qi), W4 = piece(sm.qw, qi), D4 = piece(sm.qd, qi);
+            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Wv[4] = {W4.x, W4.y, W4.z, W4.w};
+            const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+            float vB[16], vC[16], yv[kBSB], av[kBSB], bv[kBSB];
 #pragma unroll
             for (int e = kBSB - 1; e >= 0; --e) {
                 const int t = sb * kBSB + e;
-                const float2 lw = lw2[t];
-                const float ds = dsr[t];
+                const float2 lw = make_float2(Lv[e], Wv[e]);
+                const float ds = Dv[e];
                 float accA = 0.0f, accB = 0.0f, accY = 0.0f;
 #pragma unroll
                 for (int j = 0; j < kBNG; ++j) {
@@ -391,10 +402,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
                     vC[e * 4 + j] = ds * H[t][j];
                     if constexpr (GATE) accY = fmaf(Cv[j * kBSB + e], H[t][j], accY);
                 }
-                prt[t] = make_float2(accA, accB);
+                av[e] = accA;
+                bv[e] = accB;
                 yv[e] = accY;
             }
-            if constexpr (GATE) pyt[sb] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+            const int qo = quad_out(lane, sb);
+            piece(sm.pa[wv], qo) = make_float4(av[0], av[1], av[2], av[3]);
+            piece(sm.pb[wv], qo) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+            if constexpr (GATE) piece(sm.py[wv], qo) = make_float4(yv[0], yv[1], yv[2], yv[3]);
             float sB[4], sC[4];
             wave_sum16(vB, sB);
             wave_sum16(vC, sC);
@@ -412,33 +427,33 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     auto epilogue = [&](int c, const Keep& k) {
         if constexpr (CARRY) return;
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
-        const float4* lwr = reinterpret_cast<const float4*>(&sm.lw[pr * S::kLW]) + pq * 2;
-        const float4 lw01 = lwr[0], lw23 = lwr[1];
-        const float4 ds4 = *(reinterpret_cast<const float4*>(&sm.ds[pr * S::kDS]) + pq);
-        const float kl[4] = {lw01.x, lw01.z, lw23.x, lw23.z};
-        const float kds[4] = {ds4.x, ds4.y, ds4.z, ds4.w};
+        const float4 L4 = piece(sm.ql, quad_in(pr, pq)), D4 = piece(sm.qd, quad_in(pr, pq));
+        const float kl[4] = {L4.x, L4.y, L4.z, L4.w}, kds[4] = {D4.x, D4.y, D4.z, D4.w};
+        const int qo = quad_out(pr, pq);
         float dxv[4], ddv[4], dzv[4];
         if constexpr (GATE) {
             // dz = dy silu'(z) (C.h + D x), the waves' partial sums added in order
-            float4 y4 = reinterpret_cast<const float4*>(&sm.py[0][pr * S::kDS])[pq];
+            float4 y4 = piece(sm.py[0], qo);
 #pragma unroll
             for (int g = 1; g < kBG; ++g) {
-                const float4 v = reinterpret_cast<const float4*>(&sm.py[g][pr * S::kDS])[pq];
+                const float4 v = piece(sm.py[g], qo);
                 y4.x += v.x; y4.y += v.y; y4.z += v.z; y4.w += v.w;
             }
             const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) dzv[e] = fmaf(Dd, k.x[e], yv[e]) * k.dzf[e];
         }
+        // the waves' (sum q A, sum dh B') of the thread's 4 tokens, added in wave order
+        float AAs[4] = {0.0f, 0.0f, 0.0f, 0.0f}, BBs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int g = 0; g < kBG; ++g) {
+            const float4 va = piece(sm.pa[g], qo), vb = piece(sm.pb[g], qo);
+            AAs[0] += va.x; AAs[1] += va.y; AAs[2] += va.z; AAs[3] += va.w;
+            BBs[0] += vb.x; BBs[1] += vb.y; BBs[2] += vb.z; BBs[3] += vb.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float AA = 0.0f, BB = 0.0f;
-#pragma unroll
-            for (int g = 0; g < kBG; ++g) {
-                const float2 p = reinterpret_cast<const float2*>(&sm.part[g][pr * S::kLW])[pq * kBTS + e];
-                AA += p.x;
-                BB += p.y;
-            }
+            const float AA = AAs[e], BB = BBs[e];
             // B was packed times ln 2: BB = ln2 * sum dh B, and delta = l ln 2.
             const float ddl = fmaf(k.x[e] * BB, kLog2e, AA);
             dxv[e] = fmaf(kl[e], BB, kds[e] * Dd);
@@ -517,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         if (row_ok)
             *reinterpret_cast<float4*>(a.rc_state + (ri * rows + row) * kN + n0) =
                 make_float4(carry[0], carry[1], carry[2], carry[3]);
-        double* red = reinterpret_cast<double*>(&sm.part[0][0]);
+        double* red = reinterpret_cast<double*>(&sm.pa[0][0]);
         red[pq * kWave + pr] = lsum_acc;
         __syncthreads();
         if (wv == 0 && row_ok) {
@@ -538,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         *reinterpret_cast<float4*>(a.pA + so * kN + n0) =
             make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
     }
-    float2* red = reinterpret_cast<float2*>(&sm.part[0][0]);
+    float2* red = reinterpret_cast<float2*>(&sm.pa[0][0]);
     red[pq * kWave + pr] = make_float2(dDacc, dTacc);
     __syncthreads();
     if (wv == 0 && row_ok) {

@@ -143,25 +143,40 @@ __device__ __forceinline__ f32x16 sload64(const float* p) {
 constexpr int kRec = 32;  // floats per (b, s, g) record
 
 // LDS of one workgroup: the per-token pairs (l, w) of the current chunk and
-// the partial readouts of the G waves. Row strides are odd multiples of 16
-// bytes, so 16-byte accesses by consecutive lanes to consecutive rows do not
-// conflict. The (l, w) of token pair k (16 bytes) sit at piece lw_swizzle(k)
-// of the row: the G threads of a row write their token slices in the same
-// instruction, and without the swizzle slices 64 bytes apart (G = 4) fall in
-// the same banks; the scan reads token pairs (16 bytes, 8 lanes per pass)
-// from 8 consecutive rows, conflict-free at the odd row stride.
+// the partial readouts of the G waves, accessed 16 bytes (a piece) at a time.
+// On gfx950 a 16-byte LDS write is served 8 lanes at a time from 32 banks and
+// a 16-byte read 16 lanes at a time from 64 banks, so the 8 lanes of a write
+// must hit distinct pieces mod 8 and the 16 lanes of a read distinct pieces
+// mod 16.
+// * (l, w): rows of 17 pieces; token pair k of a row at piece lw_swizzle(k).
+//   The scan reads one pair of 16 consecutive rows (distinct at the odd
+//   stride); the G threads of a row write their token slices in the same
+//   instruction, and without the swizzle slices 64 bytes apart (G = 4) would
+//   share banks. The swizzle keeps the pairs of a sub-block consecutive, so
+//   the 8 slices of one row (G = 8: 2 pairs each, of one parity) still meet
+//   two to a bank group.
+// * partial readouts: rows of 8 pieces (4 tokens each), piece k of row r at
+//   k ^ f(r) with f a permutation of r mod 8: the scan writes one piece of 8
+//   consecutive rows, and the per-token threads read 4 rows x 4 slices
+//   (G = 4), of which rows r and r + 2 share a half of the banks and get
+//   pieces of opposite parity. With one wave (a thread per row) rows are 9
+//   pieces apart instead.
 template <int G>
 __device__ __forceinline__ constexpr int lw_swizzle(int k) {
     // flip a bit of the pair index in the upper half of the chunk's 16 pairs:
-    // the piece positions (mod 8 pieces = 32 banks) of the G threads of two
-    // rows then all differ
+    // the pieces (mod 8) of the G threads of two rows then all differ
     return k ^ (((k >> 3) & 1) * (G == 2 ? 4 : G == 4 ? 2 : 0));
+}
+template <int G>
+__device__ __forceinline__ int yp_piece(int row, int k) {
+    if constexpr (G == 1) return row * (kChunk / 4 + 1) + k;
+    else return row * (kChunk / 4) + (k ^ (((row >> 1) & 3) | ((row & 1) << 2)));
 }
 
 template <int G, int CH, int MODE>
 struct alignas(16) Smem {
     static constexpr int kPairB = CH * 8 + 16;  // float2-per-token row stride (bytes)
-    static constexpr int kYB = CH * 4 + 16;     // float-per-token row stride (bytes)
+    static constexpr int kYB = CH * 4 + (G == 1 ? 16 : 0);  // float-per-token row stride (bytes)
     unsigned char lw[kWave * kPairB];
     static constexpr int kBase = MODE >= 4 ? MODE - 4 : MODE;  // 4, 5: 0, 1 with the conv
     static constexpr bool kReadout = kBase == 0 || kBase == 3;
@@ -519,7 +534,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                 out[0] = lw2[sb];
             }
         };
-        float* yrow = reinterpret_cast<float*>(&sm.yp[READOUT ? wv : 0][lane * S::kYB]);
+        float* yp = reinterpret_cast<float*>(&sm.yp[READOUT ? wv : 0][0]);
         // Ping-pong operand buffers (two sub-blocks per loop trip), so that no
         // register has to be copied at the loop back-edge.
         f32x16 B0 = sload64(rec), C0, B1, C1;
@@ -531,12 +546,13 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             if constexpr (SB >= 4) {
 #pragma unroll
                 for (int k = 0; k < SB / 4; ++k)
-                    *reinterpret_cast<float4*>(yrow + sb * SB + 4 * k) =
+                    reinterpret_cast<float4*>(yp)[yp_piece<G>(lane, sb * (SB / 4) + k)] =
                         make_float4(yv[4 * k], yv[4 * k + 1], yv[4 * k + 2], yv[4 * k + 3]);
             } else if constexpr (SB == 2) {
-                *reinterpret_cast<float2*>(yrow + sb * SB) = make_float2(yv[0], yv[1]);
+                *reinterpret_cast<float2*>(yp + 4 * yp_piece<G>(lane, sb >> 1) + 2 * (sb & 1)) =
+                    make_float2(yv[0], yv[1]);
             } else {
-                yrow[sb] = yv[0];
+                yp[4 * yp_piece<G>(lane, sb >> 2) + (sb & 3)] = yv[0];
             }
         };
         auto half = [&](int sb, const f32x16& Bc, const f32x16& Cc, const float2* lc, f32x16& Bn,
@@ -600,11 +616,11 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
         float yv[TS];
 #pragma unroll
         for (int j = 0; j < TS; j += 4) {
-            float4 acc = *reinterpret_cast<const float4*>(&sm.yp[0][pr * S::kYB + (pq * TS + j) * 4]);
+            const int yq = yp_piece<G>(pr, (pq * TS + j) / 4);
+            float4 acc = reinterpret_cast<const float4*>(&sm.yp[0][0])[yq];
 #pragma unroll
             for (int g = 1; g < G; ++g) {
-                const float4 q =
-                    *reinterpret_cast<const float4*>(&sm.yp[g][pr * S::kYB + (pq * TS + j) * 4]);
+                const float4 q = reinterpret_cast<const float4*>(&sm.yp[g][0])[yq];
                 acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
             }
             yv[j] = acc.x; yv[j + 1] = acc.y; yv[j + 2] = acc.z; yv[j + 3] = acc.w;
