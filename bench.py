@@ -35,11 +35,13 @@ TRANS_SLOTS = 2            # v_exp/v_log/v_rcp occupy a wave twice as long as an
 
 # HBM traffic of one output-pass launch on the headline workload: rocprofv3
 # --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
-# counter reads for a copy of known size with the same access pattern
-# (profiles/ holds the runs). It is valid only for the device code it was
-# taken on, identified by the sha256 of the forward kernel's sources: the part
-# of fwd.hip before the B/C pack (the kernel and everything it uses; the host
-# launch code comes after it) and common.hpp.
+# same counter reads for a plain copy kernel of known size (torch's copy of
+# 1 GiB: FETCH_SIZE reads half the bytes moved, WRITE_SIZE all of them; the
+# profiles/ summary also lists the factors of copies with the scan's row
+# access pattern, for comparison). It is valid only for the device code it
+# was taken on, identified by the sha256 of the forward kernel's sources: the
+# part of fwd.hip before the B/C pack (the kernels and everything they use;
+# the host launch code comes after it) and common.hpp.
 TRAFFIC = {"sources_sha256": "f5ba76788ad56e6bcb77b3796413a0c660b4f4d5cac4316ff691f213f82fe87a",
            "fetch_kib": 219127.6, "fetch_factor": 2.0, "write_kib": 147916.8, "write_factor": 1.0}
 
@@ -669,9 +671,9 @@ def measured_ceilings(torch, dev):
 
 
 def cpu_baseline(w, inp, reps=3):
-    """The oracle as it stands, on the whole workload (every row, every token;
-    about 1e9 (token, state) updates in float64), all host threads, repeated
-    ``reps`` times (some 10-30 s of CPU time in all)."""
+    """The oracle as it stands, on the whole headline workload (every row,
+    every token; about 1e9 (token, state) updates in float64), all host
+    threads, repeated ``reps`` times; plus one thread on one batch entry."""
     import oracle
 
     nt = oracle.default_threads()
@@ -695,6 +697,61 @@ def cpu_baseline(w, inp, reps=3):
             "single_thread": {"value": round(e1 / dt1 / 1e9, 6), "unit": "Gelem/s",
                               "sample": f"{sl.stop - sl.start} batch entries ({e1:,} elements), "
                                         f"{dt1:.2f} s on 1 thread"}}
+
+
+def cpu_baseline_per_config():
+    """The oracle timed on every workload of the benchmark's configuration
+    list, all host threads and one: the forward workloads over all their
+    rows (Gelem/s), the decode workload as the 512-token prefill of all 256
+    sequences (timed on its own) and one step over every row (us per step).
+    Some 20-40 s of host time in all."""
+    import oracle
+    from selective_state_space_48_amd import workloads as W
+
+    nt = oracle.default_threads()
+    res = {"cores": nt, "kind": "oracle"}
+    for name in ("tiny_f32_b1_l256_d16", "m130m_f32_b8_l2048_d1536", W.HEADLINE, "long_f32_b1_l1048576_d128"):
+        w = W.get(name)
+        inp = W.fwd_inputs(w)
+        kw = dict(D=inp["D"], z=inp["z"] if w.gate else None, dt_bias=inp["dt_bias"])
+        t0 = time.perf_counter()
+        oracle.fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], nthreads=nt, **kw)
+        dt = time.perf_counter() - t0
+        # one thread on a bounded slice: one batch entry, at most 32 rows
+        nr = min(w.dim, 32)
+        sl = (slice(0, 1), slice(0, nr))
+        t0 = time.perf_counter()
+        oracle.fwd(inp["x"][sl], inp["delta"][sl], inp["A"][:nr], inp["B"][:1], inp["C"][:1],
+                   D=inp["D"][:nr], z=None if kw["z"] is None else inp["z"][sl],
+                   dt_bias=inp["dt_bias"][:nr], nthreads=1)
+        dt1 = time.perf_counter() - t0
+        res[name] = {"Gelem_per_s": round(w.elements / dt / 1e9, 6), "s_wall": round(dt, 4),
+                     "Gelem_per_s_1_thread": round(nr * w.seqlen / dt1 / 1e9, 6),
+                     "sample": f"all {w.rows} rows x {w.seqlen} tokens on {nt} threads; "
+                               f"1 thread: {nr} rows"}
+        del inp
+    wd = W.get(W.DECODE)
+    p = W.params(wd)
+    t0 = time.perf_counter()
+    h = np.empty((wd.batch, wd.dim, wd.dstate))
+    gen = 0.0
+    for b in range(wd.batch):
+        g0 = time.perf_counter()
+        pre = W.prefill_inputs(wd, b)
+        gen += time.perf_counter() - g0
+        r = oracle.fwd(pre["x"], pre["delta"], p["A"], pre["B"], np.zeros_like(pre["B"]), D=p["D"],
+                       dt_bias=p["dt_bias"], nthreads=nt)
+        h[b] = r["last_state"][0]
+    prefill = time.perf_counter() - t0 - gen
+    si = W.step_inputs(wd, 0)
+    t0 = time.perf_counter()
+    oracle.step(h, si["x"], si["delta"], p["A"], si["B"], si["C"], D=p["D"], z=si["z"])
+    step = time.perf_counter() - t0
+    res[W.DECODE] = {"us_per_step": round(step * 1e6, 1), "prefill_s": round(prefill, 3),
+                     "sample": f"one step over all {wd.rows} rows (the step oracle is one "
+                               f"thread); prefill: {wd.prefill} tokens of all {wd.batch} "
+                               f"sequences on {nt} threads, input generation excluded"}
+    return res
 
 
 def copy_calibration(torch, dev, gib=1, reps=3):
@@ -798,7 +855,16 @@ def main():
                     "frac": round(hbm / HBM_PEAK, 4), "bytes_per_launch": bytes_,
                     "traffic_over_algorithmic": None if traffic is None else round(traffic / bytes_, 3),
                     "copy_GBps": ceil["copy_GBps"],
-                    "frac_of_copy": round(hbm / 1e9 / ceil["copy_GBps"], 4)},
+                    "frac_of_copy": round(hbm / 1e9 / ceil["copy_GBps"], 4),
+                    # the aim of 70% of the HBM peak on this workload, and why it
+                    # is out of reach for this method without packed fp32
+                    "target_frac": 0.70, "target_met": bool(hbm / HBM_PEAK >= 0.70),
+                    "bound_by": "VALU issue: one exp (2 slots) and four fp32 operations per "
+                                "(token, state) make 6 slots, 96 per element, plus the per-token "
+                                "softplus/silu; the method's 110 slots per element take "
+                                f"{slots / SLOT_PEAK * 1e6:.0f} us at the 2.4 GHz slot peak, "
+                                f"above the {bytes_ / (0.7 * HBM_PEAK) * 1e6:.0f} us that 70% of "
+                                "8 TB/s allows"},
             "per_call": dist,
             "wall_s_timed": round(wall, 4),
         })
@@ -813,10 +879,19 @@ def main():
         cold = ddist["cold"]["p50_us"]
         log(f"[bench] decode: {us:.2f} us/step back to back ({kus:.2f} us kernel, {gbs:.0f} GB/s); "
             f"cold median {cold:.2f} us")
-        extras["decode"] = {"workload": wd.name, "us_per_step": round(us, 3),
-                            "kernel_us": round(kus, 3), "achieved_GBps": round(gbs, 1),
-                            "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
-                            "cold_p50_GBps": round(step_bytes(wd) / (cold * 1e-6) / 1e9, 1),
+        # Primary: the median of the 64 distinct steps each run right after a
+        # 512 MB scratch write that evicts the last-level cache (the 84 MB
+        # state would otherwise stay in it between back-to-back steps; in a
+        # model the other layers run in between). Back to back: secondary.
+        cold_gbs = step_bytes(wd) / (cold * 1e-6) / 1e9
+        extras["decode"] = {"workload": wd.name, "us_per_step": round(cold, 3),
+                            "us_per_step_is": "cold p50 (caches evicted before each step)",
+                            "achieved_GBps": round(cold_gbs, 1),
+                            "frac_hbm": round(cold_gbs * 1e9 / HBM_PEAK, 4),
+                            "back_to_back_us_per_step": round(us, 3),
+                            "back_to_back_kernel_us": round(kus, 3),
+                            "back_to_back_kernel_GBps": round(gbs, 1),
+                            "back_to_back_kernel_frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4),
                             "bytes_per_step": step_bytes(wd), "per_step": ddist}
         # the same at one sequence, where the launches rather than the bytes set the rate
         extras["block_decode"] = [time_block_decode(wd, torch, dev),
@@ -869,6 +944,10 @@ def main():
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp)
         log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+        if not args.no_extras:
+            log("[bench] cpu baseline per configuration (oracle)")
+            out["cpu_baseline_per_config"] = cpu_baseline_per_config()
+            log(f"[bench] cpu baseline per configuration: {out['cpu_baseline_per_config']}")
 
     print(json.dumps(out), flush=True)
 
