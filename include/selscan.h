@@ -296,7 +296,8 @@ int selscan_step_ex(float* state, const void* x, const void* delta, const float*
  *                        whether or not D / dt_bias are given)
  * Workspace: about (B d ceil(L/16) + 2 B ceil(d/64) ceil(L/16) 16) * 64 bytes
  * (checkpoints and per-row-block partial sums; 0.4 GB at B 8, L 2048, d 4096),
- * taken with hipMallocAsync on the stream and returned with hipFreeAsync.
+ * taken with hipMallocAsync on the stream and returned with hipFreeAsync
+ * (selscan_bwd_ex takes caller-owned workspace instead).
  * Outputs must not overlap inputs or each other. Deterministic.
  */
 int selscan_bwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -327,6 +328,12 @@ int selscan_bwd(const void* x, const void* delta, const float* A, const void* B,
  *              chip). At most 65536; the segment length is rounded up to 32
  *              tokens, so fewer segments may run. Results agree to rounding;
  *              each choice is deterministic.
+ *   workspace : caller-owned device memory of workspace_bytes bytes, 256-byte
+ *               aligned, at least selscan_bwd_workspace_size(); NULL means
+ *               the library takes and returns its own on the stream. The
+ *               contents on entry do not matter; the call uses it until its
+ *               work on the stream completes. It must not overlap any input
+ *               or output.
  */
 typedef struct {
     const float* h0;
@@ -334,6 +341,8 @@ typedef struct {
     float* dh0;
     int32_t segments;
     const float* ckpt;
+    void* workspace;
+    uint64_t workspace_bytes;
 } selscan_bwd_opts_t;
 
 /*
@@ -358,6 +367,14 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
                    void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
                    float* ddt_bias, const selscan_dims_t* dims, const selscan_bwd_opts_t* opts,
                    void* stream);
+
+/*
+ * Bytes of workspace selscan_bwd_ex needs for these dims and options (only
+ * opts->segments and whether opts->ckpt is set matter; opts may be NULL).
+ * Host only. Returns SELSCAN_OK and sets *bytes, or an argument error.
+ */
+int selscan_bwd_workspace_size(const selscan_dims_t* dims, const selscan_bwd_opts_t* opts,
+                               uint64_t* bytes);
 
 /*
  * selscan_ssd_fwd — Mamba-2's state space dual (SSD) layer: the selective SSM

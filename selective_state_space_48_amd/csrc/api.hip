@@ -514,6 +514,7 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
                    float* ddt_bias, const selscan_dims_t* dims, const selscan_bwd_opts_t* opts,
                    void* stream) {
     const selscan_bwd_opts_t o = opts ? *opts : selscan_bwd_opts_t{};
+    if (o.workspace && (reinterpret_cast<uintptr_t>(o.workspace) & 255u)) return SELSCAN_ERR_CONFIG;
     if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
     Sizes sz;
     int rc = check_fwd_dims(dims, &sz);
@@ -569,8 +570,17 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
         ((dims->dim + kWave - 1) / kWave) * dims->batch * segments > INT32_MAX)
         return SELSCAN_ERR_DIMS;
     const size_t ws_bytes = bwd_workspace_bytes(dims->batch, L, dims->dim, segments, o.ckpt != nullptr);
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws) {
+    if (o.workspace) {
+        if (o.workspace_bytes < ws_bytes) return SELSCAN_ERR_CONFIG;
+        const Span w = span(o.workspace, int64_t(ws_bytes));
+        for (const Span& s : outs)
+            if (overlaps(s, w)) return SELSCAN_ERR_ALIAS;
+        for (const Span& s : ins)
+            if (overlaps(s, w)) return SELSCAN_ERR_ALIAS;
+    }
+    void* ws = o.workspace;
+    const bool own = ws == nullptr;
+    if (own && (hipMallocAsync(&ws, ws_bytes, st) != hipSuccess || !ws)) {
         (void)hipGetLastError();
         return SELSCAN_ERR_ALLOC;
     }
@@ -579,8 +589,25 @@ int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void*
     const hipError_t e = launch_bwd(t, dims->batch, L, dims->dim,
                                     dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32,
                                     segments, seg_len, ws, st);
-    (void)hipFreeAsync(ws, st);
+    if (own) (void)hipFreeAsync(ws, st);
     return e == hipSuccess ? SELSCAN_OK : SELSCAN_ERR_LAUNCH;
+}
+
+int selscan_bwd_workspace_size(const selscan_dims_t* dims, const selscan_bwd_opts_t* opts,
+                               uint64_t* bytes) {
+    if (!bytes) return SELSCAN_ERR_NULL;
+    Sizes sz;
+    const int rc = check_fwd_dims(dims, &sz);
+    if (rc != SELSCAN_OK) return rc;
+    const selscan_bwd_opts_t o = opts ? *opts : selscan_bwd_opts_t{};
+    if (o.segments < 0 || o.segments > 65536) return SELSCAN_ERR_CONFIG;
+    *bytes = 0;
+    if (sz.rows == 0 || dims->seqlen == 0) return SELSCAN_OK;
+    int32_t segments = 1;
+    int64_t seg_len = dims->seqlen;
+    bwd_segments(dims, o.segments, &segments, &seg_len);
+    *bytes = bwd_workspace_bytes(dims->batch, dims->seqlen, dims->dim, segments, o.ckpt != nullptr);
+    return SELSCAN_OK;
 }
 
 int selscan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,

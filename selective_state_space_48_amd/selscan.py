@@ -50,7 +50,8 @@ class StepOpts(ctypes.Structure):
 
 class BwdOpts(ctypes.Structure):
     _fields_ = [("h0", ctypes.c_void_p), ("dlast_state", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
-                ("segments", ctypes.c_int32), ("ckpt", ctypes.c_void_p)]
+                ("segments", ctypes.c_int32), ("ckpt", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class SsdDims(ctypes.Structure):
@@ -94,6 +95,8 @@ def _load() -> ctypes.CDLL:
     lib.selscan_bwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, vp, vp, vp, fp, vp, vp, fp, vp,
                                    fp, dims_p, ctypes.POINTER(BwdOpts), vp]
     lib.selscan_bwd_ex.restype = ctypes.c_int
+    lib.selscan_bwd_workspace_size.argtypes = [dims_p, ctypes.POINTER(BwdOpts), ctypes.POINTER(ctypes.c_uint64)]
+    lib.selscan_bwd_workspace_size.restype = ctypes.c_int
     lib.selscan_ssd_fwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, vp, fp, ctypes.POINTER(SsdDims), vp]
     lib.selscan_ssd_fwd.restype = ctypes.c_int
     lib.selscan_ssd_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, fp, fp, vp, fp, ctypes.POINTER(SsdDims), vp]
@@ -166,6 +169,17 @@ def workspace_size(batch: int, L: int, dim: int, dtype: torch.dtype, N: int = 16
                    flag if conv else None, None, None, None, int(variant))
     out = ctypes.c_uint64(0)
     _check(lib.selscan_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out)))
+    return int(out.value)
+
+
+def bwd_workspace_size(batch: int, L: int, dim: int, dtype: torch.dtype, N: int = 16, *,
+                       segments: int = 0, ckpt: bool = False) -> int:
+    """Bytes of device workspace a backward call of this shape needs (``ckpt``:
+    the call is given the forward's checkpoints)."""
+    dims = Dims(batch, L, dim, N, _DTYPES[dtype])
+    opts = BwdOpts(None, None, None, int(segments), ctypes.c_void_p(256) if ckpt else None)
+    out = ctypes.c_uint64(0)
+    _check(lib.selscan_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(out)))
     return int(out.value)
 
 
@@ -337,7 +351,8 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
         dt_bias: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
         want_dD: bool = True, want_ddt_bias: bool = True, segments: int = 0,
         h0: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
-        want_dh0: bool = False, ckpt: Optional[torch.Tensor] = None) -> dict:
+        want_dh0: bool = False, ckpt: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None) -> dict:
     """Backward pass (selscan_bwd): gradients for the output gradient ``dy``.
 
     Returns a dict with dx, ddelta, dB, dC (input dtype), dA [dim, N] fp32, and
@@ -345,7 +360,10 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
     ``h0`` (the forward's initial state), ``dlast_state`` (the gradient into
     its final state), ``want_dh0`` (adds dh0 [batch, dim, N] fp32), ``ckpt``
     (the checkpoints a ``fwd(..., ckpt=...)`` over the same inputs wrote) and
-    ``segments`` other than 0 (automatic) call selscan_bwd_ex.
+    ``segments`` other than 0 (automatic) are passed to selscan_bwd_ex.
+    ``workspace`` is a uint8 device tensor of at least ``bwd_workspace_size(...)``
+    bytes; by default one is taken from torch's allocator, so that the library
+    allocates nothing.
     """
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
@@ -378,11 +396,16 @@ def bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, 
             _ptr(dy), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
             _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out.get("ddt_bias")),
             ctypes.byref(dims))
-    if segments == 0 and h0 is None and dlast_state is None and not want_dh0 and ckpt is None:
-        _check(lib.selscan_bwd(*args, _stream(dev)))
-    else:
-        opts = BwdOpts(_ptr(h0), _ptr(dlast_state), _ptr(out.get("dh0")), segments, _ptr(ckpt))
-        _check(lib.selscan_bwd_ex(*args, ctypes.byref(opts), _stream(dev)))
+    opts = BwdOpts(_ptr(h0), _ptr(dlast_state), _ptr(out.get("dh0")), segments, _ptr(ckpt))
+    need = ctypes.c_uint64(0)
+    _check(lib.selscan_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(need)))
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _req(workspace, "workspace", torch.uint8, None, dev)
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel()
+    _check(lib.selscan_bwd_ex(*args, ctypes.byref(opts), _stream(dev)))
     return out
 
 

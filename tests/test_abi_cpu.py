@@ -22,7 +22,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"selscan_fwd", "selscan_fwd_ex", "selscan_fwd_workspace_size", "selscan_step", "selscan_step_ex",
-            "selscan_bwd", "selscan_bwd_ex", "selscan_conv1d_bwd", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
+            "selscan_bwd", "selscan_bwd_ex", "selscan_bwd_workspace_size", "selscan_conv1d_bwd", "selscan_ssd_fwd", "selscan_ssd_fwd_ex", "selscan_ssd_step", "selscan_conv1d", "selscan_conv1d_step",
             "selscan_timing_start",
             "selscan_timing_stop", "selscan_strerror", "selscan_version", "selscan_fwd_noalloc"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
@@ -432,6 +432,53 @@ def test_bwd_argument_checks():
     p = [P(i) for i in range(17)]
     p[13] = ctypes.c_void_p(BASE + 12 * SPAN + 64)  # dC inside dB
     assert bwd_call(D(), p) == S.ERR_ALIAS
+
+
+def bwd_ws_size(dims, segments=0, ckpt=False):
+    o = S.BwdOpts(segments=segments, ckpt=BASE if ckpt else None)
+    out = ctypes.c_uint64(0)
+    rc = S.lib.selscan_bwd_workspace_size(ctypes.byref(dims) if dims is not None else None,
+                                          ctypes.byref(o), ctypes.byref(out))
+    return rc, out.value
+
+
+def test_bwd_workspace_size():
+    # 1.4B-shaped layer: B/C records, checkpoints every 16 tokens, per-row-block
+    # dB/dC partials, per-row dA/dD/ddt_bias partials (one segment)
+    rows, nck = 8 * 4096, 2048 // 16
+    packed = 8 * 2048 * 2 * 16 * 4
+    ckpt = nck * rows * 16 * 4
+    pbc = 2 * (4096 // 64) * 8 * 2048 * 16 * 4
+    per_row = rows * 16 * 4 + 2 * rows * 4
+    dims = D(batch=8, L=2048, dim=4096, dtype=S.BF16)
+    assert bwd_ws_size(dims) == (S.OK, packed + ckpt + pbc + per_row)
+    assert bwd_ws_size(dims, ckpt=True) == (S.OK, packed + pbc + per_row)
+    assert bwd_ws_size(D(L=0)) == (S.OK, 0)
+    assert bwd_ws_size(D(batch=0)) == (S.OK, 0)
+    # more segments: more per-row partials and the segment states
+    rc1, b1 = bwd_ws_size(D(batch=1, L=4096, dim=128), segments=1)
+    rc4, b4 = bwd_ws_size(D(batch=1, L=4096, dim=128), segments=4)
+    assert rc1 == rc4 == S.OK and b4 > b1
+    assert bwd_ws_size(None)[0] == S.ERR_NULL
+    assert bwd_ws_size(D(N=8))[0] == S.ERR_DSTATE
+    assert bwd_ws_size(D(), segments=-1)[0] == S.ERR_CONFIG
+    out = ctypes.c_uint64(0)
+    assert S.lib.selscan_bwd_workspace_size(ctypes.byref(D()), None, None) == S.ERR_NULL
+    assert S.lib.selscan_bwd_workspace_size(ctypes.byref(D()), None, ctypes.byref(out)) == S.OK
+    assert out.value == bwd_ws_size(D())[1]
+
+
+def test_bwd_caller_workspace_checks():
+    p = [P(i) for i in range(17)]
+    need = bwd_ws_size(D())[1]
+    o = S.BwdOpts(workspace=BASE + 30 * SPAN + 16, workspace_bytes=need)   # not 256-byte aligned
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_CONFIG
+    o = S.BwdOpts(workspace=BASE + 30 * SPAN, workspace_bytes=need - 1)     # too small
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_CONFIG
+    o = S.BwdOpts(workspace=BASE + 9 * SPAN, workspace_bytes=need)          # over dx
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
+    o = S.BwdOpts(workspace=BASE + 0 * SPAN, workspace_bytes=need)          # over x
+    assert S.lib.selscan_bwd_ex(*p, ctypes.byref(D()), ctypes.byref(o), None) == S.ERR_ALIAS
 
 
 def test_bwd_ex_option_checks():

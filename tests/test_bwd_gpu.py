@@ -100,6 +100,34 @@ def test_bwd_deterministic():
         assert torch.equal(g1[k], g2[k]), k
 
 
+def test_bwd_library_workspace_matches_caller_workspace():
+    """selscan_bwd (the library takes and returns its workspace on the stream)
+    gives bit for bit what selscan_bwd_ex gives with a caller-owned workspace
+    (the binding's default) that holds garbage on entry."""
+    import ctypes
+    inp = small(M14, batch=2, seqlen=200, dim=128)
+    dy = W._maybe_bf16(W.get(M14), _dy((2, 128, 200), 7))
+    case("bwd library workspace vs caller workspace")
+    td = TDT["bf16"]
+    x, dl, A, B, C = (dev(inp["x"], td), dev(inp["delta"], td), dev(inp["A"]), dev(inp["B"], td),
+                      dev(inp["C"], td))
+    D, z, bias, g = dev(inp["D"]), dev(inp["z"], td), dev(inp["dt_bias"]), dev(dy, td)
+    need = selscan.bwd_workspace_size(2, 200, 128, torch.bfloat16)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=x.device)
+    g1 = selscan.bwd(x, dl, A, B, C, D=D, z=z, dt_bias=bias, dy=g, workspace=ws)
+    g2 = {k: torch.empty_like(v) for k, v in g1.items()}
+    dims = selscan.Dims(2, 200, 128, 16, selscan.BF16)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = selscan.lib.selscan_bwd(p(x), p(dl), p(A), p(B), p(C), p(D), p(z), p(bias), p(g),
+                                 p(g2["dx"]), p(g2["ddelta"]), p(g2["dA"]), p(g2["dB"]), p(g2["dC"]),
+                                 p(g2["dD"]), p(g2["dz"]), p(g2["ddt_bias"]), ctypes.byref(dims),
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == selscan.OK, selscan.strerror(rc)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g1[k], g2[k]), k
+
+
 def test_bwd_long_sequence_small_steps():
     """4096 tokens with step sizes ~1e-4..1e-2: long-lived states, many chunks."""
     inp = small("long_f32_b1_l1048576_d128", seqlen=4096, dim=64)
