@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     // block -> (segment, batch entry, 64-row block)
-    int64_t blk = blockIdx.x;
+    int64_t blk = xcd_tile(blockIdx.x, gridDim.x);
     const int rb = int(blk % a.row_blocks);
     blk /= a.row_blocks;
     const int64_t b = blk % a.batch;

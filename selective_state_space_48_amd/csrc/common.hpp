@@ -28,6 +28,17 @@ template <> __device__ __forceinline__ bf16_bits from_f32<bf16_bits>(float v) {
     return __builtin_bit_cast(bf16_bits, (__bf16)v);
 }
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) round robin:
+// workgroup i runs on XCD i % 8. xcd_tile renumbers them so that consecutive
+// tile numbers run on one XCD: of n = 8 q + r workgroups, XCD x takes the
+// tiles from x q + min(x, r) on, q + 1 of them if x < r, else q. Tiles that
+// read the same data (the row blocks of one batch entry and segment, which
+// share its B/C records) then share an L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t i, int64_t n) {
+    const int64_t q = n / 8, r = n % 8, x = i % 8;
+    return x * q + (x < r ? x : r) + i / 8;
+}
+
 // Two floats rounded to bfloat16 (nearest even) and packed low, high into a
 // 32-bit word: one v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     const int lane = tid % kWave;
 
     // block -> (segment, batch entry, 64-row block)
-    int64_t blk = blockIdx.x;
+    int64_t blk = xcd_tile(blockIdx.x, gridDim.x);
     const int rb = int(blk % a.row_blocks);
     blk /= a.row_blocks;
     const int64_t b = blk % a.batch;
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
 
-    int64_t blk = blockIdx.x;
+    int64_t blk = xcd_tile(blockIdx.x, gridDim.x);
     const int rb = int(blk % a.row_blocks);
     blk /= a.row_blocks;
     const int64_t b = blk % a.batch;
