@@ -436,8 +436,8 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
 #pragma unroll
     for (int jj = 0; jj < TS / 2; ++jj) lw_piece[jj] = lw_swizzle<G>(pq * (TS / 2) + jj);
     // ---- per-token phase before the scan ----
-    // (l, w) go to LDS for all G waves; D*x and silu(z) stay in this thread's
-    // registers until its epilogue of the same slice. Tokens past the segment
+    // (l, w) go to LDS for all G waves; x (for the D skip) and silu(z) stay
+    // in this thread's registers until its epilogue of the same slice. Tokens past the segment
     // end get l = w = 0, which makes their scan step the identity. B was
     // scaled by ln 2 when packed, so w = l * x with l in log2 units.
     auto prologue = [&](int c, const Slice& sl, float* dxo, float* gzo) {
@@ -495,8 +495,9 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
                     w[u] = l[u] * xs[j + u];
                     if constexpr (BASE == 1) lsum_acc += double(l[u]);
                     if constexpr (READOUT) {
-                        dxo[j + u] = Dd * xs[j + u];
-                        gzo[j + u] = 1.0f;
+                        // the D skip: x, multiplied in the epilogue's FMA (with
+                        // one wave, whose 32 tokens a thread holds, the product)
+                        dxo[j + u] = G == 1 ? Dd * xs[j + u] : xs[j + u];
                         if constexpr (LOADZ) gzo[j + u] = silu(zs[j + u]);
                     }
                 }
@@ -626,7 +627,10 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             yv[j] = acc.x; yv[j + 1] = acc.y; yv[j + 2] = acc.z; yv[j + 3] = acc.w;
         }
 #pragma unroll
-        for (int j = 0; j < TS; ++j) yv[j] = (yv[j] + dx[j]) * gz[j];
+        for (int j = 0; j < TS; ++j) {
+            yv[j] = G == 1 ? yv[j] + dx[j] : fmaf(Dd, dx[j], yv[j]);
+            if constexpr (LOADZ) yv[j] *= gz[j];
+        }
         T* Y = static_cast<T*>(a.y) + prow * a.L;
         // Rows off a 16-byte boundary (RAW, 16-byte vectors), chunk wholly
         // inside the row: the chunk's bytes are written as the aligned
@@ -685,8 +689,8 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
     // lead); otherwise chunk c+3 at every c (two chunks of lead). The
     // epilogue's y stores come after the loads, so no wait for loads (vmcnt,
     // which on this chip also counts stores) waits for fresh stores.
-    // Register sets: chunk c+1's inputs are in `next`; the D*x and gate
-    // values alternate between two arrays by chunk parity (no copies).
+    // Register sets: chunk c+1's inputs are in `next`; the D-skip inputs and
+    // gate values alternate between two arrays by chunk parity (no copies).
     constexpr bool PAIR = VEC && sizeof(T) * CH < 128;
     float dxA[TS], gzA[TS], dxB[TS], gzB[TS];
     // The scan runs at a raised wave priority and the per-token phases at the
@@ -794,7 +798,6 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     constexpr int NSB = CH / SB;       // sub-blocks per chunk
     constexpr bool READOUT = MODE == 0;
     constexpr bool LOADZ = GATE && READOUT;
-    constexpr int EB = 4 * int(sizeof(T));          // bytes per io load: 4 tokens
     constexpr int QC = 128 / (CH * int(sizeof(T)));  // chunks per load group (one line per row)
     static_assert(NS == 4 || NS == 8, "4 or 8 scan waves");
     static_assert(NSB % 2 == 0, "sub-blocks per chunk must be even");
@@ -956,18 +959,20 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     const int64_t prow = b * a.dim + (prow_ok ? dp : d0);  // clamped for safe reads
     const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;
     const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
-    const T* __restrict__ X = static_cast<const T*>(a.x);
-    const T* __restrict__ DL = static_cast<const T*>(a.delta);
-    const T* __restrict__ Z = static_cast<const T*>(a.z);
+    // this lane's row of each tensor; token indices within a row fit in 32 bits
+    const T* __restrict__ Xr = static_cast<const T*>(a.x) + prow * a.L;
+    const T* __restrict__ DLr = static_cast<const T*>(a.delta) + prow * a.L;
+    const T* __restrict__ Zr = LOADZ ? static_cast<const T*>(a.z) + prow * a.L : nullptr;
+    T* __restrict__ Yr = READOUT ? static_cast<T*>(a.y) + prow * a.L : nullptr;
+    const int tb = int(t_begin), te = int(t_end), L32 = int(a.L);
     using V = typename std::conditional<sizeof(T) == 4, uint4, uint2>::type;
     struct Group {
         V x[QC], d[QC], z[LOADZ ? QC : 1];
     };
     // The lane's 4 tokens of chunk c: a vector past the row's end is read
     // from the row's last vector instead (valid memory, values discarded).
-    auto ld = [&](const T* base, int c) -> V {
-        const int64_t ts = t_begin + int64_t(c) * CH + q * 4;
-        const T* p = base + prow * a.L + min(ts, a.L - 4);
+    auto ld = [&](const T* row, int c) -> V {
+        const T* p = row + min(tb + c * CH + q * 4, L32 - 4);
         if constexpr (sizeof(T) == 4) {
             const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
             return make_uint4(v.x, v.y, v.z, v.w);
@@ -978,12 +983,12 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     };
     auto load_group = [&](int k, Group& g) {
 #pragma unroll
-        for (int j = 0; j < QC; ++j) g.x[j] = ld(X, k * QC + j);
+        for (int j = 0; j < QC; ++j) g.x[j] = ld(Xr, k * QC + j);
 #pragma unroll
-        for (int j = 0; j < QC; ++j) g.d[j] = ld(DL, k * QC + j);
+        for (int j = 0; j < QC; ++j) g.d[j] = ld(DLr, k * QC + j);
         if constexpr (LOADZ) {
 #pragma unroll
-            for (int j = 0; j < QC; ++j) g.z[j] = ld(Z, k * QC + j);
+            for (int j = 0; j < QC; ++j) g.z[j] = ld(Zr, k * QC + j);
         }
     };
     auto unpack4 = [](const V& v, float* o) {
@@ -996,33 +1001,37 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     };
     double lsum_acc = 0.0;
     uint32_t sink = 0;
-    // per-token phase of chunk c (tokens past the segment end: identity steps)
+    // per-token phase of chunk c (tokens past the segment end: identity
+    // steps). Whether the chunk lies wholly inside the segment is the same for
+    // the whole wave: only the last chunks take the masking.
     auto prologue = [&](int c, const V& xv, const V& dv, const V& zv, float* dxo, float* gzo) {
-        const int64_t ts = t_begin + int64_t(c) * CH + q * 4;
         float xs[4], ds[4], zs[4];
         unpack4(xv, xs);
         unpack4(dv, ds);
         if constexpr (LOADZ) unpack4(zv, zs);
-        const int nvalid = int(min(int64_t(4), max(int64_t(0), t_end - ts)));
-        float l[4], w[4];
+        auto body = [&](auto masked) {
+            const int nvalid = masked ? min(4, max(0, te - (tb + c * CH + q * 4))) : 4;
+            float l[4], w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            l[e] = softplus_log2_of(fmaf(ds[e], kLog2e, biasl));
-            if (e >= nvalid) {
-                l[e] = 0.0f;
-                xs[e] = 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                l[e] = softplus_log2_of(fmaf(ds[e], kLog2e, biasl));
+                if (masked && e >= nvalid) {
+                    l[e] = 0.0f;
+                    xs[e] = 0.0f;
+                }
+                w[e] = l[e] * xs[e];
+                if constexpr (MODE == 1) lsum_acc += double(l[e]);
+                if constexpr (READOUT) {
+                    dxo[e] = Dd * xs[e];
+                    if constexpr (LOADZ) gzo[e] = silu(zs[e]);
+                }
             }
-            w[e] = l[e] * xs[e];
-            if constexpr (MODE == 1) lsum_acc += double(l[e]);
-            if constexpr (READOUT) {
-                dxo[e] = Dd * xs[e];
-                gzo[e] = 1.0f;
-                if constexpr (LOADZ) gzo[e] = silu(zs[e]);
-            }
-        }
-        float4* dst = reinterpret_cast<float4*>(&sm.lw[c & 1][r * S::kLwB + q * 32]);
-        dst[0] = make_float4(l[0], w[0], l[1], w[1]);
-        dst[1] = make_float4(l[2], w[2], l[3], w[3]);
+            float4* dst = reinterpret_cast<float4*>(&sm.lw[c & 1][r * S::kLwB + q * 32]);
+            dst[0] = make_float4(l[0], w[0], l[1], w[1]);
+            dst[1] = make_float4(l[2], w[2], l[3], w[3]);
+        };
+        if (tb + (c + 1) * CH <= te) body(std::false_type{});
+        else body(std::true_type{});
     };
     // The B/C records of chunk c (2 KB per block: NSB sub-blocks x NS scan
     // waves x 128 bytes) are brought into the scalar data cache, which the
@@ -1047,7 +1056,7 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     // chunk the compiler's waits for the next chunks' loads count past the
     // fresh stores instead of draining them.
     auto epilogue = [&](int c, const float* dx, const float* gz) {
-        const int64_t ts = t_begin + int64_t(c) * CH + q * 4;
+        const int ts = tb + c * CH + q * 4;
         float4 acc = *reinterpret_cast<const float4*>(&sm.yp[c & 1][0][yp_index(r, q)]);
 #pragma unroll
         for (int g = 1; g < NS; ++g) {
@@ -1056,9 +1065,12 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
         }
         float yv[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) yv[e] = (yv[e] + dx[e]) * gz[e];
-        const bool real = prow_ok && c >= 0 && ts < t_end;
-        T* dst = real ? static_cast<T*>(a.y) + prow * a.L + ts : static_cast<T*>(a.dump) + 4 * (io & 15);
+        for (int e = 0; e < 4; ++e) {
+            yv[e] += dx[e];
+            if constexpr (LOADZ) yv[e] *= gz[e];
+        }
+        const bool real = prow_ok && c >= 0 && ts < te;
+        T* dst = real ? Yr + ts : static_cast<T*>(a.dump) + 4 * (io & 15);
         if constexpr (sizeof(T) == 4) {
             u32x4 v = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]),
                        __float_as_uint(yv[3])};
