@@ -798,7 +798,11 @@ __global__ __launch_bounds__(kWave*(NS + kWsIo)) void fwd_ws_kernel(FwdKArgs a) 
     constexpr int NSB = CH / SB;       // sub-blocks per chunk
     constexpr bool READOUT = MODE == 0;
     constexpr bool LOADZ = GATE && READOUT;
-    constexpr int QC = 128 / (CH * int(sizeof(T)));  // chunks per load group (one line per row)
+    // chunks per load group: one 128-byte line per row, or two for fp32 rows
+    // without a gate and 4 scan waves (registers allow it there; the rows of
+    // such grids are long and far apart in memory, and 256-byte runs per row
+    // took the million-token output pass from 607 to 573 us)
+    constexpr int QC = ((sizeof(T) == 4 && NS == 4 && !LOADZ) ? 256 : 128) / (CH * int(sizeof(T)));
     static_assert(NS == 4 || NS == 8, "4 or 8 scan waves");
     static_assert(NSB % 2 == 0, "sub-blocks per chunk must be even");
     using S = WsSmem<NS, READOUT>;
