@@ -110,7 +110,8 @@ int selscan_fwd(const void* x, const void* delta, const float* A, const void* B,
  *               aligned, at least selscan_fwd_workspace_size(); NULL means
  *               the library takes and returns its own on the stream. The
  *               contents on entry do not matter; the call uses it until its
- *               work on the stream completes.
+ *               work on the stream completes. It must not overlap any input
+ *               or output (SELSCAN_ERR_ALIAS).
  *   segments  : sequence segments scanned in parallel (1 = one pass per row;
  *               > 1 = segment states, a carry pass, then the output pass);
  *               0 = automatic. At most 65536; the segment length is rounded
@@ -360,7 +361,9 @@ typedef struct {
  * overlap any input or other output. A segmented call takes, beyond the workspace above,
  * 2 S B d 16 fp32 states, S B d doubles and S-fold dA/dD/ddt_bias partial
  * sums. Errors as selscan_bwd, plus SELSCAN_ERR_CONFIG for segments out of
- * range.
+ * range or a caller workspace that is misaligned or smaller than
+ * selscan_bwd_workspace_size(), and SELSCAN_ERR_ALIAS for one that overlaps
+ * an input or output.
  */
 int selscan_bwd_ex(const void* x, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* dt_bias, const void* dy, void* dx,

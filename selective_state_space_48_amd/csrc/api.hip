@@ -307,6 +307,14 @@ int fwd_impl(const void* x, const void* delta, const float* A, const void* B, co
     FwdShape shape{dims->batch, L, dims->dim, dims->dtype == SELSCAN_BF16 ? DType::BF16 : DType::F32};
     const size_t ws_bytes = (sz.rows > 0 && L > 0) ? fwd_workspace_bytes(shape, plan) : 0;
     if (o.workspace && o.workspace_bytes < ws_bytes) return SELSCAN_ERR_CONFIG;
+    if (o.workspace) {
+        // the workspace must be nobody else's memory
+        const Span w = span(o.workspace, int64_t(ws_bytes));
+        for (const Span& s : ins)
+            if (overlaps(s, w)) return SELSCAN_ERR_ALIAS;
+        for (const Span& s : {out_y, out_s, in_h0, out_c, in_cw, in_cb, in_cp, out_cl})
+            if (overlaps(s, w)) return SELSCAN_ERR_ALIAS;
+    }
     if (noalloc && ws_bytes > kScratchBytes) return SELSCAN_ERR_SCRATCH;
 
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -313,6 +313,10 @@ def test_workspace_too_small_or_misaligned():
     need = workspace_size(D())[1]
     assert fwd_call(D(), ws=P(13), ws_bytes=need - 1) == S.ERR_CONFIG
     assert fwd_call(D(), ws=ctypes.c_void_p(BASE + 13 * SPAN + 16), ws_bytes=need) == S.ERR_CONFIG
+    # a workspace over an output or an input
+    assert fwd_call(D(), ws=P(8), ws_bytes=need) == S.ERR_ALIAS           # y
+    assert fwd_call(D(), ws=P(0), ws_bytes=need) == S.ERR_ALIAS           # x
+    assert fwd_call(D(), h0=P(12), ws=P(12), ws_bytes=need) == S.ERR_ALIAS  # h0
 
 
 def test_timing_argument_errors():
