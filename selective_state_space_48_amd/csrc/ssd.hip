@@ -30,9 +30,12 @@
 // from chunk to chunk (never in LDS): each wave forms C.H over its half of
 // the state rows for both t blocks, and the two waves of a p block exchange
 // those partial products (4 KB per wave) through LDS.
-// Tiles are staged in LDS with rows padded by 16 bytes so that the 16-byte
-// operand reads of 32 lanes on 32 rows spread over the banks. The next
-// chunk's inputs are loaded into registers while the current one computes.
+// Tiles are staged in LDS as the rows arrive (16-byte writes, no transposes):
+// the operands whose contraction runs over tokens (x for the outputs, B and
+// the weighted x for the state) are read with the LDS transpose read, and
+// the masked scores have a tile of their own, so a chunk takes three
+// barriers. The next chunk's inputs are loaded into registers while the
+// current one computes, by whole 128-byte lines.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -101,36 +104,103 @@ struct SsdArgs {
     int64_t batch, L, H;
 };
 
-// One chunk's inputs as this thread loads them: token s = lane of B, C and x
-// pieces (16 bytes each; B and C pieces wv + 4k of N/8, x pieces wv + 4k of
-// 8) and the raw step of token lane.
+// One chunk's inputs as this thread loads them. Wave wv loads tokens
+// 16 wv .. 16 wv + 15 as whole rows, consecutive lanes on consecutive 16-byte
+// pieces (every load instruction covers whole 128-byte lines): B and C piece
+// k of token tokB(k), x piece k of token tokX(k); and the raw step of token
+// lane, which every wave needs for its running decay.
 template <int N>
 struct ChunkRegs {
-    static constexpr int NB = N / 8 / 4;  // 16-byte pieces of a B (or C) row per thread
+    static constexpr int NP = N / 8;      // 16-byte pieces of a B (or C) row
+    static constexpr int NB = NP / 4;     // of them per thread
     uint4 b[NB], c[NB], x[2];
     float dl;
     bool ok;  // token lane exists (tokens past the end take step 0: an identity step)
+    static __device__ __forceinline__ int tokB(int wv, int k, int lane) { return 16 * wv + k * (64 / NP) + lane / NP; }
+    static __device__ __forceinline__ int tokX(int wv, int k, int lane) { return 16 * wv + 8 * k + lane / 8; }
 };
+
+// LDS tiles are stored row-major without padding; their 16-byte pieces are
+// permuted within each row by an XOR with a function of the row, chosen so
+// that every access of the kernel spreads over the banks (16-byte reads: 16
+// lanes on distinct pieces mod 16; 8-byte and transposed reads: 32 lanes on
+// distinct 8-byte units mod 32; 16-byte writes: 8 lanes on distinct pieces
+// mod 8; 4-byte writes: 32 lanes on distinct words mod 32).
+// Rows of 16 pieces (B and C, N = 128): any 16 consecutive rows differ mod 16,
+// any 8 consecutive rows differ mod 8, and each aligned group of 4 rows puts a
+// given 64-byte run into 4 different 64-byte bank ranges.
+__device__ __forceinline__ int swz16(int r) {
+    return ((r & 3) << 2) ^ (r & 3) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+}
+// Rows of 8 pieces (B and C for N = 64, x): 8 consecutive rows differ mod 8,
+// even and odd rows each differ among any 8, and rows j, j + 2 of an aligned
+// group of 4 land in different halves of the 32 banks.
+__device__ __forceinline__ int swz8(int r) {
+    const int m = (r >> 1) & 7;
+    return (((m & 1) << 2) | ((m >> 1) & 3)) ^ ((r & 1) << 1);
+}
+// The masked scores [t][s]: 16-byte reads of 16 consecutive rows, and 4-byte
+// writes that put rows R, R + 1 (R even) into different halves of the banks.
+__device__ __forceinline__ int swzm(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+// Element offset of (row, col) in a tile of NPR pieces per row.
+template <int NPR>
+__device__ __forceinline__ int at(int row, int col) {
+    const int sw = NPR == 16 ? swz16(row) : swz8(row);
+    return row * NPR * 8 + (((col >> 3) ^ sw) << 3) + (col & 7);
+}
+__device__ __forceinline__ int atm(int row, int col) {
+    return row * kQ + (((col >> 3) ^ swzm(row)) << 3) + (col & 7);
+}
+
+// ds_read_b64_tr_b16: every lane reads 4 bf16 and the wave's 16-lane groups
+// exchange them so that lane i receives element i % 4 of what lane
+// 16 (i / 16) + 4 e + (i % 16) / 4 read, e = 0..3 (checked on gfx950). Lane
+// (g = l / 16, j = l % 16 / 4, q = l % 4) reading row k0 + 8 (g / 2) + j at
+// column c + 4 q therefore hands lane i the column of lane i's tile position
+// at rows k0 + 8 (i / 32) + 0..3: half of a matrix-core operand whose
+// contraction index runs down the rows of a row-major tile.
+__device__ __forceinline__ bf16x4 ldtr(const bf16_bits* p) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4*)(const_cast<bf16_bits*>(p)));
+    return __builtin_bit_cast(bf16x4, v);
+}
+// Operand (K = tile rows k0 .. k0 + 15, columns c0 .. c0 + 31) of a row-major
+// tile of NPR pieces per row: lane l gets rows k0 + 8 (l / 32) + 0..7 of
+// column c0 + perm(l % 32), perm swapping bits 2 and 3 when PERM is set.
+template <int NPR, bool PERM>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16_bits* tile, int k0, int c0, int lane) {
+    const int g = lane / 16, j = (lane % 16) / 4, q = lane % 4;
+    const int qq = PERM ? (((q & 1) << 1) | (q >> 1)) : q;
+    const int row = k0 + 8 * (g / 2) + j, col = c0 + 16 * (g % 2) + 4 * qq;
+    const bf16x4 lo = ldtr(tile + at<NPR>(row, col));
+    const bf16x4 hi = ldtr(tile + at<NPR>(row + 4, col));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// State rows are held in the accumulators in the order that makes the
+// carry-in product's C operand one contiguous 16-byte read: accumulator row i
+// of a 32-row tile is state row tau(i) (bits 2 and 3 swapped).
+__device__ __forceinline__ int tau(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 template <int N>
 __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
-    constexpr int NR = N + 8;        // row stride (bf16) of [.][n] tiles
-    constexpr int QR = kQ + 8;       // row stride of [.][s] tiles
+    constexpr int NP = N / 8;        // 16-byte pieces per B/C row
     constexpr int NT = N / 32;       // 32-row tiles of the state
     constexpr int NTW = NT / 2;      // state tiles per wave
     using R = ChunkRegs<N>;
-    __shared__ alignas(16) bf16_bits Cs[kQ * NR];      // C rows [t][n]
-    __shared__ alignas(16) bf16_bits BsMs[kQ * NR];    // B rows [s][n]; later the masked scores [t][s]
-    __shared__ alignas(16) bf16_bits Bw[N * QR];       // 2^(cum_end - cum_s) delta_s B^T: [n][s]
-    __shared__ alignas(16) bf16_bits Xt[kP * QR];      // x^T [p][s]
+    __shared__ alignas(16) bf16_bits Cs[kQ * N];       // C rows [t][n]
+    __shared__ alignas(16) bf16_bits Bs[kQ * N];       // B rows [s][n]
+    __shared__ alignas(16) bf16_bits Xn[kQ * kP];      // x rows [s][p]
+    __shared__ alignas(16) bf16_bits Xw[kQ * kP];      // 2^(cum_end - cum_s) delta_s x_s: [s][p]
+    __shared__ alignas(16) bf16_bits Ms[kQ * kQ];      // masked scores [t][s]
     __shared__ alignas(16) float4 Yx[4][4][64];       // carry-in partial sums for the partner wave
     __shared__ float cums[kQ], dts[kQ], gcum[kQ];      // running log2-decay, step and 2^cum of the chunk's tokens
-    bf16_bits* Ms = BsMs;
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
     const int pb = wv % 2, tb = wv / 2;
-    const int64_t bh = blockIdx.x;
+    // The heads of a batch entry, which read the same B and C rows, run on one XCD (one L2).
+    const int64_t bh = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t b = bh / a.H, h = bh % a.H;
     const int nc = int((a.L + kQ - 1) / kQ);
     const float Ah = a.A[h] * kLog2e;                      // log2 decay per unit step
@@ -141,26 +211,27 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     // row: valid memory) so that they need no branches; staging zeroes such
     // tokens, whose step is 0 (an identity step).
     auto load = [&](int c, R& r) {
-        const int64_t t = int64_t(c) * kQ + lane;
-        r.ok = t < a.L;
-        const int64_t tt = r.ok ? t : a.L - 1;
+        const int64_t t0 = int64_t(c) * kQ, last = a.L - 1;
+        r.ok = t0 + lane < a.L;
 #pragma unroll
         for (int k = 0; k < R::NB; ++k) {
-            const int q8 = wv + 4 * k;
-            r.b[k] = *reinterpret_cast<const uint4*>(a.B + (b * a.L + tt) * N + q8 * 8);
-            r.c[k] = *reinterpret_cast<const uint4*>(a.C + (b * a.L + tt) * N + q8 * 8);
+            const int64_t t = min(t0 + R::tokB(wv, k, lane), last);
+            r.b[k] = *reinterpret_cast<const uint4*>(a.B + (b * a.L + t) * N + (lane % NP) * 8);
+            r.c[k] = *reinterpret_cast<const uint4*>(a.C + (b * a.L + t) * N + (lane % NP) * 8);
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
-            r.x[k] = *reinterpret_cast<const uint4*>(a.x + ((b * a.L + tt) * a.H + h) * kP + (wv + 4 * k) * 8);
-        r.dl = to_f32(a.delta[(b * a.L + tt) * a.H + h]);
+        for (int k = 0; k < 2; ++k) {
+            const int64_t t = min(t0 + R::tokX(wv, k, lane), last);
+            r.x[k] = *reinterpret_cast<const uint4*>(a.x + ((b * a.L + t) * a.H + h) * kP + (lane % 8) * 8);
+        }
+        r.dl = to_f32(a.delta[(b * a.L + min(t0 + lane, last)) * a.H + h]);
     };
 
-    // State tiles (fp32 accumulators), from h0 or zero: rows
-    // n = 32 (tb NTW + j) + acc_row, columns p = 32 pb + lane % 32. The wave
-    // keeps its own rows of the state for its p block from chunk to chunk;
-    // the carry-in product C H is summed over n in two halves, one per wave
-    // of the p block, which swap partial sums through LDS.
+    // State tiles (fp32 accumulators), from h0 or zero: accumulator row i of
+    // tile j is state row n = 32 (tb NTW + j) + tau(i), column p = 32 pb +
+    // lane % 32. The wave keeps its own rows of the state for its p block
+    // from chunk to chunk; the carry-in product C H is summed over n in two
+    // halves, one per wave of the p block, which swap partial sums through LDS.
     f32x16 H[NTW];
     if (a.h0) {
         const float* src = a.h0 + (b * a.H + h) * int64_t(N) * kP;
@@ -168,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                H[j][r] = src[int64_t((tb * NTW + j) * 32 + acc_row(r, lane)) * kP + pb * 32 + lane % 32];
+                H[j][r] = src[int64_t((tb * NTW + j) * 32 + tau(acc_row(r, lane))) * kP + pb * 32 + lane % 32];
     } else {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
@@ -191,6 +262,17 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             if (tg0 + dr < a.L) *reinterpret_cast<uint32_t*>(yrow + dr * rs) = ypend[k];
         }
     };
+    // Of each pair of rows (dr, dr + 1) held by a lane pair (columns s, s + 1),
+    // the even lane keeps row dr and the odd lane row dr + 1, swapping one
+    // value through a DPP quad permutation (lanes 0<->1, 2<->3); returns the
+    // two adjacent columns of the lane's row, packed as bf16.
+    auto pair_rows = [&](float v0, float v1) {
+        const bool odd = lane & 1;
+        const float send = odd ? v0 : v1;
+        const float recv = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xb1, 0xf, 0xf, false));
+        return odd ? pack_bf16x2(recv, v1) : pack_bf16x2(v0, recv);
+    };
 
     R cur;
     load(0, cur);
@@ -198,14 +280,14 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         // Staging (and the stores and prefetch issued with it) runs at a
         // raised wave priority, the matrix products at the base one: the
         // other workgroup's waves on the same SIMDs then reach their next
-        // chunk's products sooner (measured: about 8% less time).
+        // chunk's products sooner.
         __builtin_amdgcn_s_setprio(1);
         // ---- per-token: step size and running log2-decay, token = lane (every wave) ----
         const float sp = softplus_log2(cur.dl + bias) * kLn2;
         const float dt = cur.ok ? sp : 0.0f;
         const float cum = wave_prefix_sum(dt * Ah);
         const float cend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cum), kQ - 1));
-        // ---- stage chunk c ----
+        // ---- stage chunk c: rows as loaded, 16-byte writes ----
         {
             const int s = lane;
             if (wv == 0) {
@@ -213,33 +295,35 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 cums[s] = cum;
                 dts[s] = dt;
             }
-            const float ws = exp2_hw(cend - cum) * dt;  // weight of token s in the state update
+            const float ws_t = exp2_hw(cend - cum) * dt;  // weight of token s in the state update
             if (int64_t(c + 1) * kQ > a.L) {  // the last chunk is partial (a uniform branch)
                 const uint4 zero = make_uint4(0, 0, 0, 0);
+                const int64_t t0 = int64_t(c) * kQ;
 #pragma unroll
                 for (int k = 0; k < R::NB; ++k)
-                    if (!cur.ok) cur.b[k] = cur.c[k] = zero;
+                    if (t0 + R::tokB(wv, k, lane) >= a.L) cur.b[k] = cur.c[k] = zero;
 #pragma unroll
                 for (int k = 0; k < 2; ++k)
-                    if (!cur.ok) cur.x[k] = zero;
+                    if (t0 + R::tokX(wv, k, lane) >= a.L) cur.x[k] = zero;
             }
 #pragma unroll
             for (int k = 0; k < R::NB; ++k) {
-                const int q8 = wv + 4 * k;
-                *reinterpret_cast<uint4*>(&Cs[s * NR + q8 * 8]) = cur.c[k];
-                *reinterpret_cast<uint4*>(&BsMs[s * NR + q8 * 8]) = cur.b[k];
-                bf16_bits v[8];
-                split8(cur.b[k], v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Bw[(q8 * 8 + e) * QR + s] = tobf(ws * bfval(v[e]));
+                const int tok = R::tokB(wv, k, lane), col = (lane % NP) * 8;
+                *reinterpret_cast<uint4*>(&Cs[at<NP>(tok, col)]) = cur.c[k];
+                *reinterpret_cast<uint4*>(&Bs[at<NP>(tok, col)]) = cur.b[k];
             }
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int q8 = wv + 4 * k;
-                bf16_bits v[8];
-                split8(cur.x[k], v);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Xt[(q8 * 8 + e) * QR + s] = v[e];
+                const int tok = R::tokX(wv, k, lane), col = (lane % 8) * 8;
+                const float ws = __shfl(ws_t, tok, 64);  // the weight of this piece's token
+                const uint4 v = cur.x[k];
+                *reinterpret_cast<uint4*>(&Xn[at<8>(tok, col)]) = v;
+                uint4 w;
+                w.x = pack_bf16x2(ws * bf16_lo(v.x), ws * bf16_hi(v.x));
+                w.y = pack_bf16x2(ws * bf16_lo(v.y), ws * bf16_hi(v.y));
+                w.z = pack_bf16x2(ws * bf16_lo(v.z), ws * bf16_hi(v.z));
+                w.w = pack_bf16x2(ws * bf16_lo(v.w), ws * bf16_hi(v.w));
+                *reinterpret_cast<uint4*>(&Xw[at<8>(tok, col)]) = w;
             }
         }
         if (c > 0) store_y(c - 1);
@@ -248,11 +332,10 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         __builtin_amdgcn_s_setprio(0);
 
         // ---- carry-in partials: C (both t blocks) times this wave's state rows ----
-        // The state's accumulator layout is the B operand of this product
-        // once the contraction index runs in a permuted order: registers
-        // 8 kb .. 8 kb + 7 of a lane hold state rows 16 kb + 4 (lane / 32) +
-        // {0..3, 8..11} of the tile, so the C operand is read in the same
-        // order (two 8-byte pieces per lane).
+        // Registers 8 kb .. 8 kb + 7 of a state tile hold accumulator rows
+        // 16 kb + 4 (lane / 32) + {0..3, 8..11}, i.e. state rows 16 kb +
+        // 8 (lane / 32) + 0..7: as the B operand they pair with one 16-byte
+        // piece of each C row.
         f32x16 Yp[2] = {f32x16{}, f32x16{}};
         {
 #pragma unroll
@@ -262,14 +345,10 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                     bf16x8 hb;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) hb[e] = __bf16(H[j][8 * kb + e]);
-                    const int n0 = (tb * NTW + j) * 32 + 16 * kb + 4 * (lane / 32);
+                    const int n0 = (tb * NTW + j) * 32 + 16 * kb + 8 * (lane / 32);
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const bf16_bits* crow = &Cs[(tt * 32 + lane % 32) * NR + n0];
-                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(crow);
-                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(crow + 8);
-                        Yp[tt] = mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), hb, Yp[tt]);
-                    }
+                    for (int tt = 0; tt < 2; ++tt)
+                        Yp[tt] = mfma(lds8(&Cs[at<NP>(tt * 32 + lane % 32, n0)]), hb, Yp[tt]);
                 }
             }
             // the partner wave (same p block, other t block) gets its tile's half
@@ -281,29 +360,32 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         }
 
         // ---- scores of the lower block triangle: wave 0 (0,0), wave 1 (1,0), wave 2 (1,1) ----
-        const int gt = wv == 0 ? 0 : 1, gs = wv == 2 ? 1 : 0;
-        f32x16 G = {};
         if (wv < 3) {
+            const int gt = wv == 0 ? 0 : 1, gs = wv == 2 ? 1 : 0;
+            f32x16 G = {};
 #pragma unroll
             for (int ks = 0; ks < N / 16; ++ks) {
                 const int k0 = ks * 16 + 8 * (lane / 32);
-                G = mfma(lds8(&Cs[(gt * 32 + lane % 32) * NR + k0]), lds8(&BsMs[(gs * 32 + lane % 32) * NR + k0]), G);
+                G = mfma(lds8(&Cs[at<NP>(gt * 32 + lane % 32, k0)]), lds8(&Bs[at<NP>(gs * 32 + lane % 32, k0)]), G);
             }
-        }
-        __syncthreads();  // every read of B rows is done: the scores take their place
-        if (wv < 3) {
             // Branch-free: every lane forms its 16 values and keeps those on
             // or below the diagonal (the exponent is clamped at 0 above it).
             const int s = gs * 32 + lane % 32;
             const float cs = cums[s], ds = dts[s];
             const int t0 = gt * 32 + 4 * (lane / 32);  // row of G[0]
             const float* crow = &cums[t0];
-            bf16_bits* mrow = &Ms[t0 * QR + s];
+            float m[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int dr = 8 * (r / 4) + r % 4;
-                const float m = G[r] * exp2_hw(fminf(crow[dr] - cs, 0.0f)) * ds;
-                mrow[dr * QR] = tobf(t0 + dr >= s ? m : 0.0f);
+                const float v = G[r] * exp2_hw(fminf(crow[dr] - cs, 0.0f)) * ds;
+                m[r] = t0 + dr >= s ? v : 0.0f;
+            }
+            const int odd = lane & 1;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int dr = 8 * (r / 4) + r % 4;
+                *reinterpret_cast<uint32_t*>(&Ms[atm(t0 + dr + odd, s & ~1)]) = pair_rows(m[r], m[r + 1]);
             }
         }
         __syncthreads();
@@ -315,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             for (int ks = 0; ks < kQ / 16; ++ks) {
                 if (ks < 2 * (tb + 1)) {  // s blocks above the diagonal are all masked
                     const int k0 = ks * 16 + 8 * (lane / 32);
-                    y1 = mfma(lds8(&Ms[(tb * 32 + lane % 32) * QR + k0]), lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), y1);
+                    y1 = mfma(lds8(&Ms[atm(tb * 32 + lane % 32, k0)]), tr_operand<8, false>(Xn, ks * 16, pb * 32, lane), y1);
                 }
             }
             // C H: this wave's half plus the partner's (written before the last barrier)
@@ -328,39 +410,29 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             const int p = pb * 32 + lane % 32;
             const int t0 = tb * 32 + 4 * (lane / 32);  // chunk row of y1[0]
             const float* grow = &gcum[t0];
-            const bf16_bits* xcol = &Xt[p * QR + t0];
             float v[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int dr = 8 * (r / 4) + r % 4;
-                v[r] = fmaf(grow[dr], y2[r], y1[r]) + Dh * bfval(xcol[dr]);
+                v[r] = fmaf(grow[dr], y2[r], y1[r]) + Dh * bfval(Xn[at<8>(t0 + dr, p)]);
             }
-            // Stores of two adjacent columns at once: of each pair of rows
-            // (dr, dr+1), the even lane of a lane pair stores row dr and the
-            // odd lane row dr+1, swapping one value through a DPP quad
-            // permutation (lanes 0<->1, 2<->3).
-            const bool odd = lane & 1;
+            // Stores of two adjacent columns at once (rows paired as in the scores).
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float send = odd ? v[r] : v[r + 1];
-                const float recv = __builtin_bit_cast(
-                    float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xb1, 0xf, 0xf, false));
-                const float lo = odd ? recv : v[r], hi = odd ? v[r + 1] : recv;
-                ypend[r / 2] = pack_bf16x2(lo, hi);
-            }
+            for (int r = 0; r < 16; r += 2) ypend[r / 2] = pair_rows(v[r], v[r + 1]);
         }
-        // ---- state: H <- 2^cum_end H + (w B)^T x over this wave's tiles ----
+        // ---- state: H <- 2^cum_end H + B^T (w x) over this wave's tiles ----
         {
             const float gend = exp2_hw(cend);
+            bf16x8 xw[kQ / 16];
+#pragma unroll
+            for (int ks = 0; ks < kQ / 16; ++ks) xw[ks] = tr_operand<8, false>(Xw, ks * 16, pb * 32, lane);
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int nb = tb * NTW + j;
                 f32x16 acc = H[j] * gend;
 #pragma unroll
-                for (int ks = 0; ks < kQ / 16; ++ks) {
-                    const int k0 = ks * 16 + 8 * (lane / 32);
-                    acc = mfma(lds8(&Bw[(nb * 32 + lane % 32) * QR + k0]), lds8(&Xt[(pb * 32 + lane % 32) * QR + k0]), acc);
-                }
+                for (int ks = 0; ks < kQ / 16; ++ks)
+                    acc = mfma(tr_operand<NP, true>(Bs, ks * 16, nb * 32, lane), xw[ks], acc);
                 H[j] = acc;
             }
         }
@@ -373,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                dst[int64_t((tb * NTW + j) * 32 + acc_row(r, lane)) * kP + pb * 32 + lane % 32] = H[j][r];
+                dst[int64_t((tb * NTW + j) * 32 + tau(acc_row(r, lane))) * kP + pb * 32 + lane % 32] = H[j][r];
     }
 }
 
