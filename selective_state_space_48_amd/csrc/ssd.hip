@@ -177,6 +177,15 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16_bits* tile, int k0, int 
     const bf16x4 hi = ldtr(tile + at<NPR>(row + 4, col));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// Raw buffer resource of `bytes` bytes at p (loads past the end read zeros,
+// stores past it are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // State rows are held in the accumulators in the order that makes the
 // carry-in product's C operand one contiguous 16-byte read: accumulator row i
 // of a 32-row tile is state row tau(i) (bits 2 and 3 swapped).
@@ -210,21 +219,39 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     // Loads are unconditional (a token past the end reads the last token's
     // row: valid memory) so that they need no branches; staging zeroes such
     // tokens, whose step is 0 (an identity step).
+    // Chunk loads and stores go through buffer resources based at the
+    // chunk's first token and sized to its last valid one: a token past the
+    // end reads zeros and its stores are dropped by the hardware's range
+    // check, so the partial last chunk needs no guards. Lane offsets are
+    // fixed; only the (scalar) resources change from chunk to chunk.
+    const int64_t xs = a.H * kP;  // elements from one token's x (or y) row to the next
+    int vB[R::NB], vX[2];
+#pragma unroll
+    for (int k = 0; k < R::NB; ++k) vB[k] = (R::tokB(wv, k, lane) * N + (lane % NP) * 8) * 2;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) vX[k] = int((R::tokX(wv, k, lane) * xs + (lane % 8) * 8) * 2);
+    const int vD = int(lane * a.H * 2);
+    auto valid = [&](int c) { return int(min(int64_t(kQ), a.L - int64_t(c) * kQ)); };
+    // Bytes from a chunk's first row to the end of the last valid row's
+    // `row` elements, rows `stride` elements apart; 0 for a chunk past the
+    // end (the prefetch after the last chunk), so that nothing is read.
+    auto span = [](int nv, int64_t stride, int64_t row) { return nv > 0 ? int(((nv - 1) * stride + row) * 2) : 0; };
     auto load = [&](int c, R& r) {
-        const int64_t t0 = int64_t(c) * kQ, last = a.L - 1;
-        r.ok = t0 + lane < a.L;
+        const int64_t t0 = int64_t(c) * kQ;
+        const int nv = valid(c);
+        r.ok = lane < nv;
+        const auto rB = buf_rsrc(a.B + (b * a.L + t0) * N, span(nv, N, N));
+        const auto rC = buf_rsrc(a.C + (b * a.L + t0) * N, span(nv, N, N));
+        const auto rX = buf_rsrc(a.x + ((b * a.L + t0) * a.H + h) * kP, span(nv, xs, kP));
+        const auto rD = buf_rsrc(a.delta + (b * a.L + t0) * a.H + h, span(nv, a.H, 1));
 #pragma unroll
         for (int k = 0; k < R::NB; ++k) {
-            const int64_t t = min(t0 + R::tokB(wv, k, lane), last);
-            r.b[k] = *reinterpret_cast<const uint4*>(a.B + (b * a.L + t) * N + (lane % NP) * 8);
-            r.c[k] = *reinterpret_cast<const uint4*>(a.C + (b * a.L + t) * N + (lane % NP) * 8);
+            r.b[k] = buf_load16(rB, vB[k]);
+            r.c[k] = buf_load16(rC, vB[k]);
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int64_t t = min(t0 + R::tokX(wv, k, lane), last);
-            r.x[k] = *reinterpret_cast<const uint4*>(a.x + ((b * a.L + t) * a.H + h) * kP + (lane % 8) * 8);
-        }
-        r.dl = to_f32(a.delta[(b * a.L + min(t0 + lane, last)) * a.H + h]);
+        for (int k = 0; k < 2; ++k) r.x[k] = buf_load16(rX, vX[k]);
+        r.dl = to_f32(bf16_bits(__builtin_amdgcn_raw_buffer_load_b16(rD, vD, 0, 0)));
     };
 
     // State tiles (fp32 accumulators), from h0 or zero: accumulator row i of
@@ -250,16 +277,14 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
     // prefetch is issued: vector-memory waits count stores too, in issue
     // order, so a store issued after a prefetch would hold up the wait for it.
     uint32_t ypend[8];  // two adjacent columns (bf16) for each pair of rows
+    const int vY = int(((tb * 32 + 4 * (lane / 32) + (lane & 1)) * xs + pb * 32 + (lane % 32 & ~1)) * 2);
     auto store_y = [&](int c) {
-        const bool odd = lane & 1;
-        const int p = pb * 32 + lane % 32;
-        const int64_t tg0 = int64_t(c) * kQ + tb * 32 + 4 * (lane / 32) + (odd ? 1 : 0);
-        bf16_bits* yrow = a.y + ((b * a.L + tg0) * a.H + h) * kP + (p & ~1);
-        const int64_t rs = a.H * kP;  // elements from one token to the next
+        const int64_t t0 = int64_t(c) * kQ;
+        const auto rY = buf_rsrc(a.y + ((b * a.L + t0) * a.H + h) * kP, span(valid(c), xs, kP));
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int dr = 8 * (k / 2) + 2 * (k % 2);  // rows dr and dr + 1 of the pair
-            if (tg0 + dr < a.L) *reinterpret_cast<uint32_t*>(yrow + dr * rs) = ypend[k];
+            __builtin_amdgcn_raw_buffer_store_b32(ypend[k], rY, vY + int(dr * xs * 2), 0, 0);
         }
     };
     // Of each pair of rows (dr, dr + 1) held by a lane pair (columns s, s + 1),
@@ -296,16 +321,6 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 dts[s] = dt;
             }
             const float ws_t = exp2_hw(cend - cum) * dt;  // weight of token s in the state update
-            if (int64_t(c + 1) * kQ > a.L) {  // the last chunk is partial (a uniform branch)
-                const uint4 zero = make_uint4(0, 0, 0, 0);
-                const int64_t t0 = int64_t(c) * kQ;
-#pragma unroll
-                for (int k = 0; k < R::NB; ++k)
-                    if (t0 + R::tokB(wv, k, lane) >= a.L) cur.b[k] = cur.c[k] = zero;
-#pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    if (t0 + R::tokX(wv, k, lane) >= a.L) cur.x[k] = zero;
-            }
 #pragma unroll
             for (int k = 0; k < R::NB; ++k) {
                 const int tok = R::tokB(wv, k, lane), col = (lane % NP) * 8;
