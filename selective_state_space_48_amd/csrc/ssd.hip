@@ -272,10 +272,10 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         for (int j = 0; j < NTW; ++j) H[j] = f32x16{};
     }
 
-    // The output of a chunk is stored in the next iteration, once that
-    // iteration's prefetched inputs have been consumed and before the next
-    // prefetch is issued: vector-memory waits count stores too, in issue
-    // order, so a store issued after a prefetch would hold up the wait for it.
+    // A chunk's outputs are stored as soon as they are formed, after the
+    // next chunk's loads were issued. Vector-memory waits count loads and
+    // stores together in issue order, so the wait for those loads (at the
+    // next chunk's staging) leaves the stores in flight.
     uint32_t ypend[8];  // two adjacent columns (bf16) for each pair of rows
     const int vY = int(((tb * 32 + 4 * (lane / 32) + (lane & 1)) * xs + pb * 32 + (lane % 32 & ~1)) * 2);
     auto store_y = [&](int c) {
@@ -301,6 +301,12 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
 
     R cur;
     load(0, cur);
+    // Zeros for the first chunk's outputs (overwritten by the same lanes in
+    // the first iteration): the loop is then entered, like every back edge,
+    // with 8 stores behind the loads of the chunk it starts with.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ypend[k] = 0;
+    store_y(0);
     for (int c = 0; c < nc; ++c) {
         // Staging (and the stores and prefetch issued with it) runs at a
         // raised wave priority, the matrix products at the base one: the
@@ -341,7 +347,6 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
                 *reinterpret_cast<uint4*>(&Xw[at<8>(tok, col)]) = w;
             }
         }
-        if (c > 0) store_y(c - 1);
         load(c + 1, cur);  // next chunk's inputs, in flight during this chunk
         __syncthreads();
         __builtin_amdgcn_s_setprio(0);
@@ -434,6 +439,7 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
             // Stores of two adjacent columns at once (rows paired as in the scores).
 #pragma unroll
             for (int r = 0; r < 16; r += 2) ypend[r / 2] = pair_rows(v[r], v[r + 1]);
+            store_y(c);
         }
         // ---- state: H <- 2^cum_end H + B^T (w x) over this wave's tiles ----
         {
@@ -453,7 +459,6 @@ __global__ __launch_bounds__(256, 2) void ssd_fused(SsdArgs a) {
         }
         __syncthreads();  // every read of this chunk's tiles is done
     }
-    store_y(nc - 1);
     if (a.last_state) {
         float* dst = a.last_state + (b * a.H + h) * int64_t(N) * kP;
 #pragma unroll
