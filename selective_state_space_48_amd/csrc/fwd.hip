@@ -1245,6 +1245,84 @@ __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ A,
     }
 }
 
+// The same carries for many segments and few chains: a workgroup takes 64
+// chains (one per lane) and kCarryW waves, each wave a run of consecutive
+// segments. A wave first composes its run from a zero state (the run's decay
+// 2^(A_n * its summed steps) and its end state), the runs are then chained in
+// order through LDS to give each run its entering state, and each wave
+// rescans its run from that state, writing the state entering every segment.
+// Chain length: two runs plus the number of waves, instead of all segments.
+constexpr int kCarryW = 16;
+__global__ __launch_bounds__(64 * kCarryW) void carry_runs_kernel(const float* __restrict__ A,
+                                                                 const float* __restrict__ seg_state,
+                                                                 const double* __restrict__ seg_lsum,
+                                                                 const float* __restrict__ h0,
+                                                                 float* __restrict__ carry, int64_t rows,
+                                                                 int64_t dim, int32_t segments) {
+    __shared__ float agg_a[kCarryW][64], agg_b[kCarryW][64];
+    const int lane = threadIdx.x % 64;
+    const int w = threadIdx.x / 64;
+    const int64_t chains = rows * kN;
+    const int64_t i = int64_t(blockIdx.x) * 64 + lane;
+    const bool ok = i < chains;
+    const int64_t r = ok ? i / kN : 0;
+    const int n = int(i % kN);
+    const double An = ok ? double(A[(r % dim) * kN + n]) : 0.0;
+    const int steps = segments - 1;  // transitions s -> s + 1
+    const int per = (steps + kCarryW - 1) / kCarryW;
+    const int s0 = min(steps, w * per), s1 = min(steps, s0 + per);
+    // 1) the run from zero (loads issued U at a time, ahead of their use)
+    constexpr int U = 8;
+    float beta = 0.0f;
+    double lsum = 0.0;
+    if (ok) {
+        for (int s = s0; s < s1; s += U) {
+            float st[U];
+            double ls[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = min(s + u, s1 - 1);
+                st[u] = seg_state[int64_t(q) * chains + i];
+                ls[u] = seg_lsum[int64_t(q) * rows + r];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (s + u < s1) {
+                    beta = fmaf(exp2_hw(float(An * ls[u])), beta, st[u]);
+                    lsum += ls[u];
+                }
+            }
+        }
+    }
+    agg_a[w][lane] = exp2_hw(float(An * lsum));
+    agg_b[w][lane] = beta;
+    __syncthreads();
+    // 2) the state entering this wave's run
+    float H = (ok && h0) ? h0[i] : 0.0f;
+    for (int v = 0; v < w; ++v) H = fmaf(agg_a[v][lane], H, agg_b[v][lane]);
+    // 3) rescan the run from it
+    if (ok) {
+        if (w == 0) carry[i] = H;
+        for (int s = s0; s < s1; s += U) {
+            float st[U];
+            double ls[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = min(s + u, s1 - 1);
+                st[u] = seg_state[int64_t(q) * chains + i];
+                ls[u] = seg_lsum[int64_t(q) * rows + r];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (s + u < s1) {
+                    H = fmaf(exp2_hw(float(An * ls[u])), H, st[u]);
+                    carry[int64_t(s + u + 1) * chains + i] = H;
+                }
+            }
+        }
+    }
+}
+
 template <typename T, int G, bool GATE, bool VEC, int MODE>
 hipError_t launch_one(const FwdKArgs& k, int64_t blocks, hipStream_t st) {
     hipLaunchKernelGGL((fwd_kernel<T, G, GATE, VEC, MODE>), dim3(unsigned(blocks)),
@@ -1424,10 +1502,7 @@ hipError_t launch_fwd(const FwdTensors& t, const FwdShape& s, const FwdPlan& p, 
     }
     if (e != hipSuccess) return e;
     // 2) carries
-    const int64_t nthreads = int64_t(rows) * kN;
-    hipLaunchKernelGGL(carry_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream,
-                       t.A, seg_state, seg_lsum, t.h0, carry, int64_t(rows), s.dim, p.segments);
-    e = hipGetLastError();
+    e = launch_carry(t.A, seg_state, seg_lsum, t.h0, carry, int64_t(rows), s.dim, p.segments, stream);
     if (e != hipSuccess) return e;
     // 3) output pass from the carried-in states
     k.h0 = carry;
@@ -1439,8 +1514,14 @@ hipError_t launch_carry(const float* A, const float* seg_state, const double* se
                         const float* h0, float* carry, int64_t rows, int64_t dim, int32_t segments,
                         hipStream_t stream) {
     const int64_t nthreads = rows * kN;
-    hipLaunchKernelGGL(carry_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream,
-                       A, seg_state, seg_lsum, h0, carry, rows, dim, segments);
+    // Many segments over few chains (the long-sequence plans): runs per wave,
+    // so that the sequential chain is short; otherwise one thread per chain.
+    if (segments > 4 * kCarryW && nthreads <= 65536)
+        hipLaunchKernelGGL(carry_runs_kernel, dim3(unsigned((nthreads + 63) / 64)), dim3(64 * kCarryW), 0,
+                           stream, A, seg_state, seg_lsum, h0, carry, rows, dim, segments);
+    else
+        hipLaunchKernelGGL(carry_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream,
+                           A, seg_state, seg_lsum, h0, carry, rows, dim, segments);
     return hipGetLastError();
 }
 

@@ -144,6 +144,7 @@ SEGMENTED = [
     (2, 1000, 65, "bf16", 7),   # six of 160 and a last of 40, ragged rows
     (1, 100, 40, "bf16", 10),   # rounds to 32-token segments: 4 run
     (3, 520, 130, "f32", 5),
+    (1, 6400, 40, "f32", 200),  # many segments over few rows: carries formed in runs per wave
 ]
 
 

@@ -76,6 +76,18 @@ def test_every_launch_variant(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("segments", [65, 200])
+def test_many_segments_few_rows(dtype, segments):
+    """Many segments over few rows, as in the long-sequence plans: the carries
+    are composed in runs of segments per wave, chained through LDS, instead of
+    one sequential chain per (row, state)."""
+    inp = small(M14 if dtype == "bf16" else "m130m_f32_b8_l2048_d1536", batch=1, seqlen=6400, dim=40)
+    case(f"{segments} segments {dtype} b1 L6400 d40")
+    y, hs = gpu_fwd(inp, dtype, segments=segments)
+    assert_close(y, hs, oracle_fwd(inp), dtype, f"{segments} segments {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("L,dim,segments", [(1101, 130, 1), (1101, 130, 3), (37, 64, 1), (2048, 64, 0)])
 def test_eight_waves(dtype, L, dim, segments):
     """8 waves of 2 states per row block (bf16: 8-byte token slices): element
