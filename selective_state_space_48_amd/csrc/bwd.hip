@@ -102,11 +102,13 @@ __device__ __forceinline__ int quad_in(int row, int k) { return row * 4 + (k ^ (
 __device__ __forceinline__ int quad_out(int row, int k) { return row * 4 + (k ^ ((row >> 1) & 3)); }
 __device__ __forceinline__ float4& piece(float* base, int i) { return reinterpret_cast<float4*>(base)[i]; }
 
-// 4 consecutive tokens of type T as one load: 16 bytes (fp32) or 8 (bf16).
+// 4 consecutive tokens of type T as one load: 16 bytes (fp32) or 8 (bf16),
+// at any element-aligned address (rows need not start on a vector boundary:
+// gfx950's global loads and stores take unaligned addresses whole).
 template <typename T> struct Quad;
 template <> struct Quad<float> {
     using V = uint4;
-    static __device__ __forceinline__ V load(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+    static __device__ __forceinline__ V load(const float* p) { V v; __builtin_memcpy(&v, p, sizeof(V)); return v; }
     static __device__ __forceinline__ void unpack(const V& v, float* o) {
         o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
         o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
@@ -115,11 +117,11 @@ template <> struct Quad<float> {
         return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                           __float_as_uint(f[3]));
     }
-    static __device__ __forceinline__ void store(float* p, const V& v) { *reinterpret_cast<uint4*>(p) = v; }
+    static __device__ __forceinline__ void store(float* p, const V& v) { __builtin_memcpy(p, &v, sizeof(V)); }
 };
 template <> struct Quad<bf16_bits> {
     using V = uint2;
-    static __device__ __forceinline__ V load(const bf16_bits* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ V load(const bf16_bits* p) { V v; __builtin_memcpy(&v, p, sizeof(V)); return v; }
     static __device__ __forceinline__ void unpack(const V& v, float* o) {
         o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
     }
@@ -129,7 +131,7 @@ template <> struct Quad<bf16_bits> {
         };
         return make_uint2(p(f[0], f[1]), p(f[2], f[3]));
     }
-    static __device__ __forceinline__ void store(bf16_bits* p, const V& v) { *reinterpret_cast<uint2*>(p) = v; }
+    static __device__ __forceinline__ void store(bf16_bits* p, const V& v) { __builtin_memcpy(p, &v, sizeof(V)); }
 };
 
 // Sum of a over lanes {l, l^32} in lanes 0..31 and of b in lanes 32..63.
@@ -164,7 +166,7 @@ __device__ __forceinline__ void wave_sum16(const float* v, float* o) {
 
 // CARRY: the carry pass of a segmented backward (only the adjoint carry,
 // swept back over the segment from zero, and the summed step sizes).
-template <typename T, bool GATE, bool VEC, bool CARRY>
+template <typename T, bool GATE, bool CARRY>
 __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     using Q = Quad<T>;
     __shared__ BwdSmem sm;
@@ -205,13 +207,11 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     const float biasl = (a.dt_bias && prow_ok) ? a.dt_bias[dp] * kLog2e : 0.0f;
     const float Dd = (a.D && prow_ok) ? a.D[dp] : 0.0f;
 
-    // Without VEC the four tokens are loaded element by element, unconverted
-    // and from clamped addresses (no condition), so that the loads stay in
-    // flight until the prologue, which converts them and masks tokens past
-    // the row's end.
+    // A thread's four tokens are one vector load per tensor (at any
+    // alignment); a group that runs past the row's end is loaded element by
+    // element, zero past the end.
     struct In {
         typename Q::V x, d, z, g;
-        T xe[VEC ? 1 : 4], de[VEC ? 1 : 4], ze[VEC || !GATE ? 1 : 4], ge[VEC ? 1 : 4];
         float2 bc;  // 8 bytes of the chunk's packed B/C records
     };
     // The chunk's records are one contiguous 2 KiB block of P: 8 bytes a thread.
@@ -220,17 +220,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         in.bc = reinterpret_cast<const float2*>(Pb + int64_t(c) * (kBNSB * kBG * kRecF))[tid];
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
         const int64_t off = prow * a.L + t0;
-        if constexpr (!VEC) {
-            const int64_t last = prow * a.L + a.L - 1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t i = min(off + e, last);
-                in.xe[e] = X[i];
-                in.de[e] = DL[i];
-                if constexpr (GATE) in.ze[e] = Z[i];
-                in.ge[e] = DY[i];
-            }
-        } else if (t0 + kBTS <= a.L) {
+        if (t0 + kBTS <= a.L) {
             in.x = Q::load(X + off);
             in.d = Q::load(DL + off);
             if constexpr (GATE) in.z = Q::load(Z + off);
@@ -262,21 +252,10 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
     auto prologue = [&](int c, const In& in, Keep& k) {
         const int64_t t0 = int64_t(c) * kBCH + pq * kBTS;
         float xs[4], us[4], zs[4], gs[4];
-        if constexpr (VEC) {
-            Q::unpack(in.x, xs);
-            Q::unpack(in.d, us);
-            Q::unpack(in.g, gs);
-            if constexpr (GATE) Q::unpack(in.z, zs);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool ok = t0 + e < a.L;  // past the row's end: the clamped load's value
-                xs[e] = ok ? to_f32(in.xe[e]) : 0.0f;
-                us[e] = ok ? to_f32(in.de[e]) : 0.0f;
-                gs[e] = ok ? to_f32(in.ge[e]) : 0.0f;
-                zs[e] = (GATE && ok) ? to_f32(in.ze[e]) : 0.0f;
-            }
-        }
+        Q::unpack(in.x, xs);
+        Q::unpack(in.d, us);
+        Q::unpack(in.g, gs);
+        if constexpr (GATE) Q::unpack(in.z, zs);
         float l[4], w[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -468,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdKArgs a) {
         T* DXo = static_cast<T*>(a.dx);
         T* DDo = static_cast<T*>(a.ddelta);
         T* DZo = static_cast<T*>(a.dz);
-        if (VEC && t0 + kBTS <= a.L) {
+        if (t0 + kBTS <= a.L) {
             Q::store(DXo + off, Q::pack(dxv));
             Q::store(DDo + off, Q::pack(ddv));
             if constexpr (GATE) Q::store(DZo + off, Q::pack(dzv));
@@ -719,15 +698,10 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t dim, int32_t segments, bo
 }
 
 template <typename T, bool CARRY>
-hipError_t launch_bwd_kernel(const BwdKArgs& k, bool gate, bool vec, int64_t blocks, hipStream_t st) {
+hipError_t launch_bwd_kernel(const BwdKArgs& k, bool gate, int64_t blocks, hipStream_t st) {
     const dim3 grid{unsigned(blocks)}, block{256};
-    if (gate) {
-        if (vec) hipLaunchKernelGGL((bwd_kernel<T, true, true, CARRY>), grid, block, 0, st, k);
-        else hipLaunchKernelGGL((bwd_kernel<T, true, false, CARRY>), grid, block, 0, st, k);
-    } else {
-        if (vec) hipLaunchKernelGGL((bwd_kernel<T, false, true, CARRY>), grid, block, 0, st, k);
-        else hipLaunchKernelGGL((bwd_kernel<T, false, false, CARRY>), grid, block, 0, st, k);
-    }
+    if (gate) hipLaunchKernelGGL((bwd_kernel<T, true, CARRY>), grid, block, 0, st, k);
+    else hipLaunchKernelGGL((bwd_kernel<T, false, CARRY>), grid, block, 0, st, k);
     return hipGetLastError();
 }
 
@@ -773,7 +747,6 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
     k.segments = segments;
     k.seg_len = segments > 1 ? seg_len : int64_t(k.nck) * kBCH;
     const int64_t per_seg = int64_t(k.row_blocks) * batch;
-    const bool vec = L % 4 == 0;
     const bool gate = t.z != nullptr;
     const int64_t rows = batch * dim;
     if (segments > 1) {
@@ -782,7 +755,7 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
         kc.seg0 = 1;
         kc.rc_state = seg_state;
         kc.rc_lsum = seg_lsum;
-        e = launch_bwd_kernel<T, true>(kc, gate, vec, per_seg * (segments - 1), st);
+        e = launch_bwd_kernel<T, true>(kc, gate, per_seg * (segments - 1), st);
         if (e != hipSuccess) return e;
         e = launch_carry(t.A, seg_state, seg_lsum, t.dlast, carry, rows, dim, segments, st);
         if (e != hipSuccess) return e;
@@ -791,7 +764,7 @@ hipError_t bwd_t(const BwdTensors& t, int64_t batch, int64_t L, int64_t dim, int
         k.carry_in = t.dlast;
     }
     k.dh0 = t.dh0;
-    e = launch_bwd_kernel<T, false>(k, gate, vec, per_seg * segments, st);
+    e = launch_bwd_kernel<T, false>(k, gate, per_seg * segments, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce_bc<T>), dim3(unsigned((batch * 4 * L + kWave - 1) / kWave)), dim3(256), 0, st,
                        k.pB, k.pC, static_cast<T*>(t.dB), static_cast<T*>(t.dC), batch, L, k.Lp,

@@ -632,42 +632,19 @@ __global__ __launch_bounds__(kWave* G) void fwd_kernel(FwdKArgs a) {
             if constexpr (LOADZ) yv[j] *= gz[j];
         }
         T* Y = static_cast<T*>(a.y) + prow * a.L;
-        // Rows off a 16-byte boundary (RAW, 16-byte vectors), chunk wholly
-        // inside the row: the chunk's bytes are written as the aligned
-        // 16-byte blocks inside them, each the tail of one vector and the head
-        // of the next (the next lane's first vector for a lane's last), and
-        // element stores for the part before the first block boundary (lane
-        // 0) and after the last (lane G-1). Cached stores: the lines at a
-        // chunk's ends are completed by the neighbouring chunks' stores.
+        // Rows off a 16-byte boundary (RAW), chunk wholly inside the row: the
+        // thread's vectors are stored as they are, as 16-byte stores at
+        // 2-byte (bf16) or 4-byte (fp32) aligned addresses, which gfx950's
+        // global memory path takes whole (measured: 384 -> 328 us at the
+        // headline shape with L 2047, against element stores and the
+        // aligned-block shuffle this replaced).
         if constexpr (RAW && VB == 16) {
             if (t_begin + int64_t(c + 1) * CH <= t_end) {
-                uint4 v[SV];
-#pragma unroll
-                for (int k = 0; k < SV; ++k) v[k] = pack16<T, V>(yv + k * V);
-                uint4 nx;
-                nx.x = uint32_t(__shfl_down(int(v[0].x), 1, 64));
-                nx.y = uint32_t(__shfl_down(int(v[0].y), 1, 64));
-                nx.z = uint32_t(__shfl_down(int(v[0].z), 1, 64));
-                nx.w = uint32_t(__shfl_down(int(v[0].w), 1, 64));
                 if (!prow_ok) return;
-                const int64_t cb = (prow * a.L + t_begin + int64_t(c) * CH) * int64_t(sizeof(T));
-                const int s2 = int((16 - (cb & 15)) & 15);  // bytes before the first boundary
-                char* Yb = static_cast<char*>(a.y) + cb + s2 + int64_t(pq) * SV * 16;
 #pragma unroll
                 for (int k = 0; k < SV; ++k) {
-                    const bool last = pq == G - 1 && k == SV - 1;
-                    if (!last || s2 == 0) {
-                        *reinterpret_cast<uint4*>(Yb + 16 * k) = extract16(v[k], k + 1 < SV ? v[k + 1] : nx, s2);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < V; ++e)
-                            if (e * int(sizeof(T)) >= s2) Y[ts + k * V + e] = from_f32<T>(yv[k * V + e]);
-                    }
-                }
-                if (pq == 0) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        if (e * int(sizeof(T)) < s2) Y[ts + e] = from_f32<T>(yv[e]);
+                    const uint4 v = pack16<T, V>(yv + k * V);
+                    __builtin_memcpy(Y + ts + k * V, &v, 16);
                 }
                 return;
             }
