@@ -156,32 +156,18 @@ __global__ __launch_bounds__(256) void conv1d_kernel(const T* __restrict__ x,
         if (!active) return;
         __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(out + r * L + t0));
     } else {
-        // A row off a 16-byte boundary: each thread writes the aligned 16-byte
-        // block that starts s2 bytes into its vector (its tail and the head of
-        // the next thread's vector) when that block lies inside the row, and
-        // element stores for what no block covers (a row's ends, a wave's
-        // last lane, a block that would leave the row).
-        const u32x4 mine = pack_vec<T>(o);
-        u32x4 next;
-        next.x = uint32_t(__shfl_down(int(mine.x), 1, 64));
-        next.y = uint32_t(__shfl_down(int(mine.y), 1, 64));
-        next.z = uint32_t(__shfl_down(int(mine.z), 1, 64));
-        next.w = uint32_t(__shfl_down(int(mine.w), 1, 64));
+        // A row off a 16-byte boundary: the vector as one 16-byte store at its
+        // (2- or 4-byte aligned) address when it lies inside the row, which
+        // gfx950's global memory path takes whole; element stores at the row's end.
         if (!active) return;
-        const int lane = threadIdx.x % 64;
-        const int64_t es = int64_t(sizeof(T));
-        const int64_t bo = (r * L + t0) * es, row_end = (r * L + L) * es;
-        const int s2 = int((16 - (bo & 15)) & 15);  // bytes before the first 16-byte boundary
-        const bool own_block = (s2 == 0 || lane != 63) && bo + s2 + 16 <= row_end;
-        const bool head_by_prev = s2 > 0 && lane != 0 && v > 0 && bo + s2 <= row_end;
-        if (own_block)
-            *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) + bo + s2) = bytes16_at(mine, next, s2);
         T* orow = out + r * L;
+        if (t0 + V <= L) {
+            const u32x4 vo = pack_vec<T>(o);
+            __builtin_memcpy(orow + t0, &vo, 16);
+        } else {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const bool in_head = e * es < s2;
-            const bool covered = in_head ? head_by_prev : own_block;
-            if (!covered && t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
+            for (int e = 0; e < V; ++e)
+                if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
         }
     }
 }
@@ -387,36 +373,18 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
 #pragma unroll
         for (int e = 0; e < V; ++e)
             o[e] = fmaf(wd.x, gs[e + 3], fmaf(wd.y, gs[e + 2], fmaf(wd.z, gs[e + 1], wd.w * gs[e])));
-        // Rows off a 16-byte boundary: as in the forward, the aligned block
-        // that starts s2 bytes into the vector (its tail and the next lane's
-        // head), where it lies inside the row and the trip's range; element
-        // stores for the rest.
-        u32x4 mine{}, next{};
-        if constexpr (!VEC) {
-            mine = pack_vec<T>(o);
-            next.x = uint32_t(__shfl_down(int(mine.x), 1, 64));
-            next.y = uint32_t(__shfl_down(int(mine.y), 1, 64));
-            next.z = uint32_t(__shfl_down(int(mine.z), 1, 64));
-            next.w = uint32_t(__shfl_down(int(mine.w), 1, 64));
-        }
         if (v < v_hi) {
             T* orow = dx + r * L;
             if constexpr (VEC) {
                 __builtin_nontemporal_store(pack_vec<T>(o), reinterpret_cast<u32x4*>(orow + t0));
+            } else if (t0 + V <= L) {
+                // a row off a 16-byte boundary: one 16-byte store at the vector's address
+                const u32x4 vo = pack_vec<T>(o);
+                __builtin_memcpy(orow + t0, &vo, 16);
             } else {
-                const int lane = threadIdx.x % 64;
-                const int64_t es = int64_t(sizeof(T));
-                const int64_t bo = (r * L + t0) * es, row_end = (r * L + L) * es;
-                const int s2 = int((16 - (bo & 15)) & 15);
-                const bool own_block = (s2 == 0 || (lane != 63 && v + 1 < v_hi)) && bo + s2 + 16 <= row_end;
-                const bool head_by_prev = s2 > 0 && lane != 0 && bo + s2 <= row_end;
-                if (own_block)
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dx) + bo + s2) = bytes16_at(mine, next, s2);
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const bool covered = e * es < s2 ? head_by_prev : own_block;
-                    if (!covered && t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
-                }
+                for (int e = 0; e < V; ++e)
+                    if (t0 + e < L) orow[t0 + e] = from_f32<T>(o[e]);
             }
 #pragma unroll
             for (int e = 0; e < V; ++e) {
