@@ -66,6 +66,8 @@ SHAPES = [
     (2, 100, 130, "bf16"),
     (1, 300, 64, "f32"),
     (3, 64, 40, "bf16"),
+    (2, 1023, 70, "bf16"),   # rows off every vector boundary: vector loads and stores at 2-byte offsets
+    (1, 517, 33, "f32"),     # and at 4-byte offsets
 ]
 
 
