@@ -1182,6 +1182,59 @@ __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B, c
     reinterpret_cast<float4*>(P)[f] = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// The same packing for G = 4 and rows of whole 4-token vectors, as a tile
+// transpose: a workgroup takes 64 sub-blocks (256 tokens) of one batch entry,
+// reads its B and C rows with whole-line loads (consecutive threads on
+// consecutive 4-token vectors of one row), places each vector at its record
+// position in LDS (padded by one float4 per 32 so that the writes spread
+// over the banks), and writes the 2,048 float4s of its records contiguously.
+// Each float4 of a record is one 4-token vector of one state row, so the
+// tile is a permutation of whole vectors.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_bc4_kernel(const T* __restrict__ B, const T* __restrict__ C,
+                                                      float* __restrict__ P, int64_t L, int64_t Lp) {
+    constexpr int kSub = 64;                  // sub-blocks per workgroup
+    constexpr int kRecs = kSub * 32;          // float4s of their records (4 groups x 2 x 4)
+    __shared__ float4 tile[kRecs + kRecs / 32];
+    const int64_t psub = Lp / 4;
+    const int64_t tiles = (psub + kSub - 1) / kSub;
+    const int64_t b = blockIdx.x / tiles;
+    const int64_t s0 = (blockIdx.x % tiles) * kSub;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < kRecs / 256; ++m) {
+        const int i = tid + 256 * m;
+        const int k = i / (kN * kSub), n = (i / kSub) % kN, sq = i % kSub;
+        const int64_t t = (s0 + sq) * 4;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < L) {  // whole: L is a multiple of 4
+            const T* p = (k ? C : B) + (b * kN + n) * L + t;
+            if constexpr (sizeof(T) == 4) {
+                const float4 u = *reinterpret_cast<const float4*>(p);
+                v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+            } else {
+                const uint2 u = *reinterpret_cast<const uint2*>(p);
+                v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+            }
+            // B is stored times ln 2 (the scan's input term is (l x) B' with l in log2 units)
+            if (k == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= kLn2;
+            }
+        }
+        const int o = sq * 32 + (n / 4) * 8 + k * 4 + n % 4;  // position among the tile's records
+        tile[o + o / 32] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __syncthreads();
+    float4* dst = reinterpret_cast<float4*>(P) + (b * psub + s0) * 32;
+    const int64_t left = (psub - s0) * 32;  // float4s of this batch entry's records from s0 on
+#pragma unroll
+    for (int m = 0; m < kRecs / 256; ++m) {
+        const int o = tid + 256 * m;
+        if (o < left) dst[o] = tile[o + o / 32];
+    }
+}
+
 // Carry pass: for each (row, n), compose the segments in order,
 //   H_{s+1} = 2^(A_n * lsum_s) H_s + state_s,  H_0 = h0 (or 0),
 // and write the state entering every segment. 2^(A * sum of l) is the
@@ -1346,7 +1399,14 @@ hipError_t launch_pack(const void* B, const void* C, float* P, int64_t batch, in
     switch (groups) {
         case 1: hipLaunchKernelGGL((pack_bc_kernel<T, 1>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
         case 2: hipLaunchKernelGGL((pack_bc_kernel<T, 2>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
-        case 4: hipLaunchKernelGGL((pack_bc_kernel<T, 4>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
+        case 4:
+            if (L % 4 == 0) {
+                const int64_t tiles = (Lp / 4 + 63) / 64;
+                hipLaunchKernelGGL((pack_bc4_kernel<T>), dim3(unsigned(batch * tiles)), block, 0, st, b, c, P, L, Lp);
+            } else {
+                hipLaunchKernelGGL((pack_bc_kernel<T, 4>), grid, block, 0, st, b, c, P, batch, L, Lp);
+            }
+            break;
         case 8: hipLaunchKernelGGL((pack_bc_kernel<T, 8>), grid, block, 0, st, b, c, P, batch, L, Lp); break;
         default: return hipErrorInvalidValue;
     }
