@@ -159,22 +159,31 @@ def _pct(v, q):
 
 def per_call_distribution(run, torch, dev, n=20, scratch_mb=512):
     """Per-call times (µs) of ``n`` calls, each bracketed by its own events:
-    warm (right after an untimed call) and cold (right after a 512 MB scratch
-    buffer is written, which evicts the 256 MB last-level cache and the L2s)."""
+    warm (right after an untimed call); ``cold``: with the caches flushed,
+    i.e. a 512 MB scratch buffer written and then a second 512 MB buffer read,
+    so that the 256 MB last-level cache and the L2s hold neither the call's
+    data nor dirty lines waiting to be written back (the write-back of the
+    first sweep happens during the second, before the call); and
+    ``cold_dirty``: right after the write sweep alone, where the call's misses
+    also evict the sweep's dirty lines and pay for writing them back."""
     stream = torch.cuda.current_stream(dev)
     scratch = torch.empty(scratch_mb << 18, dtype=torch.float32, device=dev)
+    scratch_r = torch.ones(scratch_mb << 18, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     out = {}
-    for mode in ("warm", "cold"):
+    for mode in ("warm", "cold", "cold_dirty"):
         ts = []
         for i in range(n):
             torch.cuda.synchronize(dev)
             # The timed call is queued behind other work (a call, or the
-            # scratch fill), so the events measure its execution, not the
-            # launch latency of an idle GPU.
-            if mode == "cold":
-                scratch.fill_(float(i))
-            else:
+            # sweeps), so the events measure its execution, not the launch
+            # latency of an idle GPU.
+            if mode == "warm":
                 run()
+            else:
+                scratch.fill_(float(i))
+                if mode == "cold":
+                    torch.sum(scratch_r, dim=0, out=sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             run()
@@ -183,7 +192,7 @@ def per_call_distribution(run, torch, dev, n=20, scratch_mb=512):
             ts.append(a.elapsed_time(b) * 1e3)
         out[mode] = {"p10_us": round(_pct(ts, 0.1), 2), "p50_us": round(_pct(ts, 0.5), 2),
                      "p90_us": round(_pct(ts, 0.9), 2)}
-    del scratch
+    del scratch, scratch_r, sink
     return out
 
 
@@ -879,13 +888,17 @@ def main():
         cold = ddist["cold"]["p50_us"]
         log(f"[bench] decode: {us:.2f} us/step back to back ({kus:.2f} us kernel, {gbs:.0f} GB/s); "
             f"cold median {cold:.2f} us")
-        # Primary: the median of the 64 distinct steps each run right after a
-        # 512 MB scratch write that evicts the last-level cache (the 84 MB
-        # state would otherwise stay in it between back-to-back steps; in a
-        # model the other layers run in between). Back to back: secondary.
+        # Primary: the median of the 64 distinct steps each run with the
+        # caches flushed (a 512 MB write sweep, then a 512 MB read sweep of
+        # another buffer: the 84 MB state would otherwise stay in the 256 MB
+        # last-level cache between back-to-back steps; in a model the other
+        # layers run in between). Beside it: right after the write sweep
+        # alone (the step also writes back the sweep's dirty lines), and back
+        # to back.
         cold_gbs = step_bytes(wd) / (cold * 1e-6) / 1e9
         extras["decode"] = {"workload": wd.name, "us_per_step": round(cold, 3),
-                            "us_per_step_is": "cold p50 (caches evicted before each step)",
+                            "us_per_step_is": "cold p50 (caches flushed before each step: write sweep, then read sweep)",
+                            "cold_dirty_us_per_step": ddist["cold_dirty"]["p50_us"],
                             "achieved_GBps": round(cold_gbs, 1),
                             "frac_hbm": round(cold_gbs * 1e9 / HBM_PEAK, 4),
                             "back_to_back_us_per_step": round(us, 3),
