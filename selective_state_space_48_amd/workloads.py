@@ -214,11 +214,17 @@ def conv_inputs(w: Workload, batches: Optional[Sequence[int]] = None) -> Dict[st
     for i, b in enumerate(bs):
         x[i] = _rng(w.seed, TID_X, b).standard_normal((d, L), dtype=np.float32)
         prev[i] = _rng(w.seed, TID_CONV_PREV, b).standard_normal((d, 3), dtype=np.float32)
+    out = {"x": _maybe_bf16(w, x), "x_prev": _maybe_bf16(w, prev)}
+    out.update(conv_params(w))
+    return out
+
+
+def conv_params(w: Workload) -> Dict[str, np.ndarray]:
+    """The convolution's taps w [dim, 4] ~ N(0, 0.5^2) and bias [dim] ~ N(0, 0.1^2)
+    (float32; the streams ``conv_inputs`` uses)."""
     return {
-        "x": _maybe_bf16(w, x),
-        "x_prev": _maybe_bf16(w, prev),
-        "w": (_rng(w.seed, TID_CONV_W, 0).standard_normal((d, 4), dtype=np.float32) * 0.5),
-        "bias": (_rng(w.seed, TID_CONV_BIAS, 0).standard_normal(d, dtype=np.float32) * 0.1),
+        "w": (_rng(w.seed, TID_CONV_W, 0).standard_normal((w.dim, 4), dtype=np.float32) * 0.5),
+        "bias": (_rng(w.seed, TID_CONV_BIAS, 0).standard_normal(w.dim, dtype=np.float32) * 0.1),
     }
 
 
@@ -249,13 +255,37 @@ def ssd_inputs(batch: int, seqlen: int, heads: int, headdim: int, dstate: int, s
             out[i] = _rng(seed, TID_SSD + k, b).standard_normal(shape, dtype=np.float32)
         return _round_bf16(out)
 
-    v = np.exp(_rng(seed, TID_SSD + 5, 0).uniform(np.log(1e-3), np.log(1e-1), size=heads))
-    return {
+    out = {
         "x": draw(0, (seqlen, heads, headdim)),
         "delta": draw(1, (seqlen, heads)),
         "B": draw(2, (seqlen, dstate)),
         "C": draw(3, (seqlen, dstate)),
+    }
+    out.update(ssd_params(heads, seed))
+    return out
+
+
+def ssd_params(heads: int, seed: int) -> Dict[str, np.ndarray]:
+    """Per-head parameters of the SSD layer (the streams ``ssd_inputs`` uses):
+    A = -U[1, 16], dt_bias with softplus(dt_bias) log-uniform in [1e-3, 1e-1],
+    D ~ U[0.5, 1.5] (float32)."""
+    v = np.exp(_rng(seed, TID_SSD + 5, 0).uniform(np.log(1e-3), np.log(1e-1), size=heads))
+    return {
         "A": -_rng(seed, TID_SSD + 4, 0).uniform(1.0, 16.0, size=heads).astype(np.float32),
         "dt_bias": np.log(np.expm1(v)).astype(np.float32),
         "D": _rng(seed, TID_SSD + 6, 0).uniform(0.5, 1.5, size=heads).astype(np.float32),
     }
+
+
+def device_normal(shape, seed: int, tid: int, device, dtype):
+    """N(0, 1) values drawn directly on the device by torch's generator, seeded
+    from (seed, tid), then rounded to ``dtype``: for tensors too large to draw
+    on the host (billions of elements). These values are not those of the
+    host streams above; a comparison reads both sides' inputs from the device
+    tensor."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(tid))
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return t if dtype == torch.float32 else t.to(dtype)
