@@ -172,3 +172,43 @@ def test_ssd_past_2g_elements():
     print("[parity] large ssd: sampled heads within tolerance", flush=True)
     del x, dl, B, C, y, hs
     release()
+
+
+def test_bwd_past_2g_elements():
+    """The backward (bf16, batch 3, L 2^18, d_inner 4096: 3.2e9 elements per
+    tensor, and 13 GB of 16-token checkpoints) on sampled channels: for each,
+    the oracle's backward of that channel's rows over all batch entries gives
+    dx, ddelta and dz of those rows and the channel's dA, dD and ddt_bias
+    exactly (they sum over the batch entries of one channel). dB and dC sum over
+    all channels, which no sample gives; the other backward tests compare them."""
+    w = W.scaled(W.get(W.HEADLINE), batch=3, seqlen=1 << 18, dim=4096)
+    batch, dim, L, N = w.batch, w.dim, w.seqlen, w.dstate
+    elems = batch * dim * L
+    assert elems > 2 ** 31
+    need_gib(elems * 2 * 7 / 2 ** 30 + (L // 16) * batch * dim * N * 4 / 2 ** 30 + 8)
+    case(f"bwd bf16 B{batch} L{L} d{dim}")
+    p = W.params(w)
+    x = W.device_normal((batch, dim, L), w.seed, W.TID_X, "cuda", BF)
+    dl = W.device_normal((batch, dim, L), w.seed, W.TID_DELTA, "cuda", BF)
+    z = W.device_normal((batch, dim, L), w.seed, W.TID_Z, "cuda", BF)
+    B = W.device_normal((batch, N, L), w.seed, W.TID_B, "cuda", BF)
+    C = W.device_normal((batch, N, L), w.seed, W.TID_C, "cuda", BF)
+    dy = W.device_normal((batch, dim, L), w.seed, 99, "cuda", BF)
+    dv = {k: torch.from_numpy(v).cuda() for k, v in p.items()}
+    g = selscan.bwd(x, dl, dv["A"], B, C, D=dv["D"], z=z, dt_bias=dv["dt_bias"], dy=dy)
+    torch.cuda.synchronize()
+    Bh, Ch = host(B), host(C)
+    worst = {}
+    for d in (0, 63, 64, dim // 2 + 3, dim - 1):
+        sl = slice(d, d + 1)
+        ref = oracle.bwd(host(x[:, sl]), host(dl[:, sl]), p["A"][sl], Bh, Ch, p["D"][sl], host(z[:, sl]),
+                         p["dt_bias"][sl], dy=host(dy[:, sl]))
+        for k in ("dx", "ddelta", "dz"):
+            worst[k] = max(worst.get(k, 0.0), oracle.scaled_error(host(g[k][:, sl]), ref[k], ref[k + "_scale"]))
+        for k in ("dA", "dD", "ddt_bias"):
+            worst[k] = max(worst.get(k, 0.0), oracle.scaled_error(host(g[k][sl]), ref[k], ref[k + "_scale"]))
+    print("[parity] large bwd: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()), flush=True)
+    bad = {k: v for k, v in worst.items() if not v <= TOL["bf16"]}
+    assert not bad, bad
+    del x, dl, z, B, C, dy, g
+    release()
