@@ -218,9 +218,14 @@ __global__ __launch_bounds__(256) void conv_step_kernel(float* __restrict__ stat
 // its batch entries 256 vectors per trip, one vector per thread, with the
 // next trip's loads in flight while it computes the current one. Each thread
 // loads, beside its vector, the 4 inputs before it and the 4 inputs and
-// output gradients after it (cache hits: the neighbouring lanes' vectors),
-// so that it forms g of the 3 tokens after its vector itself; no lane waits
-// for another. The thread's sums for dw and dbias, added over its trips in
+// output gradients after it (cache hits: the neighbouring lanes' vectors).
+// dx of a vector needs g of the 3 tokens after it, which the thread holding
+// the next vector forms anyway: a lane takes them from the lane above (a
+// cross-lane shuffle), lane 63 of a wave from lane 0 of the next wave through
+// LDS (one barrier per trip); only where the next vector lies outside the
+// trip (the trip's last thread, or the end of a piece inside the row) does a
+// thread form them itself, from its own loads; after a row's last vector
+// they are 0. The thread's sums for dw and dbias, added over its trips in
 // order, then over the workgroup in a fixed order, give one partial per
 // (channel, batch group, piece); conv1d_bwd_reduce adds a channel's partials
 // in order.
@@ -321,6 +326,8 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
                                                          int32_t bgroups, int32_t pieces) {
     constexpr int V = CElem<T>::kPer16;
     __shared__ float red[5][4];
+    __shared__ float halo[2][4][4];  // by trip parity and wave: g of the wave's lane 0, first 3 tokens
+    const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
     const int64_t d = blockIdx.x / (int64_t(bgroups) * pieces);
     const int bg = int(blockIdx.x / pieces % bgroups);
     const int sg = int(blockIdx.x % pieces);
@@ -365,9 +372,37 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
             for (int e = 0; e < 3; ++e) xs[e] = x_prev ? x_prev[r * 3 + e] : 0.0f;
         }
 #pragma unroll
-        for (int e = 0; e < V + 3; ++e) {
-            const bool in_row = VEC ? (e < V || vc != nvec - 1) : t0 + e < L;
+        for (int e = 0; e < V; ++e) {
+            const bool in_row = VEC || t0 + e < L;
             gs[e] = in_row ? gof(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]), dys[e]) : 0.0f;
+        }
+        // g of the 3 tokens after the vector: 0 after the row's last vector;
+        // else from the thread that holds the next vector when it is in this
+        // trip, else formed here
+        const bool row_end = VEC ? vc == nvec - 1 : t0 + V >= L;
+        const bool from_next = threadIdx.x < 255 && v + 1 < v_hi;
+        float hn[3];
+#pragma unroll
+        for (int e = 0; e < 3; ++e) hn[e] = __shfl_down(gs[e], 1, 64);
+        const int hb = int(i & 1);
+        if (lane == 0 && wv > 0) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) halo[hb][wv][e] = gs[e];
+        }
+        __syncthreads();
+        if (lane == 63) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) hn[e] = halo[hb][(wv + 1) & 3][e];
+        }
+        if (row_end || from_next) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) gs[V + e] = row_end ? 0.0f : hn[e];
+        } else {
+#pragma unroll
+            for (int e = V; e < V + 3; ++e) {
+                const bool in_row = VEC || t0 + e < L;
+                gs[e] = in_row ? gof(conv4(wd, bd, xs[e], xs[e + 1], xs[e + 2], xs[e + 3]), dys[e]) : 0.0f;
+            }
         }
         float o[V];
 #pragma unroll
@@ -403,7 +438,6 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(const T* __restrict__ x
         cur = nxt;
     }
     // a fixed tree over the wave's lanes, then the four waves in order
-    const int lane = threadIdx.x % 64;
     float v5[5] = {aw[0], aw[1], aw[2], aw[3], ab};
 #pragma unroll
     for (int i = 0; i < 5; ++i)
