@@ -212,3 +212,60 @@ def test_bwd_past_2g_elements():
     assert not bad, bad
     del x, dl, z, B, C, dy, g
     release()
+
+
+def test_ssd_step_past_2g_state_elements():
+    """The SSD decode step on a state of 2.7e9 floats (10 GiB): batch 5120 x
+    64 heads x state 128 x 64 channels."""
+    batch, H, N, P, seed = 5120, 64, 128, 64, 6
+    assert batch * H * N * P > 2 ** 31
+    need_gib(batch * H * N * P * 4 / 2 ** 30 + 6)
+    case(f"ssd step bf16 B{batch} H{H} N{N} P{P}")
+    p = W.ssd_params(H, seed)
+    state = W.device_normal((batch, H, N, P), seed, W.TID_SSD + 10, "cuda", torch.float32) * 0.1
+    x = W.device_normal((batch, H, P), seed, W.TID_SSD + 0, "cuda", BF)
+    dl = W.device_normal((batch, H), seed, W.TID_SSD + 1, "cuda", BF)
+    B = W.device_normal((batch, N), seed, W.TID_SSD + 2, "cuda", BF)
+    C = W.device_normal((batch, N), seed, W.TID_SSD + 3, "cuda", BF)
+    picks = ((0, 0), (4096, 31), (batch - 1, 5), (batch - 1, H - 1))
+    before = {bh: host(state[bh]) for bh in picks}
+    dv = {k: torch.from_numpy(v).cuda() for k, v in p.items()}
+    y = selscan.ssd_step(state, x, dl, dv["A"], B, C, D=dv["D"], dt_bias=dv["dt_bias"])
+    torch.cuda.synchronize()
+    for (b, h) in picks:
+        ref = oracle.ssd_step(before[(b, h)][None, None], host(x[b, h])[None, None],
+                              host(dl[b, h]).reshape(1, 1), p["A"][h:h + 1], host(B[b])[None],
+                              host(C[b])[None], p["D"][h:h + 1], p["dt_bias"][h:h + 1])
+        ey = oracle.scaled_error(host(y[b, h])[None, None], ref["y"], ref["y_scale"])
+        es_ = oracle.scaled_error(host(state[b, h])[None, None], ref["state"], ref["state_scale"])
+        assert ey <= TOL["bf16"] and es_ <= TOL["bf16"], f"(b, h) = ({b}, {h}): {ey:.3e} {es_:.3e}"
+    print("[parity] large ssd step: sampled heads within tolerance", flush=True)
+    del state, x, dl, B, C, y
+    release()
+
+
+def test_conv_step_past_2g_state_elements():
+    """The convolution's decode step on a state of 3.2e9 floats (12 GiB):
+    batch 32768 x d_inner 32768 rows of 3 inputs, bf16."""
+    w = W.scaled(W.get(W.DECODE), batch=32768, dim=32768)
+    batch, dim = w.batch, w.dim
+    assert batch * dim * 3 > 2 ** 31
+    need_gib(batch * dim * (3 * 4 + 2 * 2) / 2 ** 30 + 6)
+    case(f"conv step bf16 B{batch} d{dim}")
+    cp = W.conv_params(w)
+    st = W.device_normal((batch, dim, 3), w.seed, W.TID_CONV_PREV, "cuda", BF).float()
+    x = W.device_normal((batch, dim), w.seed, W.TID_CONV_STEP0, "cuda", BF)
+    rows = flat_rows(batch, dim)
+    before = {r: host(st[r // dim, r % dim]) for r in rows}
+    out = selscan.conv1d_step(st, x, torch.from_numpy(cp["w"]).cuda(), torch.from_numpy(cp["bias"]).cuda())
+    torch.cuda.synchronize()
+    for r in rows:
+        b, d = divmod(r, dim)
+        ref = oracle.conv1d_step(before[r][None, None], host(x[b, d]).reshape(1, 1), cp["w"][d:d + 1],
+                                 cp["bias"][d:d + 1])
+        err = oracle.scaled_error(host(out[b, d]).reshape(1, 1), ref["out"], ref["out_scale"])
+        assert err <= TOL["bf16"], f"row {r}: err={err:.3e}"
+        assert np.array_equal(host(st[b, d]), ref["conv_state"][0, 0]), f"row {r}: state"
+    print("[parity] large conv step: sampled rows within tolerance", flush=True)
+    del st, x, out
+    release()
